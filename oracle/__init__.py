@@ -1,0 +1,41 @@
+"""Plain CPU oracle for draft-block verification (test infrastructure only).
+
+This package is the slow, obviously-correct reference that the HIP path is
+checked against.  It is NOT part of the product: only the test-suite, the
+smoke check in ``__graft_entry__`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it.  It shares no code, constant tables or helpers
+with the HIP library; both sides only consume the same seeded inputs.
+
+Everything is computed in float64 with explicit per-row / per-sequence loops,
+following the pages' definitions in their own order:
+
+* ``rows``   -- per-row quantities: tempered softmax, lowest-index argmax,
+  the acceptance test, inverse-CDF draws, the residual ``[p~ - q]_+``.
+* ``chain``  -- per-sequence verification of a drafted chain: greedy match,
+  lossless rejection and the linear lenient rule, with the stopping rule and
+  next-draft retention.
+* ``tree``   -- coupled shared-Gumbel state-equality verification of a draft
+  tree (and its T=0 greedy special case).
+
+Sources (pages by title):
+* "One Call Ahead: Packed Self-Speculative Decoding with Diffusion Drafting"
+  (Packed-SS): Sec. 2.2, Sec. 3.1 Eq. 1-4 and Algorithm 1, Sec. 3.2,
+  App. B.2 Algorithm 2 and Lemma B.3, App. D.1.
+* "On the SPOT: Enhancing Speculative Decoding for Diffusion Language Models
+  via Commit-Order Prediction" (SPOT): Sec. 4.1, Sec. 4.3, App. A.1, A.3
+  Eq. 5-7, App. B Eq. 10-14.
+* "Speculative Diffusion is a Tale of Two Tradeoffs" (Two Tradeoffs): Sec. 2
+  Eq. 1-5 and Theorem 1, Sec. 3.2 Algorithm 1, App. C Proposition 1.
+"""
+
+from .rows import (  # noqa: F401
+    STATUS_BAD_INPUT, STATUS_NONFINITE, STATUS_EMPTY_ROW, STATUS_Q_ZERO,
+    STATUS_Z_ZERO, STATUS_ERROR_MASK, NEAR_MARGIN,
+    row_status, tempered_softmax, argmax_lowest, acceptance_test,
+    inverse_cdf, residual_weights, stopping_index,
+)
+from .chain import verify_greedy, verify_rejection, verify_lenient  # noqa: F401
+from .tree import (  # noqa: F401
+    TREE_STATE_EQUALITY, TREE_FIXED_POSITION, state_transition,
+    verify_gumbel_tree,
+)

@@ -1,0 +1,132 @@
+"""Plant typical mistakes in the oracle (on the CPU) and check that some pin
+catches each one.  This is evidence that the pins constrain the oracle, not a
+test of the product."""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.chain as chain
+import oracle.rows as rows
+import oracle.tree as tree
+import tests.test_oracle_chain_pins as cp
+import tests.test_oracle_tree_pins as tp
+
+
+def _patch(monkeypatch, name, fn):
+    for mod in (oracle, rows, chain, tree):
+        if hasattr(mod, name):
+            monkeypatch.setattr(mod, name, fn)
+
+
+def _acc_no_min(u, p_d, q_d, lam=0.0):
+    pt = (1 - lam) * p_d + lam * q_d
+    alpha = pt / q_d if q_d > 0 else 1.0
+    return bool(u < alpha), alpha, abs(u - alpha), False
+
+
+def _acc_inverted(u, p_d, q_d, lam=0.0):
+    pt = (1 - lam) * p_d + lam * q_d
+    alpha = min(1.0, q_d / pt) if pt > 0 else 1.0
+    return bool(u < alpha), alpha, abs(u - alpha), False
+
+
+def _acc_le(u, p_d, q_d, lam=0.0):
+    pt = (1 - lam) * p_d + lam * q_d
+    alpha = min(1.0, pt / q_d) if q_d > 0 else (1.0 if pt > 0 else 0.0)
+    return bool(u <= alpha), alpha, abs(u - alpha), bool(q_d == 0 and pt > 0)
+
+
+def _acc_lam_swapped(u, p_d, q_d, lam=0.0):
+    pt = lam * p_d + (1 - lam) * q_d
+    alpha = min(1.0, pt / q_d) if q_d > 0 else (1.0 if pt > 0 else 0.0)
+    return bool(u < alpha), alpha, abs(u - alpha), False
+
+
+def _res_sign(p, q, lam=0.0):
+    pt = (1 - lam) * np.asarray(p) + lam * np.asarray(q)
+    return np.maximum(np.asarray(q) - pt, 0.0)
+
+
+def _res_plain_p(p, q, lam=0.0):
+    return np.asarray(p, np.float64).copy()
+
+
+def _softmax_times_T(x, T):
+    a = np.asarray(x, np.float64) * T
+    w = np.exp(a - a.max())
+    return w / w.sum()
+
+
+def _argmax_highest(x):
+    x = np.asarray(x, np.float64)
+    return int(np.flatnonzero(x == x.max())[-1])
+
+
+def _icdf_ge(w, u):
+    w = np.asarray(w, np.float64)
+    F = np.cumsum(w)
+    Z = F[-1]
+    c = int(np.flatnonzero(F >= u * Z)[0])
+    return c, 1.0, Z
+
+
+def _stop_ignores_eos(C, A, eos_id=-1, budget=None):
+    return A if budget is None else min(A, budget)
+
+
+MUTATIONS = [
+    ("acceptance_test", _acc_no_min, cp.test_exact_acceptance_rate_is_one_minus_tv, dict(lam=0.0)),
+    ("acceptance_test", _acc_inverted, cp.test_exact_acceptance_rate_is_one_minus_tv, dict(lam=0.0)),
+    ("acceptance_test", _acc_le, cp.test_acceptance_strict_inequality_and_zero_q, {}),
+    ("acceptance_test", _acc_lam_swapped, cp.test_exact_acceptance_rate_is_one_minus_tv, dict(lam=0.25)),
+    ("residual_weights", _res_sign, cp.test_emitted_law_exact_enumeration, dict(lam=0.0)),
+    ("residual_weights", _res_plain_p, cp.test_emitted_law_exact_enumeration, dict(lam=0.0)),
+    ("tempered_softmax", _softmax_times_T, cp.test_softmax_two_token_is_logistic, dict(T=0.3)),
+    ("argmax_lowest", _argmax_highest, cp.test_argmax_lowest_index_brute_force, {}),
+    ("inverse_cdf", _icdf_ge, cp.test_inverse_cdf_edges, {}),
+    ("stopping_index", _stop_ignores_eos, cp.test_stopping_rule_eos_and_budget, {}),
+]
+
+
+@pytest.mark.parametrize("name,fn,pin,kw", MUTATIONS,
+                         ids=[f"{m[0]}-{m[1].__name__}" for m in MUTATIONS])
+def test_pin_catches_planted_mistake(monkeypatch, name, fn, pin, kw):
+    _patch(monkeypatch, name, fn)
+    with pytest.raises(AssertionError):
+        pin(**kw)
+
+
+def test_pin_catches_retention_off_by_one(monkeypatch):
+    orig = chain.verify_greedy
+
+    def shifted(*a, **k):
+        out = orig(*a, **k)
+        nd = out["next_draft"]
+        out["next_draft"] = np.concatenate([nd[:, 1:], np.full((nd.shape[0], 1), -1, nd.dtype)], 1)
+        return out
+    monkeypatch.setattr(oracle, "verify_greedy", shifted)
+    with pytest.raises(AssertionError):
+        cp.test_greedy_fig2_worked_example()
+
+
+def test_pin_catches_gumbel_temperature_mistake(monkeypatch):
+    def wrong(x, T):
+        a = np.asarray(x, np.float64) * T
+        m = a.max()
+        return a - m - np.log(np.exp(a - m).sum())
+    monkeypatch.setattr(tree, "_log_tempered_softmax", wrong)
+    with pytest.raises(AssertionError):
+        tp.test_gumbel_draw_has_tempered_law(T=0.5)
+
+
+def test_pin_catches_walk_not_following_child(monkeypatch):
+    orig = tree.verify_gumbel_tree
+
+    def stops_at_root(*a, **k):
+        out = orig(*a, **k)
+        out["path_len"][:] = np.minimum(out["path_len"], 0)
+        return out
+    monkeypatch.setattr(oracle, "verify_gumbel_tree", stops_at_root)
+    with pytest.raises(AssertionError):
+        tp.test_orbit_tree_is_accepted_to_full_depth(T=1.0)
