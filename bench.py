@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of parallel draft-block verification on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+A step is one verify call over one batch of synthetic inputs already resident
+in HBM: every row statistic / argmax, the acceptance tests, the prefix scan,
+and the correction or bonus draw.  Workloads (sizes of the pages' setups):
+
+  c1  tiny rejection verify       B=1  K=4  V=1024   fp32
+  c2  batch lossless verify       B=8  K=8  V=32000  bf16   (default)
+  c3  lenient verify              B=32 K=16 V=128256 bf16, sigma=1, T=1, lambda=0.5
+  c4  coupled-Gumbel tree verify  B=16 S=64 L=32 V=151936 bf16
+  c5  packed greedy verify+draft  B=64 K=32 V=131072 bf16
+
+Inputs smaller than 1 GiB are replicated into several buffer sets and the
+steps rotate over them, so the 256 MiB last-level cache cannot serve them.
+Prints one JSON line: whole-job verified draft positions per second, the
+roofline of the row-streaming kernel (timed alone with HIP events on the
+launch stream), and the CPU oracle timed on a bounded sample.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "verified draft positions/sec and achieved HBM GB/s vs MI355X peak (1 GPU)"
+ROTATE_BYTES = 1 << 30         # replicate inputs up to this many bytes
+
+DESCR = {
+    "c1": "tiny rejection verify B=1 K=4 V=1024 fp32",
+    "c2": "batch lossless verify B=8 K=8 V=32000 bf16",
+    "c3": "lenient verify B=32 K=16 V=128256 bf16 sigma=1 T=1 lambda=0.5",
+    "c4": "coupled-Gumbel tree verify B=16 S=64 L=32 V=151936 bf16",
+    "c5": "packed greedy verify+draft B=64 K=32 V=131072 bf16",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="c2", choices=sorted(DESCR))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------- workloads ---
+
+class Case:
+    """One workload: prepared calls over R rotated input sets, plus what the
+    roofline and the CPU baseline need."""
+
+    def __init__(self, name, dev):
+        import draft_block_verification_amd as dbv
+        import workloads
+        self.name = name
+        self.dev = dev
+        eb = 2
+        if name in ("c1", "c2", "c3"):
+            if name == "c1":
+                x = workloads.config1()
+                eb = 4
+            elif name == "c2":
+                x = workloads.config2()
+            else:
+                x = workloads.config3(1.0, 1.0)
+            self.lam = 0.5 if name == "c3" else 0.0
+            B, K1, V = x["tgt"].shape
+            K = K1 - 1
+            n = x["draft_len"].long()
+            self.positions = int(n.sum())
+            self.kernel_bytes = int(((2 * n + 1) * V * eb).sum())      # target n+1 rows, draft n rows
+            self.kernel = "k_sample_rows"
+            per_set = (x["tgt"].numel() + x["drf"].numel()) * eb
+            self.cpu_inputs = x
+            self.calls = []
+            R = self._rotation(per_set)
+            for _ in range(R):
+                xd = {k: v.to(dev).clone() if torch.is_tensor(v) else v for k, v in x.items()}
+                fn = dbv.verify_lenient if name == "c3" else dbv.verify_rejection
+                kw = dict(draft_len=xd["draft_len"], temperature_target=x["temperature"],
+                          temperature_draft=x["temperature"], prepare=True)
+                if name == "c3":
+                    c = fn(xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"],
+                           self.lam, **kw)
+                else:
+                    c = fn(xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"], **kw)
+                self.calls.append(c)
+            self.shape = dict(B=B, K=K, V=V)
+        elif name == "c5":
+            x = workloads.config5()
+            K, W = x["K"], x["W"]
+            B, _, V = x["packed"].shape
+            n = x["draft_len"].long()
+            self.positions = int(n.sum())
+            self.kernel_bytes = int(((n + 1 + W) * V * eb).sum())
+            self.kernel = "k_greedy_rows"
+            per_set = x["packed"].numel() * eb
+            self.cpu_inputs = x
+            self.calls = []
+            for _ in range(self._rotation(per_set)):
+                p = x["packed"].to(dev)
+                self.calls.append(dbv.verify_greedy(p[:, :K + 1], x["draft_tokens"].to(dev),
+                                                    x["draft_len"].to(dev), p[:, K + 1:], prepare=True))
+            self.shape = dict(B=B, K=K, W=W, V=V)
+        else:  # c4
+            x = workloads.config4(device=dev)
+            B, S, L, V = x["logits"].shape
+            ns = x["num_states"].long()
+            self.positions = int((ns - 1).sum())
+            m = x["masked"].clone()
+            for b in range(B):
+                m[b, int(ns[b]):] = False
+            self.kernel_bytes = int(m.sum()) * V * eb
+            self.kernel = "k_tree_conf"
+            self.cpu_inputs = x
+            self.calls = [dbv.verify_gumbel_tree(
+                x["logits"], x["parent"].to(dev), x["edge_pos"].to(dev), x["edge_tok"].to(dev),
+                masked=x["masked"].to(dev), gumbel=x["gumbel"], temperature=1.0,
+                num_states=x["num_states"].to(dev), prepare=True)]
+            self.shape = dict(B=B, S=S, L=L, V=V)
+            per_set = x["logits"].numel() * eb + x["gumbel"].numel() * 4
+        self.rotation = len(self.calls)
+        self.bytes_per_set = per_set
+
+    @staticmethod
+    def _rotation(per_set):
+        return int(max(1, min(256, math.ceil(ROTATE_BYTES / max(per_set, 1)))))
+
+    # ------------------------------------------------------------ oracle --
+    def cpu_baseline(self, seconds):
+        """The oracle as it stands on a bounded sample of this workload."""
+        import oracle
+        from tests.parity import np64, npi
+        x = self.cpu_inputs
+        done_pos = 0
+        calls = 0
+        t0 = time.perf_counter()
+        if self.name in ("c1", "c2", "c3"):
+            B = x["tgt"].shape[0]
+            nb = min(B, 4) if self.name == "c3" else B
+            tgt, drf = np64(x["tgt"][:nb]), np64(x["drf"][:nb])
+            d, n = npi(x["draft_tokens"][:nb]), npi(x["draft_len"][:nb])
+            ua, ur = np64(x["u_accept"][:nb]), np64(x["u_resample"][:nb])
+            T = x["temperature"]
+            t0 = time.perf_counter()
+            while True:
+                oracle.verify_lenient(tgt, drf, d, n, T, T, self.lam, ua, ur)
+                done_pos += int(n.sum())
+                calls += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            sample = f"{nb} of {B} sequences, {calls} oracle calls"
+        elif self.name == "c5":
+            K, W = x["K"], x["W"]
+            nb = 4
+            p = x["packed"][:nb]
+            tgt, dr = np64(p[:, :K + 1]), np64(p[:, K + 1:])
+            d, n = npi(x["draft_tokens"][:nb]), npi(x["draft_len"][:nb])
+            t0 = time.perf_counter()
+            while True:
+                oracle.verify_greedy(tgt, d, n, dr)
+                done_pos += int(n.sum())
+                calls += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            sample = f"{nb} of 64 sequences, {calls} oracle calls"
+        else:
+            b = 0
+            logits = np64(x["logits"][b:b + 1])
+            G = np64(x["gumbel"][b:b + 1])
+            m = x["masked"][b:b + 1].numpy()
+            ns = npi(x["num_states"][b:b + 1])
+            t0 = time.perf_counter()
+            while True:
+                oracle.verify_gumbel_tree(logits, m, npi(x["parent"][b:b + 1]), npi(x["edge_pos"][b:b + 1]),
+                                          npi(x["edge_tok"][b:b + 1]), ns, G, 1.0)
+                done_pos += int(ns[0]) - 1
+                calls += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            sample = f"1 of 16 trees, {calls} oracle calls"
+        dt = time.perf_counter() - t0
+        return {"value": done_pos / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+                "sample": f"{sample} in {dt:.1f} s (numpy float64, one thread; host has {os.cpu_count()} cpus)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    import draft_block_verification_amd as dbv
+    from draft_block_verification_amd import _lib
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    steps = args.steps if args.steps is not None else (20 if args.workload == "c4" else 200)
+    warmup = args.warmup if args.warmup is not None else (3 if args.workload == "c4" else 20)
+
+    case = Case(args.workload, dev)
+    R = case.rotation
+    for i in range(warmup):
+        case.calls[i % R]()
+    torch.cuda.synchronize()
+
+    # Whole-step timing (events on torch's current stream = the launch stream).
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        case.calls[i % R]()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+
+    # The row-streaming kernel alone: events recorded by the library around it.
+    lib = _lib.load()
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in kev:          # create the underlying HIP events (lazy in torch)
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        lib.verify_set_timing_events(kev[i][0]._as_parameter_, kev[i][1]._as_parameter_)
+        case.calls[i % R]()
+    lib.verify_set_timing_events(None, None)
+    torch.cuda.synchronize()
+    kms = sum(a.elapsed_time(b) for a, b in kev) / steps
+    achieved = case.kernel_bytes / (kms * 1e-3) / 1e9
+
+    out = case.calls[0].outputs
+    st = out["status"].cpu()
+    if int((st & dbv.SEQ_ERROR_MASK).sum()) != 0:
+        print(json.dumps({"error": "verification reported data errors", "status": st.tolist()}))
+        sys.exit(1)
+
+    line = {
+        "metric": METRIC,
+        "value": case.positions / (ms * 1e-3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if args.workload == "c1" else "bf16",
+        "data": "synthetic",
+        "config": dict(workload=DESCR[args.workload], **case.shape,
+                       positions_per_step=case.positions, rotation_sets=R,
+                       wall_s=round(wall, 4)),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": case.kernel,
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": None,
+            "bytes_per_launch": case.kernel_bytes,
+            "kernel_ms": kms,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = case.cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,273 @@
+"""Parallel verification of a drafted token block on AMD MI355X (gfx950).
+
+Thin PyTorch binding of libdbv (include/dbv.h): it checks tensor layouts,
+allocates outputs and scratch with torch on the tensors' device, and passes
+raw device pointers and the current HIP stream to the C ABI.  Every step of
+the verification runs in the library's HIP kernels; there is no fallback.
+
+Entry points (same names as the C ABI):
+  verify_greedy, verify_rejection, verify_lenient, verify_gumbel_tree
+"""
+
+import torch
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    DBV_BF16, DBV_F32, DBV_TREE_FIXED_POSITION, DBV_TREE_STATE_EQUALITY,
+    SEQ_BAD_INPUT, SEQ_EMPTY_ROW, SEQ_ERROR_MASK, SEQ_NONFINITE, SEQ_Q_ZERO,
+    SEQ_Z_ZERO,
+)
+
+__all__ = [
+    "verify_greedy", "verify_rejection", "verify_lenient", "verify_gumbel_tree",
+    "workspace_size", "DBVError", "Prepared",
+]
+
+
+class Prepared:
+    """A verify call whose arguments (pointers, sizes, stream) were marshalled
+    once: calling it enqueues the same verification again on the same
+    buffers, with no Python-side allocation.  ``outputs`` holds the result
+    tensors; ``keep`` keeps every buffer the pointers refer to alive."""
+
+    def __init__(self, fn, name, args, outputs, keep):
+        self._fn, self._name, self._args = fn, name, args
+        self.outputs, self._keep = outputs, keep
+
+    def __call__(self):
+        _check(self._fn(*self._args), self._name)
+        return self.outputs
+
+
+class DBVError(RuntimeError):
+    def __init__(self, code, where):
+        super().__init__(f"{where}: {_lib.status_string(code)} (status {code})")
+        self.code = code
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return DBV_BF16
+    if t.dtype == torch.float32:
+        return DBV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _rows3(t, name):
+    """A [B, R, V] view with unit vocabulary stride; returns its strides."""
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [B, rows, V]")
+    if t.stride(2) != 1 and t.size(2) > 1:
+        raise ValueError(f"{name} needs a contiguous vocabulary axis")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on a GPU")
+    return t.stride(0), t.stride(1)
+
+
+def _i32(t, shape, name, device):
+    if t is None:
+        return None
+    t = torch.as_tensor(t, dtype=torch.int32, device=device).contiguous()
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}")
+    return t
+
+
+def _f32(t, shape, name, device):
+    t = torch.as_tensor(t, dtype=torch.float32, device=device).contiguous()
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}")
+    return t
+
+
+def workspace_size(kind, B, K_or_S, L, V, dtype_code):
+    return int(_lib.load().verify_workspace_size(kind, B, K_or_S, L, V, dtype_code))
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(code, where):
+    if code != _lib.DBV_OK:
+        raise DBVError(code, where)
+
+
+def verify_greedy(tgt, draft_tokens, draft_len=None, draft_rows=None, eos_id=-1,
+                  len_budget=None, workspace=None, prepare=False):
+    """Greedy verification and next-draft retention (Packed-SS, Algorithm 1).
+
+    tgt [B, K+1, V] and draft_rows [B, W, V] (bf16 or fp32, views allowed),
+    draft_tokens [B, K], draft_len [B] or None, len_budget [B] or None.
+    Returns a dict of int32 tensors: accept_len, out_tokens, num_out,
+    next_draft, next_len, status.  With prepare=True a Prepared call is
+    returned instead of running it.
+    """
+    lib = _lib.load()
+    dev = tgt.device
+    B, K1, V = tgt.shape
+    K = K1 - 1
+    ts, tr = _rows3(tgt, "tgt")
+    dt = _dtype_code(tgt)
+    W = 0
+    ds = drs = 0
+    if draft_rows is not None:
+        if draft_rows.dtype != tgt.dtype or draft_rows.shape[0] != B or draft_rows.shape[2] != V:
+            raise ValueError("draft_rows must be [B, W, V] with the dtype of tgt")
+        ds, drs = _rows3(draft_rows, "draft_rows")
+        W = draft_rows.shape[1]
+    d = _i32(draft_tokens, (B, K), "draft_tokens", dev)
+    n = _i32(draft_len, (B,), "draft_len", dev)
+    bud = _i32(len_budget, (B,), "len_budget", dev)
+    out = {
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "out_tokens": torch.empty(B, K + 1, dtype=torch.int32, device=dev),
+        "num_out": torch.empty(B, dtype=torch.int32, device=dev),
+        "next_draft": torch.empty(B, W, dtype=torch.int32, device=dev),
+        "next_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "status": torch.empty(B, dtype=torch.int32, device=dev),
+    }
+    need = workspace_size(_lib.DBV_KIND_GREEDY, B, K, W, V, dt)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    args = (B, K, V, dt, tgt.data_ptr(), ts, tr, _ptr(d), _ptr(n),
+            _ptr(draft_rows), ds, drs, W, int(eos_id), _ptr(bud),
+            out["accept_len"].data_ptr(), out["out_tokens"].data_ptr(), out["num_out"].data_ptr(),
+            out["next_draft"].data_ptr() if W else None, out["next_len"].data_ptr(),
+            out["status"].data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+    call = Prepared(lib.verify_greedy, "verify_greedy", args, out, (tgt, draft_rows, d, n, bud, ws))
+    return call if prepare else call()
+
+
+def _sampling(fn_name, tgt, drf, draft_tokens, draft_len, temperature_target,
+              temperature_draft, lam, u_accept, u_resample, eos_id, len_budget,
+              workspace, diagnostics, prepare):
+    lib = _lib.load()
+    dev = tgt.device
+    B, K1, V = tgt.shape
+    K = K1 - 1
+    ts, tr = _rows3(tgt, "tgt")
+    dt = _dtype_code(tgt)
+    if drf.dtype != tgt.dtype or tuple(drf.shape) != (B, K, V):
+        raise ValueError("drf must be [B, K, V] with the dtype of tgt")
+    ds, dr = _rows3(drf, "drf")
+    d = _i32(draft_tokens, (B, K), "draft_tokens", dev)
+    n = _i32(draft_len, (B,), "draft_len", dev)
+    bud = _i32(len_budget, (B,), "len_budget", dev)
+    ua = _f32(u_accept, (B, K), "u_accept", dev)
+    ur = _f32(u_resample, (B, K + 1), "u_resample", dev)
+    out = {
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "out_tokens": torch.empty(B, K + 1, dtype=torch.int32, device=dev),
+        "num_out": torch.empty(B, dtype=torch.int32, device=dev),
+        "status": torch.empty(B, dtype=torch.int32, device=dev),
+    }
+    if diagnostics:
+        for k in ("p_draft", "q_draft", "alpha"):
+            out[k] = torch.empty(B, K, dtype=torch.float32, device=dev)
+        out["residual_mass"] = torch.empty(B, dtype=torch.float32, device=dev)
+    need = workspace_size(_lib.DBV_KIND_REJECTION, B, K, 0, V, dt)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    args = [B, K, V, dt, tgt.data_ptr(), ts, tr, drf.data_ptr(), ds, dr, _ptr(d), _ptr(n),
+            float(temperature_target), float(temperature_draft)]
+    if fn_name == "verify_lenient":
+        args.append(float(lam))
+    args += [ua.data_ptr() if K else None, ur.data_ptr(), int(eos_id), _ptr(bud),
+             out["accept_len"].data_ptr(), out["out_tokens"].data_ptr(), out["num_out"].data_ptr(),
+             _ptr(out.get("p_draft")), _ptr(out.get("q_draft")), _ptr(out.get("alpha")),
+             _ptr(out.get("residual_mass")), out["status"].data_ptr(),
+             ws.data_ptr(), ws.numel(), _stream(dev)]
+    call = Prepared(getattr(lib, fn_name), fn_name, tuple(args), out,
+                    (tgt, drf, d, n, bud, ua, ur, ws))
+    return call if prepare else call()
+
+
+def verify_rejection(tgt, drf, draft_tokens, u_accept, u_resample, draft_len=None,
+                     temperature_target=1.0, temperature_draft=1.0, eos_id=-1,
+                     len_budget=None, workspace=None, diagnostics=True, prepare=False):
+    """Lossless rejection-sampling verification (Packed-SS, Algorithm 2).
+
+    tgt [B, K+1, V], drf [B, K, V] (same dtype), draft_tokens [B, K],
+    u_accept [B, K], u_resample [B, K+1].  Returns accept_len, out_tokens,
+    num_out, status and (with diagnostics) p_draft, q_draft, alpha,
+    residual_mass.
+    """
+    return _sampling("verify_rejection", tgt, drf, draft_tokens, draft_len,
+                     temperature_target, temperature_draft, 0.0, u_accept, u_resample,
+                     eos_id, len_budget, workspace, diagnostics, prepare)
+
+
+def verify_lenient(tgt, drf, draft_tokens, u_accept, u_resample, lam, draft_len=None,
+                   temperature_target=1.0, temperature_draft=1.0, eos_id=-1,
+                   len_budget=None, workspace=None, diagnostics=True, prepare=False):
+    """Linear lenient verification, p~ = (1 - lam) p + lam q (Two Tradeoffs,
+    Theorem 1 and Algorithm 1).  Arguments as verify_rejection plus lam."""
+    return _sampling("verify_lenient", tgt, drf, draft_tokens, draft_len,
+                     temperature_target, temperature_draft, lam, u_accept, u_resample,
+                     eos_id, len_budget, workspace, diagnostics, prepare)
+
+
+def verify_gumbel_tree(logits, parent, edge_pos, edge_tok, masked=None, gumbel=None,
+                       temperature=1.0, num_states=None, next_pos=None,
+                       mode=DBV_TREE_STATE_EQUALITY, workspace=None, prepare=False):
+    """Shared-Gumbel state-equality verification of a draft tree (SPOT,
+    Sec. 4.3, App. A.1).
+
+    logits [B, S, L, V] (vocabulary contiguous), masked [B, S, L] bool/uint8,
+    parent / edge_pos / edge_tok [B, S], gumbel [B, L, V] float32 (None at
+    temperature 0), num_states [B] or None, next_pos [B, S] in the
+    fixed-position mode.  Returns sel_pos, sel_tok, sel_conf, path_len,
+    path_nodes, commit_pos, commit_tok, num_commits, status.
+    """
+    lib = _lib.load()
+    dev = logits.device
+    if logits.dim() != 4 or (logits.stride(3) != 1 and logits.size(3) > 1) or not logits.is_cuda:
+        raise ValueError("logits must be a GPU tensor [B, S, L, V] with a contiguous vocabulary axis")
+    B, S, L, V = logits.shape
+    dt = _dtype_code(logits)
+    par = _i32(parent, (B, S), "parent", dev)
+    ep = _i32(edge_pos, (B, S), "edge_pos", dev)
+    et = _i32(edge_tok, (B, S), "edge_tok", dev)
+    ns = _i32(num_states, (B,), "num_states", dev)
+    npos = _i32(next_pos, (B, S), "next_pos", dev)
+    m = None
+    if masked is not None:
+        m = torch.as_tensor(masked, device=dev).to(torch.uint8).contiguous()
+        if tuple(m.shape) != (B, S, L):
+            raise ValueError("masked must be [B, S, L]")
+    gs = gp = 0
+    if gumbel is not None:
+        if gumbel.dtype != torch.float32 or gumbel.dim() != 3 or gumbel.shape[0] != B \
+                or gumbel.shape[1] != L or gumbel.shape[2] != V or gumbel.stride(2) != 1:
+            raise ValueError("gumbel must be float32 [B, L, V] with a contiguous vocabulary axis")
+        gs, gp = gumbel.stride(0), gumbel.stride(1)
+    out = {
+        "sel_pos": torch.empty(B, S, dtype=torch.int32, device=dev),
+        "sel_tok": torch.empty(B, S, dtype=torch.int32, device=dev),
+        "sel_conf": torch.empty(B, S, dtype=torch.float32, device=dev),
+        "path_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "path_nodes": torch.empty(B, S, dtype=torch.int32, device=dev),
+        "commit_pos": torch.empty(B, S, dtype=torch.int32, device=dev),
+        "commit_tok": torch.empty(B, S, dtype=torch.int32, device=dev),
+        "num_commits": torch.empty(B, dtype=torch.int32, device=dev),
+        "status": torch.empty(B, dtype=torch.int32, device=dev),
+    }
+    need = workspace_size(_lib.DBV_KIND_TREE, B, S, L, V, dt)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    args = (B, S, L, V, dt, logits.data_ptr(), logits.stride(0), logits.stride(1), logits.stride(2),
+            _ptr(m), par.data_ptr(), ep.data_ptr(), et.data_ptr(), _ptr(ns), _ptr(npos),
+            _ptr(gumbel), gs, gp, float(temperature), int(mode),
+            out["sel_pos"].data_ptr(), out["sel_tok"].data_ptr(), out["sel_conf"].data_ptr(),
+            out["path_len"].data_ptr(), out["path_nodes"].data_ptr(), out["commit_pos"].data_ptr(),
+            out["commit_tok"].data_ptr(), out["num_commits"].data_ptr(), out["status"].data_ptr(),
+            ws.data_ptr(), ws.numel(), _stream(dev))
+    call = Prepared(lib.verify_gumbel_tree, "verify_gumbel_tree", args, out,
+                    (logits, m, par, ep, et, ns, npos, gumbel, ws))
+    return call if prepare else call()

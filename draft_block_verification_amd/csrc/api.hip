@@ -1,0 +1,268 @@
+// libdbv C ABI: argument validation, workspace layout and kernel enqueueing.
+// The operations are defined in include/dbv.h; this file only checks what the
+// host can check and hands the call to the kernels on the caller's stream.
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/dbv.h"
+#include "dbv_launch.h"
+#include "dbv_plan.h"
+
+namespace {
+
+using dbv::kMaxBlockLen;
+using dbv::kMaxDraft;
+using dbv::kMaxStates;
+
+constexpr int kMaxDevices = 64;
+// Diagnostics events (verify_set_timing_events); off when NULL.
+std::atomic<void*> g_ev_begin{nullptr};
+std::atomic<void*> g_ev_end{nullptr};
+
+dbv::TimingEvents timing_events() {
+  dbv::TimingEvents ev;
+  void* b = g_ev_begin.load(std::memory_order_acquire);
+  void* e = g_ev_end.load(std::memory_order_acquire);
+  if (b && e) {
+    ev.begin = static_cast<hipEvent_t>(b);
+    ev.end = static_cast<hipEvent_t>(e);
+  }
+  return ev;
+}
+
+// 0 = not yet queried, 1 = gfx950, 2 = some other device.
+std::atomic<int> g_arch[kMaxDevices];
+
+// A usable gfx950 device must be current.
+dbv_status device_ready() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return DBV_ERR_NO_DEVICE;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DBV_ERR_NO_DEVICE;
+  if (dev < kMaxDevices) {
+    int s = g_arch[dev].load(std::memory_order_relaxed);
+    if (s == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DBV_ERR_NO_DEVICE;
+      s = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+      g_arch[dev].store(s, std::memory_order_relaxed);
+    }
+    if (s != 1) return DBV_ERR_NO_DEVICE;
+  }
+  return DBV_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_bytes(dbv_dtype dt) { return dt == DBV_BF16 ? 2 : 4; }
+
+bool dtype_ok(dbv_dtype dt) { return dt == DBV_F32 || dt == DBV_BF16; }
+
+dbv_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return DBV_OK;
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return DBV_ERR_WORKSPACE;
+  return DBV_OK;
+}
+
+bool temp_ok(float t) { return std::isfinite(t) && t > 0.f; }
+
+dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t ts, int64_t tr,
+                         const void* drf, int64_t ds, int64_t dr, const int32_t* draft_tokens,
+                         const int32_t* draft_len, float tt, float td, float lam, const float* u_accept,
+                         const float* u_resample, int32_t eos_id, const int32_t* len_budget,
+                         int32_t* accept_len, int32_t* out_tokens, int32_t* num_out, float* p_draft,
+                         float* q_draft, float* alpha, float* residual_mass, int32_t* status, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (B < 0 || K < 0 || K > kMaxDraft || V < 1 || !dtype_ok(dtype)) return DBV_ERR_INVALID_ARG;
+  if (!temp_ok(tt) || !temp_ok(td) || !(lam >= 0.f && lam <= 1.f)) return DBV_ERR_INVALID_ARG;
+  if (ts < 0 || tr < 0 || ds < 0 || dr < 0) return DBV_ERR_INVALID_ARG;
+  if (tgt == nullptr || u_resample == nullptr) return DBV_ERR_INVALID_ARG;
+  if (K > 0 && (drf == nullptr || draft_tokens == nullptr || u_accept == nullptr)) return DBV_ERR_INVALID_ARG;
+  if (accept_len == nullptr || out_tokens == nullptr || num_out == nullptr) return DBV_ERR_INVALID_ARG;
+  const size_t eb = elem_bytes(dtype);
+  if (!aligned(tgt, eb) || (drf && !aligned(drf, eb))) return DBV_ERR_INVALID_ARG;
+  const dbv::SamplePlan plan = dbv::plan_sample(B, K, V);
+  dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
+  if (s != DBV_OK) return s;
+  if ((s = device_ready()) != DBV_OK) return s;
+  if (B == 0) return DBV_OK;
+
+  dbv::SampleArgs a{};
+  a.B = B; a.K = K; a.V = V;
+  a.tgt = tgt; a.ts = ts; a.tr = tr;
+  a.drf = drf; a.ds = ds; a.dr = dr;
+  a.draft_tokens = draft_tokens; a.draft_len = draft_len;
+  a.kp = dbv::kLog2eHost / tt; a.kq = dbv::kLog2eHost / td;
+  a.lam = lam;
+  a.u_accept = u_accept; a.u_resample = u_resample;
+  a.eos = eos_id; a.budget = len_budget;
+  a.accept_len = accept_len; a.out_tokens = out_tokens; a.num_out = num_out;
+  a.p_draft = p_draft; a.q_draft = q_draft; a.alpha = alpha; a.residual_mass = residual_mass;
+  a.status = status;
+  char* w = static_cast<char*>(ws);
+  a.stats = reinterpret_cast<float2*>(w + plan.off_stats);
+  a.rec = reinterpret_cast<dbv::DrawRecord*>(w + plan.off_rec);
+  a.dsum = reinterpret_cast<float*>(w + plan.off_dsum);
+  a.split = plan.split; a.chunk = plan.chunk;
+  a.draw_chunks = plan.draw_chunks; a.draw_chunk = plan.draw_chunk;
+  return dbv::launch_sample(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+dbv_status verify_greedy(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
+                         int64_t tgt_row_stride, const int32_t* draft_tokens, const int32_t* draft_len,
+                         const void* draft_rows, int64_t dr_seq_stride, int64_t dr_row_stride, int W,
+                         int32_t eos_id, const int32_t* len_budget, int32_t* accept_len, int32_t* out_tokens,
+                         int32_t* num_out, int32_t* next_draft, int32_t* next_len, int32_t* status, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (B < 0 || K < 0 || K > kMaxDraft || W < 0 || W > kMaxDraft || V < 1 || !dtype_ok(dtype))
+    return DBV_ERR_INVALID_ARG;
+  if (tgt_seq_stride < 0 || tgt_row_stride < 0 || dr_seq_stride < 0 || dr_row_stride < 0)
+    return DBV_ERR_INVALID_ARG;
+  if (tgt == nullptr || (K > 0 && draft_tokens == nullptr) || (W > 0 && draft_rows == nullptr))
+    return DBV_ERR_INVALID_ARG;
+  if (accept_len == nullptr || out_tokens == nullptr || num_out == nullptr) return DBV_ERR_INVALID_ARG;
+  const size_t eb = elem_bytes(dtype);
+  if (!aligned(tgt, eb) || (draft_rows && !aligned(draft_rows, eb))) return DBV_ERR_INVALID_ARG;
+  const dbv::GreedyPlan plan = dbv::plan_greedy(B, K, W, V);
+  dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
+  if (s != DBV_OK) return s;
+  if ((s = device_ready()) != DBV_OK) return s;
+  if (B == 0) return DBV_OK;
+
+  dbv::GreedyArgs a{};
+  a.B = B; a.K = K; a.V = V; a.W = W;
+  a.tgt = tgt; a.ts = tgt_seq_stride; a.tr = tgt_row_stride;
+  a.dr = draft_rows; a.ds = dr_seq_stride; a.drr = dr_row_stride;
+  a.draft_tokens = draft_tokens; a.draft_len = draft_len;
+  a.eos = eos_id; a.budget = len_budget;
+  a.accept_len = accept_len; a.out_tokens = out_tokens; a.num_out = num_out;
+  a.next_draft = next_draft; a.next_len = next_len; a.status = status;
+  a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + plan.off_part);
+  a.split = plan.split; a.chunk = plan.chunk;
+  return dbv::launch_greedy(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
+}
+
+dbv_status verify_rejection(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
+                            int64_t tgt_row_stride, const void* drf, int64_t drf_seq_stride,
+                            int64_t drf_row_stride, const int32_t* draft_tokens, const int32_t* draft_len,
+                            float temperature_target, float temperature_draft, const float* u_accept,
+                            const float* u_resample, int32_t eos_id, const int32_t* len_budget,
+                            int32_t* accept_len, int32_t* out_tokens, int32_t* num_out, float* p_draft,
+                            float* q_draft, float* alpha, float* residual_mass, int32_t* status, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
+                       drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft, 0.f,
+                       u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft,
+                       q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
+}
+
+dbv_status verify_lenient(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
+                          int64_t tgt_row_stride, const void* drf, int64_t drf_seq_stride, int64_t drf_row_stride,
+                          const int32_t* draft_tokens, const int32_t* draft_len, float temperature_target,
+                          float temperature_draft, float lambda, const float* u_accept, const float* u_resample,
+                          int32_t eos_id, const int32_t* len_budget, int32_t* accept_len, int32_t* out_tokens,
+                          int32_t* num_out, float* p_draft, float* q_draft, float* alpha, float* residual_mass,
+                          int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
+                       drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft, lambda,
+                       u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft,
+                       q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
+}
+
+dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const void* logits, int64_t seq_stride,
+                              int64_t state_stride, int64_t pos_stride, const uint8_t* masked,
+                              const int32_t* parent, const int32_t* edge_pos, const int32_t* edge_tok,
+                              const int32_t* num_states, const int32_t* next_pos, const float* gumbel,
+                              int64_t g_seq_stride, int64_t g_pos_stride, float temperature, dbv_tree_mode mode,
+                              int32_t* sel_pos, int32_t* sel_tok, float* sel_conf, int32_t* path_len,
+                              int32_t* path_nodes, int32_t* commit_pos, int32_t* commit_tok,
+                              int32_t* num_commits, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || S < 1 || S > kMaxStates || L < 1 || L > kMaxBlockLen || V < 1 || !dtype_ok(dtype))
+    return DBV_ERR_INVALID_ARG;
+  if (mode != DBV_TREE_STATE_EQUALITY && mode != DBV_TREE_FIXED_POSITION) return DBV_ERR_INVALID_ARG;
+  if (!(std::isfinite(temperature) && temperature >= 0.f)) return DBV_ERR_INVALID_ARG;
+  if (seq_stride < 0 || state_stride < 0 || pos_stride < 0 || g_seq_stride < 0 || g_pos_stride < 0)
+    return DBV_ERR_INVALID_ARG;
+  if (logits == nullptr || parent == nullptr || edge_pos == nullptr || edge_tok == nullptr)
+    return DBV_ERR_INVALID_ARG;
+  if (mode == DBV_TREE_STATE_EQUALITY && masked == nullptr) return DBV_ERR_INVALID_ARG;
+  if (mode == DBV_TREE_FIXED_POSITION && next_pos == nullptr) return DBV_ERR_INVALID_ARG;
+  if (temperature > 0.f && gumbel == nullptr) return DBV_ERR_INVALID_ARG;
+  if (path_len == nullptr || path_nodes == nullptr || commit_pos == nullptr || commit_tok == nullptr ||
+      num_commits == nullptr)
+    return DBV_ERR_INVALID_ARG;
+  if (!aligned(logits, elem_bytes(dtype)) || (gumbel && !aligned(gumbel, 4))) return DBV_ERR_INVALID_ARG;
+  const dbv::TreePlan plan = dbv::plan_tree(B, S, L, V);
+  dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
+  if (s != DBV_OK) return s;
+  if ((s = device_ready()) != DBV_OK) return s;
+  if (B == 0) return DBV_OK;
+
+  dbv::TreeArgs a{};
+  a.B = B; a.S = S; a.L = L; a.V = V;
+  a.logits = logits; a.ss = seq_stride; a.sy = state_stride; a.sp = pos_stride;
+  a.masked = masked; a.parent = parent; a.edge_pos = edge_pos; a.edge_tok = edge_tok;
+  a.num_states = num_states; a.next_pos = mode == DBV_TREE_FIXED_POSITION ? next_pos : nullptr;
+  a.gumbel = gumbel; a.gs = g_seq_stride; a.gp = g_pos_stride;
+  a.inv_t = temperature > 0.f ? 1.f / temperature : 0.f;
+  a.fixed = mode == DBV_TREE_FIXED_POSITION ? 1 : 0;
+  a.sel_pos = sel_pos; a.sel_tok = sel_tok; a.sel_conf = sel_conf;
+  a.path_len = path_len; a.path_nodes = path_nodes;
+  a.commit_pos = commit_pos; a.commit_tok = commit_tok; a.num_commits = num_commits;
+  a.status = status;
+  char* w = static_cast<char*>(ws);
+  a.conf = reinterpret_cast<float2*>(w + plan.off_conf);
+  a.pick = reinterpret_cast<float2*>(w + plan.off_pick);
+  a.sel = reinterpret_cast<int32_t*>(w + plan.off_sel);
+  a.split1 = plan.split1; a.chunk1 = plan.chunk1;
+  a.split2 = plan.split2; a.chunk2 = plan.chunk2;
+  return dbv::launch_tree(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
+}
+
+size_t verify_workspace_size(dbv_kind kind, int B, int K_or_S, int L, int V, dbv_dtype dtype) {
+  if (B < 0 || V < 1 || !dtype_ok(dtype)) return 0;
+  switch (kind) {
+    case DBV_KIND_GREEDY:
+      if (K_or_S < 0 || K_or_S > kMaxDraft || L < 0 || L > kMaxDraft) return 0;
+      return dbv::plan_greedy(B, K_or_S, L, V).bytes;
+    case DBV_KIND_REJECTION:
+      if (K_or_S < 0 || K_or_S > kMaxDraft) return 0;
+      return dbv::plan_sample(B, K_or_S, V).bytes;
+    case DBV_KIND_TREE:
+      if (K_or_S < 1 || K_or_S > kMaxStates || L < 1 || L > kMaxBlockLen) return 0;
+      return dbv::plan_tree(B, K_or_S, L, V).bytes;
+  }
+  return 0;
+}
+
+const char* verify_status_string(dbv_status s) {
+  switch (s) {
+    case DBV_OK: return "ok";
+    case DBV_ERR_INVALID_ARG: return "invalid argument";
+    case DBV_ERR_UNSUPPORTED: return "unsupported (device or request)";
+    case DBV_ERR_NO_DEVICE: return "no usable GPU device";
+    case DBV_ERR_LAUNCH: return "kernel launch failed";
+    case DBV_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+  }
+  return "unknown status";
+}
+
+int verify_abi_version(void) { return DBV_ABI_VERSION; }
+
+void verify_set_timing_events(void* begin, void* end) {
+  g_ev_begin.store(begin, std::memory_order_release);
+  g_ev_end.store(end, std::memory_order_release);
+}
+
+}  // extern "C"

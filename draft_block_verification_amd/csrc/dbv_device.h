@@ -1,0 +1,279 @@
+// Device-side building blocks shared by the verification kernels (gfx950).
+//
+// A logit row is streamed once from HBM with 16-byte nontemporal loads
+// (8 bf16 or 4 fp32 per lane per load, a wave covering 1 KiB contiguous),
+// U loads in flight per lane.  Two per-lane reducers consume the stream:
+//   * SoftmaxStats: online (max, sum of exp2) in fp32 -- the row's softmax
+//     normaliser at temperature T, with exp folded into exp2 by k = log2(e)/T;
+//   * ArgmaxPick:   exact (value, lowest index) argmax of a per-element score.
+// Lane results are combined by wave shuffles and an LDS cross-wave step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dbv {
+
+constexpr int kBlock = 256;            // threads per workgroup: 4 wave64
+constexpr int kWaves = kBlock / 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kInf = __builtin_inff();
+
+enum : int { DT_F32 = 0, DT_BF16 = 1 };
+
+// Per-sequence status bits (same values as the public header).
+enum : int {
+  SEQ_BAD_INPUT = 1, SEQ_NONFINITE = 2, SEQ_EMPTY_ROW = 4,
+  SEQ_Q_ZERO = 8, SEQ_Z_ZERO = 16, SEQ_ERROR_MASK = 7
+};
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// NaN-propagating max (v_maximum3_f32 on gfx950): a NaN anywhere in a row
+// survives into its maximum, which is how rows with NaN are detected.
+__device__ __forceinline__ float fmaxp(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int DT> struct Elem;
+
+template <> struct Elem<DT_BF16> {
+  static constexpr int kVec = 8;
+  static constexpr int kBytes = 2;
+  __device__ static __forceinline__ float load1(const void* row, int64_t i) {
+    const uint16_t h = static_cast<const uint16_t*>(row)[i];
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+  }
+  __device__ static __forceinline__ void unpack(u32x4 w, float (&x)[kVec]) {
+    x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = __uint_as_float(w.y << 16); x[3] = __uint_as_float(w.y & 0xffff0000u);
+    x[4] = __uint_as_float(w.z << 16); x[5] = __uint_as_float(w.z & 0xffff0000u);
+    x[6] = __uint_as_float(w.w << 16); x[7] = __uint_as_float(w.w & 0xffff0000u);
+  }
+};
+
+template <> struct Elem<DT_F32> {
+  static constexpr int kVec = 4;
+  static constexpr int kBytes = 4;
+  __device__ static __forceinline__ float load1(const void* row, int64_t i) {
+    return static_cast<const float*>(row)[i];
+  }
+  __device__ static __forceinline__ void unpack(u32x4 w, float (&x)[kVec]) {
+    x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+  }
+};
+
+__device__ __forceinline__ u32x4 load16(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// ---------------------------------------------------------------------------
+// Row streaming.  Visits elements [v0, v1) of `row`; every thread sees its own
+// elements in increasing index order.  The op receives groups:
+//   op.template group<N>(x, idx0)  -- N contiguous values starting at idx0
+// Groups are the scalar head (to 16-byte alignment), U vectors at a time in
+// the body, and the scalar tail.
+// ---------------------------------------------------------------------------
+template <int DT, int U, class Op>
+__device__ __forceinline__ void stream_row(const void* row, int64_t v0, int64_t v1, Op& op) {
+  using E = Elem<DT>;
+  constexpr int W = E::kVec;
+  if (v1 <= v0) return;
+  const char* base = static_cast<const char*>(row);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(base + v0 * E::kBytes);
+  int64_t head = static_cast<int64_t>(((16u - (a & 15u)) & 15u) / E::kBytes);
+  if (head > v1 - v0) head = v1 - v0;
+  const int64_t a0 = v0 + head;
+  const int64_t nvec = (v1 - a0) / W;
+  const int64_t a1 = a0 + nvec * W;
+  const int t = threadIdx.x;
+
+  if (t < head) {
+    float x[1] = {E::load1(row, v0 + t)};
+    op.template group<1>(x, v0 + t);
+  }
+  const char* vb = base + a0 * E::kBytes;
+  int64_t i = t;
+  for (; i + (U - 1) * kBlock < nvec; i += U * kBlock) {
+    u32x4 r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[u] = load16(vb + (i + u * kBlock) * 16);
+    float x[U * W];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float y[W];
+      E::unpack(r[u], y);
+#pragma unroll
+      for (int j = 0; j < W; ++j) x[u * W + j] = y[j];
+    }
+    op.template block<U, W>(x, a0 + i * W, static_cast<int64_t>(kBlock) * W);
+  }
+  for (; i < nvec; i += kBlock) {
+    float y[W];
+    E::unpack(load16(vb + i * 16), y);
+    op.template group<W>(y, a0 + i * W);
+  }
+  if (a1 + t < v1) {
+    float x[1] = {E::load1(row, a1 + t)};
+    op.template group<1>(x, a1 + t);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Online softmax statistics: M = max x, S = sum exp2((x - M) k).
+// ---------------------------------------------------------------------------
+struct SoftmaxStats {
+  float M = -kInf;
+  float S = 0.f;
+  float k;  // log2(e) / T
+  __device__ explicit SoftmaxStats(float k_) : k(k_) {}
+
+  template <int N>
+  __device__ __forceinline__ void absorb(const float* x) {
+    float cm = x[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j) cm = fmaxp(cm, x[j]);
+    const float Mn = fmaxp(M, cm);
+    if (Mn == -kInf) return;                 // nothing but -inf so far
+    // Exactly 1 when the maximum did not move; 0 when M was -inf.
+    const float scale = fast_exp2((M - Mn) * k);
+    const float c = -Mn * k;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) s += fast_exp2(__builtin_fmaf(x[j], k, c));
+    S = S * scale + s;
+    M = Mn;
+  }
+  template <int N>
+  __device__ __forceinline__ void group(const float* x, int64_t) { absorb<N>(x); }
+  template <int U, int W>
+  __device__ __forceinline__ void block(const float* x, int64_t, int64_t) { absorb<U * W>(x); }
+};
+
+// Merge two (M, S) pairs; -inf / NaN maxima propagate.
+__device__ __forceinline__ void stats_merge(float& M, float& S, float M2, float S2, float k) {
+  const float Mn = fmaxp(M, M2);
+  if (Mn == -kInf) { M = Mn; S = 0.f; return; }
+  const float s1 = (M == -kInf) ? 0.f : S * fast_exp2((M - Mn) * k);
+  const float s2 = (M2 == -kInf) ? 0.f : S2 * fast_exp2((M2 - Mn) * k);
+  M = Mn;
+  S = s1 + s2;
+}
+
+// ---------------------------------------------------------------------------
+// Lowest-index argmax of a score.  Per lane: the group holding the lane's
+// first occurrence of its maximum is remembered; its exact index is resolved
+// afterwards by re-evaluating the score of at most kVec elements.
+// ---------------------------------------------------------------------------
+struct ArgmaxPick {
+  float best = -kInf;
+  int64_t gidx = -1;
+  bool nan = false;
+
+  template <int N>
+  __device__ __forceinline__ void group(const float* x, int64_t idx0) {
+    float m = x[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j) m = fmaxp(m, x[j]);
+    nan |= (m != m);
+    if (m > best || (gidx < 0 && m == best)) { best = m; gidx = idx0; }
+  }
+  template <int U, int W>
+  __device__ __forceinline__ void block(const float* x, int64_t idx0, int64_t ustride) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) group<W>(x + u * W, idx0 + u * ustride);
+  }
+};
+
+// Exact index of `best` inside the remembered group: the first element at or
+// after gidx (within kVec, below v1) whose score equals best.
+template <int DT, class ScoreFn>
+__device__ __forceinline__ int64_t resolve_argmax(const ArgmaxPick& a, int64_t v1, ScoreFn score) {
+  if (a.gidx < 0) return -1;
+  for (int j = 0; j < Elem<DT>::kVec && a.gidx + j < v1; ++j)
+    if (score(a.gidx + j) == a.best) return a.gidx + j;
+  return a.gidx;  // unreachable: the group's maximum is one of its elements
+}
+
+// ------------------------------------------------------------ reductions ---
+
+__device__ __forceinline__ float wave_shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ int wave_shfl_xor(int v, int m) { return __shfl_xor(v, m, 64); }
+
+// Is (v2, i2) a better (larger value, then lower index) pick than (v1, i1)?
+// Index -1 means "no pick".  NaN never wins here; it is tracked separately.
+__device__ __forceinline__ bool pick_better(float v2, int i2, float v1, int i1) {
+  if (i2 < 0) return false;
+  if (i1 < 0) return true;
+  return v2 > v1 || (v2 == v1 && i2 < i1);
+}
+
+// Workgroup argmax reduction; results valid in thread 0.
+__device__ __forceinline__ void block_argmax(float& v, int& idx, int& nan, float* s_v, int* s_i, int* s_n) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float v2 = wave_shfl_xor(v, m);
+    const int i2 = wave_shfl_xor(idx, m);
+    const int n2 = wave_shfl_xor(nan, m);
+    if (pick_better(v2, i2, v, idx)) { v = v2; idx = i2; }
+    nan |= n2;
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { s_v[w] = v; s_i[w] = idx; s_n[w] = nan; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < kWaves; ++k) {
+      if (pick_better(s_v[k], s_i[k], v, idx)) { v = s_v[k]; idx = s_i[k]; }
+      nan |= s_n[k];
+    }
+  }
+}
+
+// Workgroup (M, S) reduction; results valid in thread 0.
+__device__ __forceinline__ void block_stats(float& M, float& S, float k, float* s_m, float* s_s) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float M2 = wave_shfl_xor(M, m);
+    const float S2 = wave_shfl_xor(S, m);
+    stats_merge(M, S, M2, S2, k);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { s_m[w] = M; s_s[w] = S; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int j = 1; j < kWaves; ++j) stats_merge(M, S, s_m[j], s_s[j], k);
+  }
+}
+
+// Workgroup float sum (fixed order); result valid in thread 0.
+__device__ __forceinline__ float block_sum(float v, float* s) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += wave_shfl_xor(v, m);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) s[w] = v;
+  __syncthreads();
+  float r = 0.f;
+  if (threadIdx.x == 0) {
+    for (int j = 0; j < kWaves; ++j) r += s[j];
+  }
+  return r;
+}
+
+// Row status from a reduced maximum: NaN / +inf -> nonfinite, -inf -> empty.
+__device__ __forceinline__ int max_status(float M) {
+  if (M != M || M == kInf) return SEQ_NONFINITE;
+  if (M == -kInf) return SEQ_EMPTY_ROW;
+  return 0;
+}
+
+// Status of a softmax row from its combined statistics (M, S).
+__device__ __forceinline__ int stats_status(float M, float S) {
+  int st = max_status(M);
+  if (!st && !(S > 0.f && S < kInf)) st = SEQ_NONFINITE;
+  return st;
+}
+
+}  // namespace dbv

@@ -1,0 +1,79 @@
+// Kernel argument blocks and launchers (internal to libdbv).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dbv_plan.h"
+
+namespace dbv {
+
+struct GreedyArgs {
+  int B, K, V, W;
+  const void* tgt; int64_t ts, tr;     // target rows: element strides
+  const void* dr; int64_t ds, drr;     // drafter rows
+  const int32_t* draft_tokens;
+  const int32_t* draft_len;
+  int32_t eos;
+  const int32_t* budget;
+  int32_t* accept_len; int32_t* out_tokens; int32_t* num_out;
+  int32_t* next_draft; int32_t* next_len; int32_t* status;
+  float2* part;
+  int split;
+  int64_t chunk;
+};
+
+struct SampleArgs {
+  int B, K, V;
+  const void* tgt; int64_t ts, tr;
+  const void* drf; int64_t ds, dr;
+  const int32_t* draft_tokens;
+  const int32_t* draft_len;
+  float kp, kq;                        // log2(e) / temperature
+  float lam;                           // 0 = lossless
+  const float* u_accept; const float* u_resample;
+  int32_t eos;
+  const int32_t* budget;
+  int32_t* accept_len; int32_t* out_tokens; int32_t* num_out;
+  float* p_draft; float* q_draft; float* alpha; float* residual_mass;
+  int32_t* status;
+  float2* stats;
+  DrawRecord* rec;
+  float* dsum;
+  int split;
+  int64_t chunk;
+  int draw_chunks;
+  int64_t draw_chunk;
+};
+
+struct TreeArgs {
+  int B, S, L, V;
+  const void* logits; int64_t ss, sy, sp;   // sequence, state, position strides
+  const uint8_t* masked;
+  const int32_t* parent; const int32_t* edge_pos; const int32_t* edge_tok;
+  const int32_t* num_states; const int32_t* next_pos;
+  const float* gumbel; int64_t gs, gp;
+  float inv_t;                               // 1/T, 0 for T = 0 (greedy)
+  int fixed;                                 // 1 = fixed-position mode
+  int32_t* sel_pos; int32_t* sel_tok; float* sel_conf;
+  int32_t* path_len; int32_t* path_nodes;
+  int32_t* commit_pos; int32_t* commit_tok; int32_t* num_commits;
+  int32_t* status;
+  float2* conf;
+  float2* pick;
+  int32_t* sel;
+  int split1; int64_t chunk1;
+  int split2; int64_t chunk2;
+};
+
+// Optional events recorded around the row-streaming kernel of a call.
+struct TimingEvents {
+  hipEvent_t begin = nullptr;
+  hipEvent_t end = nullptr;
+};
+
+bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
+bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
+bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
+
+}  // namespace dbv

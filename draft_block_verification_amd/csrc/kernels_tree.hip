@@ -1,0 +1,327 @@
+// Draft-tree verification by shared-Gumbel state equality (SPOT, Sec. 4.1,
+// Sec. 4.3 and App. A.1).
+//
+//   k_tree_conf    split-V softmax statistics (M, S) of every masked row of
+//                  every state; the position's confidence is 1/S (max_v p).
+//                  In the fixed-position mode only the given position's row.
+//   k_tree_gumbel  per (state, V-chunk): s*(y) from the confidences (lowest
+//                  position on ties), then the argmax over v of
+//                  z_v / T + G[s*, v] (z_v at T = 0) -- Phi(y)'s token.
+//   k_tree_walk    per sequence: validate the tree, gather Phi(y) for every
+//                  state, walk from the root along the child equal to Phi(y),
+//                  commit Phi of the last accepted state.
+#include "dbv_device.h"
+#include "dbv_launch.h"
+
+#include <climits>
+
+namespace dbv {
+
+__device__ __forceinline__ int state_count(const int32_t* num_states, int b, int S) {
+  const int ns = num_states ? num_states[b] : S;
+  return (ns < 1 || ns > S) ? -1 : ns;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_tree_conf(TreeArgs a) {
+  __shared__ float s_m[kWaves], s_s[kWaves];
+  const int64_t gid = blockIdx.x;
+  const int64_t row = gid / a.split1;
+  const int sp = static_cast<int>(gid % a.split1);
+  const int b = static_cast<int>(row / (static_cast<int64_t>(a.S) * a.L));
+  const int y = static_cast<int>((row / a.L) % a.S);
+  const int s = static_cast<int>(row % a.L);
+  const int ns = state_count(a.num_states, b, a.S);
+  if (ns < 0 || y >= ns) return;
+  const int64_t sy = static_cast<int64_t>(b) * a.S + y;
+  if (a.fixed) {
+    if (a.next_pos[sy] != s) return;
+  } else if (!a.masked[sy * a.L + s]) {
+    return;
+  }
+  const char* rowp = static_cast<const char*>(a.logits) +
+                     (b * a.ss + y * a.sy + s * a.sp) * Elem<DT>::kBytes;
+  const int64_t v0 = static_cast<int64_t>(sp) * a.chunk1;
+  const int64_t v1 = v0 + a.chunk1 < a.V ? v0 + a.chunk1 : a.V;
+  SoftmaxStats st(kLog2e);
+  stream_row<DT, 4>(rowp, v0, v1, st);
+  float M = st.M, S = st.S;
+  block_stats(M, S, kLog2e, s_m, s_s);
+  if (threadIdx.x == 0) a.conf[gid] = make_float2(M, S);
+}
+
+__device__ __forceinline__ void combine_conf(const TreeArgs& a, int64_t row, float& M, float& S) {
+  M = -kInf;
+  S = 0.f;
+  const float2* p = a.conf + row * a.split1;
+  for (int k = 0; k < a.split1; ++k) stats_merge(M, S, p[k].x, p[k].y, kLog2e);
+}
+
+// s*(y): the masked position of largest confidence 1/S (lowest on ties), or
+// the given position in the fixed mode; -1 when there is none.
+__device__ int select_position(const TreeArgs& a, int b, int y) {
+  const int64_t sy = static_cast<int64_t>(b) * a.S + y;
+  if (a.fixed) {
+    const int np = a.next_pos[sy];
+    return (np >= 0 && np < a.L) ? np : -1;
+  }
+  int best = -1;
+  float bestS = kInf;
+  for (int s = 0; s < a.L; ++s) {
+    if (!a.masked[sy * a.L + s]) continue;
+    float M, S;
+    combine_conf(a, sy * a.L + s, M, S);
+    if (best < 0 || S < bestS) { best = s; bestS = S; }
+  }
+  return best;
+}
+
+// Argmax of z/T + g over a logit row and its Gumbel row read together.
+template <int DT>
+__device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64_t v1, float inv_t,
+                              ArgmaxPick& pk) {
+  using E = Elem<DT>;
+  constexpr int W = E::kVec;
+  const int t = threadIdx.x;
+  const uintptr_t ax = reinterpret_cast<uintptr_t>(xr + v0 * E::kBytes);
+  int64_t head = static_cast<int64_t>(((16u - (ax & 15u)) & 15u) / E::kBytes);
+  if (head > v1 - v0) head = v1 - v0;
+  const int64_t a0 = v0 + head;
+  const bool gal = ((reinterpret_cast<uintptr_t>(gr + a0)) & 15u) == 0;
+  if (!gal) {  // Gumbel row not aligned with the logits: scalar path
+    for (int64_t j = v0 + t; j < v1; j += kBlock) {
+      float x[1] = {__builtin_fmaf(E::load1(xr, j), inv_t, gr[j])};
+      pk.group<1>(x, j);
+    }
+    return;
+  }
+  const int64_t nvec = (v1 - a0) / W;
+  const int64_t a1 = a0 + nvec * W;
+  if (t < head) {
+    float x[1] = {__builtin_fmaf(E::load1(xr, v0 + t), inv_t, gr[v0 + t])};
+    pk.group<1>(x, v0 + t);
+  }
+  const char* xb = xr + a0 * E::kBytes;
+  const char* gb = reinterpret_cast<const char*>(gr + a0);
+  constexpr int GV = W / 4;  // 16-byte Gumbel loads per logit vector
+  int64_t i = t;
+  for (; i + kBlock < nvec; i += 2 * kBlock) {
+    u32x4 xr0 = load16(xb + i * 16), xr1 = load16(xb + (i + kBlock) * 16);
+    u32x4 g0[GV], g1[GV];
+#pragma unroll
+    for (int q = 0; q < GV; ++q) {
+      g0[q] = load16(gb + (i * W + q * 4) * 4);
+      g1[q] = load16(gb + ((i + kBlock) * W + q * 4) * 4);
+    }
+    float x0[W], x1[W];
+    E::unpack(xr0, x0);
+    E::unpack(xr1, x1);
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      x0[j] = __builtin_fmaf(x0[j], inv_t, __uint_as_float(g0[j / 4][j % 4]));
+      x1[j] = __builtin_fmaf(x1[j], inv_t, __uint_as_float(g1[j / 4][j % 4]));
+    }
+    pk.group<W>(x0, a0 + i * W);
+    pk.group<W>(x1, a0 + (i + kBlock) * W);
+  }
+  for (; i < nvec; i += kBlock) {
+    u32x4 xv = load16(xb + i * 16);
+    u32x4 g[GV];
+#pragma unroll
+    for (int q = 0; q < GV; ++q) g[q] = load16(gb + (i * W + q * 4) * 4);
+    float x[W];
+    E::unpack(xv, x);
+#pragma unroll
+    for (int j = 0; j < W; ++j) x[j] = __builtin_fmaf(x[j], inv_t, __uint_as_float(g[j / 4][j % 4]));
+    pk.group<W>(x, a0 + i * W);
+  }
+  if (a1 + t < v1) {
+    float x[1] = {__builtin_fmaf(E::load1(xr, a1 + t), inv_t, gr[a1 + t])};
+    pk.group<1>(x, a1 + t);
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
+  __shared__ float s_v[kWaves];
+  __shared__ int s_i[kWaves], s_n[kWaves];
+  const int64_t gid = blockIdx.x;
+  const int64_t sy = gid / a.split2;
+  const int sp = static_cast<int>(gid % a.split2);
+  const int b = static_cast<int>(sy / a.S);
+  const int y = static_cast<int>(sy % a.S);
+  const int ns = state_count(a.num_states, b, a.S);
+  if (ns < 0 || y >= ns) return;
+  const int s = select_position(a, b, y);
+  if (sp == 0 && threadIdx.x == 0) a.sel[sy] = s;
+  if (s < 0) return;
+  const char* xr = static_cast<const char*>(a.logits) +
+                   (b * a.ss + y * a.sy + s * a.sp) * Elem<DT>::kBytes;
+  const int64_t v0 = static_cast<int64_t>(sp) * a.chunk2;
+  const int64_t v1 = v0 + a.chunk2 < a.V ? v0 + a.chunk2 : a.V;
+  ArgmaxPick pk;
+  int64_t idx;
+  if (a.inv_t > 0.f) {
+    const float* gr = a.gumbel + b * a.gs + s * a.gp;
+    gumbel_argmax<DT>(xr, gr, v0, v1, a.inv_t, pk);
+    idx = resolve_argmax<DT>(pk, v1, [&](int64_t j) {
+      return __builtin_fmaf(Elem<DT>::load1(xr, j), a.inv_t, gr[j]);
+    });
+  } else {
+    stream_row<DT, 4>(xr, v0, v1, pk);
+    idx = resolve_argmax<DT>(pk, v1, [&](int64_t j) { return Elem<DT>::load1(xr, j); });
+  }
+  float v = pk.best;
+  int ii = static_cast<int>(idx);
+  int nan = pk.nan ? 1 : 0;
+  block_argmax(v, ii, nan, s_v, s_i, s_n);
+  if (threadIdx.x == 0) a.pick[gid] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
+}
+
+__global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
+  __shared__ int s_pos[kMaxStates], s_tok[kMaxStates];
+  __shared__ int s_st, s_child, s_y, s_len, s_ncommit;
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const int S = a.S;
+  const int ns = state_count(a.num_states, b, S);
+  const int64_t base = static_cast<int64_t>(b) * S;
+  const int32_t* par = a.parent + base;
+  const int32_t* ep = a.edge_pos + base;
+  const int32_t* et = a.edge_tok + base;
+  if (t == 0) s_st = ns < 0 ? SEQ_BAD_INPUT : 0;
+  __syncthreads();
+  int st = 0;
+  if (ns > 0) {
+    if (t == 0 && par[0] != -1) st |= SEQ_BAD_INPUT;
+    for (int z = t + 1; z < ns; z += kBlock) {
+      const int pz = par[z];
+      if (pz < 0 || pz >= z) st |= SEQ_BAD_INPUT;
+      if (ep[z] < 0 || ep[z] >= a.L || et[z] < 0 || et[z] >= a.V) st |= SEQ_BAD_INPUT;
+    }
+    if (a.fixed) {
+      for (int z = t; z < ns; z += kBlock) {
+        const int np = a.next_pos[base + z];
+        if (np < -1 || np >= a.L) st |= SEQ_BAD_INPUT;
+      }
+    }
+  }
+  if (st) atomicOr(&s_st, st);
+  __syncthreads();
+  st = 0;
+  const bool valid = !(s_st & SEQ_BAD_INPUT);
+  // Phi(y) per state, and the status of every row that was read.
+  for (int y = t; y < S; y += kBlock) {
+    int pos = -1, tok = -1;
+    float conf = __builtin_nanf("");
+    if (valid && y < ns) {
+      const int64_t sy = base + y;
+      if (!a.fixed) {
+        for (int s = 0; s < a.L; ++s) {
+          if (!a.masked[sy * a.L + s]) continue;
+          float M, Sum;
+          combine_conf(a, sy * a.L + s, M, Sum);
+          st |= stats_status(M, Sum);
+        }
+      }
+      pos = a.sel[sy];
+      if (pos >= 0) {
+        float M, Sum;
+        combine_conf(a, sy * a.L + pos, M, Sum);
+        st |= stats_status(M, Sum);
+        conf = 1.f / Sum;
+        float v = -kInf;
+        int idx = -1, nan = 0;
+        const float2* pk = a.pick + sy * a.split2;
+        for (int k = 0; k < a.split2; ++k) {
+          const int i2 = __float_as_int(pk[k].y);
+          if (pk[k].x != pk[k].x) { nan = 1; continue; }
+          if (pick_better(pk[k].x, i2, v, idx)) { v = pk[k].x; idx = i2; }
+        }
+        st |= nan ? SEQ_NONFINITE : max_status(v);
+        tok = idx;
+      }
+    }
+    if (y < kMaxStates) { s_pos[y] = pos; s_tok[y] = tok; }
+    if (a.sel_pos) a.sel_pos[base + y] = pos;
+    if (a.sel_tok) a.sel_tok[base + y] = tok;
+    if (a.sel_conf) a.sel_conf[base + y] = conf;
+  }
+  if (st) atomicOr(&s_st, st);
+  __syncthreads();
+  const int status = s_st;
+  int32_t* pn = a.path_nodes + base;
+  int32_t* cp = a.commit_pos + base;
+  int32_t* ct = a.commit_tok + base;
+  for (int z = t; z < S; z += kBlock) { pn[z] = -1; cp[z] = -1; ct[z] = -1; }
+  if (status & SEQ_ERROR_MASK) {
+    if (t == 0) {
+      a.path_len[b] = -1;
+      a.num_commits[b] = 0;
+      if (a.status) a.status[b] = status;
+    }
+    return;
+  }
+  if (t == 0) { s_y = 0; s_len = 0; s_ncommit = 0; }
+  __syncthreads();
+  // Walk: accept the child equal to Phi(y) (lowest node index), else commit
+  // Phi(y) and stop; a state without transition ends the walk.
+  for (int step = 0; step < ns; ++step) {
+    const int y = s_y;
+    const int pos = s_pos[y], tok = s_tok[y];
+    if (pos < 0) break;
+    if (t == 0) s_child = INT_MAX;
+    __syncthreads();
+    for (int z = y + 1 + t; z < ns; z += kBlock)
+      if (par[z] == y && ep[z] == pos && et[z] == tok) atomicMin(&s_child, z);
+    __syncthreads();
+    const int child = s_child;
+    __syncthreads();
+    if (t == 0) {
+      if (child == INT_MAX) {
+        cp[s_ncommit] = pos;
+        ct[s_ncommit] = tok;
+        s_ncommit += 1;
+      } else {
+        s_len += 1;
+        pn[s_len] = child;
+        cp[s_ncommit] = ep[child];
+        ct[s_ncommit] = et[child];
+        s_ncommit += 1;
+        s_y = child;
+      }
+    }
+    __syncthreads();
+    if (child == INT_MAX) break;
+  }
+  if (t == 0) {
+    pn[0] = 0;
+    a.path_len[b] = s_len;
+    a.num_commits[b] = s_ncommit;
+    if (a.status) a.status[b] = status;
+  }
+}
+
+bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
+  const int64_t g1 = static_cast<int64_t>(a.B) * a.S * a.L * a.split1;
+  const int64_t g2 = static_cast<int64_t>(a.B) * a.S * a.split2;
+  const dim3 blk(kBlock);
+  if (ev.begin) (void)hipEventRecord(ev.begin, stream);
+  if (dtype == DT_BF16) {
+    if (g1 > 0) hipLaunchKernelGGL(k_tree_conf<DT_BF16>, dim3(static_cast<unsigned>(g1)), blk, 0, stream, a);
+  } else {
+    if (g1 > 0) hipLaunchKernelGGL(k_tree_conf<DT_F32>, dim3(static_cast<unsigned>(g1)), blk, 0, stream, a);
+  }
+  if (hipGetLastError() != hipSuccess) return false;
+  if (ev.end) (void)hipEventRecord(ev.end, stream);
+  if (dtype == DT_BF16) {
+    if (g2 > 0) hipLaunchKernelGGL(k_tree_gumbel<DT_BF16>, dim3(static_cast<unsigned>(g2)), blk, 0, stream, a);
+  } else {
+    if (g2 > 0) hipLaunchKernelGGL(k_tree_gumbel<DT_F32>, dim3(static_cast<unsigned>(g2)), blk, 0, stream, a);
+  }
+  if (hipGetLastError() != hipSuccess) return false;
+  if (a.B > 0) hipLaunchKernelGGL(k_tree_walk, dim3(static_cast<unsigned>(a.B)), blk, 0, stream, a);
+  return hipGetLastError() == hipSuccess;
+}
+
+}  // namespace dbv

@@ -1,0 +1,252 @@
+/*
+ * dbv.h -- C ABI of libdbv, parallel verification of a drafted token block on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One call verifies a batch of B independent sequences against target-model
+ * logits that are already resident in device memory: per (sequence, position)
+ * row it takes a temperature softmax over the vocabulary, applies one
+ * acceptance test (greedy argmax match, lossless rejection min(1, p/q), the
+ * linear lenient rule, or shared-Gumbel state equality over a draft tree),
+ * finds the longest accepted prefix (or tree path) and draws the correction
+ * or bonus token from supplied uniforms.
+ *
+ * Sources (pages by title):
+ *   [PSS]  "One Call Ahead: Packed Self-Speculative Decoding with Diffusion
+ *          Drafting" -- Sec. 2.2, Sec. 3.1 (Eq. 1-4, Algorithm 1), Sec. 3.2,
+ *          App. B.2 (Algorithm 2, Lemma B.3), App. D.1 (packed row layout).
+ *   [SPOT] "On the SPOT: Enhancing Speculative Decoding for Diffusion Language
+ *          Models via Commit-Order Prediction" -- Sec. 4.1, Sec. 4.3,
+ *          App. A.1 (formal decoding model), App. A.3 (Eq. 5-7).
+ *   [TT]   "Speculative Diffusion is a Tale of Two Tradeoffs" -- Sec. 2
+ *          (Eq. 1-5, Theorem 1), Sec. 3.2 (Algorithm 1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array argument is a DEVICE pointer, allocated and owned by the
+ *   caller; the library keeps no pointer after the call returns.  Optional
+ *   arrays may be NULL where stated.
+ * - Logit tensors are row-major with the vocabulary contiguous; the other
+ *   axes are given as element strides (not bytes), so packed layouts need no
+ *   copy.  `dtype` applies to every logit tensor of a call; Gumbel tables and
+ *   uniforms are float32; tokens, lengths and tree indices are int32.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream): they return after enqueueing and outputs are valid once the
+ *   stream reaches that point.  No host<->device synchronisation and no
+ *   device allocation happen inside a call.
+ * - Scratch memory: the caller passes `ws` of at least
+ *   verify_workspace_size(...) bytes (device memory, any contents, 256-byte
+ *   aligned).  Calls that share a workspace must be ordered on one stream.
+ * - Errors: invalid host arguments return a dbv_status and launch nothing.
+ *   Data errors found on the device are reported per sequence in `status`
+ *   (dbv_seq_status bits; NULL = not reported); a sequence with an error bit
+ *   gets accept_len = -1 (path_len = -1), num_out = 0 and -1 in its token
+ *   slots.  -inf logits are legal and mean zero probability ([PSS] Lemma B.3:
+ *   neither distribution needs full support).
+ * - Ties: every argmax takes the largest value and, among equal values, the
+ *   lowest index, on the raw (untempered) inputs ([PSS] App. B.2 "fixed
+ *   tie-breaking rule"; [SPOT] App. A.1 "fixed deterministic tie-breaking").
+ */
+#ifndef DBV_H
+#define DBV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DBV_ABI_VERSION 1
+
+typedef enum {
+  DBV_OK = 0,
+  DBV_ERR_INVALID_ARG = 1, /* a host argument is out of range / NULL      */
+  DBV_ERR_UNSUPPORTED = 2, /* a valid request this build does not serve   */
+  DBV_ERR_NO_DEVICE = 3,   /* no usable gfx950 device                     */
+  DBV_ERR_LAUNCH = 4,      /* a kernel launch failed (hipGetLastError)    */
+  DBV_ERR_WORKSPACE = 5    /* ws is NULL / too small / misaligned         */
+} dbv_status;
+
+typedef enum { DBV_F32 = 0, DBV_BF16 = 1 } dbv_dtype;
+
+typedef enum {
+  DBV_TREE_STATE_EQUALITY = 0, /* s*(y) chosen by max confidence ([SPOT] 4.1) */
+  DBV_TREE_FIXED_POSITION = 1  /* s*(y) given per state in next_pos           */
+} dbv_tree_mode;
+
+/* Per-sequence status bits written to `status[b]`. */
+enum {
+  DBV_SEQ_BAD_INPUT = 1,  /* token / length / tree index out of range (error) */
+  DBV_SEQ_NONFINITE = 2,  /* a row that is read holds NaN or +inf (error)     */
+  DBV_SEQ_EMPTY_ROW = 4,  /* a row that is read is all -inf (error)           */
+  DBV_SEQ_Q_ZERO = 8,     /* q(d) == 0 < p~(d): accepted by the rule, flagged */
+  DBV_SEQ_Z_ZERO = 16     /* residual mass 0 in float32: drew from p, flagged */
+};
+#define DBV_SEQ_ERROR_MASK 7
+
+/* Workspace kinds for verify_workspace_size. */
+typedef enum {
+  DBV_KIND_GREEDY = 0,
+  DBV_KIND_REJECTION = 1, /* also verify_lenient */
+  DBV_KIND_TREE = 2
+} dbv_kind;
+
+/*
+ * verify_greedy -- temperature-0 verification plus next-draft retention.
+ * [PSS] Sec. 3.1 Eq. 1-4 and Algorithm 1:
+ *   v_i = argmax of target row i-1 for i = 1..n_b+1            (Eq. 1)
+ *   h   = leading matches d_i == v_i, h <= n_b                 (Eq. 2)
+ *   C   = (d_1..d_h, v_{h+1}),  A = h + 1
+ *   a   = min({A, len_budget[b]} U {i <= A : C_i == eos_id})  (ending condition)
+ *   z_j = argmax of draft row j-1, j = 1..W                     (Eq. 3)
+ *   next draft = (z_{a+1}, ..., z_W), next_len = max(0, W - a)  (Eq. 4)
+ *
+ * tgt         [B, K+1, V] at tgt + b*tgt_seq_stride + i*tgt_row_stride:
+ *             row i is the verifier conditional at draft position i+1; row
+ *             n_b is the bonus row; rows after n_b are not read.
+ * draft_tokens[B, K] int32 row-major; draft_len [B] (NULL = K everywhere;
+ *             a value outside [0, K] is DBV_SEQ_BAD_INPUT).
+ * draft_rows  [B, W, V] drafter rows of the same call (NULL with W = 0 to
+ *             skip retention); e.g. the packed layout of [PSS] App. D.1 is
+ *             tgt = T, draft_rows = T + (K+1)*V with shared strides.
+ * eos_id      -1 disables the EOS term; len_budget [B] (NULL disables; a
+ *             negative entry is DBV_SEQ_BAD_INPUT).
+ * Outputs: accept_len [B] (= h), out_tokens [B, K+1] (C pruned to a, -1
+ * after), num_out [B] (= a), next_draft [B, W] (-1 after next_len; NULL
+ * allowed when W = 0), next_len [B] (NULL allowed), status [B] (NULL allowed).
+ */
+dbv_status verify_greedy(int B, int K, int V, dbv_dtype dtype,
+                         const void* tgt, int64_t tgt_seq_stride, int64_t tgt_row_stride,
+                         const int32_t* draft_tokens, const int32_t* draft_len,
+                         const void* draft_rows, int64_t dr_seq_stride, int64_t dr_row_stride,
+                         int W, int32_t eos_id, const int32_t* len_budget,
+                         int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
+                         int32_t* next_draft, int32_t* next_len, int32_t* status,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * verify_rejection -- lossless speculative-sampling verification.
+ * [PSS] Sec. 3.2 and Algorithm 2; [TT] Sec. 2 "Lossless Speculative Decoding":
+ *   p_i = softmax(tgt row i / T_target), i = 0..n_b
+ *   q_i = softmax(drf row i / T_draft),  i = 0..n_b-1  (the distribution d_i
+ *         was sampled from -- the stored proposal Q of [PSS] Sec. 3.2)
+ *   accept d_i iff u_accept[b,i] < min(1, p_i(d_i) / q_i(d_i))
+ *         (evaluated as u*q < p; q(d) = 0 < p(d) accepts and is flagged)
+ *   h = leading accepts; if h < n_b the token at position h+1 is drawn from
+ *   normalize([p_h - q_h]_+) with u_resample[b,h], else the bonus from p_{n_b}
+ *   with u_resample[b,n_b]; draws use the inverse CDF in vocabulary order
+ *   (smallest c whose running sum exceeds u * total).  Then the ending
+ *   condition as in verify_greedy.
+ * drf [B, K, V] (same dtype as tgt); temperatures > 0 and finite;
+ * u_accept [B, K], u_resample [B, K+1] float32 in [0, 1).
+ * Optional diagnostics (NULL to skip): p_draft, q_draft, alpha [B, K]
+ * (0 beyond n_b); residual_mass [B] (sum of [p~-q]_+ at the rejected row,
+ * i.e. its rejection probability, 0 when the bonus was drawn; p~ = p here).
+ */
+dbv_status verify_rejection(int B, int K, int V, dbv_dtype dtype,
+                            const void* tgt, int64_t tgt_seq_stride, int64_t tgt_row_stride,
+                            const void* drf, int64_t drf_seq_stride, int64_t drf_row_stride,
+                            const int32_t* draft_tokens, const int32_t* draft_len,
+                            float temperature_target, float temperature_draft,
+                            const float* u_accept, const float* u_resample,
+                            int32_t eos_id, const int32_t* len_budget,
+                            int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
+                            float* p_draft, float* q_draft, float* alpha, float* residual_mass,
+                            int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * verify_lenient -- the linear lenient rule of [TT] Theorem 1 (Eq. 5) used in
+ * [TT] Algorithm 1: the target is relaxed to p~ = (1 - lambda) p + lambda q
+ * before the draft is tested; accept iff u < min(1, p~(d)/q(d)); a rejected
+ * position draws from normalize([p~ - q]_+) (equal to normalize([p - q]_+)
+ * for lambda < 1); the bonus after full acceptance is drawn from p, not p~.
+ * lambda in [0, 1]: 0 reproduces verify_rejection bit for bit, 1 accepts
+ * every draft.  All other arguments as verify_rejection.
+ */
+dbv_status verify_lenient(int B, int K, int V, dbv_dtype dtype,
+                          const void* tgt, int64_t tgt_seq_stride, int64_t tgt_row_stride,
+                          const void* drf, int64_t drf_seq_stride, int64_t drf_row_stride,
+                          const int32_t* draft_tokens, const int32_t* draft_len,
+                          float temperature_target, float temperature_draft, float lambda,
+                          const float* u_accept, const float* u_resample,
+                          int32_t eos_id, const int32_t* len_budget,
+                          int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
+                          float* p_draft, float* q_draft, float* alpha, float* residual_mass,
+                          int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * verify_gumbel_tree -- state-equality verification of one draft tree per
+ * sequence with shared Gumbel noise.  [SPOT] Sec. 4.1, Sec. 4.3, App. A.1:
+ *   s*(y)  = argmax over masked positions s of max_v p_s(v | y) (untempered;
+ *            ties to the lowest position)                   [STATE_EQUALITY]
+ *          = next_pos[b, y] (-1: no transition)              [FIXED_POSITION]
+ *   v*(y)  = argmax_v ( z_v / T + G[b, s*, v] )  for T > 0  -- equal to
+ *            argmax[(1/T) log p + G] since the row constant drops out;
+ *          = argmax_v z_v                         for T = 0 (G may be NULL)
+ *   An edge y -> z is accepted iff edge_pos[z] == s*(y) and
+ *   edge_tok[z] == v*(y) (z equals Phi(y)); the walk starts at node 0,
+ *   follows the accepted child (lowest node index if several), and ends by
+ *   committing Phi(y) at the first state with no accepted child; a state
+ *   with no masked position (or next_pos = -1) makes no transition.
+ *
+ * logits  [B, S, L, V] at logits + b*seq_stride + y*state_stride + s*pos_stride:
+ *         the target conditional at block position s of state y; only the
+ *         masked rows of states y < num_states[b] are read.
+ * masked  [B, S, L] uint8 (nonzero = masked); may be NULL in FIXED_POSITION.
+ * parent  [B, S]: parent[b,0] = -1, 0 <= parent[b,z] < z; edge_pos [B, S] in
+ *         [0, L), edge_tok [B, S] in [0, V) for z >= 1 (entry 0 unused).
+ * num_states [B] in [1, S] (NULL = S); next_pos [B, S] in [-1, L)
+ *         (FIXED_POSITION only, else NULL).
+ * gumbel  [B, L, V] float32 at gumbel + b*g_seq_stride + s*g_pos_stride: the
+ *         shared table row of block position s (absolute-position indexing is
+ *         the caller's job).  temperature >= 0 and finite.
+ * Outputs: sel_pos, sel_tok [B, S] (-1 for terminal / unused states; NULL
+ * allowed), sel_conf [B, S] (max_v p at s*, NULL allowed), path_len [B]
+ * (accepted edges), path_nodes [B, S] (root first, -1 after), commit_pos,
+ * commit_tok [B, S] (accepted edges then the final Phi, -1 after),
+ * num_commits [B], status [B] (NULL allowed).
+ */
+dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype,
+                              const void* logits, int64_t seq_stride, int64_t state_stride,
+                              int64_t pos_stride,
+                              const uint8_t* masked, const int32_t* parent,
+                              const int32_t* edge_pos, const int32_t* edge_tok,
+                              const int32_t* num_states, const int32_t* next_pos,
+                              const float* gumbel, int64_t g_seq_stride, int64_t g_pos_stride,
+                              float temperature, dbv_tree_mode mode,
+                              int32_t* sel_pos, int32_t* sel_tok, float* sel_conf,
+                              int32_t* path_len, int32_t* path_nodes,
+                              int32_t* commit_pos, int32_t* commit_tok, int32_t* num_commits,
+                              int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * verify_workspace_size -- bytes of scratch one call of `kind` needs.
+ *   DBV_KIND_GREEDY:    K_or_S = K, L = W (draft rows)
+ *   DBV_KIND_REJECTION: K_or_S = K, L ignored
+ *   DBV_KIND_TREE:      K_or_S = S, L = block length
+ * Returns 0 for invalid sizes.  Depends only on its arguments.
+ */
+size_t verify_workspace_size(dbv_kind kind, int B, int K_or_S, int L, int V, dbv_dtype dtype);
+
+/*
+ * verify_set_timing_events -- diagnostics hook.  With two non-NULL hipEvent_t
+ * handles, every later verify_* call records `begin` on its stream just before
+ * its row-streaming kernel (the launch that reads the logit rows: row
+ * statistics / argmax, or the tree's per-row confidences) and `end` just
+ * after it, so that kernel's own duration can be read with
+ * hipEventElapsedTime.  (NULL, NULL) turns it off.  A process-wide setting
+ * for benchmarking; not meant for concurrent calls.
+ */
+void verify_set_timing_events(void* begin, void* end);
+
+/* Static text for a dbv_status (never NULL). */
+const char* verify_status_string(dbv_status s);
+
+/* DBV_ABI_VERSION of the loaded library. */
+int verify_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DBV_H */

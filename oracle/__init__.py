@@ -36,6 +36,6 @@ from .rows import (  # noqa: F401
 )
 from .chain import verify_greedy, verify_rejection, verify_lenient  # noqa: F401
 from .tree import (  # noqa: F401
-    TREE_STATE_EQUALITY, TREE_FIXED_POSITION, state_transition,
+    TREE_STATE_EQUALITY, TREE_FIXED_POSITION, state_transition, walk,
     verify_gumbel_tree,
 )

@@ -29,7 +29,7 @@ the token is drawn there; this is the chain / autoregressive special case.
 import numpy as np
 
 from .rows import (
-    STATUS_BAD_INPUT, STATUS_NONFINITE, STATUS_ERROR_MASK, row_status,
+    STATUS_BAD_INPUT, STATUS_ERROR_MASK, row_status,
     max_probability, argmax_lowest,
 )
 
@@ -90,10 +90,14 @@ def state_transition(rows, masked_positions, gumbel, temperature, fixed_pos=None
     x = rows[s_star]
     if temperature > 0.0:
         g = np.asarray(gumbel[s_star], dtype=np.float64)
-        if not np.isfinite(g).all():
-            res["status"] = STATUS_NONFINITE
+        with np.errstate(invalid="ignore"):
+            score = _log_tempered_softmax(x, temperature) + g
+        # The score row obeys the logit-row rule: NaN / +inf (from the
+        # Gumbel row) is an error, -inf is a zero-weight entry.
+        st = row_status(score)
+        if st:
+            res["status"] = st
             return res
-        score = _log_tempered_softmax(x, temperature) + g
         tok = argmax_lowest(score)
         res["tok_margin"] = _top2_gap(score)
     else:
@@ -101,6 +105,26 @@ def state_transition(rows, masked_positions, gumbel, temperature, fixed_pos=None
     res["pos"] = int(s_star)
     res["tok"] = int(tok)
     return res
+
+
+def walk(parent, edge_pos, edge_tok, ns, pos, tok):
+    """State-equality walk from the root (SPOT, App. A.1, state-equality
+    verifier): follow the child equal to Phi(y) (lowest node index if there
+    are several), else commit Phi(y) and stop; a state with pos = -1 makes no
+    transition.  ``pos[y], tok[y]`` is Phi(y).  Returns (path, commits)."""
+    y = 0
+    path = [0]
+    commits = []
+    while pos[y] >= 0:
+        match = [z for z in range(1, ns) if parent[z] == y
+                 and edge_pos[z] == pos[y] and edge_tok[z] == tok[y]]
+        if not match:
+            commits.append((int(pos[y]), int(tok[y])))
+            break
+        y = match[0]
+        path.append(y)
+        commits.append((int(edge_pos[y]), int(edge_tok[y])))
+    return path, commits
 
 
 def verify_gumbel_tree(logits, masked, parent, edge_pos, edge_tok,
@@ -172,22 +196,8 @@ def verify_gumbel_tree(logits, masked, parent, edge_pos, edge_tok,
             out["pos_margin"][b, z] = t["pos_margin"]
             out["tok_margin"][b, z] = t["tok_margin"]
 
-        # Walk from the root following the child equal to Phi(y).
-        y = 0
-        path = [0]
-        commits = []
-        while True:
-            t = trans[y]
-            if t["pos"] < 0:          # terminal: no further transition
-                break
-            match = [z for z in range(1, ns) if parent[b, z] == y
-                     and edge_pos[b, z] == t["pos"] and edge_tok[b, z] == t["tok"]]
-            if not match:
-                commits.append((t["pos"], t["tok"]))
-                break
-            y = match[0]
-            path.append(y)
-            commits.append((int(edge_pos[b, y]), int(edge_tok[b, y])))
+        path, commits = walk(parent[b], edge_pos[b], edge_tok[b], ns,
+                             [t["pos"] for t in trans], [t["tok"] for t in trans])
         out["path_len"][b] = len(path) - 1
         out["path_nodes"][b, :len(path)] = path
         for k, (s, v) in enumerate(commits):

@@ -1,0 +1,189 @@
+"""Parity checks of GPU outputs against the float64 oracle.
+
+Integer outputs must agree exactly, except at a decision whose margin in the
+oracle is below NEAR_MARGIN: there the GPU's choice must pass the bracket
+check (it is a choice the oracle would make if the threshold moved by at most
+NEAR_MARGIN), and everything downstream is recomputed from the GPU's choice
+and compared exactly.  Near-margin decisions are counted and returned.
+Probabilities agree within a relative tolerance fixed by the input precision.
+"""
+
+from collections import Counter
+
+import numpy as np
+
+import oracle
+from oracle import NEAR_MARGIN
+
+# Relative tolerance of probabilities (p(d), q(d), alpha, conf, Z): float32
+# arithmetic on exact float32 inputs stays within ~2e-6; bf16 inputs are
+# exact in float32 as well, the looser bound covers the exp2 / summation
+# error of long rows.
+PROB_RTOL = {"float32": 1e-5, "bfloat16": 2e-3}
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64) if hasattr(t, "detach") else np.asarray(t, np.float64)
+
+
+def npi(t):
+    return t.detach().cpu().numpy().astype(np.int64) if hasattr(t, "detach") else np.asarray(t, np.int64)
+
+
+def _rel_ok(a, b, rtol, atol=1e-30):
+    return abs(a - b) <= rtol * max(abs(a), abs(b)) + atol
+
+
+def check_greedy(g, o):
+    """Greedy outputs are integer decisions on exact values: all exact."""
+    for k in ("status", "accept_len", "num_out", "out_tokens"):
+        np.testing.assert_array_equal(npi(g[k]), o[k], err_msg=k)
+    if o["next_draft"].shape[1] > 0:
+        np.testing.assert_array_equal(npi(g["next_draft"]), o["next_draft"], err_msg="next_draft")
+    np.testing.assert_array_equal(npi(g["next_len"]), o["next_len"], err_msg="next_len")
+
+
+def check_sampling(g, x, o, lam, t_target, t_draft, dtype_name, eos_id=-1, len_budget=None,
+                   seqs=None):
+    """Rejection / lenient outputs against the oracle with margin accounting.
+
+    g: GPU outputs (torch or numpy); x: the inputs as float64 numpy
+    (tgt, drf, draft_tokens, draft_len, u_accept, u_resample); o: oracle
+    result for the same inputs (possibly for the subset ``seqs``).
+    """
+    rtol = PROB_RTOL[dtype_name]
+    near = Counter()
+    st_g = npi(g["status"])
+    acc_g = npi(g["accept_len"])
+    out_g = npi(g["out_tokens"])
+    num_g = npi(g["num_out"])
+    pd_g, qd_g, al_g = (np64(g[k]) for k in ("p_draft", "q_draft", "alpha"))
+    rm_g = np64(g["residual_mass"])
+    B = len(st_g) if seqs is None else len(seqs)
+    K = x["tgt"].shape[1] - 1
+    for j in range(B):
+        b = j if seqs is None else seqs[j]
+        so = int(o["status"][j])
+        sg = int(st_g[b])
+        assert (sg & oracle.STATUS_ERROR_MASK) == (so & oracle.STATUS_ERROR_MASK), (b, sg, so)
+        assert (sg & oracle.STATUS_Q_ZERO) == (so & oracle.STATUS_Q_ZERO), (b, sg, so)
+        if (sg ^ so) & oracle.STATUS_Z_ZERO:
+            near["z_zero"] += 1
+        if so & oracle.STATUS_ERROR_MASK:
+            assert acc_g[b] == -1 and num_g[b] == 0 and (out_g[b] == -1).all(), b
+            continue
+        n = int(x["draft_len"][b])
+        d = [int(v) for v in x["draft_tokens"][b, :n]]
+        for i in range(n):
+            assert _rel_ok(pd_g[b, i], o["p_draft"][j, i], rtol), ("p", b, i, pd_g[b, i], o["p_draft"][j, i])
+            assert _rel_ok(qd_g[b, i], o["q_draft"][j, i], rtol), ("q", b, i, qd_g[b, i], o["q_draft"][j, i])
+            assert _rel_ok(al_g[b, i], o["alpha"][j, i], rtol), ("alpha", b, i)
+        for i in range(n, K):
+            assert pd_g[b, i] == 0 and qd_g[b, i] == 0 and al_g[b, i] == 0
+        h = int(acc_g[b])
+        assert 0 <= h <= n, (b, h, n)
+        for i in range(h):           # GPU accepted draft i
+            if not o["accept_bits"][j, i]:
+                assert o["accept_margin"][j, i] < NEAR_MARGIN, ("accept", b, i, o["accept_margin"][j, i])
+                near["accept"] += 1
+        if h < n and o["accept_bits"][j, h]:   # GPU rejected draft h
+            assert o["accept_margin"][j, h] < NEAR_MARGIN, ("reject", b, h, o["accept_margin"][j, h])
+            near["accept"] += 1
+        # The draw at the GPU's row h.
+        p = oracle.tempered_softmax(x["tgt"][b, h], t_target)
+        if h < n:
+            q = oracle.tempered_softmax(x["drf"][b, h], t_draft)
+            w = oracle.residual_weights(p, q, lam)
+            Zr = float(np.sum(w))
+            if Zr <= 0.0:
+                w = p
+        else:
+            w, Zr = p, 0.0
+        u = float(x["u_resample"][b, h])
+        c_o, margin, Z = oracle.inverse_cdf(w, u)
+        if num_g[b] > h:
+            c_g = int(out_g[b, h])
+            if c_g != c_o:
+                F = np.cumsum(w)
+                lo = F[c_g - 1] if c_g > 0 else 0.0
+                ok = (0 <= c_g < len(w) and w[c_g] > 0 and lo - NEAR_MARGIN * Z <= u * Z < F[c_g] + NEAR_MARGIN * Z)
+                assert ok and margin < NEAR_MARGIN, ("draw", b, h, c_g, c_o, margin)
+                near["draw"] += 1
+        else:
+            c_g = c_o
+        C = d[:h] + [c_g]
+        bud = None if len_budget is None else int(len_budget[b])
+        a = oracle.stopping_index(C, h + 1, eos_id, bud)
+        assert num_g[b] == a, (b, num_g[b], a)
+        exp = np.full(K + 1, -1)
+        exp[:a] = C[:a]
+        np.testing.assert_array_equal(out_g[b], exp, err_msg=f"out_tokens seq {b}")
+        if h < n:
+            assert _rel_ok(rm_g[b], Zr, max(rtol, 1e-4), 1e-7), ("Z", b, rm_g[b], Zr)
+        else:
+            assert rm_g[b] == 0.0
+        if h == o["accept_len"][j] and c_g == c_o:
+            near["exact"] += 1
+    return near
+
+
+def check_tree(g, x, o, dtype_name, temperature, seqs=None):
+    """Tree outputs against the oracle; near ties in s* or in the Gumbel
+    argmax are bracket-checked and the walk is redone with the GPU's
+    choices."""
+    rtol = PROB_RTOL[dtype_name]
+    near = Counter()
+    sp_g, stk_g, sc_g = npi(g["sel_pos"]), npi(g["sel_tok"]), np64(g["sel_conf"])
+    st_g = npi(g["status"])
+    pl_g, pn_g = npi(g["path_len"]), npi(g["path_nodes"])
+    cp_g, ct_g, nc_g = npi(g["commit_pos"]), npi(g["commit_tok"]), npi(g["num_commits"])
+    B = len(st_g) if seqs is None else len(seqs)
+    S = sp_g.shape[1]
+    for j in range(B):
+        b = j if seqs is None else seqs[j]
+        so, sg = int(o["status"][j]), int(st_g[b])
+        assert sg == so, (b, sg, so)
+        if so & oracle.STATUS_ERROR_MASK:
+            assert pl_g[b] == -1 and nc_g[b] == 0
+            continue
+        ns = S if x.get("num_states") is None else int(x["num_states"][b])
+        pos, tok = [], []
+        for y in range(ns):
+            po, to = int(o["sel_pos"][j, y]), int(o["sel_tok"][j, y])
+            pg, tg = int(sp_g[b, y]), int(stk_g[b, y])
+            if pg != po:
+                assert o["pos_margin"][j, y] < NEAR_MARGIN, ("s*", b, y, pg, po)
+                rows = x["logits"][b, y]
+                cg = oracle.rows.max_probability(rows[pg])
+                assert cg >= o["sel_conf"][j, y] * (1 - NEAR_MARGIN), ("s* bracket", b, y)
+                near["pos"] += 1
+                t2 = oracle.state_transition(rows, None, None if x.get("gumbel") is None else x["gumbel"][b],
+                                             temperature, fixed_pos=pg)
+                to = t2["tok"]
+                tmargin = t2["tok_margin"]
+            else:
+                tmargin = o["tok_margin"][j, y]
+            if tg != to:
+                assert tmargin < NEAR_MARGIN, ("tok", b, y, tg, to, tmargin)
+                near["tok"] += 1
+            if pg >= 0:
+                assert _rel_ok(sc_g[b, y], oracle.rows.max_probability(x["logits"][b, y, pg]), rtol), ("conf", b, y)
+            pos.append(pg)
+            tok.append(tg)
+        for y in range(ns, S):
+            assert sp_g[b, y] == -1 and stk_g[b, y] == -1
+        path, commits = oracle.walk(x["parent"][b], x["edge_pos"][b], x["edge_tok"][b], ns, pos, tok)
+        assert pl_g[b] == len(path) - 1, (b, pl_g[b], path)
+        exp = np.full(S, -1)
+        exp[:len(path)] = path
+        np.testing.assert_array_equal(pn_g[b], exp, err_msg=f"path seq {b}")
+        assert nc_g[b] == len(commits)
+        ep = np.full(S, -1)
+        et = np.full(S, -1)
+        for k, (s, v) in enumerate(commits):
+            ep[k], et[k] = s, v
+        np.testing.assert_array_equal(cp_g[b], ep)
+        np.testing.assert_array_equal(ct_g[b], et)
+        if pl_g[b] == o["path_len"][j]:
+            near["exact_path"] += 1
+    return near

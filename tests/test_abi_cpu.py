@@ -1,0 +1,174 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point declared in include/dbv.h, sizes workspaces and rejects invalid host
+arguments before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from draft_block_verification_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dbv.h")
+
+FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced here
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(verify_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libdbv.so not built")
+    return _lib.load()
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+def test_exports_match_header(lib):
+    declared = _declared_functions()
+    assert declared == sorted(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.verify_abi_version() == 1
+    for code in range(6):
+        assert lib.verify_status_string(code)
+    assert b"unknown" in lib.verify_status_string(99)
+
+
+def test_workspace_sizes(lib):
+    g = lib.verify_workspace_size(_lib.DBV_KIND_GREEDY, 64, 31, 32, 131072, _lib.DBV_BF16)
+    assert g >= 64 * (32 + 32) * 8 and g % 256 == 0
+    r = lib.verify_workspace_size(_lib.DBV_KIND_REJECTION, 32, 16, 0, 128256, _lib.DBV_BF16)
+    assert r > 0 and r % 256 == 0
+    t = lib.verify_workspace_size(_lib.DBV_KIND_TREE, 16, 64, 32, 151936, _lib.DBV_BF16)
+    assert t >= 16 * 64 * 32 * 8
+    assert lib.verify_workspace_size(_lib.DBV_KIND_TREE, 16, 0, 32, 100, 1) == 0
+    assert lib.verify_workspace_size(_lib.DBV_KIND_GREEDY, 1, -1, 0, 100, 1) == 0
+    assert lib.verify_workspace_size(_lib.DBV_KIND_GREEDY, 1, 4, 0, 0, 1) == 0
+    assert lib.verify_workspace_size(_lib.DBV_KIND_GREEDY, 1, 4, 0, 10, 7) == 0
+
+
+def _greedy(lib, **kw):
+    a = dict(B=2, K=3, V=100, dt=_lib.DBV_BF16, tgt=FAKE, ts=400, tr=100, d=FAKE, n=None,
+             dr=FAKE, ds=400, drs=100, W=4, eos=-1, bud=None, acc=FAKE, out=FAKE, num=FAKE,
+             nd=FAKE, nl=FAKE, st=FAKE, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.verify_greedy(a["B"], a["K"], a["V"], a["dt"], a["tgt"], a["ts"], a["tr"], a["d"],
+                             a["n"], a["dr"], a["ds"], a["drs"], a["W"], a["eos"], a["bud"],
+                             a["acc"], a["out"], a["num"], a["nd"], a["nl"], a["st"], a["ws"],
+                             a["wsb"], a["stream"])
+
+
+def _reject(lib, lenient=False, **kw):
+    a = dict(B=2, K=3, V=100, dt=_lib.DBV_BF16, tgt=FAKE, ts=400, tr=100, drf=FAKE, ds=300,
+             dr=100, d=FAKE, n=None, tt=1.0, td=1.0, lam=0.5, ua=FAKE, ur=FAKE, eos=-1, bud=None,
+             acc=FAKE, out=FAKE, num=FAKE, pd=None, qd=None, al=None, rm=None, st=FAKE, ws=FAKE,
+             wsb=1 << 20, stream=None)
+    a.update(kw)
+    head = [a["B"], a["K"], a["V"], a["dt"], a["tgt"], a["ts"], a["tr"], a["drf"], a["ds"], a["dr"],
+            a["d"], a["n"], a["tt"], a["td"]]
+    tail = [a["ua"], a["ur"], a["eos"], a["bud"], a["acc"], a["out"], a["num"], a["pd"], a["qd"],
+            a["al"], a["rm"], a["st"], a["ws"], a["wsb"], a["stream"]]
+    if lenient:
+        return lib.verify_lenient(*(head + [a["lam"]] + tail))
+    return lib.verify_rejection(*(head + tail))
+
+
+def _tree(lib, **kw):
+    a = dict(B=2, S=8, L=4, V=100, dt=_lib.DBV_BF16, lg=FAKE, ss=3200, sy=400, sp=100, m=FAKE,
+             par=FAKE, ep=FAKE, et=FAKE, ns=None, npos=None, g=FAKE, gs=400, gp=100, T=1.0,
+             mode=_lib.DBV_TREE_STATE_EQUALITY, o=FAKE, ws=FAKE, wsb=1 << 22, stream=None)
+    a.update(kw)
+    o = a["o"]
+    return lib.verify_gumbel_tree(a["B"], a["S"], a["L"], a["V"], a["dt"], a["lg"], a["ss"], a["sy"],
+                                  a["sp"], a["m"], a["par"], a["ep"], a["et"], a["ns"], a["npos"],
+                                  a["g"], a["gs"], a["gp"], a["T"], a["mode"], o, o, o, o, o, o, o,
+                                  o, o, a["ws"], a["wsb"], a["stream"])
+
+
+INVALID = _lib.DBV_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=-1), dict(K=-1), dict(K=5000), dict(V=0), dict(W=-2), dict(dt=3), dict(tgt=None),
+    dict(d=None), dict(dr=None), dict(ts=-1), dict(acc=None), dict(out=None), dict(num=None),
+    dict(tgt=FAKE + 1),
+])
+def test_greedy_rejects_bad_args(lib, kw):
+    assert _greedy(lib, **kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [
+    dict(tt=0.0), dict(td=-1.0), dict(tt=float("nan")), dict(td=float("inf")), dict(drf=None),
+    dict(ua=None), dict(ur=None), dict(d=None), dict(V=0), dict(dr=-5), dict(tgt=FAKE + 1),
+])
+def test_rejection_rejects_bad_args(lib, kw):
+    assert _reject(lib, **kw) == INVALID
+    assert _reject(lib, lenient=True, **kw) == INVALID
+
+
+@pytest.mark.parametrize("lam", [-0.01, 1.01, float("nan")])
+def test_lenient_rejects_bad_lambda(lib, lam):
+    assert _reject(lib, lenient=True, lam=lam) == INVALID
+
+
+@pytest.mark.parametrize("kw", [
+    dict(S=0), dict(S=5000), dict(L=0), dict(V=0), dict(mode=2), dict(T=-0.5), dict(T=float("nan")),
+    dict(m=None), dict(g=None), dict(par=None), dict(ep=None), dict(et=None), dict(o=None),
+    dict(mode=_lib.DBV_TREE_FIXED_POSITION, npos=None), dict(gs=-1), dict(g=FAKE + 2),
+])
+def test_tree_rejects_bad_args(lib, kw):
+    assert _tree(lib, **kw) == INVALID
+
+
+def test_workspace_errors(lib):
+    assert _greedy(lib, ws=None) == _lib.DBV_ERR_WORKSPACE
+    assert _greedy(lib, wsb=8) == _lib.DBV_ERR_WORKSPACE
+    assert _greedy(lib, ws=FAKE + 64) == _lib.DBV_ERR_WORKSPACE
+    assert _reject(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
+    assert _tree(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
+
+
+def test_optional_arguments_are_accepted(lib):
+    # T = 0 needs no Gumbel table; W = 0 needs no draft rows; fixed mode needs
+    # no mask.  These pass host validation (then meet the device check).
+    if _gpu_visible():
+        pytest.skip("would launch with fake pointers on a GPU")
+    nodev = _lib.DBV_ERR_NO_DEVICE
+    assert _tree(lib, T=0.0, g=None) == nodev
+    assert _tree(lib, mode=_lib.DBV_TREE_FIXED_POSITION, npos=FAKE, m=None) == nodev
+    assert _greedy(lib, W=0, dr=None, nd=None, nl=None) == nodev
+    assert _reject(lib, K=0, drf=None, d=None, ua=None) == nodev
+
+
+def test_valid_call_without_gpu_reports_no_device(lib):
+    if _gpu_visible():
+        pytest.skip("a GPU is visible")
+    assert _greedy(lib) == _lib.DBV_ERR_NO_DEVICE
+    assert _reject(lib) == _lib.DBV_ERR_NO_DEVICE
+    assert _reject(lib, lenient=True) == _lib.DBV_ERR_NO_DEVICE
+    assert _tree(lib) == _lib.DBV_ERR_NO_DEVICE
+
+
+def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
+    # The binding never falls back: a missing library is an error.
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -1,0 +1,286 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle at
+sizes the oracle finishes in seconds: several vocabulary chunks, ragged tails,
+rows that are not 16-byte aligned, exact ties, every mode and the edge cases.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import draft_block_verification_amd as dbv
+import oracle
+import workloads
+from tests.parity import check_greedy, check_sampling, check_tree, np64, npi
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _np_inputs(x):
+    return {k: (np64(v) if v.dtype.is_floating_point else npi(v)) if torch.is_tensor(v) else v
+            for k, v in x.items()}
+
+
+def _to(x, dev):
+    return {k: v.to(dev) if torch.is_tensor(v) else v for k, v in x.items()}
+
+
+# ------------------------------------------------------------------ greedy ---
+
+def _tie_logits(g, shape, dtype):
+    # small integers: many exact ties between entries of a row
+    return torch.randint(-4, 5, shape, generator=g).to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("V", [20011, 7, 4096])
+def test_greedy_parity(dev, dtype, V):
+    say("greedy", dtype, V)
+    g = torch.Generator().manual_seed(V)
+    B, K, W = 6, 7, 9
+    tgt = _tie_logits(g, (B, K + 1, V), dtype) if V == 7 else (torch.randn(B, K + 1, V, generator=g) * 3).to(dtype)
+    if V == 20011:   # plant exact top-1 ties in some rows
+        tgt[0, 0, 5] = tgt[0, 0, 17] = 1000.0
+        tgt[1, 2, 19990] = tgt[1, 2, 20005] = 1000.0
+    dr = (torch.randn(B, W, V, generator=g) * 3).to(dtype)
+    dr[2, 3, 100 % V] = dr[2, 3, 3000 % V] = 99.0
+    d = torch.argmax(tgt[:, :K].float() + (torch.rand(B, K, V, generator=g) < 0.0002).float() * 50, -1).to(torch.int32)
+    n = torch.tensor([0, 7, 3, 5, 7, 1], dtype=torch.int32)
+    res = dbv.verify_greedy(tgt.to(dev), d.to(dev), n.to(dev), dr.to(dev))
+    o = oracle.verify_greedy(np64(tgt), npi(d), npi(n), np64(dr))
+    check_greedy(res, o)
+
+
+def test_greedy_stopping_rule(dev):
+    say("greedy stopping")
+    g = torch.Generator().manual_seed(3)
+    B, K, W, V = 8, 6, 6, 3000
+    tgt = (torch.randn(B, K + 1, V, generator=g) * 3).to(torch.bfloat16)
+    d = torch.argmax(tgt[:, :K].float(), -1).to(torch.int32)   # all drafts match
+    d[3, 2] = (d[3, 2] + 1) % V
+    eos = int(d[0, 2])
+    d[1, 4] = eos
+    dr = (torch.randn(B, W, V, generator=g) * 3).to(torch.bfloat16)
+    bud = torch.tensor([10, 10, 2, 0, 3, 100, 1, 7], dtype=torch.int32)
+    res = dbv.verify_greedy(tgt.to(dev), d.to(dev), None, dr.to(dev), eos_id=eos, len_budget=bud.to(dev))
+    o = oracle.verify_greedy(np64(tgt), npi(d), None, np64(dr), eos_id=eos, len_budget=npi(bud))
+    check_greedy(res, o)
+    assert o["num_out"][0] == 3 and o["num_out"][2] == 2 and o["num_out"][3] == 0
+
+
+def test_greedy_packed_layout(dev):
+    say("greedy packed")
+    x = workloads.config5(B=8, K=8, V=5003)
+    p = x["packed"].to(dev)
+    K, W = x["K"], x["W"]
+    res = dbv.verify_greedy(p[:, :K + 1], x["draft_tokens"].to(dev), x["draft_len"].to(dev), p[:, K + 1:])
+    o = oracle.verify_greedy(np64(x["packed"][:, :K + 1]), npi(x["draft_tokens"]), npi(x["draft_len"]),
+                             np64(x["packed"][:, K + 1:]))
+    check_greedy(res, o)
+    assert W == K + 1
+
+
+# ---------------------------------------------------------------- sampling ---
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("T", [1.0, 0.7])
+@pytest.mark.parametrize("V", [20011, 9, 4104])
+def test_rejection_parity(dev, dtype, T, V):
+    say("rejection", dtype, T, V)
+    x = workloads.chain_inputs(90 + V % 7, 6, 7, V, dtype, sigma=1.0, temperature=T, random_lengths=True)
+    res = dbv.verify_rejection(x["tgt"].to(dev), x["drf"].to(dev), x["draft_tokens"].to(dev),
+                               x["u_accept"].to(dev), x["u_resample"].to(dev),
+                               draft_len=x["draft_len"].to(dev), temperature_target=T, temperature_draft=T)
+    xn = _np_inputs(x)
+    o = oracle.verify_rejection(xn["tgt"], xn["drf"], xn["draft_tokens"], xn["draft_len"], T, T,
+                                xn["u_accept"], xn["u_resample"])
+    near = check_sampling(res, xn, o, 0.0, T, T, str(dtype).split(".")[1])
+    say("near-margin", dict(near))
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.25, 0.5, 1.0])
+@pytest.mark.parametrize("sigma", [0.25, 2.0])
+def test_lenient_parity(dev, lam, sigma):
+    say("lenient", lam, sigma)
+    V = 12345
+    x = workloads.chain_inputs(77, 8, 6, V, torch.bfloat16, sigma=sigma, temperature=1.0, random_lengths=True)
+    res = dbv.verify_lenient(x["tgt"].to(dev), x["drf"].to(dev), x["draft_tokens"].to(dev),
+                             x["u_accept"].to(dev), x["u_resample"].to(dev), lam,
+                             draft_len=x["draft_len"].to(dev), temperature_target=1.0, temperature_draft=0.9)
+    xn = _np_inputs(x)
+    o = oracle.verify_lenient(xn["tgt"], xn["drf"], xn["draft_tokens"], xn["draft_len"], 1.0, 0.9, lam,
+                              xn["u_accept"], xn["u_resample"])
+    near = check_sampling(res, xn, o, lam, 1.0, 0.9, "bfloat16")
+    say("near-margin", dict(near))
+    if lam == 1.0:
+        np.testing.assert_array_equal(npi(res["accept_len"]), xn["draft_len"])
+
+
+def test_lenient_zero_is_rejection_bit_for_bit(dev):
+    say("lenient 0 == rejection")
+    x = _to(workloads.chain_inputs(78, 8, 9, 30011, torch.bfloat16, sigma=1.0, random_lengths=True), dev)
+    a = dbv.verify_rejection(x["tgt"], x["drf"], x["draft_tokens"], x["u_accept"], x["u_resample"],
+                             draft_len=x["draft_len"])
+    b = dbv.verify_lenient(x["tgt"], x["drf"], x["draft_tokens"], x["u_accept"], x["u_resample"], 0.0,
+                           draft_len=x["draft_len"])
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_sampling_stopping_rule(dev):
+    say("sampling stopping")
+    x = workloads.chain_inputs(79, 8, 6, 2000, torch.float32, sigma=0.3)
+    eos = int(x["draft_tokens"][0, 1])
+    bud = torch.tensor([7, 1, 0, 3, 2, 7, 7, 4], dtype=torch.int32)
+    xd = _to(x, dev)
+    res = dbv.verify_rejection(xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"],
+                               eos_id=eos, len_budget=bud.to(dev))
+    xn = _np_inputs(x)
+    o = oracle.verify_rejection(xn["tgt"], xn["drf"], xn["draft_tokens"], None, 1.0, 1.0,
+                                xn["u_accept"], xn["u_resample"], eos_id=eos, len_budget=npi(bud))
+    check_sampling(res, xn, o, 0.0, 1.0, 1.0, "float32", eos_id=eos, len_budget=npi(bud))
+
+
+# -------------------------------------------------------------- edge cases ---
+
+def test_chain_edge_cases(dev):
+    say("chain edge cases")
+    B, K, V = 9, 4, 3001
+    x = workloads.chain_inputs(80, B, K, V, torch.float32, sigma=1.0)
+    tgt, drf, d = x["tgt"].clone(), x["drf"].clone(), x["draft_tokens"].clone()
+    n = torch.full((B,), K, dtype=torch.int32)
+    d[0, 2] = V                      # out-of-range token
+    tgt[1, 3, 77] = float("nan")     # NaN in a row that is read
+    tgt[2, 1, :] = float("-inf")     # empty row
+    tgt[3, 4, 5] = float("inf")      # +inf in the bonus row
+    n[4] = 1
+    tgt[4, 3, 9] = float("nan")      # NaN in a row that is not read
+    n[5] = K + 1                     # bad draft length
+    drf[6, 0, int(d[6, 0])] = float("-inf")   # q(d) = 0 < p(d): accepted + flagged
+    n[7] = 0                         # empty draft: bonus from row 0
+    tgt[8, :, : V // 2] = float("-inf")        # half the vocabulary masked out
+    drf[8, :, : V // 2] = float("-inf")
+    d[8] = torch.argmax(drf[8], -1).to(torch.int32)
+    xd = dict(x, tgt=tgt, drf=drf, draft_tokens=d, draft_len=n)
+    res = dbv.verify_rejection(tgt.to(dev), drf.to(dev), d.to(dev), x["u_accept"].to(dev),
+                               x["u_resample"].to(dev), draft_len=n.to(dev))
+    xn = _np_inputs(xd)
+    o = oracle.verify_rejection(xn["tgt"], xn["drf"], xn["draft_tokens"], xn["draft_len"], 1.0, 1.0,
+                                xn["u_accept"], xn["u_resample"])
+    assert list(o["status"][:6]) == [1, 2, 4, 2, 0, 1] and o["status"][6] & oracle.STATUS_Q_ZERO
+    check_sampling(res, xn, o, 0.0, 1.0, 1.0, "float32")
+    g = dbv.verify_greedy(tgt.to(dev), d.to(dev), n.to(dev), drf.to(dev))
+    og = oracle.verify_greedy(xn["tgt"], xn["draft_tokens"], xn["draft_len"], xn["drf"])
+    check_greedy(g, og)
+
+
+@pytest.mark.parametrize("V", [1, 2, 3])
+def test_tiny_vocabulary(dev, V):
+    say("tiny V", V)
+    x = workloads.chain_inputs(81, 5, 3, V, torch.float32, sigma=1.0, random_lengths=True)
+    xd = _to(x, dev)
+    res = dbv.verify_rejection(xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"],
+                               draft_len=xd["draft_len"])
+    xn = _np_inputs(x)
+    o = oracle.verify_rejection(xn["tgt"], xn["drf"], xn["draft_tokens"], xn["draft_len"], 1.0, 1.0,
+                                xn["u_accept"], xn["u_resample"])
+    check_sampling(res, xn, o, 0.0, 1.0, 1.0, "float32")
+    g = dbv.verify_greedy(xd["tgt"], xd["draft_tokens"], xd["draft_len"], xd["drf"])
+    check_greedy(g, oracle.verify_greedy(xn["tgt"], xn["draft_tokens"], xn["draft_len"], xn["drf"]))
+
+
+def test_no_drafts(dev):
+    say("K=0, W=0")
+    x = workloads.chain_inputs(82, 4, 0, 5000, torch.bfloat16)
+    xd = _to(x, dev)
+    res = dbv.verify_rejection(xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"])
+    xn = _np_inputs(x)
+    o = oracle.verify_rejection(xn["tgt"], xn["drf"], xn["draft_tokens"], None, 1.0, 1.0,
+                                xn["u_accept"], xn["u_resample"])
+    check_sampling(res, xn, o, 0.0, 1.0, 1.0, "bfloat16")
+    g = dbv.verify_greedy(xd["tgt"], xd["draft_tokens"])
+    check_greedy(g, oracle.verify_greedy(xn["tgt"], xn["draft_tokens"]))
+
+
+def test_determinism(dev):
+    say("determinism")
+    x = _to(workloads.chain_inputs(83, 16, 8, 32000, torch.bfloat16, random_lengths=True), dev)
+    a = dbv.verify_rejection(x["tgt"], x["drf"], x["draft_tokens"], x["u_accept"], x["u_resample"],
+                             draft_len=x["draft_len"])
+    b = dbv.verify_rejection(x["tgt"], x["drf"], x["draft_tokens"], x["u_accept"], x["u_resample"],
+                             draft_len=x["draft_len"])
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+# -------------------------------------------------------------------- tree ---
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("T", [1.0, 0.7, 0.0])
+def test_tree_parity(dev, dtype, T):
+    say("tree", dtype, T)
+    x = workloads.tree_inputs(60, 3, 12, 6, 5003, dtype, sigma_node=0.05, temperature=T if T > 0 else 1.0)
+    g = dbv.verify_gumbel_tree(x["logits"].to(dev), x["parent"].to(dev), x["edge_pos"].to(dev),
+                               x["edge_tok"].to(dev), masked=x["masked"].to(dev),
+                               gumbel=x["gumbel"].to(dev) if T > 0 else None, temperature=T,
+                               num_states=x["num_states"].to(dev))
+    xn = _np_inputs(x)
+    xn["masked"] = x["masked"].numpy()
+    o = oracle.verify_gumbel_tree(xn["logits"], xn["masked"], xn["parent"], xn["edge_pos"], xn["edge_tok"],
+                                  xn["num_states"], xn["gumbel"], T)
+    near = check_tree(g, xn, o, str(dtype).split(".")[1], T)
+    say("near", dict(near), "path_len", list(o["path_len"]))
+
+
+def test_tree_fixed_position(dev):
+    say("tree fixed position")
+    x = workloads.tree_inputs(61, 2, 10, 5, 4001, torch.bfloat16, sigma_node=0.05)
+    g = torch.Generator().manual_seed(5)
+    nxt = torch.randint(-1, 5, (2, 10), generator=g).to(torch.int32)
+    r = dbv.verify_gumbel_tree(x["logits"].to(dev), x["parent"].to(dev), x["edge_pos"].to(dev),
+                               x["edge_tok"].to(dev), gumbel=x["gumbel"].to(dev), temperature=1.0,
+                               num_states=x["num_states"].to(dev), next_pos=nxt.to(dev),
+                               mode=dbv.DBV_TREE_FIXED_POSITION)
+    xn = _np_inputs(x)
+    o = oracle.verify_gumbel_tree(xn["logits"], None, xn["parent"], xn["edge_pos"], xn["edge_tok"],
+                                  xn["num_states"], xn["gumbel"], 1.0, oracle.TREE_FIXED_POSITION, npi(nxt))
+    check_tree(r, xn, o, "bfloat16", 1.0)
+
+
+def test_tree_orbit_and_edge_cases(dev):
+    say("tree orbit / edge cases")
+    # A chain tree that follows the oracle's own orbit is accepted to the end;
+    # a bad parent index and a NaN row are reported per sequence.
+    B, S, L, V = 3, 7, 6, 3000
+    gen = torch.Generator().manual_seed(11)
+    logits = (torch.randn(B, S, L, V, generator=gen) * 3).to(torch.bfloat16)
+    G = workloads.gumbel_noise((B, L, V), gen)
+    masked = torch.ones(B, S, L, dtype=torch.bool)
+    parent = torch.full((B, S), -1, dtype=torch.int32)
+    ep = torch.zeros(B, S, dtype=torch.int32)
+    et = torch.zeros(B, S, dtype=torch.int32)
+    ln = np64(logits)
+    Gn = G.numpy().astype(np.float64)
+    for b in range(B):
+        for z in range(1, S):
+            m = [s for s in range(L) if masked[b, z - 1, s]]
+            t = oracle.state_transition(ln[b, z - 1], m, Gn[b], 1.0)
+            parent[b, z] = z - 1
+            ep[b, z], et[b, z] = t["pos"], t["tok"]
+            masked[b, z] = masked[b, z - 1]
+            masked[b, z, t["pos"]] = False
+    parent[1, 3] = 5                       # child before parent: bad input
+    logits[2, 2, int(ep[2, 3]), 17] = float("nan")
+    ln = np64(logits)
+    r = dbv.verify_gumbel_tree(logits.to(dev), parent.to(dev), ep.to(dev), et.to(dev),
+                               masked=masked.to(dev), gumbel=G.to(dev), temperature=1.0)
+    o = oracle.verify_gumbel_tree(ln, masked.numpy(), npi(parent), npi(ep), npi(et), None, Gn, 1.0)
+    assert o["path_len"][0] == S - 1 and o["status"][1] == 1 and o["status"][2] == 2
+    check_tree(r, dict(logits=ln, gumbel=Gn, parent=npi(parent), edge_pos=npi(ep), edge_tok=npi(et),
+                       num_states=None), o, "bfloat16", 1.0)

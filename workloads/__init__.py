@@ -1,0 +1,228 @@
+"""Seeded synthetic inputs for draft-block verification.
+
+Shared by the tests, the smoke check and the benchmark.  This module holds no
+verification arithmetic: it only draws logits, uniforms, Gumbel noise, draft
+tokens and draft trees with torch's own random and sampling routines (the
+draft tokens stand in for a drafter's sampling, done with torch.multinomial /
+torch.argmax), so that the HIP path and the CPU oracle receive identical
+inputs.
+
+Seeds: base S0; stream j of configuration c uses S0 + 1000*c + j with
+  j = 0 target logits, 1 peak positions, 2 draft noise, 3 draft-sampling
+  uniforms, 4 accept uniforms, 5 resample uniforms, 6 Gumbel, 7 tree,
+  8 draft lengths / root masks.
+"""
+
+import math
+
+import torch
+
+S0 = 20261202
+
+
+def _gen(c, j, device="cpu"):
+    g = torch.Generator(device=device)
+    g.manual_seed(S0 + 1000 * c + j)
+    return g
+
+
+def _planted_logits(c, shape, peak, dtype, device="cpu"):
+    """z ~ N(0, 3^2) with +peak added at one seeded token per row."""
+    *lead, V = shape
+    z = torch.randn(*shape, generator=_gen(c, 0, device), device=device) * 3.0
+    if peak:
+        pos = torch.randint(0, V, (*lead, 1), generator=_gen(c, 1, device), device=device)
+        z.scatter_add_(-1, pos, torch.full((*lead, 1), float(peak), device=device))
+    return z.to(dtype)
+
+
+def chain_inputs(c, B, K, V, dtype=torch.bfloat16, sigma=1.0, temperature=1.0,
+                 peak=6.0, random_lengths=False, device="cpu"):
+    """Target rows [B, K+1, V], draft rows [B, K, V] = target + N(0, sigma^2)
+    (rounded to dtype), draft tokens sampled from softmax(draft / T), accept
+    and resample uniforms, and draft lengths."""
+    tgt = _planted_logits(c, (B, K + 1, V), peak, dtype, device)
+    noise = torch.randn(B, K, V, generator=_gen(c, 2, device), device=device) * sigma
+    drf = (tgt[:, :K].float() + noise).to(dtype)
+    if K > 0:
+        probs = torch.softmax(drf.float().reshape(B * K, V) / temperature, dim=-1)
+        d = torch.multinomial(probs, 1, generator=_gen(c, 3, device)).reshape(B, K)
+    else:
+        d = torch.zeros(B, 0, dtype=torch.int64, device=device)
+    u_acc = torch.rand(B, K, generator=_gen(c, 4, device), device=device)
+    u_res = torch.rand(B, K + 1, generator=_gen(c, 5, device), device=device)
+    if random_lengths:
+        n = torch.randint(0, K + 1, (B,), generator=_gen(c, 8, device), device=device)
+    else:
+        n = torch.full((B,), K, dtype=torch.int64, device=device)
+    return dict(tgt=tgt, drf=drf, draft_tokens=d.to(torch.int32), u_accept=u_acc,
+                u_resample=u_res, draft_len=n.to(torch.int32), temperature=temperature)
+
+
+# ------------------------------------------------------------------ configs --
+
+def config1(device="cpu"):
+    """Tiny rejection verify: B=1, K=4, V=1024, fp32, z ~ N(0,3^2) + 6 peak,
+    draft = z + N(0,1), T=1; greedy variant drafts argmax(draft)."""
+    x = chain_inputs(1, 1, 4, 1024, torch.float32, sigma=1.0, device=device)
+    x["greedy_tokens"] = torch.argmax(x["drf"].float(), dim=-1).to(torch.int32)
+    return x
+
+
+def config2(device="cpu"):
+    """Batch lossless verify: B=8, K=8, V=32000 bf16, draft noise 0.5, T=1."""
+    return chain_inputs(2, 8, 8, 32000, torch.bfloat16, sigma=0.5, device=device)
+
+
+C3_SIGMAS = (0.25, 1.0, 2.0)
+C3_TEMPS = (0.7, 1.0)
+C3_LAMBDAS = (1.0, 0.5, 0.25)
+
+
+def config3(sigma, temperature, device="cpu"):
+    """Lenient sweep setting: B=32, K=16, V=128256 bf16, draft noise sigma,
+    temperature T; the uniforms are common to every lambda."""
+    return chain_inputs(3, 32, 16, 128256, torch.bfloat16, sigma=sigma,
+                        temperature=temperature, device=device)
+
+
+def config5(device="cpu", B=64, K=32, V=131072):
+    """Packed greedy verify + draft: T[B, 2K, V] bf16; rows 0..K-1 are the
+    verifier rows (z ~ N(0,3^2) + peak), rows K..2K-1 the drafter rows
+    bf16(z + N(0,1)); K-1 drafts at most per sequence (the last verifier row
+    is the bonus row), n_b ~ U{0..K-1}; drafts d_i = argmax(z_i + N(0,1))
+    with independent noise (a stale previous draft)."""
+    c = 5
+    z = _planted_logits(c, (B, K, V), 6.0, torch.float32, device)
+    packed = torch.empty(B, 2 * K, V, dtype=torch.bfloat16, device=device)
+    packed[:, :K] = z.to(torch.bfloat16)
+    zb = packed[:, :K].float()
+    packed[:, K:] = (zb + torch.randn(B, K, V, generator=_gen(c, 2, device), device=device)).to(torch.bfloat16)
+    stale = zb[:, :K - 1] + torch.randn(B, K - 1, V, generator=_gen(c, 3, device), device=device)
+    d = torch.argmax(stale, dim=-1).to(torch.int32)
+    n = torch.randint(0, K, (B,), generator=_gen(c, 8, device), device=device).to(torch.int32)
+    return dict(packed=packed, tgt=packed[:, :K], draft_rows=packed[:, K:], draft_tokens=d,
+                draft_len=n, K=K - 1, W=K)
+
+
+# --------------------------------------------------------------------- tree --
+
+def gumbel_noise(shape, generator, device="cpu"):
+    """Gumbel(0,1) = -log(-log U) with U clamped to [2^-24, 1 - 2^-24]."""
+    u = torch.rand(*shape, generator=generator, device=device)
+    u = u.clamp(2.0 ** -24, 1.0 - 2.0 ** -24)
+    return -torch.log(-torch.log(u))
+
+
+def tree_inputs(c, B, S, L, V, dtype=torch.bfloat16, sigma_node=0.1, temperature=1.0,
+                max_depth=8, device="cpu", runner_up_below=0.6, order_temp=0.5):
+    """Draft trees grown by seeded prefix-mass sampling from root statistics.
+
+    Per sequence: c0 ~ U{0..L/2-1} committed positions at the root; root
+    logits Z0 [L, V] ~ N(0, 3^2); Gumbel table G [L, V].  Stand-in drafter:
+    position order q(s|y) = softmax over masked s of log conf0(s) / order_temp
+    with conf0 the root's max probability; token hypotheses = the coupled
+    stale draw argmax(Z0[s]/T + G[s]) plus the runner-up when conf0(s) <
+    runner_up_below; prefix mass m(z) = m(y) q(s|y) p0_s(v).  Nodes are added
+    by sampling candidates proportional to m without replacement (depth <=
+    max_depth, no duplicate children) until S nodes exist.  Node logits are
+    bf16(Z0 + sigma_node * sqrt(depth) * N(0,1)).
+    """
+    gt = _gen(c, 7, "cpu")
+    gm = _gen(c, 8, "cpu")
+    g0 = _gen(c, 0, device)
+    gG = _gen(c, 6, device)
+    gn = _gen(c, 2, device)
+    logits = torch.empty(B, S, L, V, dtype=dtype, device=device)
+    gumbel = torch.empty(B, L, V, dtype=torch.float32, device=device)
+    masked = torch.zeros(B, S, L, dtype=torch.bool)
+    parent = torch.full((B, S), -1, dtype=torch.int32)
+    epos = torch.zeros(B, S, dtype=torch.int32)
+    etok = torch.zeros(B, S, dtype=torch.int32)
+    depth = torch.zeros(B, S, dtype=torch.int32)
+    num_states = torch.zeros(B, dtype=torch.int32)
+    for b in range(B):
+        z0 = (torch.randn(L, V, generator=g0, device=device) * 3.0).to(dtype)
+        G = gumbel_noise((L, V), gG, device)
+        gumbel[b] = G
+        zf = z0.float()
+        p0 = torch.softmax(zf / temperature if temperature > 0 else zf, dim=-1)
+        conf0 = torch.softmax(zf, dim=-1).max(dim=-1).values.cpu().double()
+        score = zf / temperature + G if temperature > 0 else zf
+        top2 = torch.topk(score, 2, dim=-1).indices.cpu()
+        ptop = torch.gather(p0, 1, top2.to(p0.device)).cpu().double()
+        n0 = int(torch.randint(0, L // 2, (1,), generator=gm))
+        committed = torch.randperm(L, generator=gm)[:n0]
+        root_mask = torch.ones(L, dtype=torch.bool)
+        root_mask[committed] = False
+
+        states = [root_mask.clone()]
+        mass = [1.0]
+        nd = [0]
+        kids = [set()]
+        cand = {}
+
+        def add_candidates(y):
+            m = states[y]
+            pos = torch.nonzero(m).flatten().tolist()
+            if not pos or nd[y] >= max_depth:
+                return
+            w = torch.tensor([math.log(conf0[s]) / order_temp for s in pos], dtype=torch.float64)
+            qpos = torch.softmax(w, dim=0).tolist()
+            for s, qs in zip(pos, qpos):
+                toks = [int(top2[s, 0])]
+                ps = [float(ptop[s, 0])]
+                if conf0[s] < runner_up_below:
+                    toks.append(int(top2[s, 1]))
+                    ps.append(float(ptop[s, 1]))
+                for v, pv in zip(toks, ps):
+                    cand[(y, s, v)] = mass[y] * qs * pv
+
+        add_candidates(0)
+        while len(states) < S and cand:
+            keys = list(cand.keys())
+            w = torch.tensor([cand[k] for k in keys], dtype=torch.float64)
+            w = w / w.sum()
+            k = keys[int(torch.multinomial(w, 1, generator=gt))]
+            mz = cand.pop(k)
+            y, s, v = k
+            if (s, v) in kids[y]:
+                continue
+            kids[y].add((s, v))
+            z = len(states)
+            st = states[y].clone()
+            st[s] = False
+            states.append(st)
+            mass.append(mz)
+            nd.append(nd[y] + 1)
+            kids.append(set())
+            parent[b, z] = y
+            epos[b, z] = s
+            etok[b, z] = v
+            add_candidates(z)
+        ns = len(states)
+        num_states[b] = ns
+        # Unused slots (z >= num_states) are ignored by the verifier.
+        for z in range(ns, S):
+            states.append(root_mask.clone())
+            nd.append(0)
+            parent[b, z] = 0
+        for z in range(S):
+            masked[b, z] = states[z]
+            depth[b, z] = nd[z]
+        # node logits
+        for z in range(S):
+            if z == 0:
+                logits[b, 0] = z0
+            else:
+                eps = torch.randn(L, V, generator=gn, device=device)
+                logits[b, z] = (zf + sigma_node * math.sqrt(float(nd[z])) * eps).to(dtype)
+    return dict(logits=logits, gumbel=gumbel, masked=masked, parent=parent, edge_pos=epos,
+                edge_tok=etok, depth=depth, num_states=num_states, temperature=temperature)
+
+
+def config4(device="cpu", sigma_node=0.1, B=16, S=64, L=32, V=151936):
+    """Coupled-Gumbel tree verify: B=16 trees of S=64 states, block L=32,
+    V=151936 bf16, T=1."""
+    return tree_inputs(4, B, S, L, V, torch.bfloat16, sigma_node=sigma_node,
+                       temperature=1.0, device=device)
