@@ -19,6 +19,8 @@ using dbv::kMaxDraft;
 using dbv::kMaxStates;
 
 constexpr int kMaxDevices = 64;
+// Compute units per device, filled with the architecture check.
+std::atomic<int> g_cus[kMaxDevices];
 // Diagnostics events (verify_set_timing_events); off when NULL.
 std::atomic<void*> g_ev_begin{nullptr};
 std::atomic<void*> g_ev_end{nullptr};
@@ -52,11 +54,20 @@ dbv_status device_ready() {
       hipDeviceProp_t prop;
       if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DBV_ERR_NO_DEVICE;
       s = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+      g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
       g_arch[dev].store(s, std::memory_order_relaxed);
     }
     if (s != 1) return DBV_ERR_NO_DEVICE;
   }
   return DBV_OK;
+}
+
+dbv::RowItems items_of(const dbv::RowPlan& r) {
+  dbv::RowItems it;
+  it.chunk = r.chunk;
+  it.nchunk = r.nchunk;
+  it.items = r.items;
+  return it;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -81,6 +92,7 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
                          float* q_draft, float* alpha, float* residual_mass, int32_t* status, void* ws,
                          size_t ws_bytes, void* stream) {
   if (B < 0 || K < 0 || K > kMaxDraft || V < 1 || !dtype_ok(dtype)) return DBV_ERR_INVALID_ARG;
+  if (V > dbv::kMaxSampleV) return DBV_ERR_UNSUPPORTED;
   if (!temp_ok(tt) || !temp_ok(td) || !(lam >= 0.f && lam <= 1.f)) return DBV_ERR_INVALID_ARG;
   if (ts < 0 || tr < 0 || ds < 0 || dr < 0) return DBV_ERR_INVALID_ARG;
   if (tgt == nullptr || u_resample == nullptr) return DBV_ERR_INVALID_ARG;
@@ -89,6 +101,7 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   const size_t eb = elem_bytes(dtype);
   if (!aligned(tgt, eb) || (drf && !aligned(drf, eb))) return DBV_ERR_INVALID_ARG;
   const dbv::SamplePlan plan = dbv::plan_sample(B, K, V);
+  if (plan.r.items >= (int64_t(1) << 31)) return DBV_ERR_UNSUPPORTED;
   dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
   if (s != DBV_OK) return s;
   if ((s = device_ready()) != DBV_OK) return s;
@@ -110,12 +123,29 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.stats = reinterpret_cast<float2*>(w + plan.off_stats);
   a.rec = reinterpret_cast<dbv::DrawRecord*>(w + plan.off_rec);
   a.dsum = reinterpret_cast<float*>(w + plan.off_dsum);
-  a.split = plan.split; a.chunk = plan.chunk;
+  a.it = items_of(plan.r);
   a.draw_chunks = plan.draw_chunks; a.draw_chunk = plan.draw_chunk;
   return dbv::launch_sample(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
 }
 
 }  // namespace
+
+namespace dbv {
+
+// Resident groups of the current device (kResidentPerCU per CU), at most the
+// number of items.
+int64_t persistent_grid(int64_t items) {
+  int dev = 0;
+  int cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) cus = c;
+  }
+  const int64_t g = static_cast<int64_t>(cus) * kResidentPerCU;
+  return items < g ? items : g;
+}
+
+}  // namespace dbv
 
 extern "C" {
 
@@ -135,6 +165,7 @@ dbv_status verify_greedy(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   const size_t eb = elem_bytes(dtype);
   if (!aligned(tgt, eb) || (draft_rows && !aligned(draft_rows, eb))) return DBV_ERR_INVALID_ARG;
   const dbv::GreedyPlan plan = dbv::plan_greedy(B, K, W, V);
+  if (plan.r.items >= (int64_t(1) << 31)) return DBV_ERR_UNSUPPORTED;
   dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
   if (s != DBV_OK) return s;
   if ((s = device_ready()) != DBV_OK) return s;
@@ -149,7 +180,7 @@ dbv_status verify_greedy(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.accept_len = accept_len; a.out_tokens = out_tokens; a.num_out = num_out;
   a.next_draft = next_draft; a.next_len = next_len; a.status = status;
   a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + plan.off_part);
-  a.split = plan.split; a.chunk = plan.chunk;
+  a.it = items_of(plan.r);
   return dbv::launch_greedy(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
 }
 
@@ -204,6 +235,7 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const
     return DBV_ERR_INVALID_ARG;
   if (!aligned(logits, elem_bytes(dtype)) || (gumbel && !aligned(gumbel, 4))) return DBV_ERR_INVALID_ARG;
   const dbv::TreePlan plan = dbv::plan_tree(B, S, L, V);
+  if (plan.r.items >= (int64_t(1) << 31)) return DBV_ERR_UNSUPPORTED;
   dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
   if (s != DBV_OK) return s;
   if ((s = device_ready()) != DBV_OK) return s;
@@ -225,7 +257,7 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const
   a.conf = reinterpret_cast<float2*>(w + plan.off_conf);
   a.pick = reinterpret_cast<float2*>(w + plan.off_pick);
   a.sel = reinterpret_cast<int32_t*>(w + plan.off_sel);
-  a.split1 = plan.split1; a.chunk1 = plan.chunk1;
+  a.it = items_of(plan.r);
   a.split2 = plan.split2; a.chunk2 = plan.chunk2;
   return dbv::launch_tree(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
 }

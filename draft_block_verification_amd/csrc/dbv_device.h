@@ -101,6 +101,10 @@ __device__ __forceinline__ void stream_row(const void* row, int64_t v0, int64_t 
     u32x4 r[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) r[u] = load16(vb + (i + u * kBlock) * 16);
+    // Keep all U loads in flight before any of them is consumed: without this
+    // barrier the scheduler hoists the first unpack above the later loads and
+    // waits on the first load alone.
+    __builtin_amdgcn_sched_barrier(0);
     float x[U * W];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -111,10 +115,20 @@ __device__ __forceinline__ void stream_row(const void* row, int64_t v0, int64_t 
     }
     op.template block<U, W>(x, a0 + i * W, static_cast<int64_t>(kBlock) * W);
   }
-  for (; i < nvec; i += kBlock) {
-    float y[W];
-    E::unpack(load16(vb + i * 16), y);
-    op.template group<W>(y, a0 + i * W);
+  if (i < nvec) {  // the last (< U) vectors of this lane, loads issued together
+    u32x4 r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + u * kBlock < nvec) r[u] = load16(vb + (i + u * kBlock) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i + u * kBlock < nvec) {
+        float y[W];
+        E::unpack(r[u], y);
+        op.template group<W>(y, a0 + (i + u * kBlock) * W);
+      }
+    }
   }
   if (a1 + t < v1) {
     float x[1] = {E::load1(row, a1 + t)};
@@ -164,13 +178,13 @@ __device__ __forceinline__ void stats_merge(float& M, float& S, float M2, float 
 }
 
 // ---------------------------------------------------------------------------
-// Lowest-index argmax of a score.  Per lane: the group holding the lane's
-// first occurrence of its maximum is remembered; its exact index is resolved
-// afterwards by re-evaluating the score of at most kVec elements.
+// Lowest-index argmax of a score.  Per lane, a group whose maximum beats the
+// lane's best (rare after the first few groups) also records the exact
+// position of its first maximal element, so no element is ever re-read.
 // ---------------------------------------------------------------------------
 struct ArgmaxPick {
   float best = -kInf;
-  int64_t gidx = -1;
+  int64_t bidx = -1;
   bool nan = false;
 
   template <int N>
@@ -179,7 +193,14 @@ struct ArgmaxPick {
 #pragma unroll
     for (int j = 1; j < N; ++j) m = fmaxp(m, x[j]);
     nan |= (m != m);
-    if (m > best || (gidx < 0 && m == best)) { best = m; gidx = idx0; }
+    if (m > best || (bidx < 0 && m == best)) {
+      int j0 = 0;
+#pragma unroll
+      for (int j = N - 1; j >= 0; --j)
+        if (x[j] == m) j0 = j;
+      best = m;
+      bidx = idx0 + j0;
+    }
   }
   template <int U, int W>
   __device__ __forceinline__ void block(const float* x, int64_t idx0, int64_t ustride) {
@@ -187,16 +208,6 @@ struct ArgmaxPick {
     for (int u = 0; u < U; ++u) group<W>(x + u * W, idx0 + u * ustride);
   }
 };
-
-// Exact index of `best` inside the remembered group: the first element at or
-// after gidx (within kVec, below v1) whose score equals best.
-template <int DT, class ScoreFn>
-__device__ __forceinline__ int64_t resolve_argmax(const ArgmaxPick& a, int64_t v1, ScoreFn score) {
-  if (a.gidx < 0) return -1;
-  for (int j = 0; j < Elem<DT>::kVec && a.gidx + j < v1; ++j)
-    if (score(a.gidx + j) == a.best) return a.gidx + j;
-  return a.gidx;  // unreachable: the group's maximum is one of its elements
-}
 
 // ------------------------------------------------------------ reductions ---
 
@@ -260,6 +271,121 @@ __device__ __forceinline__ float block_sum(float v, float* s) {
     for (int j = 0; j < kWaves; ++j) r += s[j];
   }
   return r;
+}
+
+// Wave-level (M, S) reduction; every lane ends with the wave's result.
+__device__ __forceinline__ void wave_stats(float& M, float& S, float k) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float M2 = wave_shfl_xor(M, m);
+    const float S2 = wave_shfl_xor(S, m);
+    stats_merge(M, S, M2, S2, k);
+  }
+}
+
+// Wave-level argmax reduction; every lane ends with the wave's result.
+__device__ __forceinline__ void wave_argmax(float& v, int& idx, int& nan) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float v2 = wave_shfl_xor(v, m);
+    const int i2 = wave_shfl_xor(idx, m);
+    const int n2 = wave_shfl_xor(nan, m);
+    if (pick_better(v2, i2, v, idx)) { v = v2; idx = i2; }
+    nan |= n2;
+  }
+}
+
+// Persistent grid-stride loop over work items.  The validity of the next item
+// (usually one small load) is requested before the current item is streamed,
+// so skipped items cost no exposed latency.
+// Item indices are 32-bit (the host keeps plans below 2^31 items): 64-bit
+// integer division is a long software sequence on this GPU.
+template <class ValidFn, class BodyFn>
+__device__ __forceinline__ void for_items(uint32_t items, ValidFn valid, BodyFn body) {
+  uint32_t it = blockIdx.x;
+  bool ok = it < items && valid(it);
+  while (it < items) {
+    const uint32_t nx = it + gridDim.x;
+    const bool nok = nx < items && valid(nx);
+    if (ok) body(it);
+    it = nx;
+    ok = nok;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combining the per-(item, wave) partials of many rows inside one group:
+// kRowLanes lanes share a row, each loading up to kRowLoads of its partials
+// before merging (the loads are issued together), then a shuffle tree over
+// the row's lanes.  Calls fn(row, lane-0 result) once per row.
+// ---------------------------------------------------------------------------
+constexpr int kRowLanes = 8;
+constexpr int kRowLoads = 8;
+
+template <class PartFn, class DoneFn>
+__device__ __forceinline__ void combine_rows_stats(int nrows, int64_t per_row, float k, PartFn part,
+                                                   DoneFn done) {
+  const int sub = threadIdx.x % kRowLanes;
+  for (int r0 = 0; r0 < nrows; r0 += kBlock / kRowLanes) {
+    const int r = r0 + static_cast<int>(threadIdx.x) / kRowLanes;
+    float M = -kInf, S = 0.f;
+    if (r < nrows) {
+      const float2* p = part(r);
+      for (int64_t j0 = 0; j0 < per_row; j0 += kRowLanes * kRowLoads) {
+        float2 buf[kRowLoads];
+#pragma unroll
+        for (int q = 0; q < kRowLoads; ++q) {
+          const int64_t j = j0 + sub + static_cast<int64_t>(q) * kRowLanes;
+          buf[q] = j < per_row ? p[j] : make_float2(-kInf, 0.f);
+        }
+#pragma unroll
+        for (int q = 0; q < kRowLoads; ++q) stats_merge(M, S, buf[q].x, buf[q].y, k);
+      }
+    }
+#pragma unroll
+    for (int m = kRowLanes / 2; m >= 1; m >>= 1) {
+      const float M2 = __shfl_xor(M, m, 64);
+      const float S2 = __shfl_xor(S, m, 64);
+      stats_merge(M, S, M2, S2, k);
+    }
+    if (r < nrows && sub == 0) done(r, M, S);
+  }
+}
+
+template <class PartFn, class DoneFn>
+__device__ __forceinline__ void combine_rows_pick(int nrows, int64_t per_row, PartFn part, DoneFn done) {
+  const int sub = threadIdx.x % kRowLanes;
+  for (int r0 = 0; r0 < nrows; r0 += kBlock / kRowLanes) {
+    const int r = r0 + static_cast<int>(threadIdx.x) / kRowLanes;
+    float v = -kInf;
+    int idx = -1, nan = 0;
+    if (r < nrows) {
+      const float2* p = part(r);
+      for (int64_t j0 = 0; j0 < per_row; j0 += kRowLanes * kRowLoads) {
+        float2 buf[kRowLoads];
+#pragma unroll
+        for (int q = 0; q < kRowLoads; ++q) {
+          const int64_t j = j0 + sub + static_cast<int64_t>(q) * kRowLanes;
+          buf[q] = j < per_row ? p[j] : make_float2(-kInf, __int_as_float(-1));
+        }
+#pragma unroll
+        for (int q = 0; q < kRowLoads; ++q) {
+          const int i2 = __float_as_int(buf[q].y);
+          if (buf[q].x != buf[q].x) nan = 1;
+          else if (pick_better(buf[q].x, i2, v, idx)) { v = buf[q].x; idx = i2; }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = kRowLanes / 2; m >= 1; m >>= 1) {
+      const float v2 = __shfl_xor(v, m, 64);
+      const int i2 = __shfl_xor(idx, m, 64);
+      const int n2 = __shfl_xor(nan, m, 64);
+      if (pick_better(v2, i2, v, idx)) { v = v2; idx = i2; }
+      nan |= n2;
+    }
+    if (r < nrows && sub == 0) done(r, v, idx, nan);
+  }
 }
 
 // Row status from a reduced maximum: NaN / +inf -> nonfinite, -inf -> empty.

@@ -8,6 +8,14 @@
 
 namespace dbv {
 
+// Items of a persistent row-streaming launch: `rows` rows of `nchunk`
+// vocabulary chunks of `chunk` elements; item = row * nchunk + chunk index.
+struct RowItems {
+  int64_t chunk;
+  int64_t nchunk;
+  int64_t items;
+};
+
 struct GreedyArgs {
   int B, K, V, W;
   const void* tgt; int64_t ts, tr;     // target rows: element strides
@@ -18,9 +26,8 @@ struct GreedyArgs {
   const int32_t* budget;
   int32_t* accept_len; int32_t* out_tokens; int32_t* num_out;
   int32_t* next_draft; int32_t* next_len; int32_t* status;
-  float2* part;
-  int split;
-  int64_t chunk;
+  float2* part;                        // per (item, wave)
+  RowItems it;
 };
 
 struct SampleArgs {
@@ -37,11 +44,10 @@ struct SampleArgs {
   int32_t* accept_len; int32_t* out_tokens; int32_t* num_out;
   float* p_draft; float* q_draft; float* alpha; float* residual_mass;
   int32_t* status;
-  float2* stats;
-  DrawRecord* rec;
-  float* dsum;
-  int split;
-  int64_t chunk;
+  float2* stats;                       // per (item, wave)
+  DrawRecord* rec;                     // per sequence
+  float* dsum;                         // per (sequence, draw chunk)
+  RowItems it;
   int draw_chunks;
   int64_t draw_chunk;
 };
@@ -59,10 +65,10 @@ struct TreeArgs {
   int32_t* path_len; int32_t* path_nodes;
   int32_t* commit_pos; int32_t* commit_tok; int32_t* num_commits;
   int32_t* status;
-  float2* conf;
-  float2* pick;
-  int32_t* sel;
-  int split1; int64_t chunk1;
+  float2* conf;                              // per (item, wave)
+  float2* pick;                              // per (state, split2)
+  int32_t* sel;                              // per state
+  RowItems it;
   int split2; int64_t chunk2;
 };
 
@@ -71,6 +77,9 @@ struct TimingEvents {
   hipEvent_t begin = nullptr;
   hipEvent_t end = nullptr;
 };
+
+// Grid of a persistent launch: at most the resident groups of the device.
+int64_t persistent_grid(int64_t items);
 
 bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
 bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);

@@ -2,16 +2,18 @@
 // rejection / linear-lenient sampler with its correction or bonus draw.
 //
 // Greedy  (Packed-SS, Sec. 3.1, Eq. 1-4, Algorithm 1):
-//   k_greedy_rows      split-V argmax of every needed target / draft row
+//   k_greedy_rows      persistent: argmax partials of every needed target /
+//                      drafter row, per (row, vocabulary chunk, wave)
 //   k_greedy_finalize  per sequence: combine, leading matches h, C, ending
 //                      condition a, next draft z_{a+1..W}
 // Sampling (Packed-SS, Algorithm 2; Two Tradeoffs, Theorem 1, Algorithm 1):
-//   k_sample_rows      split-V online softmax statistics (M, S) per row
-//   k_sample_decide    per sequence: p(d), q(d), the acceptance tests, h,
-//                      which row the draw uses
-//   k_draw_partial     split-V mass of [p - q]_+ (or of p for the bonus)
-//   k_draw_select      per sequence: chunk holding u*Z, in-chunk scan in
-//                      vocabulary order, output assembly
+//   k_sample_rows      persistent: online softmax statistics (M, S) partials
+//   k_draw_mass        per (sequence, vocabulary chunk): the sequence's
+//                      decision (p(d), q(d), the acceptance tests, h) and the
+//                      chunk's mass of [p - q]_+ (or of p for the bonus)
+//   k_draw_select      per sequence: the token where the running mass first
+//                      exceeds u*Z (vocabulary order), output assembly.
+// The kernel boundaries are the only cross-group synchronisation.
 #include "dbv_device.h"
 #include "dbv_launch.h"
 
@@ -27,61 +29,57 @@ __device__ __forceinline__ int draft_count(const int32_t* draft_len, int b, int 
   return bad ? 0 : n;
 }
 
-__device__ __forceinline__ float2 pack_pick(float v, int idx, int nan) {
-  return make_float2(nan ? __builtin_nanf("") : v, __int_as_float(idx));
-}
-
-// Combine the split partials of one argmax row.  Returns the index and ORs
-// the row's status into st.
-__device__ __forceinline__ int combine_pick(const float2* part, int split, int& st) {
-  float v = -kInf;
-  int idx = -1;
-  int nan = 0;
-  for (int s = 0; s < split; ++s) {
-    const float2 p = part[s];
-    const int i2 = __float_as_int(p.y);
-    if (p.x != p.x) { nan = 1; continue; }
-    if (pick_better(p.x, i2, v, idx)) { v = p.x; idx = i2; }
-  }
-  if (nan) st |= SEQ_NONFINITE;
-  else st |= max_status(v);
-  return idx;
-}
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // ================================================================ greedy ===
 
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k_greedy_rows(GreedyArgs a) {
-  __shared__ float s_v[kWaves];
-  __shared__ int s_i[kWaves], s_n[kWaves];
-  const int64_t gid = blockIdx.x;
-  const int64_t row = gid / a.split;
-  const int sp = static_cast<int>(gid % a.split);
-  const int64_t ntr = static_cast<int64_t>(a.B) * (a.K + 1);
-  const char* rowp;
+__device__ __forceinline__ const char* greedy_row(const GreedyArgs& a, uint32_t row, bool& need) {
+  const uint32_t K1 = static_cast<uint32_t>(a.K + 1);
+  const uint32_t ntr = static_cast<uint32_t>(a.B) * K1;
   if (row < ntr) {
-    const int b = static_cast<int>(row / (a.K + 1));
-    const int i = static_cast<int>(row % (a.K + 1));
+    const uint32_t b = row / K1;
+    const int i = static_cast<int>(row - b * K1);
     bool bad;
-    const int n = draft_count(a.draft_len, b, a.K, bad);
-    if (bad || i > n) return;  // row is not read
-    rowp = static_cast<const char*>(a.tgt) + (b * a.ts + i * a.tr) * Elem<DT>::kBytes;
-  } else {
-    const int64_t r = row - ntr;
-    const int b = static_cast<int>(r / a.W);
-    const int j = static_cast<int>(r % a.W);
-    rowp = static_cast<const char*>(a.dr) + (b * a.ds + j * a.drr) * Elem<DT>::kBytes;
+    const int n = draft_count(a.draft_len, static_cast<int>(b), a.K, bad);
+    need = !bad && i <= n;
+    return static_cast<const char*>(a.tgt) + (static_cast<int64_t>(b) * a.ts + i * a.tr) * Elem<DT>::kBytes;
   }
-  const int64_t v0 = static_cast<int64_t>(sp) * a.chunk;
-  const int64_t v1 = v0 + a.chunk < a.V ? v0 + a.chunk : a.V;
-  ArgmaxPick pk;
-  stream_row<DT, kUnroll>(rowp, v0, v1, pk);
-  const int64_t idx = resolve_argmax<DT>(pk, v1, [&](int64_t j) { return Elem<DT>::load1(rowp, j); });
-  float v = pk.best;
-  int ii = static_cast<int>(idx);
-  int nan = pk.nan ? 1 : 0;
-  block_argmax(v, ii, nan, s_v, s_i, s_n);
-  if (threadIdx.x == 0) a.part[gid] = pack_pick(v, ii, nan);
+  const uint32_t r = row - ntr;
+  const uint32_t W = static_cast<uint32_t>(a.W);
+  const uint32_t b = r / W;
+  const int j = static_cast<int>(r - b * W);
+  need = true;
+  return static_cast<const char*>(a.dr) + (static_cast<int64_t>(b) * a.ds + j * a.drr) * Elem<DT>::kBytes;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_greedy_rows(GreedyArgs a) {
+  const uint32_t nchunk = static_cast<uint32_t>(a.it.nchunk);
+  const int64_t chunk = a.it.chunk;
+  for_items(
+      static_cast<uint32_t>(a.it.items),
+      [&](uint32_t item) {
+        bool need;
+        greedy_row<DT>(a, item / nchunk, need);
+        return need;
+      },
+      [&](uint32_t item) {
+        bool need;
+        const uint32_t row = item / nchunk;
+        const char* rowp = greedy_row<DT>(a, row, need);
+        const int64_t v0 = static_cast<int64_t>(item - row * nchunk) * chunk;
+        const int64_t v1 = v0 + chunk < a.V ? v0 + chunk : a.V;
+        ArgmaxPick pk;
+        stream_row<DT, kUnroll>(rowp, v0, v1, pk);
+        float v = pk.best;
+        int ii = static_cast<int>(pk.bidx);
+        int nan = pk.nan ? 1 : 0;
+        wave_argmax(v, ii, nan);
+        if (lane_id() == 0)
+          a.part[static_cast<int64_t>(item) * kWaves + wave_id()] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
+      });
 }
 
 __global__ __launch_bounds__(kBlock) void k_greedy_finalize(GreedyArgs a) {
@@ -90,6 +88,7 @@ __global__ __launch_bounds__(kBlock) void k_greedy_finalize(GreedyArgs a) {
   __shared__ int s_st, s_h, s_a;
   const int b = blockIdx.x;
   const int t = threadIdx.x;
+  const int64_t per_row = a.it.nchunk * kWaves;
   bool nbad;
   const int n = draft_count(a.draft_len, b, a.K, nbad);
   const int budget = a.budget ? a.budget[b] : INT_MAX;
@@ -105,12 +104,20 @@ __global__ __launch_bounds__(kBlock) void k_greedy_finalize(GreedyArgs a) {
     if (di < 0 || di >= a.V) st |= SEQ_BAD_INPUT;
   }
   const int64_t ntr = static_cast<int64_t>(a.B) * (a.K + 1);
-  if (!nbad) {
-    for (int i = t; i <= n; i += kBlock)
-      s_v[i] = combine_pick(a.part + (static_cast<int64_t>(b) * (a.K + 1) + i) * a.split, a.split, st);
-  }
-  for (int j = t; j < a.W; j += kBlock)
-    s_z[j] = combine_pick(a.part + (ntr + static_cast<int64_t>(b) * a.W + j) * a.split, a.split, st);
+  // Rows 0..n of the target, then the W drafter rows.
+  const int nt = nbad ? 0 : n + 1;
+  combine_rows_pick(
+      nt + a.W, per_row,
+      [&](int r) {
+        const int64_t row = r < nt ? static_cast<int64_t>(b) * (a.K + 1) + r
+                                   : ntr + static_cast<int64_t>(b) * a.W + (r - nt);
+        return a.part + row * per_row;
+      },
+      [&](int r, float v, int idx, int nan) {
+        st |= nan ? SEQ_NONFINITE : max_status(v);
+        if (r < nt) s_v[r] = idx;
+        else s_z[r - nt] = idx;
+      });
   if (st) atomicOr(&s_st, st);
   __syncthreads();
   const int status = s_st;
@@ -158,142 +165,53 @@ __global__ __launch_bounds__(kBlock) void k_greedy_finalize(GreedyArgs a) {
 // ============================================================== sampling ===
 
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
-  __shared__ float s_m[kWaves], s_s[kWaves];
-  const int64_t gid = blockIdx.x;
-  const int64_t row = gid / a.split;
-  const int sp = static_cast<int>(gid % a.split);
-  const int64_t ntr = static_cast<int64_t>(a.B) * (a.K + 1);
-  const char* rowp;
-  float k;
+__device__ __forceinline__ const char* sample_row(const SampleArgs& a, uint32_t row, bool& need, float& k) {
+  const uint32_t K1 = static_cast<uint32_t>(a.K + 1);
+  const uint32_t ntr = static_cast<uint32_t>(a.B) * K1;
   bool bad;
   if (row < ntr) {
-    const int b = static_cast<int>(row / (a.K + 1));
-    const int i = static_cast<int>(row % (a.K + 1));
-    const int n = draft_count(a.draft_len, b, a.K, bad);
-    if (bad || i > n) return;
-    rowp = static_cast<const char*>(a.tgt) + (b * a.ts + i * a.tr) * Elem<DT>::kBytes;
+    const uint32_t b = row / K1;
+    const int i = static_cast<int>(row - b * K1);
+    const int n = draft_count(a.draft_len, static_cast<int>(b), a.K, bad);
+    need = !bad && i <= n;
     k = a.kp;
-  } else {
-    const int64_t r = row - ntr;
-    const int b = static_cast<int>(r / a.K);
-    const int i = static_cast<int>(r % a.K);
-    const int n = draft_count(a.draft_len, b, a.K, bad);
-    if (bad || i >= n) return;
-    rowp = static_cast<const char*>(a.drf) + (b * a.ds + i * a.dr) * Elem<DT>::kBytes;
-    k = a.kq;
+    return static_cast<const char*>(a.tgt) + (static_cast<int64_t>(b) * a.ts + i * a.tr) * Elem<DT>::kBytes;
   }
-  const int64_t v0 = static_cast<int64_t>(sp) * a.chunk;
-  const int64_t v1 = v0 + a.chunk < a.V ? v0 + a.chunk : a.V;
-  SoftmaxStats st(k);
-  stream_row<DT, kUnroll>(rowp, v0, v1, st);
-  float M = st.M, S = st.S;
-  block_stats(M, S, k, s_m, s_s);
-  if (threadIdx.x == 0) a.stats[gid] = make_float2(M, S);
-}
-
-__device__ __forceinline__ void combine_stats(const float2* part, int split, float k, float& M, float& S) {
-  M = -kInf;
-  S = 0.f;
-  for (int s = 0; s < split; ++s) stats_merge(M, S, part[s].x, part[s].y, k);
+  const uint32_t r = row - ntr;
+  const uint32_t K = static_cast<uint32_t>(a.K);
+  const uint32_t b = r / K;
+  const int i = static_cast<int>(r - b * K);
+  const int n = draft_count(a.draft_len, static_cast<int>(b), a.K, bad);
+  need = !bad && i < n;
+  k = a.kq;
+  return static_cast<const char*>(a.drf) + (static_cast<int64_t>(b) * a.ds + i * a.dr) * Elem<DT>::kBytes;
 }
 
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k_sample_decide(SampleArgs a) {
-  __shared__ float s_Mp[kMaxDraft + 1], s_Sp[kMaxDraft + 1];
-  __shared__ float s_Mq[kMaxDraft], s_Sq[kMaxDraft];
-  __shared__ int s_st, s_h;
-  const int b = blockIdx.x;
-  const int t = threadIdx.x;
-  bool nbad;
-  const int n = draft_count(a.draft_len, b, a.K, nbad);
-  const int budget = a.budget ? a.budget[b] : INT_MAX;
-  if (t == 0) {
-    s_st = (nbad || budget < 0) ? SEQ_BAD_INPUT : 0;
-    s_h = n;
-  }
-  __syncthreads();
-  const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
-  const int64_t ntr = static_cast<int64_t>(a.B) * (a.K + 1);
-  int st = 0;
-  for (int i = t; i < n; i += kBlock) {
-    const int di = d[i];
-    if (di < 0 || di >= a.V) st |= SEQ_BAD_INPUT;
-  }
-  if (!nbad) {
-    for (int i = t; i <= n; i += kBlock) {
-      float M, S;
-      combine_stats(a.stats + (static_cast<int64_t>(b) * (a.K + 1) + i) * a.split, a.split, a.kp, M, S);
-      s_Mp[i] = M; s_Sp[i] = S;
-      st |= stats_status(M, S);
-    }
-    for (int i = t; i < n; i += kBlock) {
-      float M, S;
-      combine_stats(a.stats + (ntr + static_cast<int64_t>(b) * a.K + i) * a.split, a.split, a.kq, M, S);
-      s_Mq[i] = M; s_Sq[i] = S;
-      st |= stats_status(M, S);
-    }
-  }
-  if (st) atomicOr(&s_st, st);
-  __syncthreads();
-  int status = s_st;
-  DrawRecord* rec = a.rec + b;
-  if (status & SEQ_ERROR_MASK) {
-    int32_t* out = a.out_tokens + static_cast<int64_t>(b) * (a.K + 1);
-    for (int i = t; i <= a.K; i += kBlock) out[i] = -1;
-    for (int i = t; i < a.K; i += kBlock) {
-      const int64_t o = static_cast<int64_t>(b) * a.K + i;
-      if (a.p_draft) a.p_draft[o] = 0.f;
-      if (a.q_draft) a.q_draft[o] = 0.f;
-      if (a.alpha) a.alpha[o] = 0.f;
-    }
-    if (t == 0) {
-      a.accept_len[b] = -1;
-      a.num_out[b] = 0;
-      if (a.residual_mass) a.residual_mass[b] = 0.f;
-      if (a.status) a.status[b] = status;
-      rec->kind = -1;
-    }
-    return;
-  }
-  // Acceptance tests: accept d_i iff u_i * q_i(d_i) < p~_i(d_i).
-  const float lam = a.lam, oml = 1.f - a.lam;
-  int qz = 0;
-  for (int i = t; i < a.K; i += kBlock) {
-    float p = 0.f, q = 0.f, al = 0.f;
-    if (i < n) {
-      const int di = d[i];
-      const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + i * a.tr) * Elem<DT>::kBytes;
-      const char* yr = static_cast<const char*>(a.drf) + (b * a.ds + i * a.dr) * Elem<DT>::kBytes;
-      const float x = Elem<DT>::load1(xr, di);
-      const float y = Elem<DT>::load1(yr, di);
-      p = fast_exp2(__builtin_fmaf(x, a.kp, -s_Mp[i] * a.kp)) / s_Sp[i];
-      q = fast_exp2(__builtin_fmaf(y, a.kq, -s_Mq[i] * a.kq)) / s_Sq[i];
-      const float pt = oml * p + lam * q;
-      const float u = a.u_accept[static_cast<int64_t>(b) * a.K + i];
-      const bool acc = u * q < pt;
-      if (q == 0.f && pt > 0.f) qz = 1;
-      al = q > 0.f ? fminf(1.f, pt / q) : (pt > 0.f ? 1.f : 0.f);
-      if (!acc) atomicMin(&s_h, i);
-    }
-    const int64_t o = static_cast<int64_t>(b) * a.K + i;
-    if (a.p_draft) a.p_draft[o] = p;
-    if (a.q_draft) a.q_draft[o] = q;
-    if (a.alpha) a.alpha[o] = al;
-  }
-  if (qz) atomicOr(&s_st, SEQ_Q_ZERO);
-  __syncthreads();
-  if (t == 0) {
-    const int h = s_h;
-    status = s_st;
-    rec->kind = h < n ? 0 : 1;
-    rec->row = h;
-    rec->Mp = s_Mp[h]; rec->kp = a.kp; rec->Sp = s_Sp[h];
-    rec->Mq = h < n ? s_Mq[h] : 0.f; rec->kq = a.kq; rec->Sq = h < n ? s_Sq[h] : 1.f;
-    rec->u = a.u_resample[static_cast<int64_t>(b) * (a.K + 1) + h];
-    rec->pad[0] = status;
-    a.accept_len[b] = h;
-  }
+__global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
+  const uint32_t nchunk = static_cast<uint32_t>(a.it.nchunk);
+  const int64_t chunk = a.it.chunk;
+  for_items(
+      static_cast<uint32_t>(a.it.items),
+      [&](uint32_t item) {
+        bool need;
+        float k;
+        sample_row<DT>(a, item / nchunk, need, k);
+        return need;
+      },
+      [&](uint32_t item) {
+        bool need;
+        float k;
+        const uint32_t row = item / nchunk;
+        const char* rowp = sample_row<DT>(a, row, need, k);
+        const int64_t v0 = static_cast<int64_t>(item - row * nchunk) * chunk;
+        const int64_t v1 = v0 + chunk < a.V ? v0 + chunk : a.V;
+        SoftmaxStats st(k);
+        stream_row<DT, kUnroll>(rowp, v0, v1, st);
+        float M = st.M, S = st.S;
+        wave_stats(M, S, k);
+        if (lane_id() == 0) a.stats[static_cast<int64_t>(item) * kWaves + wave_id()] = make_float2(M, S);
+      });
 }
 
 // Per-element weight of the draw: residual [p - q]_+ or bonus exp2 weight.
@@ -307,14 +225,6 @@ struct DrawWeight {
     return fmaxf(ep * isp - eq * isq, 0.f);
   }
 };
-
-__device__ __forceinline__ DrawWeight make_weight(const DrawRecord& r, bool resid) {
-  DrawWeight w;
-  w.kp = r.kp; w.cp = -r.Mp * r.kp; w.isp = 1.f / r.Sp;
-  w.kq = r.kq; w.cq = -r.Mq * r.kq; w.isq = 1.f / r.Sq;
-  w.resid = resid ? 1 : 0;
-  return w;
-}
 
 struct SumOne {
   DrawWeight w;
@@ -360,31 +270,8 @@ __device__ float sum_resid(const char* xr, const char* yr, int64_t v0, int64_t v
   return s;
 }
 
-template <int DT>
-__global__ __launch_bounds__(kBlock) void k_draw_partial(SampleArgs a) {
-  __shared__ float s_sum[kWaves];
-  const int b = blockIdx.x / a.draw_chunks;
-  const int c = blockIdx.x % a.draw_chunks;
-  const DrawRecord r = a.rec[b];
-  if (r.kind < 0) return;
-  const int64_t v0 = static_cast<int64_t>(c) * a.draw_chunk;
-  const int64_t v1 = v0 + a.draw_chunk < a.V ? v0 + a.draw_chunk : a.V;
-  const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + static_cast<int64_t>(r.row) * a.tr) * Elem<DT>::kBytes;
-  float s;
-  if (r.kind == 0) {
-    const char* yr = static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(r.row) * a.dr) * Elem<DT>::kBytes;
-    s = sum_resid<DT>(xr, yr, v0, v1, make_weight(r, true));
-  } else {
-    SumOne op{make_weight(r, false)};
-    stream_row<DT, kUnroll>(xr, v0, v1, op);
-    s = op.s;
-  }
-  s = block_sum(s, s_sum);
-  if (threadIdx.x == 0) a.dsum[static_cast<int64_t>(b) * a.draw_chunks + c] = s;
-}
-
-// WG-wide exclusive scan of one float per thread (fixed order); also returns
-// the total.  Thread order is element order.
+// WG-wide exclusive scan of one float per thread in thread order; also
+// returns the total.  Contains two barriers.
 __device__ __forceinline__ float block_exclusive_scan(float v, float& total, float* s_w) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -406,116 +293,293 @@ __device__ __forceinline__ float block_exclusive_scan(float v, float& total, flo
   return base + inc - v;
 }
 
+// Weights of elements [e0, e0 + kDrawPerThread) (0 at or past `end`): the
+// thread's loads are all issued before any weight is computed.
+template <int DT>
+__device__ __forceinline__ void load_weights(const char* xr, const char* yr, int64_t e0, int64_t end,
+                                             const DrawWeight& w, float (&wv)[kDrawPerThread]) {
+  using E = Elem<DT>;
+  constexpr int W = E::kVec;
+  constexpr int NV = kDrawPerThread / W;
+  const bool vec = (((reinterpret_cast<uintptr_t>(xr + e0 * E::kBytes) |
+                      reinterpret_cast<uintptr_t>(yr + e0 * E::kBytes)) & 15u) == 0) &&
+                   e0 + kDrawPerThread <= end;
+  if (vec) {
+    u32x4 rx[NV], ry[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      rx[k] = load16(xr + (e0 + k * W) * E::kBytes);
+      if (w.resid) ry[k] = load16(yr + (e0 + k * W) * E::kBytes);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float x[W], y[W];
+      E::unpack(rx[k], x);
+      if (w.resid) E::unpack(ry[k], y);
+#pragma unroll
+      for (int j = 0; j < W; ++j) wv[k * W + j] = w(x[j], w.resid ? y[j] : 0.f);
+    }
+  } else {
+    float x[kDrawPerThread], y[kDrawPerThread];
+#pragma unroll
+    for (int j = 0; j < kDrawPerThread; ++j) {
+      const bool in = e0 + j < end;
+      x[j] = in ? E::load1(xr, e0 + j) : 0.f;
+      y[j] = in && w.resid ? E::load1(yr, e0 + j) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kDrawPerThread; ++j) wv[j] = e0 + j < end ? w(x[j], y[j]) : 0.f;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
+  __shared__ float s_Mp[kMaxDraft + 1], s_Sp[kMaxDraft + 1];
+  __shared__ float s_Mq[kMaxDraft], s_Sq[kMaxDraft];
+  __shared__ float s_red[kWaves];
+  __shared__ int s_st, s_h;
+  const int NC = a.draw_chunks;
+  const int b = blockIdx.x / NC;
+  const int c = blockIdx.x % NC;
+  const int t = threadIdx.x;
+  const int64_t per_row = a.it.nchunk * kWaves;
+
+  // ---- the sequence's decision (every group of the sequence) ------------
+  bool nbad;
+  const int n = draft_count(a.draft_len, b, a.K, nbad);
+  const int budget = a.budget ? a.budget[b] : INT_MAX;
+  if (t == 0) {
+    s_st = (nbad || budget < 0) ? SEQ_BAD_INPUT : 0;
+    s_h = n;
+  }
+  __syncthreads();
+  const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
+  const int64_t ntr = static_cast<int64_t>(a.B) * (a.K + 1);
+  int st = 0;
+  for (int i = t; i < n; i += kBlock) {
+    const int di = d[i];
+    if (di < 0 || di >= a.V) st |= SEQ_BAD_INPUT;
+  }
+  if (!nbad) {
+    // Target rows 0..n with k = kp, then drafter rows 0..n-1 with k = kq.
+    combine_rows_stats(
+        n + 1, per_row, a.kp,
+        [&](int r) { return a.stats + (static_cast<int64_t>(b) * (a.K + 1) + r) * per_row; },
+        [&](int r, float M, float S) {
+          s_Mp[r] = M; s_Sp[r] = S;
+          st |= stats_status(M, S);
+        });
+    combine_rows_stats(
+        n, per_row, a.kq,
+        [&](int r) { return a.stats + (ntr + static_cast<int64_t>(b) * a.K + r) * per_row; },
+        [&](int r, float M, float S) {
+          s_Mq[r] = M; s_Sq[r] = S;
+          st |= stats_status(M, S);
+        });
+  }
+  if (st) atomicOr(&s_st, st);
+  __syncthreads();
+  if (s_st & SEQ_ERROR_MASK) {
+    if (c == 0) {
+      int32_t* out = a.out_tokens + static_cast<int64_t>(b) * (a.K + 1);
+      for (int i = t; i <= a.K; i += kBlock) out[i] = -1;
+      for (int i = t; i < a.K; i += kBlock) {
+        const int64_t o = static_cast<int64_t>(b) * a.K + i;
+        if (a.p_draft) a.p_draft[o] = 0.f;
+        if (a.q_draft) a.q_draft[o] = 0.f;
+        if (a.alpha) a.alpha[o] = 0.f;
+      }
+      if (t == 0) {
+        a.accept_len[b] = -1;
+        a.num_out[b] = 0;
+        if (a.residual_mass) a.residual_mass[b] = 0.f;
+        if (a.status) a.status[b] = s_st;
+        a.rec[b].status = s_st;
+      }
+    }
+    return;
+  }
+  // Acceptance tests: accept d_i iff u_i * q_i(d_i) < p~_i(d_i).
+  const float lam = a.lam, oml = 1.f - a.lam;
+  int qz = 0;
+  for (int i = t; i < a.K; i += kBlock) {
+    float p = 0.f, q = 0.f, al = 0.f;
+    if (i < n) {
+      const int di = d[i];
+      const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + i * a.tr) * Elem<DT>::kBytes;
+      const char* yr = static_cast<const char*>(a.drf) + (b * a.ds + i * a.dr) * Elem<DT>::kBytes;
+      const float x = Elem<DT>::load1(xr, di);
+      const float y = Elem<DT>::load1(yr, di);
+      p = fast_exp2(__builtin_fmaf(x, a.kp, -s_Mp[i] * a.kp)) / s_Sp[i];
+      q = fast_exp2(__builtin_fmaf(y, a.kq, -s_Mq[i] * a.kq)) / s_Sq[i];
+      const float pt = oml * p + lam * q;
+      const float u = a.u_accept[static_cast<int64_t>(b) * a.K + i];
+      if (q == 0.f && pt > 0.f) qz = 1;
+      al = q > 0.f ? fminf(1.f, pt / q) : (pt > 0.f ? 1.f : 0.f);
+      if (!(u * q < pt)) atomicMin(&s_h, i);
+    }
+    if (c == 0) {
+      const int64_t o = static_cast<int64_t>(b) * a.K + i;
+      if (a.p_draft) a.p_draft[o] = p;
+      if (a.q_draft) a.q_draft[o] = q;
+      if (a.alpha) a.alpha[o] = al;
+    }
+  }
+  if (qz) atomicOr(&s_st, SEQ_Q_ZERO);
+  __syncthreads();
+  const int h = s_h;
+  const bool resid = h < n;
+  const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + static_cast<int64_t>(h) * a.tr) * Elem<DT>::kBytes;
+  const char* yr = resid
+      ? static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(h) * a.dr) * Elem<DT>::kBytes
+      : xr;
+  DrawWeight w;
+  w.kp = a.kp; w.cp = -s_Mp[h] * a.kp; w.isp = 1.f / s_Sp[h];
+  w.kq = a.kq; w.cq = resid ? -s_Mq[h] * a.kq : 0.f; w.isq = resid ? 1.f / s_Sq[h] : 1.f;
+  w.resid = resid ? 1 : 0;
+
+  // ---- this group's chunk of the draw mass ------------------------------
+  {
+    const int64_t v0 = static_cast<int64_t>(c) * a.draw_chunk;
+    const int64_t v1 = v0 + a.draw_chunk < a.V ? v0 + a.draw_chunk : a.V;
+    float s;
+    if (resid) {
+      s = sum_resid<DT>(xr, yr, v0, v1, w);
+    } else {
+      SumOne op{w};
+      stream_row<DT, kUnroll>(xr, v0, v1, op);
+      s = op.s;
+    }
+    s = block_sum(s, s_red);
+    if (t == 0) a.dsum[static_cast<int64_t>(b) * NC + c] = s;
+  }
+  if (c == 0 && t == 0) {
+    DrawRecord r;
+    r.status = s_st;
+    r.h = h;
+    r.resid = resid ? 1 : 0;
+    r.cp = w.cp; r.isp = w.isp;
+    r.cq = w.cq; r.isq = w.isq;
+    r.u = a.u_resample[static_cast<int64_t>(b) * (a.K + 1) + h];
+    a.rec[b] = r;
+  }
+}
+
+
+// One group per sequence: find the token whose running mass first exceeds
+// u * Z (vocabulary order), then assemble the outputs.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_draw_select(SampleArgs a) {
-  __shared__ float s_dsum[kMaxSplit];
-  __shared__ float s_w[kWaves];
-  __shared__ int s_pick, s_last, s_a;
-  __shared__ float s_red[kWaves];
+  __shared__ float s_dsum[kMaxDrawChunks];
+  __shared__ float s_red[kWaves], s_w[kWaves];
+  __shared__ int s_pick, s_lastpos, s_a;
+  const int NC = a.draw_chunks;
   const int b = blockIdx.x;
   const int t = threadIdx.x;
-  DrawRecord r = a.rec[b];
-  if (r.kind < 0) return;
-  int status = r.pad[0];
-  const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + static_cast<int64_t>(r.row) * a.tr) * Elem<DT>::kBytes;
-  const char* yr = r.kind == 0
-      ? static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(r.row) * a.dr) * Elem<DT>::kBytes
+  const DrawRecord rec = a.rec[b];
+  if (rec.status & SEQ_ERROR_MASK) return;          // outputs already written
+  int status = rec.status;
+  const int h = rec.h;
+  bool resid = rec.resid != 0;
+  const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
+  const int budget = a.budget ? a.budget[b] : INT_MAX;
+  const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + static_cast<int64_t>(h) * a.tr) * Elem<DT>::kBytes;
+  const char* yr = resid
+      ? static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(h) * a.dr) * Elem<DT>::kBytes
       : xr;
-  const int NC = a.draw_chunks;
-  for (int c = t; c < NC; c += kBlock) s_dsum[c] = a.dsum[static_cast<int64_t>(b) * NC + c];
+  DrawWeight w;
+  w.kp = a.kp; w.cp = rec.cp; w.isp = rec.isp;
+  w.kq = a.kq; w.cq = rec.cq; w.isq = rec.isq;
+  w.resid = rec.resid;
+
+  // ---- locate u * Z in vocabulary order ----------------------------------
+  for (int k = t; k < NC; k += kBlock) s_dsum[k] = a.dsum[static_cast<int64_t>(b) * NC + k];
   __syncthreads();
   float Z = 0.f;
-  for (int c = 0; c < NC; ++c) Z += s_dsum[c];
-  bool resid = r.kind == 0;
+  for (int k = 0; k < NC; ++k) Z += s_dsum[k];
   const float Zres = resid ? Z : 0.f;
   if (resid && !(Z > 0.f)) {
     // Residual mass vanished in float32 (p == q up to rounding): draw from p
     // with the same uniform instead, and flag it.
     status |= SEQ_Z_ZERO;
     resid = false;
-    const DrawWeight w = make_weight(r, false);
-    for (int c = 0; c < NC; ++c) {
-      const int64_t v0 = static_cast<int64_t>(c) * a.draw_chunk;
+    w.resid = 0;
+    for (int k = 0; k < NC; ++k) {
+      const int64_t v0 = static_cast<int64_t>(k) * a.draw_chunk;
       const int64_t v1 = v0 + a.draw_chunk < a.V ? v0 + a.draw_chunk : a.V;
       float s = 0.f;
       for (int64_t j = v0 + t; j < v1; j += kBlock) s += w(Elem<DT>::load1(xr, j), 0.f);
       s = block_sum(s, s_red);
       __syncthreads();
-      if (t == 0) s_dsum[c] = s;
+      if (t == 0) s_dsum[k] = s;
       __syncthreads();
     }
     Z = 0.f;
-    for (int c = 0; c < NC; ++c) Z += s_dsum[c];
+    for (int k = 0; k < NC; ++k) Z += s_dsum[k];
   }
-  const DrawWeight w = make_weight(r, resid);
-  const float target = r.u * Z;
+  const float target = rec.u * Z;
   // Chunk whose running mass first exceeds u*Z (positive chunks only).
   int cs = -1, clast = -1;
   float base = 0.f, run = 0.f;
-  for (int c = 0; c < NC; ++c) {
-    if (!(s_dsum[c] > 0.f)) continue;
-    clast = c;
-    if (run + s_dsum[c] > target) { cs = c; base = run; break; }
-    run += s_dsum[c];
+  for (int k = 0; k < NC; ++k) {
+    if (!(s_dsum[k] > 0.f)) continue;
+    clast = k;
+    if (run + s_dsum[k] > target) { cs = k; base = run; break; }
+    run += s_dsum[k];
   }
   if (cs < 0) {  // rounding: u*Z at or past the total -> last positive chunk
     cs = clast >= 0 ? clast : 0;
     base = run - (clast >= 0 ? s_dsum[clast] : 0.f);
   }
-  // Scan chunk cs in vocabulary order, 8 elements per thread per tile.
-  if (t == 0) { s_pick = INT_MAX; s_last = -1; }
+  if (t == 0) { s_pick = INT_MAX; s_lastpos = -1; }
   __syncthreads();
+  // Thread t holds elements [c0 + t*P, c0 + (t+1)*P) of the chunk (P =
+  // kDrawPerThread): their weights stay in registers for the scan.
   const int64_t c0 = static_cast<int64_t>(cs) * a.draw_chunk;
   const int64_t c1 = c0 + a.draw_chunk < a.V ? c0 + a.draw_chunk : a.V;
-  constexpr int P = 8;
-  for (int64_t tile = c0; tile < c1; tile += static_cast<int64_t>(kBlock) * P) {
-    float wv[P];
-    float tot = 0.f;
-    int lastpos = -1;
+  const int64_t e0 = c0 + static_cast<int64_t>(t) * kDrawPerThread;
+  float wv[kDrawPerThread];
+  load_weights<DT>(xr, yr, e0, c1, w, wv);
+  float loc = 0.f;
+  int lastpos = -1;
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const int64_t e = tile + static_cast<int64_t>(t) * P + j;
-      wv[j] = e < c1 ? w(Elem<DT>::load1(xr, e), Elem<DT>::load1(yr, e)) : 0.f;
-      tot += wv[j];
-      if (wv[j] > 0.f) lastpos = static_cast<int>(e);
-    }
-    float tile_total;
-    float runv = base + block_exclusive_scan(tot, tile_total, s_w);
+  for (int j = 0; j < kDrawPerThread; ++j) {
+    loc += wv[j];
+    if (wv[j] > 0.f) lastpos = static_cast<int>(e0 + j);
+  }
+  float tot;
+  const float start = base + block_exclusive_scan(loc, tot, s_w);
+  if (lastpos >= 0) atomicMax(&s_lastpos, lastpos);
+  if (loc > 0.f && start + loc > target) {
+    float r = start;
     int found = INT_MAX;
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      runv += wv[j];
-      if (found == INT_MAX && wv[j] > 0.f && runv > target)
-        found = static_cast<int>(tile + static_cast<int64_t>(t) * P + j);
+    for (int j = 0; j < kDrawPerThread; ++j) {
+      r += wv[j];
+      if (found == INT_MAX && wv[j] > 0.f && r > target) found = static_cast<int>(e0 + j);
     }
     if (found != INT_MAX) atomicMin(&s_pick, found);
-    if (lastpos >= 0) atomicMax(&s_last, lastpos);
-    __syncthreads();
-    if (s_pick != INT_MAX) break;
-    base += tile_total;
-    __syncthreads();
   }
   __syncthreads();
-  const int c = s_pick != INT_MAX ? s_pick : s_last;
+  const int tok = s_pick != INT_MAX ? s_pick : s_lastpos;
 
-  // Output assembly: C = (d_1..d_h, c), then the ending condition.
-  const int h = r.row;
-  const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
-  const int budget = a.budget ? a.budget[b] : INT_MAX;
+  // ---- output assembly: C = (d_1..d_h, c), then the ending condition ----
   const int A = h + 1;
   if (t == 0) s_a = A < budget ? A : budget;
   __syncthreads();
   if (a.eos >= 0) {
     for (int i = t; i < A; i += kBlock) {
-      const int ci = i < h ? d[i] : c;
+      const int ci = i < h ? d[i] : tok;
       if (ci == a.eos) atomicMin(&s_a, i + 1);
     }
   }
   __syncthreads();
   const int an = s_a;
   int32_t* out = a.out_tokens + static_cast<int64_t>(b) * (a.K + 1);
-  for (int i = t; i <= a.K; i += kBlock) out[i] = i < an ? (i < h ? d[i] : c) : -1;
+  for (int i = t; i <= a.K; i += kBlock) out[i] = i < an ? (i < h ? d[i] : tok) : -1;
   if (t == 0) {
+    a.accept_len[b] = h;
     a.num_out[b] = an;
     // Mass of [p~ - q]_+ = (1 - lambda) [p - q]_+: the rejection probability.
     if (a.residual_mass) a.residual_mass[b] = Zres * (1.f - a.lam);
@@ -525,6 +589,10 @@ __global__ __launch_bounds__(kBlock) void k_draw_select(SampleArgs a) {
 
 // ============================================================== launches ===
 
+static void mark(hipEvent_t e, hipStream_t s) {
+  if (e) (void)hipEventRecord(e, s);
+}
+
 #define DBV_LAUNCH(kern, grid, stream, arg)                                         \
   do {                                                                               \
     if ((grid) > 0) hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)),      \
@@ -532,12 +600,8 @@ __global__ __launch_bounds__(kBlock) void k_draw_select(SampleArgs a) {
     if (hipGetLastError() != hipSuccess) return false;                               \
   } while (0)
 
-static void mark(hipEvent_t e, hipStream_t s) {
-  if (e) (void)hipEventRecord(e, s);
-}
-
 bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
-  const int64_t grid = static_cast<int64_t>(a.B) * ((a.K + 1) + a.W) * a.split;
+  const int64_t grid = persistent_grid(a.it.items);
   mark(ev.begin, stream);
   if (dtype == DT_BF16) DBV_LAUNCH(k_greedy_rows<DT_BF16>, grid, stream, a);
   else DBV_LAUNCH(k_greedy_rows<DT_F32>, grid, stream, a);
@@ -547,19 +611,17 @@ bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const Tim
 }
 
 bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
-  const int64_t grid = static_cast<int64_t>(a.B) * ((a.K + 1) + a.K) * a.split;
+  const int64_t grid = persistent_grid(a.it.items);
   const int64_t dgrid = static_cast<int64_t>(a.B) * a.draw_chunks;
   mark(ev.begin, stream);
   if (dtype == DT_BF16) DBV_LAUNCH(k_sample_rows<DT_BF16>, grid, stream, a);
   else DBV_LAUNCH(k_sample_rows<DT_F32>, grid, stream, a);
   mark(ev.end, stream);
   if (dtype == DT_BF16) {
-    DBV_LAUNCH(k_sample_decide<DT_BF16>, a.B, stream, a);
-    DBV_LAUNCH(k_draw_partial<DT_BF16>, dgrid, stream, a);
+    DBV_LAUNCH(k_draw_mass<DT_BF16>, dgrid, stream, a);
     DBV_LAUNCH(k_draw_select<DT_BF16>, a.B, stream, a);
   } else {
-    DBV_LAUNCH(k_sample_decide<DT_F32>, a.B, stream, a);
-    DBV_LAUNCH(k_draw_partial<DT_F32>, dgrid, stream, a);
+    DBV_LAUNCH(k_draw_mass<DT_F32>, dgrid, stream, a);
     DBV_LAUNCH(k_draw_select<DT_F32>, a.B, stream, a);
   }
   return true;

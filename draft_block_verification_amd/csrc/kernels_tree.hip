@@ -1,15 +1,17 @@
 // Draft-tree verification by shared-Gumbel state equality (SPOT, Sec. 4.1,
 // Sec. 4.3 and App. A.1).
 //
-//   k_tree_conf    split-V softmax statistics (M, S) of every masked row of
-//                  every state; the position's confidence is 1/S (max_v p).
-//                  In the fixed-position mode only the given position's row.
-//   k_tree_gumbel  per (state, V-chunk): s*(y) from the confidences (lowest
-//                  position on ties), then the argmax over v of
-//                  z_v / T + G[s*, v] (z_v at T = 0) -- Phi(y)'s token.
-//   k_tree_walk    per sequence: validate the tree, gather Phi(y) for every
-//                  state, walk from the root along the child equal to Phi(y),
-//                  commit Phi of the last accepted state.
+//   k_tree_conf    persistent: softmax statistics (M, S) partials of every
+//                  masked row of every state (the position's confidence is
+//                  1/S = max_v p); in the fixed-position mode only the given
+//                  position's row.
+//   k_tree_gumbel  per (state, vocabulary chunk): s*(y) from the confidences
+//                  (lowest position on ties), then the argmax over v of
+//                  z_v / T + G[s*, v] (z_v at T = 0) -- the token of Phi(y).
+//   k_tree_walk    per sequence: validates the tree, gathers Phi(y) for every
+//                  state, walks from the root along the child equal to Phi(y)
+//                  and commits Phi of the last accepted state.
+// The kernel boundaries are the only cross-group synchronisation.
 #include "dbv_device.h"
 #include "dbv_launch.h"
 
@@ -22,58 +24,82 @@ __device__ __forceinline__ int state_count(const int32_t* num_states, int b, int
   return (ns < 1 || ns > S) ? -1 : ns;
 }
 
+// Row index -> (sequence, state, position), 32-bit arithmetic.
+__device__ __forceinline__ void split_row(const TreeArgs& a, uint32_t row, int& b, int& y, int& s) {
+  const uint32_t L = static_cast<uint32_t>(a.L);
+  const uint32_t sy = row / L;
+  s = static_cast<int>(row - sy * L);
+  const uint32_t S = static_cast<uint32_t>(a.S);
+  const uint32_t bb = sy / S;
+  y = static_cast<int>(sy - bb * S);
+  b = static_cast<int>(bb);
+}
+
+// Does row (b, y, s) need its statistics?
+__device__ __forceinline__ bool conf_row_needed(const TreeArgs& a, uint32_t row) {
+  int b, y, s;
+  split_row(a, row, b, y, s);
+  const int ns = state_count(a.num_states, b, a.S);
+  if (ns < 0 || y >= ns) return false;
+  const int64_t sy = static_cast<int64_t>(b) * a.S + y;
+  return a.fixed ? a.next_pos[sy] == s : a.masked[sy * a.L + s] != 0;
+}
+
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_tree_conf(TreeArgs a) {
-  __shared__ float s_m[kWaves], s_s[kWaves];
-  const int64_t gid = blockIdx.x;
-  const int64_t row = gid / a.split1;
-  const int sp = static_cast<int>(gid % a.split1);
-  const int b = static_cast<int>(row / (static_cast<int64_t>(a.S) * a.L));
-  const int y = static_cast<int>((row / a.L) % a.S);
-  const int s = static_cast<int>(row % a.L);
-  const int ns = state_count(a.num_states, b, a.S);
-  if (ns < 0 || y >= ns) return;
-  const int64_t sy = static_cast<int64_t>(b) * a.S + y;
-  if (a.fixed) {
-    if (a.next_pos[sy] != s) return;
-  } else if (!a.masked[sy * a.L + s]) {
-    return;
-  }
-  const char* rowp = static_cast<const char*>(a.logits) +
-                     (b * a.ss + y * a.sy + s * a.sp) * Elem<DT>::kBytes;
-  const int64_t v0 = static_cast<int64_t>(sp) * a.chunk1;
-  const int64_t v1 = v0 + a.chunk1 < a.V ? v0 + a.chunk1 : a.V;
-  SoftmaxStats st(kLog2e);
-  stream_row<DT, 4>(rowp, v0, v1, st);
-  float M = st.M, S = st.S;
-  block_stats(M, S, kLog2e, s_m, s_s);
-  if (threadIdx.x == 0) a.conf[gid] = make_float2(M, S);
+  const uint32_t nchunk = static_cast<uint32_t>(a.it.nchunk);
+  const int64_t chunk = a.it.chunk;
+  for_items(
+      static_cast<uint32_t>(a.it.items),
+      [&](uint32_t item) { return conf_row_needed(a, item / nchunk); },
+      [&](uint32_t item) {
+        const uint32_t row = item / nchunk;
+        int b, y, s;
+        split_row(a, row, b, y, s);
+        const char* rowp = static_cast<const char*>(a.logits) +
+                           (b * a.ss + y * a.sy + s * a.sp) * Elem<DT>::kBytes;
+        const int64_t v0 = static_cast<int64_t>(item - row * nchunk) * chunk;
+        const int64_t v1 = v0 + chunk < a.V ? v0 + chunk : a.V;
+        SoftmaxStats st(kLog2e);
+        stream_row<DT, 4>(rowp, v0, v1, st);
+        float M = st.M, S = st.S;
+        wave_stats(M, S, kLog2e);
+        if ((threadIdx.x & 63) == 0)
+          a.conf[static_cast<int64_t>(item) * kWaves + (threadIdx.x >> 6)] = make_float2(M, S);
+      });
 }
 
 __device__ __forceinline__ void combine_conf(const TreeArgs& a, int64_t row, float& M, float& S) {
   M = -kInf;
   S = 0.f;
-  const float2* p = a.conf + row * a.split1;
-  for (int k = 0; k < a.split1; ++k) stats_merge(M, S, p[k].x, p[k].y, kLog2e);
+  const int64_t n = a.it.nchunk * kWaves;
+  const float2* p = a.conf + row * n;
+  for (int64_t k = 0; k < n; ++k) stats_merge(M, S, p[k].x, p[k].y, kLog2e);
 }
 
 // s*(y): the masked position of largest confidence 1/S (lowest on ties), or
-// the given position in the fixed mode; -1 when there is none.
-__device__ int select_position(const TreeArgs& a, int b, int y) {
+// the given position in the fixed mode; -1 when there is none.  Every thread
+// of the group calls it; the result is uniform.
+__device__ int select_position(const TreeArgs& a, int b, int y, float* s_v, int* s_i, int* s_n, int* s_out) {
   const int64_t sy = static_cast<int64_t>(b) * a.S + y;
   if (a.fixed) {
     const int np = a.next_pos[sy];
     return (np >= 0 && np < a.L) ? np : -1;
   }
-  int best = -1;
-  float bestS = kInf;
-  for (int s = 0; s < a.L; ++s) {
+  float v = -kInf;
+  int idx = -1, nan = 0;
+  for (int s = threadIdx.x; s < a.L; s += kBlock) {
     if (!a.masked[sy * a.L + s]) continue;
     float M, S;
     combine_conf(a, sy * a.L + s, M, S);
-    if (best < 0 || S < bestS) { best = s; bestS = S; }
+    if (pick_better(-S, s, v, idx)) { v = -S; idx = s; }   // max of -S = min of S
   }
-  return best;
+  block_argmax(v, idx, nan, s_v, s_i, s_n);
+  if (threadIdx.x == 0) *s_out = idx;
+  __syncthreads();
+  const int r = *s_out;
+  __syncthreads();
+  return r;
 }
 
 // Argmax of z/T + g over a logit row and its Gumbel row read together.
@@ -141,47 +167,9 @@ __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64
   }
 }
 
-template <int DT>
-__global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
-  __shared__ float s_v[kWaves];
-  __shared__ int s_i[kWaves], s_n[kWaves];
-  const int64_t gid = blockIdx.x;
-  const int64_t sy = gid / a.split2;
-  const int sp = static_cast<int>(gid % a.split2);
-  const int b = static_cast<int>(sy / a.S);
-  const int y = static_cast<int>(sy % a.S);
-  const int ns = state_count(a.num_states, b, a.S);
-  if (ns < 0 || y >= ns) return;
-  const int s = select_position(a, b, y);
-  if (sp == 0 && threadIdx.x == 0) a.sel[sy] = s;
-  if (s < 0) return;
-  const char* xr = static_cast<const char*>(a.logits) +
-                   (b * a.ss + y * a.sy + s * a.sp) * Elem<DT>::kBytes;
-  const int64_t v0 = static_cast<int64_t>(sp) * a.chunk2;
-  const int64_t v1 = v0 + a.chunk2 < a.V ? v0 + a.chunk2 : a.V;
-  ArgmaxPick pk;
-  int64_t idx;
-  if (a.inv_t > 0.f) {
-    const float* gr = a.gumbel + b * a.gs + s * a.gp;
-    gumbel_argmax<DT>(xr, gr, v0, v1, a.inv_t, pk);
-    idx = resolve_argmax<DT>(pk, v1, [&](int64_t j) {
-      return __builtin_fmaf(Elem<DT>::load1(xr, j), a.inv_t, gr[j]);
-    });
-  } else {
-    stream_row<DT, 4>(xr, v0, v1, pk);
-    idx = resolve_argmax<DT>(pk, v1, [&](int64_t j) { return Elem<DT>::load1(xr, j); });
-  }
-  float v = pk.best;
-  int ii = static_cast<int>(idx);
-  int nan = pk.nan ? 1 : 0;
-  block_argmax(v, ii, nan, s_v, s_i, s_n);
-  if (threadIdx.x == 0) a.pick[gid] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
-}
-
-__global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
-  __shared__ int s_pos[kMaxStates], s_tok[kMaxStates];
+// The walk of one sequence.
+__device__ void tree_walk(const TreeArgs& a, int b, int* s_pos, int* s_tok) {
   __shared__ int s_st, s_child, s_y, s_len, s_ncommit;
-  const int b = blockIdx.x;
   const int t = threadIdx.x;
   const int S = a.S;
   const int ns = state_count(a.num_states, b, S);
@@ -210,20 +198,24 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
   __syncthreads();
   st = 0;
   const bool valid = !(s_st & SEQ_BAD_INPUT);
-  // Phi(y) per state, and the status of every row that was read.
+  // Status of every row that was read: all masked rows (state equality).
+  if (valid && !a.fixed) {
+    const int64_t pairs = static_cast<int64_t>(ns) * a.L;
+    for (int64_t q = t; q < pairs; q += kBlock) {
+      const int64_t sy = base + q / a.L;
+      const int s = static_cast<int>(q % a.L);
+      if (!a.masked[sy * a.L + s]) continue;
+      float M, Sum;
+      combine_conf(a, sy * a.L + s, M, Sum);
+      st |= stats_status(M, Sum);
+    }
+  }
+  // Phi(y) per state.
   for (int y = t; y < S; y += kBlock) {
     int pos = -1, tok = -1;
     float conf = __builtin_nanf("");
     if (valid && y < ns) {
       const int64_t sy = base + y;
-      if (!a.fixed) {
-        for (int s = 0; s < a.L; ++s) {
-          if (!a.masked[sy * a.L + s]) continue;
-          float M, Sum;
-          combine_conf(a, sy * a.L + s, M, Sum);
-          st |= stats_status(M, Sum);
-        }
-      }
       pos = a.sel[sy];
       if (pos >= 0) {
         float M, Sum;
@@ -242,7 +234,8 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
         tok = idx;
       }
     }
-    if (y < kMaxStates) { s_pos[y] = pos; s_tok[y] = tok; }
+    s_pos[y] = pos;
+    s_tok[y] = tok;
     if (a.sel_pos) a.sel_pos[base + y] = pos;
     if (a.sel_tok) a.sel_tok[base + y] = tok;
     if (a.sel_conf) a.sel_conf[base + y] = conf;
@@ -254,6 +247,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
   int32_t* cp = a.commit_pos + base;
   int32_t* ct = a.commit_tok + base;
   for (int z = t; z < S; z += kBlock) { pn[z] = -1; cp[z] = -1; ct[z] = -1; }
+  __syncthreads();
   if (status & SEQ_ERROR_MASK) {
     if (t == 0) {
       a.path_len[b] = -1;
@@ -264,8 +258,8 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
   }
   if (t == 0) { s_y = 0; s_len = 0; s_ncommit = 0; }
   __syncthreads();
-  // Walk: accept the child equal to Phi(y) (lowest node index), else commit
-  // Phi(y) and stop; a state without transition ends the walk.
+  // Accept the child equal to Phi(y) (lowest node index), else commit Phi(y)
+  // and stop; a state without transition ends the walk.
   for (int step = 0; step < ns; ++step) {
     const int y = s_y;
     const int pos = s_pos[y], tok = s_tok[y];
@@ -302,8 +296,49 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
   }
 }
 
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
+  __shared__ float s_v[kWaves];
+  __shared__ int s_i[kWaves], s_n[kWaves], s_sel;
+  const int64_t gid = blockIdx.x;
+  const int64_t sy = gid / a.split2;
+  const int sp = static_cast<int>(gid % a.split2);
+  const int b = static_cast<int>(sy / a.S);
+  const int y = static_cast<int>(sy % a.S);
+  const int ns = state_count(a.num_states, b, a.S);
+  if (ns > 0 && y < ns) {
+    const int s = select_position(a, b, y, s_v, s_i, s_n, &s_sel);
+    if (sp == 0 && threadIdx.x == 0) a.sel[sy] = s;
+    if (s >= 0) {
+      const char* xr = static_cast<const char*>(a.logits) +
+                       (b * a.ss + y * a.sy + s * a.sp) * Elem<DT>::kBytes;
+      const int64_t v0 = static_cast<int64_t>(sp) * a.chunk2;
+      const int64_t v1 = v0 + a.chunk2 < a.V ? v0 + a.chunk2 : a.V;
+      ArgmaxPick pk;
+      int64_t idx;
+      if (a.inv_t > 0.f) {
+        const float* gr = a.gumbel + b * a.gs + s * a.gp;
+        gumbel_argmax<DT>(xr, gr, v0, v1, a.inv_t, pk);
+      } else {
+        stream_row<DT, 4>(xr, v0, v1, pk);
+      }
+      idx = pk.bidx;
+      float v = pk.best;
+      int ii = static_cast<int>(idx);
+      int nan = pk.nan ? 1 : 0;
+      block_argmax(v, ii, nan, s_v, s_i, s_n);
+      if (threadIdx.x == 0) a.pick[gid] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
+  __shared__ int s_pos[kMaxStates], s_tok[kMaxStates];
+  tree_walk(a, blockIdx.x, s_pos, s_tok);
+}
+
 bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
-  const int64_t g1 = static_cast<int64_t>(a.B) * a.S * a.L * a.split1;
+  const int64_t g1 = persistent_grid(a.it.items);
   const int64_t g2 = static_cast<int64_t>(a.B) * a.S * a.split2;
   const dim3 blk(kBlock);
   if (ev.begin) (void)hipEventRecord(ev.begin, stream);

@@ -62,13 +62,18 @@ def verify_greedy(tgt, draft_tokens, draft_len=None, draft_rows=None,
         n = lens[b]
         status = 0
         budget = _budget(len_budget, b)
-        if n < 0 or n > K or (budget is not None and budget < 0):
+        rows_read = n + 1
+        if n < 0 or n > K:
+            # No valid draft length: there are no verifier positions, so no
+            # verifier row is read.
             status |= STATUS_BAD_INPUT
-            n = 0 if n < 0 or n > K else n
+            n, rows_read = 0, 0
+        if budget is not None and budget < 0:
+            status |= STATUS_BAD_INPUT
         d = [int(t) for t in d_all[b, :n]]
         if any(t < 0 or t >= V for t in d):
             status |= STATUS_BAD_INPUT
-        for i in range(n + 1):
+        for i in range(rows_read):
             status |= row_status(tgt[b, i])
         for j in range(W):
             status |= row_status(draft_rows[b, j])
@@ -135,13 +140,17 @@ def _sampling_verify(tgt, drf, draft_tokens, draft_len, t_target, t_draft,
         n = lens[b]
         status = 0
         budget = _budget(len_budget, b)
-        if n < 0 or n > K or (budget is not None and budget < 0):
+        rows_read = n + 1
+        if n < 0 or n > K:
+            # No valid draft length: no verifier or drafter row is read.
             status |= STATUS_BAD_INPUT
-            n = 0 if n < 0 or n > K else n
+            n, rows_read = 0, 0
+        if budget is not None and budget < 0:
+            status |= STATUS_BAD_INPUT
         d = [int(t) for t in d_all[b, :n]]
         if any(t < 0 or t >= V for t in d):
             status |= STATUS_BAD_INPUT
-        for i in range(n + 1):
+        for i in range(rows_read):
             status |= row_status(tgt[b, i])
         for i in range(n):
             status |= row_status(drf[b, i])

@@ -161,7 +161,8 @@ def test_chain_edge_cases(dev):
     tgt[3, 4, 5] = float("inf")      # +inf in the bonus row
     n[4] = 1
     tgt[4, 3, 9] = float("nan")      # NaN in a row that is not read
-    n[5] = K + 1                     # bad draft length
+    n[5] = K + 1                     # bad draft length (its rows are not read)
+    tgt[5, 0, 3] = float("nan")
     drf[6, 0, int(d[6, 0])] = float("-inf")   # q(d) = 0 < p(d): accepted + flagged
     n[7] = 0                         # empty draft: bonus from row 0
     tgt[8, :, : V // 2] = float("-inf")        # half the vocabulary masked out
