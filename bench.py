@@ -16,8 +16,11 @@ and the correction or bonus draw.  Workloads (sizes of the pages' setups):
 Inputs smaller than 1 GiB are replicated into several buffer sets and the
 steps rotate over them, so the 256 MiB last-level cache cannot serve them.
 Prints one JSON line: whole-job verified draft positions per second, the
-roofline of the row-streaming kernel (timed alone with HIP events on the
-launch stream), and the CPU oracle timed on a bounded sample.
+roofline of the row-streaming kernel (timed alone with HIP events that the
+launch stamps at the kernel's start and end), and the CPU oracle timed on a
+bounded sample.  `roofline.traffic` is the HBM bytes per launch that the
+stored counter readings (profiles/traffic.json) give for the same kernel
+sources, else null.
 """
 
 import argparse
@@ -54,7 +57,41 @@ def parse():
     ap.add_argument("--workload", default="c2", choices=sorted(DESCR))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain device copy of COPY_PROBE_BYTES five times "
+                         "(the reference kernel for scaling HBM counters)")
     return ap.parse_args()
+
+
+COPY_PROBE_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources: counter readings apply only to the kernels
+    they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(HERE, "draft_block_verification_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the stored counter readings
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factor), or None when
+    there are none for these sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get("workloads", {}).get(workload)
+    if not e or e.get("kernel") != kernel or t.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
 
 
 # --------------------------------------------------------------- workloads ---
@@ -233,7 +270,8 @@ def main():
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
 
-    # The row-streaming kernel alone: events recorded by the library around it.
+    # The row-streaming kernel alone: the library stamps these events at the
+    # kernel's own start and end (hipExtLaunchKernel).
     lib = _lib.load()
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in kev:          # create the underlying HIP events (lazy in torch)
@@ -265,9 +303,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if args.workload == "c1" else "bf16",
+        "dtype": "f32",
         "data": "synthetic",
         "config": dict(workload=DESCR[args.workload], **case.shape,
+                       logits="f32" if args.workload == "c1" else "bf16",
                        positions_per_step=case.positions, rotation_sets=R,
                        wall_s=round(wall, 4)),
         "roofline": {
@@ -277,12 +316,20 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(args.workload, case.kernel),
             "bytes_per_launch": case.kernel_bytes,
             "kernel_ms": kms,
         },
         "cpu_baseline": None,
     }
+    if args.copy_probe:
+        n = COPY_PROBE_BYTES // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_probe_bytes"] = COPY_PROBE_BYTES
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = case.cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

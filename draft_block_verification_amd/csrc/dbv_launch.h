@@ -1,6 +1,7 @@
 // Kernel argument blocks and launchers (internal to libdbv).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -77,6 +78,23 @@ struct TimingEvents {
   hipEvent_t begin = nullptr;
   hipEvent_t end = nullptr;
 };
+
+// Launch `kern(arg)` on `grid` groups of 256 threads.  With timing events the
+// launch goes through hipExtLaunchKernel, which stamps the events at the
+// kernel's own start and end (no launch gap in the interval); an empty grid
+// still records both events so that the caller can read them.
+template <typename Arg>
+bool launch(const void* kern, int64_t grid, hipStream_t stream, const Arg& arg,
+            const TimingEvents& ev = TimingEvents()) {
+  if (grid <= 0) {
+    if (ev.begin) (void)hipEventRecord(ev.begin, stream);
+    if (ev.end) (void)hipEventRecord(ev.end, stream);
+    return true;
+  }
+  void* args[] = {const_cast<Arg*>(&arg)};
+  return hipExtLaunchKernel(kern, dim3(static_cast<unsigned>(grid)), dim3(256), args, 0, stream,
+                            ev.begin, ev.end, 0) == hipSuccess;
+}
 
 // Grid of a persistent launch: at most the resident groups of the device.
 int64_t persistent_grid(int64_t items);

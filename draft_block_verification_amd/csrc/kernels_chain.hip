@@ -589,42 +589,25 @@ __global__ __launch_bounds__(kBlock) void k_draw_select(SampleArgs a) {
 
 // ============================================================== launches ===
 
-static void mark(hipEvent_t e, hipStream_t s) {
-  if (e) (void)hipEventRecord(e, s);
+template <typename K>
+static const void* fn(K* k) {
+  return reinterpret_cast<const void*>(k);
 }
 
-#define DBV_LAUNCH(kern, grid, stream, arg)                                         \
-  do {                                                                               \
-    if ((grid) > 0) hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)),      \
-                                       dim3(kBlock), 0, (stream), (arg));            \
-    if (hipGetLastError() != hipSuccess) return false;                               \
-  } while (0)
-
 bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
-  const int64_t grid = persistent_grid(a.it.items);
-  mark(ev.begin, stream);
-  if (dtype == DT_BF16) DBV_LAUNCH(k_greedy_rows<DT_BF16>, grid, stream, a);
-  else DBV_LAUNCH(k_greedy_rows<DT_F32>, grid, stream, a);
-  mark(ev.end, stream);
-  DBV_LAUNCH(k_greedy_finalize, a.B, stream, a);
-  return true;
+  const bool bf = dtype == DT_BF16;
+  return launch(bf ? fn(k_greedy_rows<DT_BF16>) : fn(k_greedy_rows<DT_F32>),
+                persistent_grid(a.it.items), stream, a, ev) &&
+         launch(fn(k_greedy_finalize), a.B, stream, a);
 }
 
 bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
-  const int64_t grid = persistent_grid(a.it.items);
-  const int64_t dgrid = static_cast<int64_t>(a.B) * a.draw_chunks;
-  mark(ev.begin, stream);
-  if (dtype == DT_BF16) DBV_LAUNCH(k_sample_rows<DT_BF16>, grid, stream, a);
-  else DBV_LAUNCH(k_sample_rows<DT_F32>, grid, stream, a);
-  mark(ev.end, stream);
-  if (dtype == DT_BF16) {
-    DBV_LAUNCH(k_draw_mass<DT_BF16>, dgrid, stream, a);
-    DBV_LAUNCH(k_draw_select<DT_BF16>, a.B, stream, a);
-  } else {
-    DBV_LAUNCH(k_draw_mass<DT_F32>, dgrid, stream, a);
-    DBV_LAUNCH(k_draw_select<DT_F32>, a.B, stream, a);
-  }
-  return true;
+  const bool bf = dtype == DT_BF16;
+  return launch(bf ? fn(k_sample_rows<DT_BF16>) : fn(k_sample_rows<DT_F32>),
+                persistent_grid(a.it.items), stream, a, ev) &&
+         launch(bf ? fn(k_draw_mass<DT_BF16>) : fn(k_draw_mass<DT_F32>),
+                static_cast<int64_t>(a.B) * a.draw_chunks, stream, a) &&
+         launch(bf ? fn(k_draw_select<DT_BF16>) : fn(k_draw_select<DT_F32>), a.B, stream, a);
 }
 
 }  // namespace dbv

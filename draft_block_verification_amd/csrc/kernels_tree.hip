@@ -337,26 +337,18 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
   tree_walk(a, blockIdx.x, s_pos, s_tok);
 }
 
+template <typename K>
+static const void* fn(K* k) {
+  return reinterpret_cast<const void*>(k);
+}
+
 bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
-  const int64_t g1 = persistent_grid(a.it.items);
-  const int64_t g2 = static_cast<int64_t>(a.B) * a.S * a.split2;
-  const dim3 blk(kBlock);
-  if (ev.begin) (void)hipEventRecord(ev.begin, stream);
-  if (dtype == DT_BF16) {
-    if (g1 > 0) hipLaunchKernelGGL(k_tree_conf<DT_BF16>, dim3(static_cast<unsigned>(g1)), blk, 0, stream, a);
-  } else {
-    if (g1 > 0) hipLaunchKernelGGL(k_tree_conf<DT_F32>, dim3(static_cast<unsigned>(g1)), blk, 0, stream, a);
-  }
-  if (hipGetLastError() != hipSuccess) return false;
-  if (ev.end) (void)hipEventRecord(ev.end, stream);
-  if (dtype == DT_BF16) {
-    if (g2 > 0) hipLaunchKernelGGL(k_tree_gumbel<DT_BF16>, dim3(static_cast<unsigned>(g2)), blk, 0, stream, a);
-  } else {
-    if (g2 > 0) hipLaunchKernelGGL(k_tree_gumbel<DT_F32>, dim3(static_cast<unsigned>(g2)), blk, 0, stream, a);
-  }
-  if (hipGetLastError() != hipSuccess) return false;
-  if (a.B > 0) hipLaunchKernelGGL(k_tree_walk, dim3(static_cast<unsigned>(a.B)), blk, 0, stream, a);
-  return hipGetLastError() == hipSuccess;
+  const bool bf = dtype == DT_BF16;
+  return launch(bf ? fn(k_tree_conf<DT_BF16>) : fn(k_tree_conf<DT_F32>),
+                persistent_grid(a.it.items), stream, a, ev) &&
+         launch(bf ? fn(k_tree_gumbel<DT_BF16>) : fn(k_tree_gumbel<DT_F32>),
+                static_cast<int64_t>(a.B) * a.S * a.split2, stream, a) &&
+         launch(fn(k_tree_walk), a.B, stream, a);
 }
 
 }  // namespace dbv
