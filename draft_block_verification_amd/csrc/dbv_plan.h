@@ -72,7 +72,8 @@ inline int choose_draw_chunks(int64_t B, int64_t V) {
   int64_t s = cdiv(1024, B > 0 ? B : 1);
   const int64_t cap = V / 2048 > 0 ? V / 2048 : 1;
   if (s > cap) s = cap;
-  const int64_t need = cdiv(V, kDrawChunkMax);
+  if (s > kMaxDrawChunks) s = kMaxDrawChunks;
+  const int64_t need = cdiv(V, kDrawChunkMax);   // <= kMaxDrawChunks for V <= kMaxSampleV
   if (s < need) s = need;
   return s < 1 ? 1 : static_cast<int>(s);
 }
@@ -159,8 +160,11 @@ inline TreePlan plan_tree(int B, int S, int L, int V) {
   // Many rows: a whole row per item keeps the per-position combine short.
   p.r = plan_rows(static_cast<int64_t>(B) * S * L, V, V > kChunkMax ? V : kChunkMax);
   p.states = static_cast<int64_t>(B) * S;
+  // The Gumbel argmax keeps no chunk in registers, so its chunks only need to
+  // cover the row: ceil(V / split2) rounded up to 256 elements.
   p.split2 = choose_split(p.states, V);
-  p.chunk2 = chunk_len(V, p.split2);
+  p.chunk2 = cdiv(cdiv(V, p.split2), 256) * 256;
+  p.split2 = static_cast<int>(cdiv(V, p.chunk2));
   p.off_conf = 0;
   p.off_pick = p.r.part_bytes;
   p.off_sel = p.off_pick + align256(static_cast<size_t>(p.states) * p.split2 * 8);

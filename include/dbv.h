@@ -230,11 +230,13 @@ size_t verify_workspace_size(dbv_kind kind, int B, int K_or_S, int L, int V, dbv
 
 /*
  * verify_set_timing_events -- diagnostics hook.  With two non-NULL hipEvent_t
- * handles, every later verify_* call records `begin` on its stream just before
+ * handles (created with timing enabled), every later verify_* call launches
  * its row-streaming kernel (the launch that reads the logit rows: row
- * statistics / argmax, or the tree's per-row confidences) and `end` just
- * after it, so that kernel's own duration can be read with
- * hipEventElapsedTime.  (NULL, NULL) turns it off.  A process-wide setting
+ * statistics / argmax, or the tree's per-row confidences) through
+ * hipExtLaunchKernel with these events, which the runtime stamps at that
+ * kernel's own start and end; hipEventElapsedTime then gives its duration
+ * without the launch gap.  If the kernel has no rows to read, both events are
+ * recorded back to back.  (NULL, NULL) turns it off.  A process-wide setting
  * for benchmarking; not meant for concurrent calls.
  */
 void verify_set_timing_events(void* begin, void* end);

@@ -1,0 +1,192 @@
+"""Parity at the benchmark workloads' full sizes, in the launch configuration
+the benchmark times (same entry points, shapes, dtypes and strides, so the
+same launch plan).
+
+Where the float64 oracle over a whole batch would take minutes, it runs on a
+seeded sample of sequences and every sequence is checked through properties
+that hold at any size:
+
+  * tiny rejection verify   B=1  K=4  V=1024   fp32  -- oracle on everything
+  * batch lossless verify   B=8  K=8  V=32000  bf16  -- oracle on everything
+  * lenient sweep           B=32 K=16 V=128256 bf16, sigma x T x lambda --
+    oracle on 4 sequences per setting; on all 32: lambda = 0 equals the
+    lossless entry point bit for bit, lambda = 1 accepts every draft, and the
+    accepted length does not fall as lambda rises (common uniforms)
+  * Gumbel tree verify      B=16 S=64 L=32 V=151936 bf16 -- oracle on 3
+    trees; on all 16 the walk is redone from the GPU's per-state choices
+  * packed greedy           B=64 K=31 W=32 V=131072 bf16 -- oracle on every
+    sequence (one at a time), with and without the stopping rule
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import draft_block_verification_amd as dbv
+import oracle
+import workloads
+from tests.parity import check_greedy, check_sampling, check_tree, np64, npi
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _take(res, seqs):
+    """Rows `seqs` of every per-sequence output."""
+    idx = torch.as_tensor(seqs, dtype=torch.long)
+    return {k: v.detach().cpu()[idx] for k, v in res.items()}
+
+
+def _sample(B, k, seed):
+    g = torch.Generator().manual_seed(seed)
+    return sorted(torch.randperm(B, generator=g)[:k].tolist())
+
+
+def _chain_np(x, seqs=None):
+    keys = ("tgt", "drf", "draft_tokens", "draft_len", "u_accept", "u_resample")
+    out = {}
+    for k in keys:
+        v = x[k] if seqs is None else x[k][torch.as_tensor(seqs, dtype=torch.long)]
+        out[k] = np64(v) if v.dtype.is_floating_point else npi(v)
+    return out
+
+
+def _sampling_call(x, dev, lam=None, T=1.0, **kw):
+    args = (x["tgt"].to(dev), x["drf"].to(dev), x["draft_tokens"].to(dev), x["u_accept"].to(dev),
+            x["u_resample"].to(dev))
+    common = dict(draft_len=x["draft_len"].to(dev), temperature_target=T, temperature_draft=T, **kw)
+    if lam is None:
+        return dbv.verify_rejection(*args, **common)
+    return dbv.verify_lenient(*args, lam, **common)
+
+
+# ---------------------------------------------------------------- chains ---
+
+def test_full_tiny_rejection_and_greedy(dev):
+    say("full tiny B=1 K=4 V=1024 fp32")
+    x = workloads.config1()
+    xn = _chain_np(x)
+    res = _sampling_call(x, dev)
+    o = oracle.verify_rejection(xn["tgt"], xn["drf"], xn["draft_tokens"], xn["draft_len"], 1.0, 1.0,
+                                xn["u_accept"], xn["u_resample"])
+    check_sampling(res, xn, o, 0.0, 1.0, 1.0, "float32")
+    for name, d in (("argmax drafts", x["greedy_tokens"]), ("sampled drafts", x["draft_tokens"])):
+        say("greedy", name)
+        g = dbv.verify_greedy(x["tgt"].to(dev), d.to(dev), x["draft_len"].to(dev), x["drf"].to(dev))
+        og = oracle.verify_greedy(xn["tgt"], npi(d), xn["draft_len"], xn["drf"])
+        check_greedy(g, og)
+
+
+def test_full_batch_lossless(dev):
+    say("full batch lossless B=8 K=8 V=32000 bf16")
+    x = workloads.config2()
+    xn = _chain_np(x)
+    res = _sampling_call(x, dev)
+    o = oracle.verify_rejection(xn["tgt"], xn["drf"], xn["draft_tokens"], xn["draft_len"], 1.0, 1.0,
+                                xn["u_accept"], xn["u_resample"])
+    near = check_sampling(res, xn, o, 0.0, 1.0, 1.0, "bfloat16")
+    say("near-margin", dict(near), "accept_len", list(o["accept_len"]))
+
+
+@pytest.mark.parametrize("T", [0.7, 1.0])
+@pytest.mark.parametrize("sigma", workloads.C3_SIGMAS)
+def test_full_lenient_sweep(dev, sigma, T):
+    say("full lenient B=32 K=16 V=128256 bf16 sigma", sigma, "T", T)
+    x = workloads.config3(sigma, T)
+    B = x["tgt"].shape[0]
+    seqs = _sample(B, 4, int(sigma * 100 + T * 10))
+    xs = _chain_np(x, seqs)
+    n = npi(x["draft_len"])
+    lossless = _sampling_call(x, dev, None, T)
+    h_prev = None
+    for lam in (0.0,) + tuple(sorted(workloads.C3_LAMBDAS)):
+        res = _sampling_call(x, dev, lam, T)
+        if lam == 0.0:
+            for k in lossless:
+                assert torch.equal(lossless[k], res[k]), k
+        h = npi(res["accept_len"])
+        if lam == 1.0:
+            np.testing.assert_array_equal(h, n)
+        o = oracle.verify_lenient(xs["tgt"], xs["drf"], xs["draft_tokens"], xs["draft_len"], T, T, lam,
+                                  xs["u_accept"], xs["u_resample"])
+        near = check_sampling(_take(res, seqs), xs, o, lam, T, T, "bfloat16")
+        if h_prev is not None:
+            # A fall in h as lambda rises can only come from near-margin
+            # decisions: check those sequences against the oracle as well.
+            bad = [b for b in range(B) if h[b] < h_prev[b]]
+            if bad:
+                xb = _chain_np(x, bad)
+                ob = oracle.verify_lenient(xb["tgt"], xb["drf"], xb["draft_tokens"], xb["draft_len"], T, T,
+                                           lam, xb["u_accept"], xb["u_resample"])
+                check_sampling(_take(res, bad), xb, ob, lam, T, T, "bfloat16")
+        h_prev = h
+        say(f"lambda={lam} mean accept length {h.mean():.3f} (sampled near-margin {dict(near)})")
+
+
+# ------------------------------------------------------------------ tree ---
+
+def test_full_gumbel_tree(dev):
+    say("full tree B=16 S=64 L=32 V=151936 bf16")
+    x = workloads.config4(device=dev)
+    B, S, L, V = x["logits"].shape
+    res = dbv.verify_gumbel_tree(x["logits"], x["parent"].to(dev), x["edge_pos"].to(dev),
+                                 x["edge_tok"].to(dev), masked=x["masked"].to(dev), gumbel=x["gumbel"],
+                                 temperature=1.0, num_states=x["num_states"].to(dev))
+    r = {k: v.cpu() for k, v in res.items()}
+    assert int((r["status"] & dbv.SEQ_ERROR_MASK).sum()) == 0
+    # Every tree: the walk from the GPU's own per-state choices.
+    for b in range(B):
+        ns = int(x["num_states"][b])
+        path, commits = oracle.walk(npi(x["parent"][b]), npi(x["edge_pos"][b]), npi(x["edge_tok"][b]), ns,
+                                    [int(v) for v in r["sel_pos"][b, :ns]], [int(v) for v in r["sel_tok"][b, :ns]])
+        assert int(r["path_len"][b]) == len(path) - 1, b
+        assert [int(v) for v in r["path_nodes"][b, :len(path)]] == path, b
+        assert int(r["num_commits"][b]) == len(commits), b
+        got = list(zip(r["commit_pos"][b, :len(commits)].tolist(), r["commit_tok"][b, :len(commits)].tolist()))
+        assert got == [tuple(c) for c in commits], b
+    say("path lengths", r["path_len"].tolist())
+    # Sampled trees: everything against the oracle.
+    for b in _sample(B, 3, 4):
+        say("oracle tree", b)
+        xb = dict(logits=np64(x["logits"][b:b + 1]), gumbel=np64(x["gumbel"][b:b + 1]),
+                  parent=npi(x["parent"][b:b + 1]), edge_pos=npi(x["edge_pos"][b:b + 1]),
+                  edge_tok=npi(x["edge_tok"][b:b + 1]), num_states=npi(x["num_states"][b:b + 1]))
+        o = oracle.verify_gumbel_tree(xb["logits"], x["masked"][b:b + 1].numpy(), xb["parent"], xb["edge_pos"],
+                                      xb["edge_tok"], xb["num_states"], xb["gumbel"], 1.0)
+        near = check_tree(_take(res, [b]), xb, o, "bfloat16", 1.0)
+        say("near", dict(near))
+        del xb, o
+
+
+# ---------------------------------------------------------------- greedy ---
+
+@pytest.mark.parametrize("stopping", [False, True])
+def test_full_packed_greedy(dev, stopping):
+    say("full packed greedy B=64 K=31 W=32 V=131072 bf16, stopping", stopping)
+    x = workloads.config5()
+    K = x["K"]
+    p = x["packed"].to(dev)
+    B = p.shape[0]
+    kw = {}
+    if stopping:
+        # EOS = the verifier argmax of one seeded row; budgets over [0, K+1].
+        g = torch.Generator().manual_seed(55)
+        b0 = int(torch.randint(0, B, (1,), generator=g))
+        kw["eos_id"] = int(torch.argmax(x["packed"][b0, 0].float()))
+        kw["len_budget"] = torch.randint(0, K + 2, (B,), generator=g).to(torch.int32)
+    res = dbv.verify_greedy(p[:, :K + 1], x["draft_tokens"].to(dev), x["draft_len"].to(dev), p[:, K + 1:],
+                            **{k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in kw.items()})
+    r = {k: v.cpu() for k, v in res.items()}
+    for b in range(B):
+        o = oracle.verify_greedy(np64(x["packed"][b:b + 1, :K + 1]), npi(x["draft_tokens"][b:b + 1]),
+                                 npi(x["draft_len"][b:b + 1]), np64(x["packed"][b:b + 1, K + 1:]),
+                                 eos_id=kw.get("eos_id", -1),
+                                 len_budget=None if not stopping else npi(kw["len_budget"][b:b + 1]))
+        check_greedy(_take(r, [b]), o)
+    say("mean accept length", float(r["accept_len"].float().mean()), "mean emitted", float(r["num_out"].float().mean()))
