@@ -62,14 +62,6 @@ dbv_status device_ready() {
   return DBV_OK;
 }
 
-dbv::RowItems items_of(const dbv::RowPlan& r) {
-  dbv::RowItems it;
-  it.chunk = r.chunk;
-  it.nchunk = r.nchunk;
-  it.items = r.items;
-  return it;
-}
-
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 size_t elem_bytes(dbv_dtype dt) { return dt == DBV_BF16 ? 2 : 4; }
@@ -83,6 +75,11 @@ dbv_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 }
 
 bool temp_ok(float t) { return std::isfinite(t) && t > 0.f; }
+
+// Stream rows are indexed in 32 bits on the device; element offsets in 64.
+bool stream_fits(int64_t max_rows, int64_t V) {
+  return max_rows < (int64_t(1) << 31) && max_rows * V < (int64_t(1) << 52);
+}
 
 dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t ts, int64_t tr,
                          const void* drf, int64_t ds, int64_t dr, const int32_t* draft_tokens,
@@ -101,7 +98,7 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   const size_t eb = elem_bytes(dtype);
   if (!aligned(tgt, eb) || (drf && !aligned(drf, eb))) return DBV_ERR_INVALID_ARG;
   const dbv::SamplePlan plan = dbv::plan_sample(B, K, V);
-  if (plan.r.items >= (int64_t(1) << 31)) return DBV_ERR_UNSUPPORTED;
+  if (!stream_fits(plan.max_rows, V)) return DBV_ERR_UNSUPPORTED;
   dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
   if (s != DBV_OK) return s;
   if ((s = device_ready()) != DBV_OK) return s;
@@ -121,9 +118,10 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.status = status;
   char* w = static_cast<char*>(ws);
   a.stats = reinterpret_cast<float2*>(w + plan.off_stats);
+  a.pre = reinterpret_cast<int32_t*>(w + plan.off_pre);
   a.rec = reinterpret_cast<dbv::DrawRecord*>(w + plan.off_rec);
   a.dsum = reinterpret_cast<float*>(w + plan.off_dsum);
-  a.it = items_of(plan.r);
+  a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(eb), dbv::resident_groups());
   a.draw_chunks = plan.draw_chunks; a.draw_chunk = plan.draw_chunk;
   return dbv::launch_sample(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
 }
@@ -132,17 +130,15 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
 
 namespace dbv {
 
-// Resident groups of the current device (kResidentPerCU per CU), at most the
-// number of items.
-int64_t persistent_grid(int64_t items) {
+// Resident groups of the current device (kResidentPerCU per CU).
+int64_t resident_groups() {
   int dev = 0;
   int cus = 256;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
     const int c = g_cus[dev].load(std::memory_order_relaxed);
     if (c > 0) cus = c;
   }
-  const int64_t g = static_cast<int64_t>(cus) * kResidentPerCU;
-  return items < g ? items : g;
+  return static_cast<int64_t>(cus) * kResidentPerCU;
 }
 
 }  // namespace dbv
@@ -165,7 +161,7 @@ dbv_status verify_greedy(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   const size_t eb = elem_bytes(dtype);
   if (!aligned(tgt, eb) || (draft_rows && !aligned(draft_rows, eb))) return DBV_ERR_INVALID_ARG;
   const dbv::GreedyPlan plan = dbv::plan_greedy(B, K, W, V);
-  if (plan.r.items >= (int64_t(1) << 31)) return DBV_ERR_UNSUPPORTED;
+  if (!stream_fits(plan.max_rows, V)) return DBV_ERR_UNSUPPORTED;
   dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
   if (s != DBV_OK) return s;
   if ((s = device_ready()) != DBV_OK) return s;
@@ -180,7 +176,9 @@ dbv_status verify_greedy(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.accept_len = accept_len; a.out_tokens = out_tokens; a.num_out = num_out;
   a.next_draft = next_draft; a.next_len = next_len; a.status = status;
   a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + plan.off_part);
-  a.it = items_of(plan.r);
+  a.pre = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan.off_pre);
+  a.elem_bytes = static_cast<int>(eb);
+  a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(eb), dbv::resident_groups());
   return dbv::launch_greedy(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
 }
 
@@ -235,7 +233,7 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const
     return DBV_ERR_INVALID_ARG;
   if (!aligned(logits, elem_bytes(dtype)) || (gumbel && !aligned(gumbel, 4))) return DBV_ERR_INVALID_ARG;
   const dbv::TreePlan plan = dbv::plan_tree(B, S, L, V);
-  if (plan.r.items >= (int64_t(1) << 31)) return DBV_ERR_UNSUPPORTED;
+  if (!stream_fits(plan.max_rows, V)) return DBV_ERR_UNSUPPORTED;
   dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
   if (s != DBV_OK) return s;
   if ((s = device_ready()) != DBV_OK) return s;
@@ -254,10 +252,13 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const
   a.commit_pos = commit_pos; a.commit_tok = commit_tok; a.num_commits = num_commits;
   a.status = status;
   char* w = static_cast<char*>(ws);
+  a.count = reinterpret_cast<int32_t*>(w + plan.off_count);
+  a.list = reinterpret_cast<int32_t*>(w + plan.off_list);
+  a.map = reinterpret_cast<int32_t*>(w + plan.off_map);
   a.conf = reinterpret_cast<float2*>(w + plan.off_conf);
   a.pick = reinterpret_cast<float2*>(w + plan.off_pick);
   a.sel = reinterpret_cast<int32_t*>(w + plan.off_sel);
-  a.it = items_of(plan.r);
+  a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(elem_bytes(dtype)), dbv::resident_groups());
   a.split2 = plan.split2; a.chunk2 = plan.chunk2;
   return dbv::launch_tree(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
 }

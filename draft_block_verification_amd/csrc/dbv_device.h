@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dbv_plan.h"
+
 namespace dbv {
 
 constexpr int kBlock = 256;            // threads per workgroup: 4 wave64
@@ -295,48 +297,170 @@ __device__ __forceinline__ void wave_argmax(float& v, int& idx, int& nan) {
   }
 }
 
-// Persistent grid-stride loop over work items.  The validity of the next item
-// (usually one small load) is requested before the current item is streamed,
-// so skipped items cost no exposed latency.
-// Item indices are 32-bit (the host keeps plans below 2^31 items): 64-bit
-// integer division is a long software sequence on this GPU.
-template <class ValidFn, class BodyFn>
-__device__ __forceinline__ void for_items(uint32_t items, ValidFn valid, BodyFn body) {
-  uint32_t it = blockIdx.x;
-  bool ok = it < items && valid(it);
-  while (it < items) {
-    const uint32_t nx = it + gridDim.x;
-    const bool nok = nx < items && valid(nx);
-    if (ok) body(it);
-    it = nx;
-    ok = nok;
+// ---------------------------------------------------------------------------
+// Flat split helpers (the split itself is defined in dbv_plan.h).
+// ---------------------------------------------------------------------------
+
+// Visits the pieces of active group g in stream order: fn(r, v0, v1) for each
+// stream row r that meets the group's range, [v0, v1) being the part of the
+// row inside it.
+template <class Fn>
+__device__ __forceinline__ void for_pieces(const FlatSplit& f, int64_t g, Fn fn) {
+  int64_t e0, e1;
+  split_range(f, g, e0, e1);
+  int64_t r = e0 / f.V;
+  for (int64_t base = r * f.V; base < e1; ++r, base += f.V) {
+    const int64_t v0 = e0 > base ? e0 - base : 0;
+    const int64_t v1 = e1 < base + f.V ? e1 - base : f.V;
+    fn(r, v0, v1);
   }
 }
 
+// Exclusive scan of one int per thread over a group of NW waves, in thread
+// order; returns the thread's offset and sets `total`.  Two barriers.
+template <int NW>
+__device__ __forceinline__ int group_exclusive_scan(int v, int& total, int* s_w) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int o = __shfl_up(inc, m, 64);
+    if (lane >= m) inc += o;
+  }
+  if (lane == 63) s_w[w] = inc;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const int x = s_w[j];
+    if (j < w) base += x;
+    total += x;
+  }
+  __syncthreads();
+  return base + inc - v;
+}
+
 // ---------------------------------------------------------------------------
-// Combining the per-(item, wave) partials of many rows inside one group:
+// Sequence directory of a chain call's stream, rebuilt in LDS by every group:
+// sequence b contributes count(b) consecutive stream rows.  Sequences are
+// taken in blocks of q (at most kSeqBlocks blocks); pre[j] is the first
+// stream row of block j and pre[nblk] the number of rows R.
+// ---------------------------------------------------------------------------
+struct SeqDir {
+  int q;
+  int nblk;
+};
+
+template <class CountFn>
+__device__ __forceinline__ SeqDir build_seq_dir(int B, CountFn count, int* pre, int* s_w) {
+  SeqDir d;
+  d.q = static_cast<int>(cdiv(B, kSeqBlocks));
+  d.nblk = static_cast<int>(cdiv(B, d.q));
+  constexpr int kPer = kSeqBlocks / kBlock;     // blocks per thread
+  int sums[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int j = threadIdx.x * kPer + k;
+    int s = 0;
+    if (j < d.nblk) {
+      const int b1 = (j + 1) * d.q < B ? (j + 1) * d.q : B;
+      for (int b = j * d.q; b < b1; ++b) s += count(b);
+    }
+    sums[k] = s;
+    mine += s;
+  }
+  int total;
+  int off = group_exclusive_scan<kWaves>(mine, total, s_w);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int j = threadIdx.x * kPer + k;
+    if (j < d.nblk) pre[j] = off;
+    off += sums[k];
+  }
+  if (threadIdx.x == 0) pre[d.nblk] = total;
+  __syncthreads();
+  return d;
+}
+
+// The sequence holding stream row r (0 <= r < R), its first stream row and
+// its row count.  With one sequence per block (B <= kSeqBlocks) everything
+// comes from the LDS prefix; otherwise the block is walked with count().
+template <class CountFn>
+__device__ __forceinline__ int find_seq(const SeqDir& d, const int* pre, int r, CountFn count, int& first,
+                                        int& cnt) {
+  int lo = 0, hi = d.nblk - 1;
+  while (lo < hi) {  // largest block j with pre[j] <= r
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  if (d.q == 1) {
+    first = pre[lo];
+    cnt = pre[lo + 1] - first;
+    return lo;
+  }
+  int b = lo * d.q;
+  int acc = pre[lo];
+  for (;;) {
+    const int c = count(b);
+    if (acc + c > r) {
+      cnt = c;
+      break;
+    }
+    acc += c;
+    ++b;
+  }
+  first = acc;
+  return b;
+}
+
+// Group 0 writes the first stream row of every sequence, pre_out[b], and
+// pre_out[B] = R, for the kernels that follow.
+template <class CountFn>
+__device__ __forceinline__ void write_seq_starts(const SeqDir& d, const int* pre, int B, CountFn count,
+                                                 int32_t* pre_out) {
+  for (int j = threadIdx.x; j < d.nblk; j += kBlock) {
+    int acc = pre[j];
+    const int b1 = (j + 1) * d.q < B ? (j + 1) * d.q : B;
+    for (int b = j * d.q; b < b1; ++b) {
+      pre_out[b] = acc;
+      acc += count(b);
+    }
+  }
+  if (threadIdx.x == 0) pre_out[B] = pre[d.nblk];
+}
+
+// ---------------------------------------------------------------------------
+// Combining the per-(slot, wave) partials of many rows inside one group:
 // kRowLanes lanes share a row, each loading up to kRowLoads of its partials
 // before merging (the loads are issued together), then a shuffle tree over
-// the row's lanes.  Calls fn(row, lane-0 result) once per row.
+// the row's lanes.  span(r, first, n) gives row r's partials as the n
+// consecutive float2 at part + first.  Calls done(r, lane-0 result) once per
+// row.
 // ---------------------------------------------------------------------------
 constexpr int kRowLanes = 8;
 constexpr int kRowLoads = 8;
 
-template <class PartFn, class DoneFn>
-__device__ __forceinline__ void combine_rows_stats(int nrows, int64_t per_row, float k, PartFn part,
+template <class SpanFn, class DoneFn>
+__device__ __forceinline__ void combine_rows_stats(int nrows, const float2* part, float k, SpanFn span,
                                                    DoneFn done) {
   const int sub = threadIdx.x % kRowLanes;
   for (int r0 = 0; r0 < nrows; r0 += kBlock / kRowLanes) {
     const int r = r0 + static_cast<int>(threadIdx.x) / kRowLanes;
     float M = -kInf, S = 0.f;
     if (r < nrows) {
-      const float2* p = part(r);
-      for (int64_t j0 = 0; j0 < per_row; j0 += kRowLanes * kRowLoads) {
+      int64_t first, n;
+      span(r, first, n);
+      const float2* p = part + first;
+      for (int64_t j0 = 0; j0 < n; j0 += kRowLanes * kRowLoads) {
         float2 buf[kRowLoads];
 #pragma unroll
         for (int q = 0; q < kRowLoads; ++q) {
           const int64_t j = j0 + sub + static_cast<int64_t>(q) * kRowLanes;
-          buf[q] = j < per_row ? p[j] : make_float2(-kInf, 0.f);
+          buf[q] = j < n ? p[j] : make_float2(-kInf, 0.f);
         }
 #pragma unroll
         for (int q = 0; q < kRowLoads; ++q) stats_merge(M, S, buf[q].x, buf[q].y, k);
@@ -352,21 +476,23 @@ __device__ __forceinline__ void combine_rows_stats(int nrows, int64_t per_row, f
   }
 }
 
-template <class PartFn, class DoneFn>
-__device__ __forceinline__ void combine_rows_pick(int nrows, int64_t per_row, PartFn part, DoneFn done) {
+template <class SpanFn, class DoneFn>
+__device__ __forceinline__ void combine_rows_pick(int nrows, const float2* part, SpanFn span, DoneFn done) {
   const int sub = threadIdx.x % kRowLanes;
   for (int r0 = 0; r0 < nrows; r0 += kBlock / kRowLanes) {
     const int r = r0 + static_cast<int>(threadIdx.x) / kRowLanes;
     float v = -kInf;
     int idx = -1, nan = 0;
     if (r < nrows) {
-      const float2* p = part(r);
-      for (int64_t j0 = 0; j0 < per_row; j0 += kRowLanes * kRowLoads) {
+      int64_t first, n;
+      span(r, first, n);
+      const float2* p = part + first;
+      for (int64_t j0 = 0; j0 < n; j0 += kRowLanes * kRowLoads) {
         float2 buf[kRowLoads];
 #pragma unroll
         for (int q = 0; q < kRowLoads; ++q) {
           const int64_t j = j0 + sub + static_cast<int64_t>(q) * kRowLanes;
-          buf[q] = j < per_row ? p[j] : make_float2(-kInf, __int_as_float(-1));
+          buf[q] = j < n ? p[j] : make_float2(-kInf, __int_as_float(-1));
         }
 #pragma unroll
         for (int q = 0; q < kRowLoads; ++q) {
@@ -386,6 +512,15 @@ __device__ __forceinline__ void combine_rows_pick(int nrows, int64_t per_row, Pa
     }
     if (r < nrows && sub == 0) done(r, v, idx, nan);
   }
+}
+
+// Serial merge of one row's partials (one thread).
+__device__ __forceinline__ void merge_span_stats(const float2* part, int64_t first, int64_t n, float k,
+                                                 float& M, float& S) {
+  M = -kInf;
+  S = 0.f;
+  const float2* p = part + first;
+  for (int64_t j = 0; j < n; ++j) stats_merge(M, S, p[j].x, p[j].y, k);
 }
 
 // Row status from a reduced maximum: NaN / +inf -> nonfinite, -inf -> empty.

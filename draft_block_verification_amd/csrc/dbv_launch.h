@@ -9,14 +9,6 @@
 
 namespace dbv {
 
-// Items of a persistent row-streaming launch: `rows` rows of `nchunk`
-// vocabulary chunks of `chunk` elements; item = row * nchunk + chunk index.
-struct RowItems {
-  int64_t chunk;
-  int64_t nchunk;
-  int64_t items;
-};
-
 struct GreedyArgs {
   int B, K, V, W;
   const void* tgt; int64_t ts, tr;     // target rows: element strides
@@ -27,8 +19,10 @@ struct GreedyArgs {
   const int32_t* budget;
   int32_t* accept_len; int32_t* out_tokens; int32_t* num_out;
   int32_t* next_draft; int32_t* next_len; int32_t* status;
-  float2* part;                        // per (item, wave)
-  RowItems it;
+  float2* part;                        // per (slot, wave)
+  int32_t* pre;                        // [B + 1] first stream row per sequence
+  int64_t grid;                        // groups of the row-streaming launch
+  int elem_bytes;                      // 2 (bf16) or 4 (fp32)
 };
 
 struct SampleArgs {
@@ -45,10 +39,11 @@ struct SampleArgs {
   int32_t* accept_len; int32_t* out_tokens; int32_t* num_out;
   float* p_draft; float* q_draft; float* alpha; float* residual_mass;
   int32_t* status;
-  float2* stats;                       // per (item, wave)
+  float2* stats;                       // per (slot, wave)
+  int32_t* pre;                        // [B + 1] first stream row per sequence
   DrawRecord* rec;                     // per sequence
   float* dsum;                         // per (sequence, draw chunk)
-  RowItems it;
+  int64_t grid;                        // groups of the row-streaming launch
   int draw_chunks;
   int64_t draw_chunk;
 };
@@ -66,10 +61,13 @@ struct TreeArgs {
   int32_t* path_len; int32_t* path_nodes;
   int32_t* commit_pos; int32_t* commit_tok; int32_t* num_commits;
   int32_t* status;
-  float2* conf;                              // per (item, wave)
+  int32_t* count;                            // rows in the stream
+  int32_t* list;                             // stream row -> flat row id
+  int32_t* map;                              // flat row id -> stream row or -1
+  float2* conf;                              // per (slot, wave)
   float2* pick;                              // per (state, split2)
   int32_t* sel;                              // per state
-  RowItems it;
+  int64_t grid;                              // groups of the row-streaming launch
   int split2; int64_t chunk2;
 };
 
@@ -79,25 +77,31 @@ struct TimingEvents {
   hipEvent_t end = nullptr;
 };
 
-// Launch `kern(arg)` on `grid` groups of 256 threads.  With timing events the
-// launch goes through hipExtLaunchKernel, which stamps the events at the
-// kernel's own start and end (no launch gap in the interval); an empty grid
-// still records both events so that the caller can read them.
+// Launch `kern(arg)` on `grid` groups of `threads` threads.  With timing
+// events the launch goes through hipExtLaunchKernel, which stamps the events
+// at the kernel's own start and end (no launch gap in the interval); an empty
+// grid still records both events so that the caller can read them.
 template <typename Arg>
-bool launch(const void* kern, int64_t grid, hipStream_t stream, const Arg& arg,
-            const TimingEvents& ev = TimingEvents()) {
+bool launch_threads(const void* kern, int64_t grid, int threads, hipStream_t stream, const Arg& arg,
+                    const TimingEvents& ev = TimingEvents()) {
   if (grid <= 0) {
     if (ev.begin) (void)hipEventRecord(ev.begin, stream);
     if (ev.end) (void)hipEventRecord(ev.end, stream);
     return true;
   }
   void* args[] = {const_cast<Arg*>(&arg)};
-  return hipExtLaunchKernel(kern, dim3(static_cast<unsigned>(grid)), dim3(256), args, 0, stream,
+  return hipExtLaunchKernel(kern, dim3(static_cast<unsigned>(grid)), dim3(threads), args, 0, stream,
                             ev.begin, ev.end, 0) == hipSuccess;
 }
 
-// Grid of a persistent launch: at most the resident groups of the device.
-int64_t persistent_grid(int64_t items);
+template <typename Arg>
+bool launch(const void* kern, int64_t grid, hipStream_t stream, const Arg& arg,
+            const TimingEvents& ev = TimingEvents()) {
+  return launch_threads(kern, grid, 256, stream, arg, ev);
+}
+
+// Resident groups of the current device (kResidentPerCU per CU).
+int64_t resident_groups();
 
 bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
 bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);

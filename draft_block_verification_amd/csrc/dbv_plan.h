@@ -1,62 +1,106 @@
 // Launch plan and workspace layout: a pure function of the call's sizes, so
-// verify_workspace_size() and the launchers always agree.  (The grid size of
-// the persistent kernels depends on the device and is chosen at launch; it
-// does not change the workspace.)
+// verify_workspace_size() and the launchers always agree.  The split of the
+// streamed rows over the groups of a launch (FlatSplit) is computed on the
+// device from the rows a call actually needs, with the same inline functions
+// the host uses to size the workspace for the largest possible row count.
 #pragma once
 
 #include <stddef.h>
 #include <stdint.h>
 
+#if defined(__HIPCC__)
+#define DBV_HD __host__ __device__
+#else
+#define DBV_HD
+#endif
+
 namespace dbv {
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 
-// Row-streaming kernels are persistent: about kResidentPerCU groups per CU
-// walk a list of (row, vocabulary chunk) items in grid-stride order, so the
-// tail of a launch is one small chunk, not one long row.  Each of a group's
-// kWavesPlan waves reduces its share of an item and writes its own partial.
+// Row-streaming kernels are persistent: at most kMaxGrid groups of 256
+// threads share the needed rows.  On 256 CUs that is 4 groups (16 waves,
+// 64 KiB of 16-byte loads in flight) per CU, which measured faster than 2, 3,
+// 6 or 8 groups per CU on every workload; kResidentPerCU bounds the grid on
+// smaller devices.
 constexpr int kResidentPerCU = 8;
 constexpr int kWavesPlan = 4;             // waves per 256-thread group
-constexpr int64_t kPlanGroups = 2048;     // 256 CUs x 8 resident groups
-constexpr int64_t kChunkMin = 2048;
-constexpr int64_t kChunkMax = 32768;
-constexpr int64_t kItemsPerGroup = 4;
+constexpr int64_t kMaxGrid = 1024;
+constexpr int64_t kUnitBytes = 4096;      // granularity of a group's range
 constexpr int kMaxSplit = 64;
 constexpr int kMaxDraft = 1024;       // K and W limit of the chain modes
 constexpr int kMaxStates = 1024;      // S limit of the tree mode
 constexpr int kMaxBlockLen = 1024;    // L limit of the tree mode
+constexpr int kSeqBlocks = 1024;      // LDS prefix entries over sequences
 
-inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+DBV_HD inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Chunk length (elements, multiple of 256) for `rows` rows of length V: about
-// kItemsPerGroup items per resident group, within [kChunkMin, max_chunk],
-// never longer than the row.
-inline int64_t choose_chunk(int64_t rows, int64_t V, int64_t max_chunk = kChunkMax) {
-  int64_t c = cdiv(rows * V, kItemsPerGroup * kPlanGroups);
-  if (c < kChunkMin) c = kChunkMin;
-  if (c > max_chunk) c = max_chunk;
-  c = cdiv(c, 256) * 256;
-  const int64_t whole = cdiv(V, 256) * 256;
-  return c < whole ? c : whole;
-}
-
-struct RowPlan {
-  int64_t rows;
-  int64_t chunk;     // elements per item
-  int64_t nchunk;    // items per row
-  int64_t items;     // rows * nchunk
-  size_t part_bytes; // float2 partial per (item, wave)
+// ---------------------------------------------------------------------------
+// Flat split.  The R needed rows of a call, in a fixed order, form one
+// stream of E = R*V elements.  It is cut into NQ units of Q elements (Q*eb =
+// kUnitBytes) and group g of the G active groups owns the units
+// [g*NQ/G, (g+1)*NQ/G): a contiguous element range, equal to within one
+// unit for every group, which may start and end inside rows.  G = min(grid,
+// NQ), so no active group is empty.
+//
+// The piece of row r inside group g's range is reduced to one partial per
+// wave, stored at slot (r + g) * waves + wave.  Along the stream each next
+// piece advances r, g or both, so r + g is unique per piece and below R + G;
+// the partials of one row are the contiguous slots of its groups
+// g_lo(r)..g_hi(r).
+// ---------------------------------------------------------------------------
+struct FlatSplit {
+  int64_t V;    // row length (elements)
+  int64_t R;    // rows in the stream
+  int64_t Q;    // elements per unit
+  int64_t NQ;   // units, ceil(R * V / Q)
+  int64_t G;    // active groups
 };
 
-inline RowPlan plan_rows(int64_t rows, int64_t V, int64_t max_chunk = kChunkMax) {
-  RowPlan r{};
-  r.rows = rows;
-  r.chunk = choose_chunk(rows, V, max_chunk);
-  r.nchunk = cdiv(V, r.chunk);
-  r.items = rows * r.nchunk;
-  r.part_bytes = align256(static_cast<size_t>(r.items) * kWavesPlan * 8);
-  return r;
+DBV_HD inline FlatSplit make_split(int64_t R, int64_t V, int64_t elem_bytes, int64_t grid) {
+  FlatSplit f;
+  f.V = V;
+  f.R = R;
+  f.Q = kUnitBytes / elem_bytes;
+  f.NQ = cdiv(R * V, f.Q);
+  f.G = f.NQ < grid ? f.NQ : grid;
+  return f;
+}
+
+// Element range [e0, e1) of active group g; never empty.
+DBV_HD inline void split_range(const FlatSplit& f, int64_t g, int64_t& e0, int64_t& e1) {
+  const int64_t E = f.R * f.V;
+  e0 = (g * f.NQ / f.G) * f.Q;
+  e1 = ((g + 1) * f.NQ / f.G) * f.Q;
+  if (e1 > E) e1 = E;
+}
+
+// The active group whose range holds element e (0 <= e < R*V): the largest g
+// with floor(g*NQ/G) <= e / Q.
+DBV_HD inline int64_t split_group(const FlatSplit& f, int64_t e) {
+  return ((e / f.Q + 1) * f.G - 1) / f.NQ;
+}
+
+// First partial slot (in units of waves) and number of groups of row r.
+DBV_HD inline void split_row_slots(const FlatSplit& f, int64_t r, int64_t& first, int64_t& ngroups) {
+  const int64_t glo = split_group(f, r * f.V);
+  const int64_t ghi = split_group(f, r * f.V + f.V - 1);
+  first = r + glo;
+  ngroups = ghi - glo + 1;
+}
+
+// Launch grid of a streaming kernel: enough groups for the largest stream
+// the call can need, at most kMaxGrid and the resident groups of the device.
+inline int64_t stream_grid(int64_t max_rows, int64_t V, int64_t elem_bytes, int64_t resident) {
+  const int64_t units = cdiv(max_rows * V, kUnitBytes / elem_bytes);
+  int64_t g = resident < kMaxGrid ? resident : kMaxGrid;
+  return units < g ? units : g;
+}
+
+// Bytes of the per-(slot, wave) float2 partials for up to max_rows rows.
+inline size_t partial_bytes(int64_t max_rows) {
+  return align256(static_cast<size_t>(max_rows + kMaxGrid) * kWavesPlan * 8);
 }
 
 // Chunks of the correction / bonus draw (one row per sequence): enough
@@ -85,17 +129,22 @@ inline int64_t chunk_len(int64_t V, int split) {
 }
 
 // ---------------------------------------------------------------- greedy ---
+// Stream order: for each sequence b, target rows 0..n_b, then its W drafter
+// rows (a sequence with an invalid draft length contributes no rows).
 struct GreedyPlan {
-  RowPlan r;          // B*(K+1) target rows followed by B*W draft rows
-  size_t off_part;    // float2 {value, index-as-bits} per (item, wave)
+  int64_t max_rows;   // B * (K + 1 + W)
+  size_t off_part;    // float2 {value, index-as-bits} per (slot, wave)
+  size_t off_pre;     // int32 [B + 1]: first stream row of each sequence
   size_t bytes;
 };
 
 inline GreedyPlan plan_greedy(int B, int K, int W, int V) {
   GreedyPlan p{};
-  p.r = plan_rows(static_cast<int64_t>(B) * (K + 1) + static_cast<int64_t>(B) * W, V);
+  p.max_rows = static_cast<int64_t>(B) * (K + 1 + W);
   p.off_part = 0;
-  p.bytes = p.r.part_bytes;
+  p.off_pre = partial_bytes(p.max_rows);
+  p.bytes = p.off_pre + align256(static_cast<size_t>(B + 1) * 4);
+  (void)V;
   return p;
 }
 
@@ -111,11 +160,14 @@ struct DrawRecord {
   float u;           // resample uniform of row h
 };
 
+// Stream order: for each sequence b, target rows 0..n_b, then drafter rows
+// 0..n_b-1.
 struct SamplePlan {
-  RowPlan r;           // B*(K+1) target rows followed by B*K draft rows
+  int64_t max_rows;    // B * (2K + 1)
   int draw_chunks;
   int64_t draw_chunk;
-  size_t off_stats;    // float2 {M, S} per (item, wave)
+  size_t off_stats;    // float2 {M, S} per (slot, wave)
+  size_t off_pre;      // int32 [B + 1]: first stream row of each sequence
   size_t off_rec;      // DrawRecord per sequence
   size_t off_dsum;     // float per (sequence, draw chunk)
   size_t bytes;
@@ -123,23 +175,29 @@ struct SamplePlan {
 
 inline SamplePlan plan_sample(int B, int K, int V) {
   SamplePlan p{};
-  p.r = plan_rows(static_cast<int64_t>(B) * (K + 1) + static_cast<int64_t>(B) * K, V);
+  p.max_rows = static_cast<int64_t>(B) * (2 * K + 1);
   p.draw_chunks = choose_draw_chunks(B, V);
   p.draw_chunk = chunk_len(V, p.draw_chunks);
   p.off_stats = 0;
-  p.off_rec = p.r.part_bytes;
+  p.off_pre = partial_bytes(p.max_rows);
+  p.off_rec = p.off_pre + align256(static_cast<size_t>(B + 1) * 4);
   p.off_dsum = p.off_rec + align256(static_cast<size_t>(B) * sizeof(DrawRecord));
   p.bytes = p.off_dsum + align256(static_cast<size_t>(B) * p.draw_chunks * 4);
   return p;
 }
 
 // ------------------------------------------------------------------ tree ---
+// Stream order: the needed (state, position) rows in (b, y, s) order, listed
+// by the planning kernel.
 struct TreePlan {
-  RowPlan r;           // B*S*L rows (masked rows only do work)
+  int64_t max_rows;    // B*S*L
   int64_t states;      // B*S
   int split2;
   int64_t chunk2;
-  size_t off_conf;     // float2 {M, S} per (item, wave)
+  size_t off_count;    // int32: rows in the stream
+  size_t off_list;     // int32 [max_rows]: flat (b*S + y)*L + s of stream row r
+  size_t off_map;      // int32 [max_rows]: stream row of flat row id, or -1
+  size_t off_conf;     // float2 {M, S} per (slot, wave)
   size_t off_pick;     // float2 {score, index-as-bits} per (state, split2)
   size_t off_sel;      // int per state: selected position
   size_t bytes;
@@ -148,7 +206,7 @@ struct TreePlan {
 // Vocabulary chunks per state for the Gumbel argmax (one row per state).
 inline int choose_split(int64_t rows, int64_t V) {
   if (rows <= 0) return 1;
-  int64_t s = cdiv(kPlanGroups, rows);
+  int64_t s = cdiv(kMaxGrid, rows);
   const int64_t cap = V / 4096 > 0 ? V / 4096 : 1;
   if (s > cap) s = cap;
   if (s > kMaxSplit) s = kMaxSplit;
@@ -157,16 +215,18 @@ inline int choose_split(int64_t rows, int64_t V) {
 
 inline TreePlan plan_tree(int B, int S, int L, int V) {
   TreePlan p{};
-  // Many rows: a whole row per item keeps the per-position combine short.
-  p.r = plan_rows(static_cast<int64_t>(B) * S * L, V, V > kChunkMax ? V : kChunkMax);
+  p.max_rows = static_cast<int64_t>(B) * S * L;
   p.states = static_cast<int64_t>(B) * S;
   // The Gumbel argmax keeps no chunk in registers, so its chunks only need to
   // cover the row: ceil(V / split2) rounded up to 256 elements.
   p.split2 = choose_split(p.states, V);
   p.chunk2 = cdiv(cdiv(V, p.split2), 256) * 256;
   p.split2 = static_cast<int>(cdiv(V, p.chunk2));
-  p.off_conf = 0;
-  p.off_pick = p.r.part_bytes;
+  p.off_count = 0;
+  p.off_list = 256;
+  p.off_map = p.off_list + align256(static_cast<size_t>(p.max_rows) * 4);
+  p.off_conf = p.off_map + align256(static_cast<size_t>(p.max_rows) * 4);
+  p.off_pick = p.off_conf + partial_bytes(p.max_rows);
   p.off_sel = p.off_pick + align256(static_cast<size_t>(p.states) * p.split2 * 8);
   p.bytes = p.off_sel + align256(static_cast<size_t>(p.states) * 4);
   return p;

@@ -3,11 +3,13 @@
 //
 // Greedy  (Packed-SS, Sec. 3.1, Eq. 1-4, Algorithm 1):
 //   k_greedy_rows      persistent: argmax partials of every needed target /
-//                      drafter row, per (row, vocabulary chunk, wave)
+//                      drafter row; the needed rows form one stream split
+//                      evenly over the groups (FlatSplit)
 //   k_greedy_finalize  per sequence: combine, leading matches h, C, ending
 //                      condition a, next draft z_{a+1..W}
 // Sampling (Packed-SS, Algorithm 2; Two Tradeoffs, Theorem 1, Algorithm 1):
 //   k_sample_rows      persistent: online softmax statistics (M, S) partials
+//                      of every needed row, split like k_greedy_rows
 //   k_draw_mass        per (sequence, vocabulary chunk): the sequence's
 //                      decision (p(d), q(d), the acceptance tests, h) and the
 //                      chunk's mass of [p - q]_+ (or of p for the bonus)
@@ -34,52 +36,42 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // ================================================================ greedy ===
 
-template <int DT>
-__device__ __forceinline__ const char* greedy_row(const GreedyArgs& a, uint32_t row, bool& need) {
-  const uint32_t K1 = static_cast<uint32_t>(a.K + 1);
-  const uint32_t ntr = static_cast<uint32_t>(a.B) * K1;
-  if (row < ntr) {
-    const uint32_t b = row / K1;
-    const int i = static_cast<int>(row - b * K1);
-    bool bad;
-    const int n = draft_count(a.draft_len, static_cast<int>(b), a.K, bad);
-    need = !bad && i <= n;
-    return static_cast<const char*>(a.tgt) + (static_cast<int64_t>(b) * a.ts + i * a.tr) * Elem<DT>::kBytes;
-  }
-  const uint32_t r = row - ntr;
-  const uint32_t W = static_cast<uint32_t>(a.W);
-  const uint32_t b = r / W;
-  const int j = static_cast<int>(r - b * W);
-  need = true;
-  return static_cast<const char*>(a.dr) + (static_cast<int64_t>(b) * a.ds + j * a.drr) * Elem<DT>::kBytes;
+// Stream rows of sequence b: target rows 0..n_b (none for an invalid draft
+// length), then its W drafter rows.
+__device__ __forceinline__ int greedy_targets(const GreedyArgs& a, int b) {
+  bool bad;
+  const int n = draft_count(a.draft_len, b, a.K, bad);
+  return bad ? 0 : n + 1;
 }
 
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_greedy_rows(GreedyArgs a) {
-  const uint32_t nchunk = static_cast<uint32_t>(a.it.nchunk);
-  const int64_t chunk = a.it.chunk;
-  for_items(
-      static_cast<uint32_t>(a.it.items),
-      [&](uint32_t item) {
-        bool need;
-        greedy_row<DT>(a, item / nchunk, need);
-        return need;
-      },
-      [&](uint32_t item) {
-        bool need;
-        const uint32_t row = item / nchunk;
-        const char* rowp = greedy_row<DT>(a, row, need);
-        const int64_t v0 = static_cast<int64_t>(item - row * nchunk) * chunk;
-        const int64_t v1 = v0 + chunk < a.V ? v0 + chunk : a.V;
-        ArgmaxPick pk;
-        stream_row<DT, kUnroll>(rowp, v0, v1, pk);
-        float v = pk.best;
-        int ii = static_cast<int>(pk.bidx);
-        int nan = pk.nan ? 1 : 0;
-        wave_argmax(v, ii, nan);
-        if (lane_id() == 0)
-          a.part[static_cast<int64_t>(item) * kWaves + wave_id()] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
-      });
+  __shared__ int s_pre[kSeqBlocks + 1];
+  __shared__ int s_w[kWaves];
+  auto count = [&](int b) { return greedy_targets(a, b) + a.W; };
+  const SeqDir dir = build_seq_dir(a.B, count, s_pre, s_w);
+  if (blockIdx.x == 0) write_seq_starts(dir, s_pre, a.B, count, a.pre);
+  const FlatSplit f = make_split(s_pre[dir.nblk], a.V, Elem<DT>::kBytes, a.grid);
+  const int64_t g = blockIdx.x;
+  if (g >= f.G) return;
+  for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1) {
+    int first, cnt;
+    const int b = find_seq(dir, s_pre, static_cast<int>(r), count, first, cnt);
+    const int j = static_cast<int>(r) - first;
+    const int nt = cnt - a.W;
+    const char* rowp =
+        j < nt ? static_cast<const char*>(a.tgt) + (static_cast<int64_t>(b) * a.ts + j * a.tr) * Elem<DT>::kBytes
+               : static_cast<const char*>(a.dr) +
+                     (static_cast<int64_t>(b) * a.ds + static_cast<int64_t>(j - nt) * a.drr) * Elem<DT>::kBytes;
+    ArgmaxPick pk;
+    stream_row<DT, kUnroll>(rowp, v0, v1, pk);
+    float v = pk.best;
+    int ii = static_cast<int>(pk.bidx);
+    int nan = pk.nan ? 1 : 0;
+    wave_argmax(v, ii, nan);
+    if (lane_id() == 0)
+      a.part[(r + g) * kWaves + wave_id()] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
+  });
 }
 
 __global__ __launch_bounds__(kBlock) void k_greedy_finalize(GreedyArgs a) {
@@ -88,10 +80,11 @@ __global__ __launch_bounds__(kBlock) void k_greedy_finalize(GreedyArgs a) {
   __shared__ int s_st, s_h, s_a;
   const int b = blockIdx.x;
   const int t = threadIdx.x;
-  const int64_t per_row = a.it.nchunk * kWaves;
   bool nbad;
   const int n = draft_count(a.draft_len, b, a.K, nbad);
   const int budget = a.budget ? a.budget[b] : INT_MAX;
+  const int p0 = a.pre[b];
+  const FlatSplit f = make_split(a.pre[a.B], a.V, a.elem_bytes, a.grid);
   if (t == 0) {
     s_st = (nbad || budget < 0) ? SEQ_BAD_INPUT : 0;
     s_h = n;
@@ -103,15 +96,14 @@ __global__ __launch_bounds__(kBlock) void k_greedy_finalize(GreedyArgs a) {
     const int di = d[i];
     if (di < 0 || di >= a.V) st |= SEQ_BAD_INPUT;
   }
-  const int64_t ntr = static_cast<int64_t>(a.B) * (a.K + 1);
-  // Rows 0..n of the target, then the W drafter rows.
+  // Stream rows p0.. of the sequence: target rows 0..n, then the W drafter rows.
   const int nt = nbad ? 0 : n + 1;
   combine_rows_pick(
-      nt + a.W, per_row,
-      [&](int r) {
-        const int64_t row = r < nt ? static_cast<int64_t>(b) * (a.K + 1) + r
-                                   : ntr + static_cast<int64_t>(b) * a.W + (r - nt);
-        return a.part + row * per_row;
+      nt + a.W, a.part,
+      [&](int r, int64_t& first, int64_t& cnt) {
+        split_row_slots(f, p0 + r, first, cnt);
+        first *= kWaves;
+        cnt *= kWaves;
       },
       [&](int r, float v, int idx, int nan) {
         st |= nan ? SEQ_NONFINITE : max_status(v);
@@ -164,54 +156,41 @@ __global__ __launch_bounds__(kBlock) void k_greedy_finalize(GreedyArgs a) {
 
 // ============================================================== sampling ===
 
-template <int DT>
-__device__ __forceinline__ const char* sample_row(const SampleArgs& a, uint32_t row, bool& need, float& k) {
-  const uint32_t K1 = static_cast<uint32_t>(a.K + 1);
-  const uint32_t ntr = static_cast<uint32_t>(a.B) * K1;
+// Stream rows of sequence b: target rows 0..n_b, then drafter rows
+// 0..n_b-1; none for an invalid draft length.
+__device__ __forceinline__ int sample_count(const SampleArgs& a, int b) {
   bool bad;
-  if (row < ntr) {
-    const uint32_t b = row / K1;
-    const int i = static_cast<int>(row - b * K1);
-    const int n = draft_count(a.draft_len, static_cast<int>(b), a.K, bad);
-    need = !bad && i <= n;
-    k = a.kp;
-    return static_cast<const char*>(a.tgt) + (static_cast<int64_t>(b) * a.ts + i * a.tr) * Elem<DT>::kBytes;
-  }
-  const uint32_t r = row - ntr;
-  const uint32_t K = static_cast<uint32_t>(a.K);
-  const uint32_t b = r / K;
-  const int i = static_cast<int>(r - b * K);
-  const int n = draft_count(a.draft_len, static_cast<int>(b), a.K, bad);
-  need = !bad && i < n;
-  k = a.kq;
-  return static_cast<const char*>(a.drf) + (static_cast<int64_t>(b) * a.ds + i * a.dr) * Elem<DT>::kBytes;
+  const int n = draft_count(a.draft_len, b, a.K, bad);
+  return bad ? 0 : 2 * n + 1;
 }
 
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
-  const uint32_t nchunk = static_cast<uint32_t>(a.it.nchunk);
-  const int64_t chunk = a.it.chunk;
-  for_items(
-      static_cast<uint32_t>(a.it.items),
-      [&](uint32_t item) {
-        bool need;
-        float k;
-        sample_row<DT>(a, item / nchunk, need, k);
-        return need;
-      },
-      [&](uint32_t item) {
-        bool need;
-        float k;
-        const uint32_t row = item / nchunk;
-        const char* rowp = sample_row<DT>(a, row, need, k);
-        const int64_t v0 = static_cast<int64_t>(item - row * nchunk) * chunk;
-        const int64_t v1 = v0 + chunk < a.V ? v0 + chunk : a.V;
-        SoftmaxStats st(k);
-        stream_row<DT, kUnroll>(rowp, v0, v1, st);
-        float M = st.M, S = st.S;
-        wave_stats(M, S, k);
-        if (lane_id() == 0) a.stats[static_cast<int64_t>(item) * kWaves + wave_id()] = make_float2(M, S);
-      });
+  __shared__ int s_pre[kSeqBlocks + 1];
+  __shared__ int s_w[kWaves];
+  auto count = [&](int b) { return sample_count(a, b); };
+  const SeqDir dir = build_seq_dir(a.B, count, s_pre, s_w);
+  if (blockIdx.x == 0) write_seq_starts(dir, s_pre, a.B, count, a.pre);
+  const FlatSplit f = make_split(s_pre[dir.nblk], a.V, Elem<DT>::kBytes, a.grid);
+  const int64_t g = blockIdx.x;
+  if (g >= f.G) return;
+  for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1) {
+    int first, cnt;
+    const int b = find_seq(dir, s_pre, static_cast<int>(r), count, first, cnt);
+    const int j = static_cast<int>(r) - first;
+    const int n = (cnt - 1) / 2;
+    const bool target = j <= n;
+    const float k = target ? a.kp : a.kq;
+    const char* rowp =
+        target ? static_cast<const char*>(a.tgt) + (static_cast<int64_t>(b) * a.ts + j * a.tr) * Elem<DT>::kBytes
+               : static_cast<const char*>(a.drf) +
+                     (static_cast<int64_t>(b) * a.ds + static_cast<int64_t>(j - n - 1) * a.dr) * Elem<DT>::kBytes;
+    SoftmaxStats st(k);
+    stream_row<DT, kUnroll>(rowp, v0, v1, st);
+    float M = st.M, S = st.S;
+    wave_stats(M, S, k);
+    if (lane_id() == 0) a.stats[(r + g) * kWaves + wave_id()] = make_float2(M, S);
+  });
 }
 
 // Per-element weight of the draw: residual [p - q]_+ or bonus exp2 weight.
@@ -343,7 +322,6 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   const int b = blockIdx.x / NC;
   const int c = blockIdx.x % NC;
   const int t = threadIdx.x;
-  const int64_t per_row = a.it.nchunk * kWaves;
 
   // ---- the sequence's decision (every group of the sequence) ------------
   bool nbad;
@@ -355,24 +333,34 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   }
   __syncthreads();
   const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
-  const int64_t ntr = static_cast<int64_t>(a.B) * (a.K + 1);
   int st = 0;
   for (int i = t; i < n; i += kBlock) {
     const int di = d[i];
     if (di < 0 || di >= a.V) st |= SEQ_BAD_INPUT;
   }
   if (!nbad) {
-    // Target rows 0..n with k = kp, then drafter rows 0..n-1 with k = kq.
+    // Stream rows p0..p0+n: target rows 0..n (k = kp); p0+n+1..: drafter
+    // rows 0..n-1 (k = kq).
+    const int p0 = a.pre[b];
+    const FlatSplit f = make_split(a.pre[a.B], a.V, Elem<DT>::kBytes, a.grid);
     combine_rows_stats(
-        n + 1, per_row, a.kp,
-        [&](int r) { return a.stats + (static_cast<int64_t>(b) * (a.K + 1) + r) * per_row; },
+        n + 1, a.stats, a.kp,
+        [&](int r, int64_t& first, int64_t& cnt) {
+          split_row_slots(f, p0 + r, first, cnt);
+          first *= kWaves;
+          cnt *= kWaves;
+        },
         [&](int r, float M, float S) {
           s_Mp[r] = M; s_Sp[r] = S;
           st |= stats_status(M, S);
         });
     combine_rows_stats(
-        n, per_row, a.kq,
-        [&](int r) { return a.stats + (ntr + static_cast<int64_t>(b) * a.K + r) * per_row; },
+        n, a.stats, a.kq,
+        [&](int r, int64_t& first, int64_t& cnt) {
+          split_row_slots(f, p0 + n + 1 + r, first, cnt);
+          first *= kWaves;
+          cnt *= kWaves;
+        },
         [&](int r, float M, float S) {
           s_Mq[r] = M; s_Sq[r] = S;
           st |= stats_status(M, S);
@@ -596,15 +584,13 @@ static const void* fn(K* k) {
 
 bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
   const bool bf = dtype == DT_BF16;
-  return launch(bf ? fn(k_greedy_rows<DT_BF16>) : fn(k_greedy_rows<DT_F32>),
-                persistent_grid(a.it.items), stream, a, ev) &&
+  return launch(bf ? fn(k_greedy_rows<DT_BF16>) : fn(k_greedy_rows<DT_F32>), a.grid, stream, a, ev) &&
          launch(fn(k_greedy_finalize), a.B, stream, a);
 }
 
 bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
   const bool bf = dtype == DT_BF16;
-  return launch(bf ? fn(k_sample_rows<DT_BF16>) : fn(k_sample_rows<DT_F32>),
-                persistent_grid(a.it.items), stream, a, ev) &&
+  return launch(bf ? fn(k_sample_rows<DT_BF16>) : fn(k_sample_rows<DT_F32>), a.grid, stream, a, ev) &&
          launch(bf ? fn(k_draw_mass<DT_BF16>) : fn(k_draw_mass<DT_F32>),
                 static_cast<int64_t>(a.B) * a.draw_chunks, stream, a) &&
          launch(bf ? fn(k_draw_select<DT_BF16>) : fn(k_draw_select<DT_F32>), a.B, stream, a);

@@ -1,10 +1,14 @@
 // Draft-tree verification by shared-Gumbel state equality (SPOT, Sec. 4.1,
 // Sec. 4.3 and App. A.1).
 //
+//   k_tree_plan    one group: lists the needed rows -- every masked row of
+//                  every valid state, or in the fixed-position mode only the
+//                  given position's row -- in (sequence, state, position)
+//                  order, and maps each (state, position) to its list index
 //   k_tree_conf    persistent: softmax statistics (M, S) partials of every
-//                  masked row of every state (the position's confidence is
-//                  1/S = max_v p); in the fixed-position mode only the given
-//                  position's row.
+//                  listed row (the position's confidence is 1/S = max_v p);
+//                  the listed rows form one stream split evenly over the
+//                  groups (FlatSplit)
 //   k_tree_gumbel  per (state, vocabulary chunk): s*(y) from the confidences
 //                  (lowest position on ties), then the argmax over v of
 //                  z_v / T + G[s*, v] (z_v at T = 0) -- the token of Phi(y).
@@ -24,63 +28,97 @@ __device__ __forceinline__ int state_count(const int32_t* num_states, int b, int
   return (ns < 1 || ns > S) ? -1 : ns;
 }
 
-// Row index -> (sequence, state, position), 32-bit arithmetic.
-__device__ __forceinline__ void split_row(const TreeArgs& a, uint32_t row, int& b, int& y, int& s) {
+// Flat row id (b*S + y)*L + s -> (sequence, state, position); ids are below
+// 2^31 (checked by the host), so 32-bit arithmetic suffices.
+__device__ __forceinline__ void split_flat(const TreeArgs& a, uint32_t flat, int& b, int& y, int& s) {
   const uint32_t L = static_cast<uint32_t>(a.L);
-  const uint32_t sy = row / L;
-  s = static_cast<int>(row - sy * L);
+  const uint32_t sy = flat / L;
+  s = static_cast<int>(flat - sy * L);
   const uint32_t S = static_cast<uint32_t>(a.S);
   const uint32_t bb = sy / S;
   y = static_cast<int>(sy - bb * S);
   b = static_cast<int>(bb);
 }
 
-// Does row (b, y, s) need its statistics?
-__device__ __forceinline__ bool conf_row_needed(const TreeArgs& a, uint32_t row) {
+// Is row (b, y, s) needed: a masked position (or the given position in the
+// fixed mode) of a state below num_states[b]?
+__device__ __forceinline__ bool tree_row_needed(const TreeArgs& a, uint32_t flat) {
   int b, y, s;
-  split_row(a, row, b, y, s);
+  split_flat(a, flat, b, y, s);
   const int ns = state_count(a.num_states, b, a.S);
   if (ns < 0 || y >= ns) return false;
   const int64_t sy = static_cast<int64_t>(b) * a.S + y;
-  return a.fixed ? a.next_pos[sy] == s : a.masked[sy * a.L + s] != 0;
+  return a.fixed ? a.next_pos[sy] == s : a.masked[flat] != 0;
+}
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanPer = 16;   // row ids per thread per pass
+
+__global__ __launch_bounds__(kPlanThreads) void k_tree_plan(TreeArgs a) {
+  __shared__ int s_w[kPlanThreads / 64];
+  const uint32_t F = static_cast<uint32_t>(a.B) * a.S * a.L;
+  int base = 0;  // stream rows listed by earlier passes
+  for (uint32_t t0 = 0; t0 < F; t0 += kPlanThreads * kPlanPer) {
+    const uint32_t f0 = t0 + threadIdx.x * kPlanPer;
+    uint32_t bits = 0;
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < kPlanPer; ++k) {
+      if (f0 + k < F && tree_row_needed(a, f0 + k)) {
+        bits |= 1u << k;
+        ++c;
+      }
+    }
+    int total;
+    int off = base + group_exclusive_scan<kPlanThreads / 64>(c, total, s_w);
+#pragma unroll
+    for (int k = 0; k < kPlanPer; ++k) {
+      if (f0 + k < F) {
+        if ((bits >> k) & 1u) {
+          a.list[off] = static_cast<int32_t>(f0 + k);
+          a.map[f0 + k] = off;
+          ++off;
+        } else {
+          a.map[f0 + k] = -1;
+        }
+      }
+    }
+    base += total;
+  }
+  if (threadIdx.x == 0) *a.count = base;
 }
 
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_tree_conf(TreeArgs a) {
-  const uint32_t nchunk = static_cast<uint32_t>(a.it.nchunk);
-  const int64_t chunk = a.it.chunk;
-  for_items(
-      static_cast<uint32_t>(a.it.items),
-      [&](uint32_t item) { return conf_row_needed(a, item / nchunk); },
-      [&](uint32_t item) {
-        const uint32_t row = item / nchunk;
-        int b, y, s;
-        split_row(a, row, b, y, s);
-        const char* rowp = static_cast<const char*>(a.logits) +
-                           (b * a.ss + y * a.sy + s * a.sp) * Elem<DT>::kBytes;
-        const int64_t v0 = static_cast<int64_t>(item - row * nchunk) * chunk;
-        const int64_t v1 = v0 + chunk < a.V ? v0 + chunk : a.V;
-        SoftmaxStats st(kLog2e);
-        stream_row<DT, 4>(rowp, v0, v1, st);
-        float M = st.M, S = st.S;
-        wave_stats(M, S, kLog2e);
-        if ((threadIdx.x & 63) == 0)
-          a.conf[static_cast<int64_t>(item) * kWaves + (threadIdx.x >> 6)] = make_float2(M, S);
-      });
+  const FlatSplit f = make_split(*a.count, a.V, Elem<DT>::kBytes, a.grid);
+  const int64_t g = blockIdx.x;
+  if (g >= f.G) return;
+  for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1) {
+    int b, y, s;
+    split_flat(a, static_cast<uint32_t>(a.list[r]), b, y, s);
+    const char* rowp = static_cast<const char*>(a.logits) +
+                       (b * a.ss + y * a.sy + s * a.sp) * Elem<DT>::kBytes;
+    SoftmaxStats st(kLog2e);
+    stream_row<DT, 4>(rowp, v0, v1, st);
+    float M = st.M, S = st.S;
+    wave_stats(M, S, kLog2e);
+    if ((threadIdx.x & 63) == 0) a.conf[(r + g) * kWaves + (threadIdx.x >> 6)] = make_float2(M, S);
+  });
 }
 
-__device__ __forceinline__ void combine_conf(const TreeArgs& a, int64_t row, float& M, float& S) {
-  M = -kInf;
-  S = 0.f;
-  const int64_t n = a.it.nchunk * kWaves;
-  const float2* p = a.conf + row * n;
-  for (int64_t k = 0; k < n; ++k) stats_merge(M, S, p[k].x, p[k].y, kLog2e);
+// Combined statistics of the listed row with flat id `flat`.
+__device__ __forceinline__ void combine_conf(const TreeArgs& a, const FlatSplit& f, int64_t flat, float& M,
+                                             float& S) {
+  int64_t first, n;
+  split_row_slots(f, a.map[flat], first, n);
+  merge_span_stats(a.conf, first * kWaves, n * kWaves, kLog2e, M, S);
 }
 
 // s*(y): the masked position of largest confidence 1/S (lowest on ties), or
 // the given position in the fixed mode; -1 when there is none.  Every thread
 // of the group calls it; the result is uniform.
-__device__ int select_position(const TreeArgs& a, int b, int y, float* s_v, int* s_i, int* s_n, int* s_out) {
+__device__ int select_position(const TreeArgs& a, const FlatSplit& f, int b, int y, float* s_v, int* s_i,
+                                int* s_n, int* s_out) {
   const int64_t sy = static_cast<int64_t>(b) * a.S + y;
   if (a.fixed) {
     const int np = a.next_pos[sy];
@@ -91,7 +129,7 @@ __device__ int select_position(const TreeArgs& a, int b, int y, float* s_v, int*
   for (int s = threadIdx.x; s < a.L; s += kBlock) {
     if (!a.masked[sy * a.L + s]) continue;
     float M, S;
-    combine_conf(a, sy * a.L + s, M, S);
+    combine_conf(a, f, sy * a.L + s, M, S);
     if (pick_better(-S, s, v, idx)) { v = -S; idx = s; }   // max of -S = min of S
   }
   block_argmax(v, idx, nan, s_v, s_i, s_n);
@@ -168,7 +206,7 @@ __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64
 }
 
 // The walk of one sequence.
-__device__ void tree_walk(const TreeArgs& a, int b, int* s_pos, int* s_tok) {
+__device__ void tree_walk(const TreeArgs& a, const FlatSplit& f, int b, int* s_pos, int* s_tok) {
   __shared__ int s_st, s_child, s_y, s_len, s_ncommit;
   const int t = threadIdx.x;
   const int S = a.S;
@@ -206,7 +244,7 @@ __device__ void tree_walk(const TreeArgs& a, int b, int* s_pos, int* s_tok) {
       const int s = static_cast<int>(q % a.L);
       if (!a.masked[sy * a.L + s]) continue;
       float M, Sum;
-      combine_conf(a, sy * a.L + s, M, Sum);
+      combine_conf(a, f, sy * a.L + s, M, Sum);
       st |= stats_status(M, Sum);
     }
   }
@@ -219,7 +257,7 @@ __device__ void tree_walk(const TreeArgs& a, int b, int* s_pos, int* s_tok) {
       pos = a.sel[sy];
       if (pos >= 0) {
         float M, Sum;
-        combine_conf(a, sy * a.L + pos, M, Sum);
+        combine_conf(a, f, sy * a.L + pos, M, Sum);
         st |= stats_status(M, Sum);
         conf = 1.f / Sum;
         float v = -kInf;
@@ -307,7 +345,8 @@ __global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
   const int y = static_cast<int>(sy % a.S);
   const int ns = state_count(a.num_states, b, a.S);
   if (ns > 0 && y < ns) {
-    const int s = select_position(a, b, y, s_v, s_i, s_n, &s_sel);
+    const FlatSplit f = make_split(*a.count, a.V, Elem<DT>::kBytes, a.grid);
+    const int s = select_position(a, f, b, y, s_v, s_i, s_n, &s_sel);
     if (sp == 0 && threadIdx.x == 0) a.sel[sy] = s;
     if (s >= 0) {
       const char* xr = static_cast<const char*>(a.logits) +
@@ -332,9 +371,11 @@ __global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
   }
 }
 
+template <int DT>
 __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
   __shared__ int s_pos[kMaxStates], s_tok[kMaxStates];
-  tree_walk(a, blockIdx.x, s_pos, s_tok);
+  const FlatSplit f = make_split(*a.count, a.V, Elem<DT>::kBytes, a.grid);
+  tree_walk(a, f, blockIdx.x, s_pos, s_tok);
 }
 
 template <typename K>
@@ -344,11 +385,11 @@ static const void* fn(K* k) {
 
 bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
   const bool bf = dtype == DT_BF16;
-  return launch(bf ? fn(k_tree_conf<DT_BF16>) : fn(k_tree_conf<DT_F32>),
-                persistent_grid(a.it.items), stream, a, ev) &&
+  return launch_threads(fn(k_tree_plan), 1, kPlanThreads, stream, a) &&
+         launch(bf ? fn(k_tree_conf<DT_BF16>) : fn(k_tree_conf<DT_F32>), a.grid, stream, a, ev) &&
          launch(bf ? fn(k_tree_gumbel<DT_BF16>) : fn(k_tree_gumbel<DT_F32>),
                 static_cast<int64_t>(a.B) * a.S * a.split2, stream, a) &&
-         launch(fn(k_tree_walk), a.B, stream, a);
+         launch(bf ? fn(k_tree_walk<DT_BF16>) : fn(k_tree_walk<DT_F32>), a.B, stream, a);
 }
 
 }  // namespace dbv

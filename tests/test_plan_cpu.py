@@ -1,10 +1,12 @@
 """Launch-plan invariants of the HIP library, checked on the host.
 
-The plans (vocabulary chunking, draw chunks, workspace layout) are plain C++
-shared by the launchers and verify_workspace_size; tests/native/plan_check.cpp
-includes that header, is compiled here with g++ and asserts, over a grid of
-sizes up to the largest vocabularies, that every chunking covers whole rows
-and that workspace sections are aligned and disjoint.
+The plans (the flat split of the streamed rows over a launch's groups, the
+draw chunks, the workspace layout) are plain C++ shared by the kernels, the
+launchers and verify_workspace_size; tests/native/plan_check.cpp includes
+that header, is compiled here with g++ and asserts, over a grid of sizes up to
+the largest vocabularies, that the split covers the stream exactly once with
+unique partial slots, that every row's partials are found again, and that
+workspace sections are aligned and disjoint.
 """
 
 import os
