@@ -97,7 +97,7 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   if (accept_len == nullptr || out_tokens == nullptr || num_out == nullptr) return DBV_ERR_INVALID_ARG;
   const size_t eb = elem_bytes(dtype);
   if (!aligned(tgt, eb) || (drf && !aligned(drf, eb))) return DBV_ERR_INVALID_ARG;
-  const dbv::SamplePlan plan = dbv::plan_sample(B, K, V);
+  const dbv::SamplePlan plan = dbv::plan_sample(B, K, V, static_cast<int64_t>(elem_bytes(dtype)));
   if (!stream_fits(plan.max_rows, V)) return DBV_ERR_UNSUPPORTED;
   dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
   if (s != DBV_OK) return s;
@@ -120,9 +120,11 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.stats = reinterpret_cast<float2*>(w + plan.off_stats);
   a.pre = reinterpret_cast<int32_t*>(w + plan.off_pre);
   a.rec = reinterpret_cast<dbv::DrawRecord*>(w + plan.off_rec);
-  a.dsum = reinterpret_cast<float*>(w + plan.off_dsum);
+  a.tmass = reinterpret_cast<float*>(w + plan.off_tmass);
   a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(eb), dbv::resident_groups());
-  a.draw_chunks = plan.draw_chunks; a.draw_chunk = plan.draw_chunk;
+  a.tiles = static_cast<int>(plan.tiles);
+  a.tpc = static_cast<int>(plan.tpc);
+  a.chunks = static_cast<int>(plan.chunks);
   return dbv::launch_sample(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
 }
 
@@ -271,7 +273,7 @@ size_t verify_workspace_size(dbv_kind kind, int B, int K_or_S, int L, int V, dbv
       return dbv::plan_greedy(B, K_or_S, L, V).bytes;
     case DBV_KIND_REJECTION:
       if (K_or_S < 0 || K_or_S > kMaxDraft) return 0;
-      return dbv::plan_sample(B, K_or_S, V).bytes;
+      return dbv::plan_sample(B, K_or_S, V, static_cast<int64_t>(elem_bytes(dtype))).bytes;
     case DBV_KIND_TREE:
       if (K_or_S < 1 || K_or_S > kMaxStates || L < 1 || L > kMaxBlockLen) return 0;
       return dbv::plan_tree(B, K_or_S, L, V).bytes;

@@ -308,7 +308,7 @@ template <class Fn>
 __device__ __forceinline__ void for_pieces(const FlatSplit& f, int64_t g, Fn fn) {
   int64_t e0, e1;
   split_range(f, g, e0, e1);
-  int64_t r = e0 / f.V;
+  int64_t r = udiv(e0, f.V);
   for (int64_t base = r * f.V; base < e1; ++r, base += f.V) {
     const int64_t v0 = e0 > base ? e0 - base : 0;
     const int64_t v1 = e1 < base + f.V ? e1 - base : f.V;
@@ -444,11 +444,11 @@ __device__ __forceinline__ void write_seq_starts(const SeqDir& d, const int* pre
 constexpr int kRowLanes = 8;
 constexpr int kRowLoads = 8;
 
-template <class SpanFn, class DoneFn>
+template <int NT = kBlock, class SpanFn, class DoneFn>
 __device__ __forceinline__ void combine_rows_stats(int nrows, const float2* part, float k, SpanFn span,
                                                    DoneFn done) {
   const int sub = threadIdx.x % kRowLanes;
-  for (int r0 = 0; r0 < nrows; r0 += kBlock / kRowLanes) {
+  for (int r0 = 0; r0 < nrows; r0 += NT / kRowLanes) {
     const int r = r0 + static_cast<int>(threadIdx.x) / kRowLanes;
     float M = -kInf, S = 0.f;
     if (r < nrows) {
@@ -476,10 +476,10 @@ __device__ __forceinline__ void combine_rows_stats(int nrows, const float2* part
   }
 }
 
-template <class SpanFn, class DoneFn>
+template <int NT = kBlock, class SpanFn, class DoneFn>
 __device__ __forceinline__ void combine_rows_pick(int nrows, const float2* part, SpanFn span, DoneFn done) {
   const int sub = threadIdx.x % kRowLanes;
-  for (int r0 = 0; r0 < nrows; r0 += kBlock / kRowLanes) {
+  for (int r0 = 0; r0 < nrows; r0 += NT / kRowLanes) {
     const int r = r0 + static_cast<int>(threadIdx.x) / kRowLanes;
     float v = -kInf;
     int idx = -1, nan = 0;

@@ -42,10 +42,11 @@ struct SampleArgs {
   float2* stats;                       // per (slot, wave)
   int32_t* pre;                        // [B + 1] first stream row per sequence
   DrawRecord* rec;                     // per sequence
-  float* dsum;                         // per (sequence, draw chunk)
+  float* tmass;                        // per (sequence, draw tile)
   int64_t grid;                        // groups of the row-streaming launch
-  int draw_chunks;
-  int64_t draw_chunk;
+  int tiles;                           // draw tiles per row
+  int tpc;                             // draw tiles per mass-kernel group
+  int chunks;                          // mass-kernel groups per sequence
 };
 
 struct TreeArgs {

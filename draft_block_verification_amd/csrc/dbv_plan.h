@@ -33,7 +33,18 @@ constexpr int kMaxStates = 1024;      // S limit of the tree mode
 constexpr int kMaxBlockLen = 1024;    // L limit of the tree mode
 constexpr int kSeqBlocks = 1024;      // LDS prefix entries over sequences
 
-DBV_HD inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// Division of non-negative values; on the device it takes the 32-bit
+// instruction sequence when both operands fit (64-bit division is a long
+// software routine on this GPU).
+DBV_HD inline int64_t udiv(int64_t a, int64_t b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (((static_cast<uint64_t>(a) | static_cast<uint64_t>(b)) >> 32) == 0)
+    return static_cast<int64_t>(static_cast<uint32_t>(a) / static_cast<uint32_t>(b));
+#endif
+  return a / b;
+}
+
+DBV_HD inline int64_t cdiv(int64_t a, int64_t b) { return udiv(a + b - 1, b); }
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // ---------------------------------------------------------------------------
@@ -71,15 +82,15 @@ DBV_HD inline FlatSplit make_split(int64_t R, int64_t V, int64_t elem_bytes, int
 // Element range [e0, e1) of active group g; never empty.
 DBV_HD inline void split_range(const FlatSplit& f, int64_t g, int64_t& e0, int64_t& e1) {
   const int64_t E = f.R * f.V;
-  e0 = (g * f.NQ / f.G) * f.Q;
-  e1 = ((g + 1) * f.NQ / f.G) * f.Q;
+  e0 = udiv(g * f.NQ, f.G) * f.Q;
+  e1 = udiv((g + 1) * f.NQ, f.G) * f.Q;
   if (e1 > E) e1 = E;
 }
 
 // The active group whose range holds element e (0 <= e < R*V): the largest g
 // with floor(g*NQ/G) <= e / Q.
 DBV_HD inline int64_t split_group(const FlatSplit& f, int64_t e) {
-  return ((e / f.Q + 1) * f.G - 1) / f.NQ;
+  return udiv((udiv(e, f.Q) + 1) * f.G - 1, f.NQ);
 }
 
 // First partial slot (in units of waves) and number of groups of row r.
@@ -92,6 +103,7 @@ DBV_HD inline void split_row_slots(const FlatSplit& f, int64_t r, int64_t& first
 
 // Launch grid of a streaming kernel: enough groups for the largest stream
 // the call can need, at most kMaxGrid and the resident groups of the device.
+// (Giving small streams fewer, fuller groups measured no faster.)
 inline int64_t stream_grid(int64_t max_rows, int64_t V, int64_t elem_bytes, int64_t resident) {
   const int64_t units = cdiv(max_rows * V, kUnitBytes / elem_bytes);
   int64_t g = resident < kMaxGrid ? resident : kMaxGrid;
@@ -103,29 +115,30 @@ inline size_t partial_bytes(int64_t max_rows) {
   return align256(static_cast<size_t>(max_rows + kMaxGrid) * kWavesPlan * 8);
 }
 
-// Chunks of the correction / bonus draw (one row per sequence): enough
-// groups in total, at least 2048 elements each, and never more than
-// kDrawChunkMax elements so that the final in-order scan holds a chunk in
-// registers (kBlock threads x kDrawVecs vectors of 8).
-constexpr int kDrawVecs = 4;
-constexpr int kDrawPerThread = 8 * kDrawVecs;          // elements per thread
-constexpr int64_t kDrawChunkMax = 256 * kDrawPerThread;
-constexpr int kMaxDrawChunks = 256;                    // V <= 2^21 in sampling
-constexpr int64_t kMaxSampleV = kDrawChunkMax * kMaxDrawChunks;
-inline int choose_draw_chunks(int64_t B, int64_t V) {
-  int64_t s = cdiv(1024, B > 0 ? B : 1);
-  const int64_t cap = V / 2048 > 0 ? V / 2048 : 1;
-  if (s > cap) s = cap;
-  if (s > kMaxDrawChunks) s = kMaxDrawChunks;
-  const int64_t need = cdiv(V, kDrawChunkMax);   // <= kMaxDrawChunks for V <= kMaxSampleV
-  if (s < need) s = need;
-  return s < 1 ? 1 : static_cast<int>(s);
-}
+// The correction / bonus draw.  Its row is cut into tiles of 64 16-byte
+// vectors (one coalesced wave load per row: 512 bf16 or 256 fp32 elements).
+// The mass kernel gives each sequence draw_chunks groups of whole tiles and
+// stores every tile's mass; the select kernel (kDrawThreads threads per
+// sequence) scans the tile masses for the tile where the running mass
+// crosses u*Z, and one wave rescans that tile in vocabulary order.
+// kMaxDrawTiles bounds the tiles per row (at most kDrawTilesPerThread per
+// select thread), and so the vocabulary of the sampling entry points.
+constexpr int kDrawThreads = 1024;
+constexpr int kMaxDrawTiles = 8192;
+constexpr int kDrawTilesPerThread = kMaxDrawTiles / kDrawThreads;
+constexpr int64_t kMaxSampleV = int64_t(1) << 21;   // <= kMaxDrawTiles tiles of 256 fp32
+constexpr int64_t kDrawGroups = 1024;               // mass-kernel groups to aim for
 
-inline int64_t chunk_len(int64_t V, int split) {
-  int64_t c = cdiv(V, split);
-  c = cdiv(c, 256) * 256;
-  return c < kDrawChunkMax ? c : kDrawChunkMax;
+DBV_HD inline int64_t draw_tile(int64_t elem_bytes) { return 64 * 16 / elem_bytes; }
+inline int64_t draw_tiles(int64_t V, int64_t elem_bytes) { return cdiv(V, draw_tile(elem_bytes)); }
+
+// Tiles per mass-kernel group: about kDrawGroups groups in all, at least one
+// tile each.
+inline int64_t draw_tiles_per_chunk(int64_t B, int64_t V, int64_t elem_bytes) {
+  const int64_t nt = draw_tiles(V, elem_bytes);
+  const int64_t chunks = cdiv(kDrawGroups, B > 0 ? B : 1);
+  const int64_t tpc = cdiv(nt, chunks);
+  return tpc > 0 ? tpc : 1;
 }
 
 // ---------------------------------------------------------------- greedy ---
@@ -149,8 +162,8 @@ inline GreedyPlan plan_greedy(int B, int K, int W, int V) {
 }
 
 // -------------------------------------------------------------- sampling ---
-// Per-sequence decision handed from the draw-mass kernel to the select
-// kernel (written by the sequence's chunk-0 group).
+// Per-sequence decision handed from the mass kernel to the select kernel
+// (written by the sequence's chunk-0 group).
 struct DrawRecord {
   int status;        // sequence status bits; error bits mean "done"
   int h;             // accepted drafts; the draw uses row h
@@ -164,25 +177,27 @@ struct DrawRecord {
 // 0..n_b-1.
 struct SamplePlan {
   int64_t max_rows;    // B * (2K + 1)
-  int draw_chunks;
-  int64_t draw_chunk;
+  int64_t tiles;       // draw tiles per row
+  int64_t tpc;         // draw tiles per mass-kernel group
+  int64_t chunks;      // mass-kernel groups per sequence
   size_t off_stats;    // float2 {M, S} per (slot, wave)
   size_t off_pre;      // int32 [B + 1]: first stream row of each sequence
   size_t off_rec;      // DrawRecord per sequence
-  size_t off_dsum;     // float per (sequence, draw chunk)
+  size_t off_tmass;    // float per (sequence, draw tile)
   size_t bytes;
 };
 
-inline SamplePlan plan_sample(int B, int K, int V) {
+inline SamplePlan plan_sample(int B, int K, int V, int64_t elem_bytes) {
   SamplePlan p{};
   p.max_rows = static_cast<int64_t>(B) * (2 * K + 1);
-  p.draw_chunks = choose_draw_chunks(B, V);
-  p.draw_chunk = chunk_len(V, p.draw_chunks);
+  p.tiles = draw_tiles(V, elem_bytes);
+  p.tpc = draw_tiles_per_chunk(B, V, elem_bytes);
+  p.chunks = cdiv(p.tiles, p.tpc);
   p.off_stats = 0;
   p.off_pre = partial_bytes(p.max_rows);
   p.off_rec = p.off_pre + align256(static_cast<size_t>(B + 1) * 4);
-  p.off_dsum = p.off_rec + align256(static_cast<size_t>(B) * sizeof(DrawRecord));
-  p.bytes = p.off_dsum + align256(static_cast<size_t>(B) * p.draw_chunks * 4);
+  p.off_tmass = p.off_rec + align256(static_cast<size_t>(B) * sizeof(DrawRecord));
+  p.bytes = p.off_tmass + align256(static_cast<size_t>(B) * p.tiles * 4);
   return p;
 }
 

@@ -10,11 +10,13 @@
 // Sampling (Packed-SS, Algorithm 2; Two Tradeoffs, Theorem 1, Algorithm 1):
 //   k_sample_rows      persistent: online softmax statistics (M, S) partials
 //                      of every needed row, split like k_greedy_rows
-//   k_draw_mass        per (sequence, vocabulary chunk): the sequence's
+//   k_draw_mass        per (sequence, chunk of draw tiles): the sequence's
 //                      decision (p(d), q(d), the acceptance tests, h) and the
-//                      chunk's mass of [p - q]_+ (or of p for the bonus)
-//   k_draw_select      per sequence: the token where the running mass first
-//                      exceeds u*Z (vocabulary order), output assembly.
+//                      masses of [p - q]_+ (or of p for the bonus) over the
+//                      chunk's tiles of row h
+//   k_draw_select      per sequence (1024 threads): the tile, then the token,
+//                      where the running mass first exceeds u*Z (vocabulary
+//                      order), and output assembly.
 // The kernel boundaries are the only cross-group synchronisation.
 #include "dbv_device.h"
 #include "dbv_launch.h"
@@ -205,53 +207,67 @@ struct DrawWeight {
   }
 };
 
-struct SumOne {
-  DrawWeight w;
-  float s = 0.f;
-  template <int N>
-  __device__ __forceinline__ void group(const float* x, int64_t) {
-#pragma unroll
-    for (int j = 0; j < N; ++j) s += w(x[j], 0.f);
-  }
-  template <int U, int W>
-  __device__ __forceinline__ void block(const float* x, int64_t, int64_t) { group<U * W>(x, 0); }
-};
+constexpr int kTileBatch = 8;   // tiles a wave reads together (16 loads per lane)
 
-// Sum of the residual weights over [v0, v1) of two rows read together.
-template <int DT>
-__device__ float sum_resid(const char* xr, const char* yr, int64_t v0, int64_t v1, const DrawWeight& w) {
+// Masses of the draw row's tiles [t_lo, t_hi) (64 16-byte vectors each, of
+// the row and, for the residual, of drafter row yr), by the NW waves of the
+// group: wave w takes tiles t_lo + w, t_lo + w + NW, ..., kTileBatch of them
+// at a time with all their loads in flight; lane l sums the weights of the
+// tile's l-th vector and the wave reduces them into out[tile].  `vec` says
+// both rows are 16-byte aligned; otherwise (and for the row's last, partial
+// vector) elements are loaded one by one.  Byte offsets stay below 2^32
+// (V <= kMaxSampleV), so the loads take a uniform 64-bit base and 32-bit lane
+// offsets.
+template <int DT, int NW>
+__device__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo, int t_hi, bool vec,
+                            const DrawWeight& w, float* out) {
   using E = Elem<DT>;
   constexpr int W = E::kVec;
-  float s = 0.f;
-  const uintptr_t ax = reinterpret_cast<uintptr_t>(xr + v0 * E::kBytes);
-  const uintptr_t ay = reinterpret_cast<uintptr_t>(yr + v0 * E::kBytes);
-  const int t = threadIdx.x;
-  if (((ax ^ ay) & 15u) != 0) {  // rows disagree on alignment: scalar path
-    for (int64_t j = v0 + t; j < v1; j += kBlock) s += w(E::load1(xr, j), E::load1(yr, j));
-    return s;
-  }
-  int64_t head = static_cast<int64_t>(((16u - (ax & 15u)) & 15u) / E::kBytes);
-  if (head > v1 - v0) head = v1 - v0;
-  const int64_t a0 = v0 + head;
-  const int64_t nvec = (v1 - a0) / W;
-  const int64_t a1 = a0 + nvec * W;
-  if (t < head) s += w(E::load1(xr, v0 + t), E::load1(yr, v0 + t));
-  const char* xb = xr + a0 * E::kBytes;
-  const char* yb = yr + a0 * E::kBytes;
-  for (int64_t i = t; i < nvec; i += kBlock) {
-    float x[W], y[W];
-    E::unpack(load16(xb + i * 16), x);
-    E::unpack(load16(yb + i * 16), y);
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const uint32_t Vn = static_cast<uint32_t>(V);
+  for (int t0 = t_lo + wv; t0 < t_hi; t0 += NW * kTileBatch) {
+    u32x4 rx[kTileBatch], ry[kTileBatch];
+    bool full[kTileBatch];
 #pragma unroll
-    for (int j = 0; j < W; ++j) s += w(x[j], y[j]);
+    for (int k = 0; k < kTileBatch; ++k) {
+      const int tile = t0 + k * NW;
+      const uint32_t e = static_cast<uint32_t>(tile) * (64 * W) + lane * W;   // the lane's first element
+      full[k] = vec && tile < t_hi && e + W <= Vn;
+      if (full[k]) {
+        rx[k] = load16(xr + e * E::kBytes);
+        ry[k] = w.resid ? load16(yr + e * E::kBytes) : rx[k];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < kTileBatch; ++k) {
+      const int tile = t0 + k * NW;
+      if (tile < t_hi) {   // uniform across the wave
+        const uint32_t e = static_cast<uint32_t>(tile) * (64 * W) + lane * W;
+        float m = 0.f;
+        if (full[k]) {
+          float x[W], y[W];
+          E::unpack(rx[k], x);
+          E::unpack(ry[k], y);
+#pragma unroll
+          for (int j = 0; j < W; ++j) m += w(x[j], y[j]);
+        } else {
+          for (int j = 0; j < W; ++j)
+            if (e + j < Vn) m += w(E::load1(xr, e + j), w.resid ? E::load1(yr, e + j) : 0.f);
+        }
+#pragma unroll
+        for (int sh = 32; sh >= 1; sh >>= 1) m += wave_shfl_xor(m, sh);
+        if (lane == 0) out[tile] = m;
+      }
+    }
   }
-  if (a1 + t < v1) s += w(E::load1(xr, a1 + t), E::load1(yr, a1 + t));
-  return s;
 }
 
-// WG-wide exclusive scan of one float per thread in thread order; also
-// returns the total.  Contains two barriers.
-__device__ __forceinline__ float block_exclusive_scan(float v, float& total, float* s_w) {
+// Exclusive scan of one float per thread over NW waves, in thread order;
+// also returns the total.  Two barriers.
+template <int NW>
+__device__ __forceinline__ float group_exclusive_scan_f(float v, float& total, float* s_w) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   float inc = v;
@@ -264,7 +280,7 @@ __device__ __forceinline__ float block_exclusive_scan(float v, float& total, flo
   __syncthreads();
   float base = 0.f;
   total = 0.f;
-  for (int j = 0; j < kWaves; ++j) {
+  for (int j = 0; j < NW; ++j) {
     if (j < w) base += s_w[j];
     total += s_w[j];
   }
@@ -272,77 +288,64 @@ __device__ __forceinline__ float block_exclusive_scan(float v, float& total, flo
   return base + inc - v;
 }
 
-// Weights of elements [e0, e0 + kDrawPerThread) (0 at or past `end`): the
-// thread's loads are all issued before any weight is computed.
-template <int DT>
-__device__ __forceinline__ void load_weights(const char* xr, const char* yr, int64_t e0, int64_t end,
-                                             const DrawWeight& w, float (&wv)[kDrawPerThread]) {
-  using E = Elem<DT>;
-  constexpr int W = E::kVec;
-  constexpr int NV = kDrawPerThread / W;
-  const bool vec = (((reinterpret_cast<uintptr_t>(xr + e0 * E::kBytes) |
-                      reinterpret_cast<uintptr_t>(yr + e0 * E::kBytes)) & 15u) == 0) &&
-                   e0 + kDrawPerThread <= end;
-  if (vec) {
-    u32x4 rx[NV], ry[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      rx[k] = load16(xr + (e0 + k * W) * E::kBytes);
-      if (w.resid) ry[k] = load16(yr + (e0 + k * W) * E::kBytes);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      float x[W], y[W];
-      E::unpack(rx[k], x);
-      if (w.resid) E::unpack(ry[k], y);
-#pragma unroll
-      for (int j = 0; j < W; ++j) wv[k * W + j] = w(x[j], w.resid ? y[j] : 0.f);
-    }
-  } else {
-    float x[kDrawPerThread], y[kDrawPerThread];
-#pragma unroll
-    for (int j = 0; j < kDrawPerThread; ++j) {
-      const bool in = e0 + j < end;
-      x[j] = in ? E::load1(xr, e0 + j) : 0.f;
-      y[j] = in && w.resid ? E::load1(yr, e0 + j) : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < kDrawPerThread; ++j) wv[j] = e0 + j < end ? w(x[j], y[j]) : 0.f;
-  }
-}
+constexpr int kDraftsPerThread = (kMaxDraft + kBlock - 1) / kBlock;   // drafts of one thread
 
+// Per (sequence, chunk of draw tiles), kBlock threads:
+//  1. Every input of the decision is requested at once: the length, budget,
+//     draft tokens, accept uniforms and stream position; then the row
+//     statistics partials and the logits at the draft tokens.
+//  2. p(d), q(d), the acceptance tests (u * q(d) < p~(d)) and h; chunk 0
+//     writes the diagnostics and the decision record.
+//  3. The masses of the chunk's tiles of row h: [p - q]_+ against drafter
+//     row h if a draft was rejected, else the bonus weight p.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   __shared__ float s_Mp[kMaxDraft + 1], s_Sp[kMaxDraft + 1];
   __shared__ float s_Mq[kMaxDraft], s_Sq[kMaxDraft];
-  __shared__ float s_red[kWaves];
   __shared__ int s_st, s_h;
-  const int NC = a.draw_chunks;
-  const int b = blockIdx.x / NC;
-  const int c = blockIdx.x % NC;
+  using E = Elem<DT>;
+  const int b = blockIdx.x / a.chunks;
+  const int c = blockIdx.x - b * a.chunks;
   const int t = threadIdx.x;
 
-  // ---- the sequence's decision (every group of the sequence) ------------
+  // ---- 1. inputs ----------------------------------------------------------
   bool nbad;
   const int n = draft_count(a.draft_len, b, a.K, nbad);
   const int budget = a.budget ? a.budget[b] : INT_MAX;
+  const int p0 = a.pre[b];
+  const int R = a.pre[a.B];
+  const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
+  int di[kDraftsPerThread];
+  float ui[kDraftsPerThread], xi[kDraftsPerThread], yi[kDraftsPerThread];
+#pragma unroll
+  for (int k = 0; k < kDraftsPerThread; ++k) {
+    const int i = t + k * kBlock;
+    di[k] = i < a.K ? d[i] : 0;
+    ui[k] = i < a.K ? a.u_accept[static_cast<int64_t>(b) * a.K + i] : 0.f;
+  }
+  int st = 0;
+#pragma unroll
+  for (int k = 0; k < kDraftsPerThread; ++k) {
+    const int i = t + k * kBlock;
+    xi[k] = yi[k] = 0.f;
+    if (i < n) {
+      if (di[k] < 0 || di[k] >= a.V) {
+        st |= SEQ_BAD_INPUT;
+      } else {
+        xi[k] = E::load1(static_cast<const char*>(a.tgt) + (b * a.ts + i * a.tr) * E::kBytes, di[k]);
+        yi[k] = E::load1(static_cast<const char*>(a.drf) + (b * a.ds + i * a.dr) * E::kBytes, di[k]);
+      }
+    }
+  }
   if (t == 0) {
     s_st = (nbad || budget < 0) ? SEQ_BAD_INPUT : 0;
     s_h = n;
   }
   __syncthreads();
-  const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
-  int st = 0;
-  for (int i = t; i < n; i += kBlock) {
-    const int di = d[i];
-    if (di < 0 || di >= a.V) st |= SEQ_BAD_INPUT;
-  }
   if (!nbad) {
     // Stream rows p0..p0+n: target rows 0..n (k = kp); p0+n+1..: drafter
     // rows 0..n-1 (k = kq).
-    const int p0 = a.pre[b];
-    const FlatSplit f = make_split(a.pre[a.B], a.V, Elem<DT>::kBytes, a.grid);
+    const FlatSplit f = make_split(R, a.V, E::kBytes, a.grid);
     combine_rows_stats(
         n + 1, a.stats, a.kp,
         [&](int r, int64_t& first, int64_t& cnt) {
@@ -388,176 +391,205 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
     }
     return;
   }
-  // Acceptance tests: accept d_i iff u_i * q_i(d_i) < p~_i(d_i).
-  const float lam = a.lam, oml = 1.f - a.lam;
-  int qz = 0;
-  for (int i = t; i < a.K; i += kBlock) {
+
+  // ---- 2. acceptance tests: accept d_i iff u_i * q_i(d_i) < p~_i(d_i) ----
+#pragma unroll
+  for (int k = 0; k < kDraftsPerThread; ++k) {
+    const int i = t + k * kBlock;
     float p = 0.f, q = 0.f, al = 0.f;
     if (i < n) {
-      const int di = d[i];
-      const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + i * a.tr) * Elem<DT>::kBytes;
-      const char* yr = static_cast<const char*>(a.drf) + (b * a.ds + i * a.dr) * Elem<DT>::kBytes;
-      const float x = Elem<DT>::load1(xr, di);
-      const float y = Elem<DT>::load1(yr, di);
-      p = fast_exp2(__builtin_fmaf(x, a.kp, -s_Mp[i] * a.kp)) / s_Sp[i];
-      q = fast_exp2(__builtin_fmaf(y, a.kq, -s_Mq[i] * a.kq)) / s_Sq[i];
-      const float pt = oml * p + lam * q;
-      const float u = a.u_accept[static_cast<int64_t>(b) * a.K + i];
-      if (q == 0.f && pt > 0.f) qz = 1;
+      p = fast_exp2(__builtin_fmaf(xi[k], a.kp, -s_Mp[i] * a.kp)) / s_Sp[i];
+      q = fast_exp2(__builtin_fmaf(yi[k], a.kq, -s_Mq[i] * a.kq)) / s_Sq[i];
+      const float pt = (1.f - a.lam) * p + a.lam * q;
+      if (q == 0.f && pt > 0.f) atomicOr(&s_st, SEQ_Q_ZERO);
       al = q > 0.f ? fminf(1.f, pt / q) : (pt > 0.f ? 1.f : 0.f);
-      if (!(u * q < pt)) atomicMin(&s_h, i);
+      if (!(ui[k] * q < pt)) atomicMin(&s_h, i);
     }
-    if (c == 0) {
+    if (c == 0 && i < a.K) {
       const int64_t o = static_cast<int64_t>(b) * a.K + i;
       if (a.p_draft) a.p_draft[o] = p;
       if (a.q_draft) a.q_draft[o] = q;
       if (a.alpha) a.alpha[o] = al;
     }
   }
-  if (qz) atomicOr(&s_st, SEQ_Q_ZERO);
   __syncthreads();
-  const int h = s_h;
+  // Uniform across the group: keeps the row addresses in scalar registers.
+  const int h = __builtin_amdgcn_readfirstlane(s_h);
   const bool resid = h < n;
-  const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + static_cast<int64_t>(h) * a.tr) * Elem<DT>::kBytes;
+  const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + static_cast<int64_t>(h) * a.tr) * E::kBytes;
   const char* yr = resid
-      ? static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(h) * a.dr) * Elem<DT>::kBytes
+      ? static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(h) * a.dr) * E::kBytes
       : xr;
   DrawWeight w;
   w.kp = a.kp; w.cp = -s_Mp[h] * a.kp; w.isp = 1.f / s_Sp[h];
   w.kq = a.kq; w.cq = resid ? -s_Mq[h] * a.kq : 0.f; w.isq = resid ? 1.f / s_Sq[h] : 1.f;
   w.resid = resid ? 1 : 0;
-
-  // ---- this group's chunk of the draw mass ------------------------------
-  {
-    const int64_t v0 = static_cast<int64_t>(c) * a.draw_chunk;
-    const int64_t v1 = v0 + a.draw_chunk < a.V ? v0 + a.draw_chunk : a.V;
-    float s;
-    if (resid) {
-      s = sum_resid<DT>(xr, yr, v0, v1, w);
-    } else {
-      SumOne op{w};
-      stream_row<DT, kUnroll>(xr, v0, v1, op);
-      s = op.s;
-    }
-    s = block_sum(s, s_red);
-    if (t == 0) a.dsum[static_cast<int64_t>(b) * NC + c] = s;
-  }
   if (c == 0 && t == 0) {
     DrawRecord r;
     r.status = s_st;
     r.h = h;
-    r.resid = resid ? 1 : 0;
+    r.resid = w.resid;
     r.cp = w.cp; r.isp = w.isp;
     r.cq = w.cq; r.isq = w.isq;
     r.u = a.u_resample[static_cast<int64_t>(b) * (a.K + 1) + h];
     a.rec[b] = r;
   }
+
+  // ---- 3. this chunk's tile masses ---------------------------------------
+  const bool vec = ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0;
+  const int t_lo = c * a.tpc;
+  const int t_hi = t_lo + a.tpc < a.tiles ? t_lo + a.tpc : a.tiles;
+  tile_masses<DT, kWaves>(xr, yr, a.V, t_lo, t_hi, vec, w, a.tmass + static_cast<int64_t>(b) * a.tiles);
 }
 
+constexpr int kDrawWaves = kDrawThreads / 64;
 
-// One group per sequence: find the token whose running mass first exceeds
-// u * Z (vocabulary order), then assemble the outputs.
+// One group of kDrawThreads threads per sequence: the tile where the running
+// mass first exceeds u*Z (the last positive tile if rounding leaves u*Z at or
+// past the total), the token inside it in vocabulary order, and the output
+// assembly C = (d_1..d_h, c) with the ending condition.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k_draw_select(SampleArgs a) {
-  __shared__ float s_dsum[kMaxDrawChunks];
-  __shared__ float s_red[kWaves], s_w[kWaves];
-  __shared__ int s_pick, s_lastpos, s_a;
-  const int NC = a.draw_chunks;
+__global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
+  __shared__ float s_tile[kMaxDrawTiles];
+  __shared__ float s_w[kDrawWaves];
+  __shared__ float s_Z, s_base;
+  __shared__ int s_ct, s_lt, s_cs, s_pick, s_a;
+  using E = Elem<DT>;
   const int b = blockIdx.x;
   const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wv = t >> 6;
+  const int ntiles = a.tiles;
+  const int q = static_cast<int>(cdiv(ntiles, kDrawThreads));   // tiles per thread, <= kDrawTilesPerThread
+  // Everything this group reads first is requested together: the decision
+  // record, the budget and this thread's tile masses.
   const DrawRecord rec = a.rec[b];
-  if (rec.status & SEQ_ERROR_MASK) return;          // outputs already written
-  int status = rec.status;
-  const int h = rec.h;
-  bool resid = rec.resid != 0;
-  const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
   const int budget = a.budget ? a.budget[b] : INT_MAX;
-  const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + static_cast<int64_t>(h) * a.tr) * Elem<DT>::kBytes;
-  const char* yr = resid
-      ? static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(h) * a.dr) * Elem<DT>::kBytes
+  const float* tmass = a.tmass + static_cast<int64_t>(b) * ntiles;
+  float m0[kDrawTilesPerThread];
+#pragma unroll
+  for (int k = 0; k < kDrawTilesPerThread; ++k) {
+    const int tile = t * q + k;
+    m0[k] = (k < q && tile < ntiles) ? tmass[tile] : 0.f;
+  }
+  if (rec.status & SEQ_ERROR_MASK) return;          // outputs already written
+  const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
+  const int h = __builtin_amdgcn_readfirstlane(rec.h);
+  int status = rec.status;
+  const bool resid0 = rec.resid != 0;
+  const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + static_cast<int64_t>(h) * a.tr) * E::kBytes;
+  const char* yr = resid0
+      ? static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(h) * a.dr) * E::kBytes
       : xr;
   DrawWeight w;
   w.kp = a.kp; w.cp = rec.cp; w.isp = rec.isp;
   w.kq = a.kq; w.cq = rec.cq; w.isq = rec.isq;
   w.resid = rec.resid;
+  constexpr int TE = 64 * E::kVec;                              // elements per tile
 
-  // ---- locate u * Z in vocabulary order ----------------------------------
-  for (int k = t; k < NC; k += kBlock) s_dsum[k] = a.dsum[static_cast<int64_t>(b) * NC + k];
-  __syncthreads();
-  float Z = 0.f;
-  for (int k = 0; k < NC; ++k) Z += s_dsum[k];
-  const float Zres = resid ? Z : 0.f;
-  if (resid && !(Z > 0.f)) {
+  // Thread t holds the masses of tiles [t*q, (t+1)*q); an exclusive scan
+  // gives it the mass before them, and the group's total Z.
+  auto locate = [&](const float (&m)[kDrawTilesPerThread]) {
+    if (t == 0) { s_ct = INT_MAX; s_lt = -1; }
+    float loc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kDrawTilesPerThread; ++k) loc += m[k];
+    float Z;
+    const float start = group_exclusive_scan_f<kDrawWaves>(loc, Z, s_w);
+    const float target = rec.u * Z;
+    int hit = INT_MAX, last = -1;
+    float run = start;
+#pragma unroll
+    for (int k = 0; k < kDrawTilesPerThread; ++k) {
+      if (m[k] > 0.f) {
+        if (hit == INT_MAX && run + m[k] > target) hit = t * q + k;
+        last = t * q + k;
+      }
+      run += m[k];
+    }
+    if (hit != INT_MAX) atomicMin(&s_ct, hit);
+    if (last >= 0) atomicMax(&s_lt, last);
+    __syncthreads();
+    const int ct = s_ct != INT_MAX ? s_ct : (s_lt >= 0 ? s_lt : 0);
+    if (t == ct / q) {   // the owner of the chosen tile writes the mass before it
+      float before = start;
+#pragma unroll
+      for (int k = 0; k < kDrawTilesPerThread; ++k)
+        if (t * q + k < ct) before += m[k];
+      s_base = before;
+      s_Z = Z;
+      s_cs = ct;
+    }
+    __syncthreads();
+  };
+  locate(m0);
+  const float Zres = resid0 ? s_Z : 0.f;
+  if (resid0 && !(s_Z > 0.f)) {
     // Residual mass vanished in float32 (p == q up to rounding): draw from p
-    // with the same uniform instead, and flag it.
+    // with the same uniform instead, and flag it.  (This group recomputes
+    // the tile masses of p alone; the case has probability zero in exact
+    // arithmetic.)
     status |= SEQ_Z_ZERO;
-    resid = false;
     w.resid = 0;
-    for (int k = 0; k < NC; ++k) {
-      const int64_t v0 = static_cast<int64_t>(k) * a.draw_chunk;
-      const int64_t v1 = v0 + a.draw_chunk < a.V ? v0 + a.draw_chunk : a.V;
-      float s = 0.f;
-      for (int64_t j = v0 + t; j < v1; j += kBlock) s += w(Elem<DT>::load1(xr, j), 0.f);
-      s = block_sum(s, s_red);
-      __syncthreads();
-      if (t == 0) s_dsum[k] = s;
-      __syncthreads();
-    }
-    Z = 0.f;
-    for (int k = 0; k < NC; ++k) Z += s_dsum[k];
-  }
-  const float target = rec.u * Z;
-  // Chunk whose running mass first exceeds u*Z (positive chunks only).
-  int cs = -1, clast = -1;
-  float base = 0.f, run = 0.f;
-  for (int k = 0; k < NC; ++k) {
-    if (!(s_dsum[k] > 0.f)) continue;
-    clast = k;
-    if (run + s_dsum[k] > target) { cs = k; base = run; break; }
-    run += s_dsum[k];
-  }
-  if (cs < 0) {  // rounding: u*Z at or past the total -> last positive chunk
-    cs = clast >= 0 ? clast : 0;
-    base = run - (clast >= 0 ? s_dsum[clast] : 0.f);
-  }
-  if (t == 0) { s_pick = INT_MAX; s_lastpos = -1; }
-  __syncthreads();
-  // Thread t holds elements [c0 + t*P, c0 + (t+1)*P) of the chunk (P =
-  // kDrawPerThread): their weights stay in registers for the scan.
-  const int64_t c0 = static_cast<int64_t>(cs) * a.draw_chunk;
-  const int64_t c1 = c0 + a.draw_chunk < a.V ? c0 + a.draw_chunk : a.V;
-  const int64_t e0 = c0 + static_cast<int64_t>(t) * kDrawPerThread;
-  float wv[kDrawPerThread];
-  load_weights<DT>(xr, yr, e0, c1, w, wv);
-  float loc = 0.f;
-  int lastpos = -1;
+    yr = xr;
+    const bool vec = (reinterpret_cast<uintptr_t>(xr) & 15u) == 0;
+    tile_masses<DT, kDrawWaves>(xr, yr, a.V, 0, ntiles, vec, w, s_tile);
+    __syncthreads();
+    float m1[kDrawTilesPerThread];
 #pragma unroll
-  for (int j = 0; j < kDrawPerThread; ++j) {
-    loc += wv[j];
-    if (wv[j] > 0.f) lastpos = static_cast<int>(e0 + j);
-  }
-  float tot;
-  const float start = base + block_exclusive_scan(loc, tot, s_w);
-  if (lastpos >= 0) atomicMax(&s_lastpos, lastpos);
-  if (loc > 0.f && start + loc > target) {
-    float r = start;
-    int found = INT_MAX;
-#pragma unroll
-    for (int j = 0; j < kDrawPerThread; ++j) {
-      r += wv[j];
-      if (found == INT_MAX && wv[j] > 0.f && r > target) found = static_cast<int>(e0 + j);
+    for (int k = 0; k < kDrawTilesPerThread; ++k) {
+      const int tile = t * q + k;
+      m1[k] = (k < q && tile < ntiles) ? s_tile[tile] : 0.f;
     }
-    if (found != INT_MAX) atomicMin(&s_pick, found);
+    locate(m1);
   }
-  __syncthreads();
-  const int tok = s_pick != INT_MAX ? s_pick : s_lastpos;
+  const float target = rec.u * s_Z;
 
+  // Wave 0 rescans the chosen tile in vocabulary order: lane l holds the
+  // weights of the tile's l-th vector; a wave scan gives each lane the mass
+  // before its vector.
+  if (wv == 0) {
+    const int ct = __builtin_amdgcn_readfirstlane(s_cs);
+    const int64_t e0 = static_cast<int64_t>(ct) * TE + lane * E::kVec;
+    float wt[E::kVec];
+    float loc = 0.f;
+#pragma unroll
+    for (int j = 0; j < E::kVec; ++j) {
+      const int64_t e = e0 + j;
+      wt[j] = e < a.V ? w(E::load1(xr, e), w.resid ? E::load1(yr, e) : 0.f) : 0.f;
+      loc += wt[j];
+    }
+    float inc = loc;
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+      const float o = __shfl_up(inc, k, 64);
+      if (lane >= k) inc += o;
+    }
+    const float start = s_base + inc - loc;
+    int found = -1, lastpos = -1;
+    float r = start;
+#pragma unroll
+    for (int j = 0; j < E::kVec; ++j) {
+      r += wt[j];
+      if (wt[j] > 0.f) {
+        if (found < 0 && r > target) found = static_cast<int>(e0 + j);
+        lastpos = static_cast<int>(e0 + j);
+      }
+    }
+    const uint64_t hits = __ballot(found >= 0);
+    const uint64_t poss = __ballot(lastpos >= 0);
+    int tok = -1;
+    if (hits) tok = __shfl(found, __builtin_ctzll(hits), 64);
+    else if (poss) tok = __shfl(lastpos, 63 - __builtin_clzll(poss), 64);
+    if (lane == 0) s_pick = tok;
+  }
   // ---- output assembly: C = (d_1..d_h, c), then the ending condition ----
   const int A = h + 1;
   if (t == 0) s_a = A < budget ? A : budget;
   __syncthreads();
+  const int tok = s_pick;
   if (a.eos >= 0) {
-    for (int i = t; i < A; i += kBlock) {
+    for (int i = t; i < A; i += kDrawThreads) {   // A can be K + 1 = kDrawThreads + 1
       const int ci = i < h ? d[i] : tok;
       if (ci == a.eos) atomicMin(&s_a, i + 1);
     }
@@ -565,7 +597,7 @@ __global__ __launch_bounds__(kBlock) void k_draw_select(SampleArgs a) {
   __syncthreads();
   const int an = s_a;
   int32_t* out = a.out_tokens + static_cast<int64_t>(b) * (a.K + 1);
-  for (int i = t; i <= a.K; i += kBlock) out[i] = i < an ? (i < h ? d[i] : tok) : -1;
+  for (int i = t; i <= a.K; i += kDrawThreads) out[i] = i < an ? (i < h ? d[i] : tok) : -1;
   if (t == 0) {
     a.accept_len[b] = h;
     a.num_out[b] = an;
@@ -591,9 +623,9 @@ bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const Tim
 bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
   const bool bf = dtype == DT_BF16;
   return launch(bf ? fn(k_sample_rows<DT_BF16>) : fn(k_sample_rows<DT_F32>), a.grid, stream, a, ev) &&
-         launch(bf ? fn(k_draw_mass<DT_BF16>) : fn(k_draw_mass<DT_F32>),
-                static_cast<int64_t>(a.B) * a.draw_chunks, stream, a) &&
-         launch(bf ? fn(k_draw_select<DT_BF16>) : fn(k_draw_select<DT_F32>), a.B, stream, a);
+         launch(bf ? fn(k_draw_mass<DT_BF16>) : fn(k_draw_mass<DT_F32>), static_cast<int64_t>(a.B) * a.chunks,
+                stream, a) &&
+         launch_threads(bf ? fn(k_draw_select<DT_BF16>) : fn(k_draw_select<DT_F32>), a.B, kDrawThreads, stream, a);
 }
 
 }  // namespace dbv

@@ -10,8 +10,8 @@
 //     order, as consecutive slots;
 //   * a launch never has more active groups than kMaxGrid, so every slot fits
 //     the workspace sized by partial_bytes(max_rows).
-// Plans: the draw chunks cover the row and fit the select kernel's register
-// scan; workspace sections are 256-byte aligned and do not overlap.
+// Plans: the draw tiles of the largest vocabulary fit the LDS tile array and
+// 32-bit offsets; workspace sections are 256-byte aligned and do not overlap.
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -96,21 +96,28 @@ int main() {
   const int Bs[] = {1, 2, 3, 8, 16, 32, 64, 128, 1000};
   const int Ks[] = {0, 1, 4, 8, 16, 31, 64};
   for (int64_t V : PVs) {
+    // The draw's tiles fit the LDS array of tile masses for either element
+    // size, and byte offsets within a row fit 32 bits.
+    for (int64_t eb : {2, 4}) {
+      if (V <= kMaxSampleV)
+        CHECK(cdiv(V, draw_tile(eb)) <= kMaxDrawTiles, "V=%lld eb=%lld tiles", (long long)V, (long long)eb);
+    }
+    CHECK(kMaxSampleV * 4 < (int64_t(1) << 32), "draw offsets");
     for (int B : Bs) {
       for (int K : Ks) {
-        const SamplePlan s = plan_sample(B, K, static_cast<int>(V));
-        CHECK(s.max_rows == static_cast<int64_t>(B) * (2 * K + 1), "sample rows");
-        CHECK(s.draw_chunks >= 1 && s.draw_chunks <= kMaxDrawChunks, "V=%lld B=%d draw_chunks=%d",
-              (long long)V, B, s.draw_chunks);
-        CHECK(s.draw_chunk <= kDrawChunkMax && s.draw_chunk % 256 == 0, "V=%lld draw_chunk=%lld",
-              (long long)V, (long long)s.draw_chunk);
-        CHECK(s.draw_chunks * s.draw_chunk >= V, "V=%lld B=%d draw %d x %lld", (long long)V, B,
-              s.draw_chunks, (long long)s.draw_chunk);
-        CHECK(s.off_pre % 256 == 0 && s.off_rec % 256 == 0 && s.off_dsum % 256 == 0, "sample offsets");
-        CHECK(s.off_pre >= static_cast<size_t>(s.max_rows + kMaxGrid) * kWavesPlan * 8, "pre overlaps stats");
-        CHECK(s.off_rec >= s.off_pre + static_cast<size_t>(B + 1) * 4, "rec overlaps pre");
-        CHECK(s.off_dsum >= s.off_rec + static_cast<size_t>(B) * sizeof(DrawRecord), "dsum overlaps rec");
-        CHECK(s.bytes >= s.off_dsum + static_cast<size_t>(B) * s.draw_chunks * 4, "sample bytes");
+        for (int64_t eb : {2, 4}) {
+          const SamplePlan s = plan_sample(B, K, static_cast<int>(V), eb);
+          CHECK(s.max_rows == static_cast<int64_t>(B) * (2 * K + 1), "sample rows");
+          CHECK(s.tiles == cdiv(V, draw_tile(eb)) && s.tpc >= 1 && s.chunks * s.tpc >= s.tiles &&
+                    (s.chunks - 1) * s.tpc < s.tiles,
+                "V=%lld B=%d tiles %lld tpc %lld chunks %lld", (long long)V, B, (long long)s.tiles,
+                (long long)s.tpc, (long long)s.chunks);
+          CHECK(s.off_pre % 256 == 0 && s.off_rec % 256 == 0 && s.off_tmass % 256 == 0, "sample offsets");
+          CHECK(s.off_pre >= static_cast<size_t>(s.max_rows + kMaxGrid) * kWavesPlan * 8, "pre overlaps stats");
+          CHECK(s.off_rec >= s.off_pre + static_cast<size_t>(B + 1) * 4, "rec overlaps pre");
+          CHECK(s.off_tmass >= s.off_rec + static_cast<size_t>(B) * sizeof(DrawRecord), "tmass overlaps rec");
+          CHECK(s.bytes >= s.off_tmass + static_cast<size_t>(B) * s.tiles * 4, "sample bytes");
+        }
 
         const GreedyPlan g = plan_greedy(B, K, K + 1, static_cast<int>(V));
         CHECK(g.max_rows == static_cast<int64_t>(B) * (2 * K + 2), "greedy rows");

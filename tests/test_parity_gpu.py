@@ -220,6 +220,65 @@ def test_determinism(dev):
         assert torch.equal(a[k], b[k]), k
 
 
+def test_max_draft_length(dev):
+    # K = W = 1024, the largest the library takes: 2K+1 rows per sequence are
+    # combined by one group.  Sequence 0 drafts from the target itself (q = p,
+    # every draft accepted, bonus from row K); sequence 1 drafts with noise.
+    say("max draft length")
+    B, K, V = 2, 1024, 257
+    x = workloads.chain_inputs(84, B, K, V, torch.float32, sigma=1.0)
+    x["drf"][0] = x["tgt"][0, :K]
+    x["draft_tokens"][0] = torch.multinomial(torch.softmax(x["drf"][0], -1), 1,
+                                             generator=torch.Generator().manual_seed(5))[:, 0].to(torch.int32)
+    xd = _to(x, dev)
+    res = dbv.verify_rejection(xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"],
+                               draft_len=xd["draft_len"])
+    xn = _np_inputs(x)
+    o = oracle.verify_rejection(xn["tgt"], xn["drf"], xn["draft_tokens"], xn["draft_len"], 1.0, 1.0,
+                                xn["u_accept"], xn["u_resample"])
+    assert o["accept_len"][0] == K
+    check_sampling(res, xn, o, 0.0, 1.0, 1.0, "float32")
+    g = dbv.verify_greedy(xd["tgt"], xd["draft_tokens"], xd["draft_len"], xd["drf"])
+    check_greedy(g, oracle.verify_greedy(xn["tgt"], xn["draft_tokens"], xn["draft_len"], xn["drf"]))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_largest_vocabulary(dev, dtype):
+    # V = 2^21, the largest the sampling entry points take: the draw's
+    # segments are at their longest (8 elements per thread in the rescan).
+    say("largest V", dtype)
+    V = 1 << 21
+    x = workloads.chain_inputs(85, 2, 2, V, dtype, sigma=2.0)
+    x["draft_tokens"][1, 0] = (x["draft_tokens"][1, 0] + 7) % V   # a likely reject
+    xd = _to(x, dev)
+    res = dbv.verify_rejection(xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"])
+    xn = _np_inputs(x)
+    o = oracle.verify_rejection(xn["tgt"], xn["drf"], xn["draft_tokens"], None, 1.0, 1.0,
+                                xn["u_accept"], xn["u_resample"])
+    near = check_sampling(res, xn, o, 0.0, 1.0, 1.0, str(dtype).split(".")[1])
+    say("near-margin", dict(near))
+
+
+def test_many_sequences(dev):
+    # More sequences than one LDS directory entry each (B > 1024): rows are
+    # located through blocks of sequences; some lengths are invalid.
+    say("many sequences")
+    B, K, V = 1500, 2, 200
+    x = workloads.chain_inputs(86, B, K, V, torch.bfloat16, sigma=1.0, random_lengths=True)
+    x["draft_len"][7] = K + 1
+    x["draft_len"][1100] = -1
+    xd = _to(x, dev)
+    res = dbv.verify_rejection(xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"],
+                               draft_len=xd["draft_len"])
+    xn = _np_inputs(x)
+    o = oracle.verify_rejection(xn["tgt"], xn["drf"], xn["draft_tokens"], xn["draft_len"], 1.0, 1.0,
+                                xn["u_accept"], xn["u_resample"])
+    assert o["status"][7] == oracle.STATUS_BAD_INPUT and o["status"][1100] == oracle.STATUS_BAD_INPUT
+    check_sampling(res, xn, o, 0.0, 1.0, 1.0, "bfloat16")
+    g = dbv.verify_greedy(xd["tgt"], xd["draft_tokens"], xd["draft_len"], xd["drf"])
+    check_greedy(g, oracle.verify_greedy(xn["tgt"], xn["draft_tokens"], xn["draft_len"], xn["drf"]))
+
+
 # -------------------------------------------------------------------- tree ---
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
