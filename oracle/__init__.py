@@ -12,8 +12,10 @@ following the pages' definitions in their own order:
 * ``rows``   -- per-row quantities: tempered softmax, lowest-index argmax,
   the acceptance test, inverse-CDF draws, the residual ``[p~ - q]_+``.
 * ``chain``  -- per-sequence verification of a drafted chain: greedy match,
-  lossless rejection and the linear lenient rule, with the stopping rule and
-  next-draft retention.
+  lossless rejection, the linear lenient rule and the modified Cactus rule,
+  with the stopping rule and next-draft retention.
+* ``cactus`` -- the modified Cactus budget: gamma from the Bernoulli KL
+  budget, the modified target p~ and its residual.
 * ``tree``   -- coupled shared-Gumbel state-equality verification of a draft
   tree (and its T=0 greedy special case).
 
@@ -25,7 +27,8 @@ Sources (pages by title):
   via Commit-Order Prediction" (SPOT): Sec. 4.1, Sec. 4.3, App. A.1, A.3
   Eq. 5-7, App. B Eq. 10-14.
 * "Speculative Diffusion is a Tale of Two Tradeoffs" (Two Tradeoffs): Sec. 2
-  Eq. 1-5 and Theorem 1, Sec. 3.2 Algorithm 1, App. C Proposition 1.
+  Eq. 1-5 and Theorem 1, Sec. 3.2 Algorithm 1, App. C Proposition 1,
+  App. E (modified Cactus, Eq. 17-18).
 """
 
 from .rows import (  # noqa: F401
@@ -34,7 +37,10 @@ from .rows import (  # noqa: F401
     row_status, tempered_softmax, argmax_lowest, acceptance_test,
     inverse_cdf, residual_weights, stopping_index,
 )
-from .chain import verify_greedy, verify_rejection, verify_lenient  # noqa: F401
+from .chain import verify_greedy, verify_rejection, verify_lenient, verify_cactus  # noqa: F401
+from .cactus import (  # noqa: F401
+    cactus_divergence, cactus_gamma, cactus_target, cactus_acceptance, cactus_residual,
+)
 from .tree import (  # noqa: F401
     TREE_STATE_EQUALITY, TREE_FIXED_POSITION, state_transition, walk,
     verify_gumbel_tree,

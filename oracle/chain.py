@@ -21,6 +21,7 @@ from .rows import (
     row_status, tempered_softmax, argmax_lowest, acceptance_test,
     inverse_cdf, residual_weights, stopping_index,
 )
+from .cactus import cactus_acceptance, cactus_residual
 
 
 def _lengths(draft_len, B, K):
@@ -102,8 +103,10 @@ def verify_greedy(tgt, draft_tokens, draft_len=None, draft_rows=None,
 
 
 def _sampling_verify(tgt, drf, draft_tokens, draft_len, t_target, t_draft,
-                     lam, u_accept, u_resample, eos_id, len_budget):
+                     lam, u_accept, u_resample, eos_id, len_budget, delta=None):
     """Rejection-sampling verification of a chain; lam = 0 is lossless.
+    With ``delta`` set, the modified Cactus rule (oracle.cactus) replaces
+    the linear one: each drafted token's target is p~ with p~(d) = gamma.
 
     Packed-SS, Algorithm 2 (and Two Tradeoffs, Algorithm 1 for lam > 0):
       p_i = target distributions, i = 1..|D|+1
@@ -132,6 +135,7 @@ def _sampling_verify(tgt, drf, draft_tokens, draft_len, t_target, t_draft,
         out_tokens=np.full((B, K + 1), -1, np.int32),
         status=np.zeros(B, np.int32),
         p_draft=np.zeros((B, K)), q_draft=np.zeros((B, K)), alpha=np.zeros((B, K)),
+        gamma=np.zeros((B, K)),
         accept_bits=np.zeros((B, K), bool), accept_margin=np.full((B, K), np.inf),
         residual_mass=np.zeros(B), draw_margin=np.full(B, np.inf),
         draw_row=np.full(B, -1, np.int32), draw_kind=[None] * B,
@@ -161,7 +165,12 @@ def _sampling_verify(tgt, drf, draft_tokens, draft_len, t_target, t_draft,
         p = [tempered_softmax(tgt[b, i], t_target) for i in range(n + 1)]
         q = [tempered_softmax(drf[b, i], t_draft) for i in range(n)]
         for i in range(n):
-            acc, alpha, margin, qz = acceptance_test(ua[b, i], p[i][d[i]], q[i][d[i]], lam)
+            if delta is None:
+                acc, alpha, margin, qz = acceptance_test(ua[b, i], p[i][d[i]], q[i][d[i]], lam)
+                gamma = (1.0 - lam) * p[i][d[i]] + lam * q[i][d[i]]
+            else:
+                acc, alpha, margin, qz, gamma = cactus_acceptance(ua[b, i], p[i][d[i]], q[i][d[i]], delta)
+            out["gamma"][b, i] = gamma
             out["p_draft"][b, i] = p[i][d[i]]
             out["q_draft"][b, i] = q[i][d[i]]
             out["alpha"][b, i] = alpha
@@ -174,7 +183,10 @@ def _sampling_verify(tgt, drf, draft_tokens, draft_len, t_target, t_draft,
             h += 1
 
         if h < n:
-            r = residual_weights(p[h], q[h], lam)
+            if delta is None:
+                r = residual_weights(p[h], q[h], lam)
+            else:
+                r = cactus_residual(p[h], q[h], d[h], out["gamma"][b, h])
             if np.sum(r) > 0.0:
                 c, margin, Z = inverse_cdf(r, ur[b, h])
                 kind = "residual"
@@ -218,3 +230,16 @@ def verify_lenient(tgt, drf, draft_tokens, draft_len, t_target, t_draft, lam,
     return _sampling_verify(tgt, drf, draft_tokens, draft_len, t_target,
                             t_draft, float(lam), u_accept, u_resample, eos_id,
                             len_budget)
+
+
+def verify_cactus(tgt, drf, draft_tokens, draft_len, t_target, t_draft, delta,
+                  u_accept, u_resample, eos_id=-1, len_budget=None):
+    """Verification with the modified Cactus rule (Two Tradeoffs, App. E):
+    gamma solves Phi(gamma) = delta exactly, accept with min{1, gamma/q(d)},
+    correct from normalize([p~ - q]_+), bonus from p.  delta = 0 is the
+    lossless rule."""
+    if not (delta >= 0.0 and np.isfinite(delta)):
+        raise ValueError("delta must be finite and >= 0")
+    return _sampling_verify(tgt, drf, draft_tokens, draft_len, t_target,
+                            t_draft, 0.0, u_accept, u_resample, eos_id,
+                            len_budget, delta=float(delta))

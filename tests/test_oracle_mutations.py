@@ -5,16 +5,20 @@ test of the product."""
 import numpy as np
 import pytest
 
+import math
+
 import oracle
+import oracle.cactus as cactus
 import oracle.chain as chain
 import oracle.rows as rows
 import oracle.tree as tree
+import tests.test_oracle_cactus_pins as kp
 import tests.test_oracle_chain_pins as cp
 import tests.test_oracle_tree_pins as tp
 
 
 def _patch(monkeypatch, name, fn):
-    for mod in (oracle, rows, chain, tree):
+    for mod in (oracle, rows, chain, tree, cactus):
         if hasattr(mod, name):
             monkeypatch.setattr(mod, name, fn)
 
@@ -75,6 +79,25 @@ def _stop_ignores_eos(C, A, eos_id=-1, budget=None):
     return A if budget is None else min(A, budget)
 
 
+def _gamma_taylor(p, delta, iters=0):
+    return min(p + math.sqrt(2.0 * delta * p * (1.0 - p)), 1.0)
+
+
+def _target_not_rescaled(p, y, gamma):
+    pt = np.asarray(p, np.float64).copy()
+    pt[y] = gamma
+    return pt
+
+
+def _residual_lossless(p, q, y, gamma):
+    return np.maximum(np.asarray(p, np.float64) - np.asarray(q, np.float64), 0.0)
+
+
+def _acceptance_ignores_budget(u, p_y, q_y, delta):
+    alpha = min(1.0, p_y / q_y) if q_y > 0 else 1.0
+    return bool(u < alpha), alpha, abs(u - alpha), False, p_y
+
+
 MUTATIONS = [
     ("acceptance_test", _acc_no_min, cp.test_exact_acceptance_rate_is_one_minus_tv, dict(lam=0.0)),
     ("acceptance_test", _acc_inverted, cp.test_exact_acceptance_rate_is_one_minus_tv, dict(lam=0.0)),
@@ -86,6 +109,10 @@ MUTATIONS = [
     ("argmax_lowest", _argmax_highest, cp.test_argmax_lowest_index_brute_force, {}),
     ("inverse_cdf", _icdf_ge, cp.test_inverse_cdf_edges, {}),
     ("stopping_index", _stop_ignores_eos, cp.test_stopping_rule_eos_and_budget, {}),
+    ("cactus_gamma", _gamma_taylor, kp.test_modified_target_meets_kl_budget_exactly, dict(delta=0.25)),
+    ("cactus_target", _target_not_rescaled, kp.test_modified_target_meets_kl_budget_exactly, dict(delta=0.25)),
+    ("cactus_residual", _residual_lossless, kp.test_emitted_law_and_acceptance_rate, dict(delta=0.3)),
+    ("cactus_acceptance", _acceptance_ignores_budget, kp.test_emitted_law_and_acceptance_rate, dict(delta=0.3)),
 ]
 
 
