@@ -12,6 +12,7 @@ and the correction or bonus draw.  Workloads (sizes of the pages' setups):
   c3  lenient verify              B=32 K=16 V=128256 bf16, sigma=1, T=1, lambda=0.5
   c4  coupled-Gumbel tree verify  B=16 S=64 L=32 V=151936 bf16
   c5  packed greedy verify+draft  B=64 K=32 V=131072 bf16
+  c3c modified-Cactus verify      B=32 K=16 V=128256 bf16, sigma=1, T=1, delta=1
 
 Inputs smaller than 1 GiB are replicated into several buffer sets and the
 steps rotate over them, so the 256 MiB last-level cache cannot serve them.
@@ -46,7 +47,9 @@ DESCR = {
     "c3": "lenient verify B=32 K=16 V=128256 bf16 sigma=1 T=1 lambda=0.5",
     "c4": "coupled-Gumbel tree verify B=16 S=64 L=32 V=151936 bf16",
     "c5": "packed greedy verify+draft B=64 K=32 V=131072 bf16",
+    "c3c": "modified-Cactus verify B=32 K=16 V=128256 bf16 sigma=1 T=1 delta=1",
 }
+CACTUS_DELTA = 1.0
 
 
 def parse():
@@ -106,7 +109,7 @@ class Case:
         self.name = name
         self.dev = dev
         eb = 2
-        if name in ("c1", "c2", "c3"):
+        if name in ("c1", "c2", "c3", "c3c"):
             if name == "c1":
                 x = workloads.config1()
                 eb = 4
@@ -127,14 +130,15 @@ class Case:
             R = self._rotation(per_set)
             for _ in range(R):
                 xd = {k: v.to(dev).clone() if torch.is_tensor(v) else v for k, v in x.items()}
-                fn = dbv.verify_lenient if name == "c3" else dbv.verify_rejection
                 kw = dict(draft_len=xd["draft_len"], temperature_target=x["temperature"],
                           temperature_draft=x["temperature"], prepare=True)
+                args = (xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"])
                 if name == "c3":
-                    c = fn(xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"],
-                           self.lam, **kw)
+                    c = dbv.verify_lenient(*args, self.lam, **kw)
+                elif name == "c3c":
+                    c = dbv.verify_cactus(*args, CACTUS_DELTA, **kw)
                 else:
-                    c = fn(xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"], **kw)
+                    c = dbv.verify_rejection(*args, **kw)
                 self.calls.append(c)
             self.shape = dict(B=B, K=K, V=V)
         elif name == "c5":
@@ -186,16 +190,19 @@ class Case:
         done_pos = 0
         calls = 0
         t0 = time.perf_counter()
-        if self.name in ("c1", "c2", "c3"):
+        if self.name in ("c1", "c2", "c3", "c3c"):
             B = x["tgt"].shape[0]
-            nb = min(B, 4) if self.name == "c3" else B
+            nb = min(B, 4) if self.name in ("c3", "c3c") else B
             tgt, drf = np64(x["tgt"][:nb]), np64(x["drf"][:nb])
             d, n = npi(x["draft_tokens"][:nb]), npi(x["draft_len"][:nb])
             ua, ur = np64(x["u_accept"][:nb]), np64(x["u_resample"][:nb])
             T = x["temperature"]
             t0 = time.perf_counter()
             while True:
-                oracle.verify_lenient(tgt, drf, d, n, T, T, self.lam, ua, ur)
+                if self.name == "c3c":
+                    oracle.verify_cactus(tgt, drf, d, n, T, T, CACTUS_DELTA, ua, ur)
+                else:
+                    oracle.verify_lenient(tgt, drf, d, n, T, T, self.lam, ua, ur)
                 done_pos += int(n.sum())
                 calls += 1
                 if time.perf_counter() - t0 >= seconds:

@@ -6,7 +6,8 @@ raw device pointers and the current HIP stream to the C ABI.  Every step of
 the verification runs in the library's HIP kernels; there is no fallback.
 
 Entry points (same names as the C ABI):
-  verify_greedy, verify_rejection, verify_lenient, verify_gumbel_tree
+  verify_greedy, verify_rejection, verify_lenient, verify_cactus,
+  verify_gumbel_tree
 """
 
 import torch
@@ -19,7 +20,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "verify_greedy", "verify_rejection", "verify_lenient", "verify_gumbel_tree",
+    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_gumbel_tree",
     "workspace_size", "DBVError", "Prepared",
 ]
 
@@ -177,7 +178,7 @@ def _sampling(fn_name, tgt, drf, draft_tokens, draft_len, temperature_target,
     ws = workspace if workspace is not None else _workspace(need, dev)
     args = [B, K, V, dt, tgt.data_ptr(), ts, tr, drf.data_ptr(), ds, dr, _ptr(d), _ptr(n),
             float(temperature_target), float(temperature_draft)]
-    if fn_name == "verify_lenient":
+    if fn_name in ("verify_lenient", "verify_cactus"):
         args.append(float(lam))
     args += [ua.data_ptr() if K else None, ur.data_ptr(), int(eos_id), _ptr(bud),
              out["accept_len"].data_ptr(), out["out_tokens"].data_ptr(), out["num_out"].data_ptr(),
@@ -211,6 +212,18 @@ def verify_lenient(tgt, drf, draft_tokens, u_accept, u_resample, lam, draft_len=
     Theorem 1 and Algorithm 1).  Arguments as verify_rejection plus lam."""
     return _sampling("verify_lenient", tgt, drf, draft_tokens, draft_len,
                      temperature_target, temperature_draft, lam, u_accept, u_resample,
+                     eos_id, len_budget, workspace, diagnostics, prepare)
+
+
+def verify_cactus(tgt, drf, draft_tokens, u_accept, u_resample, delta, draft_len=None,
+                  temperature_target=1.0, temperature_draft=1.0, eos_id=-1,
+                  len_budget=None, workspace=None, diagnostics=True, prepare=False):
+    """Verification with the modified Cactus rule (Two Tradeoffs, App. E):
+    the drafted token's target mass is raised to the largest gamma whose
+    rescaled target stays within KL budget delta of p.  Arguments as
+    verify_rejection plus delta >= 0 (0 = lossless)."""
+    return _sampling("verify_cactus", tgt, drf, draft_tokens, draft_len,
+                     temperature_target, temperature_draft, delta, u_accept, u_resample,
                      eos_id, len_budget, workspace, diagnostics, prepare)
 
 

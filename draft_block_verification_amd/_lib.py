@@ -31,7 +31,7 @@ SEQ_Z_ZERO = 16
 SEQ_ERROR_MASK = 7
 
 EXPORTS = (
-    "verify_greedy", "verify_rejection", "verify_lenient", "verify_gumbel_tree",
+    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_gumbel_tree",
     "verify_workspace_size", "verify_status_string", "verify_abi_version",
     "verify_set_timing_events",
 )
@@ -50,6 +50,8 @@ _SIGS = {
                          _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "verify_lenient": [_i, _i, _i, _i, _p, _i64, _i64, _p, _i64, _i64, _p, _p, _f, _f, _f, _p, _p,
                        _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
+    "verify_cactus": [_i, _i, _i, _i, _p, _i64, _i64, _p, _i64, _i64, _p, _p, _f, _f, _f, _p, _p,
+                      _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "verify_gumbel_tree": [_i, _i, _i, _i, _i, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p,
                            _i64, _i64, _f, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "verify_workspace_size": [_i, _i, _i, _i, _i, _i],

@@ -83,7 +83,8 @@ bool stream_fits(int64_t max_rows, int64_t V) {
 
 dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t ts, int64_t tr,
                          const void* drf, int64_t ds, int64_t dr, const int32_t* draft_tokens,
-                         const int32_t* draft_len, float tt, float td, float lam, const float* u_accept,
+                         const int32_t* draft_len, float tt, float td, int rule, float lam, float delta,
+                         const float* u_accept,
                          const float* u_resample, int32_t eos_id, const int32_t* len_budget,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* num_out, float* p_draft,
                          float* q_draft, float* alpha, float* residual_mass, int32_t* status, void* ws,
@@ -91,6 +92,7 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   if (B < 0 || K < 0 || K > kMaxDraft || V < 1 || !dtype_ok(dtype)) return DBV_ERR_INVALID_ARG;
   if (V > dbv::kMaxSampleV) return DBV_ERR_UNSUPPORTED;
   if (!temp_ok(tt) || !temp_ok(td) || !(lam >= 0.f && lam <= 1.f)) return DBV_ERR_INVALID_ARG;
+  if (!(std::isfinite(delta) && delta >= 0.f)) return DBV_ERR_INVALID_ARG;
   if (ts < 0 || tr < 0 || ds < 0 || dr < 0) return DBV_ERR_INVALID_ARG;
   if (tgt == nullptr || u_resample == nullptr) return DBV_ERR_INVALID_ARG;
   if (K > 0 && (drf == nullptr || draft_tokens == nullptr || u_accept == nullptr)) return DBV_ERR_INVALID_ARG;
@@ -110,7 +112,9 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.drf = drf; a.ds = ds; a.dr = dr;
   a.draft_tokens = draft_tokens; a.draft_len = draft_len;
   a.kp = dbv::kLog2eHost / tt; a.kq = dbv::kLog2eHost / td;
+  a.rule = rule;
   a.lam = lam;
+  a.delta = delta;
   a.u_accept = u_accept; a.u_resample = u_resample;
   a.eos = eos_id; a.budget = len_budget;
   a.accept_len = accept_len; a.out_tokens = out_tokens; a.num_out = num_out;
@@ -193,8 +197,8 @@ dbv_status verify_rejection(int B, int K, int V, dbv_dtype dtype, const void* tg
                             float* q_draft, float* alpha, float* residual_mass, int32_t* status, void* ws,
                             size_t ws_bytes, void* stream) {
   return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
-                       drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft, 0.f,
-                       u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft,
+                       drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft,
+                       dbv::RULE_LINEAR, 0.f, 0.f, u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft,
                        q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
 }
 
@@ -206,9 +210,22 @@ dbv_status verify_lenient(int B, int K, int V, dbv_dtype dtype, const void* tgt,
                           int32_t* num_out, float* p_draft, float* q_draft, float* alpha, float* residual_mass,
                           int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
-                       drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft, lambda,
-                       u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft,
+                       drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft,
+                       dbv::RULE_LINEAR, lambda, 0.f, u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft,
                        q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
+}
+
+dbv_status verify_cactus(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
+                         int64_t tgt_row_stride, const void* drf, int64_t drf_seq_stride, int64_t drf_row_stride,
+                         const int32_t* draft_tokens, const int32_t* draft_len, float temperature_target,
+                         float temperature_draft, float delta, const float* u_accept, const float* u_resample,
+                         int32_t eos_id, const int32_t* len_budget, int32_t* accept_len, int32_t* out_tokens,
+                         int32_t* num_out, float* p_draft, float* q_draft, float* alpha, float* residual_mass,
+                         int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
+                       drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft,
+                       dbv::RULE_CACTUS, 0.f, delta, u_accept, u_resample, eos_id, len_budget, accept_len,
+                       out_tokens, num_out, p_draft, q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
 }
 
 dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const void* logits, int64_t seq_stride,

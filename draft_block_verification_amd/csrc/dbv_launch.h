@@ -25,6 +25,8 @@ struct GreedyArgs {
   int elem_bytes;                      // 2 (bf16) or 4 (fp32)
 };
 
+enum : int { RULE_LINEAR = 0, RULE_CACTUS = 1 };
+
 struct SampleArgs {
   int B, K, V;
   const void* tgt; int64_t ts, tr;
@@ -32,7 +34,9 @@ struct SampleArgs {
   const int32_t* draft_tokens;
   const int32_t* draft_len;
   float kp, kq;                        // log2(e) / temperature
-  float lam;                           // 0 = lossless
+  int rule;                            // RULE_LINEAR or RULE_CACTUS
+  float lam;                           // linear rule: 0 = lossless
+  float delta;                         // Cactus rule: KL budget
   const float* u_accept; const float* u_resample;
   int32_t eos;
   const int32_t* budget;

@@ -167,10 +167,13 @@ inline GreedyPlan plan_greedy(int B, int K, int W, int V) {
 struct DrawRecord {
   int status;        // sequence status bits; error bits mean "done"
   int h;             // accepted drafts; the draw uses row h
-  int resid;         // 1: residual [p - q]_+ at row h, 0: bonus from p
-  float cp, isp;     // exp2 offset and 1/S of target row h
+  int resid;         // 1: residual [p~ - q]_+ at row h, 0: bonus from p
+  float cp, isp;     // exp2 offset and scale of target row h (1/S, times the
+                     // Cactus rescaling of the other tokens)
   float cq, isq;     // same for drafter row h (residual only)
   float u;           // resample uniform of row h
+  int excl;          // Cactus: the drafted token of row h, whose weight is
+  float wexcl;       // wexcl = [gamma - q(d)]_+; -1 for the linear rule
 };
 
 // Stream order: for each sequence b, target rows 0..n_b, then drafter rows

@@ -195,17 +195,66 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
   });
 }
 
-// Per-element weight of the draw: residual [p - q]_+ or bonus exp2 weight.
+// Per-element weight of the draw: residual [p~ - q]_+ or bonus exp2 weight.
+// For the linear rule p~ = p up to the (1 - lambda) factor, which the
+// normalisation removes; for the Cactus rule isp also carries the rescaling
+// (1 - gamma) / (1 - p(d)) of every token but the drafted one, element
+// `excl`, whose weight is wexcl = [gamma - q(d)]_+.
 struct DrawWeight {
   float kp, cp, isp, kq, cq, isq;
   int resid;
+  int excl;
+  float wexcl;
   __device__ __forceinline__ float operator()(float x, float y) const {
     const float ep = fast_exp2(__builtin_fmaf(x, kp, cp));
     if (!resid) return ep;
     const float eq = fast_exp2(__builtin_fmaf(y, kq, cq));
     return fmaxf(ep * isp - eq * isq, 0.f);
   }
+  // The weight of element e.
+  __device__ __forceinline__ float at(uint32_t e, float x, float y) const {
+    const float v = (*this)(x, y);
+    return static_cast<int>(e) == excl ? wexcl : v;
+  }
 };
+
+// The modified Cactus target mass on a drafted token ("Speculative Diffusion
+// is a Tale of Two Tradeoffs", App. E): the largest gamma in [p, 1] with
+//   Phi(gamma) = gamma log(gamma/p) + (1-gamma) log((1-gamma)/(1-p)) <= delta,
+// the Bernoulli KL of Eq. 17 (the KL of the modified target from p).  Solved
+// as the page does, by Newton's method, from the Taylor value of Eq. 18.
+// With x = gamma - p both logarithms are log1p terms, L1 = log1p(x/p) and
+// L2 = log1p(-x/(1-p)), shared by Phi = gamma L1 + (1-gamma) L2 and
+// Phi' = L1 - L2; float32 then loses accuracy in Phi only where Phi is of
+// order x^2, and the error that leaves in gamma is of order x times that
+// loss.  The iteration stops once the Newton step is below float32
+// resolution of gamma (it converges in at most 8 steps over p in
+// [1e-12, 1), delta in [1e-8, 40]); a step that would leave the bracket
+// [lo, hi] known around the root bisects instead.
+__device__ float cactus_gamma(float p, float delta) {
+  if (!(p > 0.f)) return 0.f;            // Phi = +inf for any gamma > 0
+  if (p >= 1.f) return 1.f;
+  if (!(delta > 0.f)) return p;          // delta = 0: the lossless target
+  if (-logf(p) <= delta) return 1.f;     // Phi(1) = -log p
+  const float xmax = 1.f - p;            // x lives in (0, 1 - p)
+  float lo = 0.f, hi = xmax;
+  float x = sqrtf(2.f * delta * p * xmax);
+  if (!(x < hi)) x = 0.5f * hi;
+  for (int it = 0; it < 40; ++it) {
+    const float g = p + x;
+    const float L1 = log1pf(x / p);
+    const float L2 = log1pf(-x / xmax);
+    const float f = g * L1 + (1.f - g) * L2 - delta;
+    if (f > 0.f) hi = x;
+    else lo = x;
+    const float step = f / (L1 - L2);
+    if (fabsf(step) <= 2e-7f * g) break;
+    float xn = x - step;
+    if (!(xn > lo && xn < hi)) xn = 0.5f * (lo + hi);
+    x = xn;
+  }
+  return fminf(p + x, 1.f);
+}
 
 constexpr int kTileBatch = 8;   // tiles a wave reads together (16 loads per lane)
 
@@ -251,10 +300,10 @@ __device__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo,
           E::unpack(rx[k], x);
           E::unpack(ry[k], y);
 #pragma unroll
-          for (int j = 0; j < W; ++j) m += w(x[j], y[j]);
+          for (int j = 0; j < W; ++j) m += w.at(e + j, x[j], y[j]);
         } else {
           for (int j = 0; j < W; ++j)
-            if (e + j < Vn) m += w(E::load1(xr, e + j), w.resid ? E::load1(yr, e + j) : 0.f);
+            if (e + j < Vn) m += w.at(e + j, E::load1(xr, e + j), w.resid ? E::load1(yr, e + j) : 0.f);
         }
 #pragma unroll
         for (int sh = 32; sh >= 1; sh >>= 1) m += wave_shfl_xor(m, sh);
@@ -302,6 +351,7 @@ template <int DT>
 __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   __shared__ float s_Mp[kMaxDraft + 1], s_Sp[kMaxDraft + 1];
   __shared__ float s_Mq[kMaxDraft], s_Sq[kMaxDraft];
+  __shared__ float s_p[kMaxDraft], s_pt[kMaxDraft], s_q[kMaxDraft];
   __shared__ int s_st, s_h;
   using E = Elem<DT>;
   const int b = blockIdx.x / a.chunks;
@@ -393,6 +443,8 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   }
 
   // ---- 2. acceptance tests: accept d_i iff u_i * q_i(d_i) < p~_i(d_i) ----
+  // Linear rule: p~(d) = (1 - lambda) p(d) + lambda q(d).  Cactus rule:
+  // p~(d) = gamma(p(d), delta).
 #pragma unroll
   for (int k = 0; k < kDraftsPerThread; ++k) {
     const int i = t + k * kBlock;
@@ -400,7 +452,10 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
     if (i < n) {
       p = fast_exp2(__builtin_fmaf(xi[k], a.kp, -s_Mp[i] * a.kp)) / s_Sp[i];
       q = fast_exp2(__builtin_fmaf(yi[k], a.kq, -s_Mq[i] * a.kq)) / s_Sq[i];
-      const float pt = (1.f - a.lam) * p + a.lam * q;
+      const float pt = a.rule == RULE_CACTUS ? cactus_gamma(p, a.delta) : (1.f - a.lam) * p + a.lam * q;
+      s_p[i] = p;
+      s_pt[i] = pt;
+      s_q[i] = q;
       if (q == 0.f && pt > 0.f) atomicOr(&s_st, SEQ_Q_ZERO);
       al = q > 0.f ? fminf(1.f, pt / q) : (pt > 0.f ? 1.f : 0.f);
       if (!(ui[k] * q < pt)) atomicMin(&s_h, i);
@@ -424,6 +479,18 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   w.kp = a.kp; w.cp = -s_Mp[h] * a.kp; w.isp = 1.f / s_Sp[h];
   w.kq = a.kq; w.cq = resid ? -s_Mq[h] * a.kq : 0.f; w.isq = resid ? 1.f / s_Sq[h] : 1.f;
   w.resid = resid ? 1 : 0;
+  w.excl = -1;
+  w.wexcl = 0.f;
+  if (resid && a.rule == RULE_CACTUS) {
+    // p~(v) = (1 - gamma) / (1 - p(d)) p(v) for v != d, p~(d) = gamma.
+    const float ph = s_p[h];
+    const float c_rest = ph < 1.f ? static_cast<float>((1.0 - static_cast<double>(s_pt[h])) /
+                                                       (1.0 - static_cast<double>(ph)))
+                                  : 0.f;
+    w.isp *= c_rest;
+    w.excl = d[h];
+    w.wexcl = fmaxf(s_pt[h] - s_q[h], 0.f);
+  }
   if (c == 0 && t == 0) {
     DrawRecord r;
     r.status = s_st;
@@ -432,6 +499,8 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
     r.cp = w.cp; r.isp = w.isp;
     r.cq = w.cq; r.isq = w.isq;
     r.u = a.u_resample[static_cast<int64_t>(b) * (a.K + 1) + h];
+    r.excl = w.excl;
+    r.wexcl = w.wexcl;
     a.rec[b] = r;
   }
 
@@ -485,6 +554,8 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
   w.kp = a.kp; w.cp = rec.cp; w.isp = rec.isp;
   w.kq = a.kq; w.cq = rec.cq; w.isq = rec.isq;
   w.resid = rec.resid;
+  w.excl = rec.excl;
+  w.wexcl = rec.wexcl;
   constexpr int TE = 64 * E::kVec;                              // elements per tile
 
   // Thread t holds the masses of tiles [t*q, (t+1)*q); an exclusive scan
@@ -531,6 +602,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
     // arithmetic.)
     status |= SEQ_Z_ZERO;
     w.resid = 0;
+    w.excl = -1;
     yr = xr;
     const bool vec = (reinterpret_cast<uintptr_t>(xr) & 15u) == 0;
     tile_masses<DT, kDrawWaves>(xr, yr, a.V, 0, ntiles, vec, w, s_tile);
@@ -556,7 +628,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
 #pragma unroll
     for (int j = 0; j < E::kVec; ++j) {
       const int64_t e = e0 + j;
-      wt[j] = e < a.V ? w(E::load1(xr, e), w.resid ? E::load1(yr, e) : 0.f) : 0.f;
+      wt[j] = e < a.V ? w.at(static_cast<uint32_t>(e), E::load1(xr, e), w.resid ? E::load1(yr, e) : 0.f) : 0.f;
       loc += wt[j];
     }
     float inc = loc;

@@ -8,7 +8,8 @@
  * acceptance test (greedy argmax match, lossless rejection min(1, p/q), the
  * linear lenient rule, or shared-Gumbel state equality over a draft tree),
  * finds the longest accepted prefix (or tree path) and draws the correction
- * or bonus token from supplied uniforms.
+ * or bonus token from supplied uniforms.  verify_cactus adds the modified
+ * Cactus acceptance rule.
  *
  * Sources (pages by title):
  *   [PSS]  "One Call Ahead: Packed Self-Speculative Decoding with Diffusion
@@ -18,7 +19,8 @@
  *          Models via Commit-Order Prediction" -- Sec. 4.1, Sec. 4.3,
  *          App. A.1 (formal decoding model), App. A.3 (Eq. 5-7).
  *   [TT]   "Speculative Diffusion is a Tale of Two Tradeoffs" -- Sec. 2
- *          (Eq. 1-5, Theorem 1), Sec. 3.2 (Algorithm 1).
+ *          (Eq. 1-5, Theorem 1), Sec. 3.2 (Algorithm 1), App. E (modified
+ *          Cactus, Eq. 17-18).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -87,7 +89,7 @@ enum {
 /* Workspace kinds for verify_workspace_size. */
 typedef enum {
   DBV_KIND_GREEDY = 0,
-  DBV_KIND_REJECTION = 1, /* also verify_lenient */
+  DBV_KIND_REJECTION = 1, /* also verify_lenient and verify_cactus */
   DBV_KIND_TREE = 2
 } dbv_kind;
 
@@ -173,6 +175,31 @@ dbv_status verify_lenient(int B, int K, int V, dbv_dtype dtype,
                           int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
                           float* p_draft, float* q_draft, float* alpha, float* residual_mass,
                           int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * verify_cactus -- the modified Cactus rule of [TT] App. E: the target is
+ * modified after the drafted token d is seen, to the p~ with the largest
+ * p~(d) = gamma whose KL divergence from p stays within the budget `delta`,
+ * every other token rescaled by (1 - gamma) / (1 - p(d)).  gamma solves
+ *   gamma log(gamma / p(d)) + (1 - gamma) log((1 - gamma) / (1 - p(d))) = delta
+ * ([TT] App. E, Eq. 17) exactly (Newton's method, as the page does), or is 1
+ * when -log p(d) <= delta, or 0 when p(d) = 0.  Accept d iff
+ * u_accept < min(1, gamma / q(d)); a rejected position draws from
+ * normalize([p~ - q]_+); the bonus after full acceptance is drawn from p.
+ * delta >= 0 and finite (DBV_ERR_INVALID_ARG otherwise); delta = 0 is the
+ * lossless rule.  alpha reports min(1, gamma / q(d)); residual_mass the sum of
+ * [p~ - q]_+ at the rejected row.  All other arguments as verify_rejection.
+ */
+dbv_status verify_cactus(int B, int K, int V, dbv_dtype dtype,
+                         const void* tgt, int64_t tgt_seq_stride, int64_t tgt_row_stride,
+                         const void* drf, int64_t drf_seq_stride, int64_t drf_row_stride,
+                         const int32_t* draft_tokens, const int32_t* draft_len,
+                         float temperature_target, float temperature_draft, float delta,
+                         const float* u_accept, const float* u_resample,
+                         int32_t eos_id, const int32_t* len_budget,
+                         int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
+                         float* p_draft, float* q_draft, float* alpha, float* residual_mass,
+                         int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * verify_gumbel_tree -- state-equality verification of one draft tree per

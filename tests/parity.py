@@ -44,8 +44,9 @@ def check_greedy(g, o):
 
 
 def check_sampling(g, x, o, lam, t_target, t_draft, dtype_name, eos_id=-1, len_budget=None,
-                   seqs=None):
-    """Rejection / lenient outputs against the oracle with margin accounting.
+                   seqs=None, delta=None):
+    """Rejection / lenient / Cactus (``delta`` set) outputs against the oracle
+    with margin accounting.
 
     g: GPU outputs (torch or numpy); x: the inputs as float64 numpy
     (tgt, drf, draft_tokens, draft_len, u_accept, u_resample); o: oracle
@@ -93,7 +94,10 @@ def check_sampling(g, x, o, lam, t_target, t_draft, dtype_name, eos_id=-1, len_b
         p = oracle.tempered_softmax(x["tgt"][b, h], t_target)
         if h < n:
             q = oracle.tempered_softmax(x["drf"][b, h], t_draft)
-            w = oracle.residual_weights(p, q, lam)
+            if delta is None:
+                w = oracle.residual_weights(p, q, lam)
+            else:
+                w = oracle.cactus_residual(p, q, d[h], oracle.cactus_gamma(p[d[h]], delta))
             Zr = float(np.sum(w))
             if Zr <= 0.0:
                 w = p

@@ -75,9 +75,9 @@ def _greedy(lib, **kw):
                              a["wsb"], a["stream"])
 
 
-def _reject(lib, lenient=False, **kw):
+def _reject(lib, lenient=False, cactus=False, **kw):
     a = dict(B=2, K=3, V=100, dt=_lib.DBV_BF16, tgt=FAKE, ts=400, tr=100, drf=FAKE, ds=300,
-             dr=100, d=FAKE, n=None, tt=1.0, td=1.0, lam=0.5, ua=FAKE, ur=FAKE, eos=-1, bud=None,
+             dr=100, d=FAKE, n=None, tt=1.0, td=1.0, lam=0.5, delta=1.0, ua=FAKE, ur=FAKE, eos=-1, bud=None,
              acc=FAKE, out=FAKE, num=FAKE, pd=None, qd=None, al=None, rm=None, st=FAKE, ws=FAKE,
              wsb=1 << 20, stream=None)
     a.update(kw)
@@ -87,6 +87,8 @@ def _reject(lib, lenient=False, **kw):
             a["al"], a["rm"], a["st"], a["ws"], a["wsb"], a["stream"]]
     if lenient:
         return lib.verify_lenient(*(head + [a["lam"]] + tail))
+    if cactus:
+        return lib.verify_cactus(*(head + [a["delta"]] + tail))
     return lib.verify_rejection(*(head + tail))
 
 
@@ -121,11 +123,17 @@ def test_greedy_rejects_bad_args(lib, kw):
 def test_rejection_rejects_bad_args(lib, kw):
     assert _reject(lib, **kw) == INVALID
     assert _reject(lib, lenient=True, **kw) == INVALID
+    assert _reject(lib, cactus=True, **kw) == INVALID
 
 
 @pytest.mark.parametrize("lam", [-0.01, 1.01, float("nan")])
 def test_lenient_rejects_bad_lambda(lib, lam):
     assert _reject(lib, lenient=True, lam=lam) == INVALID
+
+
+@pytest.mark.parametrize("delta", [-0.01, float("nan"), float("inf")])
+def test_cactus_rejects_bad_budget(lib, delta):
+    assert _reject(lib, cactus=True, delta=delta) == INVALID
 
 
 @pytest.mark.parametrize("kw", [
@@ -163,6 +171,7 @@ def test_valid_call_without_gpu_reports_no_device(lib):
     assert _greedy(lib) == _lib.DBV_ERR_NO_DEVICE
     assert _reject(lib) == _lib.DBV_ERR_NO_DEVICE
     assert _reject(lib, lenient=True) == _lib.DBV_ERR_NO_DEVICE
+    assert _reject(lib, cactus=True, delta=0.0) == _lib.DBV_ERR_NO_DEVICE
     assert _tree(lib) == _lib.DBV_ERR_NO_DEVICE
 
 

@@ -12,6 +12,10 @@ that hold at any size:
     oracle on 4 sequences per setting; on all 32: lambda = 0 equals the
     lossless entry point bit for bit, lambda = 1 accepts every draft, and the
     accepted length does not fall as lambda rises (common uniforms)
+  * Cactus sweep            the same shape, sigma = 1, T = 1, budgets
+    delta in {0, 0.25, 1, 4, 16} -- oracle on 4 sequences per budget; on all
+    32: delta = 0 equals the lossless entry point, and the accepted length
+    does not fall as delta rises
   * Gumbel tree verify      B=16 S=64 L=32 V=151936 bf16 -- oracle on 3
     trees; on all 16 the walk is redone from the GPU's per-state choices
   * packed greedy           B=64 K=31 W=32 V=131072 bf16 -- oracle on every
@@ -127,6 +131,40 @@ def test_full_lenient_sweep(dev, sigma, T):
                 check_sampling(_take(res, bad), xb, ob, lam, T, T, "bfloat16")
         h_prev = h
         say(f"lambda={lam} mean accept length {h.mean():.3f} (sampled near-margin {dict(near)})")
+
+
+C3_DELTAS = (0.25, 1.0, 4.0, 16.0)
+
+
+def test_full_cactus_sweep(dev):
+    say("full Cactus B=32 K=16 V=128256 bf16 sigma 1 T 1")
+    x = workloads.config3(1.0, 1.0)
+    B = x["tgt"].shape[0]
+    seqs = _sample(B, 4, 77)
+    xs = _chain_np(x, seqs)
+    args = (x["tgt"].to(dev), x["drf"].to(dev), x["draft_tokens"].to(dev), x["u_accept"].to(dev),
+            x["u_resample"].to(dev))
+    common = dict(draft_len=x["draft_len"].to(dev))
+    lossless = dbv.verify_rejection(*args, **common)
+    h_prev = None
+    for delta in (0.0,) + C3_DELTAS:
+        res = dbv.verify_cactus(*args, delta, **common)
+        if delta == 0.0:
+            for k in lossless:
+                assert torch.equal(lossless[k], res[k]), k
+        h = npi(res["accept_len"])
+        o = oracle.verify_cactus(xs["tgt"], xs["drf"], xs["draft_tokens"], xs["draft_len"], 1.0, 1.0, delta,
+                                 xs["u_accept"], xs["u_resample"])
+        near = check_sampling(_take(res, seqs), xs, o, 0.0, 1.0, 1.0, "bfloat16", delta=delta)
+        if h_prev is not None:
+            bad = [b for b in range(B) if h[b] < h_prev[b]]
+            if bad:
+                xb = _chain_np(x, bad)
+                ob = oracle.verify_cactus(xb["tgt"], xb["drf"], xb["draft_tokens"], xb["draft_len"], 1.0, 1.0,
+                                          delta, xb["u_accept"], xb["u_resample"])
+                check_sampling(_take(res, bad), xb, ob, 0.0, 1.0, 1.0, "bfloat16", delta=delta)
+        h_prev = h
+        say(f"delta={delta} mean accept length {h.mean():.3f} (sampled near-margin {dict(near)})")
 
 
 # ------------------------------------------------------------------ tree ---

@@ -147,6 +147,55 @@ def test_sampling_stopping_rule(dev):
     check_sampling(res, xn, o, 0.0, 1.0, 1.0, "float32", eos_id=eos, len_budget=npi(bud))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("delta", [0.0, 0.25, 2.0, 12.0])
+def test_cactus_parity(dev, dtype, delta):
+    say("cactus", dtype, delta)
+    x = workloads.chain_inputs(87, 8, 6, 12345, dtype, sigma=1.5, temperature=1.0, random_lengths=True)
+    res = dbv.verify_cactus(x["tgt"].to(dev), x["drf"].to(dev), x["draft_tokens"].to(dev),
+                            x["u_accept"].to(dev), x["u_resample"].to(dev), delta,
+                            draft_len=x["draft_len"].to(dev), temperature_target=1.0, temperature_draft=0.9)
+    xn = _np_inputs(x)
+    o = oracle.verify_cactus(xn["tgt"], xn["drf"], xn["draft_tokens"], xn["draft_len"], 1.0, 0.9, delta,
+                             xn["u_accept"], xn["u_resample"])
+    near = check_sampling(res, xn, o, 0.0, 1.0, 0.9, str(dtype).split(".")[1], delta=delta)
+    say("near-margin", dict(near), "h", list(o["accept_len"]))
+
+
+def test_cactus_zero_budget_is_rejection(dev):
+    say("cactus 0 == rejection")
+    x = _to(workloads.chain_inputs(88, 8, 9, 30011, torch.bfloat16, sigma=1.0, random_lengths=True), dev)
+    a = dbv.verify_rejection(x["tgt"], x["drf"], x["draft_tokens"], x["u_accept"], x["u_resample"],
+                             draft_len=x["draft_len"])
+    b = dbv.verify_cactus(x["tgt"], x["drf"], x["draft_tokens"], x["u_accept"], x["u_resample"], 0.0,
+                          draft_len=x["draft_len"])
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_cactus_edge_cases(dev):
+    # p(d) = 0 (its logit is -inf): gamma = 0, always rejected; the stopping
+    # rule; a bad draft token; an empty draft.
+    say("cactus edge cases")
+    B, K, V = 6, 4, 3001
+    x = workloads.chain_inputs(89, B, K, V, torch.float32, sigma=1.0)
+    tgt, d = x["tgt"].clone(), x["draft_tokens"].clone()
+    n = torch.full((B,), K, dtype=torch.int32)
+    tgt[0, 0, int(d[0, 0])] = float("-inf")
+    d[1, 1] = -3
+    n[2] = 0
+    eos = int(d[3, 0])
+    bud = torch.tensor([9, 9, 9, 9, 2, 0], dtype=torch.int32)
+    xd = dict(x, tgt=tgt, draft_tokens=d, draft_len=n)
+    res = dbv.verify_cactus(tgt.to(dev), x["drf"].to(dev), d.to(dev), x["u_accept"].to(dev),
+                            x["u_resample"].to(dev), 3.0, draft_len=n.to(dev), eos_id=eos, len_budget=bud.to(dev))
+    xn = _np_inputs(xd)
+    o = oracle.verify_cactus(xn["tgt"], xn["drf"], xn["draft_tokens"], xn["draft_len"], 1.0, 1.0, 3.0,
+                             xn["u_accept"], xn["u_resample"], eos_id=eos, len_budget=npi(bud))
+    assert o["accept_len"][0] == 0 and o["status"][1] == oracle.STATUS_BAD_INPUT
+    check_sampling(res, xn, o, 0.0, 1.0, 1.0, "float32", eos_id=eos, len_budget=npi(bud), delta=3.0)
+
+
 # -------------------------------------------------------------- edge cases ---
 
 def test_chain_edge_cases(dev):
