@@ -16,13 +16,17 @@ following the pages' definitions in their own order:
   with the stopping rule and next-draft retention.
 * ``cactus`` -- the modified Cactus budget: gamma from the Bernoulli KL
   budget, the modified target p~ and its residual.
+* ``anyorder`` -- one any-order greedy verification call (Packed-SS App. C,
+  Algorithm 3): a chosen order over the active positions, missing drafts,
+  the ending position and retention by position.
 * ``tree``   -- coupled shared-Gumbel state-equality verification of a draft
   tree (and its T=0 greedy special case).
 
 Sources (pages by title):
 * "One Call Ahead: Packed Self-Speculative Decoding with Diffusion Drafting"
   (Packed-SS): Sec. 2.2, Sec. 3.1 Eq. 1-4 and Algorithm 1, Sec. 3.2,
-  App. B.2 Algorithm 2 and Lemma B.3, App. D.1.
+  App. B.2 Algorithm 2 and Lemma B.3, App. C Algorithm 3 and Prop. C.1,
+  App. D.1.
 * "On the SPOT: Enhancing Speculative Decoding for Diffusion Language Models
   via Commit-Order Prediction" (SPOT): Sec. 4.1, Sec. 4.3, App. A.1, A.3
   Eq. 5-7, App. B Eq. 10-14.
@@ -41,6 +45,7 @@ from .chain import verify_greedy, verify_rejection, verify_lenient, verify_cactu
 from .cactus import (  # noqa: F401
     cactus_divergence, cactus_gamma, cactus_target, cactus_acceptance, cactus_residual,
 )
+from .anyorder import NO_END, verify_greedy_any_order  # noqa: F401
 from .tree import (  # noqa: F401
     TREE_STATE_EQUALITY, TREE_FIXED_POSITION, state_transition, walk,
     verify_gumbel_tree,

@@ -157,3 +157,51 @@ def test_pin_catches_walk_not_following_child(monkeypatch):
     monkeypatch.setattr(oracle, "verify_gumbel_tree", stops_at_root)
     with pytest.raises(AssertionError):
         tp.test_orbit_tree_is_accepted_to_full_depth(T=1.0)
+
+
+# ------------------------------------------------- any-order verification ---
+
+import tests.test_oracle_anyorder_pins as ap  # noqa: E402
+import oracle.anyorder as anyorder  # noqa: E402
+
+
+def _ao_ignores_order(tgt, order, num_active, positions, draft_tokens, draft_rows=None, eos_id=-1,
+                      end_pos=None):
+    ident = np.tile(np.arange(np.asarray(order).shape[1]), (np.asarray(order).shape[0], 1))
+    return anyorder.verify_greedy_any_order(tgt, ident, num_active, positions, draft_tokens, draft_rows,
+                                            eos_id, end_pos)
+
+
+def _ao_eos_truncates_by_rank(tgt, order, num_active, positions, draft_tokens, draft_rows=None, eos_id=-1,
+                              end_pos=None):
+    out = anyorder.verify_greedy_any_order(tgt, order, num_active, positions, draft_tokens, draft_rows,
+                                           -1, end_pos)
+    if eos_id >= 0:
+        for b in range(out["acc_tok"].shape[0]):
+            toks = out["acc_tok"][b].tolist()
+            if eos_id in toks:
+                k = toks.index(eos_id) + 1
+                out["acc_tok"][b, k:] = -1
+                out["acc_pos"][b, k:] = -1
+                out["num_accepted"][b] = min(out["num_accepted"][b], k)
+    return out
+
+
+def _ao_keeps_beyond_end(tgt, order, num_active, positions, draft_tokens, draft_rows=None, eos_id=-1,
+                         end_pos=None):
+    out = anyorder.verify_greedy_any_order(tgt, order, num_active, positions, draft_tokens, draft_rows,
+                                           eos_id, end_pos)
+    free = anyorder.verify_greedy_any_order(tgt, order, num_active, positions, draft_tokens, draft_rows)
+    out["next_draft"] = free["next_draft"]
+    return out
+
+
+@pytest.mark.parametrize("fn,pin", [
+    (_ao_ignores_order, ap.test_serial_reference_of_proposition_c1),
+    (_ao_eos_truncates_by_rank, ap.test_worked_example_order_end_and_retention),
+    (_ao_keeps_beyond_end, ap.test_worked_example_order_end_and_retention),
+], ids=["ignores-order", "eos-by-rank", "keeps-beyond-end"])
+def test_any_order_pin_catches_planted_mistake(monkeypatch, fn, pin):
+    monkeypatch.setattr(oracle, "verify_greedy_any_order", fn)
+    with pytest.raises(AssertionError):
+        pin()
