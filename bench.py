@@ -13,6 +13,8 @@ and the correction or bonus draw.  Workloads (sizes of the pages' setups):
   c4  coupled-Gumbel tree verify  B=16 S=64 L=32 V=151936 bf16
   c5  packed greedy verify+draft  B=64 K=32 V=131072 bf16
   c3c modified-Cactus verify      B=32 K=16 V=128256 bf16, sigma=1, T=1, delta=1
+  c5ao any-order greedy verify    B=64 U=32 V=131072 bf16 (verifier rows by rank,
+                                  drafter rows by slot)
 
 Inputs smaller than 1 GiB are replicated into several buffer sets and the
 steps rotate over them, so the 256 MiB last-level cache cannot serve them.
@@ -48,6 +50,7 @@ DESCR = {
     "c4": "coupled-Gumbel tree verify B=16 S=64 L=32 V=151936 bf16",
     "c5": "packed greedy verify+draft B=64 K=32 V=131072 bf16",
     "c3c": "modified-Cactus verify B=32 K=16 V=128256 bf16 sigma=1 T=1 delta=1",
+    "c5ao": "any-order greedy verify B=64 U=32 V=131072 bf16",
 }
 CACTUS_DELTA = 1.0
 
@@ -157,6 +160,24 @@ class Case:
                 self.calls.append(dbv.verify_greedy(p[:, :K + 1], x["draft_tokens"].to(dev),
                                                     x["draft_len"].to(dev), p[:, K + 1:], prepare=True))
             self.shape = dict(B=B, K=K, W=W, V=V)
+        elif name == "c5ao":
+            x = workloads.config5_any_order()
+            B, U, V = x["tgt"].shape
+            u = x["num_active"].long()
+            kappa = self._kappa(x)
+            nver = torch.minimum(kappa + 1, u)
+            self.positions = int(kappa.sum())                            # drafted positions checked
+            self.kernel_bytes = int(((nver + u) * V * eb).sum())         # verifier rows read + drafter rows
+            self.kernel = "k_ao_rows"
+            per_set = (x["tgt"].numel() + x["draft_rows"].numel()) * eb
+            self.cpu_inputs = x
+            self.calls = []
+            for _ in range(self._rotation(per_set)):
+                xd = {k: v.to(dev).clone() for k, v in x.items()}
+                self.calls.append(dbv.verify_greedy_any_order(
+                    xd["tgt"], xd["order"], xd["draft_tokens"], num_active=xd["num_active"],
+                    positions=xd["positions"], draft_rows=xd["draft_rows"], prepare=True))
+            self.shape = dict(B=B, U=U, V=V)
         else:  # c4
             x = workloads.config4(device=dev)
             B, S, L, V = x["logits"].shape
@@ -176,6 +197,15 @@ class Case:
             per_set = x["logits"].numel() * eb + x["gumbel"].numel() * 4
         self.rotation = len(self.calls)
         self.bytes_per_set = per_set
+
+    @staticmethod
+    def _kappa(x):
+        """Leading ranks whose slot holds a draft, per sequence (host-side
+        count of the positions a call verifies)."""
+        d = torch.gather(x["draft_tokens"].long(), 1, x["order"].long())
+        r = torch.arange(d.shape[1])[None, :]
+        have = (d >= 0) & (r < x["num_active"].long()[:, None])
+        return torch.cumprod(have.long(), dim=1).sum(dim=1)
 
     @staticmethod
     def _rotation(per_set):
@@ -218,6 +248,19 @@ class Case:
             while True:
                 oracle.verify_greedy(tgt, d, n, dr)
                 done_pos += int(n.sum())
+                calls += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            sample = f"{nb} of 64 sequences, {calls} oracle calls"
+        elif self.name == "c5ao":
+            nb = 4
+            args = (np64(x["tgt"][:nb]), npi(x["order"][:nb]), npi(x["num_active"][:nb]),
+                    npi(x["positions"][:nb]), npi(x["draft_tokens"][:nb]), np64(x["draft_rows"][:nb]))
+            kap = int(self._kappa({k: v[:nb] for k, v in x.items()}).sum())
+            t0 = time.perf_counter()
+            while True:
+                oracle.verify_greedy_any_order(*args)
+                done_pos += kap
                 calls += 1
                 if time.perf_counter() - t0 >= seconds:
                     break

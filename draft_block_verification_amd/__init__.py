@@ -7,7 +7,7 @@ the verification runs in the library's HIP kernels; there is no fallback.
 
 Entry points (same names as the C ABI):
   verify_greedy, verify_rejection, verify_lenient, verify_cactus,
-  verify_gumbel_tree
+  verify_greedy_any_order, verify_gumbel_tree
 """
 
 import torch
@@ -20,8 +20,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_gumbel_tree",
-    "workspace_size", "DBVError", "Prepared",
+    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus",
+    "verify_greedy_any_order", "verify_gumbel_tree", "workspace_size", "DBVError", "Prepared",
 ]
 
 
@@ -225,6 +225,52 @@ def verify_cactus(tgt, drf, draft_tokens, u_accept, u_resample, delta, draft_len
     return _sampling("verify_cactus", tgt, drf, draft_tokens, draft_len,
                      temperature_target, temperature_draft, delta, u_accept, u_resample,
                      eos_id, len_budget, workspace, diagnostics, prepare)
+
+
+def verify_greedy_any_order(tgt, order, draft_tokens, num_active=None, positions=None,
+                            draft_rows=None, eos_id=-1, end_pos=None, workspace=None, prepare=False):
+    """One any-order greedy verification call (Packed-SS, App. C, Algorithm 3).
+
+    tgt [B, U, V] verifier rows in rank order; order [B, U] (slot checked at
+    rank r); draft_tokens [B, U] by slot (-1 = missing); num_active [B] or
+    None; positions [B, U] or None; draft_rows [B, U, V] by slot or None;
+    end_pos [B] or None.  Returns accept_len, num_accepted, acc_pos, acc_tok,
+    new_end, next_draft, status (int32).
+    """
+    lib = _lib.load()
+    dev = tgt.device
+    B, U, V = tgt.shape
+    ts, tr = _rows3(tgt, "tgt")
+    dt = _dtype_code(tgt)
+    ds = drs = 0
+    if draft_rows is not None:
+        if draft_rows.dtype != tgt.dtype or tuple(draft_rows.shape) != (B, U, V):
+            raise ValueError("draft_rows must be [B, U, V] with the dtype of tgt")
+        ds, drs = _rows3(draft_rows, "draft_rows")
+    o = _i32(order, (B, U), "order", dev)
+    d = _i32(draft_tokens, (B, U), "draft_tokens", dev)
+    na = _i32(num_active, (B,), "num_active", dev)
+    ps = _i32(positions, (B, U), "positions", dev)
+    ep = _i32(end_pos, (B,), "end_pos", dev)
+    out = {
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "num_accepted": torch.empty(B, dtype=torch.int32, device=dev),
+        "acc_pos": torch.empty(B, U, dtype=torch.int32, device=dev),
+        "acc_tok": torch.empty(B, U, dtype=torch.int32, device=dev),
+        "new_end": torch.empty(B, dtype=torch.int32, device=dev),
+        "next_draft": torch.empty(B, U, dtype=torch.int32, device=dev),
+        "status": torch.empty(B, dtype=torch.int32, device=dev),
+    }
+    need = workspace_size(_lib.DBV_KIND_ANY_ORDER, B, U, 0, V, dt)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    args = (B, U, V, dt, tgt.data_ptr(), ts, tr, _ptr(o), _ptr(na), _ptr(ps), _ptr(d),
+            _ptr(draft_rows), ds, drs, int(eos_id), _ptr(ep),
+            out["accept_len"].data_ptr(), out["num_accepted"].data_ptr(), out["acc_pos"].data_ptr(),
+            out["acc_tok"].data_ptr(), out["new_end"].data_ptr(), out["next_draft"].data_ptr(),
+            out["status"].data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+    call = Prepared(lib.verify_greedy_any_order, "verify_greedy_any_order", args, out,
+                    (tgt, draft_rows, o, d, na, ps, ep, ws))
+    return call if prepare else call()
 
 
 def verify_gumbel_tree(logits, parent, edge_pos, edge_tok, masked=None, gumbel=None,

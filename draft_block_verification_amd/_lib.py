@@ -22,6 +22,7 @@ DBV_TREE_FIXED_POSITION = 1
 DBV_KIND_GREEDY = 0
 DBV_KIND_REJECTION = 1
 DBV_KIND_TREE = 2
+DBV_KIND_ANY_ORDER = 3
 
 SEQ_BAD_INPUT = 1
 SEQ_NONFINITE = 2
@@ -31,8 +32,8 @@ SEQ_Z_ZERO = 16
 SEQ_ERROR_MASK = 7
 
 EXPORTS = (
-    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_gumbel_tree",
-    "verify_workspace_size", "verify_status_string", "verify_abi_version",
+    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_greedy_any_order",
+    "verify_gumbel_tree", "verify_workspace_size", "verify_status_string", "verify_abi_version",
     "verify_set_timing_events",
 )
 
@@ -52,6 +53,8 @@ _SIGS = {
                        _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "verify_cactus": [_i, _i, _i, _i, _p, _i64, _i64, _p, _i64, _i64, _p, _p, _f, _f, _f, _p, _p,
                       _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
+    "verify_greedy_any_order": [_i, _i, _i, _i, _p, _i64, _i64, _p, _p, _p, _p, _p, _i64, _i64, _i32, _p,
+                                _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "verify_gumbel_tree": [_i, _i, _i, _i, _i, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p,
                            _i64, _i64, _f, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "verify_workspace_size": [_i, _i, _i, _i, _i, _i],

@@ -228,6 +228,50 @@ dbv_status verify_cactus(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
                        out_tokens, num_out, p_draft, q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
 }
 
+dbv_status verify_greedy_any_order(int B, int U, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
+                                   int64_t tgt_row_stride, const int32_t* order, const int32_t* num_active,
+                                   const int32_t* positions, const int32_t* draft_tokens, const void* draft_rows,
+                                   int64_t dr_seq_stride, int64_t dr_row_stride, int32_t eos_id,
+                                   const int32_t* end_pos, int32_t* accept_len, int32_t* num_accepted,
+                                   int32_t* acc_pos, int32_t* acc_tok, int32_t* new_end, int32_t* next_draft,
+                                   int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || U < 0 || U > kMaxDraft || V < 1 || !dtype_ok(dtype)) return DBV_ERR_INVALID_ARG;
+  if (tgt_seq_stride < 0 || tgt_row_stride < 0 || dr_seq_stride < 0 || dr_row_stride < 0)
+    return DBV_ERR_INVALID_ARG;
+  if (tgt == nullptr || (U > 0 && (order == nullptr || draft_tokens == nullptr))) return DBV_ERR_INVALID_ARG;
+  if (accept_len == nullptr || num_accepted == nullptr || acc_pos == nullptr || acc_tok == nullptr ||
+      new_end == nullptr)
+    return DBV_ERR_INVALID_ARG;
+  const size_t eb = elem_bytes(dtype);
+  if (!aligned(tgt, eb) || (draft_rows && !aligned(draft_rows, eb))) return DBV_ERR_INVALID_ARG;
+  const dbv::AnyOrderPlan plan = dbv::plan_any_order(B, U);
+  if (!stream_fits(plan.max_rows, V)) return DBV_ERR_UNSUPPORTED;
+  dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
+  if (s != DBV_OK) return s;
+  if ((s = device_ready()) != DBV_OK) return s;
+  if (B == 0) return DBV_OK;
+
+  dbv::AnyOrderArgs a{};
+  a.B = B; a.U = U; a.V = V;
+  a.tgt = tgt; a.ts = tgt_seq_stride; a.tr = tgt_row_stride;
+  a.dr = draft_rows; a.ds = dr_seq_stride; a.drr = dr_row_stride;
+  a.order = order; a.num_active = num_active; a.positions = positions; a.draft_tokens = draft_tokens;
+  a.eos = eos_id; a.end_pos = end_pos;
+  a.accept_len = accept_len; a.num_accepted = num_accepted; a.acc_pos = acc_pos; a.acc_tok = acc_tok;
+  a.new_end = new_end; a.next_draft = next_draft; a.status = status;
+  char* w = static_cast<char*>(ws);
+  a.part = reinterpret_cast<float2*>(w + plan.off_part);
+  a.pre = reinterpret_cast<int32_t*>(w + plan.off_pre);
+  int32_t* seq = reinterpret_cast<int32_t*>(w + plan.off_seq);
+  a.rows = seq;
+  a.nver = seq + B;
+  a.kappa = seq + 2 * static_cast<int64_t>(B);
+  a.pstat = seq + 3 * static_cast<int64_t>(B);
+  a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(eb), dbv::resident_groups());
+  return dbv::launch_any_order(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK
+                                                                                           : DBV_ERR_LAUNCH;
+}
+
 dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const void* logits, int64_t seq_stride,
                               int64_t state_stride, int64_t pos_stride, const uint8_t* masked,
                               const int32_t* parent, const int32_t* edge_pos, const int32_t* edge_tok,
@@ -294,6 +338,9 @@ size_t verify_workspace_size(dbv_kind kind, int B, int K_or_S, int L, int V, dbv
     case DBV_KIND_TREE:
       if (K_or_S < 1 || K_or_S > kMaxStates || L < 1 || L > kMaxBlockLen) return 0;
       return dbv::plan_tree(B, K_or_S, L, V).bytes;
+    case DBV_KIND_ANY_ORDER:
+      if (K_or_S < 0 || K_or_S > kMaxDraft) return 0;
+      return dbv::plan_any_order(B, K_or_S).bytes;
   }
   return 0;
 }

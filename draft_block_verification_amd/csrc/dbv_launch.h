@@ -53,6 +53,27 @@ struct SampleArgs {
   int chunks;                          // mass-kernel groups per sequence
 };
 
+struct AnyOrderArgs {
+  int B, U, V;
+  const void* tgt; int64_t ts, tr;     // verifier rows by rank
+  const void* dr; int64_t ds, drr;     // drafter rows by slot (NULL: none)
+  const int32_t* order;                // [B, U] slot checked at rank r
+  const int32_t* num_active;           // [B] u_b (NULL: U)
+  const int32_t* positions;            // [B, U] output position of slot j (NULL: j)
+  const int32_t* draft_tokens;         // [B, U] by slot, -1 = missing
+  int32_t eos;
+  const int32_t* end_pos;              // [B] E (NULL: no limit)
+  int32_t* accept_len; int32_t* num_accepted; int32_t* acc_pos; int32_t* acc_tok;
+  int32_t* new_end; int32_t* next_draft; int32_t* status;
+  float2* part;                        // per (slot, wave)
+  int32_t* pre;                        // [B + 1] first stream row per sequence
+  int32_t* rows;                       // [B] stream rows of the sequence
+  int32_t* nver;                       // [B] verifier rows read
+  int32_t* kappa;                      // [B]
+  int32_t* pstat;                      // [B] status bits found by the plan
+  int64_t grid;                        // groups of the row-streaming launch
+};
+
 struct TreeArgs {
   int B, S, L, V;
   const void* logits; int64_t ss, sy, sp;   // sequence, state, position strides
@@ -111,5 +132,6 @@ int64_t resident_groups();
 bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
 bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
 bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
+bool launch_any_order(const AnyOrderArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
 
 }  // namespace dbv

@@ -161,6 +161,27 @@ inline GreedyPlan plan_greedy(int B, int K, int W, int V) {
   return p;
 }
 
+// ------------------------------------------------------------- any-order ---
+// Stream order: for each sequence b, its verifier rows by rank 0..nver_b-1
+// (nver_b = min(kappa_b + 1, u_b)), then its drafter rows by slot 0..u_b-1.
+struct AnyOrderPlan {
+  int64_t max_rows;   // B * 2U
+  size_t off_part;    // float2 {value, index-as-bits} per (slot, wave)
+  size_t off_pre;     // int32 [B + 1]: first stream row of each sequence
+  size_t off_seq;     // int32 [4][B]: rows, nver, kappa, status per sequence
+  size_t bytes;
+};
+
+inline AnyOrderPlan plan_any_order(int B, int U) {
+  AnyOrderPlan p{};
+  p.max_rows = static_cast<int64_t>(B) * 2 * U;
+  p.off_part = 0;
+  p.off_pre = partial_bytes(p.max_rows);
+  p.off_seq = p.off_pre + align256(static_cast<size_t>(B + 1) * 4);
+  p.bytes = p.off_seq + align256(static_cast<size_t>(B) * 4 * 4);
+  return p;
+}
+
 // -------------------------------------------------------------- sampling ---
 // Per-sequence decision handed from the mass kernel to the select kernel
 // (written by the sequence's chunk-0 group).

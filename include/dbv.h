@@ -14,7 +14,8 @@
  * Sources (pages by title):
  *   [PSS]  "One Call Ahead: Packed Self-Speculative Decoding with Diffusion
  *          Drafting" -- Sec. 2.2, Sec. 3.1 (Eq. 1-4, Algorithm 1), Sec. 3.2,
- *          App. B.2 (Algorithm 2, Lemma B.3), App. D.1 (packed row layout).
+ *          App. B.2 (Algorithm 2, Lemma B.3), App. C (Algorithm 3, any-order
+ *          verification), App. D.1 (packed row layout).
  *   [SPOT] "On the SPOT: Enhancing Speculative Decoding for Diffusion Language
  *          Models via Commit-Order Prediction" -- Sec. 4.1, Sec. 4.3,
  *          App. A.1 (formal decoding model), App. A.3 (Eq. 5-7).
@@ -90,7 +91,8 @@ enum {
 typedef enum {
   DBV_KIND_GREEDY = 0,
   DBV_KIND_REJECTION = 1, /* also verify_lenient and verify_cactus */
-  DBV_KIND_TREE = 2
+  DBV_KIND_TREE = 2,
+  DBV_KIND_ANY_ORDER = 3  /* K_or_S = U (window), L ignored */
 } dbv_kind;
 
 /*
@@ -202,6 +204,51 @@ dbv_status verify_cactus(int B, int K, int V, dbv_dtype dtype,
                          int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * verify_greedy_any_order -- one any-order greedy verification call
+ * ([PSS] App. C, Algorithm 3, lines 6-15).  Per sequence b the call covers
+ * the u_b unresolved output positions of its active window, in textual order
+ * ("slots" j = 0..u_b-1 at output positions pos[j]), checked in the order
+ * pi chosen before the call (order[b, r] = the slot checked at rank r):
+ *   kappa = leading ranks whose slot has a draft (draft_tokens >= 0)
+ *   v_r   = argmax of verifier row r, r < min(kappa + 1, u)       (Eq. 8)
+ *   z_j   = argmax of drafter row j, j < u
+ *   h     = leading ranks r < kappa with draft(pi(r)) == v_r
+ *   A     = min(h + 1, u),  C = ((pos[pi(r)], v_r))_{r < A}
+ *   E'    = min({end_pos[b]} U {pos of an accepted EOS})
+ *   C'    = the pairs of C at positions <= E' (in rank order)
+ *   next draft: z_j at the slots not in C with pos[j] <= E'.
+ *
+ * tgt         [B, U, V] verifier rows in rank order (row r is the verifier at
+ *             pi(r) given the drafts at earlier ranks); rows at ranks >=
+ *             min(kappa + 1, u) are not read.
+ * order       [B, U] int32, a permutation of 0..u_b-1 in its first u_b entries.
+ * num_active  [B] u_b in [0, U] (NULL = U).
+ * positions   [B, U] strictly increasing over the first u_b slots (NULL:
+ *             slot j is at position j).
+ * draft_tokens[B, U] by slot, -1 = no draft yet, else in [0, V).
+ * draft_rows  [B, U, V] drafter rows by slot (NULL: no next draft; then
+ *             next_draft, if given, is filled with -1).
+ * eos_id      -1 disables the EOS term; end_pos [B] E before the call (NULL:
+ *             no limit, reported as INT32_MAX).
+ * Outputs: accept_len [B] (= h), num_accepted [B] (= |C'|), acc_pos, acc_tok
+ * [B, U] (C' in rank order, -1 after), new_end [B] (= E'), next_draft [B, U]
+ * (by slot, -1 where no draft is kept; NULL allowed), status [B] (NULL
+ * allowed).  An order that is not a permutation, positions that do not
+ * increase, a draft token outside [-1, V) or u_b outside [0, U] is
+ * DBV_SEQ_BAD_INPUT; no row of that sequence is read.
+ */
+dbv_status verify_greedy_any_order(int B, int U, int V, dbv_dtype dtype,
+                                   const void* tgt, int64_t tgt_seq_stride, int64_t tgt_row_stride,
+                                   const int32_t* order, const int32_t* num_active,
+                                   const int32_t* positions, const int32_t* draft_tokens,
+                                   const void* draft_rows, int64_t dr_seq_stride, int64_t dr_row_stride,
+                                   int32_t eos_id, const int32_t* end_pos,
+                                   int32_t* accept_len, int32_t* num_accepted,
+                                   int32_t* acc_pos, int32_t* acc_tok, int32_t* new_end,
+                                   int32_t* next_draft, int32_t* status,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
  * verify_gumbel_tree -- state-equality verification of one draft tree per
  * sequence with shared Gumbel noise.  [SPOT] Sec. 4.1, Sec. 4.3, App. A.1:
  *   s*(y)  = argmax over masked positions s of max_v p_s(v | y) (untempered;
@@ -251,6 +298,7 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype,
  *   DBV_KIND_GREEDY:    K_or_S = K, L = W (draft rows)
  *   DBV_KIND_REJECTION: K_or_S = K, L ignored
  *   DBV_KIND_TREE:      K_or_S = S, L = block length
+ *   DBV_KIND_ANY_ORDER: K_or_S = U, L ignored
  * Returns 0 for invalid sizes.  Depends only on its arguments.
  */
 size_t verify_workspace_size(dbv_kind kind, int B, int K_or_S, int L, int V, dbv_dtype dtype);

@@ -43,6 +43,13 @@ def check_greedy(g, o):
     np.testing.assert_array_equal(npi(g["next_len"]), o["next_len"], err_msg="next_len")
 
 
+def check_any_order(g, o):
+    """Any-order greedy outputs are integer decisions on exact values: all
+    exact."""
+    for k in ("status", "accept_len", "num_accepted", "acc_pos", "acc_tok", "new_end", "next_draft"):
+        np.testing.assert_array_equal(npi(g[k]), np.asarray(o[k], np.int64), err_msg=k)
+
+
 def check_sampling(g, x, o, lam, t_target, t_draft, dtype_name, eos_id=-1, len_budget=None,
                    seqs=None, delta=None):
     """Rejection / lenient / Cactus (``delta`` set) outputs against the oracle

@@ -62,6 +62,9 @@ def test_workspace_sizes(lib):
     assert lib.verify_workspace_size(_lib.DBV_KIND_GREEDY, 1, -1, 0, 100, 1) == 0
     assert lib.verify_workspace_size(_lib.DBV_KIND_GREEDY, 1, 4, 0, 0, 1) == 0
     assert lib.verify_workspace_size(_lib.DBV_KIND_GREEDY, 1, 4, 0, 10, 7) == 0
+    a = lib.verify_workspace_size(_lib.DBV_KIND_ANY_ORDER, 64, 32, 0, 131072, _lib.DBV_BF16)
+    assert a >= 64 * 64 * 8 * 4 and a % 256 == 0
+    assert lib.verify_workspace_size(_lib.DBV_KIND_ANY_ORDER, 1, 2000, 0, 100, 1) == 0
 
 
 def _greedy(lib, **kw):
@@ -102,6 +105,17 @@ def _tree(lib, **kw):
                                   a["sp"], a["m"], a["par"], a["ep"], a["et"], a["ns"], a["npos"],
                                   a["g"], a["gs"], a["gp"], a["T"], a["mode"], o, o, o, o, o, o, o,
                                   o, o, a["ws"], a["wsb"], a["stream"])
+
+
+def _any_order(lib, **kw):
+    a = dict(B=2, U=4, V=100, dt=_lib.DBV_BF16, tgt=FAKE, ts=400, tr=100, order=FAKE, na=None, pos=None,
+             d=FAKE, dr=FAKE, ds=400, drs=100, eos=-1, end=None, o=FAKE, nd=FAKE, st=FAKE, ws=FAKE,
+             wsb=1 << 20, stream=None)
+    a.update(kw)
+    o = a["o"]
+    return lib.verify_greedy_any_order(a["B"], a["U"], a["V"], a["dt"], a["tgt"], a["ts"], a["tr"], a["order"],
+                                       a["na"], a["pos"], a["d"], a["dr"], a["ds"], a["drs"], a["eos"], a["end"],
+                                       o, o, o, o, o, a["nd"], a["st"], a["ws"], a["wsb"], a["stream"])
 
 
 INVALID = _lib.DBV_ERR_INVALID_ARG
@@ -145,12 +159,21 @@ def test_tree_rejects_bad_args(lib, kw):
     assert _tree(lib, **kw) == INVALID
 
 
+@pytest.mark.parametrize("kw", [
+    dict(B=-1), dict(U=-1), dict(U=5000), dict(V=0), dict(dt=3), dict(tgt=None), dict(order=None),
+    dict(d=None), dict(o=None), dict(ts=-1), dict(drs=-1), dict(tgt=FAKE + 1), dict(dr=FAKE + 1),
+])
+def test_any_order_rejects_bad_args(lib, kw):
+    assert _any_order(lib, **kw) == INVALID
+
+
 def test_workspace_errors(lib):
     assert _greedy(lib, ws=None) == _lib.DBV_ERR_WORKSPACE
     assert _greedy(lib, wsb=8) == _lib.DBV_ERR_WORKSPACE
     assert _greedy(lib, ws=FAKE + 64) == _lib.DBV_ERR_WORKSPACE
     assert _reject(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
     assert _tree(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
+    assert _any_order(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
 
 
 def test_optional_arguments_are_accepted(lib):
@@ -163,6 +186,8 @@ def test_optional_arguments_are_accepted(lib):
     assert _tree(lib, mode=_lib.DBV_TREE_FIXED_POSITION, npos=FAKE, m=None) == nodev
     assert _greedy(lib, W=0, dr=None, nd=None, nl=None) == nodev
     assert _reject(lib, K=0, drf=None, d=None, ua=None) == nodev
+    assert _any_order(lib, dr=None, nd=None, st=None) == nodev
+    assert _any_order(lib, U=0, order=None, d=None) == nodev
 
 
 def test_valid_call_without_gpu_reports_no_device(lib):
@@ -173,6 +198,7 @@ def test_valid_call_without_gpu_reports_no_device(lib):
     assert _reject(lib, lenient=True) == _lib.DBV_ERR_NO_DEVICE
     assert _reject(lib, cactus=True, delta=0.0) == _lib.DBV_ERR_NO_DEVICE
     assert _tree(lib) == _lib.DBV_ERR_NO_DEVICE
+    assert _any_order(lib, na=FAKE, pos=FAKE, eos=3, end=FAKE) == _lib.DBV_ERR_NO_DEVICE
 
 
 def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):

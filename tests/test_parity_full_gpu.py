@@ -20,6 +20,8 @@ that hold at any size:
     trees; on all 16 the walk is redone from the GPU's per-state choices
   * packed greedy           B=64 K=31 W=32 V=131072 bf16 -- oracle on every
     sequence (one at a time), with and without the stopping rule
+  * any-order greedy        B=64 U=32 V=131072 bf16 -- oracle on every
+    sequence, with and without EOS / end position
 """
 
 import sys
@@ -31,7 +33,7 @@ import torch
 import draft_block_verification_amd as dbv
 import oracle
 import workloads
-from tests.parity import check_greedy, check_sampling, check_tree, np64, npi
+from tests.parity import check_any_order, check_greedy, check_sampling, check_tree, np64, npi
 
 pytestmark = pytest.mark.gpu
 
@@ -228,3 +230,22 @@ def test_full_packed_greedy(dev, stopping):
                                  len_budget=None if not stopping else npi(kw["len_budget"][b:b + 1]))
         check_greedy(_take(r, [b]), o)
     say("mean accept length", float(r["accept_len"].float().mean()), "mean emitted", float(r["num_out"].float().mean()))
+
+
+# -------------------------------------------------------------- any-order ---
+
+def test_full_any_order(dev):
+    say("full any-order B=64 U=32 V=131072 bf16")
+    x = workloads.config5_any_order()
+    xd = {k: v.to(dev) for k, v in x.items()}
+    for eos, end in ((-1, None), (int(x["draft_tokens"][x["draft_tokens"] >= 0][0]), x["positions"][:, 20].clone())):
+        g = dbv.verify_greedy_any_order(xd["tgt"], xd["order"], xd["draft_tokens"], num_active=xd["num_active"],
+                                        positions=xd["positions"], draft_rows=xd["draft_rows"], eos_id=eos,
+                                        end_pos=None if end is None else end.to(dev))
+        for b0 in range(0, 64, 8):
+            sl = slice(b0, b0 + 8)
+            o = oracle.verify_greedy_any_order(
+                np64(x["tgt"][sl]), npi(x["order"][sl]), npi(x["num_active"][sl]), npi(x["positions"][sl]),
+                npi(x["draft_tokens"][sl]), np64(x["draft_rows"][sl]), eos, None if end is None else npi(end[sl]))
+            check_any_order({k: v[sl] for k, v in g.items()}, o)
+        say("eos", eos, "mean accepted", float(g["num_accepted"].float().mean()))

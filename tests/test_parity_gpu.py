@@ -12,7 +12,7 @@ import torch
 import draft_block_verification_amd as dbv
 import oracle
 import workloads
-from tests.parity import check_greedy, check_sampling, check_tree, np64, npi
+from tests.parity import check_any_order, check_greedy, check_sampling, check_tree, np64, npi
 
 pytestmark = pytest.mark.gpu
 
@@ -194,6 +194,60 @@ def test_cactus_edge_cases(dev):
                              xn["u_accept"], xn["u_resample"], eos_id=eos, len_budget=npi(bud))
     assert o["accept_len"][0] == 0 and o["status"][1] == oracle.STATUS_BAD_INPUT
     check_sampling(res, xn, o, 0.0, 1.0, 1.0, "float32", eos_id=eos, len_budget=npi(bud), delta=3.0)
+
+
+# --------------------------------------------------------------- any-order ---
+
+def _ao_run(dev, x, eos_id=-1, end_pos=None, draft_rows=True, positions=True):
+    g = dbv.verify_greedy_any_order(
+        x["tgt"].to(dev), x["order"].to(dev), x["draft_tokens"].to(dev), num_active=x["num_active"].to(dev),
+        positions=x["positions"].to(dev) if positions else None,
+        draft_rows=x["draft_rows"].to(dev) if draft_rows else None, eos_id=eos_id,
+        end_pos=None if end_pos is None else end_pos.to(dev))
+    o = oracle.verify_greedy_any_order(
+        np64(x["tgt"]), npi(x["order"]), npi(x["num_active"]), npi(x["positions"]) if positions else None,
+        npi(x["draft_tokens"]), np64(x["draft_rows"]) if draft_rows else None, eos_id,
+        None if end_pos is None else npi(end_pos))
+    return g, o
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("agree", [0.6, 0.95])
+def test_any_order_parity(dev, dtype, agree):
+    say("any-order", dtype, agree)
+    x = workloads.anyorder_inputs(91, 12, 16, 5003, dtype, agree=agree, missing=0.15)
+    g, o = _ao_run(dev, x)
+    check_any_order(g, o)
+    # with an EOS (a token some drafts carry) and an end position
+    eos = int(x["draft_tokens"][x["draft_tokens"] >= 0][3])
+    end = x["positions"][:, 5].clone()
+    g, o = _ao_run(dev, x, eos_id=eos, end_pos=end)
+    check_any_order(g, o)
+    say("h", list(o["accept_len"]), "kept", list(o["num_accepted"]))
+
+
+def test_any_order_edge_cases(dev):
+    say("any-order edge cases")
+    x = workloads.anyorder_inputs(92, 8, 6, 777, torch.float32, missing=0.0, full=True)
+    x["tgt"] = torch.randint(-3, 4, x["tgt"].shape, generator=torch.Generator().manual_seed(3)).float()
+    # drafts = the verifier argmax (lowest index on ties) so windows fill up
+    for b in range(8):
+        for r in range(6):
+            x["draft_tokens"][b, int(x["order"][b, r])] = int(torch.argmax(x["tgt"][b, r]))
+    x["order"][1, 2] = x["order"][1, 3]           # not a permutation
+    x["positions"][2, 4] = x["positions"][2, 3]   # positions do not increase
+    x["draft_tokens"][3, 0] = -2                  # bad token
+    x["num_active"][4] = 0                        # empty window
+    x["num_active"][5] = 7                        # more than U
+    x["draft_tokens"][6, int(x["order"][6, 0])] = -1   # missing at rank 0: kappa = 0
+    g, o = _ao_run(dev, x)
+    check_any_order(g, o)
+    assert o["accept_len"][0] == 6 and o["num_accepted"][0] == 6          # A = u
+    assert list(o["status"][1:4]) == [1, 1, 1] and o["status"][5] == 1
+    assert o["num_accepted"][4] == 0 and o["kappa"][6] == 0 and o["num_accepted"][6] == 1
+    g, o = _ao_run(dev, x, draft_rows=False, positions=False)
+    check_any_order(g, o)
+    assert (npi(g["next_draft"]) == -1).all()
 
 
 # -------------------------------------------------------------- edge cases ---

@@ -226,3 +226,55 @@ def config4(device="cpu", sigma_node=0.1, B=16, S=64, L=32, V=151936):
     V=151936 bf16, T=1."""
     return tree_inputs(4, B, S, L, V, torch.bfloat16, sigma_node=sigma_node,
                        temperature=1.0, device=device)
+
+
+# -------------------------------------------------------------- any-order --
+
+def anyorder_inputs(c, B, U, V, dtype=torch.bfloat16, missing=0.1, agree=0.85, device="cpu",
+                    with_draft_rows=True, full=False):
+    """One any-order greedy verification call per sequence.
+
+    u_b ~ U{1..U} unresolved slots (all U when ``full``) at increasing output
+    positions; the order is a seeded permutation of the slots (standing in
+    for a confidence order chosen before the call); verifier rows by rank are
+    z ~ N(0, 3^2) with a +6 planted peak; the draft at the slot of rank r is
+    the verifier's argmax with probability ``agree`` and a uniform token
+    otherwise, and is missing (-1) with probability ``missing``; drafter rows
+    by slot are dtype(z + N(0, 1)) of the slot's own verifier row.
+    """
+    tgt = _planted_logits(c, (B, U, V), 6.0, dtype, device)
+    g3 = _gen(c, 3, "cpu")
+    g8 = _gen(c, 8, "cpu")
+    best = torch.argmax(tgt.float(), dim=-1).cpu()     # by rank
+    if full:
+        u = torch.full((B,), U, dtype=torch.int32)
+    else:
+        u = torch.randint(1, U + 1, (B,), generator=g8).to(torch.int32)
+    order = torch.zeros(B, U, dtype=torch.int32)
+    drafts = torch.full((B, U), -1, dtype=torch.int32)
+    positions = torch.zeros(B, U, dtype=torch.int32)
+    for b in range(B):
+        n = int(u[b])
+        perm = torch.randperm(n, generator=g3)
+        order[b, :n] = perm.to(torch.int32)
+        order[b, n:] = torch.arange(n, U, dtype=torch.int32)
+        start = int(torch.randint(1, 1000, (1,), generator=g8))
+        gaps = torch.randint(1, 3, (U,), generator=g8)
+        positions[b] = (start + torch.cumsum(gaps, 0)).to(torch.int32)
+        coin = torch.rand(n, generator=g3)
+        other = torch.randint(0, V, (n,), generator=g3)
+        for r in range(n):
+            if coin[r] < missing:
+                continue
+            drafts[b, int(perm[r])] = int(best[b, r]) if coin[r] < missing + (1 - missing) * agree else int(other[r])
+    out = dict(tgt=tgt, order=order, draft_tokens=drafts, num_active=u, positions=positions)
+    if with_draft_rows:
+        dr = (tgt.float() + torch.randn(B, U, V, generator=_gen(c, 5, device), device=device)).to(dtype)
+        out["draft_rows"] = dr
+    return out
+
+
+def config5_any_order(device="cpu"):
+    """Any-order packed greedy verify: B=64 sequences, window U=32 slots,
+    V=131072 bf16, verifier rows by rank plus drafter rows by slot."""
+    return anyorder_inputs(6, 64, 32, 131072, torch.bfloat16, device=device)
