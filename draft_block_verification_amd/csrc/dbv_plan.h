@@ -123,7 +123,11 @@ inline size_t partial_bytes(int64_t max_rows) {
 // crosses u*Z, and one wave rescans that tile in vocabulary order.
 // kMaxDrawTiles bounds the tiles per row (at most kDrawTilesPerThread per
 // select thread), and so the vocabulary of the sampling entry points.
+// Rows of at most kFusedDrawTiles tiles skip the split: one group per
+// sequence makes the decision, computes every tile mass into LDS and draws,
+// which saves a kernel boundary and the round trip of the masses.
 constexpr int kDrawThreads = 1024;
+constexpr int kFusedDrawTiles = 16;
 constexpr int kMaxDrawTiles = 8192;
 constexpr int kDrawTilesPerThread = kMaxDrawTiles / kDrawThreads;
 constexpr int64_t kMaxSampleV = int64_t(1) << 21;   // <= kMaxDrawTiles tiles of 256 fp32

@@ -260,14 +260,14 @@ constexpr int kTileBatch = 8;   // tiles a wave reads together (16 loads per lan
 
 // Masses of the draw row's tiles [t_lo, t_hi) (64 16-byte vectors each, of
 // the row and, for the residual, of drafter row yr), by the NW waves of the
-// group: wave w takes tiles t_lo + w, t_lo + w + NW, ..., kTileBatch of them
+// group: wave w takes tiles t_lo + w, t_lo + w + NW, ..., TB of them
 // at a time with all their loads in flight; lane l sums the weights of the
 // tile's l-th vector and the wave reduces them into out[tile].  `vec` says
 // both rows are 16-byte aligned; otherwise (and for the row's last, partial
 // vector) elements are loaded one by one.  Byte offsets stay below 2^32
 // (V <= kMaxSampleV), so the loads take a uniform 64-bit base and 32-bit lane
 // offsets.
-template <int DT, int NW>
+template <int DT, int NW, int TB = kTileBatch>
 __device__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo, int t_hi, bool vec,
                             const DrawWeight& w, float* out) {
   using E = Elem<DT>;
@@ -275,11 +275,11 @@ __device__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo,
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const uint32_t Vn = static_cast<uint32_t>(V);
-  for (int t0 = t_lo + wv; t0 < t_hi; t0 += NW * kTileBatch) {
-    u32x4 rx[kTileBatch], ry[kTileBatch];
-    bool full[kTileBatch];
+  for (int t0 = t_lo + wv; t0 < t_hi; t0 += NW * TB) {
+    u32x4 rx[TB], ry[TB];
+    bool full[TB];
 #pragma unroll
-    for (int k = 0; k < kTileBatch; ++k) {
+    for (int k = 0; k < TB; ++k) {
       const int tile = t0 + k * NW;
       const uint32_t e = static_cast<uint32_t>(tile) * (64 * W) + lane * W;   // the lane's first element
       full[k] = vec && tile < t_hi && e + W <= Vn;
@@ -290,7 +290,7 @@ __device__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo,
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < kTileBatch; ++k) {
+    for (int k = 0; k < TB; ++k) {
       const int tile = t0 + k * NW;
       if (tile < t_hi) {   // uniform across the wave
         const uint32_t e = static_cast<uint32_t>(tile) * (64 * W) + lane * W;
@@ -337,46 +337,49 @@ __device__ __forceinline__ float group_exclusive_scan_f(float v, float& total, f
   return base + inc - v;
 }
 
-constexpr int kDraftsPerThread = (kMaxDraft + kBlock - 1) / kBlock;   // drafts of one thread
+// LDS of the decision step (per sequence): row statistics of the target rows
+// 0..n and drafter rows 0..n-1, and d, p(d), p~(d), q(d) of the rejected
+// draft.
+struct DecideLds {
+  float Mp[kMaxDraft + 1], Sp[kMaxDraft + 1];
+  float Mq[kMaxDraft], Sq[kMaxDraft];
+  int st, h;
+  int dh;
+  float ph, pth, qh;
+};
 
-// Per (sequence, chunk of draw tiles), kBlock threads:
-//  1. Every input of the decision is requested at once: the length, budget,
-//     draft tokens, accept uniforms and stream position; then the row
-//     statistics partials and the logits at the draft tokens.
-//  2. p(d), q(d), the acceptance tests (u * q(d) < p~(d)) and h; chunk 0
-//     writes the diagnostics and the decision record.
-//  3. The masses of the chunk's tiles of row h: [p - q]_+ against drafter
-//     row h if a draft was rejected, else the bonus weight p.
-template <int DT>
-__global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
-  __shared__ float s_Mp[kMaxDraft + 1], s_Sp[kMaxDraft + 1];
-  __shared__ float s_Mq[kMaxDraft], s_Sq[kMaxDraft];
-  __shared__ float s_p[kMaxDraft], s_pt[kMaxDraft], s_q[kMaxDraft];
-  __shared__ int s_st, s_h;
+// The decision of sequence b by a group of NT threads:
+//  1. Every input is requested at once: the length, budget, draft tokens,
+//     accept uniforms and stream position; then the row statistics partials
+//     and the logits at the draft tokens.
+//  2. p(d), q(d), the acceptance tests (u * q(d) < p~(d)) and h.  With
+//     `first`, the group writes the diagnostics (and, for a sequence with a
+//     data error, every output).
+// Returns the draw record: row h, its weight parameters and the uniform; its
+// status carries the error bits when there is nothing to draw.
+template <int DT, int NT>
+__device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, DecideLds& s) {
+  constexpr int DPT = (kMaxDraft + NT - 1) / NT;   // drafts of one thread
   using E = Elem<DT>;
-  const int b = blockIdx.x / a.chunks;
-  const int c = blockIdx.x - b * a.chunks;
   const int t = threadIdx.x;
-
-  // ---- 1. inputs ----------------------------------------------------------
   bool nbad;
   const int n = draft_count(a.draft_len, b, a.K, nbad);
   const int budget = a.budget ? a.budget[b] : INT_MAX;
   const int p0 = a.pre[b];
   const int R = a.pre[a.B];
   const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
-  int di[kDraftsPerThread];
-  float ui[kDraftsPerThread], xi[kDraftsPerThread], yi[kDraftsPerThread];
+  int di[DPT];
+  float ui[DPT], xi[DPT], yi[DPT];
 #pragma unroll
-  for (int k = 0; k < kDraftsPerThread; ++k) {
-    const int i = t + k * kBlock;
+  for (int k = 0; k < DPT; ++k) {
+    const int i = t + k * NT;
     di[k] = i < a.K ? d[i] : 0;
     ui[k] = i < a.K ? a.u_accept[static_cast<int64_t>(b) * a.K + i] : 0.f;
   }
   int st = 0;
 #pragma unroll
-  for (int k = 0; k < kDraftsPerThread; ++k) {
-    const int i = t + k * kBlock;
+  for (int k = 0; k < DPT; ++k) {
+    const int i = t + k * NT;
     xi[k] = yi[k] = 0.f;
     if (i < n) {
       if (di[k] < 0 || di[k] >= a.V) {
@@ -388,44 +391,46 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
     }
   }
   if (t == 0) {
-    s_st = (nbad || budget < 0) ? SEQ_BAD_INPUT : 0;
-    s_h = n;
+    s.st = (nbad || budget < 0) ? SEQ_BAD_INPUT : 0;
+    s.h = n;
   }
   __syncthreads();
   if (!nbad) {
     // Stream rows p0..p0+n: target rows 0..n (k = kp); p0+n+1..: drafter
     // rows 0..n-1 (k = kq).
     const FlatSplit f = make_split(R, a.V, E::kBytes, a.grid);
-    combine_rows_stats(
+    combine_rows_stats<NT>(
         n + 1, a.stats, a.kp,
-        [&](int r, int64_t& first, int64_t& cnt) {
-          split_row_slots(f, p0 + r, first, cnt);
-          first *= kWaves;
+        [&](int r, int64_t& first_slot, int64_t& cnt) {
+          split_row_slots(f, p0 + r, first_slot, cnt);
+          first_slot *= kWaves;
           cnt *= kWaves;
         },
         [&](int r, float M, float S) {
-          s_Mp[r] = M; s_Sp[r] = S;
+          s.Mp[r] = M; s.Sp[r] = S;
           st |= stats_status(M, S);
         });
-    combine_rows_stats(
+    combine_rows_stats<NT>(
         n, a.stats, a.kq,
-        [&](int r, int64_t& first, int64_t& cnt) {
-          split_row_slots(f, p0 + n + 1 + r, first, cnt);
-          first *= kWaves;
+        [&](int r, int64_t& first_slot, int64_t& cnt) {
+          split_row_slots(f, p0 + n + 1 + r, first_slot, cnt);
+          first_slot *= kWaves;
           cnt *= kWaves;
         },
         [&](int r, float M, float S) {
-          s_Mq[r] = M; s_Sq[r] = S;
+          s.Mq[r] = M; s.Sq[r] = S;
           st |= stats_status(M, S);
         });
   }
-  if (st) atomicOr(&s_st, st);
+  if (st) atomicOr(&s.st, st);
   __syncthreads();
-  if (s_st & SEQ_ERROR_MASK) {
-    if (c == 0) {
+  DrawRecord rec{};
+  if (s.st & SEQ_ERROR_MASK) {
+    rec.status = s.st;
+    if (first) {
       int32_t* out = a.out_tokens + static_cast<int64_t>(b) * (a.K + 1);
-      for (int i = t; i <= a.K; i += kBlock) out[i] = -1;
-      for (int i = t; i < a.K; i += kBlock) {
+      for (int i = t; i <= a.K; i += NT) out[i] = -1;
+      for (int i = t; i < a.K; i += NT) {
         const int64_t o = static_cast<int64_t>(b) * a.K + i;
         if (a.p_draft) a.p_draft[o] = 0.f;
         if (a.q_draft) a.q_draft[o] = 0.f;
@@ -435,32 +440,32 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
         a.accept_len[b] = -1;
         a.num_out[b] = 0;
         if (a.residual_mass) a.residual_mass[b] = 0.f;
-        if (a.status) a.status[b] = s_st;
-        a.rec[b].status = s_st;
+        if (a.status) a.status[b] = s.st;
       }
     }
-    return;
+    return rec;
   }
 
-  // ---- 2. acceptance tests: accept d_i iff u_i * q_i(d_i) < p~_i(d_i) ----
-  // Linear rule: p~(d) = (1 - lambda) p(d) + lambda q(d).  Cactus rule:
+  // Acceptance tests: accept d_i iff u_i * q_i(d_i) < p~_i(d_i).  Linear
+  // rule: p~(d) = (1 - lambda) p(d) + lambda q(d).  Cactus rule:
   // p~(d) = gamma(p(d), delta).
+  float pk[DPT], ptk[DPT], qk[DPT];
 #pragma unroll
-  for (int k = 0; k < kDraftsPerThread; ++k) {
-    const int i = t + k * kBlock;
-    float p = 0.f, q = 0.f, al = 0.f;
+  for (int k = 0; k < DPT; ++k) {
+    const int i = t + k * NT;
+    float p = 0.f, q = 0.f, pt = 0.f, al = 0.f;
     if (i < n) {
-      p = fast_exp2(__builtin_fmaf(xi[k], a.kp, -s_Mp[i] * a.kp)) / s_Sp[i];
-      q = fast_exp2(__builtin_fmaf(yi[k], a.kq, -s_Mq[i] * a.kq)) / s_Sq[i];
-      const float pt = a.rule == RULE_CACTUS ? cactus_gamma(p, a.delta) : (1.f - a.lam) * p + a.lam * q;
-      s_p[i] = p;
-      s_pt[i] = pt;
-      s_q[i] = q;
-      if (q == 0.f && pt > 0.f) atomicOr(&s_st, SEQ_Q_ZERO);
+      p = fast_exp2(__builtin_fmaf(xi[k], a.kp, -s.Mp[i] * a.kp)) / s.Sp[i];
+      q = fast_exp2(__builtin_fmaf(yi[k], a.kq, -s.Mq[i] * a.kq)) / s.Sq[i];
+      pt = a.rule == RULE_CACTUS ? cactus_gamma(p, a.delta) : (1.f - a.lam) * p + a.lam * q;
+      if (q == 0.f && pt > 0.f) atomicOr(&s.st, SEQ_Q_ZERO);
       al = q > 0.f ? fminf(1.f, pt / q) : (pt > 0.f ? 1.f : 0.f);
-      if (!(ui[k] * q < pt)) atomicMin(&s_h, i);
+      if (!(ui[k] * q < pt)) atomicMin(&s.h, i);
     }
-    if (c == 0 && i < a.K) {
+    pk[k] = p;
+    ptk[k] = pt;
+    qk[k] = q;
+    if (first && i < a.K) {
       const int64_t o = static_cast<int64_t>(b) * a.K + i;
       if (a.p_draft) a.p_draft[o] = p;
       if (a.q_draft) a.q_draft[o] = q;
@@ -469,104 +474,127 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   }
   __syncthreads();
   // Uniform across the group: keeps the row addresses in scalar registers.
-  const int h = __builtin_amdgcn_readfirstlane(s_h);
+  const int h = __builtin_amdgcn_readfirstlane(s.h);
   const bool resid = h < n;
-  const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + static_cast<int64_t>(h) * a.tr) * E::kBytes;
-  const char* yr = resid
-      ? static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(h) * a.dr) * E::kBytes
-      : xr;
-  DrawWeight w;
-  w.kp = a.kp; w.cp = -s_Mp[h] * a.kp; w.isp = 1.f / s_Sp[h];
-  w.kq = a.kq; w.cq = resid ? -s_Mq[h] * a.kq : 0.f; w.isq = resid ? 1.f / s_Sq[h] : 1.f;
-  w.resid = resid ? 1 : 0;
-  w.excl = -1;
-  w.wexcl = 0.f;
+  if (resid && a.rule == RULE_CACTUS) {
+    // The owner of draft h shares its token and probabilities.
+#pragma unroll
+    for (int k = 0; k < DPT; ++k)
+      if (t + k * NT == h) {
+        s.dh = di[k];
+        s.ph = pk[k];
+        s.pth = ptk[k];
+        s.qh = qk[k];
+      }
+    __syncthreads();
+  }
+  rec.status = s.st;
+  rec.h = h;
+  rec.resid = resid ? 1 : 0;
+  rec.cp = -s.Mp[h] * a.kp;
+  rec.isp = 1.f / s.Sp[h];
+  rec.cq = resid ? -s.Mq[h] * a.kq : 0.f;
+  rec.isq = resid ? 1.f / s.Sq[h] : 1.f;
+  rec.u = a.u_resample[static_cast<int64_t>(b) * (a.K + 1) + h];
+  rec.excl = -1;
+  rec.wexcl = 0.f;
   if (resid && a.rule == RULE_CACTUS) {
     // p~(v) = (1 - gamma) / (1 - p(d)) p(v) for v != d, p~(d) = gamma.
-    const float ph = s_p[h];
-    const float c_rest = ph < 1.f ? static_cast<float>((1.0 - static_cast<double>(s_pt[h])) /
+    const float ph = s.ph;
+    const float c_rest = ph < 1.f ? static_cast<float>((1.0 - static_cast<double>(s.pth)) /
                                                        (1.0 - static_cast<double>(ph)))
                                   : 0.f;
-    w.isp *= c_rest;
-    w.excl = d[h];
-    w.wexcl = fmaxf(s_pt[h] - s_q[h], 0.f);
+    rec.isp *= c_rest;
+    rec.excl = s.dh;
+    rec.wexcl = fmaxf(s.pth - s.qh, 0.f);
   }
-  if (c == 0 && t == 0) {
-    DrawRecord r;
-    r.status = s_st;
-    r.h = h;
-    r.resid = w.resid;
-    r.cp = w.cp; r.isp = w.isp;
-    r.cq = w.cq; r.isq = w.isq;
-    r.u = a.u_resample[static_cast<int64_t>(b) * (a.K + 1) + h];
-    r.excl = w.excl;
-    r.wexcl = w.wexcl;
-    a.rec[b] = r;
-  }
+  return rec;
+}
 
-  // ---- 3. this chunk's tile masses ---------------------------------------
+__device__ __forceinline__ DrawWeight draw_weight(const SampleArgs& a, const DrawRecord& r) {
+  DrawWeight w;
+  w.kp = a.kp; w.cp = r.cp; w.isp = r.isp;
+  w.kq = a.kq; w.cq = r.cq; w.isq = r.isq;
+  w.resid = r.resid;
+  w.excl = r.excl;
+  w.wexcl = r.wexcl;
+  return w;
+}
+
+// Row h of sequence b: the target row, and the drafter row for a residual.
+template <int DT>
+__device__ __forceinline__ void draw_rows(const SampleArgs& a, int b, int h, bool resid, const char*& xr,
+                                          const char*& yr) {
+  using E = Elem<DT>;
+  xr = static_cast<const char*>(a.tgt) + (b * a.ts + static_cast<int64_t>(h) * a.tr) * E::kBytes;
+  yr = resid ? static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(h) * a.dr) * E::kBytes : xr;
+}
+
+// Per (sequence, chunk of draw tiles), kBlock threads: the decision (chunk 0
+// writes the diagnostics and the record), then the masses of the chunk's
+// tiles of row h: [p~ - q]_+ against drafter row h if a draft was rejected,
+// else the bonus weight p.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
+  __shared__ DecideLds s;
+  const int b = blockIdx.x / a.chunks;
+  const int c = blockIdx.x - b * a.chunks;
+  const DrawRecord rec = draw_decide<DT, kBlock>(a, b, c == 0, s);
+  if (c == 0 && threadIdx.x == 0) a.rec[b] = rec;
+  if (rec.status & SEQ_ERROR_MASK) return;
+  const char *xr, *yr;
+  draw_rows<DT>(a, b, rec.h, rec.resid != 0, xr, yr);
   const bool vec = ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0;
   const int t_lo = c * a.tpc;
   const int t_hi = t_lo + a.tpc < a.tiles ? t_lo + a.tpc : a.tiles;
-  tile_masses<DT, kWaves>(xr, yr, a.V, t_lo, t_hi, vec, w, a.tmass + static_cast<int64_t>(b) * a.tiles);
+  tile_masses<DT, kWaves>(xr, yr, a.V, t_lo, t_hi, vec, draw_weight(a, rec),
+                          a.tmass + static_cast<int64_t>(b) * a.tiles);
 }
 
 constexpr int kDrawWaves = kDrawThreads / 64;
 
-// One group of kDrawThreads threads per sequence: the tile where the running
-// mass first exceeds u*Z (the last positive tile if rounding leaves u*Z at or
-// past the total), the token inside it in vocabulary order, and the output
-// assembly C = (d_1..d_h, c) with the ending condition.
+struct SelectLds {
+  float tile[kMaxDrawTiles];
+  float w[kDrawWaves];
+  float Z, base;
+  int ct, lt, cs, pick, a;
+};
+
+// The draw of sequence b by kDrawThreads threads, given its record and this
+// thread's tile masses m0 (tiles [t*q, (t+1)*q), q = ceil(tiles / threads)):
+// the tile where the running mass first exceeds u*Z (the last positive tile
+// if rounding leaves u*Z at or past the total), the token inside it in
+// vocabulary order, and the output assembly C = (d_1..d_h, c) with the
+// ending condition.
+// dt is this thread's draft token d_{t+1} (t < K), requested with the first
+// loads; every output position i < h <= K <= kDrawThreads is some thread's t.
 template <int DT>
-__global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
-  __shared__ float s_tile[kMaxDrawTiles];
-  __shared__ float s_w[kDrawWaves];
-  __shared__ float s_Z, s_base;
-  __shared__ int s_ct, s_lt, s_cs, s_pick, s_a;
+__device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, int budget, int dt,
+                            const float (&m0)[kDrawTilesPerThread], SelectLds& s) {
+  static_assert(kMaxDraft <= kDrawThreads, "one draft token per thread");
   using E = Elem<DT>;
-  const int b = blockIdx.x;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wv = t >> 6;
   const int ntiles = a.tiles;
   const int q = static_cast<int>(cdiv(ntiles, kDrawThreads));   // tiles per thread, <= kDrawTilesPerThread
-  // Everything this group reads first is requested together: the decision
-  // record, the budget and this thread's tile masses.
-  const DrawRecord rec = a.rec[b];
-  const int budget = a.budget ? a.budget[b] : INT_MAX;
-  const float* tmass = a.tmass + static_cast<int64_t>(b) * ntiles;
-  float m0[kDrawTilesPerThread];
-#pragma unroll
-  for (int k = 0; k < kDrawTilesPerThread; ++k) {
-    const int tile = t * q + k;
-    m0[k] = (k < q && tile < ntiles) ? tmass[tile] : 0.f;
-  }
-  if (rec.status & SEQ_ERROR_MASK) return;          // outputs already written
-  const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
   const int h = __builtin_amdgcn_readfirstlane(rec.h);
   int status = rec.status;
   const bool resid0 = rec.resid != 0;
-  const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + static_cast<int64_t>(h) * a.tr) * E::kBytes;
-  const char* yr = resid0
-      ? static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(h) * a.dr) * E::kBytes
-      : xr;
-  DrawWeight w;
-  w.kp = a.kp; w.cp = rec.cp; w.isp = rec.isp;
-  w.kq = a.kq; w.cq = rec.cq; w.isq = rec.isq;
-  w.resid = rec.resid;
-  w.excl = rec.excl;
-  w.wexcl = rec.wexcl;
+  const char *xr, *yr;
+  draw_rows<DT>(a, b, h, resid0, xr, yr);
+  DrawWeight w = draw_weight(a, rec);
   constexpr int TE = 64 * E::kVec;                              // elements per tile
 
   // Thread t holds the masses of tiles [t*q, (t+1)*q); an exclusive scan
   // gives it the mass before them, and the group's total Z.
   auto locate = [&](const float (&m)[kDrawTilesPerThread]) {
-    if (t == 0) { s_ct = INT_MAX; s_lt = -1; }
+    if (t == 0) { s.ct = INT_MAX; s.lt = -1; }
     float loc = 0.f;
 #pragma unroll
     for (int k = 0; k < kDrawTilesPerThread; ++k) loc += m[k];
     float Z;
-    const float start = group_exclusive_scan_f<kDrawWaves>(loc, Z, s_w);
+    const float start = group_exclusive_scan_f<kDrawWaves>(loc, Z, s.w);
     const float target = rec.u * Z;
     int hit = INT_MAX, last = -1;
     float run = start;
@@ -578,24 +606,24 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
       }
       run += m[k];
     }
-    if (hit != INT_MAX) atomicMin(&s_ct, hit);
-    if (last >= 0) atomicMax(&s_lt, last);
+    if (hit != INT_MAX) atomicMin(&s.ct, hit);
+    if (last >= 0) atomicMax(&s.lt, last);
     __syncthreads();
-    const int ct = s_ct != INT_MAX ? s_ct : (s_lt >= 0 ? s_lt : 0);
+    const int ct = s.ct != INT_MAX ? s.ct : (s.lt >= 0 ? s.lt : 0);
     if (t == ct / q) {   // the owner of the chosen tile writes the mass before it
       float before = start;
 #pragma unroll
       for (int k = 0; k < kDrawTilesPerThread; ++k)
         if (t * q + k < ct) before += m[k];
-      s_base = before;
-      s_Z = Z;
-      s_cs = ct;
+      s.base = before;
+      s.Z = Z;
+      s.cs = ct;
     }
     __syncthreads();
   };
   locate(m0);
-  const float Zres = resid0 ? s_Z : 0.f;
-  if (resid0 && !(s_Z > 0.f)) {
+  const float Zres = resid0 ? s.Z : 0.f;
+  if (resid0 && !(s.Z > 0.f)) {
     // Residual mass vanished in float32 (p == q up to rounding): draw from p
     // with the same uniform instead, and flag it.  (This group recomputes
     // the tile masses of p alone; the case has probability zero in exact
@@ -605,23 +633,23 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
     w.excl = -1;
     yr = xr;
     const bool vec = (reinterpret_cast<uintptr_t>(xr) & 15u) == 0;
-    tile_masses<DT, kDrawWaves>(xr, yr, a.V, 0, ntiles, vec, w, s_tile);
+    tile_masses<DT, kDrawWaves, 2>(xr, yr, a.V, 0, ntiles, vec, w, s.tile);
     __syncthreads();
     float m1[kDrawTilesPerThread];
 #pragma unroll
     for (int k = 0; k < kDrawTilesPerThread; ++k) {
       const int tile = t * q + k;
-      m1[k] = (k < q && tile < ntiles) ? s_tile[tile] : 0.f;
+      m1[k] = (k < q && tile < ntiles) ? s.tile[tile] : 0.f;
     }
     locate(m1);
   }
-  const float target = rec.u * s_Z;
+  const float target = rec.u * s.Z;
 
   // Wave 0 rescans the chosen tile in vocabulary order: lane l holds the
   // weights of the tile's l-th vector; a wave scan gives each lane the mass
   // before its vector.
   if (wv == 0) {
-    const int ct = __builtin_amdgcn_readfirstlane(s_cs);
+    const int ct = __builtin_amdgcn_readfirstlane(s.cs);
     const int64_t e0 = static_cast<int64_t>(ct) * TE + lane * E::kVec;
     float wt[E::kVec];
     float loc = 0.f;
@@ -637,7 +665,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
       const float o = __shfl_up(inc, k, 64);
       if (lane >= k) inc += o;
     }
-    const float start = s_base + inc - loc;
+    const float start = s.base + inc - loc;
     int found = -1, lastpos = -1;
     float r = start;
 #pragma unroll
@@ -653,23 +681,23 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
     int tok = -1;
     if (hits) tok = __shfl(found, __builtin_ctzll(hits), 64);
     else if (poss) tok = __shfl(lastpos, 63 - __builtin_clzll(poss), 64);
-    if (lane == 0) s_pick = tok;
+    if (lane == 0) s.pick = tok;
   }
   // ---- output assembly: C = (d_1..d_h, c), then the ending condition ----
   const int A = h + 1;
-  if (t == 0) s_a = A < budget ? A : budget;
+  if (t == 0) s.a = A < budget ? A : budget;
   __syncthreads();
-  const int tok = s_pick;
+  const int tok = s.pick;
   if (a.eos >= 0) {
     for (int i = t; i < A; i += kDrawThreads) {   // A can be K + 1 = kDrawThreads + 1
-      const int ci = i < h ? d[i] : tok;
-      if (ci == a.eos) atomicMin(&s_a, i + 1);
+      const int ci = i < h ? dt : tok;
+      if (ci == a.eos) atomicMin(&s.a, i + 1);
     }
   }
   __syncthreads();
-  const int an = s_a;
+  const int an = s.a;
   int32_t* out = a.out_tokens + static_cast<int64_t>(b) * (a.K + 1);
-  for (int i = t; i <= a.K; i += kDrawThreads) out[i] = i < an ? (i < h ? d[i] : tok) : -1;
+  for (int i = t; i <= a.K; i += kDrawThreads) out[i] = i < an ? (i < h ? dt : tok) : -1;
   if (t == 0) {
     a.accept_len[b] = h;
     a.num_out[b] = an;
@@ -677,6 +705,61 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
     if (a.residual_mass) a.residual_mass[b] = Zres * (1.f - a.lam);
     if (a.status) a.status[b] = status;
   }
+}
+
+// Second kernel of the split draw: one group per sequence reads the record
+// and the tile masses that k_draw_mass wrote.
+template <int DT>
+__global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
+  __shared__ SelectLds s;
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const int ntiles = a.tiles;
+  const int q = static_cast<int>(cdiv(ntiles, kDrawThreads));
+  // Everything this group reads first is requested together: the decision
+  // record, the budget and this thread's tile masses.
+  const DrawRecord rec = a.rec[b];
+  const int budget = a.budget ? a.budget[b] : INT_MAX;
+  const int dt = t < a.K ? a.draft_tokens[static_cast<int64_t>(b) * a.K + t] : -1;
+  const float* tmass = a.tmass + static_cast<int64_t>(b) * ntiles;
+  float m0[kDrawTilesPerThread];
+#pragma unroll
+  for (int k = 0; k < kDrawTilesPerThread; ++k) {
+    const int tile = t * q + k;
+    m0[k] = (k < q && tile < ntiles) ? tmass[tile] : 0.f;
+  }
+  if (rec.status & SEQ_ERROR_MASK) return;          // outputs already written
+  draw_select<DT>(a, b, rec, budget, dt, m0, s);
+}
+
+// The whole draw of one sequence in one group of kDrawThreads threads (for
+// rows of at most kFusedDrawTiles tiles): the decision, every tile mass of
+// row h into LDS, then the draw.
+template <int DT>
+__global__ __launch_bounds__(kDrawThreads) void k_draw_fused(SampleArgs a) {
+  __shared__ DecideLds sd;
+  __shared__ SelectLds s;
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const DrawRecord rec = draw_decide<DT, kDrawThreads>(a, b, true, sd);
+  if (rec.status & SEQ_ERROR_MASK) return;
+  const int budget = a.budget ? a.budget[b] : INT_MAX;
+  const int dt = t < a.K ? a.draft_tokens[static_cast<int64_t>(b) * a.K + t] : -1;
+  const char *xr, *yr;
+  draw_rows<DT>(a, b, rec.h, rec.resid != 0, xr, yr);
+  const bool vec = ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0;
+  const int ntiles = a.tiles;
+  tile_masses<DT, kDrawWaves, 8>(xr, yr, a.V, 0, ntiles, vec, draw_weight(a, rec), s.tile);
+  __syncthreads();
+  const int q = static_cast<int>(cdiv(ntiles, kDrawThreads));
+  float m0[kDrawTilesPerThread];
+#pragma unroll
+  for (int k = 0; k < kDrawTilesPerThread; ++k) {
+    const int tile = t * q + k;
+    m0[k] = (k < q && tile < ntiles) ? s.tile[tile] : 0.f;
+  }
+  __syncthreads();   // the fallback in draw_select may overwrite s.tile
+  draw_select<DT>(a, b, rec, budget, dt, m0, s);
 }
 
 // ============================================================== launches ===
@@ -694,8 +777,10 @@ bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const Tim
 
 bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
   const bool bf = dtype == DT_BF16;
-  return launch(bf ? fn(k_sample_rows<DT_BF16>) : fn(k_sample_rows<DT_F32>), a.grid, stream, a, ev) &&
-         launch(bf ? fn(k_draw_mass<DT_BF16>) : fn(k_draw_mass<DT_F32>), static_cast<int64_t>(a.B) * a.chunks,
+  if (!launch(bf ? fn(k_sample_rows<DT_BF16>) : fn(k_sample_rows<DT_F32>), a.grid, stream, a, ev)) return false;
+  if (a.tiles <= kFusedDrawTiles)
+    return launch_threads(bf ? fn(k_draw_fused<DT_BF16>) : fn(k_draw_fused<DT_F32>), a.B, kDrawThreads, stream, a);
+  return launch(bf ? fn(k_draw_mass<DT_BF16>) : fn(k_draw_mass<DT_F32>), static_cast<int64_t>(a.B) * a.chunks,
                 stream, a) &&
          launch_threads(bf ? fn(k_draw_select<DT_BF16>) : fn(k_draw_select<DT_F32>), a.B, kDrawThreads, stream, a);
 }
