@@ -21,6 +21,9 @@ following the pages' definitions in their own order:
   the ending position and retention by position.
 * ``tree``   -- coupled shared-Gumbel state-equality verification of a draft
   tree (and its T=0 greedy special case).
+* ``spot``   -- chain verification on the joint (position, token) space:
+  rejection sampling per link (SPOT App. B) and the confidence-gated hybrid
+  of coupled-noise match and rejection sampling.
 
 Sources (pages by title):
 * "One Call Ahead: Packed Self-Speculative Decoding with Diffusion Drafting"
@@ -46,6 +49,7 @@ from .cactus import (  # noqa: F401
     cactus_divergence, cactus_gamma, cactus_target, cactus_acceptance, cactus_residual,
 )
 from .anyorder import NO_END, verify_greedy_any_order  # noqa: F401
+from .spot import MODE_RS, MODE_MATCH, rs_link, rs_residual, verify_spot_chain  # noqa: F401
 from .tree import (  # noqa: F401
     TREE_STATE_EQUALITY, TREE_FIXED_POSITION, state_transition, walk,
     verify_gumbel_tree,

@@ -205,3 +205,47 @@ def test_any_order_pin_catches_planted_mistake(monkeypatch, fn, pin):
     monkeypatch.setattr(oracle, "verify_greedy_any_order", fn)
     with pytest.raises(AssertionError):
         pin()
+
+
+# ------------------------------------------------ joint-space chain (SPOT) ---
+
+import tests.test_oracle_spot_pins as sp  # noqa: E402
+import oracle.spot as spot  # noqa: E402
+
+_rs_link = spot.rs_link
+_rs_residual = spot.rs_residual
+_verify_spot = spot.verify_spot_chain
+
+
+def _sp_residual_unscaled(p, qhat, c):
+    return _rs_residual(p, qhat, 1.0)
+
+
+def _sp_link_ignores_position(u, p, qhat, c, on_star, tok):
+    return _rs_link(u, p, qhat, c, True, tok)
+
+
+def _sp_link_unscaled(u, p, qhat, c, on_star, tok):
+    return _rs_link(u, p, qhat, 1.0, on_star, tok)
+
+
+@pytest.mark.parametrize("name,fn,pin", [
+    ("rs_residual", _sp_residual_unscaled, sp.test_worked_example_by_hand),
+    ("rs_residual", _sp_residual_unscaled, lambda: sp.test_joint_space_commit_law_and_acceptance(52)),
+    ("rs_link", _sp_link_ignores_position, sp.test_worked_example_by_hand),
+    ("rs_link", _sp_link_ignores_position, lambda: sp.test_joint_space_commit_law_and_acceptance(52)),
+    ("rs_link", _sp_link_unscaled, lambda: sp.test_joint_space_commit_law_and_acceptance(53)),
+], ids=["residual-unscaled-hand", "residual-unscaled-law", "ignores-position-hand", "ignores-position-law",
+        "ratio-unscaled-law"])
+def test_spot_pin_catches_planted_mistake(monkeypatch, name, fn, pin):
+    monkeypatch.setattr(spot, name, fn)
+    with pytest.raises(AssertionError):
+        pin()
+
+
+def test_spot_pin_catches_wrong_gate(monkeypatch):
+    def gate_mirrored(*a, tau=0.6, **k):
+        return _verify_spot(*a, tau=1.0 - tau, **k)
+    monkeypatch.setattr(oracle, "verify_spot_chain", gate_mirrored)
+    with pytest.raises(AssertionError):
+        sp.test_gate_picks_the_verifier()
