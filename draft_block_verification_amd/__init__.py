@@ -20,7 +20,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus",
+    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_spot_chain",
     "verify_greedy_any_order", "verify_gumbel_tree", "workspace_size", "DBVError", "Prepared",
 ]
 
@@ -225,6 +225,65 @@ def verify_cactus(tgt, drf, draft_tokens, u_accept, u_resample, delta, draft_len
     return _sampling("verify_cactus", tgt, drf, draft_tokens, draft_len,
                      temperature_target, temperature_draft, delta, u_accept, u_resample,
                      eos_id, len_budget, workspace, diagnostics, prepare)
+
+
+def verify_spot_chain(tgt, drf, pos_star, prop_pos, prop_tok, q_pos_star, u_accept, u_resample,
+                      gumbel=None, tau=0.6, draft_len=None, temperature_target=1.0, temperature_draft=1.0,
+                      eos_id=-1, len_budget=None, workspace=None, diagnostics=True, prepare=False):
+    """Chain verification on the joint (position, token) space (SPOT App. B,
+    Eq. 10-14), gated per link between rejection sampling and coupled-noise
+    match when Gumbel rows are given (match where the drafter's confidence
+    at the link reaches tau).
+
+    tgt [B, K+1, V] target rows at each link's position s*; drf [B, K, V]
+    drafter rows at s*; pos_star [B, K+1]; prop_pos, prop_tok [B, K];
+    q_pos_star [B, K] (the drafter's probability of s*); u_accept [B, K];
+    u_resample [B, K+1]; gumbel [B, K+1, V] float32 or None.  Outputs as
+    verify_rejection.
+    """
+    lib = _lib.load()
+    dev = tgt.device
+    B, K1, V = tgt.shape
+    K = K1 - 1
+    ts, tr = _rows3(tgt, "tgt")
+    dt = _dtype_code(tgt)
+    if drf.dtype != tgt.dtype or tuple(drf.shape) != (B, K, V):
+        raise ValueError("drf must be [B, K, V] with the dtype of tgt")
+    ds, dr = _rows3(drf, "drf")
+    gs = gr = 0
+    if gumbel is not None:
+        if gumbel.dtype != torch.float32 or tuple(gumbel.shape) != (B, K + 1, V):
+            raise ValueError("gumbel must be float32 [B, K+1, V]")
+        gs, gr = _rows3(gumbel, "gumbel")
+    ps = _i32(pos_star, (B, K + 1), "pos_star", dev)
+    pp = _i32(prop_pos, (B, K), "prop_pos", dev)
+    d = _i32(prop_tok, (B, K), "prop_tok", dev)
+    c = _f32(q_pos_star, (B, K), "q_pos_star", dev)
+    n = _i32(draft_len, (B,), "draft_len", dev)
+    bud = _i32(len_budget, (B,), "len_budget", dev)
+    ua = _f32(u_accept, (B, K), "u_accept", dev)
+    ur = _f32(u_resample, (B, K + 1), "u_resample", dev)
+    out = {
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "out_tokens": torch.empty(B, K + 1, dtype=torch.int32, device=dev),
+        "num_out": torch.empty(B, dtype=torch.int32, device=dev),
+        "status": torch.empty(B, dtype=torch.int32, device=dev),
+    }
+    if diagnostics:
+        for k in ("p_draft", "q_draft", "alpha"):
+            out[k] = torch.empty(B, K, dtype=torch.float32, device=dev)
+        out["residual_mass"] = torch.empty(B, dtype=torch.float32, device=dev)
+    need = workspace_size(_lib.DBV_KIND_REJECTION, B, K, 0, V, dt)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    args = (B, K, V, dt, tgt.data_ptr(), ts, tr, drf.data_ptr(), ds, dr, _ptr(ps), _ptr(pp), _ptr(d), _ptr(c),
+            _ptr(n), float(temperature_target), float(temperature_draft), _ptr(gumbel), gs, gr, float(tau),
+            _ptr(ua), ur.data_ptr(), int(eos_id), _ptr(bud), out["accept_len"].data_ptr(),
+            out["out_tokens"].data_ptr(), out["num_out"].data_ptr(), _ptr(out.get("p_draft")),
+            _ptr(out.get("q_draft")), _ptr(out.get("alpha")), _ptr(out.get("residual_mass")),
+            out["status"].data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+    call = Prepared(lib.verify_spot_chain, "verify_spot_chain", args, out,
+                    (tgt, drf, gumbel, ps, pp, d, c, n, bud, ua, ur, ws))
+    return call if prepare else call()
 
 
 def verify_greedy_any_order(tgt, order, draft_tokens, num_active=None, positions=None,

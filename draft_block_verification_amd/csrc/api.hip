@@ -81,9 +81,22 @@ bool stream_fits(int64_t max_rows, int64_t V) {
   return max_rows < (int64_t(1) << 31) && max_rows * V < (int64_t(1) << 52);
 }
 
+// The acceptance rule of a sampling call and its parameters.
+struct Rule {
+  int rule = dbv::RULE_LINEAR;
+  float lam = 0.f;                      // linear rule
+  float delta = 0.f;                    // Cactus rule
+  const int32_t* pos_star = nullptr;    // joint-space chain
+  const int32_t* prop_pos = nullptr;
+  const float* qpos = nullptr;
+  const float* gumbel = nullptr;
+  int64_t gs = 0, grs = 0;
+  float tau = 0.f;
+};
+
 dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t ts, int64_t tr,
                          const void* drf, int64_t ds, int64_t dr, const int32_t* draft_tokens,
-                         const int32_t* draft_len, float tt, float td, int rule, float lam, float delta,
+                         const int32_t* draft_len, float tt, float td, const Rule& rl,
                          const float* u_accept,
                          const float* u_resample, int32_t eos_id, const int32_t* len_budget,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* num_out, float* p_draft,
@@ -91,8 +104,14 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
                          size_t ws_bytes, void* stream) {
   if (B < 0 || K < 0 || K > kMaxDraft || V < 1 || !dtype_ok(dtype)) return DBV_ERR_INVALID_ARG;
   if (V > dbv::kMaxSampleV) return DBV_ERR_UNSUPPORTED;
-  if (!temp_ok(tt) || !temp_ok(td) || !(lam >= 0.f && lam <= 1.f)) return DBV_ERR_INVALID_ARG;
-  if (!(std::isfinite(delta) && delta >= 0.f)) return DBV_ERR_INVALID_ARG;
+  if (!temp_ok(tt) || !temp_ok(td) || !(rl.lam >= 0.f && rl.lam <= 1.f)) return DBV_ERR_INVALID_ARG;
+  if (!(std::isfinite(rl.delta) && rl.delta >= 0.f)) return DBV_ERR_INVALID_ARG;
+  if (rl.rule == dbv::RULE_SPOT) {
+    if (rl.pos_star == nullptr || (K > 0 && (rl.prop_pos == nullptr || rl.qpos == nullptr)))
+      return DBV_ERR_INVALID_ARG;
+    if (std::isnan(rl.tau) || rl.gs < 0 || rl.grs < 0) return DBV_ERR_INVALID_ARG;
+    if (rl.gumbel && !aligned(rl.gumbel, 4)) return DBV_ERR_INVALID_ARG;
+  }
   if (ts < 0 || tr < 0 || ds < 0 || dr < 0) return DBV_ERR_INVALID_ARG;
   if (tgt == nullptr || u_resample == nullptr) return DBV_ERR_INVALID_ARG;
   if (K > 0 && (drf == nullptr || draft_tokens == nullptr || u_accept == nullptr)) return DBV_ERR_INVALID_ARG;
@@ -112,9 +131,13 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.drf = drf; a.ds = ds; a.dr = dr;
   a.draft_tokens = draft_tokens; a.draft_len = draft_len;
   a.kp = dbv::kLog2eHost / tt; a.kq = dbv::kLog2eHost / td;
-  a.rule = rule;
-  a.lam = lam;
-  a.delta = delta;
+  a.rule = rl.rule;
+  a.lam = rl.lam;
+  a.delta = rl.delta;
+  a.pos_star = rl.pos_star; a.prop_pos = rl.prop_pos; a.qpos = rl.qpos;
+  a.gumbel = rl.gumbel; a.gs = rl.gs; a.grs = rl.grs;
+  a.inv_t = 1.f / tt;
+  a.tau = rl.tau;
   a.u_accept = u_accept; a.u_resample = u_resample;
   a.eos = eos_id; a.budget = len_budget;
   a.accept_len = accept_len; a.out_tokens = out_tokens; a.num_out = num_out;
@@ -122,6 +145,7 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.status = status;
   char* w = static_cast<char*>(ws);
   a.stats = reinterpret_cast<float2*>(w + plan.off_stats);
+  a.gpart = reinterpret_cast<float2*>(w + plan.off_gpart);
   a.pre = reinterpret_cast<int32_t*>(w + plan.off_pre);
   a.rec = reinterpret_cast<dbv::DrawRecord*>(w + plan.off_rec);
   a.tmass = reinterpret_cast<float*>(w + plan.off_tmass);
@@ -130,6 +154,19 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.tpc = static_cast<int>(plan.tpc);
   a.chunks = static_cast<int>(plan.chunks);
   return dbv::launch_sample(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
+}
+
+Rule lenient_rule(float lam) {
+  Rule r;
+  r.lam = lam;
+  return r;
+}
+
+Rule cactus_rule(float delta) {
+  Rule r;
+  r.rule = dbv::RULE_CACTUS;
+  r.delta = delta;
+  return r;
 }
 
 }  // namespace
@@ -198,7 +235,7 @@ dbv_status verify_rejection(int B, int K, int V, dbv_dtype dtype, const void* tg
                             size_t ws_bytes, void* stream) {
   return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
                        drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft,
-                       dbv::RULE_LINEAR, 0.f, 0.f, u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft,
+                       Rule{}, u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft,
                        q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
 }
 
@@ -211,7 +248,8 @@ dbv_status verify_lenient(int B, int K, int V, dbv_dtype dtype, const void* tgt,
                           int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
                        drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft,
-                       dbv::RULE_LINEAR, lambda, 0.f, u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft,
+                       lenient_rule(lambda), u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens,
+                       num_out, p_draft,
                        q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
 }
 
@@ -224,8 +262,33 @@ dbv_status verify_cactus(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
                          int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
                        drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft,
-                       dbv::RULE_CACTUS, 0.f, delta, u_accept, u_resample, eos_id, len_budget, accept_len,
+                       cactus_rule(delta), u_accept, u_resample, eos_id, len_budget, accept_len,
                        out_tokens, num_out, p_draft, q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
+}
+
+dbv_status verify_spot_chain(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
+                             int64_t tgt_row_stride, const void* drf, int64_t drf_seq_stride,
+                             int64_t drf_row_stride, const int32_t* pos_star, const int32_t* prop_pos,
+                             const int32_t* prop_tok, const float* q_pos_star, const int32_t* draft_len,
+                             float temperature_target, float temperature_draft, const float* gumbel,
+                             int64_t g_seq_stride, int64_t g_row_stride, float tau, const float* u_accept,
+                             const float* u_resample, int32_t eos_id, const int32_t* len_budget,
+                             int32_t* accept_len, int32_t* out_tokens, int32_t* num_out, float* p_draft,
+                             float* q_draft, float* alpha, float* residual_mass, int32_t* status, void* ws,
+                             size_t ws_bytes, void* stream) {
+  Rule r;
+  r.rule = dbv::RULE_SPOT;
+  r.pos_star = pos_star;
+  r.prop_pos = prop_pos;
+  r.qpos = q_pos_star;
+  r.gumbel = gumbel;
+  r.gs = g_seq_stride;
+  r.grs = g_row_stride;
+  r.tau = tau;
+  return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
+                       drf_row_stride, prop_tok, draft_len, temperature_target, temperature_draft, r, u_accept,
+                       u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft, q_draft, alpha,
+                       residual_mass, status, ws, ws_bytes, stream);
 }
 
 dbv_status verify_greedy_any_order(int B, int U, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,

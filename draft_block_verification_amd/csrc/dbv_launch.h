@@ -25,7 +25,7 @@ struct GreedyArgs {
   int elem_bytes;                      // 2 (bf16) or 4 (fp32)
 };
 
-enum : int { RULE_LINEAR = 0, RULE_CACTUS = 1 };
+enum : int { RULE_LINEAR = 0, RULE_CACTUS = 1, RULE_SPOT = 2 };
 
 struct SampleArgs {
   int B, K, V;
@@ -34,9 +34,18 @@ struct SampleArgs {
   const int32_t* draft_tokens;
   const int32_t* draft_len;
   float kp, kq;                        // log2(e) / temperature
-  int rule;                            // RULE_LINEAR or RULE_CACTUS
+  int rule;                            // RULE_LINEAR, RULE_CACTUS or RULE_SPOT
   float lam;                           // linear rule: 0 = lossless
   float delta;                         // Cactus rule: KL budget
+  // Joint-space chain (RULE_SPOT): per link the target's position s*, the
+  // proposal's position, the drafter's probability of s*, and optionally
+  // the Gumbel rows of the target rows with the gate threshold.
+  const int32_t* pos_star;             // [B, K+1]
+  const int32_t* prop_pos;             // [B, K]
+  const float* qpos;                   // [B, K]
+  const float* gumbel; int64_t gs, grs;
+  float inv_t;                         // 1 / temperature of the target
+  float tau;
   const float* u_accept; const float* u_resample;
   int32_t eos;
   const int32_t* budget;
@@ -44,6 +53,7 @@ struct SampleArgs {
   float* p_draft; float* q_draft; float* alpha; float* residual_mass;
   int32_t* status;
   float2* stats;                       // per (slot, wave)
+  float2* gpart;                       // per (slot, wave), with Gumbel rows
   int32_t* pre;                        // [B + 1] first stream row per sequence
   DrawRecord* rec;                     // per sequence
   float* tmass;                        // per (sequence, draw tile)

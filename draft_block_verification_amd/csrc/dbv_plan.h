@@ -199,6 +199,8 @@ struct DrawRecord {
   float u;           // resample uniform of row h
   int excl;          // Cactus: the drafted token of row h, whose weight is
   float wexcl;       // wexcl = [gamma - q(d)]_+; -1 for the linear rule
+  int fixed;         // >= 0: the committed token is known (a coupled-noise
+                     // commit) and nothing is drawn; -1 otherwise
 };
 
 // Stream order: for each sequence b, target rows 0..n_b, then drafter rows
@@ -209,6 +211,8 @@ struct SamplePlan {
   int64_t tpc;         // draw tiles per mass-kernel group
   int64_t chunks;      // mass-kernel groups per sequence
   size_t off_stats;    // float2 {M, S} per (slot, wave)
+  size_t off_gpart;    // float2 {score, index-as-bits} per (slot, wave):
+                       // Gumbel argmax partials of target rows
   size_t off_pre;      // int32 [B + 1]: first stream row of each sequence
   size_t off_rec;      // DrawRecord per sequence
   size_t off_tmass;    // float per (sequence, draw tile)
@@ -222,7 +226,8 @@ inline SamplePlan plan_sample(int B, int K, int V, int64_t elem_bytes) {
   p.tpc = draw_tiles_per_chunk(B, V, elem_bytes);
   p.chunks = cdiv(p.tiles, p.tpc);
   p.off_stats = 0;
-  p.off_pre = partial_bytes(p.max_rows);
+  p.off_gpart = partial_bytes(p.max_rows);
+  p.off_pre = p.off_gpart + partial_bytes(p.max_rows);
   p.off_rec = p.off_pre + align256(static_cast<size_t>(B + 1) * 4);
   p.off_tmass = p.off_rec + align256(static_cast<size_t>(B) * sizeof(DrawRecord));
   p.bytes = p.off_tmass + align256(static_cast<size_t>(B) * p.tiles * 4);

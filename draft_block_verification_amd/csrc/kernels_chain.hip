@@ -166,7 +166,65 @@ __device__ __forceinline__ int sample_count(const SampleArgs& a, int b) {
   return bad ? 0 : 2 * n + 1;
 }
 
+// One pass over elements [v0, v1) of a target row and its Gumbel row: the
+// softmax statistics of x and the lowest-index argmax of x/T + g.  A Gumbel
+// row whose alignment differs from the logits' is read element by element.
 template <int DT>
+__device__ void stats_and_gumbel(const char* xr, const float* gr, int64_t v0, int64_t v1, float inv_t,
+                                 SoftmaxStats& st, ArgmaxPick& pk) {
+  using E = Elem<DT>;
+  constexpr int W = E::kVec;
+  constexpr int GV = W / 4;  // 16-byte Gumbel loads per logit vector
+  const int t = threadIdx.x;
+  auto one = [&](int64_t j) {
+    float x[1] = {E::load1(xr, j)};
+    float sc[1] = {__builtin_fmaf(x[0], inv_t, gr[j])};
+    st.template absorb<1>(x);
+    pk.group<1>(sc, j);
+  };
+  if (v1 <= v0) return;
+  const uintptr_t ax = reinterpret_cast<uintptr_t>(xr + v0 * E::kBytes);
+  int64_t head = static_cast<int64_t>(((16u - (ax & 15u)) & 15u) / E::kBytes);
+  if (head > v1 - v0) head = v1 - v0;
+  const int64_t a0 = v0 + head;
+  if ((reinterpret_cast<uintptr_t>(gr + a0) & 15u) != 0) {
+    for (int64_t j = v0 + t; j < v1; j += kBlock) one(j);
+    return;
+  }
+  const int64_t nvec = (v1 - a0) / W;
+  const int64_t a1 = a0 + nvec * W;
+  if (t < head) one(v0 + t);
+  const char* xb = xr + a0 * E::kBytes;
+  const char* gb = reinterpret_cast<const char*>(gr + a0);
+  for (int64_t i = t; i < nvec; i += 2 * kBlock) {
+    const bool two = i + kBlock < nvec;
+    u32x4 xv[2], g[2][GV];
+    xv[0] = load16(xb + i * 16);
+#pragma unroll
+    for (int q = 0; q < GV; ++q) g[0][q] = load16(gb + (i * W + q * 4) * 4);
+    if (two) {
+      xv[1] = load16(xb + (i + kBlock) * 16);
+#pragma unroll
+      for (int q = 0; q < GV; ++q) g[1][q] = load16(gb + ((i + kBlock) * W + q * 4) * 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && !two) break;
+      float x[W], sc[W];
+      E::unpack(xv[u], x);
+#pragma unroll
+      for (int j = 0; j < W; ++j) sc[j] = __builtin_fmaf(x[j], inv_t, __uint_as_float(g[u][j / 4][j % 4]));
+      st.template absorb<W>(x);
+      pk.group<W>(sc, a0 + (i + u * kBlock) * W);
+    }
+  }
+  if (a1 + t < v1) one(a1 + t);
+}
+
+// GUM: target rows are read with their Gumbel rows (joint-space chain with
+// coupled-noise links).
+template <int DT, bool GUM>
 __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
   __shared__ int s_pre[kSeqBlocks + 1];
   __shared__ int s_w[kWaves];
@@ -188,7 +246,18 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
                : static_cast<const char*>(a.drf) +
                      (static_cast<int64_t>(b) * a.ds + static_cast<int64_t>(j - n - 1) * a.dr) * Elem<DT>::kBytes;
     SoftmaxStats st(k);
-    stream_row<DT, kUnroll>(rowp, v0, v1, st);
+    if (GUM && target) {
+      ArgmaxPick pk;
+      stats_and_gumbel<DT>(rowp, a.gumbel + b * a.gs + static_cast<int64_t>(j) * a.grs, v0, v1, a.inv_t, st, pk);
+      float v = pk.best;
+      int ii = static_cast<int>(pk.bidx);
+      int nan = pk.nan ? 1 : 0;
+      wave_argmax(v, ii, nan);
+      if (lane_id() == 0)
+        a.gpart[(r + g) * kWaves + wave_id()] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
+    } else {
+      stream_row<DT, kUnroll>(rowp, v0, v1, st);
+    }
     float M = st.M, S = st.S;
     wave_stats(M, S, k);
     if (lane_id() == 0) a.stats[(r + g) * kWaves + wave_id()] = make_float2(M, S);
@@ -343,9 +412,10 @@ __device__ __forceinline__ float group_exclusive_scan_f(float v, float& total, f
 struct DecideLds {
   float Mp[kMaxDraft + 1], Sp[kMaxDraft + 1];
   float Mq[kMaxDraft], Sq[kMaxDraft];
+  int g[kMaxDraft + 1];      // joint-space chain: Gumbel argmax of target rows
   int st, h;
-  int dh;
-  float ph, pth, qh;
+  int dh, modeh;
+  float ph, pth, qh, ch;
 };
 
 // The decision of sequence b by a group of NT threads:
@@ -368,19 +438,31 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
   const int p0 = a.pre[b];
   const int R = a.pre[a.B];
   const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
-  int di[DPT];
-  float ui[DPT], xi[DPT], yi[DPT];
+  const bool spot = a.rule == RULE_SPOT;
+  int di[DPT], psk[DPT], ppk[DPT];
+  float ui[DPT], xi[DPT], yi[DPT], ck[DPT];
 #pragma unroll
   for (int k = 0; k < DPT; ++k) {
     const int i = t + k * NT;
+    const int64_t o = static_cast<int64_t>(b) * a.K + i;
     di[k] = i < a.K ? d[i] : 0;
-    ui[k] = i < a.K ? a.u_accept[static_cast<int64_t>(b) * a.K + i] : 0.f;
+    ui[k] = i < a.K ? a.u_accept[o] : 0.f;
+    psk[k] = ppk[k] = 0;
+    ck[k] = 0.f;
+    if (spot) {
+      // pos_star covers links 0..K (the bonus row's position included).
+      psk[k] = i <= a.K ? a.pos_star[static_cast<int64_t>(b) * (a.K + 1) + i] : 0;
+      ppk[k] = i < a.K ? a.prop_pos[o] : 0;
+      ck[k] = i < a.K ? a.qpos[o] : 0.f;
+    }
   }
   int st = 0;
 #pragma unroll
   for (int k = 0; k < DPT; ++k) {
     const int i = t + k * NT;
     xi[k] = yi[k] = 0.f;
+    if (spot && i < n && psk[k] < 0) st |= SEQ_BAD_INPUT;
+    if (spot && i < n && !(ck[k] >= 0.f && ck[k] <= 1.f)) st |= SEQ_BAD_INPUT;
     if (i < n) {
       if (di[k] < 0 || di[k] >= a.V) {
         st |= SEQ_BAD_INPUT;
@@ -391,7 +473,9 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
     }
   }
   if (t == 0) {
-    s.st = (nbad || budget < 0) ? SEQ_BAD_INPUT : 0;
+    // pos_star of the bonus row n (rows 0..n-1 are checked with their links)
+    const bool bad_star = spot && !nbad && a.pos_star[static_cast<int64_t>(b) * (a.K + 1) + n] < 0;
+    s.st = (nbad || budget < 0 || bad_star) ? SEQ_BAD_INPUT : 0;
     s.h = n;
   }
   __syncthreads();
@@ -421,6 +505,18 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
           s.Mq[r] = M; s.Sq[r] = S;
           st |= stats_status(M, S);
         });
+    if (spot && a.gumbel)
+      combine_rows_pick<NT>(
+          n + 1, a.gpart,
+          [&](int r, int64_t& first_slot, int64_t& cnt) {
+            split_row_slots(f, p0 + r, first_slot, cnt);
+            first_slot *= kWaves;
+            cnt *= kWaves;
+          },
+          [&](int r, float v, int idx, int nan) {
+            s.g[r] = idx;
+            st |= nan ? SEQ_NONFINITE : max_status(v);
+          });
   }
   if (st) atomicOr(&s.st, st);
   __syncthreads();
@@ -449,18 +545,40 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
   // Acceptance tests: accept d_i iff u_i * q_i(d_i) < p~_i(d_i).  Linear
   // rule: p~(d) = (1 - lambda) p(d) + lambda q(d).  Cactus rule:
   // p~(d) = gamma(p(d), delta).
+  // Joint-space chain: q(z~) = c qhat(v~) on s*; a proposal elsewhere is
+  // rejected (alpha = 0).  A link whose drafter confidence max qhat = 1/S
+  // reaches tau (with Gumbel rows) is verified by coupled-noise match.
   float pk[DPT], ptk[DPT], qk[DPT];
+  int mk[DPT];
 #pragma unroll
   for (int k = 0; k < DPT; ++k) {
     const int i = t + k * NT;
     float p = 0.f, q = 0.f, pt = 0.f, al = 0.f;
+    mk[k] = 0;
     if (i < n) {
       p = fast_exp2(__builtin_fmaf(xi[k], a.kp, -s.Mp[i] * a.kp)) / s.Sp[i];
       q = fast_exp2(__builtin_fmaf(yi[k], a.kq, -s.Mq[i] * a.kq)) / s.Sq[i];
-      pt = a.rule == RULE_CACTUS ? cactus_gamma(p, a.delta) : (1.f - a.lam) * p + a.lam * q;
-      if (q == 0.f && pt > 0.f) atomicOr(&s.st, SEQ_Q_ZERO);
-      al = q > 0.f ? fminf(1.f, pt / q) : (pt > 0.f ? 1.f : 0.f);
-      if (!(ui[k] * q < pt)) atomicMin(&s.h, i);
+      bool acc;
+      if (spot) {
+        const bool on = ppk[k] == psk[k];
+        mk[k] = (a.gumbel && 1.f / s.Sq[i] >= a.tau) ? 1 : 0;
+        q *= ck[k];
+        pt = p;
+        if (mk[k]) {
+          acc = on && di[k] == s.g[i];
+          al = acc ? 1.f : 0.f;
+        } else {
+          if (on && q == 0.f && p > 0.f) atomicOr(&s.st, SEQ_Q_ZERO);
+          al = on ? (q > 0.f ? fminf(1.f, p / q) : (p > 0.f ? 1.f : 0.f)) : 0.f;
+          acc = on && ui[k] * q < p;
+        }
+      } else {
+        pt = a.rule == RULE_CACTUS ? cactus_gamma(p, a.delta) : (1.f - a.lam) * p + a.lam * q;
+        if (q == 0.f && pt > 0.f) atomicOr(&s.st, SEQ_Q_ZERO);
+        al = q > 0.f ? fminf(1.f, pt / q) : (pt > 0.f ? 1.f : 0.f);
+        acc = ui[k] * q < pt;
+      }
+      if (!acc) atomicMin(&s.h, i);
     }
     pk[k] = p;
     ptk[k] = pt;
@@ -476,8 +594,8 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
   // Uniform across the group: keeps the row addresses in scalar registers.
   const int h = __builtin_amdgcn_readfirstlane(s.h);
   const bool resid = h < n;
-  if (resid && a.rule == RULE_CACTUS) {
-    // The owner of draft h shares its token and probabilities.
+  if (resid && a.rule != RULE_LINEAR) {
+    // The owner of draft h shares its token, probabilities and verifier.
 #pragma unroll
     for (int k = 0; k < DPT; ++k)
       if (t + k * NT == h) {
@@ -485,6 +603,8 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
         s.ph = pk[k];
         s.pth = ptk[k];
         s.qh = qk[k];
+        s.modeh = mk[k];
+        s.ch = ck[k];
       }
     __syncthreads();
   }
@@ -498,6 +618,17 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
   rec.u = a.u_resample[static_cast<int64_t>(b) * (a.K + 1) + h];
   rec.excl = -1;
   rec.wexcl = 0.f;
+  rec.fixed = -1;
+  if (spot) {
+    if (resid ? s.modeh != 0 : a.gumbel != nullptr) {
+      // A match link's rejection, or the bonus with Gumbel rows: the commit
+      // is the target's coupled-noise token; nothing is drawn.
+      rec.fixed = s.g[h];
+      rec.resid = 0;
+    } else if (resid) {
+      rec.isq *= s.ch;   // residual [p - c qhat]_+
+    }
+  }
   if (resid && a.rule == RULE_CACTUS) {
     // p~(v) = (1 - gamma) / (1 - p(d)) p(v) for v != d, p~(d) = gamma.
     const float ph = s.ph;
@@ -541,7 +672,7 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   const int c = blockIdx.x - b * a.chunks;
   const DrawRecord rec = draw_decide<DT, kBlock>(a, b, c == 0, s);
   if (c == 0 && threadIdx.x == 0) a.rec[b] = rec;
-  if (rec.status & SEQ_ERROR_MASK) return;
+  if ((rec.status & SEQ_ERROR_MASK) || rec.fixed >= 0) return;
   const char *xr, *yr;
   draw_rows<DT>(a, b, rec.h, rec.resid != 0, xr, yr);
   const bool vec = ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0;
@@ -621,9 +752,10 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
     }
     __syncthreads();
   };
-  locate(m0);
+  const bool draw = rec.fixed < 0;   // uniform across the group
+  if (draw) locate(m0);
   const float Zres = resid0 ? s.Z : 0.f;
-  if (resid0 && !(s.Z > 0.f)) {
+  if (draw && resid0 && !(s.Z > 0.f)) {
     // Residual mass vanished in float32 (p == q up to rounding): draw from p
     // with the same uniform instead, and flag it.  (This group recomputes
     // the tile masses of p alone; the case has probability zero in exact
@@ -648,7 +780,9 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
   // Wave 0 rescans the chosen tile in vocabulary order: lane l holds the
   // weights of the tile's l-th vector; a wave scan gives each lane the mass
   // before its vector.
-  if (wv == 0) {
+  if (!draw) {
+    if (t == 0) s.pick = rec.fixed;
+  } else if (wv == 0) {
     const int ct = __builtin_amdgcn_readfirstlane(s.cs);
     const int64_t e0 = static_cast<int64_t>(ct) * TE + lane * E::kVec;
     float wt[E::kVec];
@@ -749,7 +883,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_fused(SampleArgs a) {
   draw_rows<DT>(a, b, rec.h, rec.resid != 0, xr, yr);
   const bool vec = ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0;
   const int ntiles = a.tiles;
-  tile_masses<DT, kDrawWaves, 8>(xr, yr, a.V, 0, ntiles, vec, draw_weight(a, rec), s.tile);
+  if (rec.fixed < 0) tile_masses<DT, kDrawWaves, 8>(xr, yr, a.V, 0, ntiles, vec, draw_weight(a, rec), s.tile);
   __syncthreads();
   const int q = static_cast<int>(cdiv(ntiles, kDrawThreads));
   float m0[kDrawTilesPerThread];
@@ -777,7 +911,9 @@ bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const Tim
 
 bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
   const bool bf = dtype == DT_BF16;
-  if (!launch(bf ? fn(k_sample_rows<DT_BF16>) : fn(k_sample_rows<DT_F32>), a.grid, stream, a, ev)) return false;
+  const void* rows = a.gumbel ? (bf ? fn(k_sample_rows<DT_BF16, true>) : fn(k_sample_rows<DT_F32, true>))
+                              : (bf ? fn(k_sample_rows<DT_BF16, false>) : fn(k_sample_rows<DT_F32, false>));
+  if (!launch(rows, a.grid, stream, a, ev)) return false;
   if (a.tiles <= kFusedDrawTiles)
     return launch_threads(bf ? fn(k_draw_fused<DT_BF16>) : fn(k_draw_fused<DT_F32>), a.B, kDrawThreads, stream, a);
   return launch(bf ? fn(k_draw_mass<DT_BF16>) : fn(k_draw_mass<DT_F32>), static_cast<int64_t>(a.B) * a.chunks,

@@ -9,7 +9,9 @@
  * linear lenient rule, or shared-Gumbel state equality over a draft tree),
  * finds the longest accepted prefix (or tree path) and draws the correction
  * or bonus token from supplied uniforms.  verify_cactus adds the modified
- * Cactus acceptance rule.
+ * Cactus acceptance rule, verify_spot_chain chain verification on the joint
+ * (position, token) space and verify_greedy_any_order any-order greedy
+ * verification.
  *
  * Sources (pages by title):
  *   [PSS]  "One Call Ahead: Packed Self-Speculative Decoding with Diffusion
@@ -18,7 +20,8 @@
  *          verification), App. D.1 (packed row layout).
  *   [SPOT] "On the SPOT: Enhancing Speculative Decoding for Diffusion Language
  *          Models via Commit-Order Prediction" -- Sec. 4.1, Sec. 4.3,
- *          App. A.1 (formal decoding model), App. A.3 (Eq. 5-7).
+ *          App. A.1 (formal decoding model), App. A.3 (Eq. 5-7), App. B
+ *          (Eq. 10-14, Proposition 3), Table 22 (regime law).
  *   [TT]   "Speculative Diffusion is a Tale of Two Tradeoffs" -- Sec. 2
  *          (Eq. 1-5, Theorem 1), Sec. 3.2 (Algorithm 1), App. E (modified
  *          Cactus, Eq. 17-18).
@@ -90,7 +93,7 @@ enum {
 /* Workspace kinds for verify_workspace_size. */
 typedef enum {
   DBV_KIND_GREEDY = 0,
-  DBV_KIND_REJECTION = 1, /* also verify_lenient and verify_cactus */
+  DBV_KIND_REJECTION = 1, /* also verify_lenient, verify_cactus, verify_spot_chain */
   DBV_KIND_TREE = 2,
   DBV_KIND_ANY_ORDER = 3  /* K_or_S = U (window), L ignored */
 } dbv_kind;
@@ -202,6 +205,54 @@ dbv_status verify_cactus(int B, int K, int V, dbv_dtype dtype,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
                          float* p_draft, float* q_draft, float* alpha, float* residual_mass,
                          int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * verify_spot_chain -- chain verification on the joint (position, token)
+ * space ([SPOT] App. B, Eq. 10-14 and Proposition 3), optionally gated
+ * per link between rejection sampling and coupled-noise match.  Link k
+ * (k = 0..n_b-1) sits at verified state y_k; the target commits at position
+ * s*_k = pos_star[b, k] with token law p_k = softmax(tgt row k /
+ * temperature_target) (Eq. 10); the drafter proposed (prop_pos[b, k],
+ * prop_tok[b, k]) from q_k(s, v) = q_pos_k(s) qhat_{k,s}(v) (Eq. 12), where
+ * drf row k holds the drafter's logits at position s*_k (qhat =
+ * softmax(drf row / temperature_draft)) and q_pos_star[b, k] = q_pos_k(s*_k)
+ * (float32 in [0, 1]).  Row n_b of tgt (position pos_star[b, n_b]) is the
+ * bonus row.
+ *   Rejection sampling (Eq. 13-14): a proposal off s*_k is rejected; on
+ *   s*_k accept iff u_accept < min(1, p_k(v) / (c_k qhat(v))), c_k =
+ *   q_pos_star; a rejected link commits at s*_k a draw from
+ *   normalize([p_k - c_k qhat]_+) with u_resample[b, k].
+ *   Coupled-noise match ([SPOT] Sec. 4.1): with Gumbel rows (gumbel[b, k, :]
+ *   float32 at element offset b*g_seq_stride + k*g_row_stride, the shared
+ *   noise of position s*_k) a link whose drafter confidence max_v qhat(v)
+ *   is >= tau accepts iff the proposal is (s*_k, argmax_v(x_v/T + g_v)); a
+ *   rejected match link commits that argmax.  tau > 1 disables match;
+ *   gumbel = NULL means rejection sampling on every link.
+ *   The bonus after n_b accepted links is the Gumbel argmax of row n_b when
+ *   Gumbel rows are given, else a draw from p_{n_b} with u_resample[b, n_b].
+ * The committed position of output i is pos_star[b, i].  out_tokens, the
+ * ending condition, accept_len, num_out and status as verify_rejection;
+ * p_draft = p_k(v), q_draft = c_k qhat(v), alpha = the link's acceptance
+ * probability (0 off s*_k; 1 or 0 for a match link), residual_mass = the
+ * sum of [p - c qhat]_+ at a rejected rejection-sampling link (0 otherwise).
+ * Bad input (DBV_SEQ_BAD_INPUT): q_pos_star outside [0, 1], pos_star < 0 at
+ * a link or the bonus row, a proposal token outside [0, V).  With Gumbel
+ * rows, every row 0..n_b is read with its Gumbel row and their score rows
+ * obey the logit-row rule.  tau must not be NaN.  Workspace kind:
+ * DBV_KIND_REJECTION.
+ */
+dbv_status verify_spot_chain(int B, int K, int V, dbv_dtype dtype,
+                             const void* tgt, int64_t tgt_seq_stride, int64_t tgt_row_stride,
+                             const void* drf, int64_t drf_seq_stride, int64_t drf_row_stride,
+                             const int32_t* pos_star, const int32_t* prop_pos, const int32_t* prop_tok,
+                             const float* q_pos_star, const int32_t* draft_len,
+                             float temperature_target, float temperature_draft,
+                             const float* gumbel, int64_t g_seq_stride, int64_t g_row_stride, float tau,
+                             const float* u_accept, const float* u_resample,
+                             int32_t eos_id, const int32_t* len_budget,
+                             int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
+                             float* p_draft, float* q_draft, float* alpha, float* residual_mass,
+                             int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * verify_greedy_any_order -- one any-order greedy verification call

@@ -149,9 +149,10 @@ def verify_spot_chain(tgt, drf, pos_star, prop_pos, prop_tok, q_pos_star, draft_
         for i in range(n):
             status |= row_status(drf[b, i])
         scores = []
-        if G is not None and not (status & STATUS_ERROR_MASK):
+        if G is not None:
             for i in range(rows_read):
-                s = _gumbel_scores(tgt[b, i], G[b, i], t_target)
+                with np.errstate(invalid="ignore", over="ignore"):
+                    s = _gumbel_scores(tgt[b, i], G[b, i], t_target)
                 status |= row_status(s)
                 scores.append(s)
         if status & STATUS_ERROR_MASK:

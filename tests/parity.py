@@ -198,3 +198,97 @@ def check_tree(g, x, o, dtype_name, temperature, seqs=None):
         if pl_g[b] == o["path_len"][j]:
             near["exact_path"] += 1
     return near
+
+
+def check_spot(g, x, o, t_target, t_draft, tau, dtype_name, eos_id=-1, len_budget=None, seqs=None):
+    """Joint-space chain outputs (rejection sampling and the gated hybrid)
+    against the oracle, with margin accounting as check_sampling.  A link
+    whose drafter confidence lies within the probability tolerance of tau
+    may take the other verifier on the GPU: such a sequence is counted as
+    near-margin and its downstream outputs are not compared.
+
+    x: inputs as float64 / int64 numpy (tgt, drf, pos_star, prop_pos,
+    prop_tok, q_pos_star, draft_len, u_accept, u_resample, gumbel or None).
+    """
+    rtol = PROB_RTOL[dtype_name]
+    near = Counter()
+    st_g, acc_g, out_g, num_g = (npi(g[k]) for k in ("status", "accept_len", "out_tokens", "num_out"))
+    pd_g, qd_g, al_g = (np64(g[k]) for k in ("p_draft", "q_draft", "alpha"))
+    rm_g = np64(g["residual_mass"])
+    B = len(st_g) if seqs is None else len(seqs)
+    K = x["tgt"].shape[1] - 1
+    G = x.get("gumbel")
+    for j in range(B):
+        b = j if seqs is None else seqs[j]
+        so, sg = int(o["status"][j]), int(st_g[b])
+        assert (sg & oracle.STATUS_ERROR_MASK) == (so & oracle.STATUS_ERROR_MASK), (b, sg, so)
+        assert (sg & oracle.STATUS_Q_ZERO) == (so & oracle.STATUS_Q_ZERO), (b, sg, so)
+        if (sg ^ so) & oracle.STATUS_Z_ZERO:
+            near["z_zero"] += 1
+        if so & oracle.STATUS_ERROR_MASK:
+            assert acc_g[b] == -1 and num_g[b] == 0 and (out_g[b] == -1).all(), b
+            continue
+        n = int(x["draft_len"][b])
+        d = [int(v) for v in x["prop_tok"][b, :n]]
+        for i in range(n):
+            assert _rel_ok(pd_g[b, i], o["p_draft"][j, i], rtol), ("p", b, i, pd_g[b, i], o["p_draft"][j, i])
+            assert _rel_ok(qd_g[b, i], o["q_draft"][j, i], rtol), ("q", b, i, qd_g[b, i], o["q_draft"][j, i])
+        for i in range(n, K):
+            assert pd_g[b, i] == 0 and qd_g[b, i] == 0 and al_g[b, i] == 0
+        h = int(acc_g[b])
+        assert 0 <= h <= n, (b, h, n)
+        if (o["gate_margin"][j, :min(h + 1, n)] < rtol).any():
+            near["gate"] += 1
+            continue
+        for i in range(n):
+            if o["mode"][j, i] == oracle.MODE_RS:
+                assert _rel_ok(al_g[b, i], o["alpha"][j, i], rtol), ("alpha", b, i)
+            elif al_g[b, i] != o["alpha"][j, i]:
+                assert o["accept_margin"][j, i] < NEAR_MARGIN, ("match alpha", b, i)
+        for i in range(h):
+            if not o["accept_bits"][j, i]:
+                assert o["accept_margin"][j, i] < NEAR_MARGIN, ("accept", b, i, o["accept_margin"][j, i])
+                near["accept"] += 1
+        if h < n and o["accept_bits"][j, h]:
+            assert o["accept_margin"][j, h] < NEAR_MARGIN, ("reject", b, h, o["accept_margin"][j, h])
+            near["accept"] += 1
+        # The commit at the GPU's row h.
+        p = oracle.tempered_softmax(x["tgt"][b, h], t_target)
+        Zr = 0.0
+        if h < n and o["mode"][j, h] == oracle.MODE_RS or (h == n and G is None):
+            if h < n:
+                qh = oracle.tempered_softmax(x["drf"][b, h], t_draft)
+                w = oracle.rs_residual(p, qh, x["q_pos_star"][b, h])
+                Zr = float(np.sum(w))
+                if Zr <= 0.0:
+                    w = p
+            else:
+                w = p
+            u = float(x["u_resample"][b, h])
+            c_o, margin, Z = oracle.inverse_cdf(w, u)
+            bracket = lambda c_g: (0 <= c_g < len(w) and w[c_g] > 0 and  # noqa: E731
+                                   (np.cumsum(w)[c_g - 1] if c_g > 0 else 0.0) - NEAR_MARGIN * Z <= u * Z
+                                   < np.cumsum(w)[c_g] + NEAR_MARGIN * Z)
+        else:
+            with np.errstate(invalid="ignore"):
+                sc = np.asarray(x["tgt"][b, h], np.float64) / t_target + np.asarray(G[b, h], np.float64)
+            c_o = oracle.argmax_lowest(sc)
+            top = np.sort(sc)
+            margin = float(top[-1] - top[-2]) if len(top) > 1 else np.inf
+            bracket = lambda c_g: sc[c_g] >= top[-1] - NEAR_MARGIN  # noqa: E731
+        if num_g[b] > h:
+            c_g = int(out_g[b, h])
+            if c_g != c_o:
+                assert bracket(c_g) and margin < NEAR_MARGIN, ("commit", b, h, c_g, c_o, margin)
+                near["draw"] += 1
+        else:
+            c_g = c_o
+        C = d[:h] + [c_g]
+        bud = None if len_budget is None else int(len_budget[b])
+        a = oracle.stopping_index(C, h + 1, eos_id, bud)
+        assert num_g[b] == a, (b, num_g[b], a)
+        exp = np.full(K + 1, -1)
+        exp[:a] = C[:a]
+        np.testing.assert_array_equal(out_g[b], exp, err_msg=f"out_tokens seq {b}")
+        assert _rel_ok(rm_g[b], Zr, max(rtol, 1e-4), 1e-7), ("Z", b, rm_g[b], Zr)
+    return near

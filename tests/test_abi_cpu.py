@@ -107,6 +107,18 @@ def _tree(lib, **kw):
                                   o, o, a["ws"], a["wsb"], a["stream"])
 
 
+def _spot(lib, **kw):
+    a = dict(B=2, K=3, V=100, dt=_lib.DBV_BF16, tgt=FAKE, ts=400, tr=100, drf=FAKE, ds=300, dr=100, ps=FAKE,
+             pp=FAKE, d=FAKE, c=FAKE, n=None, tt=1.0, td=1.0, g=FAKE, gs=400, gr=100, tau=0.6, ua=FAKE, ur=FAKE,
+             eos=-1, bud=None, o=FAKE, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    o = a["o"]
+    return lib.verify_spot_chain(a["B"], a["K"], a["V"], a["dt"], a["tgt"], a["ts"], a["tr"], a["drf"], a["ds"],
+                                 a["dr"], a["ps"], a["pp"], a["d"], a["c"], a["n"], a["tt"], a["td"], a["g"],
+                                 a["gs"], a["gr"], a["tau"], a["ua"], a["ur"], a["eos"], a["bud"], o, o, o, None,
+                                 None, None, None, o, a["ws"], a["wsb"], a["stream"])
+
+
 def _any_order(lib, **kw):
     a = dict(B=2, U=4, V=100, dt=_lib.DBV_BF16, tgt=FAKE, ts=400, tr=100, order=FAKE, na=None, pos=None,
              d=FAKE, dr=FAKE, ds=400, drs=100, eos=-1, end=None, o=FAKE, nd=FAKE, st=FAKE, ws=FAKE,
@@ -167,6 +179,15 @@ def test_any_order_rejects_bad_args(lib, kw):
     assert _any_order(lib, **kw) == INVALID
 
 
+@pytest.mark.parametrize("kw", [
+    dict(B=-1), dict(K=-1), dict(K=5000), dict(V=0), dict(dt=3), dict(tgt=None), dict(ps=None), dict(pp=None),
+    dict(c=None), dict(d=None), dict(drf=None), dict(ua=None), dict(ur=None), dict(o=None), dict(tt=0.0),
+    dict(td=float("nan")), dict(tau=float("nan")), dict(gs=-1), dict(gr=-2), dict(g=FAKE + 2), dict(tgt=FAKE + 1),
+])
+def test_spot_chain_rejects_bad_args(lib, kw):
+    assert _spot(lib, **kw) == INVALID
+
+
 def test_workspace_errors(lib):
     assert _greedy(lib, ws=None) == _lib.DBV_ERR_WORKSPACE
     assert _greedy(lib, wsb=8) == _lib.DBV_ERR_WORKSPACE
@@ -174,6 +195,7 @@ def test_workspace_errors(lib):
     assert _reject(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
     assert _tree(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
     assert _any_order(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
+    assert _spot(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
 
 
 def test_optional_arguments_are_accepted(lib):
@@ -188,6 +210,8 @@ def test_optional_arguments_are_accepted(lib):
     assert _reject(lib, K=0, drf=None, d=None, ua=None) == nodev
     assert _any_order(lib, dr=None, nd=None, st=None) == nodev
     assert _any_order(lib, U=0, order=None, d=None) == nodev
+    assert _spot(lib, g=None, tau=float("inf")) == nodev
+    assert _spot(lib, K=0, drf=None, pp=None, d=None, c=None, ua=None) == nodev
 
 
 def test_valid_call_without_gpu_reports_no_device(lib):

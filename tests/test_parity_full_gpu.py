@@ -22,6 +22,8 @@ that hold at any size:
     sequence (one at a time), with and without the stopping rule
   * any-order greedy        B=64 U=32 V=131072 bf16 -- oracle on every
     sequence, with and without EOS / end position
+  * joint-space chain       B=16 K=8 V=151936 bf16, hybrid gate tau=0.6 and
+    rejection sampling only -- oracle on every sequence
 """
 
 import sys
@@ -33,7 +35,7 @@ import torch
 import draft_block_verification_amd as dbv
 import oracle
 import workloads
-from tests.parity import check_any_order, check_greedy, check_sampling, check_tree, np64, npi
+from tests.parity import check_any_order, check_greedy, check_sampling, check_spot, check_tree, np64, npi
 
 pytestmark = pytest.mark.gpu
 
@@ -249,3 +251,23 @@ def test_full_any_order(dev):
                 npi(x["draft_tokens"][sl]), np64(x["draft_rows"][sl]), eos, None if end is None else npi(end[sl]))
             check_any_order({k: v[sl] for k, v in g.items()}, o)
         say("eos", eos, "mean accepted", float(g["num_accepted"].float().mean()))
+
+
+# ------------------------------------------------------- joint-space chain ---
+
+def test_full_spot_chain(dev):
+    say("full joint-space chain B=16 K=8 V=151936 bf16")
+    x = workloads.config4_spot_chain()
+    xd = {k: v.to(dev) if torch.is_tensor(v) else v for k, v in x.items()}
+    for G in (xd["gumbel"], None):
+        g = dbv.verify_spot_chain(xd["tgt"], xd["drf"], xd["pos_star"], xd["prop_pos"], xd["prop_tok"],
+                                  xd["q_pos_star"], xd["u_accept"], xd["u_resample"], gumbel=G, tau=0.6,
+                                  draft_len=xd["draft_len"])
+        xn = {k: (np64(v) if v.is_floating_point() else npi(v)) if torch.is_tensor(v) else v for k, v in x.items()}
+        if G is None:
+            xn["gumbel"] = None
+        o = oracle.verify_spot_chain(xn["tgt"], xn["drf"], xn["pos_star"], xn["prop_pos"], xn["prop_tok"],
+                                     xn["q_pos_star"], xn["draft_len"], 1.0, 1.0, xn["u_accept"],
+                                     xn["u_resample"], gumbel=xn["gumbel"], tau=0.6)
+        near = check_spot(g, xn, o, 1.0, 1.0, 0.6, "bfloat16")
+        say("gumbel", G is not None, "mean h", float(o["accept_len"].mean()), "near", dict(near))

@@ -12,7 +12,7 @@ import torch
 import draft_block_verification_amd as dbv
 import oracle
 import workloads
-from tests.parity import check_any_order, check_greedy, check_sampling, check_tree, np64, npi
+from tests.parity import check_any_order, check_greedy, check_sampling, check_spot, check_tree, np64, npi
 
 pytestmark = pytest.mark.gpu
 
@@ -194,6 +194,86 @@ def test_cactus_edge_cases(dev):
                              xn["u_accept"], xn["u_resample"], eos_id=eos, len_budget=npi(bud))
     assert o["accept_len"][0] == 0 and o["status"][1] == oracle.STATUS_BAD_INPUT
     check_sampling(res, xn, o, 0.0, 1.0, 1.0, "float32", eos_id=eos, len_budget=npi(bud), delta=3.0)
+
+
+# ------------------------------------------------------- joint-space chain ---
+
+def _spot_np(x):
+    out = {k: (np64(v) if v.is_floating_point() else npi(v)) if torch.is_tensor(v) else v for k, v in x.items()}
+    return out
+
+
+def _spot_run(dev, x, tau=0.6, gumbel=True, eos_id=-1, len_budget=None):
+    G = x["gumbel"] if gumbel else None
+    g = dbv.verify_spot_chain(
+        x["tgt"].to(dev), x["drf"].to(dev), x["pos_star"].to(dev), x["prop_pos"].to(dev), x["prop_tok"].to(dev),
+        x["q_pos_star"].to(dev), x["u_accept"].to(dev), x["u_resample"].to(dev),
+        gumbel=None if G is None else G.to(dev), tau=tau, draft_len=x["draft_len"].to(dev),
+        temperature_target=x["temperature"], temperature_draft=x["temperature"], eos_id=eos_id,
+        len_budget=None if len_budget is None else len_budget.to(dev))
+    xn = _spot_np(dict(x, gumbel=G))
+    o = oracle.verify_spot_chain(xn["tgt"], xn["drf"], xn["pos_star"], xn["prop_pos"], xn["prop_tok"],
+                                 xn["q_pos_star"], xn["draft_len"], x["temperature"], x["temperature"],
+                                 xn["u_accept"], xn["u_resample"], gumbel=xn["gumbel"], tau=tau, eos_id=eos_id,
+                                 len_budget=None if len_budget is None else npi(len_budget))
+    return g, xn, o
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("V", [5003, 40000])
+@pytest.mark.parametrize("gumbel", [True, False])
+def test_spot_chain_parity(dev, dtype, V, gumbel):
+    say("spot chain", dtype, V, gumbel)
+    x = workloads.spot_chain_inputs(61, 24, 8, V, dtype, temperature=0.9, random_lengths=True, gumbel=gumbel)
+    g, xn, o = _spot_run(dev, x, gumbel=gumbel)
+    near = check_spot(g, xn, o, 0.9, 0.9, 0.6, str(dtype).split(".")[-1])
+    say("h", list(o["accept_len"]), "match links", int(o["mode"].sum()), "near", dict(near))
+    if gumbel:
+        assert 0 < o["mode"].sum() < o["mode"].size
+
+
+def test_spot_certain_positions_equal_rejection(dev):
+    say("spot = rejection")
+    x = workloads.spot_chain_inputs(62, 16, 6, 9001, torch.float32, random_lengths=True, gumbel=False)
+    x["prop_pos"] = x["pos_star"][:, :6].clone()
+    x["q_pos_star"] = torch.ones(16, 6)
+    g, xn, o = _spot_run(dev, x, gumbel=False)
+    r = dbv.verify_rejection(x["tgt"].to(dev), x["drf"].to(dev), x["prop_tok"].to(dev), x["u_accept"].to(dev),
+                             x["u_resample"].to(dev), draft_len=x["draft_len"].to(dev))
+    for k in ("accept_len", "out_tokens", "num_out", "status", "p_draft", "q_draft", "alpha", "residual_mass"):
+        assert torch.equal(g[k], r[k]), k
+    check_spot(g, xn, o, 1.0, 1.0, 0.6, "float32")
+
+
+def test_spot_edge_cases(dev):
+    say("spot edge cases")
+    B, K, V = 10, 5, 3001
+    x = workloads.spot_chain_inputs(63, B, K, V, torch.float32)
+    x["q_pos_star"][0, 1] = 1.5                 # c outside [0, 1]
+    x["q_pos_star"][1, 0] = float("nan")
+    x["pos_star"][2, K] = -1                    # bonus row position
+    x["pos_star"][3, 2] = -4
+    x["prop_tok"][4, 3] = V                     # token out of range
+    x["gumbel"][5, 2, 17] = float("nan")        # a Gumbel row that is read
+    x["draft_len"][6] = 0                       # bonus only
+    x["draft_len"][7] = 2
+    x["gumbel"][7, 4, 5] = float("nan")         # beyond n: never read
+    x["q_pos_star"][8] = 0.0                    # q = 0 at the proposal
+    g, xn, o = _spot_run(dev, x)
+    assert list(o["status"][:6]) == [1, 1, 1, 1, 1, 2], o["status"]
+    assert o["status"][7] == 0
+    check_spot(g, xn, o, 1.0, 1.0, 0.6, "float32")
+    for tau in (1.5, 0.0, -1.0):                # no match link / every link matches
+        g, xn, o = _spot_run(dev, x, tau=tau)
+        check_spot(g, xn, o, 1.0, 1.0, tau, "float32")
+    eos = int(x["prop_tok"][9, 0])
+    bud = torch.tensor([5, 5, 5, 5, 5, 5, 5, 5, 1, 0], dtype=torch.int32)
+    g, xn, o = _spot_run(dev, x, eos_id=eos, len_budget=bud)
+    check_spot(g, xn, o, 1.0, 1.0, 0.6, "float32", eos_id=eos, len_budget=npi(bud))
+    x0 = workloads.spot_chain_inputs(64, 4, 0, 777, torch.float32)   # K = 0
+    for gum in (True, False):
+        g, xn, o = _spot_run(dev, x0, gumbel=gum)
+        check_spot(g, xn, o, 1.0, 1.0, 0.6, "float32")
 
 
 # --------------------------------------------------------------- any-order ---

@@ -278,3 +278,57 @@ def config5_any_order(device="cpu"):
     """Any-order packed greedy verify: B=64 sequences, window U=32 slots,
     V=131072 bf16, verifier rows by rank plus drafter rows by slot."""
     return anyorder_inputs(6, 64, 32, 131072, torch.bfloat16, device=device)
+
+
+# ------------------------------------------------------- joint-space chain --
+
+def spot_chain_inputs(c, B, K, V, dtype=torch.bfloat16, sigma=1.0, temperature=1.0, on_star=0.85,
+                      gumbel=True, L=32, random_lengths=False, peak=20.0, device="cpu"):
+    """A drafted chain of K links per sequence on the joint (position, token)
+    space, with the target's rows at each link's position.
+
+    Target rows [B, K+1, V]: z ~ N(0, 3^2) + ``peak`` at one token (the
+    default makes the target's argmax carry most of the mass, as the pages
+    report for T <= 1).  Drafter rows at the same positions:
+    (z + N(0, sigma^2)) * m, the sharpness m in {0.5, 1, 1.5} per link (so
+    the drafter's confidence falls on both sides of typical gate
+    thresholds).  pos_star ~ U{0..L-1}; the proposal sits on pos_star with
+    probability ``on_star`` (else on the next position mod L); q_pos_star ~
+    U(0.3, 1); the proposed token is the drafter's Gumbel argmax under the
+    link's shared noise row (a coupled drafter), noise rows Gumbel(0, 1)
+    float32 [B, K+1, V] (None without ``gumbel``, then the proposal is a
+    draw from the drafter's softmax).
+    """
+    tgt = _planted_logits(c, (B, K + 1, V), peak, dtype, device)
+    noise = torch.randn(B, K, V, generator=_gen(c, 2, device), device=device) * sigma
+    m = torch.tensor([0.5, 1.0, 1.5], device=device)[
+        torch.randint(0, 3, (B, K, 1), generator=_gen(c, 6, device), device=device)]
+    drf = ((tgt[:, :K].float() + noise) * m).to(dtype)
+    g8 = _gen(c, 8, "cpu")
+    pos_star = torch.randint(0, L, (B, K + 1), generator=g8).to(torch.int32)
+    off = torch.rand(B, K, generator=g8) >= on_star
+    prop_pos = torch.where(off, (pos_star[:, :K] + 1) % L, pos_star[:, :K]).to(torch.int32)
+    q_pos = 0.3 + 0.7 * torch.rand(B, K, generator=g8)
+    G = gumbel_noise((B, K + 1, V), _gen(c, 9, device), device) if gumbel else None
+    if K > 0 and G is not None:
+        d = torch.argmax(drf.float() / temperature + G[:, :K], dim=-1)
+    elif K > 0:
+        probs = torch.softmax(drf.float().reshape(B * K, V) / temperature, dim=-1)
+        d = torch.multinomial(probs, 1, generator=_gen(c, 3, device)).reshape(B, K)
+    else:
+        d = torch.zeros(B, 0, dtype=torch.int64, device=device)
+    u_acc = torch.rand(B, K, generator=_gen(c, 4, device), device=device)
+    u_res = torch.rand(B, K + 1, generator=_gen(c, 5, device), device=device)
+    if random_lengths:
+        n = torch.randint(0, K + 1, (B,), generator=g8)
+    else:
+        n = torch.full((B,), K, dtype=torch.int64)
+    return dict(tgt=tgt, drf=drf, pos_star=pos_star, prop_pos=prop_pos, prop_tok=d.to(torch.int32).cpu(),
+                q_pos_star=q_pos, gumbel=G, u_accept=u_acc, u_resample=u_res, draft_len=n.to(torch.int32),
+                temperature=temperature)
+
+
+def config4_spot_chain(device="cpu"):
+    """Joint-space chain, hybrid gate: B=16 sequences, K=8 links, V=151936
+    bf16, sigma=1, T=1, Gumbel rows for every target row."""
+    return spot_chain_inputs(41, 16, 8, 151936, torch.bfloat16, device=device)
