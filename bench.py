@@ -15,6 +15,8 @@ and the correction or bonus draw.  Workloads (sizes of the pages' setups):
   c3c modified-Cactus verify      B=32 K=16 V=128256 bf16, sigma=1, T=1, delta=1
   c5ao any-order greedy verify    B=64 U=32 V=131072 bf16 (verifier rows by rank,
                                   drafter rows by slot)
+  c4s joint-space chain, hybrid   B=16 K=8 V=151936 bf16, T=1, tau=0.6, Gumbel
+                                  rows for every target row
 
 Inputs smaller than 1 GiB are replicated into several buffer sets and the
 steps rotate over them, so the 256 MiB last-level cache cannot serve them.
@@ -51,7 +53,9 @@ DESCR = {
     "c5": "packed greedy verify+draft B=64 K=32 V=131072 bf16",
     "c3c": "modified-Cactus verify B=32 K=16 V=128256 bf16 sigma=1 T=1 delta=1",
     "c5ao": "any-order greedy verify B=64 U=32 V=131072 bf16",
+    "c4s": "joint-space chain hybrid B=16 K=8 V=151936 bf16 T=1 tau=0.6",
 }
+SPOT_TAU = 0.6
 CACTUS_DELTA = 1.0
 
 
@@ -73,13 +77,20 @@ COPY_PROBE_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 
 
-def kernel_source_hash():
-    """Hash of the HIP sources: counter readings apply only to the kernels
-    they were taken on."""
+# The source file that defines each measured kernel; its counter readings
+# hold only for that file and the headers every kernel file includes.
+KERNEL_FILES = {"k_sample_rows": "kernels_chain.hip", "k_greedy_rows": "kernels_chain.hip",
+                "k_tree_conf": "kernels_tree.hip", "k_ao_rows": "kernels_anyorder.hip"}
+SHARED_HEADERS = ("dbv_device.h", "dbv_launch.h", "dbv_plan.h")
+
+
+def kernel_source_hash(kernel):
+    """Hash of the HIP sources of `kernel`: counter readings apply only to
+    the code they were taken on."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(HERE, "draft_block_verification_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in (KERNEL_FILES[kernel],) + SHARED_HEADERS:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -95,7 +106,7 @@ def measured_traffic(workload, kernel):
     except (OSError, ValueError):
         return None
     e = t.get("workloads", {}).get(workload)
-    if not e or e.get("kernel") != kernel or t.get("source_hash") != kernel_source_hash():
+    if not e or e.get("kernel") != kernel or e.get("source_hash") != kernel_source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
 
@@ -160,6 +171,25 @@ class Case:
                 self.calls.append(dbv.verify_greedy(p[:, :K + 1], x["draft_tokens"].to(dev),
                                                     x["draft_len"].to(dev), p[:, K + 1:], prepare=True))
             self.shape = dict(B=B, K=K, W=W, V=V)
+        elif name == "c4s":
+            x = workloads.config4_spot_chain()
+            B, K1, V = x["tgt"].shape
+            K = K1 - 1
+            n = x["draft_len"].long()
+            self.positions = int(n.sum())
+            # target rows 0..n with their float32 Gumbel rows, drafter rows 0..n-1
+            self.kernel_bytes = int(((n + 1) * V * (eb + 4) + n * V * eb).sum())
+            self.kernel = "k_sample_rows"
+            per_set = (x["tgt"].numel() + x["drf"].numel()) * eb + x["gumbel"].numel() * 4
+            self.cpu_inputs = x
+            self.calls = []
+            for _ in range(self._rotation(per_set)):
+                xd = {k: v.to(dev).clone() if torch.is_tensor(v) else v for k, v in x.items()}
+                self.calls.append(dbv.verify_spot_chain(
+                    xd["tgt"], xd["drf"], xd["pos_star"], xd["prop_pos"], xd["prop_tok"], xd["q_pos_star"],
+                    xd["u_accept"], xd["u_resample"], gumbel=xd["gumbel"], tau=SPOT_TAU, draft_len=xd["draft_len"],
+                    prepare=True))
+            self.shape = dict(B=B, K=K, V=V)
         elif name == "c5ao":
             x = workloads.config5_any_order()
             B, U, V = x["tgt"].shape
@@ -252,6 +282,22 @@ class Case:
                 if time.perf_counter() - t0 >= seconds:
                     break
             sample = f"{nb} of 64 sequences, {calls} oracle calls"
+        elif self.name == "c4s":
+            nb = 2
+            xs = {k: v[:nb] if torch.is_tensor(v) else v for k, v in x.items()}
+            args = [np64(xs["tgt"]), np64(xs["drf"]), npi(xs["pos_star"]), npi(xs["prop_pos"]),
+                    npi(xs["prop_tok"]), np64(xs["q_pos_star"]), npi(xs["draft_len"]), 1.0, 1.0,
+                    np64(xs["u_accept"]), np64(xs["u_resample"])]
+            G = np64(xs["gumbel"])
+            npos = int(xs["draft_len"].sum())
+            t0 = time.perf_counter()
+            while True:
+                oracle.verify_spot_chain(*args, gumbel=G, tau=SPOT_TAU)
+                done_pos += npos
+                calls += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            sample = f"{nb} of 16 sequences, {calls} oracle calls"
         elif self.name == "c5ao":
             nb = 4
             args = (np64(x["tgt"][:nb]), npi(x["order"][:nb]), npi(x["num_active"][:nb]),

@@ -1,5 +1,5 @@
 // Any-order greedy verification of one packed call (Packed-SS, App. C,
-// Algorithm 3, lines 6-15):
+// Algorithm 3, the verification steps of one iteration):
 //
 //   k_ao_plan      per sequence: checks the order (a permutation of the u
 //                  active slots), the slot positions (increasing) and the

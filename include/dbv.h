@@ -256,7 +256,7 @@ dbv_status verify_spot_chain(int B, int K, int V, dbv_dtype dtype,
 
 /*
  * verify_greedy_any_order -- one any-order greedy verification call
- * ([PSS] App. C, Algorithm 3, lines 6-15).  Per sequence b the call covers
+ * ([PSS] App. C, Algorithm 3, its verification steps).  Per sequence b the call covers
  * the u_b unresolved output positions of its active window, in textual order
  * ("slots" j = 0..u_b-1 at output positions pos[j]), checked in the order
  * pi chosen before the call (order[b, r] = the slot checked at rank r):

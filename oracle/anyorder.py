@@ -3,7 +3,7 @@ infrastructure).
 
 "One Call Ahead: Packed Self-Speculative Decoding with Diffusion Drafting",
 App. C (Any-Order Extension), Algorithm 3, the verification part of one
-iteration t (lines 6-15).  Per sequence the call sees the u unresolved
+iteration t.  Per sequence the call sees the u unresolved
 output positions of its active window, in textual order ("slots"
 j = 0..u-1, output positions pos[j]), an order pi over them chosen before
 the call (order[r] = the slot checked at rank r), the available draft tokens
@@ -11,14 +11,14 @@ the call (order[r] = the slot checked at rank r), the available draft tokens
 order (row r is the verifier at pi(r) given the drafts at earlier ranks,
 Eq. 8) and the drafter rows by slot.
 
-  kappa = leading ranks whose position has a draft            (line 6)
-  v_r   = argmax of verifier row r, r < min(kappa + 1, u)      (line 7, Eq. 8)
-  z_j   = argmax of drafter row j, j < u                        (line 8)
-  h     = leading ranks r < kappa with d(pi(r)) = v_r           (line 9)
-  A     = min(h + 1, u);  C = ((pos[pi(r)], v_r))_{r < A}       (line 10)
-  E'    = min({E} U {position of an EOS in C})                  (line 11)
-  C'    = the pairs of C at positions <= E'                     (line 12)
-  next draft: z_j for the slots j not in C with pos[j] <= E'    (lines 14-15)
+  kappa = leading ranks whose position has a draft
+  v_r   = argmax of verifier row r, r < min(kappa + 1, u)   (Eq. 8)
+  z_j   = argmax of drafter row j, j < u
+  h     = leading ranks r < kappa with d(pi(r)) = v_r
+  A     = min(h + 1, u);  C = ((pos[pi(r)], v_r))_{r < A}
+  E'    = min({E} U {position of an EOS in C})
+  C'    = the pairs of C at positions <= E'
+  next draft: z_j for the slots j not in C with pos[j] <= E'
 
 Readings (where the page is silent):
 * The verifier rows arrive in rank order (the order in which the packed call
