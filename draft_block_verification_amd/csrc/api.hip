@@ -119,7 +119,7 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   const size_t eb = elem_bytes(dtype);
   if (!aligned(tgt, eb) || (drf && !aligned(drf, eb))) return DBV_ERR_INVALID_ARG;
   const dbv::SamplePlan plan = dbv::plan_sample(B, K, V, static_cast<int64_t>(elem_bytes(dtype)));
-  if (!stream_fits(plan.max_rows, V)) return DBV_ERR_UNSUPPORTED;
+  if (!stream_fits(plan.max_vrows, V)) return DBV_ERR_UNSUPPORTED;
   dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
   if (s != DBV_OK) return s;
   if ((s = device_ready()) != DBV_OK) return s;
@@ -149,7 +149,9 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.pre = reinterpret_cast<int32_t*>(w + plan.off_pre);
   a.rec = reinterpret_cast<dbv::DrawRecord*>(w + plan.off_rec);
   a.tmass = reinterpret_cast<float*>(w + plan.off_tmass);
-  a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(eb), dbv::resident_groups());
+  const int64_t P = rl.gumbel ? dbv::gumbel_parts(static_cast<int64_t>(eb)) : 1;
+  a.grid = dbv::stream_grid(static_cast<int64_t>(B) * (P * (K + 1) + K), V, static_cast<int64_t>(eb),
+                            dbv::resident_groups());
   a.tiles = static_cast<int>(plan.tiles);
   a.tpc = static_cast<int>(plan.tpc);
   a.chunks = static_cast<int>(plan.chunks);

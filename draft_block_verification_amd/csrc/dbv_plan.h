@@ -204,9 +204,24 @@ struct DrawRecord {
 };
 
 // Stream order: for each sequence b, target rows 0..n_b, then drafter rows
-// 0..n_b-1.
+// 0..n_b-1.  With Gumbel rows each target row is cut into gumbel_parts(eb)
+// stream rows ("parts"), so that every stream row carries about the same
+// bytes: a target element then costs eb + 4 bytes against eb for a drafter
+// element.
+DBV_HD inline int gumbel_parts(int64_t elem_bytes) { return static_cast<int>((elem_bytes + 4) / elem_bytes); }
+
+// Element offset in target row of stream offset v (a multiple of 8 below V,
+// or V) in part k of P: parts are V_P = floor(V / 8P) * 8 elements wide, the
+// last takes the rest.  Monotone in v, so pieces stay contiguous.
+DBV_HD inline int64_t part_offset(int64_t V, int P, int k, int64_t v) {
+  const int64_t vp = V / (8 * P) * 8;
+  if (v >= V) return k + 1 < P ? (k + 1) * vp : V;
+  return k * vp + v / (8 * P) * 8;
+}
+
 struct SamplePlan {
   int64_t max_rows;    // B * (2K + 1)
+  int64_t max_vrows;   // B * (4K + 3): stream rows with Gumbel rows (<= 3 parts)
   int64_t tiles;       // draw tiles per row
   int64_t tpc;         // draw tiles per mass-kernel group
   int64_t chunks;      // mass-kernel groups per sequence
@@ -222,12 +237,13 @@ struct SamplePlan {
 inline SamplePlan plan_sample(int B, int K, int V, int64_t elem_bytes) {
   SamplePlan p{};
   p.max_rows = static_cast<int64_t>(B) * (2 * K + 1);
+  p.max_vrows = static_cast<int64_t>(B) * (4 * K + 3);
   p.tiles = draw_tiles(V, elem_bytes);
   p.tpc = draw_tiles_per_chunk(B, V, elem_bytes);
   p.chunks = cdiv(p.tiles, p.tpc);
   p.off_stats = 0;
-  p.off_gpart = partial_bytes(p.max_rows);
-  p.off_pre = p.off_gpart + partial_bytes(p.max_rows);
+  p.off_gpart = partial_bytes(p.max_vrows);
+  p.off_pre = p.off_gpart + partial_bytes(p.max_vrows);
   p.off_rec = p.off_pre + align256(static_cast<size_t>(B + 1) * 4);
   p.off_tmass = p.off_rec + align256(static_cast<size_t>(B) * sizeof(DrawRecord));
   p.bytes = p.off_tmass + align256(static_cast<size_t>(B) * p.tiles * 4);

@@ -158,23 +158,55 @@ __global__ __launch_bounds__(kBlock) void k_greedy_finalize(GreedyArgs a) {
 
 // ============================================================== sampling ===
 
-// Stream rows of sequence b: target rows 0..n_b, then drafter rows
-// 0..n_b-1; none for an invalid draft length.
-__device__ __forceinline__ int sample_count(const SampleArgs& a, int b) {
+// Stream rows of sequence b: target rows 0..n_b (P stream rows each), then
+// drafter rows 0..n_b-1; none for an invalid draft length.
+__device__ __forceinline__ int sample_count(const SampleArgs& a, int b, int P) {
   bool bad;
   const int n = draft_count(a.draft_len, b, a.K, bad);
-  return bad ? 0 : 2 * n + 1;
+  return bad ? 0 : P * (n + 1) + n;
 }
 
-// One pass over elements [v0, v1) of a target row and its Gumbel row: the
-// softmax statistics of x and the lowest-index argmax of x/T + g.  A Gumbel
-// row whose alignment differs from the logits' is read element by element.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Four consecutive logits as float32, from one 8-byte (bf16) or 16-byte
+// (fp32) nontemporal load.
 template <int DT>
+struct Quad;
+
+template <>
+struct Quad<DT_BF16> {
+  typedef u32x2 raw;
+  __device__ static __forceinline__ raw load(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  }
+  __device__ static __forceinline__ void unpack(raw w, float (&x)[4]) {
+    x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = __uint_as_float(w.y << 16); x[3] = __uint_as_float(w.y & 0xffff0000u);
+  }
+};
+
+template <>
+struct Quad<DT_F32> {
+  typedef u32x4 raw;
+  __device__ static __forceinline__ raw load(const char* p) { return load16(p); }
+  __device__ static __forceinline__ void unpack(raw w, float (&x)[4]) {
+    x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+  }
+};
+
+// One pass over elements [v0, v1) of a target row and its Gumbel row: the
+// softmax statistics of x and the lowest-index argmax of x/T + g.  Lane l
+// takes four consecutive elements per step, so both the logit loads (8 or
+// 16 bytes) and the Gumbel loads (16 bytes) are contiguous across the wave;
+// every lane keeps U steps in flight.  Rows whose logits and Gumbel values
+// cannot both be aligned are read element by element.
+template <int DT, int U>
 __device__ void stats_and_gumbel(const char* xr, const float* gr, int64_t v0, int64_t v1, float inv_t,
                                  SoftmaxStats& st, ArgmaxPick& pk) {
   using E = Elem<DT>;
-  constexpr int W = E::kVec;
-  constexpr int GV = W / 4;  // 16-byte Gumbel loads per logit vector
+  using Q = Quad<DT>;
+  constexpr int XB = 4 * E::kBytes;
   const int t = threadIdx.x;
   auto one = [&](int64_t j) {
     float x[1] = {E::load1(xr, j)};
@@ -182,43 +214,45 @@ __device__ void stats_and_gumbel(const char* xr, const float* gr, int64_t v0, in
     st.template absorb<1>(x);
     pk.group<1>(sc, j);
   };
+  auto use = [&](typename Q::raw xv, u32x4 g, int64_t idx) {
+    float x[4], sc[4];
+    Q::unpack(xv, x);
+    sc[0] = __builtin_fmaf(x[0], inv_t, __uint_as_float(g.x));
+    sc[1] = __builtin_fmaf(x[1], inv_t, __uint_as_float(g.y));
+    sc[2] = __builtin_fmaf(x[2], inv_t, __uint_as_float(g.z));
+    sc[3] = __builtin_fmaf(x[3], inv_t, __uint_as_float(g.w));
+    st.template absorb<4>(x);
+    pk.group<4>(sc, idx);
+  };
   if (v1 <= v0) return;
-  const uintptr_t ax = reinterpret_cast<uintptr_t>(xr + v0 * E::kBytes);
-  int64_t head = static_cast<int64_t>(((16u - (ax & 15u)) & 15u) / E::kBytes);
+  const uintptr_t ag = reinterpret_cast<uintptr_t>(gr + v0);
+  int64_t head = static_cast<int64_t>(((16u - (ag & 15u)) & 15u) / 4u);
   if (head > v1 - v0) head = v1 - v0;
   const int64_t a0 = v0 + head;
-  if ((reinterpret_cast<uintptr_t>(gr + a0) & 15u) != 0) {
+  if ((ag & 3u) != 0 || (reinterpret_cast<uintptr_t>(xr + a0 * E::kBytes) % XB) != 0) {
     for (int64_t j = v0 + t; j < v1; j += kBlock) one(j);
     return;
   }
-  const int64_t nvec = (v1 - a0) / W;
-  const int64_t a1 = a0 + nvec * W;
+  const int64_t nq = (v1 - a0) / 4;
+  const int64_t a1 = a0 + nq * 4;
   if (t < head) one(v0 + t);
   const char* xb = xr + a0 * E::kBytes;
   const char* gb = reinterpret_cast<const char*>(gr + a0);
-  for (int64_t i = t; i < nvec; i += 2 * kBlock) {
-    const bool two = i + kBlock < nvec;
-    u32x4 xv[2], g[2][GV];
-    xv[0] = load16(xb + i * 16);
+  int64_t i = t;
+  for (; i + (U - 1) * kBlock < nq; i += U * kBlock) {
+    typename Q::raw xv[U];
+    u32x4 g[U];
 #pragma unroll
-    for (int q = 0; q < GV; ++q) g[0][q] = load16(gb + (i * W + q * 4) * 4);
-    if (two) {
-      xv[1] = load16(xb + (i + kBlock) * 16);
-#pragma unroll
-      for (int q = 0; q < GV; ++q) g[1][q] = load16(gb + ((i + kBlock) * W + q * 4) * 4);
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = i + u * kBlock;
+      xv[u] = Q::load(xb + k * XB);
+      g[u] = load16(gb + k * 16);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (u == 1 && !two) break;
-      float x[W], sc[W];
-      E::unpack(xv[u], x);
-#pragma unroll
-      for (int j = 0; j < W; ++j) sc[j] = __builtin_fmaf(x[j], inv_t, __uint_as_float(g[u][j / 4][j % 4]));
-      st.template absorb<W>(x);
-      pk.group<W>(sc, a0 + (i + u * kBlock) * W);
-    }
+    for (int u = 0; u < U; ++u) use(xv[u], g[u], a0 + (i + u * kBlock) * 4);
   }
+  for (; i < nq; i += kBlock) use(Q::load(xb + i * XB), load16(gb + i * 16), a0 + i * 4);
   if (a1 + t < v1) one(a1 + t);
 }
 
@@ -228,40 +262,67 @@ template <int DT, bool GUM>
 __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
   __shared__ int s_pre[kSeqBlocks + 1];
   __shared__ int s_w[kWaves];
-  auto count = [&](int b) { return sample_count(a, b); };
+  constexpr int P = GUM ? (Elem<DT>::kBytes + 4) / Elem<DT>::kBytes : 1;
+  auto count = [&](int b) { return sample_count(a, b, P); };
   const SeqDir dir = build_seq_dir(a.B, count, s_pre, s_w);
   if (blockIdx.x == 0) write_seq_starts(dir, s_pre, a.B, count, a.pre);
   const FlatSplit f = make_split(s_pre[dir.nblk], a.V, Elem<DT>::kBytes, a.grid);
   const int64_t g = blockIdx.x;
   if (g >= f.G) return;
+  // With Gumbel rows, the parts of one target row that this group reads are
+  // accumulated together and written once, at slot (first stream row of the
+  // target row) + group.
+  SoftmaxStats acc(a.kp);
+  ArgmaxPick accp;
+  int64_t pend = -1;
+  auto flush = [&]() {
+    float M = acc.M, S = acc.S;
+    wave_stats(M, S, a.kp);
+    float v = accp.best;
+    int ii = static_cast<int>(accp.bidx);
+    int nan = accp.nan ? 1 : 0;
+    wave_argmax(v, ii, nan);
+    if (lane_id() == 0) {
+      a.stats[(pend + g) * kWaves + wave_id()] = make_float2(M, S);
+      a.gpart[(pend + g) * kWaves + wave_id()] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
+    }
+    acc = SoftmaxStats(a.kp);
+    accp = ArgmaxPick();
+    pend = -1;
+  };
   for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1) {
     int first, cnt;
     const int b = find_seq(dir, s_pre, static_cast<int>(r), count, first, cnt);
     const int j = static_cast<int>(r) - first;
-    const int n = (cnt - 1) / 2;
-    const bool target = j <= n;
+    const int n = (cnt - P) / (P + 1);
+    const bool target = j < P * (n + 1);
+    const int jt = j / P;   // target row of a target part
     const float k = target ? a.kp : a.kq;
     const char* rowp =
-        target ? static_cast<const char*>(a.tgt) + (static_cast<int64_t>(b) * a.ts + j * a.tr) * Elem<DT>::kBytes
+        target ? static_cast<const char*>(a.tgt) + (static_cast<int64_t>(b) * a.ts + jt * a.tr) * Elem<DT>::kBytes
                : static_cast<const char*>(a.drf) +
-                     (static_cast<int64_t>(b) * a.ds + static_cast<int64_t>(j - n - 1) * a.dr) * Elem<DT>::kBytes;
-    SoftmaxStats st(k);
+                     (static_cast<int64_t>(b) * a.ds + static_cast<int64_t>(j - P * (n + 1)) * a.dr) *
+                         Elem<DT>::kBytes;
     if (GUM && target) {
-      ArgmaxPick pk;
-      stats_and_gumbel<DT>(rowp, a.gumbel + b * a.gs + static_cast<int64_t>(j) * a.grs, v0, v1, a.inv_t, st, pk);
-      float v = pk.best;
-      int ii = static_cast<int>(pk.bidx);
-      int nan = pk.nan ? 1 : 0;
-      wave_argmax(v, ii, nan);
-      if (lane_id() == 0)
-        a.gpart[(r + g) * kWaves + wave_id()] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
-    } else {
-      stream_row<DT, kUnroll>(rowp, v0, v1, st);
+      const int part = j - jt * P;
+      const int64_t base = r - part;
+      if (pend != base) {
+        if (pend >= 0) flush();
+        pend = base;
+      }
+      stats_and_gumbel<DT, 2 * kUnroll>(rowp, a.gumbel + b * a.gs + static_cast<int64_t>(jt) * a.grs,
+                                    part_offset(a.V, P, part, v0), part_offset(a.V, P, part, v1), a.inv_t, acc,
+                                    accp);
+      return;
     }
+    if (GUM && pend >= 0) flush();
+    SoftmaxStats st(k);
+    stream_row<DT, kUnroll>(rowp, v0, v1, st);
     float M = st.M, S = st.S;
     wave_stats(M, S, k);
     if (lane_id() == 0) a.stats[(r + g) * kWaves + wave_id()] = make_float2(M, S);
   });
+  if (GUM && pend >= 0) flush();
 }
 
 // Per-element weight of the draw: residual [p~ - q]_+ or bonus exp2 weight.
@@ -480,24 +541,35 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
   }
   __syncthreads();
   if (!nbad) {
-    // Stream rows p0..p0+n: target rows 0..n (k = kp); p0+n+1..: drafter
+    // Stream rows from p0: target rows 0..n (k = kp), each in P parts when
+    // read with Gumbel rows (their partials are merged part by part: the
+    // thread that finishes row r is the same in every pass); then drafter
     // rows 0..n-1 (k = kq).
     const FlatSplit f = make_split(R, a.V, E::kBytes, a.grid);
-    combine_rows_stats<NT>(
-        n + 1, a.stats, a.kp,
-        [&](int r, int64_t& first_slot, int64_t& cnt) {
-          split_row_slots(f, p0 + r, first_slot, cnt);
-          first_slot *= kWaves;
-          cnt *= kWaves;
-        },
-        [&](int r, float M, float S) {
-          s.Mp[r] = M; s.Sp[r] = S;
-          st |= stats_status(M, S);
-        });
+    // With Gumbel rows a target row is P consecutive stream rows; each group
+    // that reads any of them wrote one partial at slot (first stream row of
+    // the target row) + group.
+    const int P = (spot && a.gumbel) ? gumbel_parts(E::kBytes) : 1;
+    auto tspan = [&](int r, int64_t& first_slot, int64_t& cnt) {
+      const int64_t v = p0 + static_cast<int64_t>(r) * P;
+      const int64_t glo = split_group(f, v * f.V);
+      const int64_t ghi = split_group(f, (v + P) * f.V - 1);
+      first_slot = (v + glo) * kWaves;
+      cnt = (ghi - glo + 1) * kWaves;
+    };
+    combine_rows_stats<NT>(n + 1, a.stats, a.kp, tspan, [&](int r, float M, float S) {
+      s.Mp[r] = M; s.Sp[r] = S;
+      st |= stats_status(M, S);
+    });
+    if (P > 1)
+      combine_rows_pick<NT>(n + 1, a.gpart, tspan, [&](int r, float v, int idx, int nan) {
+        s.g[r] = idx;
+        st |= nan ? SEQ_NONFINITE : max_status(v);
+      });
     combine_rows_stats<NT>(
         n, a.stats, a.kq,
         [&](int r, int64_t& first_slot, int64_t& cnt) {
-          split_row_slots(f, p0 + n + 1 + r, first_slot, cnt);
+          split_row_slots(f, p0 + static_cast<int64_t>(P) * (n + 1) + r, first_slot, cnt);
           first_slot *= kWaves;
           cnt *= kWaves;
         },
@@ -505,18 +577,6 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
           s.Mq[r] = M; s.Sq[r] = S;
           st |= stats_status(M, S);
         });
-    if (spot && a.gumbel)
-      combine_rows_pick<NT>(
-          n + 1, a.gpart,
-          [&](int r, int64_t& first_slot, int64_t& cnt) {
-            split_row_slots(f, p0 + r, first_slot, cnt);
-            first_slot *= kWaves;
-            cnt *= kWaves;
-          },
-          [&](int r, float v, int idx, int nan) {
-            s.g[r] = idx;
-            st |= nan ? SEQ_NONFINITE : max_status(v);
-          });
   }
   if (st) atomicOr(&s.st, st);
   __syncthreads();

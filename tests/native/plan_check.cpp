@@ -74,7 +74,62 @@ static void check_split(int64_t R, int64_t V, int64_t eb, int64_t grid) {
   }
 }
 
+// Merged partials of multi-part rows: a logical row is P consecutive stream
+// rows (a target row read with its Gumbel row) or one; each group writes one
+// partial per logical row it touches, at slot (first stream row) + group.
+// The slots are unique and below R + G, and the span the decision step
+// computes for a P-part row (groups of its first through last element)
+// lists exactly the groups that wrote it.
+static void check_merged(const std::vector<int>& parts, int64_t V, int64_t eb, int64_t grid) {
+  std::vector<int64_t> start;   // first stream row of each logical row
+  int64_t R = 0;
+  for (int p : parts) {
+    start.push_back(R);
+    R += p;
+  }
+  const FlatSplit f = make_split(R, V, eb, grid);
+  std::vector<int64_t> owner(static_cast<size_t>(R), -1);   // logical row of each stream row
+  for (size_t l = 0; l < parts.size(); ++l)
+    for (int k = 0; k < parts[l]; ++k) owner[start[l] + k] = static_cast<int64_t>(l);
+  std::vector<int> used(static_cast<size_t>(R + f.G), 0);
+  std::vector<std::vector<int64_t>> writers(parts.size());
+  for (int64_t g = 0; g < f.G; ++g) {
+    int64_t e0, e1;
+    split_range(f, g, e0, e1);
+    int64_t last = -1;
+    for (int64_t r = e0 / V; r * V < e1; ++r) {
+      const int64_t l = owner[r];
+      if (l == last) continue;   // accumulated into the same partial
+      last = l;
+      const int64_t s = start[l] + g;
+      CHECK(s < R + f.G && used[s] == 0, "merged slot %lld (V=%lld)", (long long)s, (long long)V);
+      if (s < R + f.G) used[s] = 1;
+      writers[l].push_back(g);
+    }
+  }
+  for (size_t l = 0; l < parts.size(); ++l) {
+    const int64_t v = start[l], P = parts[l];
+    const int64_t glo = split_group(f, v * V), ghi = split_group(f, (v + P) * V - 1);
+    const auto& w = writers[l];
+    CHECK(static_cast<int64_t>(w.size()) == ghi - glo + 1, "row %zu writers %zu vs %lld", l, w.size(),
+          (long long)(ghi - glo + 1));
+    for (size_t k = 0; k < w.size(); ++k) CHECK(w[k] == glo + static_cast<int64_t>(k), "row %zu writer", l);
+  }
+}
+
 int main() {
+  // Sequences of P-part target rows followed by one-part drafter rows.
+  for (int P : {2, 3})
+    for (int64_t V : {1, 7, 1000, 2048, 32000, 151936})
+      for (int64_t grid : {1, 5, 256, 1024}) {
+        std::vector<int> parts;
+        for (int n : {0, 3, 1, 8, 0, 5}) {
+          for (int i = 0; i <= n; ++i) parts.push_back(P);
+          for (int i = 0; i < n; ++i) parts.push_back(1);
+        }
+        check_merged(parts, V, P == 3 ? 2 : 4, grid);
+      }
+
   // Flat split over small and benchmark-like shapes.
   const int64_t Rs[] = {1, 2, 3, 5, 9, 17, 64, 136, 1000, 1056, 3124};
   const int64_t Vs[] = {1, 2, 7, 255, 1000, 1024, 2047, 2048, 2049, 32000, 128256, 151936};
@@ -85,6 +140,31 @@ int main() {
         for (int64_t grid : grids) check_split(R, V, eb, grid);
   // A tree-sized stream.
   check_split(21000, 151936, 2, 2048);
+
+  // Parts of a target row read with its Gumbel row: contiguous, in order,
+  // covering [0, V), 16-byte aligned starts, each within 16 + (V mod 8P) of
+  // V / P elements.
+  for (int64_t V : {1, 7, 8, 23, 24, 25, 48, 1000, 1024, 2049, 32000, 151936, 152064}) {
+    for (int P : {2, 3}) {
+      int64_t prev = 0;
+      for (int k = 0; k < P; ++k) {
+        const int64_t lo = part_offset(V, P, k, 0), hi = part_offset(V, P, k, V);
+        CHECK(lo == prev && hi >= lo && lo % 8 == 0, "part V=%lld P=%d k=%d [%lld, %lld)", (long long)V, P, k,
+              (long long)lo, (long long)hi);
+        const int64_t want = V / P;
+        CHECK(hi - lo <= want + 16 + V % (8 * P) && hi - lo + 16 + V % (8 * P) >= want, "part balance V=%lld",
+              (long long)V);
+        int64_t last = lo;
+        for (int64_t v = 0; v <= V; v += (V > 4096 ? 2048 : 1)) {   // monotone inside the part
+          const int64_t o = part_offset(V, P, k, v);
+          CHECK(o >= last && o >= lo && o <= hi, "part monotone V=%lld P=%d v=%lld", (long long)V, P, (long long)v);
+          last = o;
+        }
+        prev = hi;
+      }
+      CHECK(prev == V, "parts cover V=%lld P=%d", (long long)V, P);
+    }
+  }
 
   // Launch grids stay within kMaxGrid for any device.
   CHECK(stream_grid(1000000, 151936, 2, 1 << 20) == kMaxGrid, "stream_grid cap");
@@ -112,8 +192,14 @@ int main() {
                     (s.chunks - 1) * s.tpc < s.tiles,
                 "V=%lld B=%d tiles %lld tpc %lld chunks %lld", (long long)V, B, (long long)s.tiles,
                 (long long)s.tpc, (long long)s.chunks);
-          CHECK(s.off_pre % 256 == 0 && s.off_rec % 256 == 0 && s.off_tmass % 256 == 0, "sample offsets");
-          CHECK(s.off_pre >= static_cast<size_t>(s.max_rows + kMaxGrid) * kWavesPlan * 8, "pre overlaps stats");
+          CHECK(s.off_pre % 256 == 0 && s.off_rec % 256 == 0 && s.off_tmass % 256 == 0 && s.off_gpart % 256 == 0,
+                "sample offsets");
+          // Gumbel-row streams: P parts per target row, at most 3.
+          const int64_t P = gumbel_parts(eb);
+          CHECK(P >= 2 && P <= 3 && s.max_vrows >= static_cast<int64_t>(B) * (P * (K + 1) + K), "vrows");
+          CHECK(s.off_gpart >= static_cast<size_t>(s.max_vrows + kMaxGrid) * kWavesPlan * 8, "gpart overlaps stats");
+          CHECK(s.off_pre >= s.off_gpart + static_cast<size_t>(s.max_vrows + kMaxGrid) * kWavesPlan * 8,
+                "pre overlaps gpart");
           CHECK(s.off_rec >= s.off_pre + static_cast<size_t>(B + 1) * 4, "rec overlaps pre");
           CHECK(s.off_tmass >= s.off_rec + static_cast<size_t>(B) * sizeof(DrawRecord), "tmass overlaps rec");
           CHECK(s.bytes >= s.off_tmass + static_cast<size_t>(B) * s.tiles * 4, "sample bytes");
