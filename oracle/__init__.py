@@ -21,6 +21,8 @@ following the pages' definitions in their own order:
   the ending position and retention by position.
 * ``tree``   -- coupled shared-Gumbel state-equality verification of a draft
   tree (and its T=0 greedy special case).
+* ``sparse`` -- lossless verification against a stored sparse (top-k /
+  top-p) drafter distribution.
 * ``spot``   -- chain verification on the joint (position, token) space:
   rejection sampling per link (SPOT App. B) and the confidence-gated hybrid
   of coupled-noise match and rejection sampling.
@@ -28,7 +30,8 @@ following the pages' definitions in their own order:
 Sources (pages by title):
 * "One Call Ahead: Packed Self-Speculative Decoding with Diffusion Drafting"
   (Packed-SS): Sec. 2.2, Sec. 3.1 Eq. 1-4 and Algorithm 1, Sec. 3.2,
-  App. B.2 Algorithm 2 and Lemma B.3, App. C Algorithm 3 and Prop. C.1,
+  Sec. 3.2 (stored sparse Q), App. B.2 Algorithm 2 and Lemma B.3, App. C
+  Algorithm 3 and Prop. C.1,
   App. D.1.
 * "On the SPOT: Enhancing Speculative Decoding for Diffusion Language Models
   via Commit-Order Prediction" (SPOT): Sec. 4.1, Sec. 4.3, App. A.1, A.3
@@ -49,6 +52,7 @@ from .cactus import (  # noqa: F401
     cactus_divergence, cactus_gamma, cactus_target, cactus_acceptance, cactus_residual,
 )
 from .anyorder import NO_END, verify_greedy_any_order  # noqa: F401
+from .sparse import dense_q, verify_sparse  # noqa: F401
 from .spot import MODE_RS, MODE_MATCH, rs_link, rs_residual, verify_spot_chain  # noqa: F401
 from .tree import (  # noqa: F401
     TREE_STATE_EQUALITY, TREE_FIXED_POSITION, state_transition, walk,

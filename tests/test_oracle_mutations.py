@@ -249,3 +249,31 @@ def test_spot_pin_catches_wrong_gate(monkeypatch):
     monkeypatch.setattr(oracle, "verify_spot_chain", gate_mirrored)
     with pytest.raises(AssertionError):
         sp.test_gate_picks_the_verifier()
+
+
+# ------------------------------------------------------- sparse stored Q ---
+
+import tests.test_oracle_sparse_pins as zp  # noqa: E402
+import oracle.sparse as sparse  # noqa: E402
+
+_dense_q = sparse.dense_q
+_residual = sparse.residual_weights
+
+
+def _sq_drops_last(idx, prob, nnz, V):
+    return _dense_q(idx, prob, max(int(nnz) - 1, 0), V)
+
+
+def _sq_residual_on_support_only(p, q, lam=0.0):
+    r = _residual(p, q, lam)
+    return np.where(np.asarray(q) > 0, r, 0.0)
+
+
+@pytest.mark.parametrize("name,fn,pin", [
+    ("dense_q", _sq_drops_last, zp.test_worked_example_by_hand),
+    ("residual_weights", _sq_residual_on_support_only, lambda: zp.test_truncated_drafter_law_and_acceptance(3)),
+], ids=["drops-last-entry", "residual-on-support"])
+def test_sparse_pin_catches_planted_mistake(monkeypatch, name, fn, pin):
+    monkeypatch.setattr(sparse, name, fn)
+    with pytest.raises(AssertionError):
+        pin()
