@@ -17,6 +17,7 @@ and the correction or bonus draw.  Workloads (sizes of the pages' setups):
                                   drafter rows by slot)
   c4s joint-space chain, hybrid   B=16 K=8 V=151936 bf16, T=1, tau=0.6, Gumbel
                                   rows for every target row
+  c3q stored sparse-Q verify      B=32 K=16 V=151936 bf16, top-k = 20 drafter Q
 
 Inputs smaller than 1 GiB are replicated into several buffer sets and the
 steps rotate over them, so the 256 MiB last-level cache cannot serve them.
@@ -54,6 +55,7 @@ DESCR = {
     "c3c": "modified-Cactus verify B=32 K=16 V=128256 bf16 sigma=1 T=1 delta=1",
     "c5ao": "any-order greedy verify B=64 U=32 V=131072 bf16",
     "c4s": "joint-space chain hybrid B=16 K=8 V=151936 bf16 T=1 tau=0.6",
+    "c3q": "sparse stored-Q verify B=32 K=16 V=151936 bf16 top-k=20",
 }
 SPOT_TAU = 0.6
 CACTUS_DELTA = 1.0
@@ -171,6 +173,23 @@ class Case:
                 self.calls.append(dbv.verify_greedy(p[:, :K + 1], x["draft_tokens"].to(dev),
                                                     x["draft_len"].to(dev), p[:, K + 1:], prepare=True))
             self.shape = dict(B=B, K=K, W=W, V=V)
+        elif name == "c3q":
+            x = workloads.config3_sparse()
+            B, K1, V = x["tgt"].shape
+            K = K1 - 1
+            n = x["draft_len"].long()
+            self.positions = int(n.sum())
+            self.kernel_bytes = int(((n + 1) * V * eb).sum())     # target rows only; Q is a few KB
+            self.kernel = "k_sample_rows"
+            per_set = x["tgt"].numel() * eb
+            self.cpu_inputs = x
+            self.calls = []
+            for _ in range(self._rotation(per_set)):
+                xd = {k: v.to(dev).clone() if torch.is_tensor(v) else v for k, v in x.items()}
+                self.calls.append(dbv.verify_sparse(
+                    xd["tgt"], xd["q_idx"], xd["q_prob"], xd["q_nnz"], xd["draft_tokens"], xd["u_accept"],
+                    xd["u_resample"], draft_len=xd["draft_len"], prepare=True))
+            self.shape = dict(B=B, K=K, V=V)
         elif name == "c4s":
             x = workloads.config4_spot_chain()
             B, K1, V = x["tgt"].shape
@@ -282,6 +301,21 @@ class Case:
                 if time.perf_counter() - t0 >= seconds:
                     break
             sample = f"{nb} of 64 sequences, {calls} oracle calls"
+        elif self.name == "c3q":
+            nb = 4
+            xs = {k: v[:nb] if torch.is_tensor(v) else v for k, v in x.items()}
+            args = [np64(xs["tgt"]), npi(xs["q_idx"]), np64(xs["q_prob"]), npi(xs["q_nnz"]),
+                    npi(xs["draft_tokens"]), npi(xs["draft_len"]), 1.0, np64(xs["u_accept"]),
+                    np64(xs["u_resample"])]
+            npos = int(xs["draft_len"].sum())
+            t0 = time.perf_counter()
+            while True:
+                oracle.verify_sparse(*args)
+                done_pos += npos
+                calls += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            sample = f"{nb} of 32 sequences, {calls} oracle calls"
         elif self.name == "c4s":
             nb = 2
             xs = {k: v[:nb] if torch.is_tensor(v) else v for k, v in x.items()}

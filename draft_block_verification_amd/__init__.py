@@ -20,7 +20,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_spot_chain",
+    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_sparse", "verify_spot_chain",
     "verify_greedy_any_order", "verify_gumbel_tree", "workspace_size", "DBVError", "Prepared",
 ]
 
@@ -225,6 +225,53 @@ def verify_cactus(tgt, drf, draft_tokens, u_accept, u_resample, delta, draft_len
     return _sampling("verify_cactus", tgt, drf, draft_tokens, draft_len,
                      temperature_target, temperature_draft, delta, u_accept, u_resample,
                      eos_id, len_budget, workspace, diagnostics, prepare)
+
+
+def verify_sparse(tgt, q_idx, q_prob, q_nnz, draft_tokens, u_accept, u_resample, draft_len=None,
+                  temperature_target=1.0, eos_id=-1, len_budget=None, workspace=None, diagnostics=True,
+                  prepare=False):
+    """Lossless verification against stored sparse drafter distributions
+    (Packed-SS Sec. 3.2: only Q's nonzero entries are stored under top-k /
+    top-p truncation).
+
+    tgt [B, K+1, V]; q_idx [B, K, kmax] int, q_prob [B, K, kmax] float32,
+    q_nnz [B, K] (entries in use per row); draft_tokens [B, K]; u_accept
+    [B, K]; u_resample [B, K+1].  Outputs as verify_rejection.
+    """
+    lib = _lib.load()
+    dev = tgt.device
+    B, K1, V = tgt.shape
+    K = K1 - 1
+    ts, tr = _rows3(tgt, "tgt")
+    dt = _dtype_code(tgt)
+    kmax = int(torch.as_tensor(q_idx).shape[-1]) if K > 0 else 0
+    qi = _i32(q_idx, (B, K, kmax), "q_idx", dev)
+    qp = _f32(q_prob, (B, K, kmax), "q_prob", dev)
+    qn = _i32(q_nnz, (B, K), "q_nnz", dev)
+    d = _i32(draft_tokens, (B, K), "draft_tokens", dev)
+    n = _i32(draft_len, (B,), "draft_len", dev)
+    bud = _i32(len_budget, (B,), "len_budget", dev)
+    ua = _f32(u_accept, (B, K), "u_accept", dev)
+    ur = _f32(u_resample, (B, K + 1), "u_resample", dev)
+    out = {
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "out_tokens": torch.empty(B, K + 1, dtype=torch.int32, device=dev),
+        "num_out": torch.empty(B, dtype=torch.int32, device=dev),
+        "status": torch.empty(B, dtype=torch.int32, device=dev),
+    }
+    if diagnostics:
+        for k in ("p_draft", "q_draft", "alpha"):
+            out[k] = torch.empty(B, K, dtype=torch.float32, device=dev)
+        out["residual_mass"] = torch.empty(B, dtype=torch.float32, device=dev)
+    need = workspace_size(_lib.DBV_KIND_REJECTION, B, K, 0, V, dt)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    args = (B, K, V, dt, tgt.data_ptr(), ts, tr, _ptr(qi), _ptr(qp), _ptr(qn), kmax, _ptr(d), _ptr(n),
+            float(temperature_target), _ptr(ua), ur.data_ptr(), int(eos_id), _ptr(bud),
+            out["accept_len"].data_ptr(), out["out_tokens"].data_ptr(), out["num_out"].data_ptr(),
+            _ptr(out.get("p_draft")), _ptr(out.get("q_draft")), _ptr(out.get("alpha")),
+            _ptr(out.get("residual_mass")), out["status"].data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+    call = Prepared(lib.verify_sparse, "verify_sparse", args, out, (tgt, qi, qp, qn, d, n, bud, ua, ur, ws))
+    return call if prepare else call()
 
 
 def verify_spot_chain(tgt, drf, pos_star, prop_pos, prop_tok, q_pos_star, u_accept, u_resample,

@@ -92,6 +92,10 @@ struct Rule {
   const float* gumbel = nullptr;
   int64_t gs = 0, grs = 0;
   float tau = 0.f;
+  const int32_t* qidx = nullptr;        // stored sparse Q
+  const float* qprob = nullptr;
+  const int32_t* qnnz = nullptr;
+  int kmax = 0;
 };
 
 dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t ts, int64_t tr,
@@ -113,8 +117,16 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
     if (rl.gumbel && !aligned(rl.gumbel, 4)) return DBV_ERR_INVALID_ARG;
   }
   if (ts < 0 || tr < 0 || ds < 0 || dr < 0) return DBV_ERR_INVALID_ARG;
+  const bool sparse = rl.rule == dbv::RULE_SPARSE;
   if (tgt == nullptr || u_resample == nullptr) return DBV_ERR_INVALID_ARG;
-  if (K > 0 && (drf == nullptr || draft_tokens == nullptr || u_accept == nullptr)) return DBV_ERR_INVALID_ARG;
+  if (K > 0 && ((!sparse && drf == nullptr) || draft_tokens == nullptr || u_accept == nullptr))
+    return DBV_ERR_INVALID_ARG;
+  if (sparse) {
+    if (rl.kmax < 0) return DBV_ERR_INVALID_ARG;
+    if (rl.kmax > dbv::kMaxNnz) return DBV_ERR_UNSUPPORTED;
+    if (K > 0 && (rl.qnnz == nullptr || (rl.kmax > 0 && (rl.qidx == nullptr || rl.qprob == nullptr))))
+      return DBV_ERR_INVALID_ARG;
+  }
   if (accept_len == nullptr || out_tokens == nullptr || num_out == nullptr) return DBV_ERR_INVALID_ARG;
   const size_t eb = elem_bytes(dtype);
   if (!aligned(tgt, eb) || (drf && !aligned(drf, eb))) return DBV_ERR_INVALID_ARG;
@@ -138,6 +150,8 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.gumbel = rl.gumbel; a.gs = rl.gs; a.grs = rl.grs;
   a.inv_t = 1.f / tt;
   a.tau = rl.tau;
+  a.qidx = rl.qidx; a.qprob = rl.qprob; a.qnnz = rl.qnnz; a.kmax = rl.kmax;
+  a.drows = sparse ? 0 : 1;
   a.u_accept = u_accept; a.u_resample = u_resample;
   a.eos = eos_id; a.budget = len_budget;
   a.accept_len = accept_len; a.out_tokens = out_tokens; a.num_out = num_out;
@@ -291,6 +305,24 @@ dbv_status verify_spot_chain(int B, int K, int V, dbv_dtype dtype, const void* t
                        drf_row_stride, prop_tok, draft_len, temperature_target, temperature_draft, r, u_accept,
                        u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft, q_draft, alpha,
                        residual_mass, status, ws, ws_bytes, stream);
+}
+
+dbv_status verify_sparse(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
+                         int64_t tgt_row_stride, const int32_t* q_idx, const float* q_prob, const int32_t* q_nnz,
+                         int kmax, const int32_t* draft_tokens, const int32_t* draft_len, float temperature_target,
+                         const float* u_accept, const float* u_resample, int32_t eos_id, const int32_t* len_budget,
+                         int32_t* accept_len, int32_t* out_tokens, int32_t* num_out, float* p_draft,
+                         float* q_draft, float* alpha, float* residual_mass, int32_t* status, void* ws,
+                         size_t ws_bytes, void* stream) {
+  Rule r;
+  r.rule = dbv::RULE_SPARSE;
+  r.qidx = q_idx;
+  r.qprob = q_prob;
+  r.qnnz = q_nnz;
+  r.kmax = kmax;
+  return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, nullptr, 0, 0, draft_tokens,
+                       draft_len, temperature_target, 1.f, r, u_accept, u_resample, eos_id, len_budget, accept_len,
+                       out_tokens, num_out, p_draft, q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
 }
 
 dbv_status verify_greedy_any_order(int B, int U, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,

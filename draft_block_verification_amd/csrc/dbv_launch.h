@@ -25,7 +25,7 @@ struct GreedyArgs {
   int elem_bytes;                      // 2 (bf16) or 4 (fp32)
 };
 
-enum : int { RULE_LINEAR = 0, RULE_CACTUS = 1, RULE_SPOT = 2 };
+enum : int { RULE_LINEAR = 0, RULE_CACTUS = 1, RULE_SPOT = 2, RULE_SPARSE = 3 };
 
 struct SampleArgs {
   int B, K, V;
@@ -34,7 +34,7 @@ struct SampleArgs {
   const int32_t* draft_tokens;
   const int32_t* draft_len;
   float kp, kq;                        // log2(e) / temperature
-  int rule;                            // RULE_LINEAR, RULE_CACTUS or RULE_SPOT
+  int rule;                            // RULE_LINEAR, RULE_CACTUS, RULE_SPOT or RULE_SPARSE
   float lam;                           // linear rule: 0 = lossless
   float delta;                         // Cactus rule: KL budget
   // Joint-space chain (RULE_SPOT): per link the target's position s*, the
@@ -46,6 +46,11 @@ struct SampleArgs {
   const float* gumbel; int64_t gs, grs;
   float inv_t;                         // 1 / temperature of the target
   float tau;
+  // Stored sparse drafter distributions (RULE_SPARSE): [B, K, kmax] entries,
+  // the first qnnz[b, i] of each row in use; no drafter rows are streamed.
+  const int32_t* qidx; const float* qprob; const int32_t* qnnz;
+  int kmax;
+  int drows;                           // drafter rows are streamed (1) or not (0)
   const float* u_accept; const float* u_resample;
   int32_t eos;
   const int32_t* budget;

@@ -128,6 +128,8 @@ inline size_t partial_bytes(int64_t max_rows) {
 // which saves a kernel boundary and the round trip of the masses.
 constexpr int kDrawThreads = 1024;
 constexpr int kFusedDrawTiles = 16;
+// Stored sparse drafter distributions: at most kMaxNnz entries per row.
+constexpr int kMaxNnz = 256;
 constexpr int kMaxDrawTiles = 8192;
 constexpr int kDrawTilesPerThread = kMaxDrawTiles / kDrawThreads;
 constexpr int64_t kMaxSampleV = int64_t(1) << 21;   // <= kMaxDrawTiles tiles of 256 fp32

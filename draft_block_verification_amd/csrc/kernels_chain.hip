@@ -159,11 +159,12 @@ __global__ __launch_bounds__(kBlock) void k_greedy_finalize(GreedyArgs a) {
 // ============================================================== sampling ===
 
 // Stream rows of sequence b: target rows 0..n_b (P stream rows each), then
-// drafter rows 0..n_b-1; none for an invalid draft length.
+// drafter rows 0..n_b-1 when they are streamed; none for an invalid draft
+// length.
 __device__ __forceinline__ int sample_count(const SampleArgs& a, int b, int P) {
   bool bad;
   const int n = draft_count(a.draft_len, b, a.K, bad);
-  return bad ? 0 : P * (n + 1) + n;
+  return bad ? 0 : P * (n + 1) + (a.drows ? n : 0);
 }
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
     int first, cnt;
     const int b = find_seq(dir, s_pre, static_cast<int>(r), count, first, cnt);
     const int j = static_cast<int>(r) - first;
-    const int n = (cnt - P) / (P + 1);
+    const int n = a.drows ? (cnt - P) / (P + 1) : cnt / P - 1;
     const bool target = j < P * (n + 1);
     const int jt = j / P;   // target row of a target part
     const float k = target ? a.kp : a.kq;
@@ -472,7 +473,10 @@ __device__ __forceinline__ float group_exclusive_scan_f(float v, float& total, f
 // draft.
 struct DecideLds {
   float Mp[kMaxDraft + 1], Sp[kMaxDraft + 1];
-  float Mq[kMaxDraft], Sq[kMaxDraft];
+  // Drafter rows' statistics, or (stored sparse Q) each draft's token and
+  // Q(d) summed from its row's entries.
+  union { float Mq[kMaxDraft]; float qd[kMaxDraft]; };
+  union { float Sq[kMaxDraft]; int dtok[kMaxDraft]; };
   int g[kMaxDraft + 1];      // joint-space chain: Gumbel argmax of target rows
   int st, h;
   int dh, modeh;
@@ -500,6 +504,7 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
   const int R = a.pre[a.B];
   const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
   const bool spot = a.rule == RULE_SPOT;
+  const bool sparse = a.rule == RULE_SPARSE;
   int di[DPT], psk[DPT], ppk[DPT];
   float ui[DPT], xi[DPT], yi[DPT], ck[DPT];
 #pragma unroll
@@ -529,7 +534,8 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
         st |= SEQ_BAD_INPUT;
       } else {
         xi[k] = E::load1(static_cast<const char*>(a.tgt) + (b * a.ts + i * a.tr) * E::kBytes, di[k]);
-        yi[k] = E::load1(static_cast<const char*>(a.drf) + (b * a.ds + i * a.dr) * E::kBytes, di[k]);
+        if (!sparse)
+          yi[k] = E::load1(static_cast<const char*>(a.drf) + (b * a.ds + i * a.dr) * E::kBytes, di[k]);
       }
     }
   }
@@ -566,17 +572,48 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
         s.g[r] = idx;
         st |= nan ? SEQ_NONFINITE : max_status(v);
       });
-    combine_rows_stats<NT>(
-        n, a.stats, a.kq,
-        [&](int r, int64_t& first_slot, int64_t& cnt) {
-          split_row_slots(f, p0 + static_cast<int64_t>(P) * (n + 1) + r, first_slot, cnt);
-          first_slot *= kWaves;
-          cnt *= kWaves;
-        },
-        [&](int r, float M, float S) {
-          s.Mq[r] = M; s.Sq[r] = S;
-          st |= stats_status(M, S);
-        });
+    if (a.drows)
+      combine_rows_stats<NT>(
+          n, a.stats, a.kq,
+          [&](int r, int64_t& first_slot, int64_t& cnt) {
+            split_row_slots(f, p0 + static_cast<int64_t>(P) * (n + 1) + r, first_slot, cnt);
+            first_slot *= kWaves;
+            cnt *= kWaves;
+          },
+          [&](int r, float M, float S) {
+            s.Mq[r] = M; s.Sq[r] = S;
+            st |= stats_status(M, S);
+          });
+  }
+  if (sparse && !nbad) {
+    // Q(d_i) from row i's stored entries, every (draft, entry) pair one work
+    // item of the group; each draft's thread checks its entry count.
+#pragma unroll
+    for (int k = 0; k < DPT; ++k) {
+      const int i = t + k * NT;
+      if (i < n) {
+        const int nz = a.qnnz[static_cast<int64_t>(b) * a.K + i];
+        if (nz < 0 || nz > a.kmax) st |= SEQ_BAD_INPUT;
+        s.dtok[i] = di[k];
+        s.qd[i] = 0.f;
+      }
+    }
+    __syncthreads();
+    const int64_t items = static_cast<int64_t>(n) * a.kmax;
+    for (int64_t it = t; it < items; it += NT) {
+      const int i = static_cast<int>(it / a.kmax);
+      const int e = static_cast<int>(it - static_cast<int64_t>(i) * a.kmax);
+      const int64_t row = static_cast<int64_t>(b) * a.K + i;
+      const int nz = a.qnnz[row];
+      if (e >= nz) continue;
+      const int v = a.qidx[row * a.kmax + e];
+      const float pr = a.qprob[row * a.kmax + e];
+      if (v < 0 || v >= a.V || !(pr >= 0.f && pr <= 3.402823466e38f)) {
+        st |= SEQ_BAD_INPUT;
+        continue;
+      }
+      if (v == s.dtok[i]) atomicAdd(&s.qd[i], pr);
+    }
   }
   if (st) atomicOr(&s.st, st);
   __syncthreads();
@@ -617,7 +654,7 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
     mk[k] = 0;
     if (i < n) {
       p = fast_exp2(__builtin_fmaf(xi[k], a.kp, -s.Mp[i] * a.kp)) / s.Sp[i];
-      q = fast_exp2(__builtin_fmaf(yi[k], a.kq, -s.Mq[i] * a.kq)) / s.Sq[i];
+      q = sparse ? s.qd[i] : fast_exp2(__builtin_fmaf(yi[k], a.kq, -s.Mq[i] * a.kq)) / s.Sq[i];
       bool acc;
       if (spot) {
         const bool on = ppk[k] == psk[k];
@@ -670,11 +707,11 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
   }
   rec.status = s.st;
   rec.h = h;
-  rec.resid = resid ? 1 : 0;
+  rec.resid = resid ? (sparse ? 2 : 1) : 0;
   rec.cp = -s.Mp[h] * a.kp;
   rec.isp = 1.f / s.Sp[h];
-  rec.cq = resid ? -s.Mq[h] * a.kq : 0.f;
-  rec.isq = resid ? 1.f / s.Sq[h] : 1.f;
+  rec.cq = resid && !sparse ? -s.Mq[h] * a.kq : 0.f;
+  rec.isq = resid && !sparse ? 1.f / s.Sq[h] : 1.f;
   rec.u = a.u_resample[static_cast<int64_t>(b) * (a.K + 1) + h];
   rec.excl = -1;
   rec.wexcl = 0.f;
@@ -718,13 +755,15 @@ __device__ __forceinline__ void draw_rows(const SampleArgs& a, int b, int h, boo
                                           const char*& yr) {
   using E = Elem<DT>;
   xr = static_cast<const char*>(a.tgt) + (b * a.ts + static_cast<int64_t>(h) * a.tr) * E::kBytes;
-  yr = resid ? static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(h) * a.dr) * E::kBytes : xr;
+  yr = resid && a.drows ? static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(h) * a.dr) * E::kBytes
+                        : xr;
 }
 
 // Per (sequence, chunk of draw tiles), kBlock threads: the decision (chunk 0
 // writes the diagnostics and the record), then the masses of the chunk's
 // tiles of row h: [p~ - q]_+ against drafter row h if a draft was rejected,
-// else the bonus weight p.
+// else the bonus weight p.  Against a stored sparse Q the masses are those of
+// p; the select step redoes the tiles that hold stored entries.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   __shared__ DecideLds s;
@@ -738,8 +777,9 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   const bool vec = ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0;
   const int t_lo = c * a.tpc;
   const int t_hi = t_lo + a.tpc < a.tiles ? t_lo + a.tpc : a.tiles;
-  tile_masses<DT, kWaves>(xr, yr, a.V, t_lo, t_hi, vec, draw_weight(a, rec),
-                          a.tmass + static_cast<int64_t>(b) * a.tiles);
+  DrawWeight w = draw_weight(a, rec);
+  if (w.resid == 2) w.resid = 0;
+  tile_masses<DT, kWaves>(xr, yr, a.V, t_lo, t_hi, vec, w, a.tmass + static_cast<int64_t>(b) * a.tiles);
 }
 
 constexpr int kDrawWaves = kDrawThreads / 64;
@@ -749,7 +789,23 @@ struct SelectLds {
   float w[kDrawWaves];
   float Z, base;
   int ct, lt, cs, pick, a;
+  // stored sparse Q of row h: its entries and the tiles that hold them
+  int sidx[kMaxNnz];
+  float sprob[kMaxNnz];
+  unsigned aff[kMaxDrawTiles / 32];
+  int afflist[kMaxNnz];
+  int naff, nnz;
 };
+
+// The residual weight [p - Q]_+ of element e against the stored entries of
+// Q in LDS (a linear scan: Q has at most kMaxNnz entries).
+__device__ __forceinline__ float sparse_weight(const DrawWeight& w, const SelectLds& s, uint32_t e, float x) {
+  const float p = fast_exp2(__builtin_fmaf(x, w.kp, w.cp)) * w.isp;
+  float q = 0.f;
+  for (int k = 0; k < s.nnz; ++k)
+    if (s.sidx[k] == static_cast<int>(e)) q += s.sprob[k];
+  return fmaxf(p - q, 0.f);
+}
 
 // The draw of sequence b by kDrawThreads threads, given its record and this
 // thread's tile masses m0 (tiles [t*q, (t+1)*q), q = ceil(tiles / threads)):
@@ -759,7 +815,9 @@ struct SelectLds {
 // ending condition.
 // dt is this thread's draft token d_{t+1} (t < K), requested with the first
 // loads; every output position i < h <= K <= kDrawThreads is some thread's t.
-template <int DT>
+// SPARSE: the call may verify against a stored sparse Q (the fused draw
+// never does).
+template <int DT, bool SPARSE>
 __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, int budget, int dt,
                             const float (&m0)[kDrawTilesPerThread], SelectLds& s) {
   static_assert(kMaxDraft <= kDrawThreads, "one draft token per thread");
@@ -776,6 +834,54 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
   draw_rows<DT>(a, b, h, resid0, xr, yr);
   DrawWeight w = draw_weight(a, rec);
   constexpr int TE = 64 * E::kVec;                              // elements per tile
+  const bool draw = rec.fixed < 0;   // uniform across the group
+  float mt[kDrawTilesPerThread];
+#pragma unroll
+  for (int k = 0; k < kDrawTilesPerThread; ++k) mt[k] = m0[k];
+  if (SPARSE && draw && w.resid == 2) {
+    // Residual against a stored sparse Q: the tile masses are those of p
+    // (unnormalised exp2 weights, scaled here by 1/S), and every tile
+    // holding a stored entry is summed again from its exact weights
+    // [p - Q]_+ (all zero gives exactly zero).
+    const int64_t row = static_cast<int64_t>(b) * a.K + h;
+    const int nnz = a.qnnz[row];
+    for (int k = 0; k < kDrawTilesPerThread; ++k)
+      if (k < q && t * q + k < ntiles) s.tile[t * q + k] = mt[k] * w.isp;
+    for (int i = t; i < (ntiles + 31) / 32; i += kDrawThreads) s.aff[i] = 0u;
+    for (int e = t; e < nnz; e += kDrawThreads) {
+      s.sidx[e] = a.qidx[row * a.kmax + e];
+      s.sprob[e] = a.qprob[row * a.kmax + e];
+    }
+    if (t == 0) {
+      s.naff = 0;
+      s.nnz = nnz;
+    }
+    __syncthreads();
+    for (int e = t; e < nnz; e += kDrawThreads) {
+      const int tile = s.sidx[e] / TE;
+      const unsigned bit = 1u << (tile & 31);
+      if (!(atomicOr(&s.aff[tile >> 5], bit) & bit)) s.afflist[atomicAdd(&s.naff, 1)] = tile;
+    }
+    __syncthreads();
+    for (int i = wv; i < s.naff; i += kDrawWaves) {
+      const int tile = s.afflist[i];
+      float m = 0.f;
+      for (int j = 0; j < E::kVec; ++j) {
+        const int64_t e = static_cast<int64_t>(tile) * TE + lane * E::kVec + j;
+        if (e < a.V) m += sparse_weight(w, s, static_cast<uint32_t>(e), E::load1(xr, e));
+      }
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) m += wave_shfl_xor(m, sh);
+      if (lane == 0) s.tile[tile] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kDrawTilesPerThread; ++k) {
+      const int tile = t * q + k;
+      mt[k] = (k < q && tile < ntiles) ? s.tile[tile] : 0.f;
+    }
+    __syncthreads();   // s.tile is reused by the zero-mass fallback
+  }
 
   // Thread t holds the masses of tiles [t*q, (t+1)*q); an exclusive scan
   // gives it the mass before them, and the group's total Z.
@@ -812,8 +918,7 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
     }
     __syncthreads();
   };
-  const bool draw = rec.fixed < 0;   // uniform across the group
-  if (draw) locate(m0);
+  if (draw) locate(mt);
   const float Zres = resid0 ? s.Z : 0.f;
   if (draw && resid0 && !(s.Z > 0.f)) {
     // Residual mass vanished in float32 (p == q up to rounding): draw from p
@@ -850,7 +955,9 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
 #pragma unroll
     for (int j = 0; j < E::kVec; ++j) {
       const int64_t e = e0 + j;
-      wt[j] = e < a.V ? w.at(static_cast<uint32_t>(e), E::load1(xr, e), w.resid ? E::load1(yr, e) : 0.f) : 0.f;
+      if (e >= a.V) wt[j] = 0.f;
+      else if (SPARSE && w.resid == 2) wt[j] = sparse_weight(w, s, static_cast<uint32_t>(e), E::load1(xr, e));
+      else wt[j] = w.at(static_cast<uint32_t>(e), E::load1(xr, e), w.resid ? E::load1(yr, e) : 0.f);
       loc += wt[j];
     }
     float inc = loc;
@@ -923,7 +1030,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
     m0[k] = (k < q && tile < ntiles) ? tmass[tile] : 0.f;
   }
   if (rec.status & SEQ_ERROR_MASK) return;          // outputs already written
-  draw_select<DT>(a, b, rec, budget, dt, m0, s);
+  draw_select<DT, true>(a, b, rec, budget, dt, m0, s);
 }
 
 // The whole draw of one sequence in one group of kDrawThreads threads (for
@@ -953,7 +1060,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_fused(SampleArgs a) {
     m0[k] = (k < q && tile < ntiles) ? s.tile[tile] : 0.f;
   }
   __syncthreads();   // the fallback in draw_select may overwrite s.tile
-  draw_select<DT>(a, b, rec, budget, dt, m0, s);
+  draw_select<DT, false>(a, b, rec, budget, dt, m0, s);
 }
 
 // ============================================================== launches ===
@@ -974,7 +1081,7 @@ bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const Tim
   const void* rows = a.gumbel ? (bf ? fn(k_sample_rows<DT_BF16, true>) : fn(k_sample_rows<DT_F32, true>))
                               : (bf ? fn(k_sample_rows<DT_BF16, false>) : fn(k_sample_rows<DT_F32, false>));
   if (!launch(rows, a.grid, stream, a, ev)) return false;
-  if (a.tiles <= kFusedDrawTiles)
+  if (a.tiles <= kFusedDrawTiles && a.rule != RULE_SPARSE)
     return launch_threads(bf ? fn(k_draw_fused<DT_BF16>) : fn(k_draw_fused<DT_F32>), a.B, kDrawThreads, stream, a);
   return launch(bf ? fn(k_draw_mass<DT_BF16>) : fn(k_draw_mass<DT_F32>), static_cast<int64_t>(a.B) * a.chunks,
                 stream, a) &&

@@ -9,13 +9,15 @@
  * linear lenient rule, or shared-Gumbel state equality over a draft tree),
  * finds the longest accepted prefix (or tree path) and draws the correction
  * or bonus token from supplied uniforms.  verify_cactus adds the modified
- * Cactus acceptance rule, verify_spot_chain chain verification on the joint
+ * Cactus acceptance rule, verify_sparse verification against stored sparse
+ * drafter distributions, verify_spot_chain chain verification on the joint
  * (position, token) space and verify_greedy_any_order any-order greedy
  * verification.
  *
  * Sources (pages by title):
  *   [PSS]  "One Call Ahead: Packed Self-Speculative Decoding with Diffusion
- *          Drafting" -- Sec. 2.2, Sec. 3.1 (Eq. 1-4, Algorithm 1), Sec. 3.2,
+ *          Drafting" -- Sec. 2.2, Sec. 3.1 (Eq. 1-4, Algorithm 1), Sec. 3.2
+ *          (stored sparse Q),
  *          App. B.2 (Algorithm 2, Lemma B.3), App. C (Algorithm 3, any-order
  *          verification), App. D.1 (packed row layout).
  *   [SPOT] "On the SPOT: Enhancing Speculative Decoding for Diffusion Language
@@ -93,7 +95,7 @@ enum {
 /* Workspace kinds for verify_workspace_size. */
 typedef enum {
   DBV_KIND_GREEDY = 0,
-  DBV_KIND_REJECTION = 1, /* also verify_lenient, verify_cactus, verify_spot_chain */
+  DBV_KIND_REJECTION = 1, /* also verify_lenient, verify_cactus, verify_sparse, verify_spot_chain */
   DBV_KIND_TREE = 2,
   DBV_KIND_ANY_ORDER = 3  /* K_or_S = U (window), L ignored */
 } dbv_kind;
@@ -200,6 +202,34 @@ dbv_status verify_cactus(int B, int K, int V, dbv_dtype dtype,
                          const void* drf, int64_t drf_seq_stride, int64_t drf_row_stride,
                          const int32_t* draft_tokens, const int32_t* draft_len,
                          float temperature_target, float temperature_draft, float delta,
+                         const float* u_accept, const float* u_resample,
+                         int32_t eos_id, const int32_t* len_budget,
+                         int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
+                         float* p_draft, float* q_draft, float* alpha, float* residual_mass,
+                         int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * verify_sparse -- lossless verification against stored sparse drafter
+ * distributions ([PSS] Sec. 3.2: with top-k / top-p truncation only the
+ * nonzero entries of each draft's Q need storing; the test is the lossless
+ * rule of [PSS] App. B.2, Algorithm 2).  Row i of sequence b stores Q as
+ * q_nnz[b, i] entries (token q_idx[b, i, e], probability q_prob[b, i, e]),
+ * dense [B, K, kmax] arrays of which the first q_nnz entries are used;
+ * tokens off the list have Q = 0.  Accept d_i iff u_accept <
+ * min(1, p(d_i) / Q(d_i)); a rejection draws from normalize([p - Q]_+)
+ * (= p off the stored support); the bonus after full acceptance is drawn
+ * from p.  Q is used as stored (not renormalised); the entries of one row
+ * must name distinct tokens (not checked).  Only the target rows are read
+ * from HBM.  0 <= kmax <= 256 (DBV_ERR_UNSUPPORTED above).  Bad input
+ * (DBV_SEQ_BAD_INPUT) in a row the call reads (i < n_b): q_nnz outside
+ * [0, kmax], a token outside [0, V), a probability that is negative or not
+ * finite.  Outputs as verify_rejection (q_draft = Q(d_i)).  Workspace kind:
+ * DBV_KIND_REJECTION.
+ */
+dbv_status verify_sparse(int B, int K, int V, dbv_dtype dtype,
+                         const void* tgt, int64_t tgt_seq_stride, int64_t tgt_row_stride,
+                         const int32_t* q_idx, const float* q_prob, const int32_t* q_nnz, int kmax,
+                         const int32_t* draft_tokens, const int32_t* draft_len, float temperature_target,
                          const float* u_accept, const float* u_resample,
                          int32_t eos_id, const int32_t* len_budget,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,

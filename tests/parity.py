@@ -51,9 +51,11 @@ def check_any_order(g, o):
 
 
 def check_sampling(g, x, o, lam, t_target, t_draft, dtype_name, eos_id=-1, len_budget=None,
-                   seqs=None, delta=None):
+                   seqs=None, delta=None, qfun=None):
     """Rejection / lenient / Cactus (``delta`` set) outputs against the oracle
-    with margin accounting.
+    with margin accounting.  ``qfun(b, i)`` gives the drafter distribution
+    of row i of sequence b where it is not the softmax of x["drf"] (stored
+    sparse Q).
 
     g: GPU outputs (torch or numpy); x: the inputs as float64 numpy
     (tgt, drf, draft_tokens, draft_len, u_accept, u_resample); o: oracle
@@ -100,7 +102,7 @@ def check_sampling(g, x, o, lam, t_target, t_draft, dtype_name, eos_id=-1, len_b
         # The draw at the GPU's row h.
         p = oracle.tempered_softmax(x["tgt"][b, h], t_target)
         if h < n:
-            q = oracle.tempered_softmax(x["drf"][b, h], t_draft)
+            q = qfun(b, h) if qfun is not None else oracle.tempered_softmax(x["drf"][b, h], t_draft)
             if delta is None:
                 w = oracle.residual_weights(p, q, lam)
             else:

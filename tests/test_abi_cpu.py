@@ -107,6 +107,16 @@ def _tree(lib, **kw):
                                   o, o, a["ws"], a["wsb"], a["stream"])
 
 
+def _sparse(lib, **kw):
+    a = dict(B=2, K=3, V=100, dt=_lib.DBV_BF16, tgt=FAKE, ts=400, tr=100, qi=FAKE, qp=FAKE, qn=FAKE, kmax=20,
+             d=FAKE, n=None, tt=1.0, ua=FAKE, ur=FAKE, eos=-1, bud=None, o=FAKE, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    o = a["o"]
+    return lib.verify_sparse(a["B"], a["K"], a["V"], a["dt"], a["tgt"], a["ts"], a["tr"], a["qi"], a["qp"], a["qn"],
+                             a["kmax"], a["d"], a["n"], a["tt"], a["ua"], a["ur"], a["eos"], a["bud"], o, o, o,
+                             None, None, None, None, o, a["ws"], a["wsb"], a["stream"])
+
+
 def _spot(lib, **kw):
     a = dict(B=2, K=3, V=100, dt=_lib.DBV_BF16, tgt=FAKE, ts=400, tr=100, drf=FAKE, ds=300, dr=100, ps=FAKE,
              pp=FAKE, d=FAKE, c=FAKE, n=None, tt=1.0, td=1.0, g=FAKE, gs=400, gr=100, tau=0.6, ua=FAKE, ur=FAKE,
@@ -188,6 +198,18 @@ def test_spot_chain_rejects_bad_args(lib, kw):
     assert _spot(lib, **kw) == INVALID
 
 
+@pytest.mark.parametrize("kw", [
+    dict(B=-1), dict(K=-1), dict(V=0), dict(dt=3), dict(tgt=None), dict(qi=None), dict(qp=None), dict(qn=None),
+    dict(kmax=-1), dict(d=None), dict(ua=None), dict(ur=None), dict(o=None), dict(tt=0.0), dict(tgt=FAKE + 1),
+])
+def test_sparse_rejects_bad_args(lib, kw):
+    assert _sparse(lib, **kw) == INVALID
+
+
+def test_sparse_limits(lib):
+    assert _sparse(lib, kmax=257) == _lib.DBV_ERR_UNSUPPORTED
+
+
 def test_workspace_errors(lib):
     assert _greedy(lib, ws=None) == _lib.DBV_ERR_WORKSPACE
     assert _greedy(lib, wsb=8) == _lib.DBV_ERR_WORKSPACE
@@ -196,6 +218,7 @@ def test_workspace_errors(lib):
     assert _tree(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
     assert _any_order(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
     assert _spot(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
+    assert _sparse(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
 
 
 def test_optional_arguments_are_accepted(lib):
@@ -211,6 +234,8 @@ def test_optional_arguments_are_accepted(lib):
     assert _any_order(lib, dr=None, nd=None, st=None) == nodev
     assert _any_order(lib, U=0, order=None, d=None) == nodev
     assert _spot(lib, g=None, tau=float("inf")) == nodev
+    assert _sparse(lib, kmax=0, qi=None, qp=None) == nodev
+    assert _sparse(lib, K=0, qi=None, qp=None, qn=None, d=None, ua=None) == nodev
     assert _spot(lib, K=0, drf=None, pp=None, d=None, c=None, ua=None) == nodev
 
 

@@ -24,6 +24,8 @@ that hold at any size:
     sequence, with and without EOS / end position
   * joint-space chain       B=16 K=8 V=151936 bf16, hybrid gate tau=0.6 and
     rejection sampling only -- oracle on every sequence
+  * stored sparse Q         B=32 K=16 V=151936 bf16, top-k = 20 -- oracle on
+    every sequence
 """
 
 import sys
@@ -271,3 +273,24 @@ def test_full_spot_chain(dev):
                                      xn["u_resample"], gumbel=xn["gumbel"], tau=0.6)
         near = check_spot(g, xn, o, 1.0, 1.0, 0.6, "bfloat16")
         say("gumbel", G is not None, "mean h", float(o["accept_len"].mean()), "near", dict(near))
+
+
+# ---------------------------------------------------------------- sparse Q ---
+
+def test_full_sparse(dev):
+    say("full sparse Q B=32 K=16 V=151936 bf16 top-k 20")
+    x = workloads.config3_sparse()
+    g = dbv.verify_sparse(x["tgt"].to(dev), x["q_idx"].to(dev), x["q_prob"].to(dev), x["q_nnz"].to(dev),
+                          x["draft_tokens"].to(dev), x["u_accept"].to(dev), x["u_resample"].to(dev),
+                          draft_len=x["draft_len"].to(dev))
+    qi, qp, qn = npi(x["q_idx"]), np64(x["q_prob"]), npi(x["q_nnz"])
+    xn = dict(tgt=np64(x["tgt"]), draft_tokens=npi(x["draft_tokens"]), draft_len=npi(x["draft_len"]),
+              u_accept=np64(x["u_accept"]), u_resample=np64(x["u_resample"]))
+    V = x["tgt"].shape[-1]
+    for b0 in range(0, 32, 8):
+        sl = list(range(b0, b0 + 8))
+        o = oracle.verify_sparse(xn["tgt"][sl], qi[sl], qp[sl], qn[sl], xn["draft_tokens"][sl],
+                                 xn["draft_len"][sl], 1.0, xn["u_accept"][sl], xn["u_resample"][sl])
+        near = check_sampling(g, xn, o, 0.0, 1.0, 1.0, "bfloat16", seqs=sl,
+                              qfun=lambda b, i: oracle.dense_q(qi[b, i], qp[b, i], qn[b, i], V))
+        say("seqs", b0, "h", list(o["accept_len"]), "near", dict(near))

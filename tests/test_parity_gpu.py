@@ -196,6 +196,77 @@ def test_cactus_edge_cases(dev):
     check_sampling(res, xn, o, 0.0, 1.0, 1.0, "float32", eos_id=eos, len_budget=npi(bud), delta=3.0)
 
 
+# --------------------------------------------------------------- sparse Q ---
+
+def _sparse_run(dev, x, eos_id=-1, len_budget=None):
+    g = dbv.verify_sparse(x["tgt"].to(dev), x["q_idx"].to(dev), x["q_prob"].to(dev), x["q_nnz"].to(dev),
+                          x["draft_tokens"].to(dev), x["u_accept"].to(dev), x["u_resample"].to(dev),
+                          draft_len=x["draft_len"].to(dev), temperature_target=x["temperature"], eos_id=eos_id,
+                          len_budget=None if len_budget is None else len_budget.to(dev))
+    xn = dict(tgt=np64(x["tgt"]), draft_tokens=npi(x["draft_tokens"]), draft_len=npi(x["draft_len"]),
+              u_accept=np64(x["u_accept"]), u_resample=np64(x["u_resample"]))
+    qi, qp, qn = npi(x["q_idx"]), np64(x["q_prob"]), npi(x["q_nnz"])
+    o = oracle.verify_sparse(xn["tgt"], qi, qp, qn, xn["draft_tokens"], xn["draft_len"], x["temperature"],
+                             xn["u_accept"], xn["u_resample"], eos_id=eos_id,
+                             len_budget=None if len_budget is None else npi(len_budget))
+    V = x["tgt"].shape[-1]
+    qfun = lambda b, i: oracle.dense_q(qi[b, i], qp[b, i], qn[b, i], V)  # noqa: E731
+    return g, xn, o, qfun
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("V,topk,peak", [(5003, 20, 12.0), (40000, 7, 20.0), (151936, 256, 20.0)])
+def test_sparse_parity(dev, dtype, V, topk, peak):
+    say("sparse", dtype, V, topk)
+    x = workloads.sparse_inputs(66, 12, 8, V, dtype, topk=topk, peak=peak, random_lengths=True)
+    g, xn, o, qfun = _sparse_run(dev, x)
+    near = check_sampling(g, xn, o, 0.0, x["temperature"], x["temperature"], str(dtype).split(".")[-1], qfun=qfun)
+    say("h", list(o["accept_len"]), "near", dict(near))
+
+
+def test_sparse_full_support_equals_rejection(dev):
+    # every token stored: the dense drafter distribution
+    say("sparse = rejection")
+    B, K, V = 6, 4, 256
+    x = workloads.chain_inputs(67, B, K, V, torch.float32, sigma=1.0, random_lengths=True)
+    q = torch.softmax(x["drf"].float(), dim=-1)
+    perm = torch.randperm(V, generator=torch.Generator().manual_seed(5))
+    sx = dict(tgt=x["tgt"], q_idx=perm.expand(B, K, V).to(torch.int32).clone(),
+              q_prob=q[:, :, perm].contiguous(), q_nnz=torch.full((B, K), V, dtype=torch.int32),
+              draft_tokens=x["draft_tokens"], u_accept=x["u_accept"], u_resample=x["u_resample"],
+              draft_len=x["draft_len"], temperature=1.0)
+    g, xn, o, qfun = _sparse_run(dev, sx)
+    check_sampling(g, xn, o, 0.0, 1.0, 1.0, "float32", qfun=qfun)
+    r = oracle.verify_rejection(np64(x["tgt"]), np64(x["drf"]), npi(x["draft_tokens"]), npi(x["draft_len"]),
+                                1.0, 1.0, np64(x["u_accept"]), np64(x["u_resample"]))
+    np.testing.assert_array_equal(o["accept_len"], r["accept_len"])
+
+
+def test_sparse_edge_cases(dev):
+    say("sparse edge cases")
+    B, K, V = 9, 4, 3001
+    x = workloads.sparse_inputs(68, B, K, V, torch.float32, topk=5, kmax=8, peak=12.0)
+    x["q_nnz"][0, 1] = 9                     # more entries than kmax
+    x["q_idx"][1, 0, 2] = V                  # token out of range
+    x["q_prob"][2, 2, 0] = -0.5              # negative probability
+    x["q_prob"][3, 0, 4] = float("inf")
+    x["q_idx"][4, 3, 6] = -7                 # beyond q_nnz: never read
+    x["q_nnz"][5, 0] = 0                     # empty stored Q: d has Q = 0
+    x["draft_len"][6] = 0                    # bonus only
+    x["draft_len"][7] = 2
+    x["q_prob"][7, 3, 0] = float("nan")      # row beyond n: never read
+    # the draft token of sequence 8, row 1, is outside its stored support
+    x["q_idx"][8, 1, :5] = torch.arange(5, dtype=torch.int32) + int(x["draft_tokens"][8, 1]) + 1
+    x["q_idx"][8, 1, :5] %= V
+    g, xn, o, qfun = _sparse_run(dev, x)
+    assert list(o["status"][:4]) == [1, 1, 1, 1] and o["status"][4] == 0, o["status"]
+    check_sampling(g, xn, o, 0.0, 1.0, 1.0, "float32", qfun=qfun)
+    eos = int(x["draft_tokens"][4, 0])
+    bud = torch.tensor([3, 3, 3, 3, 3, 3, 3, 1, 0], dtype=torch.int32)
+    g, xn, o, qfun = _sparse_run(dev, x, eos_id=eos, len_budget=bud)
+    check_sampling(g, xn, o, 0.0, 1.0, 1.0, "float32", eos_id=eos, len_budget=npi(bud), qfun=qfun)
+
+
 # ------------------------------------------------------- joint-space chain ---
 
 def _spot_np(x):

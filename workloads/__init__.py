@@ -332,3 +332,45 @@ def config4_spot_chain(device="cpu"):
     """Joint-space chain, hybrid gate: B=16 sequences, K=8 links, V=151936
     bf16, sigma=1, T=1, Gumbel rows for every target row."""
     return spot_chain_inputs(41, 16, 8, 151936, torch.bfloat16, device=device)
+
+
+# ------------------------------------------------------------- sparse Q --
+
+def sparse_inputs(c, B, K, V, dtype=torch.bfloat16, topk=20, sigma=1.0, temperature=1.0,
+                  random_lengths=False, kmax=None, peak=6.0, device="cpu"):
+    """A drafted chain whose drafter distributions are stored sparse: each
+    draft row keeps the ``topk`` most likely tokens of softmax(drafter / T),
+    renormalised (top-k truncation), as (token, probability) entries sorted
+    by probability; the draft token is drawn from that truncated Q with a
+    seeded uniform.  Target rows [B, K+1, V]: z ~ N(0, 3^2) + ``peak`` at one
+    token; the drafter logits z + N(0, sigma^2) are not passed on.
+    """
+    kmax = topk if kmax is None else kmax
+    tgt = _planted_logits(c, (B, K + 1, V), peak, dtype, device)
+    drf = (tgt[:, :K].float() + torch.randn(B, K, V, generator=_gen(c, 2, device), device=device) * sigma)
+    probs = torch.softmax(drf / temperature, dim=-1)
+    top = torch.topk(probs, topk, dim=-1)
+    qp = top.values / top.values.sum(dim=-1, keepdim=True)
+    u = torch.rand(B, K, 1, generator=_gen(c, 3, device), device=device)
+    pick = (torch.cumsum(qp, dim=-1) <= u * qp.sum(dim=-1, keepdim=True)).sum(dim=-1).clamp(max=topk - 1)
+    d = torch.gather(top.indices, -1, pick.unsqueeze(-1)).squeeze(-1)
+    q_idx = torch.zeros(B, K, kmax, dtype=torch.int32)
+    q_prob = torch.zeros(B, K, kmax, dtype=torch.float32)
+    q_idx[:, :, :topk] = top.indices.to(torch.int32).cpu()
+    q_prob[:, :, :topk] = qp.float().cpu()
+    q_nnz = torch.full((B, K), topk, dtype=torch.int32)
+    u_acc = torch.rand(B, K, generator=_gen(c, 4, device), device=device)
+    u_res = torch.rand(B, K + 1, generator=_gen(c, 5, device), device=device)
+    if random_lengths:
+        n = torch.randint(0, K + 1, (B,), generator=_gen(c, 8, "cpu"))
+    else:
+        n = torch.full((B,), K, dtype=torch.int64)
+    return dict(tgt=tgt, q_idx=q_idx, q_prob=q_prob, q_nnz=q_nnz, draft_tokens=d.to(torch.int32).cpu(),
+                u_accept=u_acc, u_resample=u_res, draft_len=n.to(torch.int32), temperature=temperature)
+
+
+def config3_sparse(device="cpu"):
+    """Sparse stored-Q verify: B=32, K=16, V=151936 bf16, top-k = 20 drafter
+    storage (the truncation Qwen3 recommends for this vocabulary), T=1, a
+    +20 target peak (the target's argmax carries most of the mass)."""
+    return sparse_inputs(31, 32, 16, 151936, torch.bfloat16, topk=20, peak=20.0, device=device)
