@@ -468,6 +468,11 @@ __device__ __forceinline__ float group_exclusive_scan_f(float v, float& total, f
   return base + inc - v;
 }
 
+// Rule families, one set of draw kernels each, so that no family carries
+// another's code: the token chain (linear and Cactus rules), the joint-space
+// chain, and the token chain against stored sparse Q.
+enum : int { FAM_TOKEN = 0, FAM_SPOT = 1, FAM_SPARSE = 2 };
+
 // LDS of the decision step (per sequence): row statistics of the target rows
 // 0..n and drafter rows 0..n-1, and d, p(d), p~(d), q(d) of the rejected
 // draft.
@@ -492,7 +497,7 @@ struct DecideLds {
 //     data error, every output).
 // Returns the draw record: row h, its weight parameters and the uniform; its
 // status carries the error bits when there is nothing to draw.
-template <int DT, int NT>
+template <int DT, int NT, int FAM>
 __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, DecideLds& s) {
   constexpr int DPT = (kMaxDraft + NT - 1) / NT;   // drafts of one thread
   using E = Elem<DT>;
@@ -503,8 +508,8 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
   const int p0 = a.pre[b];
   const int R = a.pre[a.B];
   const int32_t* d = a.draft_tokens + static_cast<int64_t>(b) * a.K;
-  const bool spot = a.rule == RULE_SPOT;
-  const bool sparse = a.rule == RULE_SPARSE;
+  constexpr bool spot = FAM == FAM_SPOT;
+  constexpr bool sparse = FAM == FAM_SPARSE;
   int di[DPT], psk[DPT], ppk[DPT];
   float ui[DPT], xi[DPT], yi[DPT], ck[DPT];
 #pragma unroll
@@ -764,12 +769,12 @@ __device__ __forceinline__ void draw_rows(const SampleArgs& a, int b, int h, boo
 // tiles of row h: [p~ - q]_+ against drafter row h if a draft was rejected,
 // else the bonus weight p.  Against a stored sparse Q the masses are those of
 // p; the select step redoes the tiles that hold stored entries.
-template <int DT>
+template <int DT, int FAM>
 __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   __shared__ DecideLds s;
   const int b = blockIdx.x / a.chunks;
   const int c = blockIdx.x - b * a.chunks;
-  const DrawRecord rec = draw_decide<DT, kBlock>(a, b, c == 0, s);
+  const DrawRecord rec = draw_decide<DT, kBlock, FAM>(a, b, c == 0, s);
   if (c == 0 && threadIdx.x == 0) a.rec[b] = rec;
   if ((rec.status & SEQ_ERROR_MASK) || rec.fixed >= 0) return;
   const char *xr, *yr;
@@ -778,7 +783,7 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   const int t_lo = c * a.tpc;
   const int t_hi = t_lo + a.tpc < a.tiles ? t_lo + a.tpc : a.tiles;
   DrawWeight w = draw_weight(a, rec);
-  if (w.resid == 2) w.resid = 0;
+  if (FAM == FAM_SPARSE && w.resid == 2) w.resid = 0;
   tile_masses<DT, kWaves>(xr, yr, a.V, t_lo, t_hi, vec, w, a.tmass + static_cast<int64_t>(b) * a.tiles);
 }
 
@@ -789,7 +794,10 @@ struct SelectLds {
   float w[kDrawWaves];
   float Z, base;
   int ct, lt, cs, pick, a;
-  // stored sparse Q of row h: its entries and the tiles that hold them
+};
+
+// The stored sparse Q of row h: its entries and the tiles that hold them.
+struct SparseLds {
   int sidx[kMaxNnz];
   float sprob[kMaxNnz];
   unsigned aff[kMaxDrawTiles / 32];
@@ -797,14 +805,30 @@ struct SelectLds {
   int naff, nnz;
 };
 
-// The residual weight [p - Q]_+ of element e against the stored entries of
-// Q in LDS (a linear scan: Q has at most kMaxNnz entries).
-__device__ __forceinline__ float sparse_weight(const DrawWeight& w, const SelectLds& s, uint32_t e, float x) {
-  const float p = fast_exp2(__builtin_fmaf(x, w.kp, w.cp)) * w.isp;
-  float q = 0.f;
-  for (int k = 0; k < s.nnz; ++k)
-    if (s.sidx[k] == static_cast<int>(e)) q += s.sprob[k];
-  return fmaxf(p - q, 0.f);
+// Residual weights [p - Q]_+ of one lane's N consecutive elements e0.. with
+// logits x, against the stored entries of Q in LDS: one pass over the
+// entries (at most kMaxNnz, the same address for every lane) adds each
+// entry's probability to the element it names.  Elements at or past V get
+// weight 0.
+template <int N>
+__device__ __forceinline__ void sparse_weights(const DrawWeight& w, const SparseLds& s, int64_t e0, int64_t V,
+                                               const float (&x)[N], float (&out)[N]) {
+  float q[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) q[j] = 0.f;
+  const int nnz = s.nnz;
+#pragma unroll 4
+  for (int k = 0; k < nnz; ++k) {
+    const int64_t d = s.sidx[k] - e0;
+    const float pr = s.sprob[k];
+#pragma unroll
+    for (int j = 0; j < N; ++j) q[j] += d == j ? pr : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const float p = fast_exp2(__builtin_fmaf(x[j], w.kp, w.cp)) * w.isp;
+    out[j] = e0 + j < V ? fmaxf(p - q[j], 0.f) : 0.f;
+  }
 }
 
 // The draw of sequence b by kDrawThreads threads, given its record and this
@@ -815,11 +839,10 @@ __device__ __forceinline__ float sparse_weight(const DrawWeight& w, const Select
 // ending condition.
 // dt is this thread's draft token d_{t+1} (t < K), requested with the first
 // loads; every output position i < h <= K <= kDrawThreads is some thread's t.
-// SPARSE: the call may verify against a stored sparse Q (the fused draw
-// never does).
+// SPARSE: the call verifies against a stored sparse Q, whose LDS is sp.
 template <int DT, bool SPARSE>
 __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, int budget, int dt,
-                            const float (&m0)[kDrawTilesPerThread], SelectLds& s) {
+                            const float (&m0)[kDrawTilesPerThread], SelectLds& s, SparseLds* sp) {
   static_assert(kMaxDraft <= kDrawThreads, "one draft token per thread");
   using E = Elem<DT>;
   const int t = threadIdx.x;
@@ -847,29 +870,32 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
     const int nnz = a.qnnz[row];
     for (int k = 0; k < kDrawTilesPerThread; ++k)
       if (k < q && t * q + k < ntiles) s.tile[t * q + k] = mt[k] * w.isp;
-    for (int i = t; i < (ntiles + 31) / 32; i += kDrawThreads) s.aff[i] = 0u;
+    for (int i = t; i < (ntiles + 31) / 32; i += kDrawThreads) sp->aff[i] = 0u;
     for (int e = t; e < nnz; e += kDrawThreads) {
-      s.sidx[e] = a.qidx[row * a.kmax + e];
-      s.sprob[e] = a.qprob[row * a.kmax + e];
+      sp->sidx[e] = a.qidx[row * a.kmax + e];
+      sp->sprob[e] = a.qprob[row * a.kmax + e];
     }
     if (t == 0) {
-      s.naff = 0;
-      s.nnz = nnz;
+      sp->naff = 0;
+      sp->nnz = nnz;
     }
     __syncthreads();
     for (int e = t; e < nnz; e += kDrawThreads) {
-      const int tile = s.sidx[e] / TE;
+      const int tile = sp->sidx[e] / TE;
       const unsigned bit = 1u << (tile & 31);
-      if (!(atomicOr(&s.aff[tile >> 5], bit) & bit)) s.afflist[atomicAdd(&s.naff, 1)] = tile;
+      if (!(atomicOr(&sp->aff[tile >> 5], bit) & bit)) sp->afflist[atomicAdd(&sp->naff, 1)] = tile;
     }
     __syncthreads();
-    for (int i = wv; i < s.naff; i += kDrawWaves) {
-      const int tile = s.afflist[i];
+    for (int i = wv; i < sp->naff; i += kDrawWaves) {
+      const int tile = sp->afflist[i];
+      const int64_t e0 = static_cast<int64_t>(tile) * TE + lane * E::kVec;
+      float x[E::kVec], wt[E::kVec];
+#pragma unroll
+      for (int j = 0; j < E::kVec; ++j) x[j] = e0 + j < a.V ? E::load1(xr, e0 + j) : 0.f;
+      sparse_weights<E::kVec>(w, *sp, e0, a.V, x, wt);
       float m = 0.f;
-      for (int j = 0; j < E::kVec; ++j) {
-        const int64_t e = static_cast<int64_t>(tile) * TE + lane * E::kVec + j;
-        if (e < a.V) m += sparse_weight(w, s, static_cast<uint32_t>(e), E::load1(xr, e));
-      }
+#pragma unroll
+      for (int j = 0; j < E::kVec; ++j) m += wt[j];
 #pragma unroll
       for (int sh = 32; sh >= 1; sh >>= 1) m += wave_shfl_xor(m, sh);
       if (lane == 0) s.tile[tile] = m;
@@ -952,14 +978,20 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
     const int64_t e0 = static_cast<int64_t>(ct) * TE + lane * E::kVec;
     float wt[E::kVec];
     float loc = 0.f;
+    if (SPARSE && w.resid == 2) {
+      float x[E::kVec];
 #pragma unroll
-    for (int j = 0; j < E::kVec; ++j) {
-      const int64_t e = e0 + j;
-      if (e >= a.V) wt[j] = 0.f;
-      else if (SPARSE && w.resid == 2) wt[j] = sparse_weight(w, s, static_cast<uint32_t>(e), E::load1(xr, e));
-      else wt[j] = w.at(static_cast<uint32_t>(e), E::load1(xr, e), w.resid ? E::load1(yr, e) : 0.f);
-      loc += wt[j];
+      for (int j = 0; j < E::kVec; ++j) x[j] = e0 + j < a.V ? E::load1(xr, e0 + j) : 0.f;
+      sparse_weights<E::kVec>(w, *sp, e0, a.V, x, wt);
+    } else {
+#pragma unroll
+      for (int j = 0; j < E::kVec; ++j) {
+        const int64_t e = e0 + j;
+        wt[j] = e < a.V ? w.at(static_cast<uint32_t>(e), E::load1(xr, e), w.resid ? E::load1(yr, e) : 0.f) : 0.f;
+      }
     }
+#pragma unroll
+    for (int j = 0; j < E::kVec; ++j) loc += wt[j];
     float inc = loc;
 #pragma unroll
     for (int k = 1; k < 64; k <<= 1) {
@@ -1010,7 +1042,7 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
 
 // Second kernel of the split draw: one group per sequence reads the record
 // and the tile masses that k_draw_mass wrote.
-template <int DT>
+template <int DT, int FAM>
 __global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
   __shared__ SelectLds s;
   const int b = blockIdx.x;
@@ -1030,19 +1062,25 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
     m0[k] = (k < q && tile < ntiles) ? tmass[tile] : 0.f;
   }
   if (rec.status & SEQ_ERROR_MASK) return;          // outputs already written
-  draw_select<DT, true>(a, b, rec, budget, dt, m0, s);
+  if constexpr (FAM == FAM_SPARSE) {
+    __shared__ SparseLds sp;
+    draw_select<DT, true>(a, b, rec, budget, dt, m0, s, &sp);
+  } else {
+    draw_select<DT, false>(a, b, rec, budget, dt, m0, s, nullptr);
+  }
 }
 
 // The whole draw of one sequence in one group of kDrawThreads threads (for
 // rows of at most kFusedDrawTiles tiles): the decision, every tile mass of
 // row h into LDS, then the draw.
-template <int DT>
+template <int DT, int FAM>
 __global__ __launch_bounds__(kDrawThreads) void k_draw_fused(SampleArgs a) {
+  static_assert(FAM != FAM_SPARSE, "stored sparse Q takes the split draw");
   __shared__ DecideLds sd;
   __shared__ SelectLds s;
   const int b = blockIdx.x;
   const int t = threadIdx.x;
-  const DrawRecord rec = draw_decide<DT, kDrawThreads>(a, b, true, sd);
+  const DrawRecord rec = draw_decide<DT, kDrawThreads, FAM>(a, b, true, sd);
   if (rec.status & SEQ_ERROR_MASK) return;
   const int budget = a.budget ? a.budget[b] : INT_MAX;
   const int dt = t < a.K ? a.draft_tokens[static_cast<int64_t>(b) * a.K + t] : -1;
@@ -1060,7 +1098,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_fused(SampleArgs a) {
     m0[k] = (k < q && tile < ntiles) ? s.tile[tile] : 0.f;
   }
   __syncthreads();   // the fallback in draw_select may overwrite s.tile
-  draw_select<DT, false>(a, b, rec, budget, dt, m0, s);
+  draw_select<DT, false>(a, b, rec, budget, dt, m0, s, nullptr);
 }
 
 // ============================================================== launches ===
@@ -1081,11 +1119,21 @@ bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const Tim
   const void* rows = a.gumbel ? (bf ? fn(k_sample_rows<DT_BF16, true>) : fn(k_sample_rows<DT_F32, true>))
                               : (bf ? fn(k_sample_rows<DT_BF16, false>) : fn(k_sample_rows<DT_F32, false>));
   if (!launch(rows, a.grid, stream, a, ev)) return false;
-  if (a.tiles <= kFusedDrawTiles && a.rule != RULE_SPARSE)
-    return launch_threads(bf ? fn(k_draw_fused<DT_BF16>) : fn(k_draw_fused<DT_F32>), a.B, kDrawThreads, stream, a);
-  return launch(bf ? fn(k_draw_mass<DT_BF16>) : fn(k_draw_mass<DT_F32>), static_cast<int64_t>(a.B) * a.chunks,
-                stream, a) &&
-         launch_threads(bf ? fn(k_draw_select<DT_BF16>) : fn(k_draw_select<DT_F32>), a.B, kDrawThreads, stream, a);
+  const int fam = a.rule == RULE_SPOT ? FAM_SPOT : (a.rule == RULE_SPARSE ? FAM_SPARSE : FAM_TOKEN);
+  // [family][dtype == bf16]
+  static const void* const fused[2][2] = {{fn(k_draw_fused<DT_F32, FAM_TOKEN>), fn(k_draw_fused<DT_BF16, FAM_TOKEN>)},
+                                          {fn(k_draw_fused<DT_F32, FAM_SPOT>), fn(k_draw_fused<DT_BF16, FAM_SPOT>)}};
+  static const void* const mass[3][2] = {{fn(k_draw_mass<DT_F32, FAM_TOKEN>), fn(k_draw_mass<DT_BF16, FAM_TOKEN>)},
+                                         {fn(k_draw_mass<DT_F32, FAM_SPOT>), fn(k_draw_mass<DT_BF16, FAM_SPOT>)},
+                                         {fn(k_draw_mass<DT_F32, FAM_SPARSE>), fn(k_draw_mass<DT_BF16, FAM_SPARSE>)}};
+  static const void* const select[3][2] = {
+      {fn(k_draw_select<DT_F32, FAM_TOKEN>), fn(k_draw_select<DT_BF16, FAM_TOKEN>)},
+      {fn(k_draw_select<DT_F32, FAM_SPOT>), fn(k_draw_select<DT_BF16, FAM_SPOT>)},
+      {fn(k_draw_select<DT_F32, FAM_SPARSE>), fn(k_draw_select<DT_BF16, FAM_SPARSE>)}};
+  if (a.tiles <= kFusedDrawTiles && fam != FAM_SPARSE)
+    return launch_threads(fused[fam][bf], a.B, kDrawThreads, stream, a);
+  return launch(mass[fam][bf], static_cast<int64_t>(a.B) * a.chunks, stream, a) &&
+         launch_threads(select[fam][bf], a.B, kDrawThreads, stream, a);
 }
 
 }  // namespace dbv
