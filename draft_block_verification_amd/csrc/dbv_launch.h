@@ -62,6 +62,7 @@ struct SampleArgs {
   int32_t* pre;                        // [B + 1] first stream row per sequence
   DrawRecord* rec;                     // per sequence
   float* tmass;                        // per (sequence, draw tile)
+  SparseRow* sq;                       // per sequence: stored sparse Q of row h
   int64_t grid;                        // groups of the row-streaming launch
   int tiles;                           // draw tiles per row
   int tpc;                             // draw tiles per mass-kernel group

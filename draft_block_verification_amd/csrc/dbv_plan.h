@@ -205,6 +205,15 @@ struct DrawRecord {
                      // commit) and nothing is drawn; -1 otherwise
 };
 
+// The stored sparse Q of the draw row h, handed from the mass kernel to the
+// select kernel (which then reads it together with the record).
+struct SparseRow {
+  int nnz;
+  int pad[3];
+  int idx[kMaxNnz];
+  float prob[kMaxNnz];
+};
+
 // Stream order: for each sequence b, target rows 0..n_b, then drafter rows
 // 0..n_b-1.  With Gumbel rows each target row is cut into gumbel_parts(eb)
 // stream rows ("parts"), so that every stream row carries about the same
@@ -233,6 +242,7 @@ struct SamplePlan {
   size_t off_pre;      // int32 [B + 1]: first stream row of each sequence
   size_t off_rec;      // DrawRecord per sequence
   size_t off_tmass;    // float per (sequence, draw tile)
+  size_t off_sq;       // SparseRow per sequence (stored sparse Q of row h)
   size_t bytes;
 };
 
@@ -248,7 +258,8 @@ inline SamplePlan plan_sample(int B, int K, int V, int64_t elem_bytes) {
   p.off_pre = p.off_gpart + partial_bytes(p.max_vrows);
   p.off_rec = p.off_pre + align256(static_cast<size_t>(B + 1) * 4);
   p.off_tmass = p.off_rec + align256(static_cast<size_t>(B) * sizeof(DrawRecord));
-  p.bytes = p.off_tmass + align256(static_cast<size_t>(B) * p.tiles * 4);
+  p.off_sq = p.off_tmass + align256(static_cast<size_t>(B) * p.tiles * 4);
+  p.bytes = p.off_sq + align256(static_cast<size_t>(B) * sizeof(SparseRow));
   return p;
 }
 

@@ -398,14 +398,40 @@ constexpr int kTileBatch = 8;   // tiles a wave reads together (16 loads per lan
 // vector) elements are loaded one by one.  Byte offsets stay below 2^32
 // (V <= kMaxSampleV), so the loads take a uniform 64-bit base and 32-bit lane
 // offsets.
-template <int DT, int NW, int TB = kTileBatch>
+// Stored entries of a sparse Q that fall in some element range, in LDS:
+// Q(v) is the sum of the entries naming v (zero off the list).
+struct QList {
+  const int* idx;
+  const float* prob;
+  int n;
+  // Q of the N consecutive elements from e0.
+  template <int N>
+  __device__ __forceinline__ void lookup(uint32_t e0, float (&q)[N]) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) q[j] = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < n; ++k) {
+      const uint32_t d = static_cast<uint32_t>(idx[k]) - e0;
+      const float pr = prob[k];
+#pragma unroll
+      for (int j = 0; j < N; ++j) q[j] += d == static_cast<uint32_t>(j) ? pr : 0.f;
+    }
+  }
+};
+
+// SP: the residual against a stored sparse Q, weight [p - Q]_+ with p =
+// exp2(x kp + cp) isp and Q from `ql`; no drafter row is read.
+template <int DT, int NW, int TB = kTileBatch, bool SP = false>
 __device__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo, int t_hi, bool vec,
-                            const DrawWeight& w, float* out) {
+                            const DrawWeight& w, float* out, const QList* ql = nullptr) {
   using E = Elem<DT>;
   constexpr int W = E::kVec;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const uint32_t Vn = static_cast<uint32_t>(V);
+  auto sparse_w = [&](float x, float q) {
+    return fmaxf(fast_exp2(__builtin_fmaf(x, w.kp, w.cp)) * w.isp - q, 0.f);
+  };
   for (int t0 = t_lo + wv; t0 < t_hi; t0 += NW * TB) {
     u32x4 rx[TB], ry[TB];
     bool full[TB];
@@ -416,7 +442,7 @@ __device__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo,
       full[k] = vec && tile < t_hi && e + W <= Vn;
       if (full[k]) {
         rx[k] = load16(xr + e * E::kBytes);
-        ry[k] = w.resid ? load16(yr + e * E::kBytes) : rx[k];
+        ry[k] = (!SP && w.resid) ? load16(yr + e * E::kBytes) : rx[k];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -426,7 +452,18 @@ __device__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo,
       if (tile < t_hi) {   // uniform across the wave
         const uint32_t e = static_cast<uint32_t>(tile) * (64 * W) + lane * W;
         float m = 0.f;
-        if (full[k]) {
+        if constexpr (SP) {
+          float x[W], q[W];
+          if (full[k]) {
+            E::unpack(rx[k], x);
+          } else {
+#pragma unroll
+            for (int j = 0; j < W; ++j) x[j] = e + j < Vn ? E::load1(xr, e + j) : 0.f;
+          }
+          ql->lookup<W>(e, q);
+#pragma unroll
+          for (int j = 0; j < W; ++j) m += e + j < Vn ? sparse_w(x[j], q[j]) : 0.f;
+        } else if (full[k]) {
           float x[W], y[W];
           E::unpack(rx[k], x);
           E::unpack(ry[k], y);
@@ -782,9 +819,44 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   const bool vec = ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0;
   const int t_lo = c * a.tpc;
   const int t_hi = t_lo + a.tpc < a.tiles ? t_lo + a.tpc : a.tiles;
-  DrawWeight w = draw_weight(a, rec);
-  if (FAM == FAM_SPARSE && w.resid == 2) w.resid = 0;
-  tile_masses<DT, kWaves>(xr, yr, a.V, t_lo, t_hi, vec, w, a.tmass + static_cast<int64_t>(b) * a.tiles);
+  const DrawWeight w = draw_weight(a, rec);
+  float* out = a.tmass + static_cast<int64_t>(b) * a.tiles;
+  if constexpr (FAM == FAM_SPARSE) {
+    if (w.resid == 2) {
+      // Residual against the stored Q of row h: the entries that fall in this
+      // group's tiles go to LDS; chunk 0 hands the whole row to the select
+      // kernel.
+      __shared__ int c_idx[kMaxNnz];
+      __shared__ float c_prob[kMaxNnz];
+      __shared__ int c_n;
+      constexpr int TE = 64 * Elem<DT>::kVec;
+      const int64_t row = static_cast<int64_t>(b) * a.K + rec.h;
+      const int nnz = a.qnnz[row];
+      const int t = threadIdx.x;
+      if (t == 0) c_n = 0;
+      __syncthreads();
+      SparseRow* sr = a.sq + b;
+      for (int e = t; e < nnz; e += kBlock) {
+        const int v = a.qidx[row * a.kmax + e];
+        const float pr = a.qprob[row * a.kmax + e];
+        if (c == 0) {
+          sr->idx[e] = v;
+          sr->prob[e] = pr;
+        }
+        if (v >= t_lo * TE && v < t_hi * TE) {
+          const int k = atomicAdd(&c_n, 1);
+          c_idx[k] = v;
+          c_prob[k] = pr;
+        }
+      }
+      if (c == 0 && t == 0) sr->nnz = nnz;
+      __syncthreads();
+      const QList ql{c_idx, c_prob, c_n};
+      tile_masses<DT, kWaves, 4, true>(xr, yr, a.V, t_lo, t_hi, vec, w, out, &ql);
+      return;
+    }
+  }
+  tile_masses<DT, kWaves>(xr, yr, a.V, t_lo, t_hi, vec, w, out);
 }
 
 constexpr int kDrawWaves = kDrawThreads / 64;
@@ -796,40 +868,13 @@ struct SelectLds {
   int ct, lt, cs, pick, a;
 };
 
-// The stored sparse Q of row h: its entries and the tiles that hold them.
+// The stored sparse Q of row h, as the mass kernel handed it over.
 struct SparseLds {
-  int sidx[kMaxNnz];
-  float sprob[kMaxNnz];
-  unsigned aff[kMaxDrawTiles / 32];
-  int afflist[kMaxNnz];
-  int naff, nnz;
+  int idx[kMaxNnz];
+  float prob[kMaxNnz];
+  int nnz;
 };
 
-// Residual weights [p - Q]_+ of one lane's N consecutive elements e0.. with
-// logits x, against the stored entries of Q in LDS: one pass over the
-// entries (at most kMaxNnz, the same address for every lane) adds each
-// entry's probability to the element it names.  Elements at or past V get
-// weight 0.
-template <int N>
-__device__ __forceinline__ void sparse_weights(const DrawWeight& w, const SparseLds& s, int64_t e0, int64_t V,
-                                               const float (&x)[N], float (&out)[N]) {
-  float q[N];
-#pragma unroll
-  for (int j = 0; j < N; ++j) q[j] = 0.f;
-  const int nnz = s.nnz;
-#pragma unroll 4
-  for (int k = 0; k < nnz; ++k) {
-    const int64_t d = s.sidx[k] - e0;
-    const float pr = s.sprob[k];
-#pragma unroll
-    for (int j = 0; j < N; ++j) q[j] += d == j ? pr : 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < N; ++j) {
-    const float p = fast_exp2(__builtin_fmaf(x[j], w.kp, w.cp)) * w.isp;
-    out[j] = e0 + j < V ? fmaxf(p - q[j], 0.f) : 0.f;
-  }
-}
 
 // The draw of sequence b by kDrawThreads threads, given its record and this
 // thread's tile masses m0 (tiles [t*q, (t+1)*q), q = ceil(tiles / threads)):
@@ -861,53 +906,6 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
   float mt[kDrawTilesPerThread];
 #pragma unroll
   for (int k = 0; k < kDrawTilesPerThread; ++k) mt[k] = m0[k];
-  if (SPARSE && draw && w.resid == 2) {
-    // Residual against a stored sparse Q: the tile masses are those of p
-    // (unnormalised exp2 weights, scaled here by 1/S), and every tile
-    // holding a stored entry is summed again from its exact weights
-    // [p - Q]_+ (all zero gives exactly zero).
-    const int64_t row = static_cast<int64_t>(b) * a.K + h;
-    const int nnz = a.qnnz[row];
-    for (int k = 0; k < kDrawTilesPerThread; ++k)
-      if (k < q && t * q + k < ntiles) s.tile[t * q + k] = mt[k] * w.isp;
-    for (int i = t; i < (ntiles + 31) / 32; i += kDrawThreads) sp->aff[i] = 0u;
-    for (int e = t; e < nnz; e += kDrawThreads) {
-      sp->sidx[e] = a.qidx[row * a.kmax + e];
-      sp->sprob[e] = a.qprob[row * a.kmax + e];
-    }
-    if (t == 0) {
-      sp->naff = 0;
-      sp->nnz = nnz;
-    }
-    __syncthreads();
-    for (int e = t; e < nnz; e += kDrawThreads) {
-      const int tile = sp->sidx[e] / TE;
-      const unsigned bit = 1u << (tile & 31);
-      if (!(atomicOr(&sp->aff[tile >> 5], bit) & bit)) sp->afflist[atomicAdd(&sp->naff, 1)] = tile;
-    }
-    __syncthreads();
-    for (int i = wv; i < sp->naff; i += kDrawWaves) {
-      const int tile = sp->afflist[i];
-      const int64_t e0 = static_cast<int64_t>(tile) * TE + lane * E::kVec;
-      float x[E::kVec], wt[E::kVec];
-#pragma unroll
-      for (int j = 0; j < E::kVec; ++j) x[j] = e0 + j < a.V ? E::load1(xr, e0 + j) : 0.f;
-      sparse_weights<E::kVec>(w, *sp, e0, a.V, x, wt);
-      float m = 0.f;
-#pragma unroll
-      for (int j = 0; j < E::kVec; ++j) m += wt[j];
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) m += wave_shfl_xor(m, sh);
-      if (lane == 0) s.tile[tile] = m;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kDrawTilesPerThread; ++k) {
-      const int tile = t * q + k;
-      mt[k] = (k < q && tile < ntiles) ? s.tile[tile] : 0.f;
-    }
-    __syncthreads();   // s.tile is reused by the zero-mass fallback
-  }
 
   // Thread t holds the masses of tiles [t*q, (t+1)*q); an exclusive scan
   // gives it the mass before them, and the group's total Z.
@@ -979,10 +977,15 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
     float wt[E::kVec];
     float loc = 0.f;
     if (SPARSE && w.resid == 2) {
-      float x[E::kVec];
+      // [p - Q]_+ against the stored Q of row h (as in the mass kernel)
+      float q[E::kVec];
+      const QList ql{sp->idx, sp->prob, sp->nnz};
+      ql.lookup<E::kVec>(static_cast<uint32_t>(e0), q);
 #pragma unroll
-      for (int j = 0; j < E::kVec; ++j) x[j] = e0 + j < a.V ? E::load1(xr, e0 + j) : 0.f;
-      sparse_weights<E::kVec>(w, *sp, e0, a.V, x, wt);
+      for (int j = 0; j < E::kVec; ++j)
+        wt[j] = e0 + j < a.V
+                    ? fmaxf(fast_exp2(__builtin_fmaf(E::load1(xr, e0 + j), w.kp, w.cp)) * w.isp - q[j], 0.f)
+                    : 0.f;
     } else {
 #pragma unroll
       for (int j = 0; j < E::kVec; ++j) {
@@ -1061,11 +1064,21 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
     const int tile = t * q + k;
     m0[k] = (k < q && tile < ntiles) ? tmass[tile] : 0.f;
   }
-  if (rec.status & SEQ_ERROR_MASK) return;          // outputs already written
   if constexpr (FAM == FAM_SPARSE) {
+    // The stored Q of row h, requested with the record (entries past nnz
+    // are never used).
     __shared__ SparseLds sp;
+    const SparseRow* sr = a.sq + b;
+    for (int e = t; e < kMaxNnz; e += kDrawThreads) {
+      sp.idx[e] = sr->idx[e];
+      sp.prob[e] = sr->prob[e];
+    }
+    if (t == 0) sp.nnz = sr->nnz;
+    __syncthreads();
+    if (rec.status & SEQ_ERROR_MASK) return;        // outputs already written
     draw_select<DT, true>(a, b, rec, budget, dt, m0, s, &sp);
   } else {
+    if (rec.status & SEQ_ERROR_MASK) return;        // outputs already written
     draw_select<DT, false>(a, b, rec, budget, dt, m0, s, nullptr);
   }
 }
