@@ -23,6 +23,8 @@ following the pages' definitions in their own order:
   tree (and its T=0 greedy special case).
 * ``sparse`` -- lossless verification against a stored sparse (top-k /
   top-p) drafter distribution.
+* ``truncate`` -- top-k / top-p truncation of drafter rows into that stored
+  sparse form.
 * ``spot``   -- chain verification on the joint (position, token) space:
   rejection sampling per link (SPOT App. B) and the confidence-gated hybrid
   of coupled-noise match and rejection sampling.
@@ -53,6 +55,7 @@ from .cactus import (  # noqa: F401
 )
 from .anyorder import NO_END, verify_greedy_any_order  # noqa: F401
 from .sparse import dense_q, verify_sparse  # noqa: F401
+from .truncate import truncate_row, truncate_rows  # noqa: F401
 from .spot import MODE_RS, MODE_MATCH, rs_link, rs_residual, verify_spot_chain  # noqa: F401
 from .tree import (  # noqa: F401
     TREE_STATE_EQUALITY, TREE_FIXED_POSITION, state_transition, walk,

@@ -277,3 +277,50 @@ def test_sparse_pin_catches_planted_mistake(monkeypatch, name, fn, pin):
     monkeypatch.setattr(sparse, name, fn)
     with pytest.raises(AssertionError):
         pin()
+
+
+# ------------------------------------------------- top-k / top-p storage ---
+
+import tests.test_oracle_truncate_pins as tq  # noqa: E402
+import oracle.truncate as truncate  # noqa: E402
+
+_truncate_row = truncate.truncate_row
+
+
+def _tq_ties_high(x, temperature, top_k, top_p):
+    x = np.asarray(x, np.float64)
+    rev = x[::-1]
+    idx, prob = _truncate_row(rev, temperature, top_k, top_p)
+    return (x.size - 1 - idx), prob
+
+
+def _tq_p_exclusive(x, temperature, top_k, top_p):
+    idx, prob = _truncate_row(x, temperature, top_k, top_p)
+    if top_p < 1.0 and idx.size > 1:
+        idx, prob = idx[:-1], prob[:-1] / prob[:-1].sum()
+    return idx, prob
+
+
+def _tq_p_on_full_law(x, temperature, top_k, top_p):
+    x = np.asarray(x, np.float64)
+    idx, _ = _truncate_row(x, temperature, top_k, 1.0)
+    q = oracle.tempered_softmax(x, temperature)
+    run, keep = 0.0, idx.size
+    for i, v in enumerate(idx):
+        run += q[v]
+        if run >= top_p:
+            keep = i + 1
+            break
+    kept = idx[:keep]
+    return kept, q[kept] / q[kept].sum()
+
+
+@pytest.mark.parametrize("fn,pin", [
+    (_tq_ties_high, lambda: tq.test_kept_set_order_minimality_and_ratios(82)),
+    (_tq_p_exclusive, tq.test_worked_example_by_hand),
+    (_tq_p_on_full_law, lambda: tq.test_kept_set_order_minimality_and_ratios(83)),
+], ids=["ties-to-higher-id", "top-p-one-short", "top-p-on-full-law"])
+def test_truncate_pin_catches_planted_mistake(monkeypatch, fn, pin):
+    monkeypatch.setattr(oracle, "truncate_row", fn)
+    with pytest.raises(AssertionError):
+        pin()
