@@ -18,6 +18,8 @@ and the correction or bonus draw.  Workloads (sizes of the pages' setups):
   c4s joint-space chain, hybrid   B=16 K=8 V=151936 bf16, T=1, tau=0.6, Gumbel
                                   rows for every target row
   c3q stored sparse-Q verify      B=32 K=16 V=151936 bf16, top-k = 20 drafter Q
+  c3t top-k/top-p storage         B=32 K=16 V=151936 bf16 drafter rows -> top-k 20,
+                                  top-p 0.9 sparse Q (positions = rows stored)
 
 Inputs smaller than 1 GiB are replicated into several buffer sets and the
 steps rotate over them, so the 256 MiB last-level cache cannot serve them.
@@ -56,6 +58,7 @@ DESCR = {
     "c5ao": "any-order greedy verify B=64 U=32 V=131072 bf16",
     "c4s": "joint-space chain hybrid B=16 K=8 V=151936 bf16 T=1 tau=0.6",
     "c3q": "sparse stored-Q verify B=32 K=16 V=151936 bf16 top-k=20",
+    "c3t": "top-k/top-p truncation B=32 K=16 V=151936 bf16 top-k=20 top-p=0.9",
 }
 SPOT_TAU = 0.6
 CACTUS_DELTA = 1.0
@@ -190,6 +193,21 @@ class Case:
                     xd["tgt"], xd["q_idx"], xd["q_prob"], xd["q_nnz"], xd["draft_tokens"], xd["u_accept"],
                     xd["u_resample"], draft_len=xd["draft_len"], prepare=True))
             self.shape = dict(B=B, K=K, V=V)
+        elif name == "c3t":
+            x = workloads.config3_truncate()
+            B, K, V = x["drf"].shape
+            n = x["draft_len"].long()
+            self.positions = int(n.sum())
+            self.kernel_bytes = int((n * V * eb).sum())                 # drafter rows 0..n-1, read once
+            self.kernel = "k_truncate"
+            per_set = x["drf"].numel() * eb
+            self.cpu_inputs = x
+            self.calls = []
+            for _ in range(self._rotation(per_set)):
+                xd = {k: v.to(dev).clone() if torch.is_tensor(v) else v for k, v in x.items()}
+                self.calls.append(dbv.truncate_top_k_top_p(xd["drf"], x["top_k"], x["top_p"], kmax=x["top_k"],
+                                                           lengths=xd["draft_len"], prepare=True))
+            self.shape = dict(B=B, K=K, V=V)
         elif name == "c4s":
             x = workloads.config4_spot_chain()
             B, K1, V = x["tgt"].shape
@@ -301,6 +319,18 @@ class Case:
                 if time.perf_counter() - t0 >= seconds:
                     break
             sample = f"{nb} of 64 sequences, {calls} oracle calls"
+        elif self.name == "c3t":
+            nb = 1
+            rows = np64(x["drf"][:nb])
+            npos = int(x["draft_len"][:nb].sum())
+            t0 = time.perf_counter()
+            while True:
+                oracle.truncate_rows(rows, 1.0, x["top_k"], x["top_p"], x["top_k"], npi(x["draft_len"][:nb]))
+                done_pos += npos
+                calls += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            sample = f"{nb} of 32 sequences, {calls} oracle calls"
         elif self.name == "c3q":
             nb = 4
             xs = {k: v[:nb] if torch.is_tensor(v) else v for k, v in x.items()}
@@ -417,7 +447,7 @@ def main():
     achieved = case.kernel_bytes / (kms * 1e-3) / 1e9
 
     out = case.calls[0].outputs
-    st = out["status"].cpu()
+    st = out["status"].cpu() if "status" in out else (out["q_nnz"].cpu() < 0).to(torch.int32)
     if int((st & dbv.SEQ_ERROR_MASK).sum()) != 0:
         print(json.dumps({"error": "verification reported data errors", "status": st.tolist()}))
         sys.exit(1)

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_sparse", "verify_spot_chain",
+    "truncate_top_k_top_p",
     "verify_greedy_any_order", "verify_gumbel_tree", "workspace_size", "DBVError", "Prepared",
 ]
 
@@ -271,6 +272,29 @@ def verify_sparse(tgt, q_idx, q_prob, q_nnz, draft_tokens, u_accept, u_resample,
             _ptr(out.get("p_draft")), _ptr(out.get("q_draft")), _ptr(out.get("alpha")),
             _ptr(out.get("residual_mass")), out["status"].data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
     call = Prepared(lib.verify_sparse, "verify_sparse", args, out, (tgt, qi, qp, qn, d, n, bud, ua, ur, ws))
+    return call if prepare else call()
+
+
+def truncate_top_k_top_p(rows, top_k, top_p=1.0, kmax=None, lengths=None, temperature=1.0, prepare=False):
+    """Top-k / top-p truncation of drafter rows [B, K, V] into the stored
+    sparse form verify_sparse reads (Packed-SS Sec. 3.2).  Returns q_idx
+    [B, K, kmax] int32, q_prob [B, K, kmax] float32 and q_nnz [B, K] int32
+    (-1 for a row that is not a distribution; entries past q_nnz are 0)."""
+    lib = _lib.load()
+    dev = rows.device
+    B, K, V = rows.shape
+    ss, rs = _rows3(rows, "rows")
+    dt = _dtype_code(rows)
+    kmax = int(top_k) if kmax is None else int(kmax)
+    n = _i32(lengths, (B,), "lengths", dev)
+    out = {
+        "q_idx": torch.zeros(B, K, kmax, dtype=torch.int32, device=dev),
+        "q_prob": torch.zeros(B, K, kmax, dtype=torch.float32, device=dev),
+        "q_nnz": torch.empty(B, K, dtype=torch.int32, device=dev),
+    }
+    args = (B, K, V, dt, rows.data_ptr(), ss, rs, _ptr(n), float(temperature), int(top_k), float(top_p), kmax,
+            out["q_idx"].data_ptr(), out["q_prob"].data_ptr(), out["q_nnz"].data_ptr(), _stream(dev))
+    call = Prepared(lib.truncate_top_k_top_p, "truncate_top_k_top_p", args, out, (rows, n))
     return call if prepare else call()
 
 

@@ -32,7 +32,8 @@ SEQ_Z_ZERO = 16
 SEQ_ERROR_MASK = 7
 
 EXPORTS = (
-    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_sparse", "verify_spot_chain",
+    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_sparse", "truncate_top_k_top_p",
+    "verify_spot_chain",
     "verify_greedy_any_order", "verify_gumbel_tree", "verify_workspace_size", "verify_status_string", "verify_abi_version",
     "verify_set_timing_events",
 )
@@ -56,6 +57,8 @@ _SIGS = {
     # B K V dt tgt ts tr qidx qprob qnnz kmax d len tt ua ur eos bud acc out num pd qd al rm st ws wsb stream
     "verify_sparse": [_i, _i, _i, _i, _p, _i64, _i64, _p, _p, _p, _i, _p, _p, _f, _p, _p, _i32, _p, _p, _p, _p,
                       _p, _p, _p, _p, _p, _p, _sz, _p],
+    # B K V dt rows ss rs lengths T top_k top_p kmax q_idx q_prob q_nnz stream
+    "truncate_top_k_top_p": [_i, _i, _i, _i, _p, _i64, _i64, _p, _f, _i, _f, _i, _p, _p, _p, _p],
     # B K V dt tgt ts tr drf ds dr pos_star prop_pos prop_tok qpos len tt td gumbel gs gr tau ua ur eos
     # bud acc out num pd qd al rm st ws wsb stream
     "verify_spot_chain": [_i, _i, _i, _i, _p, _i64, _i64, _p, _i64, _i64, _p, _p, _p, _p, _p, _f, _f, _p,

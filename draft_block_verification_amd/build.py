@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdbv.so")
-SOURCES = ["api.hip", "kernels_chain.hip", "kernels_tree.hip", "kernels_anyorder.hip"]
+SOURCES = ["api.hip", "kernels_chain.hip", "kernels_tree.hip", "kernels_anyorder.hip", "kernels_truncate.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

@@ -326,6 +326,32 @@ dbv_status verify_sparse(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
                        out_tokens, num_out, p_draft, q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
 }
 
+dbv_status truncate_top_k_top_p(int B, int K, int V, dbv_dtype dtype, const void* rows, int64_t seq_stride,
+                                int64_t row_stride, const int32_t* lengths, float temperature, int top_k,
+                                float top_p, int kmax, int32_t* q_idx, float* q_prob, int32_t* q_nnz,
+                                void* stream) {
+  if (B < 0 || K < 0 || V < 1 || !dtype_ok(dtype) || seq_stride < 0 || row_stride < 0) return DBV_ERR_INVALID_ARG;
+  if (V > dbv::kMaxSampleV || kmax > dbv::kMaxNnz) return DBV_ERR_UNSUPPORTED;
+  if (!temp_ok(temperature) || kmax < 1 || top_k < 1 || top_k > kmax || !(top_p > 0.f && top_p <= 1.f))
+    return DBV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * K > 0 && (rows == nullptr || q_idx == nullptr || q_prob == nullptr ||
+                                           q_nnz == nullptr))
+    return DBV_ERR_INVALID_ARG;
+  if (rows && !aligned(rows, elem_bytes(dtype))) return DBV_ERR_INVALID_ARG;
+  dbv_status s = device_ready();
+  if (s != DBV_OK) return s;
+  if (static_cast<int64_t>(B) * K == 0) return DBV_OK;
+  dbv::TruncArgs a{};
+  a.B = B; a.K = K; a.V = V;
+  a.rows = rows; a.ss = seq_stride; a.rs = row_stride;
+  a.lengths = lengths;
+  a.kq = dbv::kLog2eHost / temperature;
+  a.top_k = top_k; a.top_p = top_p; a.kmax = kmax;
+  a.q_idx = q_idx; a.q_prob = q_prob; a.q_nnz = q_nnz;
+  return dbv::launch_truncate(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK
+                                                                                         : DBV_ERR_LAUNCH;
+}
+
 dbv_status verify_greedy_any_order(int B, int U, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
                                    int64_t tgt_row_stride, const int32_t* order, const int32_t* num_active,
                                    const int32_t* positions, const int32_t* draft_tokens, const void* draft_rows,

@@ -113,6 +113,19 @@ struct TreeArgs {
   int split2; int64_t chunk2;
 };
 
+// Top-k / top-p truncation of rows [B, K, V] (row i of sequence b read
+// only for i < lengths[b]) into stored sparse form [B, K, kmax].
+struct TruncArgs {
+  int B, K, V;
+  const void* rows; int64_t ss, rs;
+  const int32_t* lengths;              // [B] or NULL (= K)
+  float kq;                            // log2(e) / temperature
+  int top_k;
+  float top_p;
+  int kmax;
+  int32_t* q_idx; float* q_prob; int32_t* q_nnz;
+};
+
 // Optional events recorded around the row-streaming kernel of a call.
 struct TimingEvents {
   hipEvent_t begin = nullptr;
@@ -149,5 +162,6 @@ bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const Tim
 bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
 bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
 bool launch_any_order(const AnyOrderArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
+bool launch_truncate(const TruncArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
 
 }  // namespace dbv

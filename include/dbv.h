@@ -10,7 +10,8 @@
  * finds the longest accepted prefix (or tree path) and draws the correction
  * or bonus token from supplied uniforms.  verify_cactus adds the modified
  * Cactus acceptance rule, verify_sparse verification against stored sparse
- * drafter distributions, verify_spot_chain chain verification on the joint
+ * drafter distributions (truncate_top_k_top_p writes them from drafter
+ * rows), verify_spot_chain chain verification on the joint
  * (position, token) space and verify_greedy_any_order any-order greedy
  * verification.
  *
@@ -235,6 +236,28 @@ dbv_status verify_sparse(int B, int K, int V, dbv_dtype dtype,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
                          float* p_draft, float* q_draft, float* alpha, float* residual_mass,
                          int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * truncate_top_k_top_p -- stores drafter distributions in the sparse form
+ * verify_sparse reads ([PSS] Sec. 3.2: under top-k or top-p truncation only
+ * the nonzero entries of Q need storing).  For row i of sequence b (logits
+ * at element offset b*seq_stride + i*row_stride, read only for i <
+ * lengths[b]; lengths NULL = K): q = softmax(x / temperature); keep the
+ * top_k tokens of largest logit (equal logits: the lower token id first);
+ * within them, sorted by probability, keep the shortest prefix whose mass
+ * reaches top_p of theirs (all of them for top_p = 1); renormalise.  Writes
+ * q_idx[b, i, 0..nnz), q_prob[b, i, 0..nnz) in that order ([B, K, kmax]
+ * int32 / float32) and q_nnz[b, i] = nnz; rows not read get nnz = 0; a row
+ * holding NaN or +inf, or no finite logit, gets nnz = -1 (verify_sparse
+ * then reports DBV_SEQ_BAD_INPUT for a draft that uses it).  Entries past
+ * nnz are left as they were.  1 <= top_k <= kmax <= 256, 0 < top_p <= 1,
+ * temperature > 0 (DBV_ERR_INVALID_ARG; kmax > 256 or V > 2^21:
+ * DBV_ERR_UNSUPPORTED).  No workspace.
+ */
+dbv_status truncate_top_k_top_p(int B, int K, int V, dbv_dtype dtype,
+                                const void* rows, int64_t seq_stride, int64_t row_stride,
+                                const int32_t* lengths, float temperature, int top_k, float top_p,
+                                int kmax, int32_t* q_idx, float* q_prob, int32_t* q_nnz, void* stream);
 
 /*
  * verify_spot_chain -- chain verification on the joint (position, token)

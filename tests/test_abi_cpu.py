@@ -19,7 +19,7 @@ FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced here
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(verify_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"^(?:dbv_status|size_t|const char\s*\*|int|void)\s+(\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -117,6 +117,15 @@ def _sparse(lib, **kw):
                              None, None, None, None, o, a["ws"], a["wsb"], a["stream"])
 
 
+def _trunc(lib, **kw):
+    a = dict(B=2, K=3, V=100, dt=_lib.DBV_BF16, rows=FAKE, ss=300, rs=100, n=None, T=1.0, k=20, p=0.9, kmax=20,
+             o=FAKE, stream=None)
+    a.update(kw)
+    o = a["o"]
+    return lib.truncate_top_k_top_p(a["B"], a["K"], a["V"], a["dt"], a["rows"], a["ss"], a["rs"], a["n"], a["T"],
+                                    a["k"], a["p"], a["kmax"], o, o, o, a["stream"])
+
+
 def _spot(lib, **kw):
     a = dict(B=2, K=3, V=100, dt=_lib.DBV_BF16, tgt=FAKE, ts=400, tr=100, drf=FAKE, ds=300, dr=100, ps=FAKE,
              pp=FAKE, d=FAKE, c=FAKE, n=None, tt=1.0, td=1.0, g=FAKE, gs=400, gr=100, tau=0.6, ua=FAKE, ur=FAKE,
@@ -210,6 +219,20 @@ def test_sparse_limits(lib):
     assert _sparse(lib, kmax=257) == _lib.DBV_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("kw", [
+    dict(B=-1), dict(K=-1), dict(V=0), dict(dt=3), dict(rows=None), dict(ss=-1), dict(T=0.0), dict(T=float("nan")),
+    dict(k=0), dict(k=21), dict(p=0.0), dict(p=1.5), dict(p=float("nan")), dict(kmax=0), dict(o=None),
+    dict(rows=FAKE + 1),
+])
+def test_truncate_rejects_bad_args(lib, kw):
+    assert _trunc(lib, **kw) == INVALID
+
+
+def test_truncate_limits(lib):
+    assert _trunc(lib, kmax=300, k=20) == _lib.DBV_ERR_UNSUPPORTED
+    assert _trunc(lib, V=(1 << 21) + 1) == _lib.DBV_ERR_UNSUPPORTED
+
+
 def test_workspace_errors(lib):
     assert _greedy(lib, ws=None) == _lib.DBV_ERR_WORKSPACE
     assert _greedy(lib, wsb=8) == _lib.DBV_ERR_WORKSPACE
@@ -235,6 +258,8 @@ def test_optional_arguments_are_accepted(lib):
     assert _any_order(lib, U=0, order=None, d=None) == nodev
     assert _spot(lib, g=None, tau=float("inf")) == nodev
     assert _sparse(lib, kmax=0, qi=None, qp=None) == nodev
+    assert _trunc(lib, n=FAKE, p=1.0) == nodev
+    assert _trunc(lib, B=0, rows=None, o=None) == nodev
     assert _sparse(lib, K=0, qi=None, qp=None, qn=None, d=None, ua=None) == nodev
     assert _spot(lib, K=0, drf=None, pp=None, d=None, c=None, ua=None) == nodev
 

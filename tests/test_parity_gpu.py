@@ -267,6 +267,113 @@ def test_sparse_edge_cases(dev):
     check_sampling(g, xn, o, 0.0, 1.0, 1.0, "float32", eos_id=eos, len_budget=npi(bud), qfun=qfun)
 
 
+# ------------------------------------------------------ top-k / top-p store ---
+
+def _trunc_check(g, rows, T, k, p, kmax, lengths=None, dtype_name="float32"):
+    """GPU truncation against the oracle: the same entry count (a top-p cut
+    whose running mass lies within the tolerance of p may move by one), the
+    same tokens in the same order, probabilities within the tolerance."""
+    rtol = PROB_RTOL_T[dtype_name]
+    qi, qp, qn = oracle.truncate_rows(rows, T, k, p, kmax, lengths)
+    gi, gp, gn = npi(g["q_idx"]), np64(g["q_prob"]), npi(g["q_nnz"])
+    B, K, V = rows.shape
+    near = 0
+    for b in range(B):
+        for i in range(K):
+            no, ng = int(qn[b, i]), int(gn[b, i])
+            if no <= 0:
+                assert ng == no, (b, i, ng, no)
+                continue
+            if ng != no:
+                # the top-p cut: the running mass at the shorter count is within tolerance of p
+                idx, _ = oracle.truncate_row(rows[b, i], T, k, 1.0)
+                a = rows[b, i][idx] / T
+                w = np.exp(a - a.max())
+                w /= w.sum()
+                c = np.cumsum(w)
+                assert abs(ng - no) == 1 and abs(c[min(ng, no) - 1] - p) < 10 * rtol, (b, i, ng, no)
+                near += 1
+            m = min(ng, no)
+            np.testing.assert_array_equal(gi[b, i, :m], qi[b, i, :m], err_msg=f"row {b},{i}")
+            if ng == no:
+                np.testing.assert_allclose(gp[b, i, :m], qp[b, i, :m], rtol=rtol, atol=1e-30)
+    return near
+
+
+PROB_RTOL_T = {"float32": 1e-5, "bfloat16": 1e-5}   # inputs exact in float32 either way
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("V,k,p", [(1000, 20, 1.0), (1000, 20, 0.9), (151936, 20, 0.9), (151936, 256, 0.95),
+                                   (50257, 1, 1.0), (37, 64, 0.5)])
+def test_truncate_parity(dev, dtype, V, k, p):
+    say("truncate", dtype, V, k, p)
+    g0 = torch.Generator().manual_seed(91)
+    rows = (torch.randn(6, 4, V, generator=g0) * 3.0).to(dtype)
+    lengths = torch.tensor([4, 0, 2, 4, 1, 3], dtype=torch.int32)
+    kmax = max(k, 1) if k <= 256 else 256
+    kk = min(k, kmax)
+    g = dbv.truncate_top_k_top_p(rows.to(dev), kk, p, kmax=kmax, lengths=lengths.to(dev), temperature=0.8)
+    near = _trunc_check(g, np64(rows), 0.8, kk, p, kmax, npi(lengths), str(dtype).split(".")[-1])
+    say("near top-p cuts", near)
+
+
+def test_truncate_ties_and_bad_rows(dev):
+    say("truncate ties / bad rows")
+    g0 = torch.Generator().manual_seed(92)
+    rows = torch.randint(-4, 5, (5, 3, 3001), generator=g0).float()   # many equal logits: id cut-offs
+    rows[0, 1, 7] = float("nan")
+    rows[1, 0] = float("-inf")                                        # no finite logit
+    rows[1, 1, :] = float("-inf")
+    rows[1, 1, :5] = 1.0                                               # fewer finite entries than k
+    rows[2, 2, 100] = float("inf")
+    rows[3, 0, :] = -0.0
+    rows[3, 0, 50:60] = 0.0                                            # -0 and +0 tie
+    for dtype in (torch.float32, torch.bfloat16):
+        for k, p in ((12, 1.0), (12, 0.3), (200, 0.97)):
+            x = rows.to(dtype)
+            g = dbv.truncate_top_k_top_p(x.to(dev), k, p, kmax=200, temperature=1.3)
+            _trunc_check(g, np64(x), 1.3, k, p, 200, None, str(dtype).split(".")[-1])
+            assert npi(g["q_nnz"])[0, 1] == -1 and npi(g["q_nnz"])[1, 0] == -1 and npi(g["q_nnz"])[2, 2] == -1
+
+
+def test_truncate_flat_rows(dev):
+    # More logits at or above the threshold than the LDS candidates hold:
+    # a flat row, a row with a few distinct values, and a row with fewer
+    # finite logits than k over a large vocabulary.
+    say("truncate flat rows")
+    g0 = torch.Generator().manual_seed(94)
+    V = 20000
+    rows = torch.zeros(3, 2, V)
+    rows[0, 1] = torch.randint(0, 3, (V,), generator=g0).float()
+    rows[1, 0, :] = float("-inf")
+    rows[1, 0, torch.randperm(V, generator=g0)[:7]] = torch.randn(7, generator=g0)
+    rows[1, 1] = torch.randn(V, generator=g0) * 1e-3
+    rows[2, 0] = torch.round(torch.randn(V, generator=g0) * 2) / 2
+    for dtype in (torch.float32, torch.bfloat16):
+        for k, p in ((16, 1.0), (100, 0.5), (256, 0.99)):
+            x = rows.to(dtype)
+            g = dbv.truncate_top_k_top_p(x.to(dev), k, p, kmax=256, temperature=0.9)
+            _trunc_check(g, np64(x), 0.9, k, p, 256, None, str(dtype).split(".")[-1])
+
+
+def test_truncate_then_verify_sparse(dev):
+    # drafter rows -> stored top-k Q -> verification, against the oracle end to end
+    say("truncate -> verify_sparse")
+    x = workloads.chain_inputs(93, 8, 6, 5003, torch.bfloat16, sigma=1.0, random_lengths=True)
+    st = dbv.truncate_top_k_top_p(x["drf"].to(dev), 20, 0.9, kmax=24, lengths=x["draft_len"].to(dev))
+    qi, qp, qn = (npi(st["q_idx"]), np64(st["q_prob"]), npi(st["q_nnz"]))
+    # draft tokens: the first stored token of each row (a valid draw from Q)
+    d = torch.tensor(qi[:, :, 0], dtype=torch.int32)
+    g = dbv.verify_sparse(x["tgt"].to(dev), st["q_idx"], st["q_prob"], st["q_nnz"], d.to(dev),
+                          x["u_accept"].to(dev), x["u_resample"].to(dev), draft_len=x["draft_len"].to(dev))
+    xn = dict(tgt=np64(x["tgt"]), draft_tokens=npi(d), draft_len=npi(x["draft_len"]),
+              u_accept=np64(x["u_accept"]), u_resample=np64(x["u_resample"]))
+    o = oracle.verify_sparse(xn["tgt"], qi, qp, qn, xn["draft_tokens"], xn["draft_len"], 1.0, xn["u_accept"],
+                             xn["u_resample"])
+    check_sampling(g, xn, o, 0.0, 1.0, 1.0, "bfloat16", qfun=lambda b, i: oracle.dense_q(qi[b, i], qp[b, i], qn[b, i], 5003))
+
+
 # ------------------------------------------------------- joint-space chain ---
 
 def _spot_np(x):

@@ -374,3 +374,14 @@ def config3_sparse(device="cpu"):
     storage (the truncation Qwen3 recommends for this vocabulary), T=1, a
     +20 target peak (the target's argmax carries most of the mass)."""
     return sparse_inputs(31, 32, 16, 151936, torch.bfloat16, topk=20, peak=20.0, device=device)
+
+
+def config3_truncate(device="cpu"):
+    """Drafter-side storage of the sparse-Q workload: drafter rows
+    [32, 16, 151936] bf16 = z + N(0, 1) (z the planted target logits),
+    truncated to top-k 20, top-p 0.9."""
+    c = 32
+    z = _planted_logits(c, (32, 16, 151936), 20.0, torch.float32, device)
+    drf = (z + torch.randn(32, 16, 151936, generator=_gen(c, 2, device), device=device)).to(torch.bfloat16)
+    n = torch.full((32,), 16, dtype=torch.int32)
+    return dict(drf=drf, draft_len=n, top_k=20, top_p=0.9)
