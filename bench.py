@@ -85,7 +85,8 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 # The source file that defines each measured kernel; its counter readings
 # hold only for that file and the headers every kernel file includes.
 KERNEL_FILES = {"k_sample_rows": "kernels_chain.hip", "k_greedy_rows": "kernels_chain.hip",
-                "k_tree_conf": "kernels_tree.hip", "k_ao_rows": "kernels_anyorder.hip"}
+                "k_tree_conf": "kernels_tree.hip", "k_ao_rows": "kernels_anyorder.hip",
+                "k_truncate": "kernels_truncate.hip"}
 SHARED_HEADERS = ("dbv_device.h", "dbv_launch.h", "dbv_plan.h")
 
 

@@ -28,6 +28,9 @@ following the pages' definitions in their own order:
 * ``spot``   -- chain verification on the joint (position, token) space:
   rejection sampling per link (SPOT App. B) and the confidence-gated hybrid
   of coupled-noise match and rejection sampling.
+* ``ddtree`` -- prefix-conditional draft-tree construction: token hypotheses
+  from the stale conditionals, prefix masses and the top-D tree (SPOT
+  Sec. 4.2 Eq. 3, App. C.2 Algorithm 2).
 
 Sources (pages by title):
 * "One Call Ahead: Packed Self-Speculative Decoding with Diffusion Drafting"
@@ -36,8 +39,8 @@ Sources (pages by title):
   Algorithm 3 and Prop. C.1,
   App. D.1.
 * "On the SPOT: Enhancing Speculative Decoding for Diffusion Language Models
-  via Commit-Order Prediction" (SPOT): Sec. 4.1, Sec. 4.3, App. A.1, A.3
-  Eq. 5-7, App. B Eq. 10-14.
+  via Commit-Order Prediction" (SPOT): Sec. 4.1, Sec. 4.2 Eq. 3, Sec. 4.3
+  Eq. 4, App. A.1, A.3 Eq. 5-7, App. B Eq. 10-14, App. C.2 Algorithm 2.
 * "Speculative Diffusion is a Tale of Two Tradeoffs" (Two Tradeoffs): Sec. 2
   Eq. 1-5 and Theorem 1, Sec. 3.2 Algorithm 1, App. C Proposition 1,
   App. E (modified Cactus, Eq. 17-18).
@@ -60,4 +63,8 @@ from .spot import MODE_RS, MODE_MATCH, rs_link, rs_residual, verify_spot_chain  
 from .tree import (  # noqa: F401
     TREE_STATE_EQUALITY, TREE_FIXED_POSITION, state_transition, walk,
     verify_gumbel_tree,
+)
+from .ddtree import (  # noqa: F401
+    RUNNER_UP_BELOW, hypotheses, order_distribution, table_order, best_first,
+    level_batched, tree_arrays, build_ddtree,
 )

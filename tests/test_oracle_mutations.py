@@ -324,3 +324,74 @@ def test_truncate_pin_catches_planted_mistake(monkeypatch, fn, pin):
     monkeypatch.setattr(oracle, "truncate_row", fn)
     with pytest.raises(AssertionError):
         pin()
+
+
+# ------------------------------------------------------------------ DDTree
+
+import oracle.ddtree as ddtree  # noqa: E402
+import tests.test_oracle_ddtree_pins as dp  # noqa: E402
+
+_DD_HYPOTHESES = ddtree.hypotheses
+
+
+def _dd_fill_by_level(masked, hyps, order_fn, D, tau=1.0, gamma=0.0, b=0):
+    """Fills the remaining budget from each new level, never displacing."""
+    srch = ddtree._Search(masked, hyps, order_fn, b, tau, gamma)
+    tree, frontier, levels = [], [((), 1.0)], 0
+    while frontier and len(tree) < D:
+        cand = []
+        for p, m in frontier:
+            cand.extend(srch.children(p, m))
+        levels += 1
+        cand.sort(key=lambda e: ddtree.rank_key(e[1], e[0]))
+        frontier = cand[:D - len(tree)]
+        tree = sorted(tree + frontier, key=lambda e: ddtree.rank_key(e[1], e[0]))
+    return tree, srch.status, levels
+
+
+def _dd_order_unrestricted(logits, masked_positions, tau):
+    z = np.asarray(logits, np.float64) / tau
+    w = np.exp(z - z.max())
+    q = w / w.sum()
+    out = np.zeros(z.size)
+    ms = list(masked_positions)
+    out[ms] = q[ms]
+    return out
+
+
+def _dd_runner_up_inverted(row, temperature, gumbel_row=None, runner_up_below=0.6):
+    x = np.asarray(row, np.float64)
+    p = ddtree.stale_softmax(x)
+    if temperature == 0.0:
+        v0 = rows.argmax_lowest(x)
+        hyp = [(v0, float(p[v0]))]
+        if p[v0] > runner_up_below and x.size > 1:
+            rest = x.copy()
+            rest[v0] = -np.inf
+            v1 = rows.argmax_lowest(rest)
+            hyp.append((v1, float(p[v1])))
+        return dict(hyp=hyp, top1_margin=0.0, pick_margin=np.inf)
+    return _DD_HYPOTHESES(row, temperature, gumbel_row, runner_up_below)
+
+
+def _dd_gumbel_tempered_mass(row, temperature, gumbel_row=None, runner_up_below=0.6):
+    x = np.asarray(row, np.float64)
+    if temperature == 0.0:
+        return _DD_HYPOTHESES(row, temperature, gumbel_row, runner_up_below)
+    a = x / temperature
+    p = np.exp(a - a.max())
+    p /= p.sum()
+    v = rows.argmax_lowest(np.log(p) + np.asarray(gumbel_row, np.float64))
+    return dict(hyp=[(v, float(p[v]))], top1_margin=np.inf, pick_margin=np.inf)
+
+
+@pytest.mark.parametrize("name,fn,pin", [
+    ("level_batched", _dd_fill_by_level, dp.test_hand_worked_tree),
+    ("order_distribution", _dd_order_unrestricted, lambda: dp.test_best_first_is_the_top_d_of_all_states(0)),
+    ("hypotheses", _dd_runner_up_inverted, dp.test_greedy_hypotheses_runner_up_below_threshold),
+    ("hypotheses", _dd_gumbel_tempered_mass, dp.test_gumbel_hypothesis),
+])
+def test_ddtree_pin_catches_planted_mistake(monkeypatch, name, fn, pin):
+    monkeypatch.setattr(ddtree, name, fn)
+    with pytest.raises(AssertionError):
+        pin()
