@@ -20,6 +20,9 @@ and the correction or bonus draw.  Workloads (sizes of the pages' setups):
   c3q stored sparse-Q verify      B=32 K=16 V=151936 bf16, top-k = 20 drafter Q
   c3t top-k/top-p storage         B=32 K=16 V=151936 bf16 drafter rows -> top-k 20,
                                   top-p 0.9 sparse Q (positions = rows stored)
+  c4d DDTree construction         B=16 L=32 V=151936 bf16 stale rows, T=1 (Gumbel
+                                  rows), budget D=20: hypotheses + top-D search
+                                  (positions = tree states drafted)
 
 Inputs smaller than 1 GiB are replicated into several buffer sets and the
 steps rotate over them, so the 256 MiB last-level cache cannot serve them.
@@ -59,7 +62,9 @@ DESCR = {
     "c4s": "joint-space chain hybrid B=16 K=8 V=151936 bf16 T=1 tau=0.6",
     "c3q": "sparse stored-Q verify B=32 K=16 V=151936 bf16 top-k=20",
     "c3t": "top-k/top-p truncation B=32 K=16 V=151936 bf16 top-k=20 top-p=0.9",
+    "c4d": "DDTree construction B=16 L=32 V=151936 bf16 T=1 D=20",
 }
+DD_BUDGET = 20
 SPOT_TAU = 0.6
 CACTUS_DELTA = 1.0
 
@@ -86,7 +91,7 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 # hold only for that file and the headers every kernel file includes.
 KERNEL_FILES = {"k_sample_rows": "kernels_chain.hip", "k_greedy_rows": "kernels_chain.hip",
                 "k_tree_conf": "kernels_tree.hip", "k_ao_rows": "kernels_anyorder.hip",
-                "k_truncate": "kernels_truncate.hip"}
+                "k_truncate": "kernels_truncate.hip", "k_dd_rows": "kernels_ddtree.hip"}
 SHARED_HEADERS = ("dbv_device.h", "dbv_launch.h", "dbv_plan.h")
 
 
@@ -118,6 +123,19 @@ def measured_traffic(workload, kernel):
 
 
 # --------------------------------------------------------------- workloads ---
+
+class _Steps:
+    """Prepared calls enqueued one after the other as one step."""
+
+    def __init__(self, calls):
+        self.calls = calls
+        self.outputs = calls[-1].outputs
+
+    def __call__(self):
+        for c in self.calls:
+            c()
+        return self.outputs
+
 
 class Case:
     """One workload: prepared calls over R rotated input sets, plus what the
@@ -209,6 +227,24 @@ class Case:
                 self.calls.append(dbv.truncate_top_k_top_p(xd["drf"], x["top_k"], x["top_p"], kmax=x["top_k"],
                                                            lengths=xd["draft_len"], prepare=True))
             self.shape = dict(B=B, K=K, V=V)
+        elif name == "c4d":
+            x = workloads.config4_ddtree()
+            B, L, V = x["stale"].shape
+            nm = int(x["masked"].sum())
+            self.positions = B * DD_BUDGET
+            self.kernel_bytes = nm * V * (eb + 4)                      # masked stale rows + Gumbel rows
+            self.kernel = "k_dd_rows"
+            per_set = x["stale"].numel() * eb + x["gumbel"].numel() * 4
+            self.cpu_inputs = x
+            self.calls = []
+            for _ in range(self._rotation(per_set)):
+                xd = {k: v.to(dev).clone() if torch.is_tensor(v) else v for k, v in x.items()}
+                h = dbv.ddtree_hypotheses(xd["stale"], xd["masked"], temperature=1.0, gumbel=xd["gumbel"],
+                                          prepare=True)
+                t = dbv.ddtree_build(xd["masked"], h.outputs["hyp_tok"], h.outputs["hyp_prob"],
+                                     xd["order_table"], DD_BUDGET, status=h.outputs["status"], prepare=True)
+                self.calls.append(_Steps([h, t]))
+            self.shape = dict(B=B, L=L, V=V, D=DD_BUDGET, masked_rows=nm)
         elif name == "c4s":
             x = workloads.config4_spot_chain()
             B, K1, V = x["tgt"].shape
@@ -332,6 +368,19 @@ class Case:
                 if time.perf_counter() - t0 >= seconds:
                     break
             sample = f"{nb} of 32 sequences, {calls} oracle calls"
+        elif self.name == "c4d":
+            nb = 1
+            st, m = np64(x["stale"][:nb]), npi(x["masked"][:nb])
+            G = np64(x["gumbel"][:nb])
+            fn = oracle.table_order(np64(x["order_table"][:nb]))
+            t0 = time.perf_counter()
+            while True:
+                oracle.build_ddtree(st, m, fn, DD_BUDGET, 1.0, gumbel=G)
+                done_pos += nb * DD_BUDGET
+                calls += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            sample = f"{nb} of 16 blocks, {calls} oracle calls"
         elif self.name == "c3q":
             nb = 4
             xs = {k: v[:nb] if torch.is_tensor(v) else v for k, v in x.items()}

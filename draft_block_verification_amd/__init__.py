@@ -7,7 +7,9 @@ the verification runs in the library's HIP kernels; there is no fallback.
 
 Entry points (same names as the C ABI):
   verify_greedy, verify_rejection, verify_lenient, verify_cactus,
-  verify_greedy_any_order, verify_gumbel_tree
+  verify_sparse, truncate_top_k_top_p, verify_spot_chain,
+  verify_greedy_any_order, verify_gumbel_tree,
+  ddtree_hypotheses, ddtree_level, ddtree_build
 """
 
 import torch
@@ -22,7 +24,8 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_sparse", "verify_spot_chain",
     "truncate_top_k_top_p",
-    "verify_greedy_any_order", "verify_gumbel_tree", "workspace_size", "DBVError", "Prepared",
+    "verify_greedy_any_order", "verify_gumbel_tree", "ddtree_hypotheses", "ddtree_level", "ddtree_build",
+    "workspace_size", "DBVError", "Prepared",
 ]
 
 
@@ -459,4 +462,117 @@ def verify_gumbel_tree(logits, parent, edge_pos, edge_tok, masked=None, gumbel=N
             ws.data_ptr(), ws.numel(), _stream(dev))
     call = Prepared(lib.verify_gumbel_tree, "verify_gumbel_tree", args, out,
                     (logits, m, par, ep, et, ns, npos, gumbel, ws))
+    return call if prepare else call()
+
+
+def ddtree_hypotheses(stale, masked, temperature=0.0, gumbel=None, runner_up_below=0.6, workspace=None,
+                      prepare=False):
+    """Token hypotheses of the masked positions (SPOT Sec. 4.2, Eq. 4).
+
+    stale [B, L, V] stale target logits (bf16 or fp32), masked [B, L];
+    gumbel [B, L, V] float32 when temperature > 0.  Returns hyp_tok [B, L, 2]
+    int32, hyp_prob [B, L, 2] float32 and status [B] int32."""
+    lib = _lib.load()
+    dev = stale.device
+    B, L, V = stale.shape
+    ss, sp = _rows3(stale, "stale")
+    dt = _dtype_code(stale)
+    m = torch.as_tensor(masked, device=dev).to(torch.uint8).contiguous()
+    if tuple(m.shape) != (B, L):
+        raise ValueError("masked must be [B, L]")
+    gs = gp = 0
+    if temperature > 0:
+        if gumbel is None or gumbel.dtype != torch.float32 or tuple(gumbel.shape) != (B, L, V):
+            raise ValueError("gumbel must be float32 [B, L, V] when temperature > 0")
+        gs, gp = _rows3(gumbel, "gumbel")
+    else:
+        gumbel = None
+    out = {
+        "hyp_tok": torch.empty(B, L, 2, dtype=torch.int32, device=dev),
+        "hyp_prob": torch.empty(B, L, 2, dtype=torch.float32, device=dev),
+        "status": torch.empty(B, dtype=torch.int32, device=dev),
+    }
+    need = workspace_size(_lib.DBV_KIND_DDTREE_HYPOTHESES, B, L, 0, V, dt)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    args = (B, L, V, dt, stale.data_ptr(), ss, sp, m.data_ptr(), _ptr(gumbel), gs, gp, float(temperature),
+            float(runner_up_below), out["hyp_tok"].data_ptr(), out["hyp_prob"].data_ptr(),
+            out["status"].data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+    call = Prepared(lib.ddtree_hypotheses, "ddtree_hypotheses", args, out, (stale, m, gumbel, ws))
+    return call if prepare else call()
+
+
+def _dd_state(B, L, D, dev, status):
+    st = {
+        "parent": torch.empty(B, D + 1, dtype=torch.int32, device=dev),
+        "edge_pos": torch.empty(B, D + 1, dtype=torch.int32, device=dev),
+        "edge_tok": torch.empty(B, D + 1, dtype=torch.int32, device=dev),
+        "mass": torch.empty(B, D + 1, dtype=torch.float32, device=dev),
+        "node_masked": torch.empty(B, D + 1, L, dtype=torch.uint8, device=dev),
+        "num_nodes": torch.empty(B, dtype=torch.int32, device=dev),
+        "frontier": torch.empty(B, max(D, 1), dtype=torch.int32, device=dev),
+        "num_frontier": torch.empty(B, dtype=torch.int32, device=dev),
+        "status": (torch.zeros(B, dtype=torch.int32, device=dev) if status is None
+                   else _i32(status, (B,), "status", dev)),
+    }
+    st["_ws"] = _workspace(workspace_size(_lib.DBV_KIND_DDTREE, B, D, L, 0, 0), dev)
+    return st
+
+
+def _dd_inputs(masked, hyp_tok, hyp_prob, dev):
+    m = torch.as_tensor(masked, device=dev).to(torch.uint8).contiguous()
+    B, L = m.shape
+    ht = _i32(hyp_tok, (B, L, 2), "hyp_tok", dev)
+    hp = _f32(hyp_prob, (B, L, 2), "hyp_prob", dev)
+    return m, ht, hp, B, L
+
+
+def _dd_out_ptrs(st):
+    return (st["parent"].data_ptr(), st["edge_pos"].data_ptr(), st["edge_tok"].data_ptr(), st["mass"].data_ptr(),
+            st["node_masked"].data_ptr(), st["num_nodes"].data_ptr(), st["frontier"].data_ptr(),
+            st["num_frontier"].data_ptr(), st["status"].data_ptr(), st["_ws"].data_ptr(), st["_ws"].numel())
+
+
+def ddtree_level(masked, hyp_tok, hyp_prob, order_logits, D, tau=1.0, gamma=0.0, state=None, status=None):
+    """One level of the DDTree search (SPOT App. C.2, Algorithm 2).
+
+    masked [B, L] the current state's masked positions; hyp_tok / hyp_prob
+    from ddtree_hypotheses; order_logits [B, F, L] float32, row j = the
+    order model's logits for frontier slot j (the root on the first level).
+    state=None starts a new search (status [B], e.g. the hypotheses' own,
+    is read and updated in place: a sequence in error is skipped); pass the
+    returned state back for the next level.  The
+    state dict holds parent, edge_pos, edge_tok, mass, node_masked,
+    num_nodes, frontier, num_frontier and status."""
+    lib = _lib.load()
+    dev = order_logits.device
+    m, ht, hp, B, L = _dd_inputs(masked, hyp_tok, hyp_prob, dev)
+    o = order_logits
+    if o.dtype != torch.float32 or o.dim() != 3 or o.shape[0] != B or o.shape[2] != L or o.stride(2) != 1:
+        raise ValueError("order_logits must be float32 [B, F, L] with a contiguous last axis")
+    first = state is None
+    if o.shape[1] < (1 if first else D):
+        raise ValueError("order_logits needs a row per frontier slot: 1 on the first level, D after")
+    st = _dd_state(B, L, D, dev, status) if first else state
+    args = (B, L, D, m.data_ptr(), ht.data_ptr(), hp.data_ptr(), o.data_ptr(), o.stride(0), o.stride(1),
+            float(tau), float(gamma), int(first)) + _dd_out_ptrs(st) + (_stream(dev),)
+    _check(lib.ddtree_level(*args), "ddtree_level")
+    st["_keep"] = (m, ht, hp, o)
+    return st
+
+
+def ddtree_build(masked, hyp_tok, hyp_prob, order_table, D, tau=1.0, gamma=0.0, status=None, prepare=False):
+    """The whole DDTree search in one launch with a first-order order
+    model: order_table [B, L+1, L] float32, row c = the order logits of a
+    state whose last committed position is c (row L: the root).  Returns the
+    state dict of ddtree_level after its last level."""
+    lib = _lib.load()
+    dev = order_table.device
+    m, ht, hp, B, L = _dd_inputs(masked, hyp_tok, hyp_prob, dev)
+    o = order_table
+    if o.dtype != torch.float32 or tuple(o.shape) != (B, L + 1, L) or o.stride(2) != 1:
+        raise ValueError("order_table must be float32 [B, L+1, L] with a contiguous last axis")
+    st = _dd_state(B, L, D, dev, status)
+    args = (B, L, D, m.data_ptr(), ht.data_ptr(), hp.data_ptr(), o.data_ptr(), o.stride(0), o.stride(1),
+            float(tau), float(gamma)) + _dd_out_ptrs(st) + (_stream(dev),)
+    call = Prepared(lib.ddtree_build, "ddtree_build", args, st, (m, ht, hp, o))
     return call if prepare else call()

@@ -23,6 +23,8 @@ DBV_KIND_GREEDY = 0
 DBV_KIND_REJECTION = 1
 DBV_KIND_TREE = 2
 DBV_KIND_ANY_ORDER = 3
+DBV_KIND_DDTREE_HYPOTHESES = 4
+DBV_KIND_DDTREE = 5
 
 SEQ_BAD_INPUT = 1
 SEQ_NONFINITE = 2
@@ -35,7 +37,7 @@ EXPORTS = (
     "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_sparse", "truncate_top_k_top_p",
     "verify_spot_chain",
     "verify_greedy_any_order", "verify_gumbel_tree", "verify_workspace_size", "verify_status_string", "verify_abi_version",
-    "verify_set_timing_events",
+    "verify_set_timing_events", "ddtree_hypotheses", "ddtree_level", "ddtree_build",
 )
 
 _i = ctypes.c_int
@@ -67,6 +69,14 @@ _SIGS = {
                                 _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "verify_gumbel_tree": [_i, _i, _i, _i, _i, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p,
                            _i64, _i64, _f, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
+    # B L V dt stale ss sp masked gumbel gs gp T below hyp_tok hyp_prob status ws wsb stream
+    "ddtree_hypotheses": [_i, _i, _i, _i, _p, _i64, _i64, _p, _p, _i64, _i64, _f, _f, _p, _p, _p, _p, _sz, _p],
+    # B L D masked hyp_tok hyp_prob order os orow tau gamma first parent pos tok mass node_masked
+    # num_nodes frontier num_frontier status ws wsb stream
+    "ddtree_level": [_i, _i, _i, _p, _p, _p, _p, _i64, _i64, _f, _f, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                     _p, _sz, _p],
+    "ddtree_build": [_i, _i, _i, _p, _p, _p, _p, _i64, _i64, _f, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                     _p, _sz, _p],
     "verify_workspace_size": [_i, _i, _i, _i, _i, _i],
     "verify_status_string": [_i],
     "verify_abi_version": [],

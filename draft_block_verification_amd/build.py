@@ -13,7 +13,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdbv.so")
-SOURCES = ["api.hip", "kernels_chain.hip", "kernels_tree.hip", "kernels_anyorder.hip", "kernels_truncate.hip"]
+SOURCES = ["api.hip", "kernels_chain.hip", "kernels_tree.hip", "kernels_anyorder.hip", "kernels_truncate.hip",
+           "kernels_ddtree.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

@@ -186,6 +186,39 @@ Rule cactus_rule(float delta) {
   return r;
 }
 
+dbv_status dd_tree_common(int B, int L, int D, const uint8_t* masked, const int32_t* hyp_tok,
+                          const float* hyp_prob, const float* order, int64_t os, int64_t orow, int table,
+                          float tau, float gamma, int first, int32_t* parent, int32_t* edge_pos,
+                          int32_t* edge_tok, float* mass, uint8_t* node_masked, int32_t* num_nodes,
+                          int32_t* frontier, int32_t* num_frontier, int32_t* status, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (B < 0 || L < 1 || L > dbv::kDDMaxBlock || D < 0 || D > dbv::kDDMaxBudget) return DBV_ERR_INVALID_ARG;
+  if (os < 0 || orow < 0 || !(std::isfinite(tau) && tau > 0.f) || !(std::isfinite(gamma) && gamma >= 0.f))
+    return DBV_ERR_INVALID_ARG;
+  if (B > 0 && (masked == nullptr || hyp_tok == nullptr || hyp_prob == nullptr || order == nullptr ||
+                parent == nullptr || edge_pos == nullptr || edge_tok == nullptr || mass == nullptr ||
+                num_nodes == nullptr || num_frontier == nullptr || (D > 0 && frontier == nullptr)))
+    return DBV_ERR_INVALID_ARG;
+  if (order && !aligned(order, 4)) return DBV_ERR_INVALID_ARG;
+  dbv_status s = check_ws(ws, ws_bytes, dbv::dd_tree_bytes(B, D));
+  if (s != DBV_OK) return s;
+  if ((s = device_ready()) != DBV_OK) return s;
+  if (B == 0) return DBV_OK;
+  dbv::DDTreeArgs a{};
+  a.B = B; a.L = L; a.D = D;
+  a.masked = masked; a.hyp_tok = hyp_tok; a.hyp_prob = hyp_prob;
+  a.order = order; a.os = os; a.orow = orow;
+  a.table = table; a.first = first ? 1 : 0;
+  a.inv_tau = 1.f / tau; a.gamma = gamma;
+  a.parent = parent; a.edge_pos = edge_pos; a.edge_tok = edge_tok; a.mass = mass;
+  a.node_masked = node_masked;
+  a.num_nodes = num_nodes; a.frontier = frontier; a.num_frontier = num_frontier;
+  a.status = status;
+  a.keys = static_cast<uint64_t*>(ws);
+  a.masks = a.keys + static_cast<size_t>(B) * (D + 1);
+  return dbv::launch_dd_tree(a, static_cast<hipStream_t>(stream)) ? DBV_OK : DBV_ERR_LAUNCH;
+}
+
 }  // namespace
 
 namespace dbv {
@@ -450,7 +483,69 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const
   return dbv::launch_tree(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
 }
 
+dbv_status ddtree_hypotheses(int B, int L, int V, dbv_dtype dtype, const void* stale, int64_t seq_stride,
+                             int64_t pos_stride, const uint8_t* masked, const float* gumbel, int64_t g_seq_stride,
+                             int64_t g_pos_stride, float temperature, float runner_up_below, int32_t* hyp_tok,
+                             float* hyp_prob, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || L < 1 || L > dbv::kDDMaxBlock || V < 1 || !dtype_ok(dtype)) return DBV_ERR_INVALID_ARG;
+  if (seq_stride < 0 || pos_stride < 0 || g_seq_stride < 0 || g_pos_stride < 0) return DBV_ERR_INVALID_ARG;
+  if (!(std::isfinite(temperature) && temperature >= 0.f) || std::isnan(runner_up_below))
+    return DBV_ERR_INVALID_ARG;
+  if (B > 0 && (stale == nullptr || masked == nullptr || hyp_tok == nullptr || hyp_prob == nullptr))
+    return DBV_ERR_INVALID_ARG;
+  if (temperature > 0.f && B > 0 && gumbel == nullptr) return DBV_ERR_INVALID_ARG;
+  if ((stale && !aligned(stale, elem_bytes(dtype))) || (gumbel && !aligned(gumbel, 4))) return DBV_ERR_INVALID_ARG;
+  const dbv::DDHypPlan plan = dbv::plan_dd_hypotheses(B, L);
+  if (!stream_fits(plan.max_rows, V)) return DBV_ERR_UNSUPPORTED;
+  dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
+  if (s != DBV_OK) return s;
+  if ((s = device_ready()) != DBV_OK) return s;
+  if (B == 0) return DBV_OK;
+  dbv::DDHypArgs a{};
+  a.B = B; a.L = L; a.V = V;
+  a.stale = stale; a.ss = seq_stride; a.sp = pos_stride;
+  a.masked = masked;
+  a.gumbel = temperature > 0.f ? gumbel : nullptr; a.gs = g_seq_stride; a.gp = g_pos_stride;
+  a.inv_t = temperature > 0.f ? 1.f / temperature : 0.f;
+  a.below = runner_up_below;
+  a.hyp_tok = hyp_tok; a.hyp_prob = hyp_prob; a.status = status;
+  char* w = static_cast<char*>(ws);
+  a.count = reinterpret_cast<int32_t*>(w + plan.off_count);
+  a.list = reinterpret_cast<int32_t*>(w + plan.off_list);
+  a.map = reinterpret_cast<int32_t*>(w + plan.off_map);
+  a.part = reinterpret_cast<dbv::DDPart*>(w + plan.off_part);
+  // Gumbel rows double the bytes per element; units of 512 elements then.
+  a.split_bytes = temperature > 0.f ? 8 : static_cast<int>(elem_bytes(dtype));
+  a.grid = dbv::stream_grid(plan.max_rows, V, a.split_bytes, dbv::resident_groups());
+  return dbv::launch_dd_hypotheses(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK
+                                                                                             : DBV_ERR_LAUNCH;
+}
+
+dbv_status ddtree_level(int B, int L, int D, const uint8_t* masked, const int32_t* hyp_tok, const float* hyp_prob,
+                        const float* order_logits, int64_t o_seq_stride, int64_t o_row_stride, float tau,
+                        float gamma, int first, int32_t* parent, int32_t* edge_pos, int32_t* edge_tok,
+                        float* mass, uint8_t* node_masked, int32_t* num_nodes, int32_t* frontier,
+                        int32_t* num_frontier, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  return dd_tree_common(B, L, D, masked, hyp_tok, hyp_prob, order_logits, o_seq_stride, o_row_stride, 0, tau,
+                        gamma, first, parent, edge_pos, edge_tok, mass, node_masked, num_nodes, frontier,
+                        num_frontier, status, ws, ws_bytes, stream);
+}
+
+dbv_status ddtree_build(int B, int L, int D, const uint8_t* masked, const int32_t* hyp_tok, const float* hyp_prob,
+                        const float* order_table, int64_t t_seq_stride, int64_t t_row_stride, float tau,
+                        float gamma, int32_t* parent, int32_t* edge_pos, int32_t* edge_tok, float* mass,
+                        uint8_t* node_masked, int32_t* num_nodes, int32_t* frontier, int32_t* num_frontier,
+                        int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  return dd_tree_common(B, L, D, masked, hyp_tok, hyp_prob, order_table, t_seq_stride, t_row_stride, 1, tau,
+                        gamma, 1, parent, edge_pos, edge_tok, mass, node_masked, num_nodes, frontier,
+                        num_frontier, status, ws, ws_bytes, stream);
+}
+
 size_t verify_workspace_size(dbv_kind kind, int B, int K_or_S, int L, int V, dbv_dtype dtype) {
+  if (kind == DBV_KIND_DDTREE) {  // the search state depends on B and D only
+    if (B < 0 || K_or_S < 0 || K_or_S > dbv::kDDMaxBudget) return 0;
+    return dbv::dd_tree_bytes(B, K_or_S);
+  }
   if (B < 0 || V < 1 || !dtype_ok(dtype)) return 0;
   switch (kind) {
     case DBV_KIND_GREEDY:
@@ -465,6 +560,11 @@ size_t verify_workspace_size(dbv_kind kind, int B, int K_or_S, int L, int V, dbv
     case DBV_KIND_ANY_ORDER:
       if (K_or_S < 0 || K_or_S > kMaxDraft) return 0;
       return dbv::plan_any_order(B, K_or_S).bytes;
+    case DBV_KIND_DDTREE_HYPOTHESES:
+      if (K_or_S < 1 || K_or_S > dbv::kDDMaxBlock) return 0;
+      return dbv::plan_dd_hypotheses(B, K_or_S).bytes;
+    case DBV_KIND_DDTREE:
+      return 0;
   }
   return 0;
 }

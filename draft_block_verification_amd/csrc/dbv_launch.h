@@ -126,6 +126,51 @@ struct TruncArgs {
   int32_t* q_idx; float* q_prob; int32_t* q_nnz;
 };
 
+// DDTree token hypotheses: partial reductions of one piece of a stale row,
+// per (slot, wave).  T = 0: softmax statistics (M, S) at temperature 1 and
+// the two largest logits (v1, i1) >= (v2, i2).  T > 0: (M, S), the argmax
+// (v1, i1) of z/T + G, the logit x there and a NaN flag of the scores.
+struct DDPart {
+  float M, S, v1;
+  int i1;
+  float v2;
+  int i2;
+  float x;
+  int nan;
+};
+
+struct DDHypArgs {
+  int B, L, V;
+  const void* stale; int64_t ss, sp;   // [B, L, V] stale logits: element strides
+  const uint8_t* masked;               // [B, L] masked positions of the current state
+  const float* gumbel; int64_t gs, gp; // [B, L, V] Gumbel rows (T > 0)
+  float inv_t;                         // 1 / T, 0 for T = 0
+  float below;                         // runner-up kept when p^(argmax) < below (T = 0)
+  int32_t* hyp_tok; float* hyp_prob;   // [B, L, 2]
+  int32_t* status;                     // [B]
+  int32_t* count;                      // rows in the stream
+  int32_t* list;                       // stream row -> b*L + s
+  int32_t* map;                        // b*L + s -> stream row or -1
+  DDPart* part;                        // per (slot, wave)
+  int64_t grid;                        // groups of the row-streaming launch
+  int split_bytes;                     // bytes per element for the split (Gumbel rows included)
+};
+
+struct DDTreeArgs {
+  int B, L, D;
+  const uint8_t* masked;               // [B, L] masked positions of the root
+  const int32_t* hyp_tok; const float* hyp_prob;   // [B, L, 2]
+  const float* order; int64_t os, orow;  // order logit rows (per frontier slot, or the table)
+  int table;                           // 1: every level from the first-order table
+  int first;                           // one-level mode: start from the root
+  float inv_tau, gamma;
+  int32_t* parent; int32_t* edge_pos; int32_t* edge_tok; float* mass;   // [B, D+1]
+  uint8_t* node_masked;                // [B, D+1, L] or NULL
+  int32_t* num_nodes; int32_t* frontier; int32_t* num_frontier;        // [B], [B, D], [B]
+  int32_t* status;                     // [B] in / out
+  uint64_t* keys; uint64_t* masks;     // [B, D+1] search state kept between levels
+};
+
 // Optional events recorded around the row-streaming kernel of a call.
 struct TimingEvents {
   hipEvent_t begin = nullptr;
@@ -163,5 +208,7 @@ bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const Tim
 bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
 bool launch_any_order(const AnyOrderArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
 bool launch_truncate(const TruncArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
+bool launch_dd_hypotheses(const DDHypArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
+bool launch_dd_tree(const DDTreeArgs& a, hipStream_t stream);
 
 }  // namespace dbv

@@ -309,4 +309,39 @@ inline TreePlan plan_tree(int B, int S, int L, int V) {
   return p;
 }
 
+// DDTree: hypotheses over the masked stale rows, then the search.  Blocks of
+// at most kDDMaxBlock positions (one bit each in a 64-bit mask) and budgets
+// of at most kDDMaxBudget states; the search keeps the tree, the frontier and
+// up to kDDMaxCand candidates of one level in LDS.
+constexpr int kDDMaxBlock = 64;
+constexpr int kDDMaxBudget = 64;
+constexpr int kDDMaxCand = kDDMaxBudget * kDDMaxBlock * 2;
+constexpr int kDDPartBytes = 32;
+
+struct DDHypPlan {
+  int64_t max_rows;    // B*L
+  size_t off_count;    // int32
+  size_t off_list;     // int32 [max_rows]
+  size_t off_map;      // int32 [max_rows]
+  size_t off_part;     // DDPart per (slot, wave)
+  size_t bytes;
+};
+
+inline DDHypPlan plan_dd_hypotheses(int B, int L) {
+  DDHypPlan p{};
+  p.max_rows = static_cast<int64_t>(B) * L;
+  p.off_count = 0;
+  p.off_list = 256;
+  p.off_map = p.off_list + align256(static_cast<size_t>(p.max_rows) * 4);
+  p.off_part = p.off_map + align256(static_cast<size_t>(p.max_rows) * 4);
+  p.bytes = p.off_part + align256(static_cast<size_t>(p.max_rows + kMaxGrid) * kWavesPlan * kDDPartBytes);
+  return p;
+}
+
+// Search state between levels: a 64-bit sort key and a 64-bit masked-set per
+// tree node.
+inline size_t dd_tree_bytes(int B, int D) {
+  return align256(static_cast<size_t>(B) * (D + 1) * 16);
+}
+
 }  // namespace dbv

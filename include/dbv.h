@@ -13,7 +13,8 @@
  * drafter distributions (truncate_top_k_top_p writes them from drafter
  * rows), verify_spot_chain chain verification on the joint
  * (position, token) space and verify_greedy_any_order any-order greedy
- * verification.
+ * verification.  ddtree_hypotheses, ddtree_level and ddtree_build construct
+ * the draft tree that verify_gumbel_tree checks.
  *
  * Sources (pages by title):
  *   [PSS]  "One Call Ahead: Packed Self-Speculative Decoding with Diffusion
@@ -22,9 +23,11 @@
  *          App. B.2 (Algorithm 2, Lemma B.3), App. C (Algorithm 3, any-order
  *          verification), App. D.1 (packed row layout).
  *   [SPOT] "On the SPOT: Enhancing Speculative Decoding for Diffusion Language
- *          Models via Commit-Order Prediction" -- Sec. 4.1, Sec. 4.3,
- *          App. A.1 (formal decoding model), App. A.3 (Eq. 5-7), App. B
- *          (Eq. 10-14, Proposition 3), Table 22 (regime law).
+ *          Models via Commit-Order Prediction" -- Sec. 4.1, Sec. 4.2 (Eq. 3,
+ *          prefix mass; adaptive budget), Sec. 4.3 (Eq. 4), App. A.1 (formal
+ *          decoding model), App. A.3 (Eq. 5-7), App. B (Eq. 10-14,
+ *          Proposition 3), App. C.2 (Algorithm 2, DDTree), Table 22 (regime
+ *          law).
  *   [TT]   "Speculative Diffusion is a Tale of Two Tradeoffs" -- Sec. 2
  *          (Eq. 1-5, Theorem 1), Sec. 3.2 (Algorithm 1), App. E (modified
  *          Cactus, Eq. 17-18).
@@ -98,7 +101,9 @@ typedef enum {
   DBV_KIND_GREEDY = 0,
   DBV_KIND_REJECTION = 1, /* also verify_lenient, verify_cactus, verify_sparse, verify_spot_chain */
   DBV_KIND_TREE = 2,
-  DBV_KIND_ANY_ORDER = 3  /* K_or_S = U (window), L ignored */
+  DBV_KIND_ANY_ORDER = 3, /* K_or_S = U (window), L ignored */
+  DBV_KIND_DDTREE_HYPOTHESES = 4, /* K_or_S = L (block length) */
+  DBV_KIND_DDTREE = 5     /* K_or_S = D (budget), L, V and dtype ignored */
 } dbv_kind;
 
 /*
@@ -398,11 +403,101 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype,
                               int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ddtree_hypotheses -- token hypotheses of the masked positions for draft-
+ * tree construction ([SPOT] Sec. 4.2 "Inference", App. C.2).  For each
+ * position s with masked[b, s] != 0 the stale target row (logits at element
+ * offset b*seq_stride + s*pos_stride) gives p^_s = softmax(row) at
+ * temperature 1 and H(s):
+ *   temperature == 0: the argmax v0 of the logits, and the runner-up v1
+ *     (largest logit other than v0) when p^_s(v0) < runner_up_below (0.6 in
+ *     [SPOT]);
+ *   temperature > 0: the coupled stale draw of Eq. 4, argmax_v (z_v /
+ *     temperature + g_v) with the Gumbel row of the position (float32 at
+ *     element offset b*g_seq_stride + s*g_pos_stride).
+ * Writes hyp_tok[b, s, 0..1] (int32, -1 = none) and hyp_prob[b, s, 0..1]
+ * (p^_s of the token, float32, 0 for none), both [B, L, 2]; unmasked
+ * positions get (-1, 0) and are not read.  status[b] (NULL allowed) is
+ * overwritten: a read row holding NaN or +inf, or no finite logit
+ * (DBV_SEQ_NONFINITE / DBV_SEQ_EMPTY_ROW), or a Gumbel score row that is not
+ * a distribution.  Ties: lowest index.  1 <= L <= 64.  Workspace kind:
+ * DBV_KIND_DDTREE_HYPOTHESES.
+ */
+dbv_status ddtree_hypotheses(int B, int L, int V, dbv_dtype dtype,
+                             const void* stale, int64_t seq_stride, int64_t pos_stride,
+                             const uint8_t* masked, const float* gumbel,
+                             int64_t g_seq_stride, int64_t g_pos_stride,
+                             float temperature, float runner_up_below,
+                             int32_t* hyp_tok, float* hyp_prob, int32_t* status,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ddtree_level -- one level of the DDTree search ([SPOT] Sec. 4.2 Eq. 3 and
+ * App. C.2 Algorithm 2), with the order model run by the caller between
+ * levels.  State: node 0 is the current state x_t (mass 1, masked positions
+ * masked[b, :]); every other node z is a hypothetical state y (+) (s, v)
+ * with parent[b, z] < z, edge_pos = s, edge_tok = v and prefix mass
+ *   m(z) = m(y) q(s | y) p^_s(v)                                  (Eq. 3)
+ * where p^_s(v) = hyp_prob of token v at s (from ddtree_hypotheses) and
+ * q(s | y) = softmax over the masked positions M(y) of the order logits /
+ * tau (the calibration temperature).  A level takes each state of the
+ * frontier (the states admitted by the previous level; the root on the
+ * first level, first != 0, which also resets the tree), reads its order
+ * logits from row j of order_logits (float32 at element offset
+ * b*o_seq_stride + j*o_row_stride for frontier slot j; only entries at M(y)
+ * are read), forms every child y (+) (s, v), s in M(y), v in H(s), with
+ * m >= gamma (the prefix-mass floor; 0 keeps all), and keeps the D states
+ * of largest mass among the tree and the new children; the frontier becomes
+ * the children so admitted.  Repeat until num_frontier is 0: the tree then
+ * holds the D states of largest mass (sequential best-first order).
+ * Outputs (caller-owned, carried between levels; rewritten by each call):
+ * nodes in rank order (mass descending, then depth ascending, then the
+ * order of creation), parent / edge_pos / edge_tok [B, D+1] int32 (-1 past
+ * num_nodes), mass [B, D+1] float32, node_masked [B, D+1, L] uint8 (the
+ * masked positions of each state; NULL allowed), num_nodes [B] (incl. the
+ * root), frontier [B, D] (node indices, -1 past num_frontier),
+ * num_frontier [B].  The layout is the one verify_gumbel_tree reads (S =
+ * D+1).  status [B] (NULL allowed) is read and or-ed: a sequence that
+ * enters with an error bit is left as it is (on the first level its tree
+ * becomes the root alone); an order row with NaN or +inf on M(y) or no
+ * finite entry there, a missing argmax hypothesis or a probability outside
+ * [0, 1] at a masked position is an error that stops the sequence.  The
+ * workspace (kind DBV_KIND_DDTREE) holds the search state from one level
+ * to the next: use the same one for every level of a search.  1 <= L <= 64,
+ * 0 <= D <= 64, tau > 0, gamma >= 0.
+ */
+dbv_status ddtree_level(int B, int L, int D, const uint8_t* masked,
+                        const int32_t* hyp_tok, const float* hyp_prob,
+                        const float* order_logits, int64_t o_seq_stride, int64_t o_row_stride,
+                        float tau, float gamma, int first,
+                        int32_t* parent, int32_t* edge_pos, int32_t* edge_tok, float* mass,
+                        uint8_t* node_masked, int32_t* num_nodes, int32_t* frontier,
+                        int32_t* num_frontier, int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ddtree_build -- the whole DDTree search in one call with a first-order
+ * order model: the order logits of state y are row c of order_table
+ * (float32 at element offset b*t_seq_stride + c*t_row_stride), c = the
+ * position committed by y's last edge, or c = L for the root; the table
+ * has L + 1 rows of L entries per sequence.  Runs the levels of
+ * ddtree_level until no state is admitted (num_frontier = 0 on return) and
+ * writes the same outputs.  Workspace kind DBV_KIND_DDTREE.
+ */
+dbv_status ddtree_build(int B, int L, int D, const uint8_t* masked,
+                        const int32_t* hyp_tok, const float* hyp_prob,
+                        const float* order_table, int64_t t_seq_stride, int64_t t_row_stride,
+                        float tau, float gamma,
+                        int32_t* parent, int32_t* edge_pos, int32_t* edge_tok, float* mass,
+                        uint8_t* node_masked, int32_t* num_nodes, int32_t* frontier,
+                        int32_t* num_frontier, int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * verify_workspace_size -- bytes of scratch one call of `kind` needs.
  *   DBV_KIND_GREEDY:    K_or_S = K, L = W (draft rows)
  *   DBV_KIND_REJECTION: K_or_S = K, L ignored
  *   DBV_KIND_TREE:      K_or_S = S, L = block length
  *   DBV_KIND_ANY_ORDER: K_or_S = U, L ignored
+ *   DBV_KIND_DDTREE_HYPOTHESES: K_or_S = L (block length), V, dtype
+ *   DBV_KIND_DDTREE:    K_or_S = D (budget); L, V and dtype ignored
  * Returns 0 for invalid sizes.  Depends only on its arguments.
  */
 size_t verify_workspace_size(dbv_kind kind, int B, int K_or_S, int L, int V, dbv_dtype dtype);

@@ -235,21 +235,23 @@ def build_ddtree(stale, masked, order_fn, D, temperature, tau=1.0, gamma=0.0, gu
     masked [B, L] the masked positions of the current state, order_fn(b,
     path) -> [L] order logits, gumbel [B, L, V] (T > 0).  Returns per
     sequence: ``hyp_tok`` / ``hyp_prob`` [B, L, 2] (-1 / 0 where absent),
-    the margins, ``status`` and ``trees`` (a list of ``tree_arrays`` dicts,
+    the margins, ``hyp_status`` (rows of the hypotheses), ``status`` (with
+    the order rows of the search) and ``trees`` (a list of ``tree_arrays`` dicts,
     None for a sequence in error)."""
     stale = np.asarray(stale)
     B, L, V = stale.shape
     masked = np.asarray(masked).astype(bool)
     out = dict(hyp_tok=np.full((B, L, 2), -1, np.int64), hyp_prob=np.zeros((B, L, 2)),
                top1_margin=np.full((B, L), np.inf), pick_margin=np.full((B, L), np.inf),
-               status=np.zeros(B, np.int64), trees=[None] * B, chosen=[None] * B)
+               status=np.zeros(B, np.int64), hyp_status=np.zeros(B, np.int64), trees=[None] * B,
+               chosen=[None] * B)
     for b in range(B):
         st = 0
         for s in range(L):
             if masked[b, s]:
                 st |= row_status(stale[b, s])
         if st & STATUS_ERROR_MASK:
-            out["status"][b] = st
+            out["status"][b] = out["hyp_status"][b] = st
             continue
         hyps = []
         for s in range(L):
@@ -268,6 +270,7 @@ def build_ddtree(stale, masked, order_fn, D, temperature, tau=1.0, gamma=0.0, gu
             for k, (v, pv) in enumerate(h["hyp"]):
                 out["hyp_tok"][b, s, k] = v
                 out["hyp_prob"][b, s, k] = pv
+        out["hyp_status"][b] = st
         if st & STATUS_ERROR_MASK:
             out["status"][b] = st
             continue

@@ -294,3 +294,111 @@ def check_spot(g, x, o, t_target, t_draft, tau, dtype_name, eos_id=-1, len_budge
         np.testing.assert_array_equal(out_g[b], exp, err_msg=f"out_tokens seq {b}")
         assert _rel_ok(rm_g[b], Zr, max(rtol, 1e-4), 1e-7), ("Z", b, rm_g[b], Zr)
     return near
+
+
+# ------------------------------------------------------------------ DDTree --
+
+def check_ddtree_hypotheses(g, o, masked, dtype_name):
+    """Hypothesis tokens exactly, their probabilities within PROB_RTOL.  A
+    position whose top-1 probability lies within PROB_RTOL of the runner-up
+    threshold (T = 0) may differ in its runner-up slot, and one whose two best
+    Gumbel scores lie within NEAR_MARGIN may differ in its token; the
+    sequences holding such positions are returned (their trees are then
+    built from different hypotheses and are not compared)."""
+    rtol = PROB_RTOL[dtype_name]
+    ht, hp = npi(g["hyp_tok"]), np64(g["hyp_prob"])
+    np.testing.assert_array_equal(npi(g["status"]), o["hyp_status"], err_msg="status")
+    amb = set()
+    B, L = masked.shape
+    for b in range(B):
+        if o["hyp_status"][b] & oracle.STATUS_ERROR_MASK:
+            continue
+        for s in range(L):
+            if not masked[b, s]:
+                assert ht[b, s].tolist() == [-1, -1] and hp[b, s].tolist() == [0.0, 0.0], (b, s)
+                continue
+            near1 = o["top1_margin"][b, s] < rtol
+            nearg = o["pick_margin"][b, s] < NEAR_MARGIN
+            if nearg:
+                amb.add(b)
+                continue
+            assert ht[b, s, 0] == o["hyp_tok"][b, s, 0], (b, s)
+            assert _rel_ok(hp[b, s, 0], o["hyp_prob"][b, s, 0], rtol), (b, s, hp[b, s, 0], o["hyp_prob"][b, s, 0])
+            if near1 and ht[b, s, 1] != o["hyp_tok"][b, s, 1]:
+                # only presence may differ; the runner-up itself is exact
+                assert min(ht[b, s, 1], o["hyp_tok"][b, s, 1]) == -1, (b, s)
+                amb.add(b)
+                continue
+            assert ht[b, s, 1] == o["hyp_tok"][b, s, 1], (b, s)
+            assert _rel_ok(hp[b, s, 1], o["hyp_prob"][b, s, 1], rtol), (b, s)
+    return amb
+
+
+def ddtree_path_mass(path, masked_row, hyp, order_fn, b, tau):
+    """Prefix mass (SPOT Eq. 3) of a path of (position, token) edges, from
+    the oracle's order distribution and hypotheses (hyp[s] = [(v, p)])."""
+    m = 1.0
+    prefix = ()
+    for s, v in path:
+        done = {e[0] for e in prefix}
+        ms = [t for t in range(len(masked_row)) if masked_row[t] and t not in done]
+        q = oracle.order_distribution(order_fn(b, prefix), ms, tau)
+        pv = dict(hyp[s])[v]
+        m *= q[s] * pv
+        prefix += ((s, v),)
+    return m
+
+
+def check_ddtree_tree(g, b, o, masked_row, hyp, order_fn, D, tau, gamma, dtype_name):
+    """The GPU tree of sequence b: a valid tree (parents first, node masks,
+    edges on masked positions with hypothesis tokens), masses equal to the
+    oracle's prefix mass of each path and non-increasing in node order, and
+    the oracle's top-D set except for states whose mass lies within the
+    tolerance of the cut (the D-th mass) or of the floor gamma.  Returns the
+    number of such near-cut states."""
+    rtol = PROB_RTOL[dtype_name]
+    n = int(npi(g["num_nodes"])[b])
+    par = npi(g["parent"])[b]
+    pos = npi(g["edge_pos"])[b]
+    tok = npi(g["edge_tok"])[b]
+    mass = np64(g["mass"])[b]
+    nm = npi(g["node_masked"])[b]
+    L = len(masked_row)
+    assert 1 <= n <= D + 1
+    assert par[0] == -1 and mass[0] == 1.0
+    assert nm[0].tolist() == [int(bool(v)) for v in masked_row]
+    paths = [()]
+    for z in range(1, n):
+        y = par[z]
+        assert 0 <= y < z, (b, z, y)
+        s, v = int(pos[z]), int(tok[z])
+        assert nm[y][s] == 1, (b, z)
+        exp_mask = nm[y].copy()
+        exp_mask[s] = 0
+        assert nm[z].tolist() == exp_mask.tolist(), (b, z)
+        assert v in dict(hyp[s]), (b, z, s, v)
+        paths.append(paths[y] + ((s, v),))
+        assert mass[z] <= mass[z - 1] or z == 1, (b, z)
+    assert (par[n:] == -1).all() and (nm[n:] == 0).all()
+    band = lambda p: rtol * (len(p) + 1)
+    for z in range(1, n):
+        m = ddtree_path_mass(paths[z], masked_row, hyp, order_fn, b, tau)
+        assert _rel_ok(mass[z], m, band(paths[z]), 1e-30), (b, z, mass[z], m)
+    chosen = o["chosen"][b]
+    omass = dict(chosen)
+    theta = chosen[-1][1] if len(chosen) == D and D > 0 else None
+    kset, oset = set(paths[1:]), set(omass)
+    near = 0
+    for p in kset - oset:
+        m = ddtree_path_mass(p, masked_row, hyp, order_fn, b, tau)
+        ok = (theta is not None and m >= theta * (1 - 2 * band(p))) or abs(m - gamma) <= 2 * band(p) * gamma
+        assert ok, (b, "extra state", p, m, theta)
+        near += 1
+    for p in oset - kset:
+        m = omass[p]
+        ok = (theta is not None and m <= theta * (1 + 2 * band(p))) or abs(m - gamma) <= 2 * band(p) * gamma
+        assert ok, (b, "missing state", p, m, theta)
+        near += 1
+    if not near:
+        assert n - 1 == len(chosen)
+    return near

@@ -126,6 +126,29 @@ def _trunc(lib, **kw):
                                     a["k"], a["p"], a["kmax"], o, o, o, a["stream"])
 
 
+def _ddhyp(lib, **kw):
+    a = dict(B=2, L=8, V=100, dt=_lib.DBV_BF16, stale=FAKE, ss=800, sp=100, m=FAKE, g=FAKE, gs=800, gp=100,
+             T=1.0, below=0.6, o=FAKE, st=FAKE, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    o = a["o"]
+    return lib.ddtree_hypotheses(a["B"], a["L"], a["V"], a["dt"], a["stale"], a["ss"], a["sp"], a["m"], a["g"],
+                                 a["gs"], a["gp"], a["T"], a["below"], o, o, a["st"], a["ws"], a["wsb"],
+                                 a["stream"])
+
+
+def _ddtree(lib, level=False, **kw):
+    a = dict(B=2, L=8, D=5, m=FAKE, ht=FAKE, hp=FAKE, order=FAKE, os=72, orow=8, tau=1.0, gamma=0.0, first=1,
+             o=FAKE, nm=FAKE, fr=FAKE, st=FAKE, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    o = a["o"]
+    head = (a["B"], a["L"], a["D"], a["m"], a["ht"], a["hp"], a["order"], a["os"], a["orow"], a["tau"],
+            a["gamma"])
+    tail = (o, o, o, o, a["nm"], o, a["fr"], o, a["st"], a["ws"], a["wsb"], a["stream"])
+    if level:
+        return lib.ddtree_level(*head, a["first"], *tail)
+    return lib.ddtree_build(*head, *tail)
+
+
 def _spot(lib, **kw):
     a = dict(B=2, K=3, V=100, dt=_lib.DBV_BF16, tgt=FAKE, ts=400, tr=100, drf=FAKE, ds=300, dr=100, ps=FAKE,
              pp=FAKE, d=FAKE, c=FAKE, n=None, tt=1.0, td=1.0, g=FAKE, gs=400, gr=100, tau=0.6, ua=FAKE, ur=FAKE,
@@ -233,6 +256,37 @@ def test_truncate_limits(lib):
     assert _trunc(lib, V=(1 << 21) + 1) == _lib.DBV_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("kw", [
+    dict(B=-1), dict(L=0), dict(L=65), dict(V=0), dict(dt=3), dict(stale=None), dict(m=None), dict(o=None),
+    dict(ss=-1), dict(gp=-1), dict(T=-1.0), dict(T=float("nan")), dict(T=float("inf")), dict(g=None),
+    dict(below=float("nan")), dict(stale=FAKE + 1), dict(g=FAKE + 2),
+])
+def test_ddtree_hypotheses_rejects_bad_args(lib, kw):
+    assert _ddhyp(lib, **kw) == INVALID
+
+
+@pytest.mark.parametrize("level", [False, True])
+@pytest.mark.parametrize("kw", [
+    dict(B=-1), dict(L=0), dict(L=65), dict(D=-1), dict(D=65), dict(m=None), dict(ht=None), dict(hp=None),
+    dict(order=None), dict(os=-1), dict(orow=-1), dict(tau=0.0), dict(tau=float("nan")), dict(gamma=-0.1),
+    dict(gamma=float("inf")), dict(o=None), dict(fr=None), dict(order=FAKE + 2),
+])
+def test_ddtree_rejects_bad_args(lib, level, kw):
+    assert _ddtree(lib, level=level, **kw) == INVALID
+
+
+def test_ddtree_workspace(lib):
+    h = lib.verify_workspace_size(_lib.DBV_KIND_DDTREE_HYPOTHESES, 16, 32, 0, 151936, _lib.DBV_BF16)
+    assert h >= 16 * 32 * 8 and h % 256 == 0
+    assert lib.verify_workspace_size(_lib.DBV_KIND_DDTREE_HYPOTHESES, 16, 65, 0, 100, 1) == 0
+    t = lib.verify_workspace_size(_lib.DBV_KIND_DDTREE, 16, 20, 32, 0, 0)
+    assert t >= 16 * 21 * 16 and t % 256 == 0
+    assert lib.verify_workspace_size(_lib.DBV_KIND_DDTREE, 16, 65, 32, 0, 0) == 0
+    assert _ddhyp(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
+    assert _ddtree(lib, wsb=16) == _lib.DBV_ERR_WORKSPACE
+    assert _ddtree(lib, level=True, ws=FAKE + 8) == _lib.DBV_ERR_WORKSPACE
+
+
 def test_workspace_errors(lib):
     assert _greedy(lib, ws=None) == _lib.DBV_ERR_WORKSPACE
     assert _greedy(lib, wsb=8) == _lib.DBV_ERR_WORKSPACE
@@ -262,6 +316,10 @@ def test_optional_arguments_are_accepted(lib):
     assert _trunc(lib, B=0, rows=None, o=None) == nodev
     assert _sparse(lib, K=0, qi=None, qp=None, qn=None, d=None, ua=None) == nodev
     assert _spot(lib, K=0, drf=None, pp=None, d=None, c=None, ua=None) == nodev
+    assert _ddhyp(lib, T=0.0, g=None, st=None) == nodev
+    assert _ddhyp(lib, B=0, stale=None, m=None, o=None) == nodev
+    assert _ddtree(lib, nm=None, st=None) == nodev
+    assert _ddtree(lib, level=True, D=0, fr=None) == nodev
 
 
 def test_valid_call_without_gpu_reports_no_device(lib):

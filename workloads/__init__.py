@@ -385,3 +385,50 @@ def config3_truncate(device="cpu"):
     drf = (z + torch.randn(32, 16, 151936, generator=_gen(c, 2, device), device=device)).to(torch.bfloat16)
     n = torch.full((32,), 16, dtype=torch.int32)
     return dict(drf=drf, draft_len=n, top_k=20, top_p=0.9)
+
+
+# ------------------------------------------------------------------ DDTree --
+
+def ddtree_inputs(c, B, L, V, dtype=torch.bfloat16, temperature=1.0, peak_lo=12.0, peak_hi=24.0,
+                  masked_min=0.5, device="cpu"):
+    """Inputs of draft-tree construction for a partly decoded block.
+
+    stale [B, L, V]: z ~ N(0, 3^2) plus a peak at one seeded token, the peak
+    height per row uniform in [peak_lo, peak_hi], so that the stale top-1
+    probability falls on both sides of 0.6 across rows.  masked [B, L]: each
+    sequence has a seeded number of masked positions in [masked_min * L, L]
+    at seeded places.  gumbel [B, L, V] float32 (None at T = 0).  Two
+    stand-in order models (the learned order model is not part of this
+    work): order_table [B, L+1, L], row c (the last committed position) =
+    -0.5 |s - c - 1| + N(0, 1), row L (the root) = -0.25 s + N(0, 1), a
+    tendency to commit next to the last commit; and a set-dependent model
+    order_A [B, L], order_B [B, L, L] whose logits for a state are order_A +
+    the sum of order_B rows over the positions it has committed.
+    """
+    z = torch.randn(B, L, V, generator=_gen(c, 0, device), device=device) * 3.0
+    pos = torch.randint(0, V, (B, L, 1), generator=_gen(c, 1, device), device=device)
+    h = peak_lo + (peak_hi - peak_lo) * torch.rand(B, L, 1, generator=_gen(c, 2, device), device=device)
+    z.scatter_add_(-1, pos, h)
+    stale = z.to(dtype)
+    gm = _gen(c, 8, "cpu")
+    masked = torch.zeros(B, L, dtype=torch.uint8)
+    lo = max(0, int(math.ceil(masked_min * L)))
+    for b in range(B):
+        k = int(torch.randint(lo, L + 1, (1,), generator=gm))
+        masked[b, torch.randperm(L, generator=gm)[:k]] = 1
+    G = gumbel_noise((B, L, V), _gen(c, 6, device), device) if temperature > 0 else None
+    go = _gen(c, 9, "cpu")
+    s = torch.arange(L, dtype=torch.float32)
+    table = torch.randn(B, L + 1, L, generator=go)
+    table[:, :L] += -0.5 * (s[None, :] - s[:, None] - 1).abs()
+    table[:, L] += -0.25 * s
+    oa = torch.randn(B, L, generator=_gen(c, 10, "cpu"))
+    ob = torch.randn(B, L, L, generator=_gen(c, 11, "cpu")) * 0.7
+    return dict(stale=stale, masked=masked.to(device), gumbel=G, temperature=temperature,
+                order_table=table.to(device), order_A=oa.to(device), order_B=ob.to(device))
+
+
+def config4_ddtree(device="cpu"):
+    """DDTree construction: B=16 blocks of L=32 positions, V=151936 bf16
+    stale rows, T=1 (coupled stale draw with Gumbel rows), budget D=20."""
+    return ddtree_inputs(45, 16, 32, 151936, torch.bfloat16, temperature=1.0, device=device)
