@@ -128,8 +128,10 @@ struct TruncArgs {
 
 // DDTree token hypotheses: partial reductions of one piece of a stale row,
 // per (slot, wave).  T = 0: softmax statistics (M, S) at temperature 1 and
-// the two largest logits (v1, i1) >= (v2, i2).  T > 0: (M, S), the argmax
-// (v1, i1) of z/T + G, the logit x there and a NaN flag of the scores.
+// the two largest logits v1 >= v2, each with the start index (i1, i2) of the
+// group of contiguous elements that holds it.  T > 0: (M, S), the best score
+// v1 of z/T + G with its group i1, and a NaN flag of the scores.  (x is
+// unused.)
 struct DDPart {
   float M, S, v1;
   int i1;
