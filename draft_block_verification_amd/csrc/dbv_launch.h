@@ -156,6 +156,7 @@ struct DDHypArgs {
   DDPart* part;                        // per (slot, wave)
   int64_t grid;                        // groups of the row-streaming launch
   int split_bytes;                     // bytes per element for the split (Gumbel rows included)
+  int fused_plan;                      // the row stream lists its rows itself (set by the launcher)
 };
 
 struct DDTreeArgs {

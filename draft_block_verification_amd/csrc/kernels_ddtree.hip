@@ -2,7 +2,9 @@
 // Eq. 4 and App. C.2 Algorithm 2).
 //
 //   k_dd_plan   one group: lists the stale rows to read -- the masked
-//               positions of every sequence -- and maps (b, s) to the list.
+//               positions of every sequence -- and maps (b, s) to the list
+//               (only for large B*L; otherwise every group of k_dd_rows lists
+//               them itself in LDS and group 0 writes the map).
 //   k_dd_rows   persistent: per listed row, partial reductions of its pieces
 //               (FlatSplit, as the verification streams): the softmax
 //               statistics at temperature 1 with the two largest logits
@@ -77,6 +79,9 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 // ------------------------------------------------------------ hypotheses ---
 
 constexpr int kDDPlanThreads = 1024;
+// Up to this many (sequence, position) flags, every group of the row stream
+// lists the rows itself and no plan kernel runs.
+constexpr int kDDFusedPlan = 8192;
 
 __global__ __launch_bounds__(kDDPlanThreads) void k_dd_plan(DDHypArgs a) {
   __shared__ int s_w[kDDPlanThreads / 64];
@@ -313,13 +318,74 @@ __device__ __forceinline__ int find_first(const char* row, const float* gr, floa
   return bal ? g0 + static_cast<int>(__ffsll(static_cast<unsigned long long>(bal))) - 1 : -1;
 }
 
+// Rows of the stream listed by every group itself when B*L is small (no plan
+// kernel): the masked flags in LDS with the count before each thread's chunk.
+struct RowDir {
+  uint8_t m[kDDFusedPlan];
+  int pre[kBlock + 1];
+  int w[kWaves];
+};
+
+// Builds the directory and returns the number of stream rows.  Group 0 also
+// writes what the plan kernel would: map, count, and the cleared status.
+__device__ int row_dir(const DDHypArgs& a, RowDir& d, bool writer) {
+  const int t = threadIdx.x;
+  const int F = a.B * a.L;
+  const int C = (F + kBlock - 1) / kBlock;
+  const int lo = t * C, hi = min(F, lo + C);
+  int cnt = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint8_t v = a.masked[i] != 0;
+    d.m[i] = v;
+    cnt += v;
+  }
+  int total;
+  const int off = group_exclusive_scan<kWaves>(cnt, total, d.w);
+  d.pre[t] = off;
+  if (t == 0) d.pre[kBlock] = total;
+  if (writer) {
+    int k = off;
+    for (int i = lo; i < hi; ++i) {
+      a.map[i] = d.m[i] ? k : -1;
+      k += d.m[i];
+    }
+    if (t == 0) *a.count = total;
+    if (a.status)
+      for (int b = t; b < a.B; b += kBlock) a.status[b] = 0;
+  }
+  __syncthreads();
+  return total;
+}
+
+// The flat id b*L + s of stream row r (the r-th masked flag).
+__device__ __forceinline__ int row_flat(const DDHypArgs& a, const RowDir& d, int r) {
+  const int F = a.B * a.L;
+  const int C = (F + kBlock - 1) / kBlock;
+  int lo = 0, hi = kBlock;                 // largest j with pre[j] <= r
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (d.pre[mid] <= r) lo = mid; else hi = mid;
+  }
+  int left = r - d.pre[lo];
+  int i = lo * C;
+  for (; i < F; ++i) {                     // the chunk holds row r
+    if (d.m[i]) {
+      if (left == 0) break;
+      --left;
+    }
+  }
+  return i;
+}
+
 template <int DT, bool GUM>
 __global__ __launch_bounds__(kBlock) void k_dd_rows(DDHypArgs a) {
-  const FlatSplit f = make_split(*a.count, a.V, a.split_bytes, a.grid);
+  __shared__ RowDir d;
   const int64_t g = blockIdx.x;
+  const int R = a.fused_plan ? row_dir(a, d, g == 0) : *a.count;
+  const FlatSplit f = make_split(R, a.V, a.split_bytes, a.grid);
   if (g >= f.G) return;
   for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1) {
-    const int flat = a.list[r];
+    const int flat = a.fused_plan ? row_flat(a, d, static_cast<int>(r)) : a.list[r];
     const int b = flat / a.L;
     const int s = flat - b * a.L;
     const char* rowp = static_cast<const char*>(a.stale) +
@@ -651,7 +717,11 @@ __device__ __forceinline__ void dd_rank(const DDTreeArgs& a, DDTreeLds& s, const
       for (; j < nx; j += P) r += X[j] > k;
     }
   }
-  for (int m = 1; m < P; m <<= 1) r += __shfl_xor(r, m, 64);
+  // sum over the P lanes of a contender (P <= 16: within one DPP row)
+  if (P >= 2) r += dpp_move<0xB1, 0xf>(0, r);     // quad_perm 1,0,3,2
+  if (P >= 4) r += dpp_move<0x4E, 0xf>(0, r);     // quad_perm 2,3,0,1
+  if (P >= 8) r += dpp_move<0x141, 0xf>(0, r);    // row_half_mirror
+  if (P >= 16) r += dpp_move<0x140, 0xf>(0, r);   // row_mirror
   if (item < nu && part == 0 && r < a.D) dd_place(s, k, src(item), r);
 }
 
@@ -690,20 +760,24 @@ __device__ void dd_level(const DDTreeArgs& a, DDTreeLds& s, int b) {
     const float e = in ? fast_exp2((z - mx) * kLog2e) : 0.f;
     const float q = e / wave_sum_dpp(e);
     const float my_mass = s.mass[y];
+    uint64_t key[2];
+    bool keep[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int tk = in ? s.htok[lane][k] : -1;
       const float m = fminf(my_mass * q * s.hp[in ? lane : 0][k], my_mass);
-      const bool ok = tk >= 0 && m >= a.gamma;
-      const uint64_t key = dd_key(m, depth, j * 128 + lane * 2 + k);
-      const bool keep = ok && key > theta;
-      const uint64_t bal = __ballot(keep);
-      if (bal == 0) continue;
-      int base = 0;
-      if (lane == 0) base = atomicAdd(&s.nc, __popcll(bal));
-      base = __builtin_amdgcn_readfirstlane(base);
-      if (keep) s.ck[base + __popcll(bal & ((1ull << lane) - 1))] = key;
+      key[k] = dd_key(m, depth, j * 128 + lane * 2 + k);
+      keep[k] = tk >= 0 && m >= a.gamma && key[k] > theta;
     }
+    const uint64_t b0 = __ballot(keep[0]), b1 = __ballot(keep[1]);
+    const int c0 = __popcll(b0);
+    if (c0 + __popcll(b1) == 0) continue;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&s.nc, c0 + __popcll(b1));   // one LDS atomic per row
+    base = __builtin_amdgcn_readfirstlane(base);
+    const uint64_t below = (1ull << lane) - 1;
+    if (keep[0]) s.ck[base + __popcll(b0 & below)] = key[0];
+    if (keep[1]) s.ck[base + c0 + __popcll(b1 & below)] = key[1];
   }
   __syncthreads();
   if (s.st & SEQ_ERROR_MASK) return;
@@ -834,11 +908,13 @@ bool launch_dd_hypotheses(const DDHypArgs& a, int dtype, hipStream_t stream, con
   const bool gum = a.inv_t > 0.f;
   const void* rows = gum ? (bf ? fn(k_dd_rows<DT_BF16, true>) : fn(k_dd_rows<DT_F32, true>))
                          : (bf ? fn(k_dd_rows<DT_BF16, false>) : fn(k_dd_rows<DT_F32, false>));
-  return launch_threads(fn(k_dd_plan), 1, kDDPlanThreads, stream, a) &&
-         launch(rows, a.grid, stream, a, ev) &&
+  DDHypArgs b = a;
+  b.fused_plan = static_cast<int64_t>(a.B) * a.L <= kDDFusedPlan ? 1 : 0;
+  return (b.fused_plan || launch_threads(fn(k_dd_plan), 1, kDDPlanThreads, stream, b)) &&
+         launch(rows, b.grid, stream, b, ev) &&
          launch(gum ? (bf ? fn(k_dd_hyp<DT_BF16, true>) : fn(k_dd_hyp<DT_F32, true>))
                     : (bf ? fn(k_dd_hyp<DT_BF16, false>) : fn(k_dd_hyp<DT_F32, false>)),
-                cdiv(static_cast<int64_t>(a.B) * a.L, kWaves), stream, a);
+                cdiv(static_cast<int64_t>(a.B) * a.L, kWaves), stream, b);
 }
 
 bool launch_dd_tree(const DDTreeArgs& a, hipStream_t stream) {

@@ -99,6 +99,20 @@ def test_hypotheses_parity(dev, dtype, T):
         assert 0 < two < npi(x["masked"]).sum()
 
 
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_hypotheses_many_rows(dev, T):
+    """B*L above the size at which the row stream lists its rows itself:
+    the separate plan kernel lists them."""
+    say("ddtree hypotheses B=200 L=48", T)
+    x = workloads.ddtree_inputs(66, 200, 48, 97, torch.float32, temperature=T, peak_lo=2.0, peak_hi=8.0)
+    h = dbv.ddtree_hypotheses(x["stale"].to(dev), x["masked"].to(dev), temperature=T,
+                              gumbel=None if x["gumbel"] is None else x["gumbel"].to(dev))
+    torch.cuda.synchronize()
+    o = _oracle(x, lambda b, p: np.zeros(48), 0, 1.0, 0.0)
+    amb = check_ddtree_hypotheses(h, o, npi(x["masked"]), "float32")
+    assert len(amb) <= 2
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("T,D,tau,gamma", [
     (0.0, 8, 1.0, 0.0), (0.0, 20, 0.7, 0.0), (1.0, 12, 1.0, 0.0), (1.0, 64, 1.0, 0.0),
