@@ -28,6 +28,8 @@ following the pages' definitions in their own order:
 * ``spot``   -- chain verification on the joint (position, token) space:
   rejection sampling per link (SPOT App. B) and the confidence-gated hybrid
   of coupled-noise match and rejection sampling.
+* ``loop``   -- multi-iteration Packed-SS decoding with greedy verification
+  (Packed-SS Sec. 3.1, Algorithm 1) over a model given as a function.
 * ``ddtree`` -- prefix-conditional draft-tree construction: token hypotheses
   from the stale conditionals, prefix masses and the top-D tree (SPOT
   Sec. 4.2 Eq. 3, App. C.2 Algorithm 2).
@@ -68,3 +70,4 @@ from .ddtree import (  # noqa: F401
     RUNNER_UP_BELOW, hypotheses, order_distribution, table_order, best_first,
     level_batched, tree_arrays, build_ddtree,
 )
+from .loop import packed_ss_greedy  # noqa: F401

@@ -395,3 +395,43 @@ def test_ddtree_pin_catches_planted_mistake(monkeypatch, name, fn, pin):
     monkeypatch.setattr(ddtree, name, fn)
     with pytest.raises(AssertionError):
         pin()
+
+
+# ------------------------------------------------------------- Packed-SS loop
+
+import oracle.loop as loopmod  # noqa: E402
+import tests.test_oracle_loop_pins as lpins  # noqa: E402
+
+_VERIFY_GREEDY = loopmod.verify_greedy
+
+
+def _retain_from_a(tgt, d, n, rows, eos_id=-1, budget=None):
+    """Keeps (z_A, ..., z_W) as the next draft: one position too early."""
+    o = _VERIFY_GREEDY(tgt, d, n, rows, eos_id, budget)
+    zs = np.asarray(rows).argmax(-1)
+    for b in range(len(o["num_out"])):
+        a = int(o["num_out"][b])
+        if a >= 1:
+            keep = zs[b, a - 1:]
+            o["next_draft"][b] = -1
+            o["next_draft"][b, :len(keep) - 1] = keep[:-1]
+    return o
+
+
+def _bonus_dropped(tgt, d, n, rows, eos_id=-1, budget=None):
+    o = _VERIFY_GREEDY(tgt, d, n, rows, eos_id, budget)
+    for b in range(len(o["num_out"])):
+        if o["accept_len"][b] >= 1 and o["num_out"][b] == o["accept_len"][b] + 1:
+            o["num_out"][b] -= 1
+            o["out_tokens"][b, o["num_out"][b]] = -1
+    return o
+
+
+@pytest.mark.parametrize("fn,pin", [
+    (_retain_from_a, lpins.test_perfect_drafter_alternates),
+    (_bonus_dropped, lpins.test_perfect_drafter_alternates),
+])
+def test_loop_pin_catches_planted_mistake(monkeypatch, fn, pin):
+    monkeypatch.setattr(loopmod, "verify_greedy", fn)
+    with pytest.raises(AssertionError):
+        pin()

@@ -432,3 +432,68 @@ def config4_ddtree(device="cpu"):
     """DDTree construction: B=16 blocks of L=32 positions, V=151936 bf16
     stale rows, T=1 (coupled stale draw with Gumbel rows), budget D=20."""
     return ddtree_inputs(45, 16, 32, 151936, torch.bfloat16, temperature=1.0, device=device)
+
+
+# ------------------------------------------------- Packed-SS loop driver --
+
+LOOP_PEAK = 30.0
+
+
+def packed_loop_inputs(c, B, W, V, L, dtype=torch.bfloat16, eps_pct=10, R=256, device="cpu"):
+    """A synthetic model for a multi-iteration Packed-SS loop: its greedy
+    continuation of sequence b is a seeded token string T[b] (the target's
+    own greedy output), and every logit row is one of R seeded rows z ~ N(0,
+    3^2) with one entry set to LOOP_PEAK = 30 (above every other logit).
+
+    * Verify row r of a call (the token after the prefix P and r draft
+      tokens) peaks at T[b, |P| + r] when those r draft tokens equal T there,
+      else at a token hashed from (b, position).
+    * Draft row j (position |P| + j, conditioned on P only) peaks at
+      T[b, |P| + j], except when a coin hashed from (b, position, call) falls
+      below eps_pct percent: then at a hashed token.
+
+    The rows are pure data (gathers of table rows and one scatter), computed
+    the same way on the CPU and on the GPU."""
+    table = (torch.randn(R, V, generator=_gen(c, 0, "cpu")) * 3.0).to(dtype)
+    T = torch.randint(0, V, (B, L + 2 * W), generator=_gen(c, 1, "cpu"))
+    return dict(table=table.to(device), T=T.to(device), B=B, W=W, V=V, L=L, R=R, eps_pct=eps_pct)
+
+
+def packed_loop_rows(inp, plen, d, n, t):
+    """Packed rows [B, 2W, V] of call t for prefix lengths plen [B], drafts
+    d [B, W-1] (-1 padded) and draft lengths n [B]: verify rows 0..W-1, then
+    draft rows W..2W-1.  Tensors on the device of inp."""
+    B, W, V, R = inp["B"], inp["W"], inp["V"], inp["R"]
+    T, table = inp["T"], inp["table"]
+    dev = T.device
+    plen = plen.to(dev).long()
+    d = d.to(dev).long()
+    n = n.to(dev).long()
+    r = torch.arange(W, device=dev)
+    pos = plen[:, None] + r[None, :]                                    # [B, W]
+    bb = torch.arange(B, device=dev)[:, None]
+    truth = torch.gather(T, 1, pos)
+    # verify row r sees the draft tokens before it: all equal to T there?
+    dm = torch.full((B, W), -1, dtype=torch.long, device=dev)
+    dm[:, :W - 1] = torch.where(r[None, :W - 1] < n[:, None], d, torch.full_like(d, -1))
+    agree = (dm == truth).long()
+    ok = torch.ones((B, W), dtype=torch.long, device=dev)
+    ok[:, 1:] = torch.cumprod(agree, dim=1)[:, :W - 1]
+    other = (pos * 2654435761 + bb * 97 + 12345) % V
+    vtok = torch.where(ok.bool(), truth, other)
+    coin = (((pos * 40503 + bb * 31 + t * 17 + 7) * 2654435761) >> 16) % 100
+    dtok = torch.where(coin >= inp["eps_pct"], truth, (pos * 2246822519 + bb * 13 + t * 7) % V)
+    vrow = (bb * 131 + pos * 7) % R
+    drow = (bb * 31 + pos * 11 + 5) % R
+    rows = torch.cat([vrow, drow], dim=1)                               # [B, 2W]
+    packed = table[rows.reshape(-1)].reshape(B, 2 * W, V).clone()
+    peak = torch.cat([vtok, dtok], dim=1)[:, :, None]
+    packed.scatter_(2, peak, torch.full(peak.shape, LOOP_PEAK, dtype=packed.dtype, device=dev))
+    return packed
+
+
+def config5_loop(device="cpu"):
+    """Packed-SS loop: B=64 sequences, W=32 (31 draft positions verified +
+    the bonus row, 32 draft rows per call), V=131072 bf16, L=256 new tokens,
+    a drafter wrong at 10% of positions."""
+    return packed_loop_inputs(51, 64, 32, 131072, 256, torch.bfloat16, eps_pct=10, device=device)
