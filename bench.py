@@ -23,6 +23,12 @@ and the correction or bonus draw.  Workloads (sizes of the pages' setups):
   c4d DDTree construction         B=16 L=32 V=151936 bf16 stale rows, T=1 (Gumbel
                                   rows), budget D=20: hypotheses + top-D search
                                   (positions = tree states drafted)
+  c5loop Packed-SS loop           B=64 W=32 V=131072 bf16, 256 new tokens per
+                                  sequence: verify_greedy once per model call
+                                  over a synthetic model with a known greedy
+                                  continuation; a step is one verify call, the
+                                  model's rows are written between steps
+                                  (untimed); reports tokens per call
 
 Inputs smaller than 1 GiB are replicated into several buffer sets and the
 steps rotate over them, so the 256 MiB last-level cache cannot serve them.
@@ -63,6 +69,7 @@ DESCR = {
     "c3q": "sparse stored-Q verify B=32 K=16 V=151936 bf16 top-k=20",
     "c3t": "top-k/top-p truncation B=32 K=16 V=151936 bf16 top-k=20 top-p=0.9",
     "c4d": "DDTree construction B=16 L=32 V=151936 bf16 T=1 D=20",
+    "c5loop": "Packed-SS greedy loop B=64 W=32 V=131072 bf16 L=256, drafter right at 90% of positions",
 }
 DD_BUDGET = 20
 SPOT_TAU = 0.6
@@ -445,6 +452,129 @@ class Case:
                 "sample": f"{sample} in {dt:.1f} s (numpy float64, one thread; host has {os.cpu_count()} cpus)"}
 
 
+def run_loop(args, dev):
+    """The Packed-SS loop workload: every verify call of the loop is timed
+    (whole call on the stream, and its row kernel through the timing hook);
+    the synthetic model's rows are written between calls and not timed.
+    Before each timed call a 2 GiB scratch write pushes the freshly written
+    rows out of the caches, so the call reads its inputs from HBM like the
+    other workloads; a second pass without it is reported beside."""
+    import draft_block_verification_amd as dbv
+    from draft_block_verification_amd import _lib
+    import workloads
+    inp = workloads.config5_loop(device=dev)
+    B, W, V, L = inp["B"], inp["W"], inp["V"], inp["L"]
+    lib = _lib.load()
+    rec = {"ms": [], "kms": [], "pos": 0, "bytes": 0, "calls": 0, "tokens": 0}
+    scratch = torch.empty(1 << 30, dtype=torch.int16, device=dev)
+
+    def model(plen, d, n, t):
+        return workloads.packed_loop_rows(inp, plen, d, n, t)
+
+    def timed_loop(record, flush=True):
+        plen = torch.zeros(B, dtype=torch.int32, device=dev)
+        d = torch.full((B, W - 1), -1, dtype=torch.int32, device=dev)
+        n = torch.zeros(B, dtype=torch.int32, device=dev)
+        done = torch.zeros(B, dtype=torch.bool, device=dev)
+        j = torch.arange(W, device=dev)
+        for t in range(4 * L):
+            if bool(done.all()):
+                break
+            packed = model(plen, d, n, t)
+            budget = torch.where(done, torch.zeros_like(plen), L - plen)
+            call = dbv.verify_greedy(packed[:, :W], d, n, packed[:, W:], len_budget=budget, prepare=True)
+            if flush:
+                scratch.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            k0.record(); k1.record()
+            torch.cuda.synchronize()
+            lib.verify_set_timing_events(k0._as_parameter_, k1._as_parameter_)
+            e0.record()
+            r = call()
+            e1.record()
+            lib.verify_set_timing_events(None, None)
+            torch.cuda.synchronize()
+            if record:
+                rec["ms"].append(e0.elapsed_time(e1))
+                rec["kms"].append(k0.elapsed_time(k1))
+                nn = n.long()
+                rec["pos"] += int(nn.sum())
+                rec["bytes"] += int(((nn + 1 + W) * V * 2).sum())
+                rec["calls"] += 1
+                rec["tokens"] += int(r["num_out"].sum())
+            a = r["num_out"]
+            plen = plen + a
+            done = done | (plen >= L)
+            n = torch.where(done, torch.zeros_like(n), r["next_len"])
+            d = torch.where(j[None, :W - 1] < n[:, None], r["next_draft"][:, :W - 1], torch.full_like(d, -1))
+            if int((r["status"] & dbv.SEQ_ERROR_MASK).sum()):
+                print(json.dumps({"error": "verification reported data errors"}))
+                sys.exit(1)
+        return plen
+
+    timed_loop(False)                     # warm-up: one whole decode
+    plen = timed_loop(True)
+    ms = sum(rec["ms"]) / rec["calls"]
+    kms = sum(rec["kms"])
+    achieved = rec["bytes"] / (kms * 1e-3) / 1e9
+    flushed = dict(rec)
+    rec.update({"ms": [], "kms": [], "pos": 0, "bytes": 0, "calls": 0, "tokens": 0})
+    timed_loop(True, flush=False)
+    no_flush = {"ms_per_step": sum(rec["ms"]) / rec["calls"],
+                "kernel_ms": sum(rec["kms"]) / rec["calls"],
+                "frac": rec["bytes"] / (sum(rec["kms"]) * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    rec = flushed
+    line = {
+        "metric": METRIC,
+        "value": rec["pos"] / (sum(rec["ms"]) * 1e-3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": rec["calls"],
+        "warmup": rec["calls"],
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": dict(workload=DESCR["c5loop"], B=B, W=W, V=V, L=L, logits="bf16",
+                       calls=rec["calls"], tokens=rec["tokens"],
+                       tokens_per_call=rec["tokens"] / (rec["calls"] * B),
+                       verified_positions=rec["pos"], all_done=bool((plen >= L).all()),
+                       rows_still_in_cache=no_flush),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_greedy_rows",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": None,
+            "bytes_per_launch": rec["bytes"] / rec["calls"],
+            "kernel_ms": kms / rec["calls"],
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle.loop as oloop
+        t0 = time.perf_counter()
+        nb = 2
+        sub = workloads.packed_loop_inputs(51, 64, W, V, L, torch.bfloat16, eps_pct=10)
+
+        def model_nb(pl, dd, nn, t):
+            # the oracle loop over the first nb sequences of the same model
+            return workloads.packed_loop_rows(sub, torch.as_tensor(pl), torch.as_tensor(dd), torch.as_tensor(nn),
+                                              t, seqs=list(range(nb))).double().numpy()
+        toks, calls = oloop.packed_ss_greedy(model_nb, nb, W, L, 4 * L)
+        dt = time.perf_counter() - t0
+        pos = int(sum(int(c["draft_len"].sum()) for c in calls))
+        line["cpu_baseline"] = {"value": pos / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+                                "sample": f"the whole loop for {nb} of 64 sequences ({len(calls)} calls) in "
+                                          f"{dt:.1f} s (numpy float64, one thread)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -458,6 +588,9 @@ def main():
     from draft_block_verification_amd import _lib
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "c5loop":
+        run_loop(args, dev)
+        return
     steps = args.steps if args.steps is not None else (20 if args.workload == "c4" else 200)
     warmup = args.warmup if args.warmup is not None else (3 if args.workload == "c4" else 20)
 

@@ -459,19 +459,23 @@ def packed_loop_inputs(c, B, W, V, L, dtype=torch.bfloat16, eps_pct=10, R=256, d
     return dict(table=table.to(device), T=T.to(device), B=B, W=W, V=V, L=L, R=R, eps_pct=eps_pct)
 
 
-def packed_loop_rows(inp, plen, d, n, t):
+def packed_loop_rows(inp, plen, d, n, t, seqs=None):
     """Packed rows [B, 2W, V] of call t for prefix lengths plen [B], drafts
     d [B, W-1] (-1 padded) and draft lengths n [B]: verify rows 0..W-1, then
-    draft rows W..2W-1.  Tensors on the device of inp."""
-    B, W, V, R = inp["B"], inp["W"], inp["V"], inp["R"]
+    draft rows W..2W-1.  With seqs (a list of sequence indices) only those
+    sequences' rows, in that order.  Tensors on the device of inp."""
+    W, V, R = inp["W"], inp["V"], inp["R"]
     T, table = inp["T"], inp["table"]
     dev = T.device
+    seq = torch.arange(inp["B"], device=dev) if seqs is None else torch.as_tensor(seqs, device=dev).long()
+    B = seq.numel()
+    T = T[seq]
     plen = plen.to(dev).long()
     d = d.to(dev).long()
     n = n.to(dev).long()
     r = torch.arange(W, device=dev)
     pos = plen[:, None] + r[None, :]                                    # [B, W]
-    bb = torch.arange(B, device=dev)[:, None]
+    bb = seq[:, None]
     truth = torch.gather(T, 1, pos)
     # verify row r sees the draft tokens before it: all equal to T there?
     dm = torch.full((B, W), -1, dtype=torch.long, device=dev)
