@@ -73,13 +73,14 @@ __device__ __forceinline__ u32x4 load16(const char* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Row streaming.  Visits elements [v0, v1) of `row`; every thread sees its own
-// elements in increasing index order.  The op receives groups:
+// Row streaming by NT threads (default: one 256-thread group).  Visits
+// elements [v0, v1) of `row`; every thread sees its own elements in
+// increasing index order.  The op receives groups:
 //   op.template group<N>(x, idx0)  -- N contiguous values starting at idx0
 // Groups are the scalar head (to 16-byte alignment), U vectors at a time in
 // the body, and the scalar tail.
 // ---------------------------------------------------------------------------
-template <int DT, int U, class Op>
+template <int DT, int U, class Op, int NT = kBlock>
 __device__ __forceinline__ void stream_row(const void* row, int64_t v0, int64_t v1, Op& op) {
   using E = Elem<DT>;
   constexpr int W = E::kVec;
@@ -99,10 +100,10 @@ __device__ __forceinline__ void stream_row(const void* row, int64_t v0, int64_t 
   }
   const char* vb = base + a0 * E::kBytes;
   int64_t i = t;
-  for (; i + (U - 1) * kBlock < nvec; i += U * kBlock) {
+  for (; i + (U - 1) * NT < nvec; i += U * NT) {
     u32x4 r[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) r[u] = load16(vb + (i + u * kBlock) * 16);
+    for (int u = 0; u < U; ++u) r[u] = load16(vb + (i + u * NT) * 16);
     // Keep all U loads in flight before any of them is consumed: without this
     // barrier the scheduler hoists the first unpack above the later loads and
     // waits on the first load alone.
@@ -115,20 +116,20 @@ __device__ __forceinline__ void stream_row(const void* row, int64_t v0, int64_t 
 #pragma unroll
       for (int j = 0; j < W; ++j) x[u * W + j] = y[j];
     }
-    op.template block<U, W>(x, a0 + i * W, static_cast<int64_t>(kBlock) * W);
+    op.template block<U, W>(x, a0 + i * W, static_cast<int64_t>(NT) * W);
   }
   if (i < nvec) {  // the last (< U) vectors of this lane, loads issued together
     u32x4 r[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (i + u * kBlock < nvec) r[u] = load16(vb + (i + u * kBlock) * 16);
+      if (i + u * NT < nvec) r[u] = load16(vb + (i + u * NT) * 16);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (i + u * kBlock < nvec) {
+      if (i + u * NT < nvec) {
         float y[W];
         E::unpack(r[u], y);
-        op.template group<W>(y, a0 + (i + u * kBlock) * W);
+        op.template group<W>(y, a0 + (i + u * NT) * W);
       }
     }
   }

@@ -3,19 +3,22 @@
 // Drafting", Sec. 3.2: only the nonzero entries of a truncated drafter
 // distribution need storing).
 //
-//   k_truncate  one group of kBlock threads per row (b, i), i < n_b, every
-//   pass streaming the row with 16-byte loads:
-//     1. each thread's largest logit (and the row's NaN / +inf check); the
-//        k-th largest of these 256 maxima, tau, has at least k logits at or
-//        above it, and for a spread-out row only a few times k;
-//     2. one pass collects every logit >= tau into LDS (at most
-//        kTruncCand); if there are more, a radix select over the whole row
-//        (8-bit digits of an order-preserving key, one pass each) takes
-//        their place;
-//     3. among the candidates, a radix select in LDS of the k-th largest
-//        key and, where more logits equal it than the top-k needs, of the
-//        cut-off token id (ties go to the lower ids);
-//     4. the k kept sorted by (logit descending, id ascending) by counting
+//   k_truncate  one group of kTB threads per row (b, i), i < n_b:
+//     1. one streaming pass: each thread keeps its three largest logits (a
+//        median-of-three cascade per element), the contiguous group and the
+//        occurrence in it of each, and the largest logit it dropped; the
+//        row's NaN / +inf check comes from the thread maxima;
+//     2. tau = the smallest, over the waves, of each wave's ceil(k/16)-th
+//        largest thread maximum: at least k logits are >= tau;
+//     3. the kept entries >= tau are the candidates; each finds its token
+//        id inside its group; a radix select in LDS gives the k-th largest
+//        key and, where more logits equal it than the top-k needs, the
+//        token-id cut-off (ties go to the lower ids);
+//     4. if some thread dropped a logit >= that k-th key, the candidates may
+//        miss a kept token: the row is read again and every logit >= tau
+//        collected (and if those overflow LDS, a radix select over the
+//        whole row, one pass per 8-bit digit, takes their place);
+//     5. the k kept sorted by (logit descending, id ascending) by counting
 //        ranks; weights exp((x - x_max) / T); the shortest prefix whose
 //        mass reaches p of the total (all k for p = 1), renormalised and
 //        written in order.
@@ -40,12 +43,16 @@ constexpr int key_bits() {
   return DT == DT_BF16 ? 16 : 32;
 }
 
-constexpr int kTruncCand = 4096;   // LDS candidates of the common path
+constexpr int kTB = 1024;          // threads per row
+constexpr int kTW = kTB / 64;      // waves per row
+constexpr int kTruncCand = 4096;   // LDS candidates (>= 3 per thread)
+static_assert(kTruncCand >= 3 * kTB, "every thread's three kept logits fit");
 
 struct TruncLds {
   int hist[256];
   int bad, digit, above, n, keep, nc;
-  float tmax[kBlock];
+  uint32_t tau_key, drop_key;
+  uint32_t wtau[kTW];
   float cx[kTruncCand];            // candidates: logit and token id
   int cid[kTruncCand];
   uint32_t ckey[kMaxNnz];          // the kept k
@@ -53,21 +60,62 @@ struct TruncLds {
   float kx[kMaxNnz];
   int sidx[kMaxNnz];
   float sx[kMaxNnz];
-  float fw[kWaves];
+  float fw[kTW];
   float sum;
 };
 
-// Each thread's largest logit and the NaN / +inf check.
-struct MaxOp {
-  float m = -kInf;
-  int bad = 0;
+// The three largest logits of a thread in order (equal logits: the earlier
+// first), each with the start index of its contiguous group and its
+// occurrence among the equal logits of that group, and the largest logit
+// that fell out.  The maximum propagates NaN (the row check).
+struct Top3Op {
+  float v0 = -kInf, v1 = -kInf, v2 = -kInf;
+  int g0 = -1, g1 = -1, g2 = -1;
+  int c0 = 0, c1 = 0, c2 = 0;
+  float drop = -kInf;
+
   template <int N>
-  __device__ __forceinline__ void group(const float* x, int64_t) {
+  __device__ __forceinline__ void group(const float* x, int64_t idx0) {
+    // Work on copies: every select below is between values, never between
+    // fields (a select between fields would become a select of addresses
+    // and keep the tracker out of registers).
+    const float o0 = v0, o1 = v1, o2 = v2;
+    const int h0 = g0, h1 = g1, h2 = g2, e0 = c0, e1 = c1, e2 = c2;
+    float n0 = o0, n1 = o1, n2 = o2, dr = drop;
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      if (x[j] != x[j] || x[j] == kInf) bad = 1;
-      m = fmaxf(m, x[j]);
+      dr = fmaxf(dr, fminf(x[j], n2));
+      n2 = __builtin_amdgcn_fmed3f(x[j], n1, n2);
+      n1 = __builtin_amdgcn_fmed3f(x[j], n0, n1);
+      n0 = fmaxp(n0, x[j]);
     }
+    drop = dr;
+    // The new list is the stable merge of the old list with the group's
+    // logits (old entries first on equal logits): walk it, matching old
+    // entries in order; the rest come from this group, with their
+    // occurrence among equal logits of the group.
+    const int gi = static_cast<int>(idx0);
+    // slot 0: old entry 0 or new
+    const bool m0 = n0 == o0;
+    const int q0g = m0 ? h0 : gi, q0c = m0 ? e0 : 0;
+    // slot 1: the next old entry is 1 if slot 0 took old 0, else 0
+    const float p1 = m0 ? o1 : o0;
+    const bool m1 = n1 == p1;
+    const int q1g = m1 ? (m0 ? h1 : h0) : gi;
+    const int q1c = m1 ? (m0 ? e1 : e0) : ((!m0 && n1 == n0) ? 1 : 0);
+    // slot 2: next old entry index = m0 + m1
+    const int io = (m0 ? 1 : 0) + (m1 ? 1 : 0);
+    const float p2 = io == 2 ? o2 : io == 1 ? o1 : o0;
+    const bool m2 = n2 == p2;
+    const int q2g = m2 ? (io == 2 ? h2 : io == 1 ? h1 : h0) : gi;
+    // a new logit's occurrence: one more than the last new logit's if equal
+    const int lastc = !m1 ? q1c : (!m0 ? q0c : -1);
+    const float lastv = !m1 ? n1 : n0;
+    const bool lastnew = !m1 || !m0;
+    const int q2c = m2 ? (io == 2 ? e2 : io == 1 ? e1 : e0) : ((lastnew && lastv == n2) ? lastc + 1 : 0);
+    v0 = n0; v1 = n1; v2 = n2;
+    g0 = q0g; g1 = q1g; g2 = q2g;
+    c0 = q0c; c1 = q1c; c2 = q2c;
   }
   template <int U, int W>
   __device__ __forceinline__ void block(const float* x, int64_t idx0, int64_t ustride) {
@@ -198,7 +246,7 @@ __device__ __forceinline__ void pick_digit(TruncLds& s, int want, bool ascending
 }
 
 __device__ __forceinline__ void clear_hist(TruncLds& s) {
-  for (int j = threadIdx.x; j < 256; j += kBlock) s.hist[j] = 0;
+  for (int j = threadIdx.x; j < 256; j += kTB) s.hist[j] = 0;
   if (threadIdx.x == 0) {
     s.digit = 0;
     s.above = 0;
@@ -210,7 +258,7 @@ __device__ __forceinline__ void clear_hist(TruncLds& s) {
 // by_index, key)` fills s.hist for one digit.  Returns the k-th largest key
 // and the id cut-off among the keys equal to it (ties to the lower ids).
 template <int KB, class Hist>
-__device__ void radix_select(TruncLds& s, int k, Hist hist, uint32_t& kth, uint32_t& id_cut) {
+__device__ __forceinline__ void radix_select(TruncLds& s, int k, Hist hist, uint32_t& kth, uint32_t& id_cut) {
   uint32_t prefix = 0, mask = 0;
   int want = k;
   for (int shift = KB - 8; shift >= 0; shift -= 8) {
@@ -245,10 +293,62 @@ __device__ void radix_select(TruncLds& s, int k, Hist hist, uint32_t& kth, uint3
   }
 }
 
-static_assert(kMaxNnz <= kBlock, "one kept entry per thread");
+static_assert(kMaxNnz <= kTB, "one kept entry per thread");
 
+// The token id of a kept logit x at occurrence c of group g: the c-th
+// element equal to x in [g, g + W) (a group holds at most W elements; a
+// one-element group's logit is its first element).
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k_truncate(TruncArgs a) {
+__device__ __forceinline__ int find_in_group(const char* row, int64_t V, int g, int c, float x) {
+  constexpr int W = Elem<DT>::kVec;
+  float y[W];
+#pragma unroll
+  for (int j = 0; j < W; ++j) {       // every load issued before the scan
+    const int64_t id = static_cast<int64_t>(g) + j;
+    y[j] = Elem<DT>::load1(row, id < V ? id : V - 1);
+  }
+  int seen = 0, hit = -1;
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    const bool eq = static_cast<int64_t>(g) + j < V && y[j] == x;
+    if (eq && seen == c && hit < 0) hit = g + j;
+    seen += eq ? 1 : 0;
+  }
+  return hit;
+}
+
+// Wave-wide unsigned maximum by DPP lane moves (identity 0); every lane of
+// the wave must be active.  The result is read from lane 63.
+template <int C, int R>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), C, R, 0xf, false));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1, 0xf>(v));    // quad_perm 1,0,3,2
+  v = max(v, dpp_u32<0x4E, 0xf>(v));    // quad_perm 2,3,0,1
+  v = max(v, dpp_u32<0x141, 0xf>(v));   // row_half_mirror
+  v = max(v, dpp_u32<0x140, 0xf>(v));   // row_mirror
+  v = max(v, dpp_u32<0x142, 0xa>(v));   // row_bcast15 into rows 1, 3
+  v = max(v, dpp_u32<0x143, 0xc>(v));   // row_bcast31 into rows 2, 3
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// The kw-th largest of the wave's keys (with multiplicity): kw times the
+// wave maximum, each time removing one lane that holds it.
+__device__ __forceinline__ uint32_t wave_kth_key(uint32_t key, int kw) {
+  const int lane = threadIdx.x & 63;
+  uint32_t res = 0;
+  for (int it = 0; it < kw; ++it) {
+    res = wave_max_u32(key);
+    const uint64_t hit = __ballot(key == res);
+    if (lane == __ffsll(static_cast<unsigned long long>(hit)) - 1) key = 0;
+  }
+  return res;
+}
+
+// Two groups per CU: at most 64 VGPRs (8 waves per SIMD).
+template <int DT>
+__global__ __launch_bounds__(kTB, 8) void k_truncate(TruncArgs a) {
   __shared__ TruncLds s;
   const int r = blockIdx.x;
   const int b = r / a.K;
@@ -266,73 +366,106 @@ __global__ __launch_bounds__(kBlock) void k_truncate(TruncArgs a) {
   const int k = a.top_k < V ? a.top_k : static_cast<int>(V);
   constexpr int KB = key_bits<DT>();
 
-  // 1. per-thread maxima; tau = the k-th largest of them
+  // 1. one pass: each thread's top three, the largest dropped logit
   if (t == 0) {
     s.bad = 0;
     s.nc = 0;
     s.n = 0;
+    s.tau_key = 0xFFFFFFFFu;
+    s.drop_key = 0;
   }
+  __syncthreads();
+  Top3Op op;
+  stream_row<DT, 2, Top3Op, kTB>(row, 0, V, op);
+  // one LDS atomic per wave for the row check and the largest dropped key
+  // (a thread that dropped nothing reports -inf: a k-th key of -inf, from a
+  // row with fewer than k finite logits, always takes the exact path)
   {
-    MaxOp op;
-    stream_row<DT, 4>(row, 0, V, op);
-    s.tmax[t] = op.m;
-    if (op.bad) atomicOr(&s.bad, 1);
+    const bool bad = __ballot(op.v0 != op.v0 || op.v0 == kInf) != 0;
+    const uint32_t dk = wave_max_u32(order_key<DT>(op.drop));
+    if ((t & 63) == 0) {
+      if (bad) atomicOr(&s.bad, 1);
+      atomicMax(&s.drop_key, dk);
+    }
+  }
+  // 2. tau: the smallest over waves of each wave's ceil(k/waves)-th largest
+  //    thread maximum (each wave has that many logits >= it)
+  {
+    const int kw = (k + kTW - 1) / kTW;
+    const uint32_t wk = wave_kth_key(order_key<DT>(op.v0), kw);
+    if ((t & 63) == 0) atomicMin(&s.tau_key, wk);
   }
   __syncthreads();
   if (s.bad) {                          // not a distribution
     if (t == 0) a.q_nnz[r] = -1;
     return;
   }
-  {
-    const float mt = s.tmax[t];
-    int rank = 0;
-    for (int u = 0; u < kBlock; ++u) {
-      const float mu = s.tmax[u];
-      rank += (mu > mt || (mu == mt && u < t)) ? 1 : 0;
-    }
-    // k <= kMaxNnz <= kBlock: some thread has rank k - 1
-    if (rank == k - 1) s.digit = static_cast<int>(order_key<DT>(mt));
-  }
-  __syncthreads();
-  const uint32_t tkey = static_cast<uint32_t>(s.digit);
-  __syncthreads();
+  const uint32_t tkey = s.tau_key;
 
-  // 2. candidates >= tau
+  // 3. candidates: the kept logits >= tau, with their token ids
   {
-    CandOp<DT> op{s, tkey};
-    stream_row<DT, 4>(row, 0, V, op);
-  }
-  __syncthreads();
-  const int nc = s.nc;
-  uint32_t kth, id_cut;
-  if (nc <= kTruncCand) {
-    // 3. select among the candidates in LDS
-    radix_select<KB>(s, k, [&](uint32_t prefix, uint32_t mask, int shift, bool by_index, uint32_t pkey) {
-      for (int c = t; c < nc; c += kBlock) {
-        const uint32_t key = order_key<DT>(s.cx[c]);
-        if (by_index) {
-          const uint32_t id = static_cast<uint32_t>(s.cid[c]);
-          if (key == pkey && (id & mask) == prefix) atomicAdd(&s.hist[(id >> shift) & 255u], 1);
-        } else if ((key & mask) == prefix) {
-          atomicAdd(&s.hist[(key >> shift) & 255u], 1);
-        }
+    auto cand = [&](float v, int g, int c) {
+      if (g >= 0 && order_key<DT>(v) >= tkey) {
+        const int slot = atomicAdd(&s.nc, 1);   // at most 3 per thread: always fits
+        s.cx[slot] = v;
+        s.cid[slot] = find_in_group<DT>(row, V, g, c, v);
       }
-    }, kth, id_cut);
-    for (int c = t; c < nc; c += kBlock) keep_token(s, order_key<DT>(s.cx[c]), s.cx[c], s.cid[c], kth, id_cut);
+    };
+    cand(op.v0, op.g0, op.c0);
+    cand(op.v1, op.g1, op.c1);
+    cand(op.v2, op.g2, op.c2);
+  }
+  __syncthreads();
+  int nc = s.nc;
+  auto lds_hist = [&](uint32_t prefix, uint32_t mask, int shift, bool by_index, uint32_t pkey) {
+    for (int c = t; c < nc; c += kTB) {
+      const uint32_t key = order_key<DT>(s.cx[c]);
+      if (by_index) {
+        const uint32_t id = static_cast<uint32_t>(s.cid[c]);
+        if (key == pkey && (id & mask) == prefix) atomicAdd(&s.hist[(id >> shift) & 255u], 1);
+      } else if ((key & mask) == prefix) {
+        atomicAdd(&s.hist[(key >> shift) & 255u], 1);
+      }
+    }
+  };
+  uint32_t kth = 0, id_cut = 0;
+  bool exact = nc >= k;
+  if (exact) {
+    radix_select<KB>(s, k, lds_hist, kth, id_cut);
+    // a dropped logit at or above the k-th key may belong to the top k
+    exact = s.drop_key < kth;
+  }
+  __syncthreads();
+  if (exact) {
+    for (int c = t; c < nc; c += kTB) keep_token(s, order_key<DT>(s.cx[c]), s.cx[c], s.cid[c], kth, id_cut);
   } else {
-    // too many logits at or above tau: select over the whole row
-    radix_select<KB>(s, k, [&](uint32_t prefix, uint32_t mask, int shift, bool by_index, uint32_t pkey) {
-      HistOp<DT> op{s, prefix, mask, shift, by_index, pkey};
-      stream_row<DT, 4>(row, 0, V, op);
-    }, kth, id_cut);
-    CollectOp<DT> op{s, kth, id_cut};
-    stream_row<DT, 4>(row, 0, V, op);
+    // 4. read the row again: every logit >= tau
+    if (t == 0) s.nc = 0;
+    __syncthreads();
+    {
+      CandOp<DT> cop{s, tkey};
+      stream_row<DT, 4, CandOp<DT>, kTB>(row, 0, V, cop);
+    }
+    __syncthreads();
+    nc = s.nc;
+    if (nc <= kTruncCand) {
+      radix_select<KB>(s, k, lds_hist, kth, id_cut);
+      for (int c = t; c < nc; c += kTB) keep_token(s, order_key<DT>(s.cx[c]), s.cx[c], s.cid[c], kth, id_cut);
+    } else {
+      // too many logits at or above tau: select over the whole row
+      radix_select<KB>(s, k, [&](uint32_t prefix, uint32_t mask, int shift, bool by_index, uint32_t pkey) {
+        HistOp<DT> hop{s, prefix, mask, shift, by_index, pkey};
+        stream_row<DT, 4, HistOp<DT>, kTB>(row, 0, V, hop);
+      }, kth, id_cut);
+      CollectOp<DT> cop{s, kth, id_cut};
+      stream_row<DT, 4, CollectOp<DT>, kTB>(row, 0, V, cop);
+    }
   }
   __syncthreads();
 
-  // 4. sort, weights, top-p prefix
+  // 5. sort, weights, top-p prefix
   const int m = s.n < kMaxNnz ? s.n : kMaxNnz;   // == k
-  for (int c = t; c < m; c += kBlock) {
+  for (int c = t; c < m; c += kTB) {
     const uint32_t kc = s.ckey[c];
     const int ic = s.cidx[c];
     int rank = 0;
@@ -346,7 +479,7 @@ __global__ __launch_bounds__(kBlock) void k_truncate(TruncArgs a) {
   __syncthreads();
   const float xmax = s.sx[0];
   const bool bad = !(xmax > -kInf) || m != k;
-  // One entry per thread: m <= kMaxNnz <= kBlock.
+  // One entry per thread: m <= kMaxNnz <= kTB.
   const float wt = (t < m && !bad) ? fast_exp2((s.sx[t] - xmax) * a.kq) : 0.f;
   const int lane = t & 63;
   const int w = t >> 6;
@@ -361,7 +494,7 @@ __global__ __launch_bounds__(kBlock) void k_truncate(TruncArgs a) {
   __syncthreads();
   float base = 0.f, total = 0.f;
 #pragma unroll
-  for (int j = 0; j < kWaves; ++j) {
+  for (int j = 0; j < kTW; ++j) {
     if (j < w) base += s.fw[j];
     total += s.fw[j];
   }
@@ -385,8 +518,8 @@ static const void* fn(K* k) {
 
 bool launch_truncate(const TruncArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
   const bool bf = dtype == DT_BF16;
-  return launch(bf ? fn(k_truncate<DT_BF16>) : fn(k_truncate<DT_F32>), static_cast<int64_t>(a.B) * a.K, stream, a,
-                ev);
+  return launch_threads(bf ? fn(k_truncate<DT_BF16>) : fn(k_truncate<DT_F32>), static_cast<int64_t>(a.B) * a.K, kTB,
+                        stream, a, ev);
 }
 
 }  // namespace dbv
