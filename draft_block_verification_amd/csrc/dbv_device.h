@@ -276,26 +276,55 @@ __device__ __forceinline__ float block_sum(float v, float* s) {
   return r;
 }
 
-// Wave-level (M, S) reduction; every lane ends with the wave's result.
-__device__ __forceinline__ void wave_stats(float& M, float& S, float k) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float M2 = wave_shfl_xor(M, m);
-    const float S2 = wave_shfl_xor(S, m);
-    stats_merge(M, S, M2, S2, k);
-  }
+// Wave-wide reductions through DPP lane moves (no LDS round trips): the
+// quad butterflies, the half-row and row mirrors, then row broadcasts 15 and
+// 31 leave the result in lane 63.  Every lane of the wave must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_move(float identity, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v), CTRL, ROWS, 0xf,
+                                                    false));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_move(int identity, int v) {
+  return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROWS, 0xf, false);
 }
 
-// Wave-level argmax reduction; every lane ends with the wave's result.
+// Wave-level (M, S) reduction through DPP lane moves; every lane ends with
+// the wave's result (read from lane 63).  Every lane must be active.
+__device__ __forceinline__ void wave_stats(float& M, float& S, float k) {
+#define DBV_STATS_STEP(C, R)                                                  \
+  stats_merge(M, S, dpp_move<C, R>(-kInf, M), dpp_move<C, R>(0.f, S), k);
+  DBV_STATS_STEP(0xB1, 0xf)
+  DBV_STATS_STEP(0x4E, 0xf)
+  DBV_STATS_STEP(0x141, 0xf)
+  DBV_STATS_STEP(0x140, 0xf)
+  DBV_STATS_STEP(0x142, 0xa)
+  DBV_STATS_STEP(0x143, 0xc)
+#undef DBV_STATS_STEP
+  M = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), 63));
+  S = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), 63));
+}
+
+// Wave-level argmax (value, lowest index, NaN flag) through DPP lane moves;
+// every lane ends with the wave's result.  Every lane must be active.
 __device__ __forceinline__ void wave_argmax(float& v, int& idx, int& nan) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float v2 = wave_shfl_xor(v, m);
-    const int i2 = wave_shfl_xor(idx, m);
-    const int n2 = wave_shfl_xor(nan, m);
-    if (pick_better(v2, i2, v, idx)) { v = v2; idx = i2; }
-    nan |= n2;
+#define DBV_PICK_STEP(C, R)                                                   \
+  {                                                                           \
+    const float v2 = dpp_move<C, R>(-kInf, v);                                \
+    const int i2 = dpp_move<C, R>(-1, idx);                                   \
+    nan |= dpp_move<C, R>(0, nan);                                            \
+    if (pick_better(v2, i2, v, idx)) { v = v2; idx = i2; }                    \
   }
+  DBV_PICK_STEP(0xB1, 0xf)
+  DBV_PICK_STEP(0x4E, 0xf)
+  DBV_PICK_STEP(0x141, 0xf)
+  DBV_PICK_STEP(0x140, 0xf)
+  DBV_PICK_STEP(0x142, 0xa)
+  DBV_PICK_STEP(0x143, 0xc)
+#undef DBV_PICK_STEP
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  idx = __builtin_amdgcn_readlane(idx, 63);
+  nan = __builtin_amdgcn_readlane(nan, 63);
 }
 
 // ---------------------------------------------------------------------------

@@ -27,19 +27,6 @@
 
 namespace dbv {
 
-// Wave-wide reductions through DPP lane moves (no LDS round trips): the
-// quad butterflies, the half-row and row mirrors, then row broadcasts 15 and
-// 31 leave the result in lane 63.  Every lane of the wave must be active.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_move(float identity, float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v), CTRL, ROWS, 0xf,
-                                                    false));
-}
-template <int CTRL, int ROWS>
-__device__ __forceinline__ int dpp_move(int identity, int v) {
-  return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROWS, 0xf, false);
-}
-
 // Reduction of a wave's partial values with a commutative, associative
 // merge: after the six DPP steps (partners always cover disjoint lanes) lane
 // 63 holds the merge of all 64 lanes.  P provides
@@ -57,6 +44,8 @@ __device__ __forceinline__ P wave_merge_dpp(P p) {
   return p;
 }
 
+// Wave maximum (NaN-propagating) and sum of one float by the same DPP steps;
+// the result is read from lane 63 and returned to every lane.
 __device__ __forceinline__ float wave_max_dpp(float v) {
   v = fmaxp(v, dpp_move<0xB1, 0xf>(-kInf, v));    // quad_perm 1,0,3,2
   v = fmaxp(v, dpp_move<0x4E, 0xf>(-kInf, v));    // quad_perm 2,3,0,1
