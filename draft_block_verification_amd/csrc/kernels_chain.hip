@@ -755,6 +755,13 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
   rec.cq = resid && !sparse ? -s.Mq[h] * a.kq : 0.f;
   rec.isq = resid && !sparse ? 1.f / s.Sq[h] : 1.f;
   rec.u = a.u_resample[static_cast<int64_t>(b) * (a.K + 1) + h];
+  if (resid && a.rule == RULE_LINEAR && !(a.lam < 1.f)) {
+    // lambda = 1: p~ = q, so [p~ - q]_+ = (1 - lambda) [p - q]_+ vanishes
+    // (a draft is rejected only where q(d) = 0); the draw then falls back to
+    // p like any residual of zero mass.
+    rec.isp = 0.f;
+    rec.isq = 0.f;
+  }
   rec.excl = -1;
   rec.wexcl = 0.f;
   rec.fixed = -1;

@@ -122,6 +122,55 @@ def test_lenient_parity(dev, lam, sigma):
         np.testing.assert_array_equal(npi(res["accept_len"]), xn["draft_len"])
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("V", [3001, 32000, 600000])
+def test_lenient_full_leniency_zero_residual(dev, dtype, V):
+    # lambda = 1 gives p~ = q: a draft with q(d) = 0 is rejected (u q(d) < 0
+    # fails) and [p~ - q]_+ is zero everywhere, so the draw falls back to p
+    # and flags Z = 0 (Two Tradeoffs, Algorithm 1 with the zero-mass reading).
+    # The row sizes take both draw paths: one group per sequence (V = 3001)
+    # and the mass / select kernels (V = 32000; V = 600000 puts two or three
+    # tiles on each select thread).
+    say("lenient lambda=1 zero residual", dtype, V)
+    B, K = 4, 5
+    x = workloads.chain_inputs(87, B, K, V, dtype, sigma=1.0)
+    for b, i in ((0, 0), (1, 2), (2, 4)):
+        x["drf"][b, i, int(x["draft_tokens"][b, i])] = float("-inf")
+    res = dbv.verify_lenient(x["tgt"].to(dev), x["drf"].to(dev), x["draft_tokens"].to(dev),
+                             x["u_accept"].to(dev), x["u_resample"].to(dev), 1.0,
+                             draft_len=x["draft_len"].to(dev))
+    xn = _np_inputs(x)
+    o = oracle.verify_lenient(xn["tgt"], xn["drf"], xn["draft_tokens"], xn["draft_len"], 1.0, 1.0, 1.0,
+                              xn["u_accept"], xn["u_resample"])
+    assert list(o["accept_len"]) == [0, 2, 4, K]
+    assert all(o["status"][:3] & oracle.STATUS_Z_ZERO) and o["status"][3] == 0
+    check_sampling(res, xn, o, 1.0, 1.0, 1.0, str(dtype).split(".")[1])
+    np.testing.assert_array_equal(npi(res["status"]), o["status"])
+    assert (np64(res["residual_mass"]) == 0).all()
+
+
+def test_max_draft_length_long_rows(dev):
+    # K = 1024 with rows long enough for the mass / select draw (20 tiles of
+    # 256 fp32): the select group assembles up to 1025 output positions, and
+    # an EOS first drafted at position 300 or later stops sequence 0 there.
+    say("max draft length, long rows")
+    B, K, V = 2, 1024, 5000
+    x = workloads.chain_inputs(88, B, K, V, torch.float32, sigma=1.0)
+    x["drf"][0] = x["tgt"][0, :K]
+    x["draft_tokens"][0] = torch.multinomial(torch.softmax(x["drf"][0], -1), 1,
+                                             generator=torch.Generator().manual_seed(6))[:, 0].to(torch.int32)
+    d0 = x["draft_tokens"][0].tolist()
+    eos = next(t for t in d0[300:] if t not in d0[:300])
+    xd = _to(x, dev)
+    res = dbv.verify_rejection(xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"],
+                               draft_len=xd["draft_len"], eos_id=eos)
+    xn = _np_inputs(x)
+    o = oracle.verify_rejection(xn["tgt"], xn["drf"], xn["draft_tokens"], xn["draft_len"], 1.0, 1.0,
+                                xn["u_accept"], xn["u_resample"], eos_id=eos)
+    assert o["accept_len"][0] == K and 300 < o["num_out"][0] < K
+    check_sampling(res, xn, o, 0.0, 1.0, 1.0, "float32", eos_id=eos)
+
+
 def test_lenient_zero_is_rejection_bit_for_bit(dev):
     say("lenient 0 == rejection")
     x = _to(workloads.chain_inputs(78, 8, 9, 30011, torch.bfloat16, sigma=1.0, random_lengths=True), dev)
