@@ -868,12 +868,34 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
 
 constexpr int kDrawWaves = kDrawThreads / 64;
 
-struct SelectLds {
-  float tile[kMaxDrawTiles];
-  float w[kDrawWaves];
+// LDS of the select step for NT threads holding TPT tile masses each (the
+// tile array serves the zero-mass fallback, which recomputes every tile).
+template <int NT, int TPT>
+struct SelectLdsT {
+  static constexpr int kThreads = NT;
+  static constexpr int kTiles = TPT;
+  float tile[NT * TPT];
+  float w[NT / 64];
   float Z, base;
   int ct, lt, cs, pick, a;
 };
+using SelectLds = SelectLdsT<kDrawThreads, kDrawTilesPerThread>;
+// Rows of at most kSmallSelect * kSmallSelectTiles tiles are selected by
+// kSmallSelect threads: four waves scan and synchronise faster than sixteen.
+constexpr int kSmallSelect = kBlock;
+constexpr int kSmallSelectTiles = 4;
+using SmallSelectLds = SelectLdsT<kSmallSelect, kSmallSelectTiles>;
+
+// Draft tokens d_{t + k NT + 1} of this thread (-1 past K).
+template <int NT>
+__device__ __forceinline__ void load_draft_tokens(const SampleArgs& a, int b, int (&dt)[(kMaxDraft + NT - 1) / NT]) {
+  constexpr int DPT = (kMaxDraft + NT - 1) / NT;
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) {
+    const int i = static_cast<int>(threadIdx.x) + k * NT;
+    dt[k] = i < a.K ? a.draft_tokens[static_cast<int64_t>(b) * a.K + i] : -1;
+  }
+}
 
 // The stored sparse Q of row h, as the mass kernel handed it over.
 struct SparseLds {
@@ -883,25 +905,29 @@ struct SparseLds {
 };
 
 
-// The draw of sequence b by kDrawThreads threads, given its record and this
-// thread's tile masses m0 (tiles [t*q, (t+1)*q), q = ceil(tiles / threads)):
+// The draw of sequence b by the NT = LDS::kThreads threads of the group,
+// given its record and this thread's TPT = LDS::kTiles tile masses m0 (tiles
+// [t*q, (t+1)*q), q = ceil(tiles / NT) <= TPT):
 // the tile where the running mass first exceeds u*Z (the last positive tile
 // if rounding leaves u*Z at or past the total), the token inside it in
 // vocabulary order, and the output assembly C = (d_1..d_h, c) with the
 // ending condition.
-// dt is this thread's draft token d_{t+1} (t < K), requested with the first
-// loads; every output position i < h <= K <= kDrawThreads is some thread's t.
+// dt[k] is draft token d_{t + k NT + 1}, requested with the first loads;
+// output position i = t + k NT, and k = DPT reaches i <= K only where i >= h.
 // SPARSE: the call verifies against a stored sparse Q, whose LDS is sp.
-template <int DT, bool SPARSE>
-__device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, int budget, int dt,
-                            const float (&m0)[kDrawTilesPerThread], SelectLds& s, SparseLds* sp) {
-  static_assert(kMaxDraft <= kDrawThreads, "one draft token per thread");
+template <int DT, bool SPARSE, class LDS>
+__device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, int budget,
+                            const int (&dt)[(kMaxDraft + LDS::kThreads - 1) / LDS::kThreads],
+                            const float (&m0)[LDS::kTiles], LDS& s, SparseLds* sp) {
+  constexpr int NT = LDS::kThreads;
+  constexpr int TPT = LDS::kTiles;
+  constexpr int DPT = (kMaxDraft + NT - 1) / NT;
   using E = Elem<DT>;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wv = t >> 6;
   const int ntiles = a.tiles;
-  const int q = static_cast<int>(cdiv(ntiles, kDrawThreads));   // tiles per thread, <= kDrawTilesPerThread
+  const int q = static_cast<int>(cdiv(ntiles, NT));   // tiles per thread, <= TPT
   const int h = __builtin_amdgcn_readfirstlane(rec.h);
   int status = rec.status;
   const bool resid0 = rec.resid != 0;
@@ -910,24 +936,24 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
   DrawWeight w = draw_weight(a, rec);
   constexpr int TE = 64 * E::kVec;                              // elements per tile
   const bool draw = rec.fixed < 0;   // uniform across the group
-  float mt[kDrawTilesPerThread];
+  float mt[TPT];
 #pragma unroll
-  for (int k = 0; k < kDrawTilesPerThread; ++k) mt[k] = m0[k];
+  for (int k = 0; k < TPT; ++k) mt[k] = m0[k];
 
   // Thread t holds the masses of tiles [t*q, (t+1)*q); an exclusive scan
   // gives it the mass before them, and the group's total Z.
-  auto locate = [&](const float (&m)[kDrawTilesPerThread]) {
+  auto locate = [&](const float (&m)[TPT]) {
     if (t == 0) { s.ct = INT_MAX; s.lt = -1; }
     float loc = 0.f;
 #pragma unroll
-    for (int k = 0; k < kDrawTilesPerThread; ++k) loc += m[k];
+    for (int k = 0; k < TPT; ++k) loc += m[k];
     float Z;
-    const float start = group_exclusive_scan_f<kDrawWaves>(loc, Z, s.w);
+    const float start = group_exclusive_scan_f<NT / 64>(loc, Z, s.w);
     const float target = rec.u * Z;
     int hit = INT_MAX, last = -1;
     float run = start;
 #pragma unroll
-    for (int k = 0; k < kDrawTilesPerThread; ++k) {
+    for (int k = 0; k < TPT; ++k) {
       if (m[k] > 0.f) {
         if (hit == INT_MAX && run + m[k] > target) hit = t * q + k;
         last = t * q + k;
@@ -941,7 +967,7 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
     if (t == ct / q) {   // the owner of the chosen tile writes the mass before it
       float before = start;
 #pragma unroll
-      for (int k = 0; k < kDrawTilesPerThread; ++k)
+      for (int k = 0; k < TPT; ++k)
         if (t * q + k < ct) before += m[k];
       s.base = before;
       s.Z = Z;
@@ -961,11 +987,11 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
     w.excl = -1;
     yr = xr;
     const bool vec = (reinterpret_cast<uintptr_t>(xr) & 15u) == 0;
-    tile_masses<DT, kDrawWaves, 2>(xr, yr, a.V, 0, ntiles, vec, w, s.tile);
+    tile_masses<DT, NT / 64, 2>(xr, yr, a.V, 0, ntiles, vec, w, s.tile);
     __syncthreads();
-    float m1[kDrawTilesPerThread];
+    float m1[TPT];
 #pragma unroll
-    for (int k = 0; k < kDrawTilesPerThread; ++k) {
+    for (int k = 0; k < TPT; ++k) {
       const int tile = t * q + k;
       m1[k] = (k < q && tile < ntiles) ? s.tile[tile] : 0.f;
     }
@@ -1032,15 +1058,21 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
   __syncthreads();
   const int tok = s.pick;
   if (a.eos >= 0) {
-    for (int i = t; i < A; i += kDrawThreads) {   // A can be K + 1 = kDrawThreads + 1
-      const int ci = i < h ? dt : tok;
-      if (ci == a.eos) atomicMin(&s.a, i + 1);
+#pragma unroll
+    for (int k = 0; k <= DPT; ++k) {
+      const int i = t + k * NT;
+      const int ci = i < h ? dt[k < DPT ? k : DPT - 1] : tok;
+      if (i < A && ci == a.eos) atomicMin(&s.a, i + 1);
     }
   }
   __syncthreads();
   const int an = s.a;
   int32_t* out = a.out_tokens + static_cast<int64_t>(b) * (a.K + 1);
-  for (int i = t; i <= a.K; i += kDrawThreads) out[i] = i < an ? (i < h ? dt : tok) : -1;
+#pragma unroll
+  for (int k = 0; k <= DPT; ++k) {
+    const int i = t + k * NT;
+    if (i <= a.K) out[i] = i < an ? (i < h ? dt[k < DPT ? k : DPT - 1] : tok) : -1;
+  }
   if (t == 0) {
     a.accept_len[b] = h;
     a.num_out[b] = an;
@@ -1050,24 +1082,27 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
   }
 }
 
-// Second kernel of the split draw: one group per sequence reads the record
-// and the tile masses that k_draw_mass wrote.
-template <int DT, int FAM>
-__global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
-  __shared__ SelectLds s;
+// Second kernel of the split draw: one group of LDS::kThreads threads per
+// sequence reads the record and the tile masses that k_draw_mass wrote.
+template <int DT, int FAM, class LDS>
+__global__ __launch_bounds__(LDS::kThreads) void k_draw_select(SampleArgs a) {
+  constexpr int NT = LDS::kThreads;
+  constexpr int TPT = LDS::kTiles;
+  __shared__ LDS s;
   const int b = blockIdx.x;
   const int t = threadIdx.x;
   const int ntiles = a.tiles;
-  const int q = static_cast<int>(cdiv(ntiles, kDrawThreads));
+  const int q = static_cast<int>(cdiv(ntiles, NT));
   // Everything this group reads first is requested together: the decision
-  // record, the budget and this thread's tile masses.
+  // record, the budget, the draft tokens and this thread's tile masses.
   const DrawRecord rec = a.rec[b];
   const int budget = a.budget ? a.budget[b] : INT_MAX;
-  const int dt = t < a.K ? a.draft_tokens[static_cast<int64_t>(b) * a.K + t] : -1;
+  int dt[(kMaxDraft + NT - 1) / NT];
+  load_draft_tokens<NT>(a, b, dt);
   const float* tmass = a.tmass + static_cast<int64_t>(b) * ntiles;
-  float m0[kDrawTilesPerThread];
+  float m0[TPT];
 #pragma unroll
-  for (int k = 0; k < kDrawTilesPerThread; ++k) {
+  for (int k = 0; k < TPT; ++k) {
     const int tile = t * q + k;
     m0[k] = (k < q && tile < ntiles) ? tmass[tile] : 0.f;
   }
@@ -1076,7 +1111,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_select(SampleArgs a) {
     // are never used).
     __shared__ SparseLds sp;
     const SparseRow* sr = a.sq + b;
-    for (int e = t; e < kMaxNnz; e += kDrawThreads) {
+    for (int e = t; e < kMaxNnz; e += NT) {
       sp.idx[e] = sr->idx[e];
       sp.prob[e] = sr->prob[e];
     }
@@ -1103,7 +1138,8 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_fused(SampleArgs a) {
   const DrawRecord rec = draw_decide<DT, kDrawThreads, FAM>(a, b, true, sd);
   if (rec.status & SEQ_ERROR_MASK) return;
   const int budget = a.budget ? a.budget[b] : INT_MAX;
-  const int dt = t < a.K ? a.draft_tokens[static_cast<int64_t>(b) * a.K + t] : -1;
+  int dt[(kMaxDraft + kDrawThreads - 1) / kDrawThreads];
+  load_draft_tokens<kDrawThreads>(a, b, dt);
   const char *xr, *yr;
   draw_rows<DT>(a, b, rec.h, rec.resid != 0, xr, yr);
   const bool vec = ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0;
@@ -1146,14 +1182,20 @@ bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const Tim
   static const void* const mass[3][2] = {{fn(k_draw_mass<DT_F32, FAM_TOKEN>), fn(k_draw_mass<DT_BF16, FAM_TOKEN>)},
                                          {fn(k_draw_mass<DT_F32, FAM_SPOT>), fn(k_draw_mass<DT_BF16, FAM_SPOT>)},
                                          {fn(k_draw_mass<DT_F32, FAM_SPARSE>), fn(k_draw_mass<DT_BF16, FAM_SPARSE>)}};
-  static const void* const select[3][2] = {
-      {fn(k_draw_select<DT_F32, FAM_TOKEN>), fn(k_draw_select<DT_BF16, FAM_TOKEN>)},
-      {fn(k_draw_select<DT_F32, FAM_SPOT>), fn(k_draw_select<DT_BF16, FAM_SPOT>)},
-      {fn(k_draw_select<DT_F32, FAM_SPARSE>), fn(k_draw_select<DT_BF16, FAM_SPARSE>)}};
+  // [small][family][dtype == bf16]
+  static const void* const select[2][3][2] = {
+      {{fn(k_draw_select<DT_F32, FAM_TOKEN, SelectLds>), fn(k_draw_select<DT_BF16, FAM_TOKEN, SelectLds>)},
+       {fn(k_draw_select<DT_F32, FAM_SPOT, SelectLds>), fn(k_draw_select<DT_BF16, FAM_SPOT, SelectLds>)},
+       {fn(k_draw_select<DT_F32, FAM_SPARSE, SelectLds>), fn(k_draw_select<DT_BF16, FAM_SPARSE, SelectLds>)}},
+      {{fn(k_draw_select<DT_F32, FAM_TOKEN, SmallSelectLds>), fn(k_draw_select<DT_BF16, FAM_TOKEN, SmallSelectLds>)},
+       {fn(k_draw_select<DT_F32, FAM_SPOT, SmallSelectLds>), fn(k_draw_select<DT_BF16, FAM_SPOT, SmallSelectLds>)},
+       {fn(k_draw_select<DT_F32, FAM_SPARSE, SmallSelectLds>),
+        fn(k_draw_select<DT_BF16, FAM_SPARSE, SmallSelectLds>)}}};
   if (a.tiles <= kFusedDrawTiles && fam != FAM_SPARSE)
     return launch_threads(fused[fam][bf], a.B, kDrawThreads, stream, a);
+  const bool small = a.tiles <= kSmallSelect * kSmallSelectTiles;
   return launch(mass[fam][bf], static_cast<int64_t>(a.B) * a.chunks, stream, a) &&
-         launch_threads(select[fam][bf], a.B, kDrawThreads, stream, a);
+         launch_threads(select[small][fam][bf], a.B, small ? kSmallSelect : kDrawThreads, stream, a);
 }
 
 }  // namespace dbv
