@@ -578,7 +578,7 @@ def run_loop(args, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it",
+        print(json.dumps({"error": "bench.py measures one GPU; runs on several GPUs are not supported",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if not torch.cuda.is_available():

@@ -73,7 +73,7 @@ extern "C" {
 typedef enum {
   DBV_OK = 0,
   DBV_ERR_INVALID_ARG = 1, /* a host argument is out of range / NULL      */
-  DBV_ERR_UNSUPPORTED = 2, /* a valid request this build does not serve   */
+  DBV_ERR_UNSUPPORTED = 2, /* a valid request beyond the library limits  */
   DBV_ERR_NO_DEVICE = 3,   /* no usable gfx950 device                     */
   DBV_ERR_LAUNCH = 4,      /* a kernel launch failed (hipGetLastError)    */
   DBV_ERR_WORKSPACE = 5    /* ws is NULL / too small / misaligned         */
