@@ -118,11 +118,12 @@ inline size_t partial_bytes(int64_t max_rows) {
 // The correction / bonus draw.  Its row is cut into tiles of 64 16-byte
 // vectors (one coalesced wave load per row: 512 bf16 or 256 fp32 elements).
 // The mass kernel gives each sequence draw_chunks groups of whole tiles and
-// stores every tile's mass; the select kernel (kDrawThreads threads per
-// sequence) scans the tile masses for the tile where the running mass
-// crosses u*Z, and one wave rescans that tile in vocabulary order.
-// kMaxDrawTiles bounds the tiles per row (at most kDrawTilesPerThread per
-// select thread), and so the vocabulary of the sampling entry points.
+// stores every tile's mass; the select kernel (one group per sequence: 256
+// threads for rows of at most 1024 tiles, else kDrawThreads) scans the tile
+// masses for the tile where the running mass crosses u*Z, and one wave
+// rescans that tile in vocabulary order.  kMaxDrawTiles bounds the tiles per
+// row (at most kDrawTilesPerThread per thread of a kDrawThreads group), and
+// so the vocabulary of the sampling entry points.
 // Rows of at most kFusedDrawTiles tiles skip the split: one group per
 // sequence makes the decision, computes every tile mass into LDS and draws,
 // which saves a kernel boundary and the round trip of the masses.

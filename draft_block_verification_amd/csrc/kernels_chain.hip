@@ -14,7 +14,7 @@
 //                      decision (p(d), q(d), the acceptance tests, h) and the
 //                      masses of [p - q]_+ (or of p for the bonus) over the
 //                      chunk's tiles of row h
-//   k_draw_select      per sequence (1024 threads): the tile, then the token,
+//   k_draw_select      per sequence (256 or 1024 threads): the tile, then the token,
 //                      where the running mass first exceeds u*Z (vocabulary
 //                      order), and output assembly.
 // The kernel boundaries are the only cross-group synchronisation.
