@@ -79,3 +79,54 @@ def test_random_chain_cases(dev, seed):
                                   **kw)
             o = oracle.verify_cactus(*args, delta, *uni, eos_id=eos, len_budget=bn)
             check_sampling(g, xn, o, 0.0, T, T, name, eos_id=eos, len_budget=bn, delta=delta)
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_random_tree_spot_any_order_cases(dev, seed):
+    # Same idea for the Gumbel tree (T = 0 and T > 0), the
+    # joint-space chain (with and without coupled-noise rows, three gates)
+    # and any-order greedy verification (with and without drafter rows and
+    # positions).
+    import tests.test_parity_gpu as fixed
+    from tests.parity import check_any_order, check_spot, check_tree
+    rng = np.random.default_rng(seed)
+    for n in range(CASES // 2):
+        kind = str(rng.choice(["tree", "spot", "any-order"]))
+        dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+        name = str(dtype).split(".")[1]
+        c = int(rng.integers(100, 5000))
+        if kind == "tree":
+            B, S = int(rng.integers(1, 6)), int(rng.choice([2, 5, 12, 33, 64]))
+            L, V = int(rng.choice([2, 4, 6, 9, 16])), int(rng.choice([7, 513, 5003, 20011]))
+            T = float(rng.choice([0.0, 0.7, 1.0]))
+            sig = float(rng.choice([0.05, 0.5]))
+            print("[case]", seed, n, kind, B, S, L, V, dtype, T, flush=True)
+            x = workloads.tree_inputs(c, B, S, L, V, dtype, sigma_node=sig, temperature=T if T > 0 else 1.0)
+            g = dbv.verify_gumbel_tree(x["logits"].to(dev), x["parent"].to(dev), x["edge_pos"].to(dev),
+                                       x["edge_tok"].to(dev), masked=x["masked"].to(dev),
+                                       gumbel=x["gumbel"].to(dev) if T > 0 else None, temperature=T,
+                                       num_states=x["num_states"].to(dev))
+            xn = fixed._np_inputs(x)
+            xn["masked"] = x["masked"].numpy()
+            o = oracle.verify_gumbel_tree(xn["logits"], xn["masked"], xn["parent"], xn["edge_pos"],
+                                          xn["edge_tok"], xn["num_states"], xn["gumbel"], T)
+            check_tree(g, xn, o, name, T)
+        elif kind == "spot":
+            B, K, V = int(rng.integers(1, 24)), int(rng.choice([1, 2, 5, 8, 16])), int(rng.choice([513, 5003, 40000]))
+            gum = bool(rng.random() < 0.6)
+            tau = float(rng.choice([0.3, 0.6, 0.9]))
+            T = float(rng.choice([0.7, 1.0]))
+            ragged = bool(rng.random() < 0.7)
+            print("[case]", seed, n, kind, B, K, V, dtype, gum, tau, flush=True)
+            x = workloads.spot_chain_inputs(c, B, K, V, dtype, temperature=T, random_lengths=ragged, gumbel=gum)
+            g, xn, o = fixed._spot_run(dev, x, tau=tau, gumbel=gum)
+            check_spot(g, xn, o, T, T, tau, name)
+        else:
+            B, U, V = int(rng.integers(1, 40)), int(rng.choice([1, 2, 5, 16, 32])), int(rng.choice([7, 513, 5003]))
+            agree = float(rng.choice([0.3, 0.8, 0.97]))
+            missing = float(rng.choice([0.0, 0.15, 0.5]))
+            rows, pos = bool(rng.random() < 0.7), bool(rng.random() < 0.7)
+            print("[case]", seed, n, kind, B, U, V, dtype, rows, pos, flush=True)
+            x = workloads.anyorder_inputs(c, B, U, V, dtype, agree=agree, missing=missing)
+            g, o = fixed._ao_run(dev, x, draft_rows=rows, positions=pos)
+            check_any_order(g, o)
