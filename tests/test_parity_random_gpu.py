@@ -130,3 +130,48 @@ def test_random_tree_spot_any_order_cases(dev, seed):
             x = workloads.anyorder_inputs(c, B, U, V, dtype, agree=agree, missing=missing)
             g, o = fixed._ao_run(dev, x, draft_rows=rows, positions=pos)
             check_any_order(g, o)
+
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_random_truncate_sparse_ddtree_cases(dev, seed):
+    # Top-k / top-p truncation (tied rows included), verification against
+    # stored sparse Q, and DDTree hypotheses plus the level-batched build.
+    import tests.test_parity_ddtree_gpu as dd
+    import tests.test_parity_gpu as fixed
+    from tests.parity import np64, npi
+    rng = np.random.default_rng(seed)
+    for n in range(CASES // 2):
+        kind = str(rng.choice(["truncate", "sparse", "ddtree"]))
+        dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+        name = str(dtype).split(".")[1]
+        c = int(rng.integers(100, 5000))
+        if kind == "truncate":
+            B, K, V = int(rng.integers(1, 8)), int(rng.integers(1, 6)), int(rng.choice([1, 5, 300, 4097, 20011]))
+            k, p = int(rng.choice([1, 2, 5, 20, 64, 256])), float(rng.choice([1.0, 0.9, 0.5, 0.05]))
+            T, scale = float(rng.choice([0.5, 0.8, 1.0, 2.0])), float(rng.choice([0.3, 3.0, 10.0]))
+            kmax = int(rng.choice([k, 256]))
+            ties = bool(rng.random() < 0.3)
+            print("[case]", seed, n, kind, B, K, V, dtype, k, p, T, kmax, ties, flush=True)
+            rows = torch.randn(B, K, V, generator=torch.Generator().manual_seed(c)) * scale
+            rows = (torch.round(rows) if ties else rows).to(dtype)
+            lengths = torch.randint(0, K + 1, (B,), dtype=torch.int32, generator=torch.Generator().manual_seed(c))
+            g = dbv.truncate_top_k_top_p(rows.to(dev), k, p, kmax=kmax, lengths=lengths.to(dev), temperature=T)
+            fixed._trunc_check(g, np64(rows), T, k, p, kmax, npi(lengths), name)
+        elif kind == "sparse":
+            B, K, V = int(rng.integers(1, 16)), int(rng.choice([1, 3, 8])), int(rng.choice([300, 5003, 40000]))
+            topk, peak = int(rng.choice([1, 5, 20, 64])), float(rng.choice([2.0, 6.0]))
+            print("[case]", seed, n, kind, B, K, V, dtype, topk, peak, flush=True)
+            x = workloads.sparse_inputs(c, B, K, V, dtype, topk=topk, peak=peak, random_lengths=True)
+            g, xn, o, qfun = fixed._sparse_run(dev, x)
+            check_sampling(g, xn, o, 0.0, x["temperature"], x["temperature"], name, qfun=qfun)
+        else:
+            B, L, V = int(rng.integers(1, 12)), int(rng.choice([1, 2, 5, 16, 32, 64])), int(rng.choice([7, 513, 2053]))
+            T, D = float(rng.choice([0.0, 0.6, 1.0])), int(rng.choice([0, 1, 3, 8, 20, 64]))
+            tau, gamma = float(rng.choice([0.7, 1.0, 1.3])), float(rng.choice([0.0, 0.0, 0.01, 0.05]))
+            rub, mm = float(rng.choice([0.6, 0.3, 0.9])), float(rng.choice([0.0, 0.5, 1.0]))
+            print("[case]", seed, n, kind, B, L, V, dtype, T, D, tau, gamma, rub, mm, flush=True)
+            x = workloads.ddtree_inputs(c, B, L, V, dtype, temperature=T, masked_min=mm)
+            h, st = dd._run_build(x, dev, D, tau, gamma, runner_up_below=rub)
+            order = oracle.table_order(np64(x["order_table"]))
+            o = dd._oracle(x, order, D, tau, gamma, runner_up_below=rub)
+            dd._check_all(h, st, o, x, order, D, tau, gamma, name)
