@@ -176,7 +176,10 @@ dbv_status verify_rejection(int B, int K, int V, dbv_dtype dtype,
  * position draws from normalize([p~ - q]_+) (equal to normalize([p - q]_+)
  * for lambda < 1); the bonus after full acceptance is drawn from p, not p~.
  * lambda in [0, 1]: 0 reproduces verify_rejection bit for bit, 1 accepts
- * every draft.  All other arguments as verify_rejection.
+ * every draft with q(d) > 0; a draft with q(d) = 0 is still rejected, and
+ * since [p~ - q]_+ is then zero everywhere its position draws from p with
+ * the Z = 0 status bit, like any residual of zero mass.  All other
+ * arguments as verify_rejection.
  */
 dbv_status verify_lenient(int B, int K, int V, dbv_dtype dtype,
                           const void* tgt, int64_t tgt_seq_stride, int64_t tgt_row_stride,
