@@ -8,9 +8,10 @@ in HBM: every row statistic / argmax, the acceptance tests, the prefix scan,
 and the correction or bonus draw.  Workloads (sizes of the pages' setups):
 
   c1  tiny rejection verify       B=1  K=4  V=1024   fp32
-  c2  batch lossless verify       B=8  K=8  V=32000  bf16   (default)
+  c2  batch lossless verify       B=8  K=8  V=32000  bf16
   c3  lenient verify              B=32 K=16 V=128256 bf16, sigma=1, T=1, lambda=0.5
-  c4  coupled-Gumbel tree verify  B=16 S=64 L=32 V=151936 bf16
+  c4  coupled-Gumbel tree verify  B=16 S=64 L=32 V=151936 bf16   (default: the
+                                  largest workload that fits one GPU)
   c5  packed greedy verify+draft  B=64 K=32 V=131072 bf16
   c3c modified-Cactus verify      B=32 K=16 V=128256 bf16, sigma=1, T=1, delta=1
   c5ao any-order greedy verify    B=64 U=32 V=131072 bf16 (verifier rows by rank,
@@ -81,7 +82,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="c2", choices=sorted(DESCR))
+    ap.add_argument("--workload", default="c4", choices=sorted(DESCR))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -143,6 +144,13 @@ class _Steps:
             c()
         return self.outputs
 
+    def timed(self, begin, end):
+        """The first call's row-streaming kernel between the events."""
+        self.calls[0].timed(begin, end)
+        for c in self.calls[1:]:
+            c()
+        return self.outputs
+
 
 class Case:
     """One workload: prepared calls over R rotated input sets, plus what the
@@ -168,6 +176,7 @@ class Case:
             n = x["draft_len"].long()
             self.positions = int(n.sum())
             self.kernel_bytes = int(((2 * n + 1) * V * eb).sum())      # target n+1 rows, draft n rows
+            self.rows = int((2 * n + 1).sum())
             self.kernel = "k_sample_rows"
             per_set = (x["tgt"].numel() + x["drf"].numel()) * eb
             self.cpu_inputs = x
@@ -193,6 +202,7 @@ class Case:
             n = x["draft_len"].long()
             self.positions = int(n.sum())
             self.kernel_bytes = int(((n + 1 + W) * V * eb).sum())
+            self.rows = int((n + 1 + W).sum())
             self.kernel = "k_greedy_rows"
             per_set = x["packed"].numel() * eb
             self.cpu_inputs = x
@@ -209,6 +219,7 @@ class Case:
             n = x["draft_len"].long()
             self.positions = int(n.sum())
             self.kernel_bytes = int(((n + 1) * V * eb).sum())     # target rows only; Q is a few KB
+            self.rows = int((n + 1).sum())
             self.kernel = "k_sample_rows"
             per_set = x["tgt"].numel() * eb
             self.cpu_inputs = x
@@ -225,6 +236,7 @@ class Case:
             n = x["draft_len"].long()
             self.positions = int(n.sum())
             self.kernel_bytes = int((n * V * eb).sum())                 # drafter rows 0..n-1, read once
+            self.rows = int(n.sum())
             self.kernel = "k_truncate"
             per_set = x["drf"].numel() * eb
             self.cpu_inputs = x
@@ -240,6 +252,7 @@ class Case:
             nm = int(x["masked"].sum())
             self.positions = B * DD_BUDGET
             self.kernel_bytes = nm * V * (eb + 4)                      # masked stale rows + Gumbel rows
+            self.rows = nm
             self.kernel = "k_dd_rows"
             per_set = x["stale"].numel() * eb + x["gumbel"].numel() * 4
             self.cpu_inputs = x
@@ -260,6 +273,7 @@ class Case:
             self.positions = int(n.sum())
             # target rows 0..n with their float32 Gumbel rows, drafter rows 0..n-1
             self.kernel_bytes = int(((n + 1) * V * (eb + 4) + n * V * eb).sum())
+            self.rows = int((2 * n + 1).sum())
             self.kernel = "k_sample_rows"
             per_set = (x["tgt"].numel() + x["drf"].numel()) * eb + x["gumbel"].numel() * 4
             self.cpu_inputs = x
@@ -279,6 +293,7 @@ class Case:
             nver = torch.minimum(kappa + 1, u)
             self.positions = int(kappa.sum())                            # drafted positions checked
             self.kernel_bytes = int(((nver + u) * V * eb).sum())         # verifier rows read + drafter rows
+            self.rows = int((nver + u).sum())
             self.kernel = "k_ao_rows"
             per_set = (x["tgt"].numel() + x["draft_rows"].numel()) * eb
             self.cpu_inputs = x
@@ -298,6 +313,7 @@ class Case:
             for b in range(B):
                 m[b, int(ns[b]):] = False
             self.kernel_bytes = int(m.sum()) * V * eb
+            self.rows = int(m.sum())                                   # masked rows of valid states
             self.kernel = "k_tree_conf"
             self.cpu_inputs = x
             self.calls = [dbv.verify_gumbel_tree(
@@ -323,133 +339,169 @@ class Case:
         return int(max(1, min(256, math.ceil(ROTATE_BYTES / max(per_set, 1)))))
 
     # ------------------------------------------------------------ oracle --
-    def cpu_baseline(self, seconds):
-        """The oracle as it stands on a bounded sample of this workload."""
+    def cpu_items(self):
+        """The oracle's units of work on a bounded sample of this workload:
+        (function, items, positions per item).  Items are whole oracle calls
+        over one sequence (chains), one block (DDTree) or one tree state
+        (the tree: state transitions, the per-state unit the walk then
+        combines; a tree's drafted positions are counted per state)."""
         import oracle
         from tests.parity import np64, npi
         x = self.cpu_inputs
-        done_pos = 0
-        calls = 0
-        t0 = time.perf_counter()
-        if self.name in ("c1", "c2", "c3", "c3c"):
+        name = self.name
+        if name in ("c1", "c2", "c3", "c3c"):
             B = x["tgt"].shape[0]
-            nb = min(B, 4) if self.name in ("c3", "c3c") else B
-            tgt, drf = np64(x["tgt"][:nb]), np64(x["drf"][:nb])
-            d, n = npi(x["draft_tokens"][:nb]), npi(x["draft_len"][:nb])
-            ua, ur = np64(x["u_accept"][:nb]), np64(x["u_resample"][:nb])
             T = x["temperature"]
-            t0 = time.perf_counter()
-            while True:
-                if self.name == "c3c":
-                    oracle.verify_cactus(tgt, drf, d, n, T, T, CACTUS_DELTA, ua, ur)
+            tgt, drf = np64(x["tgt"]), np64(x["drf"])
+            d, n = npi(x["draft_tokens"]), npi(x["draft_len"])
+            ua, ur = np64(x["u_accept"]), np64(x["u_resample"])
+            lam = self.lam
+
+            def fn(b):
+                sl = slice(b, b + 1)
+                if name == "c3c":
+                    oracle.verify_cactus(tgt[sl], drf[sl], d[sl], n[sl], T, T, CACTUS_DELTA, ua[sl], ur[sl])
                 else:
-                    oracle.verify_lenient(tgt, drf, d, n, T, T, self.lam, ua, ur)
-                done_pos += int(n.sum())
-                calls += 1
+                    oracle.verify_lenient(tgt[sl], drf[sl], d[sl], n[sl], T, T, lam, ua[sl], ur[sl])
+            return fn, list(range(B)), [int(v) for v in n]
+        if name == "c5":
+            K = x["K"]
+            p = x["packed"]
+            d, n = npi(x["draft_tokens"]), npi(x["draft_len"])
+            nb = 16
+
+            def fn(b):
+                oracle.verify_greedy(np64(p[b:b + 1, :K + 1]), d[b:b + 1], n[b:b + 1], np64(p[b:b + 1, K + 1:]))
+            return fn, list(range(nb)), [int(v) for v in n[:nb]]
+        if name == "c3t":
+            n = npi(x["draft_len"])
+            nb = 16
+
+            def fn(b):
+                oracle.truncate_rows(np64(x["drf"][b:b + 1]), 1.0, x["top_k"], x["top_p"], x["top_k"], n[b:b + 1])
+            return fn, list(range(nb)), [int(v) for v in n[:nb]]
+        if name == "c4d":
+            nb = 16
+            tab = np64(x["order_table"])
+
+            def fn(b):
+                oracle.build_ddtree(np64(x["stale"][b:b + 1]), npi(x["masked"][b:b + 1]),
+                                    oracle.table_order(tab[b:b + 1]), DD_BUDGET, 1.0, gumbel=np64(x["gumbel"][b:b + 1]))
+            return fn, list(range(nb)), [DD_BUDGET] * nb
+        if name == "c3q":
+            B = x["tgt"].shape[0]
+            a = dict(tgt=np64(x["tgt"]), qi=npi(x["q_idx"]), qp=np64(x["q_prob"]), qn=npi(x["q_nnz"]),
+                     d=npi(x["draft_tokens"]), n=npi(x["draft_len"]), ua=np64(x["u_accept"]),
+                     ur=np64(x["u_resample"]))
+
+            def fn(b):
+                sl = slice(b, b + 1)
+                oracle.verify_sparse(a["tgt"][sl], a["qi"][sl], a["qp"][sl], a["qn"][sl], a["d"][sl], a["n"][sl],
+                                     1.0, a["ua"][sl], a["ur"][sl])
+            return fn, list(range(B)), [int(v) for v in a["n"]]
+        if name == "c4s":
+            B = x["tgt"].shape[0]
+            a = {k: (np64(v) if v.is_floating_point() else npi(v)) if torch.is_tensor(v) else v
+                 for k, v in x.items()}
+
+            def fn(b):
+                sl = slice(b, b + 1)
+                oracle.verify_spot_chain(a["tgt"][sl], a["drf"][sl], a["pos_star"][sl], a["prop_pos"][sl],
+                                         a["prop_tok"][sl], a["q_pos_star"][sl], a["draft_len"][sl], 1.0, 1.0,
+                                         a["u_accept"][sl], a["u_resample"][sl], gumbel=a["gumbel"][sl],
+                                         tau=SPOT_TAU)
+            return fn, list(range(B)), [int(v) for v in a["draft_len"]]
+        if name == "c5ao":
+            kap = self._kappa(x)
+            nb = 16
+
+            def fn(b):
+                sl = slice(b, b + 1)
+                oracle.verify_greedy_any_order(np64(x["tgt"][sl]), npi(x["order"][sl]), npi(x["num_active"][sl]),
+                                               npi(x["positions"][sl]), npi(x["draft_tokens"][sl]),
+                                               np64(x["draft_rows"][sl]))
+            return fn, list(range(nb)), [int(v) for v in kap[:nb]]
+        # c4: the first trees' states (a bounded sample); logits upcast to
+        # float32 (exact for bf16) on the host once.
+        nt = 2
+        logits = x["logits"][:nt].float().cpu().numpy()
+        gum = x["gumbel"][:nt].cpu().numpy()
+        masked = x["masked"][:nt].cpu().numpy()
+        ns = npi(x["num_states"][:nt])
+        items = [(b, z) for b in range(nt) for z in range(int(ns[b]))]
+
+        def fn(item):
+            b, z = item
+            mpos = [s for s in range(masked.shape[2]) if masked[b, z, s]]
+            oracle.state_transition(logits[b, z], mpos, gum[b], 1.0)
+        # each non-root state is one drafted position of its tree
+        return fn, items, [1 if z > 0 else 0 for (_, z) in items]
+
+    def cpu_baseline(self, seconds):
+        """The oracle as it stands, on a bounded sample of this workload: on
+        one core, then on every core of the host's share (a process pool over
+        the same items).  Positions per second of oracle time."""
+        fn, items, pos = self.cpu_items()
+        one = _time_items(fn, items, pos, seconds / 2, 1)
+        # The host's share is 16 CPUs: 15 workers beside this process.
+        cores = max(1, min(15, (os.cpu_count() or 2) - 1))
+        many = _time_items(fn, items, pos, seconds / 2, cores)
+        unit = "positions/s"
+        what = {"c4": "tree states", "c4d": "blocks"}.get(self.name, "sequences")
+        return {"value": many["rate"], "unit": unit, "cores": many["cores"], "kind": "oracle",
+                "sample": f"{len(items)} {what} of the workload, {many['items']} items in {many['s']:.1f} s over "
+                          f"{many['cores']} processes (numpy float64)",
+                "one_core": {"value": one["rate"], "unit": unit, "cores": 1,
+                             "sample": f"{one['items']} items in {one['s']:.1f} s"},
+                "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
+
+
+_CPU_WORK = {}
+
+
+def _cpu_item(i):
+    _CPU_WORK["fn"](_CPU_WORK["items"][i])
+    return i
+
+
+def _time_items(fn, items, pos, seconds, cores):
+    """Run fn over the items (cycling) for about `seconds`, on `cores`
+    processes (forked after the inputs are in memory, so they are shared)."""
+    import multiprocessing as mp
+    _CPU_WORK["fn"], _CPU_WORK["items"] = fn, items
+    done_pos = done = 0
+    t0 = time.perf_counter()
+    if cores == 1:
+        while True:
+            for i in range(len(items)):
+                fn(items[i])
+                done_pos += pos[i]
+                done += 1
                 if time.perf_counter() - t0 >= seconds:
                     break
-            sample = f"{nb} of {B} sequences, {calls} oracle calls"
-        elif self.name == "c5":
-            K, W = x["K"], x["W"]
-            nb = 4
-            p = x["packed"][:nb]
-            tgt, dr = np64(p[:, :K + 1]), np64(p[:, K + 1:])
-            d, n = npi(x["draft_tokens"][:nb]), npi(x["draft_len"][:nb])
+            if time.perf_counter() - t0 >= seconds:
+                break
+    else:
+        ctx = mp.get_context("fork")
+        with ctx.Pool(cores) as pool:
             t0 = time.perf_counter()
-            while True:
-                oracle.verify_greedy(tgt, d, n, dr)
-                done_pos += int(n.sum())
-                calls += 1
-                if time.perf_counter() - t0 >= seconds:
-                    break
-            sample = f"{nb} of 64 sequences, {calls} oracle calls"
-        elif self.name == "c3t":
-            nb = 1
-            rows = np64(x["drf"][:nb])
-            npos = int(x["draft_len"][:nb].sum())
-            t0 = time.perf_counter()
-            while True:
-                oracle.truncate_rows(rows, 1.0, x["top_k"], x["top_p"], x["top_k"], npi(x["draft_len"][:nb]))
-                done_pos += npos
-                calls += 1
-                if time.perf_counter() - t0 >= seconds:
-                    break
-            sample = f"{nb} of 32 sequences, {calls} oracle calls"
-        elif self.name == "c4d":
-            nb = 1
-            st, m = np64(x["stale"][:nb]), npi(x["masked"][:nb])
-            G = np64(x["gumbel"][:nb])
-            fn = oracle.table_order(np64(x["order_table"][:nb]))
-            t0 = time.perf_counter()
-            while True:
-                oracle.build_ddtree(st, m, fn, DD_BUDGET, 1.0, gumbel=G)
-                done_pos += nb * DD_BUDGET
-                calls += 1
-                if time.perf_counter() - t0 >= seconds:
-                    break
-            sample = f"{nb} of 16 blocks, {calls} oracle calls"
-        elif self.name == "c3q":
-            nb = 4
-            xs = {k: v[:nb] if torch.is_tensor(v) else v for k, v in x.items()}
-            args = [np64(xs["tgt"]), npi(xs["q_idx"]), np64(xs["q_prob"]), npi(xs["q_nnz"]),
-                    npi(xs["draft_tokens"]), npi(xs["draft_len"]), 1.0, np64(xs["u_accept"]),
-                    np64(xs["u_resample"])]
-            npos = int(xs["draft_len"].sum())
-            t0 = time.perf_counter()
-            while True:
-                oracle.verify_sparse(*args)
-                done_pos += npos
-                calls += 1
-                if time.perf_counter() - t0 >= seconds:
-                    break
-            sample = f"{nb} of 32 sequences, {calls} oracle calls"
-        elif self.name == "c4s":
-            nb = 2
-            xs = {k: v[:nb] if torch.is_tensor(v) else v for k, v in x.items()}
-            args = [np64(xs["tgt"]), np64(xs["drf"]), npi(xs["pos_star"]), npi(xs["prop_pos"]),
-                    npi(xs["prop_tok"]), np64(xs["q_pos_star"]), npi(xs["draft_len"]), 1.0, 1.0,
-                    np64(xs["u_accept"]), np64(xs["u_resample"])]
-            G = np64(xs["gumbel"])
-            npos = int(xs["draft_len"].sum())
-            t0 = time.perf_counter()
-            while True:
-                oracle.verify_spot_chain(*args, gumbel=G, tau=SPOT_TAU)
-                done_pos += npos
-                calls += 1
-                if time.perf_counter() - t0 >= seconds:
-                    break
-            sample = f"{nb} of 16 sequences, {calls} oracle calls"
-        elif self.name == "c5ao":
-            nb = 4
-            args = (np64(x["tgt"][:nb]), npi(x["order"][:nb]), npi(x["num_active"][:nb]),
-                    npi(x["positions"][:nb]), npi(x["draft_tokens"][:nb]), np64(x["draft_rows"][:nb]))
-            kap = int(self._kappa({k: v[:nb] for k, v in x.items()}).sum())
-            t0 = time.perf_counter()
-            while True:
-                oracle.verify_greedy_any_order(*args)
-                done_pos += kap
-                calls += 1
-                if time.perf_counter() - t0 >= seconds:
-                    break
-            sample = f"{nb} of 64 sequences, {calls} oracle calls"
-        else:
-            b = 0
-            logits = np64(x["logits"][b:b + 1])
-            G = np64(x["gumbel"][b:b + 1])
-            m = x["masked"][b:b + 1].numpy()
-            ns = npi(x["num_states"][b:b + 1])
-            t0 = time.perf_counter()
-            while True:
-                oracle.verify_gumbel_tree(logits, m, npi(x["parent"][b:b + 1]), npi(x["edge_pos"][b:b + 1]),
-                                          npi(x["edge_tok"][b:b + 1]), ns, G, 1.0)
-                done_pos += int(ns[0]) - 1
-                calls += 1
-                if time.perf_counter() - t0 >= seconds:
-                    break
-            sample = f"1 of 16 trees, {calls} oracle calls"
-        dt = time.perf_counter() - t0
-        return {"value": done_pos / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
-                "sample": f"{sample} in {dt:.1f} s (numpy float64, one thread; host has {os.cpu_count()} cpus)"}
+            while time.perf_counter() - t0 < seconds:
+                for i in pool.imap_unordered(_cpu_item, range(len(items))):
+                    done_pos += pos[i]
+                    done += 1
+    dt = time.perf_counter() - t0
+    return {"rate": done_pos / dt, "items": done, "s": dt, "cores": cores}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def run_loop(args, dev):
@@ -460,11 +512,9 @@ def run_loop(args, dev):
     rows out of the caches, so the call reads its inputs from HBM like the
     other workloads; a second pass without it is reported beside."""
     import draft_block_verification_amd as dbv
-    from draft_block_verification_amd import _lib
     import workloads
     inp = workloads.config5_loop(device=dev)
     B, W, V, L = inp["B"], inp["W"], inp["V"], inp["L"]
-    lib = _lib.load()
     rec = {"ms": [], "kms": [], "pos": 0, "bytes": 0, "calls": 0, "tokens": 0}
     scratch = torch.empty(1 << 30, dtype=torch.int16, device=dev)
 
@@ -489,11 +539,9 @@ def run_loop(args, dev):
             k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             k0.record(); k1.record()
             torch.cuda.synchronize()
-            lib.verify_set_timing_events(k0._as_parameter_, k1._as_parameter_)
             e0.record()
-            r = call()
+            r = call.timed(k0, k1)
             e1.record()
-            lib.verify_set_timing_events(None, None)
             torch.cuda.synchronize()
             if record:
                 rec["ms"].append(e0.elapsed_time(e1))
@@ -585,7 +633,6 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     import draft_block_verification_amd as dbv
-    from draft_block_verification_amd import _lib
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.workload == "c5loop":
@@ -615,16 +662,13 @@ def main():
 
     # The row-streaming kernel alone: the library stamps these events at the
     # kernel's own start and end (hipExtLaunchKernel).
-    lib = _lib.load()
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in kev:          # create the underlying HIP events (lazy in torch)
         a.record()
         b.record()
     torch.cuda.synchronize()
     for i in range(steps):
-        lib.verify_set_timing_events(kev[i][0]._as_parameter_, kev[i][1]._as_parameter_)
-        case.calls[i % R]()
-    lib.verify_set_timing_events(None, None)
+        case.calls[i % R].timed(kev[i][0], kev[i][1])
     torch.cuda.synchronize()
     kms = sum(a.elapsed_time(b) for a, b in kev) / steps
     achieved = case.kernel_bytes / (kms * 1e-3) / 1e9
@@ -650,8 +694,9 @@ def main():
         "data": "synthetic",
         "config": dict(workload=DESCR[args.workload], **case.shape,
                        logits="f32" if args.workload == "c1" else "bf16",
-                       positions_per_step=case.positions, rotation_sets=R,
+                       positions_per_step=case.positions, rows_per_step=case.rows, rotation_sets=R,
                        wall_s=round(wall, 4)),
+        "rows_per_s": case.rows / (ms * 1e-3),
         "roofline": {
             "bound": "hbm",
             "kernel": case.kernel,

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
   ddtree_hypotheses, ddtree_level, ddtree_build
 """
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -33,14 +35,40 @@ class Prepared:
     """A verify call whose arguments (pointers, sizes, stream) were marshalled
     once: calling it enqueues the same verification again on the same
     buffers, with no Python-side allocation.  ``outputs`` holds the result
-    tensors; ``keep`` keeps every buffer the pointers refer to alive."""
+    tensors; ``keep`` keeps every buffer the pointers refer to alive.
+    ``options`` (a dbv_options struct, or None) is passed with every call;
+    ``timed(begin, end)`` passes the same options plus a pair of timing
+    events for this call only."""
 
-    def __init__(self, fn, name, args, outputs, keep):
-        self._fn, self._name, self._args = fn, name, args
+    def __init__(self, fn, name, args, outputs, keep, options=None):
+        self._fn, self._name, self._args = fn, name, tuple(args)
         self.outputs, self._keep = outputs, keep
+        self._opts = options
+        self._opts_ref = None if options is None else ctypes.byref(options)
 
     def __call__(self):
-        _check(self._fn(*self._args), self._name)
+        _check(self._fn(*self._args, self._opts_ref), self._name)
+        return self.outputs
+
+    def with_options(self, **fields):
+        """The same call with these dbv_options fields set as well (e.g.
+        max_groups); the outputs are shared with this call."""
+        o = _lib.Options()
+        if self._opts is not None:
+            ctypes.pointer(o)[0] = self._opts
+        for k, v in fields.items():
+            setattr(o, k, v)
+        return Prepared(self._fn, self._name, self._args, self.outputs, self._keep, o)
+
+    def timed(self, begin, end):
+        """Enqueue the call with its row-streaming kernel launched between
+        the torch.cuda.Event pair (begin, end), stamped at the kernel's own
+        start and end."""
+        o = _lib.Options()
+        if self._opts is not None:
+            ctypes.pointer(o)[0] = self._opts
+        o.row_begin, o.row_end = begin.cuda_event, end.cuda_event
+        _check(self._fn(*self._args, ctypes.byref(o)), self._name)
         return self.outputs
 
 
@@ -151,9 +179,19 @@ def verify_greedy(tgt, draft_tokens, draft_len=None, draft_rows=None, eos_id=-1,
     return call if prepare else call()
 
 
+def _chain_margins(out, B, K, dev, margins):
+    """Optional per-decision margins of a chain sampling call (dbv_options
+    accept_margin [B, K], draw_margin [B]); returns the options or None."""
+    if not margins:
+        return None
+    out["accept_margin"] = torch.empty(B, K, dtype=torch.float32, device=dev)
+    out["draw_margin"] = torch.empty(B, dtype=torch.float32, device=dev)
+    return _lib.Options(accept_margin=out["accept_margin"].data_ptr(), draw_margin=out["draw_margin"].data_ptr())
+
+
 def _sampling(fn_name, tgt, drf, draft_tokens, draft_len, temperature_target,
               temperature_draft, lam, u_accept, u_resample, eos_id, len_budget,
-              workspace, diagnostics, prepare):
+              workspace, diagnostics, prepare, margins=False):
     lib = _lib.load()
     dev = tgt.device
     B, K1, V = tgt.shape
@@ -189,51 +227,53 @@ def _sampling(fn_name, tgt, drf, draft_tokens, draft_len, temperature_target,
              _ptr(out.get("p_draft")), _ptr(out.get("q_draft")), _ptr(out.get("alpha")),
              _ptr(out.get("residual_mass")), out["status"].data_ptr(),
              ws.data_ptr(), ws.numel(), _stream(dev)]
+    opts = _chain_margins(out, B, K, dev, margins)
     call = Prepared(getattr(lib, fn_name), fn_name, tuple(args), out,
-                    (tgt, drf, d, n, bud, ua, ur, ws))
+                    (tgt, drf, d, n, bud, ua, ur, ws), opts)
     return call if prepare else call()
 
 
 def verify_rejection(tgt, drf, draft_tokens, u_accept, u_resample, draft_len=None,
                      temperature_target=1.0, temperature_draft=1.0, eos_id=-1,
-                     len_budget=None, workspace=None, diagnostics=True, prepare=False):
+                     len_budget=None, workspace=None, diagnostics=True, prepare=False, margins=False):
     """Lossless rejection-sampling verification (Packed-SS, Algorithm 2).
 
     tgt [B, K+1, V], drf [B, K, V] (same dtype), draft_tokens [B, K],
     u_accept [B, K], u_resample [B, K+1].  Returns accept_len, out_tokens,
     num_out, status and (with diagnostics) p_draft, q_draft, alpha,
-    residual_mass.
+    residual_mass; with margins also accept_margin [B, K] and draw_margin
+    [B], the per-decision margins of dbv_options.
     """
     return _sampling("verify_rejection", tgt, drf, draft_tokens, draft_len,
                      temperature_target, temperature_draft, 0.0, u_accept, u_resample,
-                     eos_id, len_budget, workspace, diagnostics, prepare)
+                     eos_id, len_budget, workspace, diagnostics, prepare, margins)
 
 
 def verify_lenient(tgt, drf, draft_tokens, u_accept, u_resample, lam, draft_len=None,
                    temperature_target=1.0, temperature_draft=1.0, eos_id=-1,
-                   len_budget=None, workspace=None, diagnostics=True, prepare=False):
+                   len_budget=None, workspace=None, diagnostics=True, prepare=False, margins=False):
     """Linear lenient verification, p~ = (1 - lam) p + lam q (Two Tradeoffs,
     Theorem 1 and Algorithm 1).  Arguments as verify_rejection plus lam."""
     return _sampling("verify_lenient", tgt, drf, draft_tokens, draft_len,
                      temperature_target, temperature_draft, lam, u_accept, u_resample,
-                     eos_id, len_budget, workspace, diagnostics, prepare)
+                     eos_id, len_budget, workspace, diagnostics, prepare, margins)
 
 
 def verify_cactus(tgt, drf, draft_tokens, u_accept, u_resample, delta, draft_len=None,
                   temperature_target=1.0, temperature_draft=1.0, eos_id=-1,
-                  len_budget=None, workspace=None, diagnostics=True, prepare=False):
+                  len_budget=None, workspace=None, diagnostics=True, prepare=False, margins=False):
     """Verification with the modified Cactus rule (Two Tradeoffs, App. E):
     the drafted token's target mass is raised to the largest gamma whose
     rescaled target stays within KL budget delta of p.  Arguments as
     verify_rejection plus delta >= 0 (0 = lossless)."""
     return _sampling("verify_cactus", tgt, drf, draft_tokens, draft_len,
                      temperature_target, temperature_draft, delta, u_accept, u_resample,
-                     eos_id, len_budget, workspace, diagnostics, prepare)
+                     eos_id, len_budget, workspace, diagnostics, prepare, margins)
 
 
 def verify_sparse(tgt, q_idx, q_prob, q_nnz, draft_tokens, u_accept, u_resample, draft_len=None,
                   temperature_target=1.0, eos_id=-1, len_budget=None, workspace=None, diagnostics=True,
-                  prepare=False):
+                  prepare=False, margins=False):
     """Lossless verification against stored sparse drafter distributions
     (Packed-SS Sec. 3.2: only Q's nonzero entries are stored under top-k /
     top-p truncation).
@@ -274,7 +314,8 @@ def verify_sparse(tgt, q_idx, q_prob, q_nnz, draft_tokens, u_accept, u_resample,
             out["accept_len"].data_ptr(), out["out_tokens"].data_ptr(), out["num_out"].data_ptr(),
             _ptr(out.get("p_draft")), _ptr(out.get("q_draft")), _ptr(out.get("alpha")),
             _ptr(out.get("residual_mass")), out["status"].data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
-    call = Prepared(lib.verify_sparse, "verify_sparse", args, out, (tgt, qi, qp, qn, d, n, bud, ua, ur, ws))
+    opts = _chain_margins(out, B, K, dev, margins)
+    call = Prepared(lib.verify_sparse, "verify_sparse", args, out, (tgt, qi, qp, qn, d, n, bud, ua, ur, ws), opts)
     return call if prepare else call()
 
 
@@ -303,7 +344,8 @@ def truncate_top_k_top_p(rows, top_k, top_p=1.0, kmax=None, lengths=None, temper
 
 def verify_spot_chain(tgt, drf, pos_star, prop_pos, prop_tok, q_pos_star, u_accept, u_resample,
                       gumbel=None, tau=0.6, draft_len=None, temperature_target=1.0, temperature_draft=1.0,
-                      eos_id=-1, len_budget=None, workspace=None, diagnostics=True, prepare=False):
+                      eos_id=-1, len_budget=None, workspace=None, diagnostics=True, prepare=False,
+                      margins=False):
     """Chain verification on the joint (position, token) space (SPOT App. B,
     Eq. 10-14), gated per link between rejection sampling and coupled-noise
     match when Gumbel rows are given (match where the drafter's confidence
@@ -355,8 +397,9 @@ def verify_spot_chain(tgt, drf, pos_star, prop_pos, prop_tok, q_pos_star, u_acce
             out["out_tokens"].data_ptr(), out["num_out"].data_ptr(), _ptr(out.get("p_draft")),
             _ptr(out.get("q_draft")), _ptr(out.get("alpha")), _ptr(out.get("residual_mass")),
             out["status"].data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+    opts = _chain_margins(out, B, K, dev, margins)
     call = Prepared(lib.verify_spot_chain, "verify_spot_chain", args, out,
-                    (tgt, drf, gumbel, ps, pp, d, c, n, bud, ua, ur, ws))
+                    (tgt, drf, gumbel, ps, pp, d, c, n, bud, ua, ur, ws), opts)
     return call if prepare else call()
 
 
@@ -555,7 +598,7 @@ def ddtree_level(masked, hyp_tok, hyp_prob, order_logits, D, tau=1.0, gamma=0.0,
     st = _dd_state(B, L, D, dev, status) if first else state
     args = (B, L, D, m.data_ptr(), ht.data_ptr(), hp.data_ptr(), o.data_ptr(), o.stride(0), o.stride(1),
             float(tau), float(gamma), int(first)) + _dd_out_ptrs(st) + (_stream(dev),)
-    _check(lib.ddtree_level(*args), "ddtree_level")
+    _check(lib.ddtree_level(*args, None), "ddtree_level")
     st["_keep"] = (m, ht, hp, o)
     return st
 

@@ -37,7 +37,14 @@ EXPORTS = (
     "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_sparse", "truncate_top_k_top_p",
     "verify_spot_chain",
     "verify_greedy_any_order", "verify_gumbel_tree", "verify_workspace_size", "verify_status_string", "verify_abi_version",
-    "verify_set_timing_events", "ddtree_hypotheses", "ddtree_level", "ddtree_build",
+    "ddtree_hypotheses", "ddtree_level", "ddtree_build",
+)
+
+# Entry points that take a trailing `const dbv_options* opts`.
+WITH_OPTIONS = (
+    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_sparse", "truncate_top_k_top_p",
+    "verify_spot_chain", "verify_greedy_any_order", "verify_gumbel_tree", "ddtree_hypotheses", "ddtree_level",
+    "ddtree_build",
 )
 
 _i = ctypes.c_int
@@ -80,10 +87,22 @@ _SIGS = {
     "verify_workspace_size": [_i, _i, _i, _i, _i, _i],
     "verify_status_string": [_i],
     "verify_abi_version": [],
-    "verify_set_timing_events": [_p, _p],
 }
-_RES = {"verify_workspace_size": _sz, "verify_status_string": ctypes.c_char_p,
-        "verify_set_timing_events": None}
+for _name in WITH_OPTIONS:
+    _SIGS[_name] = _SIGS[_name] + [_p]
+_RES = {"verify_workspace_size": _sz, "verify_status_string": ctypes.c_char_p}
+
+
+class Options(ctypes.Structure):
+    """struct dbv_options of include/dbv.h."""
+    _fields_ = [("size", ctypes.c_uint32), ("max_groups", ctypes.c_uint32),
+                ("row_begin", _p), ("row_end", _p),
+                ("accept_margin", _p), ("draw_margin", _p), ("row_tv", _p),
+                ("pos_margin", _p), ("tok_margin", _p)]
+
+    def __init__(self, **kw):
+        super().__init__(size=ctypes.sizeof(Options), **kw)
+
 
 _lib = None
 

@@ -38,19 +38,41 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
+def _filter(stderr):
+    return "\n".join(line for line in stderr.splitlines()
+                     if "packed-fp32-ops" not in line and "not a recognized feature" not in line)
+
+
 def build(verbose=False, out=LIB):
-    """Compile every HIP source into one shared library (always recompiles)."""
+    """Compile every HIP source (in parallel, one object each) and link them
+    into one shared library (always recompiles)."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        cmd = [hipcc()] + compile_flags + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    objs, errs, failed = [], [], False
+    for obj, proc in jobs:
+        _, err = proc.communicate()
+        errs.append(_filter(err))
+        failed |= proc.returncode != 0
+        objs.append(obj)
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(e for e in errs if e.strip()))
     tmp = out + ".tmp"
-    cmd = [hipcc()] + HIP_FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(line for line in res.stderr.splitlines()
-                     if "packed-fp32-ops" not in line and "not a recognized feature" not in line)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + errs)
-    if verbose and errs.strip():
-        print(errs, file=sys.stderr)
+        raise RuntimeError("link failed:\n" + _filter(res.stderr))
+    if verbose and any(e.strip() for e in errs):
+        print("\n".join(e for e in errs if e.strip()), file=sys.stderr)
     os.replace(tmp, out)
     return out
 

@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstddef>
 #include <cstring>
 
 #include <hip/hip_runtime.h>
@@ -21,21 +22,6 @@ using dbv::kMaxStates;
 constexpr int kMaxDevices = 64;
 // Compute units per device, filled with the architecture check.
 std::atomic<int> g_cus[kMaxDevices];
-// Diagnostics events (verify_set_timing_events); off when NULL.
-std::atomic<void*> g_ev_begin{nullptr};
-std::atomic<void*> g_ev_end{nullptr};
-
-dbv::TimingEvents timing_events() {
-  dbv::TimingEvents ev;
-  void* b = g_ev_begin.load(std::memory_order_acquire);
-  void* e = g_ev_end.load(std::memory_order_acquire);
-  if (b && e) {
-    ev.begin = static_cast<hipEvent_t>(b);
-    ev.end = static_cast<hipEvent_t>(e);
-  }
-  return ev;
-}
-
 // 0 = not yet queried, 1 = gfx950, 2 = some other device.
 std::atomic<int> g_arch[kMaxDevices];
 
@@ -60,6 +46,54 @@ dbv_status device_ready() {
     if (s != 1) return DBV_ERR_NO_DEVICE;
   }
   return DBV_OK;
+}
+
+// The options of one call (include/dbv.h, dbv_options), read once: fields
+// past the caller's `size` count as unset.
+struct CallOpts {
+  dbv::TimingEvents ev;
+  int64_t max_groups = 0;             // 0: no bound beyond the device's
+  float* accept_margin = nullptr;
+  float* draw_margin = nullptr;
+  float* row_tv = nullptr;
+  float* pos_margin = nullptr;
+  float* tok_margin = nullptr;
+};
+
+template <typename T>
+T opt_field(const dbv_options* o, T dbv_options::*f, size_t off) {
+  return (o && o->size >= off + sizeof(T)) ? o->*f : T();
+}
+
+// false: a malformed struct (a size too small to hold the timing events, or
+// only one of the two events).
+bool read_opts(const dbv_options* o, CallOpts& c) {
+  if (o == nullptr) return true;
+  if (o->size < offsetof(dbv_options, row_end) + sizeof(void*)) return false;
+  void* b = o->row_begin;
+  void* e = o->row_end;
+  if ((b == nullptr) != (e == nullptr)) return false;
+  c.max_groups = o->max_groups;
+  c.ev.begin = static_cast<hipEvent_t>(b);
+  c.ev.end = static_cast<hipEvent_t>(e);
+  c.accept_margin = opt_field(o, &dbv_options::accept_margin, offsetof(dbv_options, accept_margin));
+  c.draw_margin = opt_field(o, &dbv_options::draw_margin, offsetof(dbv_options, draw_margin));
+  c.row_tv = opt_field(o, &dbv_options::row_tv, offsetof(dbv_options, row_tv));
+  c.pos_margin = opt_field(o, &dbv_options::pos_margin, offsetof(dbv_options, pos_margin));
+  c.tok_margin = opt_field(o, &dbv_options::tok_margin, offsetof(dbv_options, tok_margin));
+  return true;
+}
+
+// Groups of a row-streaming launch: the device's resident groups, bounded
+// by the caller's max_groups.
+int64_t group_cap(const CallOpts& c) {
+  const int64_t r = dbv::resident_groups();
+  return c.max_groups > 0 && c.max_groups < r ? c.max_groups : r;
+}
+
+// Options of an entry point without chain or tree diagnostics.
+bool read_plain_opts(const dbv_options* o, CallOpts& c) {
+  return read_opts(o, c) && !c.accept_margin && !c.draw_margin && !c.row_tv && !c.pos_margin && !c.tok_margin;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -105,8 +139,10 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
                          const float* u_resample, int32_t eos_id, const int32_t* len_budget,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* num_out, float* p_draft,
                          float* q_draft, float* alpha, float* residual_mass, int32_t* status, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         size_t ws_bytes, void* stream, const dbv_options* opts) {
   if (B < 0 || K < 0 || K > kMaxDraft || V < 1 || !dtype_ok(dtype)) return DBV_ERR_INVALID_ARG;
+  CallOpts co;
+  if (!read_opts(opts, co) || co.pos_margin || co.tok_margin || co.row_tv) return DBV_ERR_INVALID_ARG;
   if (V > dbv::kMaxSampleV) return DBV_ERR_UNSUPPORTED;
   if (!temp_ok(tt) || !temp_ok(td) || !(rl.lam >= 0.f && rl.lam <= 1.f)) return DBV_ERR_INVALID_ARG;
   if (!(std::isfinite(rl.delta) && rl.delta >= 0.f)) return DBV_ERR_INVALID_ARG;
@@ -157,8 +193,10 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.accept_len = accept_len; a.out_tokens = out_tokens; a.num_out = num_out;
   a.p_draft = p_draft; a.q_draft = q_draft; a.alpha = alpha; a.residual_mass = residual_mass;
   a.status = status;
+  a.accept_margin = co.accept_margin;
+  a.draw_margin = co.draw_margin;
   char* w = static_cast<char*>(ws);
-  a.stats = reinterpret_cast<float2*>(w + plan.off_stats);
+  a.stats = reinterpret_cast<dbv::Stat64*>(w + plan.off_stats);
   a.gpart = reinterpret_cast<float2*>(w + plan.off_gpart);
   a.pre = reinterpret_cast<int32_t*>(w + plan.off_pre);
   a.rec = reinterpret_cast<dbv::DrawRecord*>(w + plan.off_rec);
@@ -166,11 +204,11 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.sq = reinterpret_cast<dbv::SparseRow*>(w + plan.off_sq);
   const int64_t P = rl.gumbel ? dbv::gumbel_parts(static_cast<int64_t>(eb)) : 1;
   a.grid = dbv::stream_grid(static_cast<int64_t>(B) * (P * (K + 1) + K), V, static_cast<int64_t>(eb),
-                            dbv::resident_groups());
+                            group_cap(co));
   a.tiles = static_cast<int>(plan.tiles);
   a.tpc = static_cast<int>(plan.tpc);
   a.chunks = static_cast<int>(plan.chunks);
-  return dbv::launch_sample(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
+  return dbv::launch_sample(a, dtype, static_cast<hipStream_t>(stream), co.ev) ? DBV_OK : DBV_ERR_LAUNCH;
 }
 
 Rule lenient_rule(float lam) {
@@ -191,8 +229,10 @@ dbv_status dd_tree_common(int B, int L, int D, const uint8_t* masked, const int3
                           float tau, float gamma, int first, int32_t* parent, int32_t* edge_pos,
                           int32_t* edge_tok, float* mass, uint8_t* node_masked, int32_t* num_nodes,
                           int32_t* frontier, int32_t* num_frontier, int32_t* status, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          size_t ws_bytes, void* stream, const dbv_options* opts) {
   if (B < 0 || L < 1 || L > dbv::kDDMaxBlock || D < 0 || D > dbv::kDDMaxBudget) return DBV_ERR_INVALID_ARG;
+  CallOpts co;
+  if (!read_plain_opts(opts, co)) return DBV_ERR_INVALID_ARG;
   if (os < 0 || orow < 0 || !(std::isfinite(tau) && tau > 0.f) || !(std::isfinite(gamma) && gamma >= 0.f))
     return DBV_ERR_INVALID_ARG;
   if (B > 0 && (masked == nullptr || hyp_tok == nullptr || hyp_prob == nullptr || order == nullptr ||
@@ -216,7 +256,7 @@ dbv_status dd_tree_common(int B, int L, int D, const uint8_t* masked, const int3
   a.status = status;
   a.keys = static_cast<uint64_t*>(ws);
   a.masks = a.keys + static_cast<size_t>(B) * (D + 1);
-  return dbv::launch_dd_tree(a, static_cast<hipStream_t>(stream)) ? DBV_OK : DBV_ERR_LAUNCH;
+  return dbv::launch_dd_tree(a, static_cast<hipStream_t>(stream), co.ev) ? DBV_OK : DBV_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -243,9 +283,11 @@ dbv_status verify_greedy(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
                          const void* draft_rows, int64_t dr_seq_stride, int64_t dr_row_stride, int W,
                          int32_t eos_id, const int32_t* len_budget, int32_t* accept_len, int32_t* out_tokens,
                          int32_t* num_out, int32_t* next_draft, int32_t* next_len, int32_t* status, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         size_t ws_bytes, void* stream, const dbv_options* opts) {
   if (B < 0 || K < 0 || K > kMaxDraft || W < 0 || W > kMaxDraft || V < 1 || !dtype_ok(dtype))
     return DBV_ERR_INVALID_ARG;
+  CallOpts co;
+  if (!read_plain_opts(opts, co)) return DBV_ERR_INVALID_ARG;
   if (tgt_seq_stride < 0 || tgt_row_stride < 0 || dr_seq_stride < 0 || dr_row_stride < 0)
     return DBV_ERR_INVALID_ARG;
   if (tgt == nullptr || (K > 0 && draft_tokens == nullptr) || (W > 0 && draft_rows == nullptr))
@@ -271,8 +313,8 @@ dbv_status verify_greedy(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + plan.off_part);
   a.pre = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan.off_pre);
   a.elem_bytes = static_cast<int>(eb);
-  a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(eb), dbv::resident_groups());
-  return dbv::launch_greedy(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
+  a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(eb), group_cap(co));
+  return dbv::launch_greedy(a, dtype, static_cast<hipStream_t>(stream), co.ev) ? DBV_OK : DBV_ERR_LAUNCH;
 }
 
 dbv_status verify_rejection(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
@@ -282,11 +324,11 @@ dbv_status verify_rejection(int B, int K, int V, dbv_dtype dtype, const void* tg
                             const float* u_resample, int32_t eos_id, const int32_t* len_budget,
                             int32_t* accept_len, int32_t* out_tokens, int32_t* num_out, float* p_draft,
                             float* q_draft, float* alpha, float* residual_mass, int32_t* status, void* ws,
-                            size_t ws_bytes, void* stream) {
+                            size_t ws_bytes, void* stream, const dbv_options* opts) {
   return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
                        drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft,
                        Rule{}, u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft,
-                       q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
+                       q_draft, alpha, residual_mass, status, ws, ws_bytes, stream, opts);
 }
 
 dbv_status verify_lenient(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
@@ -295,12 +337,12 @@ dbv_status verify_lenient(int B, int K, int V, dbv_dtype dtype, const void* tgt,
                           float temperature_draft, float lambda, const float* u_accept, const float* u_resample,
                           int32_t eos_id, const int32_t* len_budget, int32_t* accept_len, int32_t* out_tokens,
                           int32_t* num_out, float* p_draft, float* q_draft, float* alpha, float* residual_mass,
-                          int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+                          int32_t* status, void* ws, size_t ws_bytes, void* stream, const dbv_options* opts) {
   return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
                        drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft,
                        lenient_rule(lambda), u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens,
                        num_out, p_draft,
-                       q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
+                       q_draft, alpha, residual_mass, status, ws, ws_bytes, stream, opts);
 }
 
 dbv_status verify_cactus(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
@@ -309,11 +351,11 @@ dbv_status verify_cactus(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
                          float temperature_draft, float delta, const float* u_accept, const float* u_resample,
                          int32_t eos_id, const int32_t* len_budget, int32_t* accept_len, int32_t* out_tokens,
                          int32_t* num_out, float* p_draft, float* q_draft, float* alpha, float* residual_mass,
-                         int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+                         int32_t* status, void* ws, size_t ws_bytes, void* stream, const dbv_options* opts) {
   return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
                        drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft,
                        cactus_rule(delta), u_accept, u_resample, eos_id, len_budget, accept_len,
-                       out_tokens, num_out, p_draft, q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
+                       out_tokens, num_out, p_draft, q_draft, alpha, residual_mass, status, ws, ws_bytes, stream, opts);
 }
 
 dbv_status verify_spot_chain(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
@@ -325,7 +367,7 @@ dbv_status verify_spot_chain(int B, int K, int V, dbv_dtype dtype, const void* t
                              const float* u_resample, int32_t eos_id, const int32_t* len_budget,
                              int32_t* accept_len, int32_t* out_tokens, int32_t* num_out, float* p_draft,
                              float* q_draft, float* alpha, float* residual_mass, int32_t* status, void* ws,
-                             size_t ws_bytes, void* stream) {
+                             size_t ws_bytes, void* stream, const dbv_options* opts) {
   Rule r;
   r.rule = dbv::RULE_SPOT;
   r.pos_star = pos_star;
@@ -338,7 +380,7 @@ dbv_status verify_spot_chain(int B, int K, int V, dbv_dtype dtype, const void* t
   return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
                        drf_row_stride, prop_tok, draft_len, temperature_target, temperature_draft, r, u_accept,
                        u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft, q_draft, alpha,
-                       residual_mass, status, ws, ws_bytes, stream);
+                       residual_mass, status, ws, ws_bytes, stream, opts);
 }
 
 dbv_status verify_sparse(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
@@ -347,7 +389,7 @@ dbv_status verify_sparse(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
                          const float* u_accept, const float* u_resample, int32_t eos_id, const int32_t* len_budget,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* num_out, float* p_draft,
                          float* q_draft, float* alpha, float* residual_mass, int32_t* status, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         size_t ws_bytes, void* stream, const dbv_options* opts) {
   Rule r;
   r.rule = dbv::RULE_SPARSE;
   r.qidx = q_idx;
@@ -356,14 +398,16 @@ dbv_status verify_sparse(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   r.kmax = kmax;
   return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, nullptr, 0, 0, draft_tokens,
                        draft_len, temperature_target, 1.f, r, u_accept, u_resample, eos_id, len_budget, accept_len,
-                       out_tokens, num_out, p_draft, q_draft, alpha, residual_mass, status, ws, ws_bytes, stream);
+                       out_tokens, num_out, p_draft, q_draft, alpha, residual_mass, status, ws, ws_bytes, stream, opts);
 }
 
 dbv_status truncate_top_k_top_p(int B, int K, int V, dbv_dtype dtype, const void* rows, int64_t seq_stride,
                                 int64_t row_stride, const int32_t* lengths, float temperature, int top_k,
                                 float top_p, int kmax, int32_t* q_idx, float* q_prob, int32_t* q_nnz,
-                                void* stream) {
+                                void* stream, const dbv_options* opts) {
   if (B < 0 || K < 0 || V < 1 || !dtype_ok(dtype) || seq_stride < 0 || row_stride < 0) return DBV_ERR_INVALID_ARG;
+  CallOpts co;
+  if (!read_plain_opts(opts, co)) return DBV_ERR_INVALID_ARG;
   if (V > dbv::kMaxSampleV || kmax > dbv::kMaxNnz) return DBV_ERR_UNSUPPORTED;
   if (!temp_ok(temperature) || kmax < 1 || top_k < 1 || top_k > kmax || !(top_p > 0.f && top_p <= 1.f))
     return DBV_ERR_INVALID_ARG;
@@ -381,7 +425,7 @@ dbv_status truncate_top_k_top_p(int B, int K, int V, dbv_dtype dtype, const void
   a.kq = dbv::kLog2eHost / temperature;
   a.top_k = top_k; a.top_p = top_p; a.kmax = kmax;
   a.q_idx = q_idx; a.q_prob = q_prob; a.q_nnz = q_nnz;
-  return dbv::launch_truncate(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK
+  return dbv::launch_truncate(a, dtype, static_cast<hipStream_t>(stream), co.ev) ? DBV_OK
                                                                                          : DBV_ERR_LAUNCH;
 }
 
@@ -391,8 +435,10 @@ dbv_status verify_greedy_any_order(int B, int U, int V, dbv_dtype dtype, const v
                                    int64_t dr_seq_stride, int64_t dr_row_stride, int32_t eos_id,
                                    const int32_t* end_pos, int32_t* accept_len, int32_t* num_accepted,
                                    int32_t* acc_pos, int32_t* acc_tok, int32_t* new_end, int32_t* next_draft,
-                                   int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+                                   int32_t* status, void* ws, size_t ws_bytes, void* stream, const dbv_options* opts) {
   if (B < 0 || U < 0 || U > kMaxDraft || V < 1 || !dtype_ok(dtype)) return DBV_ERR_INVALID_ARG;
+  CallOpts co;
+  if (!read_plain_opts(opts, co)) return DBV_ERR_INVALID_ARG;
   if (tgt_seq_stride < 0 || tgt_row_stride < 0 || dr_seq_stride < 0 || dr_row_stride < 0)
     return DBV_ERR_INVALID_ARG;
   if (tgt == nullptr || (U > 0 && (order == nullptr || draft_tokens == nullptr))) return DBV_ERR_INVALID_ARG;
@@ -424,8 +470,8 @@ dbv_status verify_greedy_any_order(int B, int U, int V, dbv_dtype dtype, const v
   a.nver = seq + B;
   a.kappa = seq + 2 * static_cast<int64_t>(B);
   a.pstat = seq + 3 * static_cast<int64_t>(B);
-  a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(eb), dbv::resident_groups());
-  return dbv::launch_any_order(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK
+  a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(eb), group_cap(co));
+  return dbv::launch_any_order(a, dtype, static_cast<hipStream_t>(stream), co.ev) ? DBV_OK
                                                                                            : DBV_ERR_LAUNCH;
 }
 
@@ -436,10 +482,13 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const
                               int64_t g_seq_stride, int64_t g_pos_stride, float temperature, dbv_tree_mode mode,
                               int32_t* sel_pos, int32_t* sel_tok, float* sel_conf, int32_t* path_len,
                               int32_t* path_nodes, int32_t* commit_pos, int32_t* commit_tok,
-                              int32_t* num_commits, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+                              int32_t* num_commits, int32_t* status, void* ws, size_t ws_bytes, void* stream, const dbv_options* opts) {
   if (B < 0 || S < 1 || S > kMaxStates || L < 1 || L > kMaxBlockLen || V < 1 || !dtype_ok(dtype))
     return DBV_ERR_INVALID_ARG;
   if (mode != DBV_TREE_STATE_EQUALITY && mode != DBV_TREE_FIXED_POSITION) return DBV_ERR_INVALID_ARG;
+  CallOpts co;
+  if (!read_opts(opts, co) || co.accept_margin || co.draw_margin || co.row_tv || co.pos_margin || co.tok_margin)
+    return DBV_ERR_INVALID_ARG;
   if (!(std::isfinite(temperature) && temperature >= 0.f)) return DBV_ERR_INVALID_ARG;
   if (seq_stride < 0 || state_stride < 0 || pos_stride < 0 || g_seq_stride < 0 || g_pos_stride < 0)
     return DBV_ERR_INVALID_ARG;
@@ -478,16 +527,18 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const
   a.conf = reinterpret_cast<float2*>(w + plan.off_conf);
   a.pick = reinterpret_cast<float2*>(w + plan.off_pick);
   a.sel = reinterpret_cast<int32_t*>(w + plan.off_sel);
-  a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(elem_bytes(dtype)), dbv::resident_groups());
+  a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(elem_bytes(dtype)), group_cap(co));
   a.split2 = plan.split2; a.chunk2 = plan.chunk2;
-  return dbv::launch_tree(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK : DBV_ERR_LAUNCH;
+  return dbv::launch_tree(a, dtype, static_cast<hipStream_t>(stream), co.ev) ? DBV_OK : DBV_ERR_LAUNCH;
 }
 
 dbv_status ddtree_hypotheses(int B, int L, int V, dbv_dtype dtype, const void* stale, int64_t seq_stride,
                              int64_t pos_stride, const uint8_t* masked, const float* gumbel, int64_t g_seq_stride,
                              int64_t g_pos_stride, float temperature, float runner_up_below, int32_t* hyp_tok,
-                             float* hyp_prob, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+                             float* hyp_prob, int32_t* status, void* ws, size_t ws_bytes, void* stream, const dbv_options* opts) {
   if (B < 0 || L < 1 || L > dbv::kDDMaxBlock || V < 1 || !dtype_ok(dtype)) return DBV_ERR_INVALID_ARG;
+  CallOpts co;
+  if (!read_plain_opts(opts, co)) return DBV_ERR_INVALID_ARG;
   if (seq_stride < 0 || pos_stride < 0 || g_seq_stride < 0 || g_pos_stride < 0) return DBV_ERR_INVALID_ARG;
   if (!(std::isfinite(temperature) && temperature >= 0.f) || std::isnan(runner_up_below))
     return DBV_ERR_INVALID_ARG;
@@ -516,8 +567,8 @@ dbv_status ddtree_hypotheses(int B, int L, int V, dbv_dtype dtype, const void* s
   a.part = reinterpret_cast<dbv::DDPart*>(w + plan.off_part);
   // Gumbel rows double the bytes per element; units of 512 elements then.
   a.split_bytes = temperature > 0.f ? 8 : static_cast<int>(elem_bytes(dtype));
-  a.grid = dbv::stream_grid(plan.max_rows, V, a.split_bytes, dbv::resident_groups());
-  return dbv::launch_dd_hypotheses(a, dtype, static_cast<hipStream_t>(stream), timing_events()) ? DBV_OK
+  a.grid = dbv::stream_grid(plan.max_rows, V, a.split_bytes, group_cap(co));
+  return dbv::launch_dd_hypotheses(a, dtype, static_cast<hipStream_t>(stream), co.ev) ? DBV_OK
                                                                                              : DBV_ERR_LAUNCH;
 }
 
@@ -525,20 +576,20 @@ dbv_status ddtree_level(int B, int L, int D, const uint8_t* masked, const int32_
                         const float* order_logits, int64_t o_seq_stride, int64_t o_row_stride, float tau,
                         float gamma, int first, int32_t* parent, int32_t* edge_pos, int32_t* edge_tok,
                         float* mass, uint8_t* node_masked, int32_t* num_nodes, int32_t* frontier,
-                        int32_t* num_frontier, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+                        int32_t* num_frontier, int32_t* status, void* ws, size_t ws_bytes, void* stream, const dbv_options* opts) {
   return dd_tree_common(B, L, D, masked, hyp_tok, hyp_prob, order_logits, o_seq_stride, o_row_stride, 0, tau,
                         gamma, first, parent, edge_pos, edge_tok, mass, node_masked, num_nodes, frontier,
-                        num_frontier, status, ws, ws_bytes, stream);
+                        num_frontier, status, ws, ws_bytes, stream, opts);
 }
 
 dbv_status ddtree_build(int B, int L, int D, const uint8_t* masked, const int32_t* hyp_tok, const float* hyp_prob,
                         const float* order_table, int64_t t_seq_stride, int64_t t_row_stride, float tau,
                         float gamma, int32_t* parent, int32_t* edge_pos, int32_t* edge_tok, float* mass,
                         uint8_t* node_masked, int32_t* num_nodes, int32_t* frontier, int32_t* num_frontier,
-                        int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+                        int32_t* status, void* ws, size_t ws_bytes, void* stream, const dbv_options* opts) {
   return dd_tree_common(B, L, D, masked, hyp_tok, hyp_prob, order_table, t_seq_stride, t_row_stride, 1, tau,
                         gamma, 1, parent, edge_pos, edge_tok, mass, node_masked, num_nodes, frontier,
-                        num_frontier, status, ws, ws_bytes, stream);
+                        num_frontier, status, ws, ws_bytes, stream, opts);
 }
 
 size_t verify_workspace_size(dbv_kind kind, int B, int K_or_S, int L, int V, dbv_dtype dtype) {
@@ -583,9 +634,5 @@ const char* verify_status_string(dbv_status s) {
 
 int verify_abi_version(void) { return DBV_ABI_VERSION; }
 
-void verify_set_timing_events(void* begin, void* end) {
-  g_ev_begin.store(begin, std::memory_order_release);
-  g_ev_end.store(end, std::memory_order_release);
-}
 
 }  // extern "C"

@@ -181,6 +181,73 @@ __device__ __forceinline__ void stats_merge(float& M, float& S, float M2, float 
 }
 
 // ---------------------------------------------------------------------------
+// Softmax statistics for the sampling verifiers, accurate enough that
+// differences of two rows' probabilities keep their relative precision.
+// The reference of a running maximum M is the integer E = floor(M k): every
+// element contributes exp2(x k - E) <= 2, summed in float32 over a block and
+// added to a float64 S.  Moving the reference rescales S by an exact power of
+// two, so S is the sum of exactly the terms a later exp2(x k - E) reproduces
+// (no rounded rescale factors), and its float64 accumulation leaves only the
+// per-element rounding, which averages out.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float ref_exp(float M, float k) { return floorf(M * k); }
+
+// S (relative to the reference of M) rescaled to the reference E; 0 when M is
+// -inf.
+__device__ __forceinline__ double rescale_to(double S, float M, float k, float E) {
+  if (M == -kInf) return 0.0;
+  // Shifts below -1100 leave 0 in float64 anyway; the clamp keeps huge
+  // logit ranges inside int.
+  return __builtin_ldexp(S, static_cast<int>(fmaxf(ref_exp(M, k) - E, -1100.f)));
+}
+
+// Per-lane statistics for SoftmaxStats64's scheme: S in float32 relative to
+// E = floor(M k), rescaled by exact powers of two (ldexp) when E moves.  A
+// lane's float32 rounding is independent of the other lanes', so it averages
+// out over the float64 merge of the lanes (wave_stats64).
+struct SoftmaxStats64 {
+  float M = -kInf;
+  float E = 0.f;
+  float S = 0.f;
+  float k;  // log2(e) / T
+  __device__ explicit SoftmaxStats64(float k_) : k(k_) {}
+
+  template <int N>
+  __device__ __forceinline__ void absorb(const float* x) {
+    float cm = x[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j) cm = fmaxp(cm, x[j]);
+    const float Mn = fmaxp(M, cm);
+    if (Mn == -kInf) return;                 // nothing but -inf so far
+    if (!(Mn < kInf)) { M = Mn; return; }    // NaN / +inf: the row is in error
+    const float En = ref_exp(Mn, k);
+    // E <= En; S is 0 until the first finite maximum, and shifts below -200
+    // leave 0 in float32 anyway.
+    S = __builtin_ldexpf(S, static_cast<int>(fmaxf(E - En, -200.f)));
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) s += fast_exp2(__builtin_fmaf(x[j], k, -En));
+    S += s;
+    M = Mn;
+    E = En;
+  }
+  template <int N>
+  __device__ __forceinline__ void group(const float* x, int64_t) { absorb<N>(x); }
+  template <int U, int W>
+  __device__ __forceinline__ void block(const float* x, int64_t, int64_t) { absorb<U * W>(x); }
+};
+
+// Merge two (M, S) pairs with float64 S; -inf / NaN maxima propagate.
+__device__ __forceinline__ void stats64_merge(float& M, double& S, float M2, double S2, float k) {
+  const float Mn = fmaxp(M, M2);
+  if (Mn == -kInf) { M = Mn; S = 0.0; return; }
+  if (!(Mn < kInf)) { M = Mn; return; }
+  const float E = ref_exp(Mn, k);
+  S = rescale_to(S, M, k, E) + rescale_to(S2, M2, k, E);
+  M = Mn;
+}
+
+// ---------------------------------------------------------------------------
 // Lowest-index argmax of a score.  Per lane, a group whose maximum beats the
 // lane's best (rare after the first few groups) also records the exact
 // position of its first maximal element, so no element is ever re-read.
@@ -303,6 +370,40 @@ __device__ __forceinline__ void wave_stats(float& M, float& S, float k) {
 #undef DBV_STATS_STEP
   M = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), 63));
   S = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), 63));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_move(double identity, double v) {
+  const uint64_t iv = __builtin_bit_cast(uint64_t, identity);
+  const uint64_t vv = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(static_cast<int>(iv), static_cast<int>(vv), CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(static_cast<int>(iv >> 32), static_cast<int>(vv >> 32), CTRL, ROWS,
+                                             0xf, false);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                        static_cast<uint32_t>(lo));
+}
+
+__device__ __forceinline__ double readlane63(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(b), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), 63);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Wave-level (M, S) reduction with float64 S, same lane moves as wave_stats;
+// S enters as each lane's sum relative to floor(M k).
+__device__ __forceinline__ void wave_stats64(float& M, double& S, float k) {
+#define DBV_STATS64_STEP(C, R)                                                \
+  stats64_merge(M, S, dpp_move<C, R>(-kInf, M), dpp_move<C, R>(0.0, S), k);
+  DBV_STATS64_STEP(0xB1, 0xf)
+  DBV_STATS64_STEP(0x4E, 0xf)
+  DBV_STATS64_STEP(0x141, 0xf)
+  DBV_STATS64_STEP(0x140, 0xf)
+  DBV_STATS64_STEP(0x142, 0xa)
+  DBV_STATS64_STEP(0x143, 0xc)
+#undef DBV_STATS64_STEP
+  M = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), 63));
+  S = readlane63(S);
 }
 
 // Wave-level argmax (value, lowest index, NaN flag) through DPP lane moves;
@@ -507,6 +608,40 @@ __device__ __forceinline__ void combine_rows_stats(int nrows, const float2* part
 }
 
 template <int NT = kBlock, class SpanFn, class DoneFn>
+__device__ __forceinline__ void combine_rows_stats64(int nrows, const Stat64* part, float k, SpanFn span,
+                                                     DoneFn done) {
+  const int sub = threadIdx.x % kRowLanes;
+  for (int r0 = 0; r0 < nrows; r0 += NT / kRowLanes) {
+    const int r = r0 + static_cast<int>(threadIdx.x) / kRowLanes;
+    float M = -kInf;
+    double S = 0.0;
+    if (r < nrows) {
+      int64_t first, n;
+      span(r, first, n);
+      const Stat64* p = part + first;
+      for (int64_t j0 = 0; j0 < n; j0 += kRowLanes * kRowLoads) {
+        Stat64 buf[kRowLoads];
+#pragma unroll
+        for (int q = 0; q < kRowLoads; ++q) {
+          const int64_t j = j0 + sub + static_cast<int64_t>(q) * kRowLanes;
+          if (j < n) buf[q] = p[j];
+          else { buf[q].M = -kInf; buf[q].S = 0.0; }
+        }
+#pragma unroll
+        for (int q = 0; q < kRowLoads; ++q) stats64_merge(M, S, buf[q].M, buf[q].S, k);
+      }
+    }
+#pragma unroll
+    for (int m = kRowLanes / 2; m >= 1; m >>= 1) {
+      const float M2 = __shfl_xor(M, m, 64);
+      const double S2 = __shfl_xor(S, m, 64);
+      stats64_merge(M, S, M2, S2, k);
+    }
+    if (r < nrows && sub == 0) done(r, M, S);
+  }
+}
+
+template <int NT = kBlock, class SpanFn, class DoneFn>
 __device__ __forceinline__ void combine_rows_pick(int nrows, const float2* part, SpanFn span, DoneFn done) {
   const int sub = threadIdx.x % kRowLanes;
   for (int r0 = 0; r0 < nrows; r0 += NT / kRowLanes) {
@@ -558,6 +693,13 @@ __device__ __forceinline__ int max_status(float M) {
   if (M != M || M == kInf) return SEQ_NONFINITE;
   if (M == -kInf) return SEQ_EMPTY_ROW;
   return 0;
+}
+
+// Status of a softmax row from its float64 statistics (M, S).
+__device__ __forceinline__ int stats64_status(float M, double S) {
+  int st = max_status(M);
+  if (!st && !(S > 0.0 && S < 1e300)) st = SEQ_NONFINITE;
+  return st;
 }
 
 // Status of a softmax row from its combined statistics (M, S).

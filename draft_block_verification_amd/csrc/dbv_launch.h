@@ -57,7 +57,9 @@ struct SampleArgs {
   int32_t* accept_len; int32_t* out_tokens; int32_t* num_out;
   float* p_draft; float* q_draft; float* alpha; float* residual_mass;
   int32_t* status;
-  float2* stats;                       // per (slot, wave)
+  float* accept_margin;                // [B, K] |u - alpha| (NULL: not written)
+  float* draw_margin;                  // [B] the draw's distance from a CDF step over Z (NULL: not written)
+  Stat64* stats;                       // per (slot, wave): M and the float64 sum
   float2* gpart;                       // per (slot, wave), with Gumbel rows
   int32_t* pre;                        // [B + 1] first stream row per sequence
   DrawRecord* rec;                     // per sequence
@@ -212,6 +214,6 @@ bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingE
 bool launch_any_order(const AnyOrderArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
 bool launch_truncate(const TruncArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
 bool launch_dd_hypotheses(const DDHypArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev);
-bool launch_dd_tree(const DDTreeArgs& a, hipStream_t stream);
+bool launch_dd_tree(const DDTreeArgs& a, hipStream_t stream, const TimingEvents& ev);
 
 }  // namespace dbv

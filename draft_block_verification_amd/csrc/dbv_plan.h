@@ -110,9 +110,10 @@ inline int64_t stream_grid(int64_t max_rows, int64_t V, int64_t elem_bytes, int6
   return units < g ? units : g;
 }
 
-// Bytes of the per-(slot, wave) float2 partials for up to max_rows rows.
-inline size_t partial_bytes(int64_t max_rows) {
-  return align256(static_cast<size_t>(max_rows + kMaxGrid) * kWavesPlan * 8);
+// Bytes of the per-(slot, wave) partials (float2: 8 bytes; the sampling
+// statistics with a float64 sum: 16) for up to max_rows rows.
+inline size_t partial_bytes(int64_t max_rows, size_t bytes_per = 8) {
+  return align256(static_cast<size_t>(max_rows + kMaxGrid) * kWavesPlan * bytes_per);
 }
 
 // The correction / bonus draw.  Its row is cut into tiles of 64 16-byte
@@ -195,15 +196,26 @@ inline AnyOrderPlan plan_any_order(int B, int U) {
 struct DrawRecord {
   int status;        // sequence status bits; error bits mean "done"
   int h;             // accepted drafts; the draw uses row h
-  int resid;         // 1: residual [p~ - q]_+ at row h, 0: bonus from p
-  float cp, isp;     // exp2 offset and scale of target row h (1/S, times the
-                     // Cactus rescaling of the other tokens)
-  float cq, isq;     // same for drafter row h (residual only)
+  int resid;         // 1: residual [p~ - q]_+ at row h, 2: against stored
+                     // sparse Q, 0: bonus from p
+  float ep, isp;     // target row h: p(v) = exp2(x_v kp - ep) * isp, ep the
+                     // integer reference of the row maximum and isp = 1/S
+                     // (times the Cactus rescaling of the other tokens; 0
+                     // where the residual is known to vanish)
+  float C;           // residual: log2(q(v) / p~(v)) = (y_v kq - x_v kp) + C
   float u;           // resample uniform of row h
   int excl;          // Cactus: the drafted token of row h, whose weight is
   float wexcl;       // wexcl = [gamma - q(d)]_+; -1 for the linear rule
   int fixed;         // >= 0: the committed token is known (a coupled-noise
                      // commit) and nothing is drawn; -1 otherwise
+};
+
+// Softmax statistics partial of one piece of a sampling row: the running
+// maximum M and the sum S of exp2(x k - floor(M k)) in float64.
+struct Stat64 {
+  float M;
+  float pad;
+  double S;
 };
 
 // The stored sparse Q of the draw row h, handed from the mass kernel to the
@@ -237,7 +249,7 @@ struct SamplePlan {
   int64_t tiles;       // draw tiles per row
   int64_t tpc;         // draw tiles per mass-kernel group
   int64_t chunks;      // mass-kernel groups per sequence
-  size_t off_stats;    // float2 {M, S} per (slot, wave)
+  size_t off_stats;    // {M, float64 S} (16 bytes) per (slot, wave)
   size_t off_gpart;    // float2 {score, index-as-bits} per (slot, wave):
                        // Gumbel argmax partials of target rows
   size_t off_pre;      // int32 [B + 1]: first stream row of each sequence
@@ -255,7 +267,7 @@ inline SamplePlan plan_sample(int B, int K, int V, int64_t elem_bytes) {
   p.tpc = draw_tiles_per_chunk(B, V, elem_bytes);
   p.chunks = cdiv(p.tiles, p.tpc);
   p.off_stats = 0;
-  p.off_gpart = partial_bytes(p.max_vrows);
+  p.off_gpart = partial_bytes(p.max_vrows, 16);
   p.off_pre = p.off_gpart + partial_bytes(p.max_vrows);
   p.off_rec = p.off_pre + align256(static_cast<size_t>(B + 1) * 4);
   p.off_tmass = p.off_rec + align256(static_cast<size_t>(B) * sizeof(DrawRecord));

@@ -202,9 +202,9 @@ struct Quad<DT_F32> {
 // 16 bytes) and the Gumbel loads (16 bytes) are contiguous across the wave;
 // every lane keeps U steps in flight.  Rows whose logits and Gumbel values
 // cannot both be aligned are read element by element.
-template <int DT, int U>
+template <int DT, int U, class Stats>
 __device__ void stats_and_gumbel(const char* xr, const float* gr, int64_t v0, int64_t v1, float inv_t,
-                                 SoftmaxStats& st, ArgmaxPick& pk) {
+                                 Stats& st, ArgmaxPick& pk) {
   using E = Elem<DT>;
   using Q = Quad<DT>;
   constexpr int XB = 4 * E::kBytes;
@@ -215,15 +215,21 @@ __device__ void stats_and_gumbel(const char* xr, const float* gr, int64_t v0, in
     st.template absorb<1>(x);
     pk.group<1>(sc, j);
   };
-  auto use = [&](typename Q::raw xv, u32x4 g, int64_t idx) {
-    float x[4], sc[4];
-    Q::unpack(xv, x);
+  // The Gumbel scores of four elements go to the argmax; their logits stay
+  // in x for one absorb per U steps.
+  auto scores = [&](const float (&x)[4], u32x4 g, int64_t idx) {
+    float sc[4];
     sc[0] = __builtin_fmaf(x[0], inv_t, __uint_as_float(g.x));
     sc[1] = __builtin_fmaf(x[1], inv_t, __uint_as_float(g.y));
     sc[2] = __builtin_fmaf(x[2], inv_t, __uint_as_float(g.z));
     sc[3] = __builtin_fmaf(x[3], inv_t, __uint_as_float(g.w));
-    st.template absorb<4>(x);
     pk.group<4>(sc, idx);
+  };
+  auto use = [&](typename Q::raw xv, u32x4 g, int64_t idx) {
+    float x[4];
+    Q::unpack(xv, x);
+    scores(x, g, idx);
+    st.template absorb<4>(x);
   };
   if (v1 <= v0) return;
   const uintptr_t ag = reinterpret_cast<uintptr_t>(gr + v0);
@@ -250,8 +256,16 @@ __device__ void stats_and_gumbel(const char* xr, const float* gr, int64_t v0, in
       g[u] = load16(gb + k * 16);
     }
     __builtin_amdgcn_sched_barrier(0);
+    float xs[U * 4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) use(xv[u], g[u], a0 + (i + u * kBlock) * 4);
+    for (int u = 0; u < U; ++u) {
+      float x[4];
+      Q::unpack(xv[u], x);
+      scores(x, g[u], a0 + (i + u * kBlock) * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xs[u * 4 + j] = x[j];
+    }
+    st.template absorb<U * 4>(xs);
   }
   for (; i < nq; i += kBlock) use(Q::load(xb + i * XB), load16(gb + i * 16), a0 + i * 4);
   if (a1 + t < v1) one(a1 + t);
@@ -273,21 +287,29 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
   // With Gumbel rows, the parts of one target row that this group reads are
   // accumulated together and written once, at slot (first stream row of the
   // target row) + group.
-  SoftmaxStats acc(a.kp);
+  SoftmaxStats64 acc(a.kp);
   ArgmaxPick accp;
   int64_t pend = -1;
+  auto put = [&](int64_t slot, float M, double S) {
+    Stat64 st;
+    st.M = M;
+    st.pad = 0.f;
+    st.S = S;
+    a.stats[slot] = st;
+  };
   auto flush = [&]() {
-    float M = acc.M, S = acc.S;
-    wave_stats(M, S, a.kp);
+    float M = acc.M;
+    double S = static_cast<double>(acc.S);
+    wave_stats64(M, S, a.kp);
     float v = accp.best;
     int ii = static_cast<int>(accp.bidx);
     int nan = accp.nan ? 1 : 0;
     wave_argmax(v, ii, nan);
     if (lane_id() == 0) {
-      a.stats[(pend + g) * kWaves + wave_id()] = make_float2(M, S);
+      put((pend + g) * kWaves + wave_id(), M, S);
       a.gpart[(pend + g) * kWaves + wave_id()] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
     }
-    acc = SoftmaxStats(a.kp);
+    acc = SoftmaxStats64(a.kp);
     accp = ArgmaxPick();
     pend = -1;
   };
@@ -317,30 +339,46 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
       return;
     }
     if (GUM && pend >= 0) flush();
-    SoftmaxStats st(k);
+    SoftmaxStats64 st(k);
     stream_row<DT, kUnroll>(rowp, v0, v1, st);
-    float M = st.M, S = st.S;
-    wave_stats(M, S, k);
-    if (lane_id() == 0) a.stats[(r + g) * kWaves + wave_id()] = make_float2(M, S);
+    float M = st.M;
+    double S = static_cast<double>(st.S);
+    wave_stats64(M, S, k);
+    if (lane_id() == 0) put((r + g) * kWaves + wave_id(), M, S);
   });
   if (GUM && pend >= 0) flush();
 }
 
-// Per-element weight of the draw: residual [p~ - q]_+ or bonus exp2 weight.
-// For the linear rule p~ = p up to the (1 - lambda) factor, which the
-// normalisation removes; for the Cactus rule isp also carries the rescaling
-// (1 - gamma) / (1 - p(d)) of every token but the drafted one, element
-// `excl`, whose weight is wexcl = [gamma - q(d)]_+.
+// Per-element weight of the draw: residual [p~ - q]_+ or the bonus weight.
+// The bonus weight is exp2(x kp - ep), p up to the row normaliser.  The
+// residual is p (1 - 2^d) with d = log2(q/p) = (y kq - x kp) + C formed from
+// the logits directly (x kp split into an exact sum hx + lx), so the
+// normalisers never enter as two rounded scales whose difference would
+// dominate where p and q nearly cancel: what is left is the rounding of
+// 2^d, about one ulp of 1 times p per element, independent between
+// elements.  For the linear rule p~ = p up to the
+// (1 - lambda) factor, which the normalisation removes; for the Cactus rule
+// isp also carries the rescaling (1 - gamma) / (1 - p(d)) of every token but
+// the drafted one, element `excl`, whose weight is wexcl = [gamma - q(d)]_+.
 struct DrawWeight {
-  float kp, cp, isp, kq, cq, isq;
+  float kp, ep, isp, kq, C;
   int resid;
+  int same_t;   // kp == kq: y kq - x kp = (y - x) k, with y - x exact
   int excl;
   float wexcl;
   __device__ __forceinline__ float operator()(float x, float y) const {
-    const float ep = fast_exp2(__builtin_fmaf(x, kp, cp));
-    if (!resid) return ep;
-    const float eq = fast_exp2(__builtin_fmaf(y, kq, cq));
-    return fmaxf(ep * isp - eq * isq, 0.f);
+    const float e = fast_exp2(__builtin_fmaf(x, kp, -ep));
+    if (!resid) return e;
+    float d;
+    if (same_t) {
+      d = __builtin_fmaf(y - x, kp, C);
+    } else {
+      const float hx = x * kp;
+      const float lx = __builtin_fmaf(x, kp, -hx);
+      d = (__builtin_fmaf(y, kq, -hx) - lx) + C;
+    }
+    // d >= 0: q >= p; d NaN only where p = 0 (x = -inf)
+    return d < 0.f ? e * isp * (1.f - fast_exp2(d)) : 0.f;
   }
   // The weight of element e.
   __device__ __forceinline__ float at(uint32_t e, float x, float y) const {
@@ -387,7 +425,7 @@ __device__ float cactus_gamma(float p, float delta) {
   return fminf(p + x, 1.f);
 }
 
-constexpr int kTileBatch = 8;   // tiles a wave reads together (16 loads per lane)
+constexpr int kTileBatch = 4;   // tiles a wave reads together (8 loads per lane)
 
 // Masses of the draw row's tiles [t_lo, t_hi) (64 16-byte vectors each, of
 // the row and, for the residual, of drafter row yr), by the NW waves of the
@@ -430,7 +468,7 @@ __device__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo,
   const int wv = threadIdx.x >> 6;
   const uint32_t Vn = static_cast<uint32_t>(V);
   auto sparse_w = [&](float x, float q) {
-    return fmaxf(fast_exp2(__builtin_fmaf(x, w.kp, w.cp)) * w.isp - q, 0.f);
+    return fmaxf(fast_exp2(__builtin_fmaf(x, w.kp, -w.ep)) * w.isp - q, 0.f);
   };
   for (int t0 = t_lo + wv; t0 < t_hi; t0 += NW * TB) {
     u32x4 rx[TB], ry[TB];
@@ -477,6 +515,9 @@ __device__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo,
         for (int sh = 32; sh >= 1; sh >>= 1) m += wave_shfl_xor(m, sh);
         if (lane == 0) out[tile] = m;
       }
+      // One tile's weights at a time: interleaving the tiles' arithmetic
+      // only raises register pressure (the loads are already in flight).
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -510,15 +551,22 @@ __device__ __forceinline__ float group_exclusive_scan_f(float v, float& total, f
 // chain, and the token chain against stored sparse Q.
 enum : int { FAM_TOKEN = 0, FAM_SPOT = 1, FAM_SPARSE = 2 };
 
+// The probability of a logit x in a row with statistics (M, S) (float64 S
+// relative to the reference floor(M k)).
+__device__ __forceinline__ float prob64(float x, float k, float M, double S) {
+  return fast_exp2(__builtin_fmaf(x, k, -ref_exp(M, k))) * static_cast<float>(1.0 / S);
+}
+
 // LDS of the decision step (per sequence): row statistics of the target rows
 // 0..n and drafter rows 0..n-1, and d, p(d), p~(d), q(d) of the rejected
 // draft.
 struct DecideLds {
-  float Mp[kMaxDraft + 1], Sp[kMaxDraft + 1];
+  float Mp[kMaxDraft + 1];
+  double Sp[kMaxDraft + 1];
   // Drafter rows' statistics, or (stored sparse Q) each draft's token and
   // Q(d) summed from its row's entries.
   union { float Mq[kMaxDraft]; float qd[kMaxDraft]; };
-  union { float Sq[kMaxDraft]; int dtok[kMaxDraft]; };
+  union { double Sq[kMaxDraft]; int dtok[kMaxDraft]; };
   int g[kMaxDraft + 1];      // joint-space chain: Gumbel argmax of target rows
   int st, h;
   int dh, modeh;
@@ -605,9 +653,9 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
       first_slot = (v + glo) * kWaves;
       cnt = (ghi - glo + 1) * kWaves;
     };
-    combine_rows_stats<NT>(n + 1, a.stats, a.kp, tspan, [&](int r, float M, float S) {
+    combine_rows_stats64<NT>(n + 1, a.stats, a.kp, tspan, [&](int r, float M, double S) {
       s.Mp[r] = M; s.Sp[r] = S;
-      st |= stats_status(M, S);
+      st |= stats64_status(M, S);
     });
     if (P > 1)
       combine_rows_pick<NT>(n + 1, a.gpart, tspan, [&](int r, float v, int idx, int nan) {
@@ -615,16 +663,16 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
         st |= nan ? SEQ_NONFINITE : max_status(v);
       });
     if (a.drows)
-      combine_rows_stats<NT>(
+      combine_rows_stats64<NT>(
           n, a.stats, a.kq,
           [&](int r, int64_t& first_slot, int64_t& cnt) {
             split_row_slots(f, p0 + static_cast<int64_t>(P) * (n + 1) + r, first_slot, cnt);
             first_slot *= kWaves;
             cnt *= kWaves;
           },
-          [&](int r, float M, float S) {
+          [&](int r, float M, double S) {
             s.Mq[r] = M; s.Sq[r] = S;
-            st |= stats_status(M, S);
+            st |= stats64_status(M, S);
           });
   }
   if (sparse && !nbad) {
@@ -670,11 +718,13 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
         if (a.p_draft) a.p_draft[o] = 0.f;
         if (a.q_draft) a.q_draft[o] = 0.f;
         if (a.alpha) a.alpha[o] = 0.f;
+        if (a.accept_margin) a.accept_margin[o] = 0.f;
       }
       if (t == 0) {
         a.accept_len[b] = -1;
         a.num_out[b] = 0;
         if (a.residual_mass) a.residual_mass[b] = 0.f;
+        if (a.draw_margin) a.draw_margin[b] = 1.f;
         if (a.status) a.status[b] = s.st;
       }
     }
@@ -695,12 +745,13 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
     float p = 0.f, q = 0.f, pt = 0.f, al = 0.f;
     mk[k] = 0;
     if (i < n) {
-      p = fast_exp2(__builtin_fmaf(xi[k], a.kp, -s.Mp[i] * a.kp)) / s.Sp[i];
-      q = sparse ? s.qd[i] : fast_exp2(__builtin_fmaf(yi[k], a.kq, -s.Mq[i] * a.kq)) / s.Sq[i];
+      p = prob64(xi[k], a.kp, s.Mp[i], s.Sp[i]);
+      q = sparse ? s.qd[i] : prob64(yi[k], a.kq, s.Mq[i], s.Sq[i]);
       bool acc;
       if (spot) {
         const bool on = ppk[k] == psk[k];
-        mk[k] = (a.gumbel && 1.f / s.Sq[i] >= a.tau) ? 1 : 0;
+        // the drafter's confidence at s*: its largest token probability
+        mk[k] = (a.gumbel && prob64(s.Mq[i], a.kq, s.Mq[i], s.Sq[i]) >= a.tau) ? 1 : 0;
         q *= ck[k];
         pt = p;
         if (mk[k]) {
@@ -727,6 +778,7 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
       if (a.p_draft) a.p_draft[o] = p;
       if (a.q_draft) a.q_draft[o] = q;
       if (a.alpha) a.alpha[o] = al;
+      if (a.accept_margin) a.accept_margin[o] = i < n ? (mk[k] ? 1.f : fabsf(ui[k] - al)) : 0.f;
     }
   }
   __syncthreads();
@@ -750,17 +802,32 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
   rec.status = s.st;
   rec.h = h;
   rec.resid = resid ? (sparse ? 2 : 1) : 0;
-  rec.cp = -s.Mp[h] * a.kp;
-  rec.isp = 1.f / s.Sp[h];
-  rec.cq = resid && !sparse ? -s.Mq[h] * a.kq : 0.f;
-  rec.isq = resid && !sparse ? 1.f / s.Sq[h] : 1.f;
+  rec.ep = ref_exp(s.Mp[h], a.kp);
+  rec.isp = static_cast<float>(1.0 / s.Sp[h]);
+  // log2(q(v) / p(v)) = (y_v kq - x_v kp) + C: the integer references and
+  // the float64 sums leave C small where p and q are close, so the residual
+  // weights keep their relative precision there.
+  // C = log2(Sp 2^ep / (Sq 2^eq)), the log-partition difference of the two
+  // rows, from the ratio formed in float64 (exact power-of-two scaling):
+  // near 1 through its distance from 1 (so C keeps relative precision where
+  // it is small), elsewhere through mantissa and exponent.
+  float Cf = 0.f;
+  if (resid && !sparse) {
+    const double ratio = __builtin_ldexp(s.Sp[h] / s.Sq[h], static_cast<int>(rec.ep - ref_exp(s.Mq[h], a.kq)));
+    if (fabs(ratio - 1.0) < 0.25) {
+      Cf = log1pf(static_cast<float>(ratio - 1.0)) * kLog2e;
+    } else {
+      int ex;
+      const double m = frexp(ratio, &ex);   // ratio = m 2^ex, m in [0.5, 1)
+      Cf = static_cast<float>(ex) + log2f(static_cast<float>(m));
+    }
+  }
   rec.u = a.u_resample[static_cast<int64_t>(b) * (a.K + 1) + h];
   if (resid && a.rule == RULE_LINEAR && !(a.lam < 1.f)) {
     // lambda = 1: p~ = q, so [p~ - q]_+ = (1 - lambda) [p - q]_+ vanishes
     // (a draft is rejected only where q(d) = 0); the draw then falls back to
     // p like any residual of zero mass.
     rec.isp = 0.f;
-    rec.isq = 0.f;
   }
   rec.excl = -1;
   rec.wexcl = 0.f;
@@ -772,7 +839,7 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
       rec.fixed = s.g[h];
       rec.resid = 0;
     } else if (resid) {
-      rec.isq *= s.ch;   // residual [p - c qhat]_+
+      Cf += log2f(s.ch);   // residual [p - c qhat]_+
     }
   }
   if (resid && a.rule == RULE_CACTUS) {
@@ -782,17 +849,20 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
                                                        (1.0 - static_cast<double>(ph)))
                                   : 0.f;
     rec.isp *= c_rest;
+    Cf -= log2f(c_rest);   // residual [c_rest p - q]_+
     rec.excl = s.dh;
     rec.wexcl = fmaxf(s.pth - s.qh, 0.f);
   }
+  rec.C = Cf;
   return rec;
 }
 
 __device__ __forceinline__ DrawWeight draw_weight(const SampleArgs& a, const DrawRecord& r) {
   DrawWeight w;
-  w.kp = a.kp; w.cp = r.cp; w.isp = r.isp;
-  w.kq = a.kq; w.cq = r.cq; w.isq = r.isq;
+  w.kp = a.kp; w.ep = r.ep; w.isp = r.isp;
+  w.kq = a.kq; w.C = r.C;
   w.resid = r.resid;
+  w.same_t = a.kp == a.kq;
   w.excl = r.excl;
   w.wexcl = r.wexcl;
   return w;
@@ -863,7 +933,7 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
       return;
     }
   }
-  tile_masses<DT, kWaves>(xr, yr, a.V, t_lo, t_hi, vec, w, out);
+  tile_masses<DT, kWaves, 4>(xr, yr, a.V, t_lo, t_hi, vec, w, out);
 }
 
 constexpr int kDrawWaves = kDrawThreads / 64;
@@ -876,7 +946,7 @@ struct SelectLdsT {
   static constexpr int kTiles = TPT;
   float tile[NT * TPT];
   float w[NT / 64];
-  float Z, base;
+  float Z, base, margin;
   int ct, lt, cs, pick, a;
 };
 using SelectLds = SelectLdsT<kDrawThreads, kDrawTilesPerThread>;
@@ -1017,7 +1087,7 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
 #pragma unroll
       for (int j = 0; j < E::kVec; ++j)
         wt[j] = e0 + j < a.V
-                    ? fmaxf(fast_exp2(__builtin_fmaf(E::load1(xr, e0 + j), w.kp, w.cp)) * w.isp - q[j], 0.f)
+                    ? fmaxf(fast_exp2(__builtin_fmaf(E::load1(xr, e0 + j), w.kp, -w.ep)) * w.isp - q[j], 0.f)
                     : 0.f;
     } else {
 #pragma unroll
@@ -1037,20 +1107,34 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
     const float start = s.base + inc - loc;
     int found = -1, lastpos = -1;
     float r = start;
+    float gap = 0.f;   // distance of u*Z from the nearer end of the found token's interval
 #pragma unroll
     for (int j = 0; j < E::kVec; ++j) {
+      const float before = r;
       r += wt[j];
       if (wt[j] > 0.f) {
-        if (found < 0 && r > target) found = static_cast<int>(e0 + j);
+        if (found < 0 && r > target) {
+          found = static_cast<int>(e0 + j);
+          gap = fminf(target - before, r - target);
+        }
         lastpos = static_cast<int>(e0 + j);
       }
     }
     const uint64_t hits = __ballot(found >= 0);
     const uint64_t poss = __ballot(lastpos >= 0);
     int tok = -1;
-    if (hits) tok = __shfl(found, __builtin_ctzll(hits), 64);
-    else if (poss) tok = __shfl(lastpos, 63 - __builtin_clzll(poss), 64);
-    if (lane == 0) s.pick = tok;
+    float mg = 0.f;
+    if (hits) {
+      const int src = __builtin_ctzll(hits);
+      tok = __shfl(found, src, 64);
+      mg = __shfl(gap, src, 64);
+    } else if (poss) {
+      tok = __shfl(lastpos, 63 - __builtin_clzll(poss), 64);
+    }
+    if (lane == 0) {
+      s.pick = tok;
+      s.margin = s.Z > 0.f ? fmaxf(mg, 0.f) / s.Z : 0.f;
+    }
   }
   // ---- output assembly: C = (d_1..d_h, c), then the ending condition ----
   const int A = h + 1;
@@ -1078,6 +1162,7 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
     a.num_out[b] = an;
     // Mass of [p~ - q]_+ = (1 - lambda) [p - q]_+: the rejection probability.
     if (a.residual_mass) a.residual_mass[b] = Zres * (1.f - a.lam);
+    if (a.draw_margin) a.draw_margin[b] = draw ? s.margin : 1.f;
     if (a.status) a.status[b] = status;
   }
 }
@@ -1144,7 +1229,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_fused(SampleArgs a) {
   draw_rows<DT>(a, b, rec.h, rec.resid != 0, xr, yr);
   const bool vec = ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0;
   const int ntiles = a.tiles;
-  if (rec.fixed < 0) tile_masses<DT, kDrawWaves, 8>(xr, yr, a.V, 0, ntiles, vec, draw_weight(a, rec), s.tile);
+  if (rec.fixed < 0) tile_masses<DT, kDrawWaves, 4>(xr, yr, a.V, 0, ntiles, vec, draw_weight(a, rec), s.tile);
   __syncthreads();
   const int q = static_cast<int>(cdiv(ntiles, kDrawThreads));
   float m0[kDrawTilesPerThread];

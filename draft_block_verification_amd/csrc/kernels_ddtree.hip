@@ -906,8 +906,8 @@ bool launch_dd_hypotheses(const DDHypArgs& a, int dtype, hipStream_t stream, con
                 cdiv(static_cast<int64_t>(a.B) * a.L, kWaves), stream, b);
 }
 
-bool launch_dd_tree(const DDTreeArgs& a, hipStream_t stream) {
-  return launch_threads(fn(k_dd_tree), a.B, kDDThreads, stream, a);
+bool launch_dd_tree(const DDTreeArgs& a, hipStream_t stream, const TimingEvents& ev) {
+  return launch_threads(fn(k_dd_tree), a.B, kDDThreads, stream, a, ev);
 }
 
 }  // namespace dbv

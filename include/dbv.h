@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define DBV_ABI_VERSION 1
+#define DBV_ABI_VERSION 2
 
 typedef enum {
   DBV_OK = 0,
@@ -107,6 +107,67 @@ typedef enum {
 } dbv_kind;
 
 /*
+ * dbv_options -- optional per-call settings and diagnostic outputs.  Every
+ * entry point that launches kernels takes `const dbv_options* opts` as its
+ * last argument; NULL means no options.  The library reads the struct during
+ * the call and keeps nothing from it (nor any pointer in it) afterwards, so
+ * calls on different streams or threads stay independent.  Set `size` to
+ * sizeof(dbv_options) and every field the call does not use to 0 / NULL; a
+ * diagnostic output that the entry point does not produce is
+ * DBV_ERR_INVALID_ARG.
+ *
+ *   max_groups  an upper bound on the workgroups of the row-streaming kernel
+ *       (0: the library's choice, 4 per compute unit), e.g. to leave compute
+ *       units to concurrent work.  Every output is the same for any value, up
+ *       to decisions whose float64 margin is below 1e-5 (the float32
+ *       reductions are grouped differently).
+ *   row_begin, row_end  hipEvent_t handles created with timing enabled (both
+ *       or neither).  The call launches its row-streaming kernel (the launch
+ *       that reads the logit rows: row statistics / argmax, the tree's
+ *       confidences, the truncation pass, the hypotheses' row pass, or the
+ *       DDTree search kernel) through hipExtLaunchKernel with these events,
+ *       which the runtime stamps at that kernel's own start and end, so
+ *       hipEventElapsedTime gives its duration without launch gaps.  A call
+ *       with no rows to read records both events back to back.
+ *   Chain sampling calls (verify_rejection, verify_lenient, verify_cactus,
+ *   verify_sparse, verify_spot_chain), the per-decision margins of
+ *   [SPOT] App. B.4's implementation check and [TT] Sec. 2:
+ *   accept_margin [B, K] float32: |u_accept - alpha| of each draft i < n_b
+ *       (the distance of the accept test from flipping), 0 past n_b; a
+ *       coupled-noise match link reports 1.
+ *   draw_margin [B] float32: for a drawn correction or bonus token c, the
+ *       distance of u * Z from the nearer end of c's interval
+ *       [F(c-1), F(c)) of the running mass, over Z; 1 where the committed
+ *       token was not drawn (a Gumbel argmax) and for sequences in error.
+ *   row_tv [B, K] float32: TV(p_i, q_i) = 1/2 sum_v |p_i(v) - q_i(v)| of
+ *       each draft row i < n_b (target and drafter at their temperatures;
+ *       [TT] Sec. 2 Eq. 1-2: the lossless acceptance rate of row i is
+ *       1 - TV), 0 past n_b.  Diagnostic mode: one more pass over the draft
+ *       block's target and drafter rows.  verify_sparse: TV against the
+ *       stored Q; verify_spot_chain: TV of the token rows, p against qhat.
+ *   verify_gumbel_tree:
+ *   pos_margin [B, S] float32: relative gap (c1 - c2) / c1 of the two largest
+ *       confidences over the masked positions of each state (1 with one
+ *       masked position; 0 for terminal and unused states and in
+ *       FIXED_POSITION mode).
+ *   tok_margin [B, S] float32: the gap between the two largest scores
+ *       z_v / T + G[s*, v] (T > 0) or logits (T = 0) at s*: the margin of the
+ *       coupled transition's token (0 for terminal and unused states).
+ *       Tracking the runner-up score costs one more compare per element.
+ */
+typedef struct dbv_options {
+  uint32_t size;
+  uint32_t max_groups;
+  void* row_begin;
+  void* row_end;
+  float* accept_margin;
+  float* draw_margin;
+  float* row_tv;
+  float* pos_margin;
+  float* tok_margin;
+} dbv_options;
+
+/*
  * verify_greedy -- temperature-0 verification plus next-draft retention.
  * [PSS] Sec. 3.1 Eq. 1-4 and Algorithm 1:
  *   v_i = argmax of target row i-1 for i = 1..n_b+1            (Eq. 1)
@@ -137,7 +198,8 @@ dbv_status verify_greedy(int B, int K, int V, dbv_dtype dtype,
                          int W, int32_t eos_id, const int32_t* len_budget,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
                          int32_t* next_draft, int32_t* next_len, int32_t* status,
-                         void* ws, size_t ws_bytes, void* stream);
+                         void* ws, size_t ws_bytes, void* stream,
+                         const dbv_options* opts);
 
 /*
  * verify_rejection -- lossless speculative-sampling verification.
@@ -167,7 +229,8 @@ dbv_status verify_rejection(int B, int K, int V, dbv_dtype dtype,
                             int32_t eos_id, const int32_t* len_budget,
                             int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
                             float* p_draft, float* q_draft, float* alpha, float* residual_mass,
-                            int32_t* status, void* ws, size_t ws_bytes, void* stream);
+                            int32_t* status, void* ws, size_t ws_bytes, void* stream,
+                            const dbv_options* opts);
 
 /*
  * verify_lenient -- the linear lenient rule of [TT] Theorem 1 (Eq. 5) used in
@@ -190,7 +253,8 @@ dbv_status verify_lenient(int B, int K, int V, dbv_dtype dtype,
                           int32_t eos_id, const int32_t* len_budget,
                           int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
                           float* p_draft, float* q_draft, float* alpha, float* residual_mass,
-                          int32_t* status, void* ws, size_t ws_bytes, void* stream);
+                          int32_t* status, void* ws, size_t ws_bytes, void* stream,
+                          const dbv_options* opts);
 
 /*
  * verify_cactus -- the modified Cactus rule of [TT] App. E: the target is
@@ -215,7 +279,8 @@ dbv_status verify_cactus(int B, int K, int V, dbv_dtype dtype,
                          int32_t eos_id, const int32_t* len_budget,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
                          float* p_draft, float* q_draft, float* alpha, float* residual_mass,
-                         int32_t* status, void* ws, size_t ws_bytes, void* stream);
+                         int32_t* status, void* ws, size_t ws_bytes, void* stream,
+                         const dbv_options* opts);
 
 /*
  * verify_sparse -- lossless verification against stored sparse drafter
@@ -243,7 +308,8 @@ dbv_status verify_sparse(int B, int K, int V, dbv_dtype dtype,
                          int32_t eos_id, const int32_t* len_budget,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
                          float* p_draft, float* q_draft, float* alpha, float* residual_mass,
-                         int32_t* status, void* ws, size_t ws_bytes, void* stream);
+                         int32_t* status, void* ws, size_t ws_bytes, void* stream,
+                         const dbv_options* opts);
 
 /*
  * truncate_top_k_top_p -- stores drafter distributions in the sparse form
@@ -265,7 +331,8 @@ dbv_status verify_sparse(int B, int K, int V, dbv_dtype dtype,
 dbv_status truncate_top_k_top_p(int B, int K, int V, dbv_dtype dtype,
                                 const void* rows, int64_t seq_stride, int64_t row_stride,
                                 const int32_t* lengths, float temperature, int top_k, float top_p,
-                                int kmax, int32_t* q_idx, float* q_prob, int32_t* q_nnz, void* stream);
+                                int kmax, int32_t* q_idx, float* q_prob, int32_t* q_nnz, void* stream,
+                                const dbv_options* opts);
 
 /*
  * verify_spot_chain -- chain verification on the joint (position, token)
@@ -313,7 +380,8 @@ dbv_status verify_spot_chain(int B, int K, int V, dbv_dtype dtype,
                              int32_t eos_id, const int32_t* len_budget,
                              int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
                              float* p_draft, float* q_draft, float* alpha, float* residual_mass,
-                             int32_t* status, void* ws, size_t ws_bytes, void* stream);
+                             int32_t* status, void* ws, size_t ws_bytes, void* stream,
+                             const dbv_options* opts);
 
 /*
  * verify_greedy_any_order -- one any-order greedy verification call
@@ -358,7 +426,8 @@ dbv_status verify_greedy_any_order(int B, int U, int V, dbv_dtype dtype,
                                    int32_t* accept_len, int32_t* num_accepted,
                                    int32_t* acc_pos, int32_t* acc_tok, int32_t* new_end,
                                    int32_t* next_draft, int32_t* status,
-                                   void* ws, size_t ws_bytes, void* stream);
+                                   void* ws, size_t ws_bytes, void* stream,
+                                   const dbv_options* opts);
 
 /*
  * verify_gumbel_tree -- state-equality verification of one draft tree per
@@ -403,7 +472,8 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype,
                               int32_t* sel_pos, int32_t* sel_tok, float* sel_conf,
                               int32_t* path_len, int32_t* path_nodes,
                               int32_t* commit_pos, int32_t* commit_tok, int32_t* num_commits,
-                              int32_t* status, void* ws, size_t ws_bytes, void* stream);
+                              int32_t* status, void* ws, size_t ws_bytes, void* stream,
+                              const dbv_options* opts);
 
 /*
  * ddtree_hypotheses -- token hypotheses of the masked positions for draft-
@@ -431,7 +501,8 @@ dbv_status ddtree_hypotheses(int B, int L, int V, dbv_dtype dtype,
                              int64_t g_seq_stride, int64_t g_pos_stride,
                              float temperature, float runner_up_below,
                              int32_t* hyp_tok, float* hyp_prob, int32_t* status,
-                             void* ws, size_t ws_bytes, void* stream);
+                             void* ws, size_t ws_bytes, void* stream,
+                             const dbv_options* opts);
 
 /*
  * ddtree_level -- one level of the DDTree search ([SPOT] Sec. 4.2 Eq. 3 and
@@ -474,7 +545,8 @@ dbv_status ddtree_level(int B, int L, int D, const uint8_t* masked,
                         float tau, float gamma, int first,
                         int32_t* parent, int32_t* edge_pos, int32_t* edge_tok, float* mass,
                         uint8_t* node_masked, int32_t* num_nodes, int32_t* frontier,
-                        int32_t* num_frontier, int32_t* status, void* ws, size_t ws_bytes, void* stream);
+                        int32_t* num_frontier, int32_t* status, void* ws, size_t ws_bytes, void* stream,
+                        const dbv_options* opts);
 
 /*
  * ddtree_build -- the whole DDTree search in one call with a first-order
@@ -491,7 +563,8 @@ dbv_status ddtree_build(int B, int L, int D, const uint8_t* masked,
                         float tau, float gamma,
                         int32_t* parent, int32_t* edge_pos, int32_t* edge_tok, float* mass,
                         uint8_t* node_masked, int32_t* num_nodes, int32_t* frontier,
-                        int32_t* num_frontier, int32_t* status, void* ws, size_t ws_bytes, void* stream);
+                        int32_t* num_frontier, int32_t* status, void* ws, size_t ws_bytes, void* stream,
+                        const dbv_options* opts);
 
 /*
  * verify_workspace_size -- bytes of scratch one call of `kind` needs.
@@ -504,19 +577,6 @@ dbv_status ddtree_build(int B, int L, int D, const uint8_t* masked,
  * Returns 0 for invalid sizes.  Depends only on its arguments.
  */
 size_t verify_workspace_size(dbv_kind kind, int B, int K_or_S, int L, int V, dbv_dtype dtype);
-
-/*
- * verify_set_timing_events -- diagnostics hook.  With two non-NULL hipEvent_t
- * handles (created with timing enabled), every later verify_* call launches
- * its row-streaming kernel (the launch that reads the logit rows: row
- * statistics / argmax, or the tree's per-row confidences) through
- * hipExtLaunchKernel with these events, which the runtime stamps at that
- * kernel's own start and end; hipEventElapsedTime then gives its duration
- * without the launch gap.  If the kernel has no rows to read, both events are
- * recorded back to back.  (NULL, NULL) turns it off.  A process-wide setting
- * for benchmarking; not meant for concurrent calls.
- */
-void verify_set_timing_events(void* begin, void* end);
 
 /* Static text for a dbv_status (never NULL). */
 const char* verify_status_string(dbv_status s);

@@ -27,3 +27,21 @@ def dev():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     return torch.device("cuda:0")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Write the near-margin counts the parity checkers gathered (per
+    workload and decision kind) to the file DBV_PARITY_REPORT names."""
+    path = os.environ.get("DBV_PARITY_REPORT")
+    if not path:
+        return
+    try:
+        from tests.parity import REPORT
+    except Exception:  # pragma: no cover
+        return
+    if not REPORT:
+        return
+    import json
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as fh:
+        json.dump({k: dict(v) for k, v in sorted(REPORT.items())}, fh, indent=1, sort_keys=True)

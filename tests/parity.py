@@ -22,6 +22,31 @@ from oracle import NEAR_MARGIN
 PROB_RTOL = {"float32": 1e-5, "bfloat16": 2e-3}
 
 
+# Near-margin counts per workload and decision kind, gathered over a test
+# session (written out by tests/conftest.py when DBV_PARITY_REPORT names a
+# file).
+REPORT = {}
+
+
+def record(config, counts):
+    """Add one checker's counts (a Counter: "sequences" compared, decisions
+    per kind, those whose oracle margin is below NEAR_MARGIN ("_near") and
+    those the GPU took the other way ("_flip")) to the session report; keys
+    starting with "max_" keep the largest value seen."""
+    e = REPORT.setdefault(config, {})
+    for k, v in counts.items():
+        if k.startswith("max_"):
+            e[k] = max(e.get(k, 0.0), float(v))
+        else:
+            e[k] = e.get(k, 0) + v
+    return counts
+
+
+def _relerr(a, b):
+    m = max(abs(a), abs(b))
+    return abs(a - b) / m if m > 0 else 0.0
+
+
 def np64(t):
     return t.detach().float().cpu().numpy().astype(np.float64) if hasattr(t, "detach") else np.asarray(t, np.float64)
 
@@ -34,11 +59,15 @@ def _rel_ok(a, b, rtol, atol=1e-30):
     return abs(a - b) <= rtol * max(abs(a), abs(b)) + atol
 
 
-# Residual mass Z = sum_v [p~_v - q_v]_+ in float32: each term is a difference
-# of two probabilities that carry up to about 4 ulp each (exp2, the 1/S
-# scale, the lambda / c mix), so where p and q nearly cancel the error is
-# absolute, up to 4 eps (sum p + sum q) = 8 eps = 9.5e-7, not relative to Z.
-Z_ATOL = 8 * 2.0 ** -23
+# Residual mass Z = sum_v [p~_v - q_v]_+ = 1 - sum_v min(p~_v, q_v): the GPU
+# forms each term as p (1 - q/p) with log2(q/p) taken from the logits and
+# float64 row normalisers, so every term keeps float32 relative precision
+# even where p and q nearly cancel.  What remains is the float32 evaluation
+# of the two rows' exp2 terms (about one ulp each, independent between the
+# rows), which leaves Z off by a fraction of an ulp of the row mass 1: Z is
+# held to the probability tolerance relative to itself plus half an ulp of
+# 1, the float32 resolution of a probability of order one.
+Z_ATOL = 2.0 ** -24
 
 
 def check_greedy(g, o):
@@ -85,7 +114,8 @@ def check_sampling(g, x, o, lam, t_target, t_draft, dtype_name, eos_id=-1, len_b
         assert (sg & oracle.STATUS_ERROR_MASK) == (so & oracle.STATUS_ERROR_MASK), (b, sg, so)
         assert (sg & oracle.STATUS_Q_ZERO) == (so & oracle.STATUS_Q_ZERO), (b, sg, so)
         if (sg ^ so) & oracle.STATUS_Z_ZERO:
-            near["z_zero"] += 1
+            near["z_zero_flip"] += 1
+        near["sequences"] += 1
         if so & oracle.STATUS_ERROR_MASK:
             assert acc_g[b] == -1 and num_g[b] == 0 and (out_g[b] == -1).all(), b
             continue
@@ -95,17 +125,24 @@ def check_sampling(g, x, o, lam, t_target, t_draft, dtype_name, eos_id=-1, len_b
             assert _rel_ok(pd_g[b, i], o["p_draft"][j, i], rtol), ("p", b, i, pd_g[b, i], o["p_draft"][j, i])
             assert _rel_ok(qd_g[b, i], o["q_draft"][j, i], rtol), ("q", b, i, qd_g[b, i], o["q_draft"][j, i])
             assert _rel_ok(al_g[b, i], o["alpha"][j, i], rtol), ("alpha", b, i)
+            near["max_prob_relerr"] = max(near["max_prob_relerr"], _relerr(pd_g[b, i], o["p_draft"][j, i]),
+                                          _relerr(qd_g[b, i], o["q_draft"][j, i]),
+                                          _relerr(al_g[b, i], o["alpha"][j, i]))
         for i in range(n, K):
             assert pd_g[b, i] == 0 and qd_g[b, i] == 0 and al_g[b, i] == 0
         h = int(acc_g[b])
         assert 0 <= h <= n, (b, h, n)
+        for i in range(min(h + 1, n)):   # the tests the GPU decided: accepts i < h, the reject at h
+            near["accept_tests"] += 1
+            if o["accept_margin"][j, i] < NEAR_MARGIN:
+                near["accept_near"] += 1
         for i in range(h):           # GPU accepted draft i
             if not o["accept_bits"][j, i]:
                 assert o["accept_margin"][j, i] < NEAR_MARGIN, ("accept", b, i, o["accept_margin"][j, i])
-                near["accept"] += 1
+                near["accept_flip"] += 1
         if h < n and o["accept_bits"][j, h]:   # GPU rejected draft h
             assert o["accept_margin"][j, h] < NEAR_MARGIN, ("reject", b, h, o["accept_margin"][j, h])
-            near["accept"] += 1
+            near["accept_flip"] += 1
         # The draw at the GPU's row h.
         p = oracle.tempered_softmax(x["tgt"][b, h], t_target)
         if h < n:
@@ -121,6 +158,9 @@ def check_sampling(g, x, o, lam, t_target, t_draft, dtype_name, eos_id=-1, len_b
             w, Zr = p, 0.0
         u = float(x["u_resample"][b, h])
         c_o, margin, Z = oracle.inverse_cdf(w, u)
+        near["draws"] += 1
+        near["draw_near"] += int(margin < NEAR_MARGIN)
+        near["draw_below_4e-4"] += int(margin < 4e-4)
         if num_g[b] > h:
             c_g = int(out_g[b, h])
             if c_g != c_o:
@@ -128,7 +168,7 @@ def check_sampling(g, x, o, lam, t_target, t_draft, dtype_name, eos_id=-1, len_b
                 lo = F[c_g - 1] if c_g > 0 else 0.0
                 ok = (0 <= c_g < len(w) and w[c_g] > 0 and lo - NEAR_MARGIN * Z <= u * Z < F[c_g] + NEAR_MARGIN * Z)
                 assert ok and margin < NEAR_MARGIN, ("draw", b, h, c_g, c_o, margin)
-                near["draw"] += 1
+                near["draw_flip"] += 1
         else:
             c_g = c_o
         C = d[:h] + [c_g]
@@ -139,7 +179,8 @@ def check_sampling(g, x, o, lam, t_target, t_draft, dtype_name, eos_id=-1, len_b
         exp[:a] = C[:a]
         np.testing.assert_array_equal(out_g[b], exp, err_msg=f"out_tokens seq {b}")
         if h < n:
-            assert _rel_ok(rm_g[b], Zr, max(rtol, 1e-4), Z_ATOL), ("Z", b, rm_g[b], Zr)
+            assert _rel_ok(rm_g[b], Zr, rtol, Z_ATOL), ("Z", b, rm_g[b], Zr)
+            near["max_z_relerr"] = max(near["max_z_relerr"], _relerr(rm_g[b], Zr))
         else:
             assert rm_g[b] == 0.0
         if h == o["accept_len"][j] and c_g == c_o:
@@ -163,6 +204,7 @@ def check_tree(g, x, o, dtype_name, temperature, seqs=None):
         b = j if seqs is None else seqs[j]
         so, sg = int(o["status"][j]), int(st_g[b])
         assert sg == so, (b, sg, so)
+        near["sequences"] += 1
         if so & oracle.STATUS_ERROR_MASK:
             assert pl_g[b] == -1 and nc_g[b] == 0
             continue
@@ -171,23 +213,30 @@ def check_tree(g, x, o, dtype_name, temperature, seqs=None):
         for y in range(ns):
             po, to = int(o["sel_pos"][j, y]), int(o["sel_tok"][j, y])
             pg, tg = int(sp_g[b, y]), int(stk_g[b, y])
+            if po >= 0:
+                near["states"] += 1
+                near["pos_near"] += int(o["pos_margin"][j, y] < NEAR_MARGIN)
             if pg != po:
                 assert o["pos_margin"][j, y] < NEAR_MARGIN, ("s*", b, y, pg, po)
                 rows = x["logits"][b, y]
                 cg = oracle.rows.max_probability(rows[pg])
                 assert cg >= o["sel_conf"][j, y] * (1 - NEAR_MARGIN), ("s* bracket", b, y)
-                near["pos"] += 1
+                near["pos_flip"] += 1
                 t2 = oracle.state_transition(rows, None, None if x.get("gumbel") is None else x["gumbel"][b],
                                              temperature, fixed_pos=pg)
                 to = t2["tok"]
                 tmargin = t2["tok_margin"]
             else:
                 tmargin = o["tok_margin"][j, y]
+            if pg >= 0:
+                near["tok_near"] += int(tmargin < NEAR_MARGIN)
             if tg != to:
                 assert tmargin < NEAR_MARGIN, ("tok", b, y, tg, to, tmargin)
-                near["tok"] += 1
+                near["tok_flip"] += 1
             if pg >= 0:
-                assert _rel_ok(sc_g[b, y], oracle.rows.max_probability(x["logits"][b, y, pg]), rtol), ("conf", b, y)
+                c_o = oracle.rows.max_probability(x["logits"][b, y, pg])
+                assert _rel_ok(sc_g[b, y], c_o, rtol), ("conf", b, y)
+                near["max_conf_relerr"] = max(near["max_conf_relerr"], _relerr(sc_g[b, y], c_o))
             pos.append(pg)
             tok.append(tg)
         for y in range(ns, S):
@@ -212,9 +261,9 @@ def check_tree(g, x, o, dtype_name, temperature, seqs=None):
 def check_spot(g, x, o, t_target, t_draft, tau, dtype_name, eos_id=-1, len_budget=None, seqs=None):
     """Joint-space chain outputs (rejection sampling and the gated hybrid)
     against the oracle, with margin accounting as check_sampling.  A link
-    whose drafter confidence lies within the probability tolerance of tau
-    may take the other verifier on the GPU: such a sequence is counted as
-    near-margin and its downstream outputs are not compared.
+    whose drafter confidence lies within NEAR_MARGIN of tau may take the
+    other verifier on the GPU: such a sequence is counted as near-margin
+    ("gate") and its downstream outputs are not compared.
 
     x: inputs as float64 / int64 numpy (tgt, drf, pos_star, prop_pos,
     prop_tok, q_pos_star, draft_len, u_accept, u_resample, gumbel or None).
@@ -233,7 +282,8 @@ def check_spot(g, x, o, t_target, t_draft, tau, dtype_name, eos_id=-1, len_budge
         assert (sg & oracle.STATUS_ERROR_MASK) == (so & oracle.STATUS_ERROR_MASK), (b, sg, so)
         assert (sg & oracle.STATUS_Q_ZERO) == (so & oracle.STATUS_Q_ZERO), (b, sg, so)
         if (sg ^ so) & oracle.STATUS_Z_ZERO:
-            near["z_zero"] += 1
+            near["z_zero_flip"] += 1
+        near["sequences"] += 1
         if so & oracle.STATUS_ERROR_MASK:
             assert acc_g[b] == -1 and num_g[b] == 0 and (out_g[b] == -1).all(), b
             continue
@@ -246,21 +296,29 @@ def check_spot(g, x, o, t_target, t_draft, tau, dtype_name, eos_id=-1, len_budge
             assert pd_g[b, i] == 0 and qd_g[b, i] == 0 and al_g[b, i] == 0
         h = int(acc_g[b])
         assert 0 <= h <= n, (b, h, n)
-        if (o["gate_margin"][j, :min(h + 1, n)] < rtol).any():
-            near["gate"] += 1
+        # The gate compares the drafter's float32 confidence 1/S with tau; its
+        # error is ~1e-6, so only a gate within NEAR_MARGIN of tau may take
+        # the other verifier.  Such a sequence is counted and not compared
+        # further (its downstream law differs by construction).
+        near["gates"] += min(h + 1, n)
+        if (o["gate_margin"][j, :min(h + 1, n)] < NEAR_MARGIN).any():
+            near["gate_near"] += 1
             continue
         for i in range(n):
             if o["mode"][j, i] == oracle.MODE_RS:
                 assert _rel_ok(al_g[b, i], o["alpha"][j, i], rtol), ("alpha", b, i)
             elif al_g[b, i] != o["alpha"][j, i]:
                 assert o["accept_margin"][j, i] < NEAR_MARGIN, ("match alpha", b, i)
+        for i in range(min(h + 1, n)):
+            near["accept_tests"] += 1
+            near["accept_near"] += int(o["accept_margin"][j, i] < NEAR_MARGIN)
         for i in range(h):
             if not o["accept_bits"][j, i]:
                 assert o["accept_margin"][j, i] < NEAR_MARGIN, ("accept", b, i, o["accept_margin"][j, i])
-                near["accept"] += 1
+                near["accept_flip"] += 1
         if h < n and o["accept_bits"][j, h]:
             assert o["accept_margin"][j, h] < NEAR_MARGIN, ("reject", b, h, o["accept_margin"][j, h])
-            near["accept"] += 1
+            near["accept_flip"] += 1
         # The commit at the GPU's row h.
         p = oracle.tempered_softmax(x["tgt"][b, h], t_target)
         Zr = 0.0
@@ -285,11 +343,13 @@ def check_spot(g, x, o, t_target, t_draft, tau, dtype_name, eos_id=-1, len_budge
             top = np.sort(sc)
             margin = float(top[-1] - top[-2]) if len(top) > 1 else np.inf
             bracket = lambda c_g: sc[c_g] >= top[-1] - NEAR_MARGIN  # noqa: E731
+        near["draws"] += 1
+        near["draw_near"] += int(margin < NEAR_MARGIN)
         if num_g[b] > h:
             c_g = int(out_g[b, h])
             if c_g != c_o:
                 assert bracket(c_g) and margin < NEAR_MARGIN, ("commit", b, h, c_g, c_o, margin)
-                near["draw"] += 1
+                near["draw_flip"] += 1
         else:
             c_g = c_o
         C = d[:h] + [c_g]
@@ -299,7 +359,9 @@ def check_spot(g, x, o, t_target, t_draft, tau, dtype_name, eos_id=-1, len_budge
         exp = np.full(K + 1, -1)
         exp[:a] = C[:a]
         np.testing.assert_array_equal(out_g[b], exp, err_msg=f"out_tokens seq {b}")
-        assert _rel_ok(rm_g[b], Zr, max(rtol, 1e-4), Z_ATOL), ("Z", b, rm_g[b], Zr)
+        assert _rel_ok(rm_g[b], Zr, rtol, Z_ATOL), ("Z", b, rm_g[b], Zr)
+        if Zr > 0:
+            near["max_z_relerr"] = max(near["max_z_relerr"], _relerr(rm_g[b], Zr))
     return near
 
 
@@ -307,11 +369,12 @@ def check_spot(g, x, o, t_target, t_draft, tau, dtype_name, eos_id=-1, len_budge
 
 def check_ddtree_hypotheses(g, o, masked, dtype_name):
     """Hypothesis tokens exactly, their probabilities within PROB_RTOL.  A
-    position whose top-1 probability lies within PROB_RTOL of the runner-up
-    threshold (T = 0) may differ in its runner-up slot, and one whose two best
-    Gumbel scores lie within NEAR_MARGIN may differ in its token; the
-    sequences holding such positions are returned (their trees are then
-    built from different hypotheses and are not compared)."""
+    position whose top-1 probability (a float32 1/S, error ~1e-6) lies within
+    NEAR_MARGIN of the runner-up threshold (T = 0) may differ in its
+    runner-up slot, and one whose two best Gumbel scores lie within
+    NEAR_MARGIN may differ in its token; the sequences holding such
+    positions are returned (their trees are then built from different
+    hypotheses and are not compared)."""
     rtol = PROB_RTOL[dtype_name]
     ht, hp = npi(g["hyp_tok"]), np64(g["hyp_prob"])
     np.testing.assert_array_equal(npi(g["status"]), o["hyp_status"], err_msg="status")
@@ -324,7 +387,7 @@ def check_ddtree_hypotheses(g, o, masked, dtype_name):
             if not masked[b, s]:
                 assert ht[b, s].tolist() == [-1, -1] and hp[b, s].tolist() == [0.0, 0.0], (b, s)
                 continue
-            near1 = o["top1_margin"][b, s] < rtol
+            near1 = o["top1_margin"][b, s] < NEAR_MARGIN
             nearg = o["pick_margin"][b, s] < NEAR_MARGIN
             if nearg:
                 amb.add(b)

@@ -45,7 +45,7 @@ def test_exports_match_header(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.verify_abi_version() == 1
+    assert lib.verify_abi_version() == 2
     for code in range(6):
         assert lib.verify_status_string(code)
     assert b"unknown" in lib.verify_status_string(99)
@@ -75,7 +75,7 @@ def _greedy(lib, **kw):
     return lib.verify_greedy(a["B"], a["K"], a["V"], a["dt"], a["tgt"], a["ts"], a["tr"], a["d"],
                              a["n"], a["dr"], a["ds"], a["drs"], a["W"], a["eos"], a["bud"],
                              a["acc"], a["out"], a["num"], a["nd"], a["nl"], a["st"], a["ws"],
-                             a["wsb"], a["stream"])
+                             a["wsb"], a["stream"], a.get("opts"))
 
 
 def _reject(lib, lenient=False, cactus=False, **kw):
@@ -87,7 +87,7 @@ def _reject(lib, lenient=False, cactus=False, **kw):
     head = [a["B"], a["K"], a["V"], a["dt"], a["tgt"], a["ts"], a["tr"], a["drf"], a["ds"], a["dr"],
             a["d"], a["n"], a["tt"], a["td"]]
     tail = [a["ua"], a["ur"], a["eos"], a["bud"], a["acc"], a["out"], a["num"], a["pd"], a["qd"],
-            a["al"], a["rm"], a["st"], a["ws"], a["wsb"], a["stream"]]
+            a["al"], a["rm"], a["st"], a["ws"], a["wsb"], a["stream"], a.get("opts")]
     if lenient:
         return lib.verify_lenient(*(head + [a["lam"]] + tail))
     if cactus:
@@ -104,7 +104,7 @@ def _tree(lib, **kw):
     return lib.verify_gumbel_tree(a["B"], a["S"], a["L"], a["V"], a["dt"], a["lg"], a["ss"], a["sy"],
                                   a["sp"], a["m"], a["par"], a["ep"], a["et"], a["ns"], a["npos"],
                                   a["g"], a["gs"], a["gp"], a["T"], a["mode"], o, o, o, o, o, o, o,
-                                  o, o, a["ws"], a["wsb"], a["stream"])
+                                  o, o, a["ws"], a["wsb"], a["stream"], a.get("opts"))
 
 
 def _sparse(lib, **kw):
@@ -114,7 +114,7 @@ def _sparse(lib, **kw):
     o = a["o"]
     return lib.verify_sparse(a["B"], a["K"], a["V"], a["dt"], a["tgt"], a["ts"], a["tr"], a["qi"], a["qp"], a["qn"],
                              a["kmax"], a["d"], a["n"], a["tt"], a["ua"], a["ur"], a["eos"], a["bud"], o, o, o,
-                             None, None, None, None, o, a["ws"], a["wsb"], a["stream"])
+                             None, None, None, None, o, a["ws"], a["wsb"], a["stream"], a.get("opts"))
 
 
 def _trunc(lib, **kw):
@@ -123,7 +123,7 @@ def _trunc(lib, **kw):
     a.update(kw)
     o = a["o"]
     return lib.truncate_top_k_top_p(a["B"], a["K"], a["V"], a["dt"], a["rows"], a["ss"], a["rs"], a["n"], a["T"],
-                                    a["k"], a["p"], a["kmax"], o, o, o, a["stream"])
+                                    a["k"], a["p"], a["kmax"], o, o, o, a["stream"], a.get("opts"))
 
 
 def _ddhyp(lib, **kw):
@@ -133,7 +133,7 @@ def _ddhyp(lib, **kw):
     o = a["o"]
     return lib.ddtree_hypotheses(a["B"], a["L"], a["V"], a["dt"], a["stale"], a["ss"], a["sp"], a["m"], a["g"],
                                  a["gs"], a["gp"], a["T"], a["below"], o, o, a["st"], a["ws"], a["wsb"],
-                                 a["stream"])
+                                 a["stream"], a.get("opts"))
 
 
 def _ddtree(lib, level=False, **kw):
@@ -143,7 +143,7 @@ def _ddtree(lib, level=False, **kw):
     o = a["o"]
     head = (a["B"], a["L"], a["D"], a["m"], a["ht"], a["hp"], a["order"], a["os"], a["orow"], a["tau"],
             a["gamma"])
-    tail = (o, o, o, o, a["nm"], o, a["fr"], o, a["st"], a["ws"], a["wsb"], a["stream"])
+    tail = (o, o, o, o, a["nm"], o, a["fr"], o, a["st"], a["ws"], a["wsb"], a["stream"], a.get("opts"))
     if level:
         return lib.ddtree_level(*head, a["first"], *tail)
     return lib.ddtree_build(*head, *tail)
@@ -158,7 +158,7 @@ def _spot(lib, **kw):
     return lib.verify_spot_chain(a["B"], a["K"], a["V"], a["dt"], a["tgt"], a["ts"], a["tr"], a["drf"], a["ds"],
                                  a["dr"], a["ps"], a["pp"], a["d"], a["c"], a["n"], a["tt"], a["td"], a["g"],
                                  a["gs"], a["gr"], a["tau"], a["ua"], a["ur"], a["eos"], a["bud"], o, o, o, None,
-                                 None, None, None, o, a["ws"], a["wsb"], a["stream"])
+                                 None, None, None, o, a["ws"], a["wsb"], a["stream"], a.get("opts"))
 
 
 def _any_order(lib, **kw):
@@ -169,7 +169,7 @@ def _any_order(lib, **kw):
     o = a["o"]
     return lib.verify_greedy_any_order(a["B"], a["U"], a["V"], a["dt"], a["tgt"], a["ts"], a["tr"], a["order"],
                                        a["na"], a["pos"], a["d"], a["dr"], a["ds"], a["drs"], a["eos"], a["end"],
-                                       o, o, o, o, o, a["nd"], a["st"], a["ws"], a["wsb"], a["stream"])
+                                       o, o, o, o, o, a["nd"], a["st"], a["ws"], a["wsb"], a["stream"], a.get("opts"))
 
 
 INVALID = _lib.DBV_ERR_INVALID_ARG
@@ -339,3 +339,49 @@ def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def _opts(**kw):
+    return ctypes.byref(_lib.Options(**kw))
+
+
+def test_options_struct_matches_header():
+    # dbv_options: two uint32 then seven pointers, in this order.
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct dbv_options \{(.*?)\} dbv_options;", text, re.S).group(1)
+    fields = re.findall(r"(\w+);", body)
+    assert fields == [f for f, _ in _lib.Options._fields_]
+    assert ctypes.sizeof(_lib.Options) == 8 + 7 * ctypes.sizeof(ctypes.c_void_p)
+
+
+def test_options_are_validated(lib):
+    # One timing event without the other, or a size too small for them.
+    assert _greedy(lib, opts=_opts(row_begin=FAKE)) == INVALID
+    assert _reject(lib, opts=_opts(row_end=FAKE)) == INVALID
+    bad = _lib.Options()
+    bad.size = 8
+    assert _tree(lib, opts=ctypes.byref(bad)) == INVALID
+    # Diagnostic outputs an entry point does not produce.
+    assert _greedy(lib, opts=_opts(accept_margin=FAKE)) == INVALID
+    assert _tree(lib, opts=_opts(draw_margin=FAKE)) == INVALID
+    assert _any_order(lib, opts=_opts(row_tv=FAKE)) == INVALID
+    assert _trunc(lib, opts=_opts(pos_margin=FAKE)) == INVALID
+    assert _ddhyp(lib, opts=_opts(tok_margin=FAKE)) == INVALID
+    assert _ddtree(lib, opts=_opts(accept_margin=FAKE)) == INVALID
+    assert _reject(lib, opts=_opts(pos_margin=FAKE)) == INVALID
+    assert _spot(lib, opts=_opts(tok_margin=FAKE)) == INVALID
+    assert _sparse(lib, opts=_opts(pos_margin=FAKE)) == INVALID
+
+
+def test_options_accepted_without_gpu(lib):
+    if _gpu_visible():
+        pytest.skip("would launch with fake pointers on a GPU")
+    nodev = _lib.DBV_ERR_NO_DEVICE
+    ev = dict(row_begin=FAKE, row_end=FAKE)
+    assert _greedy(lib, opts=_opts(**ev)) == nodev
+    assert _reject(lib, opts=_opts(accept_margin=FAKE, draw_margin=FAKE, **ev)) == nodev
+    assert _reject(lib, lenient=True, opts=_opts(accept_margin=FAKE)) == nodev
+    assert _spot(lib, opts=_opts(draw_margin=FAKE)) == nodev
+    assert _sparse(lib, opts=_opts(accept_margin=FAKE)) == nodev
+    assert _tree(lib, opts=_opts(**ev)) == nodev
+    assert _ddtree(lib, opts=_opts(**ev)) == nodev

@@ -13,7 +13,7 @@ import torch
 import draft_block_verification_amd as dbv
 import oracle
 import workloads
-from tests.parity import (check_ddtree_hypotheses, check_ddtree_tree, check_tree, np64, npi)
+from tests.parity import (check_ddtree_hypotheses, check_ddtree_tree, check_tree, np64, npi, record)
 
 pytestmark = pytest.mark.gpu
 
@@ -265,13 +265,21 @@ def test_floor_above_one_and_zero_budget(dev):
         assert (npi(st["parent"])[:, 0] == -1).all()
 
 
-def test_full_size_sampled(dev):
+def test_full_size(dev):
     """The benchmarked configuration: B=16, L=32, V=151936 bf16, T=1, D=20;
-    every hypothesis and every tree checked against the oracle."""
+    every hypothesis and every one of the 16 trees checked against the
+    oracle (a tree is skipped only where a hypothesis decision lies within
+    NEAR_MARGIN, and none may be)."""
     say("ddtree full size")
     x = workloads.config4_ddtree()
     h, st = _run_build(x, dev, 20, 1.0, 0.0)
     fn = oracle.table_order(np64(x["order_table"]))
     o = _oracle(x, fn, 20, 1.0, 0.0)
+    masked = npi(x["masked"])
+    amb = check_ddtree_hypotheses(h, o, masked, "bfloat16")
+    assert not amb, amb
     near = _check_all(h, st, o, x, fn, 20, 1.0, 0.0, "bfloat16")
+    record("c4d DDTree B=16 L=32 V=151936 bf16 T=1 D=20",
+           {"blocks": masked.shape[0], "hypothesis_rows": int(masked.sum()), "trees_skipped": len(amb),
+            "near_cut_states": near})
     say("near-cut states", near)
