@@ -6,7 +6,7 @@ raw device pointers and the current HIP stream to the C ABI.  Every step of
 the verification runs in the library's HIP kernels; there is no fallback.
 
 Entry points (same names as the C ABI):
-  verify_greedy, verify_rejection, verify_lenient, verify_cactus,
+  verify_greedy, verify_rejection, verify_rejection_noalloc, verify_lenient, verify_cactus,
   verify_sparse, truncate_top_k_top_p, verify_spot_chain,
   verify_greedy_any_order, verify_gumbel_tree,
   ddtree_hypotheses, ddtree_level, ddtree_build
@@ -24,8 +24,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_sparse", "verify_spot_chain",
-    "truncate_top_k_top_p",
+    "verify_greedy", "verify_rejection", "verify_rejection_noalloc", "verify_lenient", "verify_cactus",
+    "verify_sparse", "verify_spot_chain", "truncate_top_k_top_p",
     "verify_greedy_any_order", "verify_gumbel_tree", "ddtree_hypotheses", "ddtree_level", "ddtree_build",
     "workspace_size", "DBVError", "Prepared",
 ]
@@ -191,7 +191,7 @@ def _chain_margins(out, B, K, dev, margins):
 
 def _sampling(fn_name, tgt, drf, draft_tokens, draft_len, temperature_target,
               temperature_draft, lam, u_accept, u_resample, eos_id, len_budget,
-              workspace, diagnostics, prepare, margins=False):
+              workspace, diagnostics, prepare, margins=False, noalloc=False):
     lib = _lib.load()
     dev = tgt.device
     B, K1, V = tgt.shape
@@ -216,8 +216,6 @@ def _sampling(fn_name, tgt, drf, draft_tokens, draft_len, temperature_target,
         for k in ("p_draft", "q_draft", "alpha"):
             out[k] = torch.empty(B, K, dtype=torch.float32, device=dev)
         out["residual_mass"] = torch.empty(B, dtype=torch.float32, device=dev)
-    need = workspace_size(_lib.DBV_KIND_REJECTION, B, K, 0, V, dt)
-    ws = workspace if workspace is not None else _workspace(need, dev)
     args = [B, K, V, dt, tgt.data_ptr(), ts, tr, drf.data_ptr(), ds, dr, _ptr(d), _ptr(n),
             float(temperature_target), float(temperature_draft)]
     if fn_name in ("verify_lenient", "verify_cactus"):
@@ -225,8 +223,15 @@ def _sampling(fn_name, tgt, drf, draft_tokens, draft_len, temperature_target,
     args += [ua.data_ptr() if K else None, ur.data_ptr(), int(eos_id), _ptr(bud),
              out["accept_len"].data_ptr(), out["out_tokens"].data_ptr(), out["num_out"].data_ptr(),
              _ptr(out.get("p_draft")), _ptr(out.get("q_draft")), _ptr(out.get("alpha")),
-             _ptr(out.get("residual_mass")), out["status"].data_ptr(),
-             ws.data_ptr(), ws.numel(), _stream(dev)]
+             _ptr(out.get("residual_mass")), out["status"].data_ptr()]
+    ws = None
+    if noalloc:
+        fn_name = "verify_rejection_noalloc"
+    else:
+        need = workspace_size(_lib.DBV_KIND_REJECTION, B, K, 0, V, dt)
+        ws = workspace if workspace is not None else _workspace(need, dev)
+        args += [ws.data_ptr(), ws.numel()]
+    args.append(_stream(dev))
     opts = _chain_margins(out, B, K, dev, margins)
     call = Prepared(getattr(lib, fn_name), fn_name, tuple(args), out,
                     (tgt, drf, d, n, bud, ua, ur, ws), opts)
@@ -247,6 +252,17 @@ def verify_rejection(tgt, drf, draft_tokens, u_accept, u_resample, draft_len=Non
     return _sampling("verify_rejection", tgt, drf, draft_tokens, draft_len,
                      temperature_target, temperature_draft, 0.0, u_accept, u_resample,
                      eos_id, len_budget, workspace, diagnostics, prepare, margins)
+
+
+def verify_rejection_noalloc(tgt, drf, draft_tokens, u_accept, u_resample, draft_len=None,
+                             temperature_target=1.0, temperature_draft=1.0, eos_id=-1,
+                             len_budget=None, diagnostics=True, prepare=False, margins=False):
+    """verify_rejection through the entry point that allocates nothing: its
+    scratch is the library's own device array (at most 4 MiB of workspace;
+    calls that overlap on one GPU race).  Outputs as verify_rejection."""
+    return _sampling("verify_rejection", tgt, drf, draft_tokens, draft_len,
+                     temperature_target, temperature_draft, 0.0, u_accept, u_resample,
+                     eos_id, len_budget, None, diagnostics, prepare, margins, noalloc=True)
 
 
 def verify_lenient(tgt, drf, draft_tokens, u_accept, u_resample, lam, draft_len=None,

@@ -34,7 +34,7 @@ SEQ_Z_ZERO = 16
 SEQ_ERROR_MASK = 7
 
 EXPORTS = (
-    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_sparse", "truncate_top_k_top_p",
+    "verify_greedy", "verify_rejection", "verify_rejection_noalloc", "verify_lenient", "verify_cactus", "verify_sparse", "truncate_top_k_top_p",
     "verify_spot_chain",
     "verify_greedy_any_order", "verify_gumbel_tree", "verify_workspace_size", "verify_status_string", "verify_abi_version",
     "ddtree_hypotheses", "ddtree_level", "ddtree_build",
@@ -42,7 +42,7 @@ EXPORTS = (
 
 # Entry points that take a trailing `const dbv_options* opts`.
 WITH_OPTIONS = (
-    "verify_greedy", "verify_rejection", "verify_lenient", "verify_cactus", "verify_sparse", "truncate_top_k_top_p",
+    "verify_greedy", "verify_rejection", "verify_rejection_noalloc", "verify_lenient", "verify_cactus", "verify_sparse", "truncate_top_k_top_p",
     "verify_spot_chain", "verify_greedy_any_order", "verify_gumbel_tree", "ddtree_hypotheses", "ddtree_level",
     "ddtree_build",
 )
@@ -59,6 +59,9 @@ _SIGS = {
                       _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "verify_rejection": [_i, _i, _i, _i, _p, _i64, _i64, _p, _i64, _i64, _p, _p, _f, _f, _p, _p,
                          _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
+    # verify_rejection without ws, ws_bytes
+    "verify_rejection_noalloc": [_i, _i, _i, _i, _p, _i64, _i64, _p, _i64, _i64, _p, _p, _f, _f, _p, _p,
+                                 _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p],
     "verify_lenient": [_i, _i, _i, _i, _p, _i64, _i64, _p, _i64, _i64, _p, _p, _f, _f, _f, _p, _p,
                        _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "verify_cactus": [_i, _i, _i, _i, _p, _i64, _i64, _p, _i64, _i64, _p, _p, _f, _f, _f, _p, _p,

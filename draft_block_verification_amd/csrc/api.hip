@@ -13,6 +13,14 @@
 #include "dbv_launch.h"
 #include "dbv_plan.h"
 
+// Scratch of verify_rejection_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never uses its name as
+// an address: scratch_address() keeps, per GPU, the device address that
+// hipGetSymbolAddress returns for it (looked up on the entry point's first
+// call there, with that device current).
+constexpr size_t kNoAllocBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
 namespace {
 
 using dbv::kMaxBlockLen;
@@ -98,6 +106,26 @@ bool read_plain_opts(const dbv_options* o, CallOpts& c) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// The current device's address of `scratch`, or NULL.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 size_t elem_bytes(dbv_dtype dt) { return dt == DBV_BF16 ? 2 : 4; }
 
 bool dtype_ok(dbv_dtype dt) { return dt == DBV_F32 || dt == DBV_BF16; }
@@ -139,7 +167,7 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
                          const float* u_resample, int32_t eos_id, const int32_t* len_budget,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* num_out, float* p_draft,
                          float* q_draft, float* alpha, float* residual_mass, int32_t* status, void* ws,
-                         size_t ws_bytes, void* stream, const dbv_options* opts) {
+                         size_t ws_bytes, void* stream, const dbv_options* opts, bool noalloc = false) {
   if (B < 0 || K < 0 || K > kMaxDraft || V < 1 || !dtype_ok(dtype)) return DBV_ERR_INVALID_ARG;
   CallOpts co;
   if (!read_opts(opts, co) || co.pos_margin || co.tok_margin || co.row_tv) return DBV_ERR_INVALID_ARG;
@@ -168,9 +196,14 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   if (!aligned(tgt, eb) || (drf && !aligned(drf, eb))) return DBV_ERR_INVALID_ARG;
   const dbv::SamplePlan plan = dbv::plan_sample(B, K, V, static_cast<int64_t>(elem_bytes(dtype)));
   if (!stream_fits(plan.max_vrows, V)) return DBV_ERR_UNSUPPORTED;
-  dbv_status s = check_ws(ws, ws_bytes, plan.bytes);
-  if (s != DBV_OK) return s;
+  dbv_status s = DBV_OK;
+  if (noalloc) {
+    if (plan.bytes > kNoAllocBytes) return DBV_ERR_UNSUPPORTED;
+  } else if ((s = check_ws(ws, ws_bytes, plan.bytes)) != DBV_OK) {
+    return s;
+  }
   if ((s = device_ready()) != DBV_OK) return s;
+  if (noalloc && (ws = scratch_address()) == nullptr) return DBV_ERR_NO_DEVICE;
   if (B == 0) return DBV_OK;
 
   dbv::SampleArgs a{};
@@ -329,6 +362,21 @@ dbv_status verify_rejection(int B, int K, int V, dbv_dtype dtype, const void* tg
                        drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft,
                        Rule{}, u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft,
                        q_draft, alpha, residual_mass, status, ws, ws_bytes, stream, opts);
+}
+
+dbv_status verify_rejection_noalloc(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,
+                                    int64_t tgt_row_stride, const void* drf, int64_t drf_seq_stride,
+                                    int64_t drf_row_stride, const int32_t* draft_tokens, const int32_t* draft_len,
+                                    float temperature_target, float temperature_draft, const float* u_accept,
+                                    const float* u_resample, int32_t eos_id, const int32_t* len_budget,
+                                    int32_t* accept_len, int32_t* out_tokens, int32_t* num_out, float* p_draft,
+                                    float* q_draft, float* alpha, float* residual_mass, int32_t* status,
+                                    void* stream, const dbv_options* opts) {
+  // Validated as verify_rejection; the workspace is the library's scratch.
+  return sample_common(B, K, V, dtype, tgt, tgt_seq_stride, tgt_row_stride, drf, drf_seq_stride,
+                       drf_row_stride, draft_tokens, draft_len, temperature_target, temperature_draft,
+                       Rule{}, u_accept, u_resample, eos_id, len_budget, accept_len, out_tokens, num_out, p_draft,
+                       q_draft, alpha, residual_mass, status, nullptr, kNoAllocBytes, stream, opts, true);
 }
 
 dbv_status verify_lenient(int B, int K, int V, dbv_dtype dtype, const void* tgt, int64_t tgt_seq_stride,

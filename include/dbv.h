@@ -233,6 +233,32 @@ dbv_status verify_rejection(int B, int K, int V, dbv_dtype dtype,
                             const dbv_options* opts);
 
 /*
+ * verify_rejection_noalloc -- verify_rejection for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without `ws` and
+ * `ws_bytes`, the same kernels and outputs.  Its scratch is a 4 MiB device
+ * array inside the library, one per GPU, held until the process ends; no
+ * call allocates or frees anything.  A call whose workspace
+ * (verify_workspace_size(DBV_KIND_REJECTION, ...)) exceeds 4 MiB returns
+ * DBV_ERR_UNSUPPORTED and launches nothing (B = 32, K = 16 at V = 151936
+ * needs about 0.4 MiB).  All calls on one GPU share its array, which keeps
+ * the last call's contents: calls that overlap on one GPU (on different
+ * streams, or from several threads without ordering) race; order them on
+ * one stream.  The kernels need no zeroed scratch.
+ */
+dbv_status verify_rejection_noalloc(int B, int K, int V, dbv_dtype dtype,
+                                    const void* tgt, int64_t tgt_seq_stride, int64_t tgt_row_stride,
+                                    const void* drf, int64_t drf_seq_stride, int64_t drf_row_stride,
+                                    const int32_t* draft_tokens, const int32_t* draft_len,
+                                    float temperature_target, float temperature_draft,
+                                    const float* u_accept, const float* u_resample,
+                                    int32_t eos_id, const int32_t* len_budget,
+                                    int32_t* accept_len, int32_t* out_tokens, int32_t* num_out,
+                                    float* p_draft, float* q_draft, float* alpha, float* residual_mass,
+                                    int32_t* status, void* stream,
+                                    const dbv_options* opts);
+
+/*
  * verify_lenient -- the linear lenient rule of [TT] Theorem 1 (Eq. 5) used in
  * [TT] Algorithm 1: the target is relaxed to p~ = (1 - lambda) p + lambda q
  * before the draft is tested; accept iff u < min(1, p~(d)/q(d)); a rejected

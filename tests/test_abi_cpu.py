@@ -385,3 +385,37 @@ def test_options_accepted_without_gpu(lib):
     assert _sparse(lib, opts=_opts(accept_margin=FAKE)) == nodev
     assert _tree(lib, opts=_opts(**ev)) == nodev
     assert _ddtree(lib, opts=_opts(**ev)) == nodev
+
+
+def _noalloc(lib, **kw):
+    a = dict(B=2, K=3, V=100, dt=_lib.DBV_BF16, tgt=FAKE, ts=400, tr=100, drf=FAKE, ds=300,
+             dr=100, d=FAKE, n=None, tt=1.0, td=1.0, ua=FAKE, ur=FAKE, eos=-1, bud=None,
+             acc=FAKE, out=FAKE, num=FAKE, st=FAKE, stream=None)
+    a.update(kw)
+    return lib.verify_rejection_noalloc(a["B"], a["K"], a["V"], a["dt"], a["tgt"], a["ts"], a["tr"], a["drf"],
+                                        a["ds"], a["dr"], a["d"], a["n"], a["tt"], a["td"], a["ua"], a["ur"],
+                                        a["eos"], a["bud"], a["acc"], a["out"], a["num"], None, None, None, None,
+                                        a["st"], a["stream"], a.get("opts"))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=-1), dict(K=-1), dict(K=5000), dict(V=0), dict(dt=3), dict(tgt=None), dict(drf=None), dict(ua=None),
+    dict(ur=None), dict(d=None), dict(tt=0.0), dict(td=float("nan")), dict(acc=None), dict(tgt=FAKE + 1),
+])
+def test_noalloc_rejects_bad_args(lib, kw):
+    assert _noalloc(lib, **kw) == INVALID
+
+
+def test_noalloc_limit(lib):
+    # The workspace of this call would exceed the library's 4 MiB scratch.
+    need = lib.verify_workspace_size(_lib.DBV_KIND_REJECTION, 4096, 64, 0, 151936, _lib.DBV_BF16)
+    assert need > 4 << 20
+    assert _noalloc(lib, B=4096, K=64, V=151936) == _lib.DBV_ERR_UNSUPPORTED
+    assert _noalloc(lib, V=(1 << 21) + 1) == _lib.DBV_ERR_UNSUPPORTED
+
+
+def test_noalloc_without_gpu_reports_no_device(lib):
+    if _gpu_visible():
+        pytest.skip("a GPU is visible")
+    assert _noalloc(lib) == _lib.DBV_ERR_NO_DEVICE
+    assert _noalloc(lib, B=32, K=16, V=151936) == _lib.DBV_ERR_NO_DEVICE
