@@ -607,12 +607,14 @@ __device__ __forceinline__ void combine_rows_stats(int nrows, const float2* part
   }
 }
 
-template <int NT = kBlock, class SpanFn, class DoneFn>
-__device__ __forceinline__ void combine_rows_stats64(int nrows, const Stat64* part, float k, SpanFn span,
+// kf(r) is the log2(e)/T of row r.
+template <int NT = kBlock, class KFn, class SpanFn, class DoneFn>
+__device__ __forceinline__ void combine_rows_stats64(int nrows, const Stat64* part, KFn kf, SpanFn span,
                                                      DoneFn done) {
   const int sub = threadIdx.x % kRowLanes;
   for (int r0 = 0; r0 < nrows; r0 += NT / kRowLanes) {
     const int r = r0 + static_cast<int>(threadIdx.x) / kRowLanes;
+    const float k = kf(r < nrows ? r : nrows - 1);
     float M = -kInf;
     double S = 0.0;
     if (r < nrows) {

@@ -653,27 +653,33 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
       first_slot = (v + glo) * kWaves;
       cnt = (ghi - glo + 1) * kWaves;
     };
-    combine_rows_stats64<NT>(n + 1, a.stats, a.kp, tspan, [&](int r, float M, double S) {
-      s.Mp[r] = M; s.Sp[r] = S;
-      st |= stats64_status(M, S);
-    });
+    // The target rows 0..n and the drafter rows 0..n-1 in one pass, so all
+    // their partials are requested together.
+    const int nd = a.drows ? n : 0;
+    combine_rows_stats64<NT>(
+        n + 1 + nd, a.stats, [&](int r) { return r <= n ? a.kp : a.kq; },
+        [&](int r, int64_t& first_slot, int64_t& cnt) {
+          if (r <= n) {
+            tspan(r, first_slot, cnt);
+          } else {
+            split_row_slots(f, p0 + static_cast<int64_t>(P) * (n + 1) + (r - n - 1), first_slot, cnt);
+            first_slot *= kWaves;
+            cnt *= kWaves;
+          }
+        },
+        [&](int r, float M, double S) {
+          if (r <= n) {
+            s.Mp[r] = M; s.Sp[r] = S;
+          } else {
+            s.Mq[r - n - 1] = M; s.Sq[r - n - 1] = S;
+          }
+          st |= stats64_status(M, S);
+        });
     if (P > 1)
       combine_rows_pick<NT>(n + 1, a.gpart, tspan, [&](int r, float v, int idx, int nan) {
         s.g[r] = idx;
         st |= nan ? SEQ_NONFINITE : max_status(v);
       });
-    if (a.drows)
-      combine_rows_stats64<NT>(
-          n, a.stats, a.kq,
-          [&](int r, int64_t& first_slot, int64_t& cnt) {
-            split_row_slots(f, p0 + static_cast<int64_t>(P) * (n + 1) + r, first_slot, cnt);
-            first_slot *= kWaves;
-            cnt *= kWaves;
-          },
-          [&](int r, float M, double S) {
-            s.Mq[r] = M; s.Sq[r] = S;
-            st |= stats64_status(M, S);
-          });
   }
   if (sparse && !nbad) {
     // Q(d_i) from row i's stored entries, every (draft, entry) pair one work
@@ -946,8 +952,9 @@ struct SelectLdsT {
   static constexpr int kTiles = TPT;
   float tile[NT * TPT];
   float w[NT / 64];
+  int whit[NT / 64], wlast[NT / 64];   // per wave: first hit, last positive tile
   float Z, base, margin;
-  int ct, lt, cs, pick, a;
+  int cs, pick, a;
 };
 using SelectLds = SelectLdsT<kDrawThreads, kDrawTilesPerThread>;
 // Rows of at most kSmallSelect * kSmallSelectTiles tiles are selected by
@@ -1013,7 +1020,6 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
   // Thread t holds the masses of tiles [t*q, (t+1)*q); an exclusive scan
   // gives it the mass before them, and the group's total Z.
   auto locate = [&](const float (&m)[TPT]) {
-    if (t == 0) { s.ct = INT_MAX; s.lt = -1; }
     float loc = 0.f;
 #pragma unroll
     for (int k = 0; k < TPT; ++k) loc += m[k];
@@ -1030,10 +1036,25 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
       }
       run += m[k];
     }
-    if (hit != INT_MAX) atomicMin(&s.ct, hit);
-    if (last >= 0) atomicMax(&s.lt, last);
+    // Tiles increase with the thread index: the first hit is the first lane
+    // with one in the first wave with one, the last positive tile the last
+    // such lane of the last such wave (ballots, no LDS atomics).
+    const uint64_t hb = __ballot(hit != INT_MAX);
+    const uint64_t lb = __ballot(last >= 0);
+    const int whit = __shfl(hit, hb ? __builtin_ctzll(hb) : 0, 64);
+    const int wlast = __shfl(last, lb ? 63 - __builtin_clzll(lb) : 0, 64);
+    if (lane == 0) {
+      s.whit[wv] = hb ? whit : INT_MAX;
+      s.wlast[wv] = lb ? wlast : -1;
+    }
     __syncthreads();
-    const int ct = s.ct != INT_MAX ? s.ct : (s.lt >= 0 ? s.lt : 0);
+    int fh = INT_MAX, fl = -1;
+#pragma unroll
+    for (int j = 0; j < NT / 64; ++j) {
+      if (fh == INT_MAX) fh = s.whit[j];
+      fl = s.wlast[j] >= 0 ? s.wlast[j] : fl;
+    }
+    const int ct = fh != INT_MAX ? fh : (fl >= 0 ? fl : 0);
     if (t == ct / q) {   // the owner of the chosen tile writes the mass before it
       float before = start;
 #pragma unroll
@@ -1089,6 +1110,15 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
         wt[j] = e0 + j < a.V
                     ? fmaxf(fast_exp2(__builtin_fmaf(E::load1(xr, e0 + j), w.kp, -w.ep)) * w.isp - q[j], 0.f)
                     : 0.f;
+    } else if (e0 + E::kVec <= a.V &&
+               ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0) {
+      // the lane's vector of the row (and of the drafter row) in one load each
+      float x[E::kVec], y[E::kVec];
+      E::unpack(load16(xr + e0 * E::kBytes), x);
+      if (w.resid) E::unpack(load16(yr + e0 * E::kBytes), y);
+#pragma unroll
+      for (int j = 0; j < E::kVec; ++j)
+        wt[j] = w.at(static_cast<uint32_t>(e0 + j), x[j], w.resid ? y[j] : 0.f);
     } else {
 #pragma unroll
       for (int j = 0; j < E::kVec; ++j) {
