@@ -179,19 +179,26 @@ def verify_greedy(tgt, draft_tokens, draft_len=None, draft_rows=None, eos_id=-1,
     return call if prepare else call()
 
 
-def _chain_margins(out, B, K, dev, margins):
-    """Optional per-decision margins of a chain sampling call (dbv_options
-    accept_margin [B, K], draw_margin [B]); returns the options or None."""
-    if not margins:
+def _chain_margins(out, B, K, dev, margins, row_tv=False):
+    """Optional diagnostics of a chain sampling call: the per-decision
+    margins (dbv_options accept_margin [B, K], draw_margin [B]) and the
+    per-row TV(p, q) (row_tv [B, K]); returns the options or None."""
+    if not margins and not row_tv:
         return None
-    out["accept_margin"] = torch.empty(B, K, dtype=torch.float32, device=dev)
-    out["draw_margin"] = torch.empty(B, dtype=torch.float32, device=dev)
-    return _lib.Options(accept_margin=out["accept_margin"].data_ptr(), draw_margin=out["draw_margin"].data_ptr())
+    o = _lib.Options()
+    if margins:
+        out["accept_margin"] = torch.empty(B, K, dtype=torch.float32, device=dev)
+        out["draw_margin"] = torch.empty(B, dtype=torch.float32, device=dev)
+        o.accept_margin, o.draw_margin = out["accept_margin"].data_ptr(), out["draw_margin"].data_ptr()
+    if row_tv:
+        out["row_tv"] = torch.empty(B, K, dtype=torch.float32, device=dev)
+        o.row_tv = out["row_tv"].data_ptr()
+    return o
 
 
 def _sampling(fn_name, tgt, drf, draft_tokens, draft_len, temperature_target,
               temperature_draft, lam, u_accept, u_resample, eos_id, len_budget,
-              workspace, diagnostics, prepare, margins=False, noalloc=False):
+              workspace, diagnostics, prepare, margins=False, noalloc=False, row_tv=False):
     lib = _lib.load()
     dev = tgt.device
     B, K1, V = tgt.shape
@@ -232,7 +239,7 @@ def _sampling(fn_name, tgt, drf, draft_tokens, draft_len, temperature_target,
         ws = workspace if workspace is not None else _workspace(need, dev)
         args += [ws.data_ptr(), ws.numel()]
     args.append(_stream(dev))
-    opts = _chain_margins(out, B, K, dev, margins)
+    opts = _chain_margins(out, B, K, dev, margins, row_tv)
     call = Prepared(getattr(lib, fn_name), fn_name, tuple(args), out,
                     (tgt, drf, d, n, bud, ua, ur, ws), opts)
     return call if prepare else call()
@@ -240,18 +247,20 @@ def _sampling(fn_name, tgt, drf, draft_tokens, draft_len, temperature_target,
 
 def verify_rejection(tgt, drf, draft_tokens, u_accept, u_resample, draft_len=None,
                      temperature_target=1.0, temperature_draft=1.0, eos_id=-1,
-                     len_budget=None, workspace=None, diagnostics=True, prepare=False, margins=False):
+                     len_budget=None, workspace=None, diagnostics=True, prepare=False, margins=False,
+                     row_tv=False):
     """Lossless rejection-sampling verification (Packed-SS, Algorithm 2).
 
     tgt [B, K+1, V], drf [B, K, V] (same dtype), draft_tokens [B, K],
     u_accept [B, K], u_resample [B, K+1].  Returns accept_len, out_tokens,
     num_out, status and (with diagnostics) p_draft, q_draft, alpha,
     residual_mass; with margins also accept_margin [B, K] and draw_margin
-    [B], the per-decision margins of dbv_options.
+    [B], the per-decision margins of dbv_options; with row_tv the per-row
+    TV(p_i, q_i) [B, K] (diagnostic mode, one more pass over the rows).
     """
     return _sampling("verify_rejection", tgt, drf, draft_tokens, draft_len,
                      temperature_target, temperature_draft, 0.0, u_accept, u_resample,
-                     eos_id, len_budget, workspace, diagnostics, prepare, margins)
+                     eos_id, len_budget, workspace, diagnostics, prepare, margins, row_tv=row_tv)
 
 
 def verify_rejection_noalloc(tgt, drf, draft_tokens, u_accept, u_resample, draft_len=None,
@@ -267,29 +276,31 @@ def verify_rejection_noalloc(tgt, drf, draft_tokens, u_accept, u_resample, draft
 
 def verify_lenient(tgt, drf, draft_tokens, u_accept, u_resample, lam, draft_len=None,
                    temperature_target=1.0, temperature_draft=1.0, eos_id=-1,
-                   len_budget=None, workspace=None, diagnostics=True, prepare=False, margins=False):
+                   len_budget=None, workspace=None, diagnostics=True, prepare=False, margins=False,
+                   row_tv=False):
     """Linear lenient verification, p~ = (1 - lam) p + lam q (Two Tradeoffs,
     Theorem 1 and Algorithm 1).  Arguments as verify_rejection plus lam."""
     return _sampling("verify_lenient", tgt, drf, draft_tokens, draft_len,
                      temperature_target, temperature_draft, lam, u_accept, u_resample,
-                     eos_id, len_budget, workspace, diagnostics, prepare, margins)
+                     eos_id, len_budget, workspace, diagnostics, prepare, margins, row_tv=row_tv)
 
 
 def verify_cactus(tgt, drf, draft_tokens, u_accept, u_resample, delta, draft_len=None,
                   temperature_target=1.0, temperature_draft=1.0, eos_id=-1,
-                  len_budget=None, workspace=None, diagnostics=True, prepare=False, margins=False):
+                  len_budget=None, workspace=None, diagnostics=True, prepare=False, margins=False,
+                  row_tv=False):
     """Verification with the modified Cactus rule (Two Tradeoffs, App. E):
     the drafted token's target mass is raised to the largest gamma whose
     rescaled target stays within KL budget delta of p.  Arguments as
     verify_rejection plus delta >= 0 (0 = lossless)."""
     return _sampling("verify_cactus", tgt, drf, draft_tokens, draft_len,
                      temperature_target, temperature_draft, delta, u_accept, u_resample,
-                     eos_id, len_budget, workspace, diagnostics, prepare, margins)
+                     eos_id, len_budget, workspace, diagnostics, prepare, margins, row_tv=row_tv)
 
 
 def verify_sparse(tgt, q_idx, q_prob, q_nnz, draft_tokens, u_accept, u_resample, draft_len=None,
                   temperature_target=1.0, eos_id=-1, len_budget=None, workspace=None, diagnostics=True,
-                  prepare=False, margins=False):
+                  prepare=False, margins=False, row_tv=False):
     """Lossless verification against stored sparse drafter distributions
     (Packed-SS Sec. 3.2: only Q's nonzero entries are stored under top-k /
     top-p truncation).
@@ -330,7 +341,7 @@ def verify_sparse(tgt, q_idx, q_prob, q_nnz, draft_tokens, u_accept, u_resample,
             out["accept_len"].data_ptr(), out["out_tokens"].data_ptr(), out["num_out"].data_ptr(),
             _ptr(out.get("p_draft")), _ptr(out.get("q_draft")), _ptr(out.get("alpha")),
             _ptr(out.get("residual_mass")), out["status"].data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
-    opts = _chain_margins(out, B, K, dev, margins)
+    opts = _chain_margins(out, B, K, dev, margins, row_tv)
     call = Prepared(lib.verify_sparse, "verify_sparse", args, out, (tgt, qi, qp, qn, d, n, bud, ua, ur, ws), opts)
     return call if prepare else call()
 
@@ -361,7 +372,7 @@ def truncate_top_k_top_p(rows, top_k, top_p=1.0, kmax=None, lengths=None, temper
 def verify_spot_chain(tgt, drf, pos_star, prop_pos, prop_tok, q_pos_star, u_accept, u_resample,
                       gumbel=None, tau=0.6, draft_len=None, temperature_target=1.0, temperature_draft=1.0,
                       eos_id=-1, len_budget=None, workspace=None, diagnostics=True, prepare=False,
-                      margins=False):
+                      margins=False, row_tv=False):
     """Chain verification on the joint (position, token) space (SPOT App. B,
     Eq. 10-14), gated per link between rejection sampling and coupled-noise
     match when Gumbel rows are given (match where the drafter's confidence
@@ -413,7 +424,7 @@ def verify_spot_chain(tgt, drf, pos_star, prop_pos, prop_tok, q_pos_star, u_acce
             out["out_tokens"].data_ptr(), out["num_out"].data_ptr(), _ptr(out.get("p_draft")),
             _ptr(out.get("q_draft")), _ptr(out.get("alpha")), _ptr(out.get("residual_mass")),
             out["status"].data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
-    opts = _chain_margins(out, B, K, dev, margins)
+    opts = _chain_margins(out, B, K, dev, margins, row_tv)
     call = Prepared(lib.verify_spot_chain, "verify_spot_chain", args, out,
                     (tgt, drf, gumbel, ps, pp, d, c, n, bud, ua, ur, ws), opts)
     return call if prepare else call()
@@ -467,7 +478,7 @@ def verify_greedy_any_order(tgt, order, draft_tokens, num_active=None, positions
 
 def verify_gumbel_tree(logits, parent, edge_pos, edge_tok, masked=None, gumbel=None,
                        temperature=1.0, num_states=None, next_pos=None,
-                       mode=DBV_TREE_STATE_EQUALITY, workspace=None, prepare=False):
+                       mode=DBV_TREE_STATE_EQUALITY, workspace=None, prepare=False, margins=False):
     """Shared-Gumbel state-equality verification of a draft tree (SPOT,
     Sec. 4.3, App. A.1).
 
@@ -475,7 +486,8 @@ def verify_gumbel_tree(logits, parent, edge_pos, edge_tok, masked=None, gumbel=N
     parent / edge_pos / edge_tok [B, S], gumbel [B, L, V] float32 (None at
     temperature 0), num_states [B] or None, next_pos [B, S] in the
     fixed-position mode.  Returns sel_pos, sel_tok, sel_conf, path_len,
-    path_nodes, commit_pos, commit_tok, num_commits, status.
+    path_nodes, commit_pos, commit_tok, num_commits, status; with margins
+    also pos_margin and tok_margin [B, S] (dbv_options).
     """
     lib = _lib.load()
     dev = logits.device
@@ -519,8 +531,13 @@ def verify_gumbel_tree(logits, parent, edge_pos, edge_tok, masked=None, gumbel=N
             out["path_len"].data_ptr(), out["path_nodes"].data_ptr(), out["commit_pos"].data_ptr(),
             out["commit_tok"].data_ptr(), out["num_commits"].data_ptr(), out["status"].data_ptr(),
             ws.data_ptr(), ws.numel(), _stream(dev))
+    opts = None
+    if margins:
+        out["pos_margin"] = torch.empty(B, S, dtype=torch.float32, device=dev)
+        out["tok_margin"] = torch.empty(B, S, dtype=torch.float32, device=dev)
+        opts = _lib.Options(pos_margin=out["pos_margin"].data_ptr(), tok_margin=out["tok_margin"].data_ptr())
     call = Prepared(lib.verify_gumbel_tree, "verify_gumbel_tree", args, out,
-                    (logits, m, par, ep, et, ns, npos, gumbel, ws))
+                    (logits, m, par, ep, et, ns, npos, gumbel, ws), opts)
     return call if prepare else call()
 
 

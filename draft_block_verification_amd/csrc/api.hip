@@ -170,7 +170,7 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
                          size_t ws_bytes, void* stream, const dbv_options* opts, bool noalloc = false) {
   if (B < 0 || K < 0 || K > kMaxDraft || V < 1 || !dtype_ok(dtype)) return DBV_ERR_INVALID_ARG;
   CallOpts co;
-  if (!read_opts(opts, co) || co.pos_margin || co.tok_margin || co.row_tv) return DBV_ERR_INVALID_ARG;
+  if (!read_opts(opts, co) || co.pos_margin || co.tok_margin) return DBV_ERR_INVALID_ARG;
   if (V > dbv::kMaxSampleV) return DBV_ERR_UNSUPPORTED;
   if (!temp_ok(tt) || !temp_ok(td) || !(rl.lam >= 0.f && rl.lam <= 1.f)) return DBV_ERR_INVALID_ARG;
   if (!(std::isfinite(rl.delta) && rl.delta >= 0.f)) return DBV_ERR_INVALID_ARG;
@@ -228,6 +228,7 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.status = status;
   a.accept_margin = co.accept_margin;
   a.draw_margin = co.draw_margin;
+  a.row_tv = co.row_tv;
   char* w = static_cast<char*>(ws);
   a.stats = reinterpret_cast<dbv::Stat64*>(w + plan.off_stats);
   a.gpart = reinterpret_cast<float2*>(w + plan.off_gpart);
@@ -535,8 +536,7 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const
     return DBV_ERR_INVALID_ARG;
   if (mode != DBV_TREE_STATE_EQUALITY && mode != DBV_TREE_FIXED_POSITION) return DBV_ERR_INVALID_ARG;
   CallOpts co;
-  if (!read_opts(opts, co) || co.accept_margin || co.draw_margin || co.row_tv || co.pos_margin || co.tok_margin)
-    return DBV_ERR_INVALID_ARG;
+  if (!read_opts(opts, co) || co.accept_margin || co.draw_margin || co.row_tv) return DBV_ERR_INVALID_ARG;
   if (!(std::isfinite(temperature) && temperature >= 0.f)) return DBV_ERR_INVALID_ARG;
   if (seq_stride < 0 || state_stride < 0 || pos_stride < 0 || g_seq_stride < 0 || g_pos_stride < 0)
     return DBV_ERR_INVALID_ARG;
@@ -574,7 +574,13 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const
   a.map = reinterpret_cast<int32_t*>(w + plan.off_map);
   a.conf = reinterpret_cast<float2*>(w + plan.off_conf);
   a.pick = reinterpret_cast<float2*>(w + plan.off_pick);
+  a.pick2 = reinterpret_cast<float*>(w + plan.off_pick2);
   a.sel = reinterpret_cast<int32_t*>(w + plan.off_sel);
+  a.selconf = reinterpret_cast<float*>(w + plan.off_selconf);
+  a.selstat = reinterpret_cast<int32_t*>(w + plan.off_selstat);
+  a.selgap = reinterpret_cast<float*>(w + plan.off_selgap);
+  a.pos_margin = co.pos_margin;
+  a.tok_margin = co.tok_margin;
   a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(elem_bytes(dtype)), group_cap(co));
   a.split2 = plan.split2; a.chunk2 = plan.chunk2;
   return dbv::launch_tree(a, dtype, static_cast<hipStream_t>(stream), co.ev) ? DBV_OK : DBV_ERR_LAUNCH;

@@ -36,6 +36,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float fmaxp(float a, float b) {
   return __builtin_elementwise_maximum(a, b);
 }
+// Its minimum counterpart (v_minimum3_f32).
+__device__ __forceinline__ float fminp(float a, float b) {
+  return __builtin_elementwise_minimum(a, b);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -185,15 +189,21 @@ __device__ __forceinline__ void stats_merge(float& M, float& S, float M2, float 
 // differences of two rows' probabilities keep their relative precision.
 // The reference of a running maximum M is the integer E = floor(M k): every
 // element contributes exp2(x k - E) <= 2, summed in float32 over a block and
-// added to a float64 S.  Moving the reference rescales S by an exact power of
-// two, so S is the sum of exactly the terms a later exp2(x k - E) reproduces
+// added to a float64 sum.  Moving the reference rescales by an exact power of
+// two, so the sum holds exactly the terms a later exp2(x k - E) reproduces
 // (no rounded rescale factors), and its float64 accumulation leaves only the
 // per-element rounding, which averages out.
+// What is accumulated is the rest R: the sum over every element but one copy
+// of the maximum.  The maximum's own term t = 2^(M k - E) joins only when the
+// row is complete (stats64_total), so where one token carries nearly all of
+// a row's mass no float32 addition happens at its magnitude, and the rest
+// relative to it, R / t, keeps the relative precision of R
+// (stats64_rest_rel): the mass off that token is R / (t + R).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float ref_exp(float M, float k) { return floorf(M * k); }
 
-// S (relative to the reference of M) rescaled to the reference E; 0 when M is
-// -inf.
+// A sum relative to the reference of M, rescaled to the reference E; 0 when
+// M is -inf.
 __device__ __forceinline__ double rescale_to(double S, float M, float k, float E) {
   if (M == -kInf) return 0.0;
   // Shifts below -1100 leave 0 in float64 anyway; the clamp keeps huge
@@ -201,14 +211,41 @@ __device__ __forceinline__ double rescale_to(double S, float M, float k, float E
   return __builtin_ldexp(S, static_cast<int>(fmaxf(ref_exp(M, k) - E, -1100.f)));
 }
 
-// Per-lane statistics for SoftmaxStats64's scheme: S in float32 relative to
-// E = floor(M k), rescaled by exact powers of two (ldexp) when E moves.  A
-// lane's float32 rounding is independent of the other lanes', so it averages
-// out over the float64 merge of the lanes (wave_stats64).
+// The maximum's term 2^(M k - E) for E = floor(M k), in [1, 2): one exp2 of
+// an argument formed with a single rounding (fma).
+__device__ __forceinline__ float max_term(float M, float k) {
+  return fast_exp2(__builtin_fmaf(M, k, -ref_exp(M, k)));
+}
+
+// The row sum S relative to E = floor(M k): the rest R plus the maximum's
+// term.
+__device__ __forceinline__ double stats64_total(float M, double R, float k) {
+  return R + static_cast<double>(max_term(M, k));
+}
+
+// The rest relative to the maximum's term, R / 2^(M k - E) = S / 2^(M k - E)
+// - 1 without that cancellation: the mass off one copy of the maximum over
+// the mass of that copy.
+__device__ __forceinline__ double stats64_rest_rel(float M, double R, float k) {
+  return R / static_cast<double>(max_term(M, k));
+}
+
+// log2 of the ratio of two rows' sums, each relative to its maximum's term:
+// log2((1 + r1) / (1 + r2)) for the rests r = stats64_rest_rel, through
+// log1p of (r1 - r2) / (1 + r2), so that it keeps the rests' relative
+// precision where both are small.
+__device__ __forceinline__ float log2_sum_ratio(double r1, double r2) {
+  return log1pf(static_cast<float>((r1 - r2) / (1.0 + r2))) * 1.4426950408889634f;
+}
+
+// Per-lane statistics for this scheme: R in float32 relative to E = floor(M
+// k), rescaled by exact powers of two (ldexp) when E moves.  A lane's float32
+// rounding is independent of the other lanes', so it averages out over the
+// float64 merge of the lanes (wave_stats64).
 struct SoftmaxStats64 {
   float M = -kInf;
   float E = 0.f;
-  float S = 0.f;
+  float R = 0.f;
   float k;  // log2(e) / T
   __device__ explicit SoftmaxStats64(float k_) : k(k_) {}
 
@@ -221,13 +258,25 @@ struct SoftmaxStats64 {
     if (Mn == -kInf) return;                 // nothing but -inf so far
     if (!(Mn < kInf)) { M = Mn; return; }    // NaN / +inf: the row is in error
     const float En = ref_exp(Mn, k);
-    // E <= En; S is 0 until the first finite maximum, and shifts below -200
-    // leave 0 in float32 anyway.
-    S = __builtin_ldexpf(S, static_cast<int>(fmaxf(E - En, -200.f)));
-    float s = 0.f;
+    // E <= En; R is 0 until the second finite element, and shifts below
+    // -200 leave 0 in float32 anyway.
+    R = __builtin_ldexpf(R, static_cast<int>(fmaxf(E - En, -200.f)));
+    // Elements are taken in pairs with the running maximum r before them:
+    // the two smaller of (r, x[j], x[j+1]) add their terms and the largest
+    // becomes r.  Each step only orders three values, so the terms added are
+    // those of the old M and the x[j] but one copy of the final r = Mn.
+    float run = M, s = 0.f;
 #pragma unroll
-    for (int j = 0; j < N; ++j) s += fast_exp2(__builtin_fmaf(x[j], k, -En));
-    S += s;
+    for (int j = 0; j + 1 < N; j += 2) {
+      const float a = x[j], b = x[j + 1];
+      const float lo = fminp(fminp(a, b), run);
+      const float mid = __builtin_amdgcn_fmed3f(a, b, run);
+      run = fmaxp(fmaxp(a, b), run);
+      s += fast_exp2(__builtin_fmaf(lo, k, -En));
+      s += fast_exp2(__builtin_fmaf(mid, k, -En));
+    }
+    if constexpr ((N & 1) != 0) s += fast_exp2(__builtin_fmaf(fminp(x[N - 1], run), k, -En));
+    R += s;
     M = Mn;
     E = En;
   }
@@ -237,13 +286,20 @@ struct SoftmaxStats64 {
   __device__ __forceinline__ void block(const float* x, int64_t, int64_t) { absorb<U * W>(x); }
 };
 
-// Merge two (M, S) pairs with float64 S; -inf / NaN maxima propagate.
-__device__ __forceinline__ void stats64_merge(float& M, double& S, float M2, double S2, float k) {
+// Merge two (M, R) pairs with float64 rests: the smaller maximum's own term
+// joins the rest.  -inf / NaN maxima propagate.
+__device__ __forceinline__ void stats64_merge(float& M, double& R, float M2, double R2, float k) {
   const float Mn = fmaxp(M, M2);
-  if (Mn == -kInf) { M = Mn; S = 0.0; return; }
+  if (Mn == -kInf) { M = Mn; R = 0.0; return; }
   if (!(Mn < kInf)) { M = Mn; return; }
   const float E = ref_exp(Mn, k);
-  S = rescale_to(S, M, k, E) + rescale_to(S2, M2, k, E);
+  // The partial with the smaller maximum lo brings its rest and lo's own
+  // term, rescaled by an exact power of two; the other keeps its reference.
+  const bool first_hi = M >= M2;
+  const float lo = first_hi ? M2 : M;
+  const double Rhi = first_hi ? R : R2;
+  const double Rlo = first_hi ? R2 : R;
+  R = lo == -kInf ? Rhi : Rhi + rescale_to(Rlo + static_cast<double>(max_term(lo, k)), lo, k, E);
   M = Mn;
 }
 
@@ -390,8 +446,8 @@ __device__ __forceinline__ double readlane63(double v) {
   return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// Wave-level (M, S) reduction with float64 S, same lane moves as wave_stats;
-// S enters as each lane's sum relative to floor(M k).
+// Wave-level (M, R) reduction with float64 rests (SoftmaxStats64), same lane
+// moves as wave_stats; R enters as each lane's rest relative to floor(M k).
 __device__ __forceinline__ void wave_stats64(float& M, double& S, float k) {
 #define DBV_STATS64_STEP(C, R)                                                \
   stats64_merge(M, S, dpp_move<C, R>(-kInf, M), dpp_move<C, R>(0.0, S), k);
@@ -607,7 +663,8 @@ __device__ __forceinline__ void combine_rows_stats(int nrows, const float2* part
   }
 }
 
-// kf(r) is the log2(e)/T of row r.
+// kf(r) is the log2(e)/T of row r; done(r, M, R) receives the row's
+// maximum and float64 rest.
 template <int NT = kBlock, class KFn, class SpanFn, class DoneFn>
 __device__ __forceinline__ void combine_rows_stats64(int nrows, const Stat64* part, KFn kf, SpanFn span,
                                                      DoneFn done) {
@@ -627,10 +684,10 @@ __device__ __forceinline__ void combine_rows_stats64(int nrows, const Stat64* pa
         for (int q = 0; q < kRowLoads; ++q) {
           const int64_t j = j0 + sub + static_cast<int64_t>(q) * kRowLanes;
           if (j < n) buf[q] = p[j];
-          else { buf[q].M = -kInf; buf[q].S = 0.0; }
+          else { buf[q].M = -kInf; buf[q].R = 0.0; }
         }
 #pragma unroll
-        for (int q = 0; q < kRowLoads; ++q) stats64_merge(M, S, buf[q].M, buf[q].S, k);
+        for (int q = 0; q < kRowLoads; ++q) stats64_merge(M, S, buf[q].M, buf[q].R, k);
       }
     }
 #pragma unroll
@@ -698,9 +755,9 @@ __device__ __forceinline__ int max_status(float M) {
 }
 
 // Status of a softmax row from its float64 statistics (M, S).
-__device__ __forceinline__ int stats64_status(float M, double S) {
+__device__ __forceinline__ int stats64_status(float M, double R) {
   int st = max_status(M);
-  if (!st && !(S > 0.0 && S < 1e300)) st = SEQ_NONFINITE;
+  if (!st && !(R >= 0.0 && R < 1e300)) st = SEQ_NONFINITE;
   return st;
 }
 

@@ -59,6 +59,7 @@ struct SampleArgs {
   int32_t* status;
   float* accept_margin;                // [B, K] |u - alpha| (NULL: not written)
   float* draw_margin;                  // [B] the draw's distance from a CDF step over Z (NULL: not written)
+  float* row_tv;                       // [B, K] TV(p_i, q_i) of draft rows (NULL: not computed)
   Stat64* stats;                       // per (slot, wave): M and the float64 sum
   float2* gpart;                       // per (slot, wave), with Gumbel rows
   int32_t* pre;                        // [B + 1] first stream row per sequence
@@ -108,9 +109,14 @@ struct TreeArgs {
   int32_t* count;                            // rows in the stream
   int32_t* list;                             // stream row -> flat row id
   int32_t* map;                              // flat row id -> stream row or -1
+  float* pos_margin; float* tok_margin;      // [B, S] diagnostics (NULL: not written)
   float2* conf;                              // per (slot, wave)
   float2* pick;                              // per (state, split2)
-  int32_t* sel;                              // per state
+  float* pick2;                              // per (state, split2): second-best score (tok_margin only)
+  int32_t* sel;                              // per state: s*
+  float* selconf;                            // per state: confidence at s*
+  int32_t* selstat;                          // per state: status of its rows
+  float* selgap;                             // per state: relative gap of the two best confidences
   int64_t grid;                              // groups of the row-streaming launch
   int split2; int64_t chunk2;
 };

@@ -202,20 +202,26 @@ struct DrawRecord {
                      // integer reference of the row maximum and isp = 1/S
                      // (times the Cactus rescaling of the other tokens; 0
                      // where the residual is known to vanish)
-  float C;           // residual: log2(q(v) / p~(v)) = (y_v kq - x_v kp) + C
+  float mp, mq;      // the largest logits of target and drafter row h
+  float C;           // residual: log2(q(v) / p~(v)) =
+                     //   ((y_v - mq) kq - (x_v - mp) kp) + C
   float u;           // resample uniform of row h
   int excl;          // Cactus: the drafted token of row h, whose weight is
   float wexcl;       // wexcl = [gamma - q(d)]_+; -1 for the linear rule
   int fixed;         // >= 0: the committed token is known (a coupled-noise
                      // commit) and nothing is drawn; -1 otherwise
+  int pad;
+  double isp64;      // 1/S in float64 (stored sparse Q: p(v) - Q(v) of the
+                     // listed tokens is formed in float64)
 };
 
 // Softmax statistics partial of one piece of a sampling row: the running
-// maximum M and the sum S of exp2(x k - floor(M k)) in float64.
+// maximum M and the rest R, the sum of exp2(x k - floor(M k)) over all
+// elements but one copy of M, in float64.
 struct Stat64 {
   float M;
   float pad;
-  double S;
+  double R;
 };
 
 // The stored sparse Q of the draw row h, handed from the mass kernel to the
@@ -289,14 +295,20 @@ struct TreePlan {
   size_t off_map;      // int32 [max_rows]: stream row of flat row id, or -1
   size_t off_conf;     // float2 {M, S} per (slot, wave)
   size_t off_pick;     // float2 {score, index-as-bits} per (state, split2)
+  size_t off_pick2;    // float per (state, split2): the chunk's second-best score
   size_t off_sel;      // int per state: selected position
+  size_t off_selconf;  // float per state: confidence at the selected position
+  size_t off_selstat;  // int per state: status bits of the state's rows
+  size_t off_selgap;   // float per state: relative gap of the two best confidences
   size_t bytes;
 };
 
-// Vocabulary chunks per state for the Gumbel argmax (one row per state).
+// Vocabulary chunks per state for the Gumbel argmax (one row per state):
+// about kGumbelGroups groups in all, chunks of at least 4096 elements.
+constexpr int64_t kGumbelGroups = 4096;
 inline int choose_split(int64_t rows, int64_t V) {
   if (rows <= 0) return 1;
-  int64_t s = cdiv(kMaxGrid, rows);
+  int64_t s = cdiv(kGumbelGroups, rows);
   const int64_t cap = V / 4096 > 0 ? V / 4096 : 1;
   if (s > cap) s = cap;
   if (s > kMaxSplit) s = kMaxSplit;
@@ -317,8 +329,12 @@ inline TreePlan plan_tree(int B, int S, int L, int V) {
   p.off_map = p.off_list + align256(static_cast<size_t>(p.max_rows) * 4);
   p.off_conf = p.off_map + align256(static_cast<size_t>(p.max_rows) * 4);
   p.off_pick = p.off_conf + partial_bytes(p.max_rows);
-  p.off_sel = p.off_pick + align256(static_cast<size_t>(p.states) * p.split2 * 8);
-  p.bytes = p.off_sel + align256(static_cast<size_t>(p.states) * 4);
+  p.off_pick2 = p.off_pick + align256(static_cast<size_t>(p.states) * p.split2 * 8);
+  p.off_sel = p.off_pick2 + align256(static_cast<size_t>(p.states) * p.split2 * 4);
+  p.off_selconf = p.off_sel + align256(static_cast<size_t>(p.states) * 4);
+  p.off_selstat = p.off_selconf + align256(static_cast<size_t>(p.states) * 4);
+  p.off_selgap = p.off_selstat + align256(static_cast<size_t>(p.states) * 4);
+  p.bytes = p.off_selgap + align256(static_cast<size_t>(p.states) * 4);
   return p;
 }
 

@@ -290,23 +290,23 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
   SoftmaxStats64 acc(a.kp);
   ArgmaxPick accp;
   int64_t pend = -1;
-  auto put = [&](int64_t slot, float M, double S) {
+  auto put = [&](int64_t slot, float M, double R) {
     Stat64 st;
     st.M = M;
     st.pad = 0.f;
-    st.S = S;
+    st.R = R;
     a.stats[slot] = st;
   };
   auto flush = [&]() {
     float M = acc.M;
-    double S = static_cast<double>(acc.S);
-    wave_stats64(M, S, a.kp);
+    double R = static_cast<double>(acc.R);
+    wave_stats64(M, R, a.kp);
     float v = accp.best;
     int ii = static_cast<int>(accp.bidx);
     int nan = accp.nan ? 1 : 0;
     wave_argmax(v, ii, nan);
     if (lane_id() == 0) {
-      put((pend + g) * kWaves + wave_id(), M, S);
+      put((pend + g) * kWaves + wave_id(), M, R);
       a.gpart[(pend + g) * kWaves + wave_id()] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
     }
     acc = SoftmaxStats64(a.kp);
@@ -342,11 +342,27 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
     SoftmaxStats64 st(k);
     stream_row<DT, kUnroll>(rowp, v0, v1, st);
     float M = st.M;
-    double S = static_cast<double>(st.S);
-    wave_stats64(M, S, k);
-    if (lane_id() == 0) put((r + g) * kWaves + wave_id(), M, S);
+    double R = static_cast<double>(st.R);
+    wave_stats64(M, R, k);
+    if (lane_id() == 0) put((r + g) * kWaves + wave_id(), M, R);
   });
   if (GUM && pend >= 0) flush();
+}
+
+// 1 - 2^d for d < 0 to float32 relative precision also where 2^d is close
+// to 1: for d > -0.5 a Taylor polynomial of -expm1(d ln 2) (the first
+// omitted term is below 2e-8 relative there), else 1 - exp2(d).  (Where one
+// token carries nearly all of both rows' mass, 1 - exp2(d) alone would leave
+// an error of an ulp of 1 on the whole residual.)
+__device__ __forceinline__ float one_minus_exp2(float d) {
+  const float z = d * 0.6931471805599453f;
+  float t = __builtin_fmaf(z, 1.f / 5040.f, 1.f / 720.f);
+  t = __builtin_fmaf(z, t, 1.f / 120.f);
+  t = __builtin_fmaf(z, t, 1.f / 24.f);
+  t = __builtin_fmaf(z, t, 1.f / 6.f);
+  t = __builtin_fmaf(z, t, 0.5f);
+  t = __builtin_fmaf(z, t, 1.f);
+  return d > -0.5f ? -z * t : 1.f - fast_exp2(d);
 }
 
 // Per-element weight of the draw: residual [p~ - q]_+ or the bonus weight.
@@ -354,36 +370,45 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
 // residual is p (1 - 2^d) with d = log2(q/p) = (y kq - x kp) + C formed from
 // the logits directly (x kp split into an exact sum hx + lx), so the
 // normalisers never enter as two rounded scales whose difference would
-// dominate where p and q nearly cancel: what is left is the rounding of
-// 2^d, about one ulp of 1 times p per element, independent between
-// elements.  For the linear rule p~ = p up to the
+// dominate where p and q nearly cancel, and each weight keeps float32
+// relative precision.  For the linear rule p~ = p up to the
 // (1 - lambda) factor, which the normalisation removes; for the Cactus rule
 // isp also carries the rescaling (1 - gamma) / (1 - p(d)) of every token but
 // the drafted one, element `excl`, whose weight is wexcl = [gamma - q(d)]_+.
 struct DrawWeight {
   float kp, ep, isp, kq, C;
+  float mp, mq;  // the rows' largest logits
   int resid;
-  int same_t;   // kp == kq: y kq - x kp = (y - x) k, with y - x exact
+  int same_t;    // kp == kq
   int excl;
   float wexcl;
+  double isp64;
+  // d = log2(q(v) / p~(v)) from the logits' distances to their rows' maxima
+  // (exact in float32 near the maxima, 0 at a token that is both rows'
+  // maximum, whose d is then C itself).
+  __device__ __forceinline__ float log_ratio(float x, float y) const {
+    const float dx = x - mp, dy = y - mq;
+    return same_t ? __builtin_fmaf(dy - dx, kp, C) : __builtin_fmaf(dy, kq, -(dx * kp)) + C;
+  }
   __device__ __forceinline__ float operator()(float x, float y) const {
     const float e = fast_exp2(__builtin_fmaf(x, kp, -ep));
     if (!resid) return e;
-    float d;
-    if (same_t) {
-      d = __builtin_fmaf(y - x, kp, C);
-    } else {
-      const float hx = x * kp;
-      const float lx = __builtin_fmaf(x, kp, -hx);
-      d = (__builtin_fmaf(y, kq, -hx) - lx) + C;
-    }
+    const float d = log_ratio(x, y);
     // d >= 0: q >= p; d NaN only where p = 0 (x = -inf)
-    return d < 0.f ? e * isp * (1.f - fast_exp2(d)) : 0.f;
+    return d < 0.f ? e * isp * one_minus_exp2(d) : 0.f;
   }
   // The weight of element e.
   __device__ __forceinline__ float at(uint32_t e, float x, float y) const {
     const float v = (*this)(x, y);
     return static_cast<int>(e) == excl ? wexcl : v;
+  }
+  // [p - Q]_+ against a stored sparse Q: p itself off the list (Q = 0); on
+  // it the difference is formed in float64, where p and Q may nearly cancel.
+  __device__ __forceinline__ float sparse(float x, float q) const {
+    const float p = fast_exp2(__builtin_fmaf(x, kp, -ep)) * isp;
+    if (q == 0.f) return p;
+    const double pd = exp2(static_cast<double>(x) * static_cast<double>(kp) - static_cast<double>(ep)) * isp64;
+    return static_cast<float>(fmax(pd - static_cast<double>(q), 0.0));
   }
 };
 
@@ -460,16 +485,13 @@ struct QList {
 // SP: the residual against a stored sparse Q, weight [p - Q]_+ with p =
 // exp2(x kp + cp) isp and Q from `ql`; no drafter row is read.
 template <int DT, int NW, int TB = kTileBatch, bool SP = false>
-__device__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo, int t_hi, bool vec,
+__device__ __forceinline__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo, int t_hi, bool vec,
                             const DrawWeight& w, float* out, const QList* ql = nullptr) {
   using E = Elem<DT>;
   constexpr int W = E::kVec;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const uint32_t Vn = static_cast<uint32_t>(V);
-  auto sparse_w = [&](float x, float q) {
-    return fmaxf(fast_exp2(__builtin_fmaf(x, w.kp, -w.ep)) * w.isp - q, 0.f);
-  };
   for (int t0 = t_lo + wv; t0 < t_hi; t0 += NW * TB) {
     u32x4 rx[TB], ry[TB];
     bool full[TB];
@@ -500,7 +522,7 @@ __device__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo,
           }
           ql->lookup<W>(e, q);
 #pragma unroll
-          for (int j = 0; j < W; ++j) m += e + j < Vn ? sparse_w(x[j], q[j]) : 0.f;
+          for (int j = 0; j < W; ++j) m += e + j < Vn ? w.sparse(x[j], q[j]) : 0.f;
         } else if (full[k]) {
           float x[W], y[W];
           E::unpack(rx[k], x);
@@ -551,10 +573,10 @@ __device__ __forceinline__ float group_exclusive_scan_f(float v, float& total, f
 // chain, and the token chain against stored sparse Q.
 enum : int { FAM_TOKEN = 0, FAM_SPOT = 1, FAM_SPARSE = 2 };
 
-// The probability of a logit x in a row with statistics (M, S) (float64 S
+// The probability of a logit x in a row with statistics (M, R) (float64 rest
 // relative to the reference floor(M k)).
-__device__ __forceinline__ float prob64(float x, float k, float M, double S) {
-  return fast_exp2(__builtin_fmaf(x, k, -ref_exp(M, k))) * static_cast<float>(1.0 / S);
+__device__ __forceinline__ float prob64(float x, float k, float M, double R) {
+  return fast_exp2(__builtin_fmaf(x, k, -ref_exp(M, k))) * static_cast<float>(1.0 / stats64_total(M, R, k));
 }
 
 // LDS of the decision step (per sequence): row statistics of the target rows
@@ -562,11 +584,11 @@ __device__ __forceinline__ float prob64(float x, float k, float M, double S) {
 // draft.
 struct DecideLds {
   float Mp[kMaxDraft + 1];
-  double Sp[kMaxDraft + 1];
+  double Rp[kMaxDraft + 1];
   // Drafter rows' statistics, or (stored sparse Q) each draft's token and
   // Q(d) summed from its row's entries.
   union { float Mq[kMaxDraft]; float qd[kMaxDraft]; };
-  union { double Sq[kMaxDraft]; int dtok[kMaxDraft]; };
+  union { double Rq[kMaxDraft]; int dtok[kMaxDraft]; };
   int g[kMaxDraft + 1];      // joint-space chain: Gumbel argmax of target rows
   int st, h;
   int dh, modeh;
@@ -583,7 +605,7 @@ struct DecideLds {
 // Returns the draw record: row h, its weight parameters and the uniform; its
 // status carries the error bits when there is nothing to draw.
 template <int DT, int NT, int FAM>
-__device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, DecideLds& s) {
+__device__ __forceinline__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, DecideLds& s) {
   constexpr int DPT = (kMaxDraft + NT - 1) / NT;   // drafts of one thread
   using E = Elem<DT>;
   const int t = threadIdx.x;
@@ -667,13 +689,13 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
             cnt *= kWaves;
           }
         },
-        [&](int r, float M, double S) {
+        [&](int r, float M, double R) {
           if (r <= n) {
-            s.Mp[r] = M; s.Sp[r] = S;
+            s.Mp[r] = M; s.Rp[r] = R;
           } else {
-            s.Mq[r - n - 1] = M; s.Sq[r - n - 1] = S;
+            s.Mq[r - n - 1] = M; s.Rq[r - n - 1] = R;
           }
-          st |= stats64_status(M, S);
+          st |= stats64_status(M, R);
         });
     if (P > 1)
       combine_rows_pick<NT>(n + 1, a.gpart, tspan, [&](int r, float v, int idx, int nan) {
@@ -751,13 +773,13 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
     float p = 0.f, q = 0.f, pt = 0.f, al = 0.f;
     mk[k] = 0;
     if (i < n) {
-      p = prob64(xi[k], a.kp, s.Mp[i], s.Sp[i]);
-      q = sparse ? s.qd[i] : prob64(yi[k], a.kq, s.Mq[i], s.Sq[i]);
+      p = prob64(xi[k], a.kp, s.Mp[i], s.Rp[i]);
+      q = sparse ? s.qd[i] : prob64(yi[k], a.kq, s.Mq[i], s.Rq[i]);
       bool acc;
       if (spot) {
         const bool on = ppk[k] == psk[k];
         // the drafter's confidence at s*: its largest token probability
-        mk[k] = (a.gumbel && prob64(s.Mq[i], a.kq, s.Mq[i], s.Sq[i]) >= a.tau) ? 1 : 0;
+        mk[k] = (a.gumbel && prob64(s.Mq[i], a.kq, s.Mq[i], s.Rq[i]) >= a.tau) ? 1 : 0;
         q *= ck[k];
         pt = p;
         if (mk[k]) {
@@ -809,24 +831,20 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
   rec.h = h;
   rec.resid = resid ? (sparse ? 2 : 1) : 0;
   rec.ep = ref_exp(s.Mp[h], a.kp);
-  rec.isp = static_cast<float>(1.0 / s.Sp[h]);
-  // log2(q(v) / p(v)) = (y_v kq - x_v kp) + C: the integer references and
-  // the float64 sums leave C small where p and q are close, so the residual
-  // weights keep their relative precision there.
-  // C = log2(Sp 2^ep / (Sq 2^eq)), the log-partition difference of the two
-  // rows, from the ratio formed in float64 (exact power-of-two scaling):
-  // near 1 through its distance from 1 (so C keeps relative precision where
-  // it is small), elsewhere through mantissa and exponent.
+  rec.isp64 = 1.0 / stats64_total(s.Mp[h], s.Rp[h], a.kp);
+  rec.isp = static_cast<float>(rec.isp64);
+  rec.mp = s.Mp[h];
+  rec.mq = 0.f;
+  // log2(q(v) / p(v)) = ((y_v - mq) kq - (x_v - mp) kp) + C with
+  // C = log2(Sp' / Sq'), Sp' = 1 + Rp' the target row's sum relative to its
+  // maximum's term (Rp' its rest relative to it, likewise for q).  In that
+  // form C is exact to the rests' relative precision: where one token holds
+  // nearly all of both rows' mass, C is the small difference of the two
+  // rests, which the residual weight at that token needs.
   float Cf = 0.f;
   if (resid && !sparse) {
-    const double ratio = __builtin_ldexp(s.Sp[h] / s.Sq[h], static_cast<int>(rec.ep - ref_exp(s.Mq[h], a.kq)));
-    if (fabs(ratio - 1.0) < 0.25) {
-      Cf = log1pf(static_cast<float>(ratio - 1.0)) * kLog2e;
-    } else {
-      int ex;
-      const double m = frexp(ratio, &ex);   // ratio = m 2^ex, m in [0.5, 1)
-      Cf = static_cast<float>(ex) + log2f(static_cast<float>(m));
-    }
+    rec.mq = s.Mq[h];
+    Cf = log2_sum_ratio(stats64_rest_rel(s.Mp[h], s.Rp[h], a.kp), stats64_rest_rel(s.Mq[h], s.Rq[h], a.kq));
   }
   rec.u = a.u_resample[static_cast<int64_t>(b) * (a.K + 1) + h];
   if (resid && a.rule == RULE_LINEAR && !(a.lam < 1.f)) {
@@ -834,6 +852,7 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
     // (a draft is rejected only where q(d) = 0); the draw then falls back to
     // p like any residual of zero mass.
     rec.isp = 0.f;
+    rec.isp64 = 0.0;
   }
   rec.excl = -1;
   rec.wexcl = 0.f;
@@ -850,12 +869,16 @@ __device__ DrawRecord draw_decide(const SampleArgs& a, int b, bool first, Decide
   }
   if (resid && a.rule == RULE_CACTUS) {
     // p~(v) = (1 - gamma) / (1 - p(d)) p(v) for v != d, p~(d) = gamma.
-    const float ph = s.ph;
-    const float c_rest = ph < 1.f ? static_cast<float>((1.0 - static_cast<double>(s.pth)) /
-                                                       (1.0 - static_cast<double>(ph)))
-                                  : 0.f;
-    rec.isp *= c_rest;
-    Cf -= log2f(c_rest);   // residual [c_rest p - q]_+
+    // c_rest = 1 - (gamma - p(d)) / (1 - p(d)) is often within an ulp of 1:
+    // its logarithm comes from the excess gamma - p(d) (exact in float64)
+    // through log1p.
+    const double ph = s.ph;
+    const double c_rest = ph < 1.0 ? (1.0 - static_cast<double>(s.pth)) / (1.0 - ph) : 0.0;
+    rec.isp = static_cast<float>(rec.isp * c_rest);
+    rec.isp64 *= c_rest;
+    // residual [c_rest p - q]_+
+    Cf -= ph < 1.0 ? static_cast<float>(log1p(-(static_cast<double>(s.pth) - ph) / (1.0 - ph)) * 1.4426950408889634)
+                   : -kInf;
     rec.excl = s.dh;
     rec.wexcl = fmaxf(s.pth - s.qh, 0.f);
   }
@@ -867,6 +890,8 @@ __device__ __forceinline__ DrawWeight draw_weight(const SampleArgs& a, const Dra
   DrawWeight w;
   w.kp = a.kp; w.ep = r.ep; w.isp = r.isp;
   w.kq = a.kq; w.C = r.C;
+  w.mp = r.mp; w.mq = r.mq;
+  w.isp64 = r.isp64;
   w.resid = r.resid;
   w.same_t = a.kp == a.kq;
   w.excl = r.excl;
@@ -942,6 +967,147 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
   tile_masses<DT, kWaves, 4>(xr, yr, a.V, t_lo, t_hi, vec, w, out);
 }
 
+// Combined float64 statistics (maximum, rest) of one stream row's partials
+// (one thread).
+__device__ __forceinline__ void merge_span_stats64(const Stat64* part, int64_t first, int64_t n, float k, float& M,
+                                                   double& R) {
+  M = -kInf;
+  R = 0.0;
+  for (int64_t j = 0; j < n; ++j) stats64_merge(M, R, part[first + j].M, part[first + j].R, k);
+}
+
+// Diagnostic mode: TV(p_i, q_i) = 1/2 sum_v |p_i(v) - q_i(v)| of draft row i
+// (Two Tradeoffs Sec. 2: the lossless acceptance rate of the row is 1 - TV),
+// one group per (sequence, draft row).  Dense rows: both rows are streamed
+// and |p - q| is p (1 - 2^d) where q < p, q (1 - 2^-d) elsewhere, with
+// d = log2(q/p) from the logits as in the draw.  Stored sparse Q: the sum
+// needs only the stored tokens, 1 - sum_list p + sum_list |p - Q|.
+template <int DT, int FAM>
+__global__ __launch_bounds__(kBlock) void k_row_tv(SampleArgs a) {
+  using E = Elem<DT>;
+  __shared__ float s_red[kWaves];
+  __shared__ float s_row[8];   // ep, isp, eq, isq, C, status, mp, mq
+  const int b = blockIdx.x / a.K;
+  const int i = blockIdx.x - b * a.K;
+  const int t = threadIdx.x;
+  bool nbad;
+  const int n = draft_count(a.draft_len, b, a.K, nbad);
+  float* out = a.row_tv + static_cast<int64_t>(b) * a.K + i;
+  if (nbad || i >= n) {
+    if (t == 0) *out = 0.f;
+    return;
+  }
+  const int p0 = a.pre[b];
+  const FlatSplit f = make_split(a.pre[a.B], a.V, E::kBytes, a.grid);
+  const int P = (FAM == FAM_SPOT && a.gumbel) ? gumbel_parts(E::kBytes) : 1;
+  if (t == 0) {
+    // target row i: P stream rows, one partial per group that read any part
+    const int64_t v = p0 + static_cast<int64_t>(i) * P;
+    const int64_t glo = split_group(f, v * f.V);
+    const int64_t ghi = split_group(f, (v + P) * f.V - 1);
+    float Mp, Mq = 0.f;
+    double Rp, Rq = 0.0;
+    merge_span_stats64(a.stats, (v + glo) * kWaves, (ghi - glo + 1) * kWaves, a.kp, Mp, Rp);
+    int st = stats64_status(Mp, Rp);
+    if (a.drows) {
+      int64_t first, cnt;
+      split_row_slots(f, p0 + static_cast<int64_t>(P) * (n + 1) + i, first, cnt);
+      merge_span_stats64(a.stats, first * kWaves, cnt * kWaves, a.kq, Mq, Rq);
+      st |= stats64_status(Mq, Rq);
+    }
+    s_row[0] = ref_exp(Mp, a.kp);
+    s_row[5] = __int_as_float(st);
+    s_row[6] = Mp;
+    s_row[7] = Mq;
+    if (!(st & SEQ_ERROR_MASK)) {
+      s_row[1] = static_cast<float>(1.0 / stats64_total(Mp, Rp, a.kp));
+      if (a.drows) {
+        s_row[2] = ref_exp(Mq, a.kq);
+        s_row[3] = static_cast<float>(1.0 / stats64_total(Mq, Rq, a.kq));
+        s_row[4] = log2_sum_ratio(stats64_rest_rel(Mp, Rp, a.kp), stats64_rest_rel(Mq, Rq, a.kq));
+      }
+    }
+  }
+  __syncthreads();
+  if (__float_as_int(s_row[5]) & SEQ_ERROR_MASK) {
+    if (t == 0) *out = __builtin_nanf("");
+    return;
+  }
+  const float ep = s_row[0], isp = s_row[1];
+  const char* xr = static_cast<const char*>(a.tgt) + (b * a.ts + static_cast<int64_t>(i) * a.tr) * E::kBytes;
+  float acc = 0.f;
+  if constexpr (FAM == FAM_SPARSE) {
+    // (S - sum_list e_v) / S + sum_list |e_v / S - Q_v| with e_v = exp2(x_v kp
+    // - ep) and S = sum_v e_v summed here in float64 over the whole row: the
+    // mass off the list is then a difference of two float64 sums of the same
+    // rounded terms (no cancellation error where the list holds nearly all
+    // of p), and the rounding of a dominant e_v cancels in e_v / S.
+    __shared__ double s_d[kWaves];
+    const int64_t row = static_cast<int64_t>(b) * a.K + i;
+    const int nz = min(a.qnnz[row], a.kmax);
+    double sa = 0.0;
+    const bool vec = (reinterpret_cast<uintptr_t>(xr) & 15u) == 0;
+    constexpr int W = E::kVec;
+    const int64_t nvec = vec ? a.V / W : 0;
+    for (int64_t j = t; j < nvec; j += kBlock) {
+      float x[W];
+      E::unpack(load16(xr + j * 16), x);
+#pragma unroll
+      for (int q = 0; q < W; ++q) sa += fast_exp2(__builtin_fmaf(x[q], a.kp, -ep));
+    }
+    for (int64_t e = nvec * W + t; e < a.V; e += kBlock) sa += fast_exp2(__builtin_fmaf(E::load1(xr, e), a.kp, -ep));
+    auto bsum = [&](double v) {
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      __syncthreads();
+      if ((t & 63) == 0) s_d[t >> 6] = v;
+      __syncthreads();
+      v = 0.0;
+      for (int w = 0; w < kWaves; ++w) v += s_d[w];
+      return v;
+    };
+    const double S = bsum(sa);
+    double se = 0.0, sd = 0.0;
+    for (int e = t; e < nz; e += kBlock) {
+      const int v = a.qidx[row * a.kmax + e];
+      if (v < 0 || v >= a.V) continue;
+      const double ev = fast_exp2(__builtin_fmaf(E::load1(xr, v), a.kp, -ep));
+      se += ev;
+      sd += fabs(ev / S - static_cast<double>(a.qprob[row * a.kmax + e]));
+    }
+    se = bsum(se);
+    sd = bsum(sd);
+    if (t == 0) *out = static_cast<float>(0.5 * ((S - se) / S + sd));
+    (void)isp;
+    return;
+  } else {
+    const float eq = s_row[2], isq = s_row[3];
+    const char* yr = static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(i) * a.dr) * E::kBytes;
+    DrawWeight w{};
+    w.kp = a.kp; w.kq = a.kq; w.C = s_row[4];
+    w.mp = s_row[6]; w.mq = s_row[7];
+    w.same_t = a.kp == a.kq;
+    auto absdiff = [&](float x, float y) {
+      const float d = w.log_ratio(x, y);
+      if (!(d == d)) return 0.f;   // both logits -inf: p = q = 0
+      return d < 0.f ? fast_exp2(__builtin_fmaf(x, a.kp, -ep)) * isp * one_minus_exp2(d)
+                     : fast_exp2(__builtin_fmaf(y, a.kq, -eq)) * isq * one_minus_exp2(-d);
+    };
+    const bool vec = ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0;
+    constexpr int W = E::kVec;
+    const int64_t nvec = vec ? a.V / W : 0;
+    for (int64_t j = t; j < nvec; j += kBlock) {
+      float x[W], y[W];
+      E::unpack(load16(xr + j * 16), x);
+      E::unpack(load16(yr + j * 16), y);
+#pragma unroll
+      for (int q = 0; q < W; ++q) acc += absdiff(x[q], y[q]);
+    }
+    for (int64_t e = nvec * W + t; e < a.V; e += kBlock) acc += absdiff(E::load1(xr, e), E::load1(yr, e));
+    acc = block_sum(acc, s_red);
+    if (t == 0) *out = 0.5f * acc;
+  }
+}
+
 constexpr int kDrawWaves = kDrawThreads / 64;
 
 // LDS of the select step for NT threads holding TPT tile masses each (the
@@ -993,7 +1159,7 @@ struct SparseLds {
 // output position i = t + k NT, and k = DPT reaches i <= K only where i >= h.
 // SPARSE: the call verifies against a stored sparse Q, whose LDS is sp.
 template <int DT, bool SPARSE, class LDS>
-__device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, int budget,
+__device__ __forceinline__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, int budget,
                             const int (&dt)[(kMaxDraft + LDS::kThreads - 1) / LDS::kThreads],
                             const float (&m0)[LDS::kTiles], LDS& s, SparseLds* sp) {
   constexpr int NT = LDS::kThreads;
@@ -1107,9 +1273,7 @@ __device__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, i
       ql.lookup<E::kVec>(static_cast<uint32_t>(e0), q);
 #pragma unroll
       for (int j = 0; j < E::kVec; ++j)
-        wt[j] = e0 + j < a.V
-                    ? fmaxf(fast_exp2(__builtin_fmaf(E::load1(xr, e0 + j), w.kp, -w.ep)) * w.isp - q[j], 0.f)
-                    : 0.f;
+        wt[j] = e0 + j < a.V ? w.sparse(E::load1(xr, e0 + j), q[j]) : 0.f;
     } else if (e0 + E::kVec <= a.V &&
                ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0) {
       // the lane's vector of the row (and of the drafter row) in one load each
@@ -1306,6 +1470,11 @@ bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const Tim
        {fn(k_draw_select<DT_F32, FAM_SPOT, SmallSelectLds>), fn(k_draw_select<DT_BF16, FAM_SPOT, SmallSelectLds>)},
        {fn(k_draw_select<DT_F32, FAM_SPARSE, SmallSelectLds>),
         fn(k_draw_select<DT_BF16, FAM_SPARSE, SmallSelectLds>)}}};
+  // [family][dtype == bf16]
+  static const void* const tv[3][2] = {{fn(k_row_tv<DT_F32, FAM_TOKEN>), fn(k_row_tv<DT_BF16, FAM_TOKEN>)},
+                                       {fn(k_row_tv<DT_F32, FAM_SPOT>), fn(k_row_tv<DT_BF16, FAM_SPOT>)},
+                                       {fn(k_row_tv<DT_F32, FAM_SPARSE>), fn(k_row_tv<DT_BF16, FAM_SPARSE>)}};
+  if (a.row_tv && !launch(tv[fam][bf], static_cast<int64_t>(a.B) * a.K, stream, a)) return false;
   if (a.tiles <= kFusedDrawTiles && fam != FAM_SPARSE)
     return launch_threads(fused[fam][bf], a.B, kDrawThreads, stream, a);
   const bool small = a.tiles <= kSmallSelect * kSmallSelectTiles;

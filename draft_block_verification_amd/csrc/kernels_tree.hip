@@ -20,6 +20,7 @@
 #include "dbv_launch.h"
 
 #include <climits>
+#include <type_traits>
 
 namespace dbv {
 
@@ -60,11 +61,26 @@ __global__ __launch_bounds__(kPlanThreads) void k_tree_plan(TreeArgs a) {
   int base = 0;  // stream rows listed by earlier passes
   for (uint32_t t0 = 0; t0 < F; t0 += kPlanThreads * kPlanPer) {
     const uint32_t f0 = t0 + threadIdx.x * kPlanPer;
+    // Every request of this thread's ids is issued before any is used (ids
+    // past F are clamped to F - 1 and ignored).
+    int ns[kPlanPer], pos[kPlanPer], ys[kPlanPer], ss[kPlanPer];
+    uint8_t mk[kPlanPer];
+#pragma unroll
+    for (int k = 0; k < kPlanPer; ++k) {
+      const uint32_t flat = f0 + k < F ? f0 + k : F - 1;
+      int b;
+      split_flat(a, flat, b, ys[k], ss[k]);
+      ns[k] = state_count(a.num_states, b, a.S);
+      const int64_t sy = static_cast<int64_t>(b) * a.S + ys[k];
+      pos[k] = a.fixed ? a.next_pos[sy] : 0;
+      mk[k] = a.fixed ? 0 : a.masked[flat];
+    }
     uint32_t bits = 0;
     int c = 0;
 #pragma unroll
     for (int k = 0; k < kPlanPer; ++k) {
-      if (f0 + k < F && tree_row_needed(a, f0 + k)) {
+      const bool need = f0 + k < F && ns[k] >= 0 && ys[k] < ns[k] && (a.fixed ? pos[k] == ss[k] : mk[k] != 0);
+      if (need) {
         bits |= 1u << k;
         ++c;
       }
@@ -115,35 +131,123 @@ __device__ __forceinline__ void combine_conf(const TreeArgs& a, const FlatSplit&
 }
 
 // s*(y): the masked position of largest confidence 1/S (lowest on ties), or
-// the given position in the fixed mode; -1 when there is none.  Every thread
-// of the group calls it; the result is uniform.
-__device__ int select_position(const TreeArgs& a, const FlatSplit& f, int b, int y, float* s_v, int* s_i,
-                                int* s_n, int* s_out) {
+// the given position in the fixed mode; -1 when there is none.  Also the
+// status bits of every row the state reads, the confidence at s*, and (with
+// `gap`) the relative gap 1 - S(s*)/S(second) of the two best confidences
+// (1 with a single masked position, 0 in the fixed mode).  Every thread of
+// the group calls it; the results are uniform.
+struct Selection {
+  int pos;
+  int status;
+  float conf;
+  float gap;
+};
+
+__device__ Selection select_position(const TreeArgs& a, const FlatSplit& f, int b, int y, bool gap, float* s_v,
+                                     int* s_i, int* s_n, int* s_out, float* s_f) {
   const int64_t sy = static_cast<int64_t>(b) * a.S + y;
+  Selection r{-1, 0, __builtin_nanf(""), 0.f};
   if (a.fixed) {
     const int np = a.next_pos[sy];
-    return (np >= 0 && np < a.L) ? np : -1;
+    if (np >= 0 && np < a.L) {
+      float M, S;
+      combine_conf(a, f, sy * a.L + np, M, S);
+      r.pos = np;
+      r.status = stats_status(M, S);
+      r.conf = 1.f / S;
+    }
+    return r;
   }
+  constexpr int kPer = (kMaxBlockLen + kBlock - 1) / kBlock;   // positions of one thread
+  float negs[kPer];
   float v = -kInf;
-  int idx = -1, nan = 0;
-  for (int s = threadIdx.x; s < a.L; s += kBlock) {
-    if (!a.masked[sy * a.L + s]) continue;
-    float M, S;
-    combine_conf(a, f, sy * a.L + s, M, S);
-    if (pick_better(-S, s, v, idx)) { v = -S; idx = s; }   // max of -S = min of S
+  int idx = -1, nan = 0, st = 0;
+  if (threadIdx.x == 0) s_out[1] = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int s = static_cast<int>(threadIdx.x) + k * kBlock;
+    negs[k] = -kInf;
+    if (s < a.L && a.masked[sy * a.L + s]) {
+      float M, S;
+      combine_conf(a, f, sy * a.L + s, M, S);
+      st |= stats_status(M, S);
+      negs[k] = -S;
+      if (pick_better(-S, s, v, idx)) { v = -S; idx = s; }   // max of -S = min of S
+    }
   }
+  __syncthreads();
+  if (st) atomicOr(&s_out[1], st);
   block_argmax(v, idx, nan, s_v, s_i, s_n);
-  if (threadIdx.x == 0) *s_out = idx;
+  if (threadIdx.x == 0) {
+    s_out[0] = idx;
+    s_f[0] = v;
+  }
   __syncthreads();
-  const int r = *s_out;
+  r.pos = s_out[0];
+  r.status = s_out[1];
+  const float best = s_f[0];
+  r.conf = r.pos >= 0 ? -1.f / best : __builtin_nanf("");
   __syncthreads();
+  if (gap && r.pos >= 0) {
+    // the largest -S over the other masked positions
+    float v2 = -kInf;
+    int i2 = -1, n2 = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int s = static_cast<int>(threadIdx.x) + k * kBlock;
+      if (s < a.L && s != r.pos && negs[k] > -kInf && pick_better(negs[k], s, v2, i2)) { v2 = negs[k]; i2 = s; }
+    }
+    block_argmax(v2, i2, n2, s_v, s_i, s_n);
+    if (threadIdx.x == 0) s_f[1] = i2 >= 0 ? 1.f - best / v2 : 1.f;   // 1 - S(s*) / S(second)
+    __syncthreads();
+    r.gap = s_f[1];
+    __syncthreads();
+  }
   return r;
 }
 
+// Lowest-index argmax that also keeps the second-largest score: per element
+// second = med3(best, second, x) before best = max(best, x), so two equal
+// largest scores leave second = best.
+struct ArgmaxPick2 : ArgmaxPick {
+  float second = -kInf;
+  template <int N>
+  __device__ __forceinline__ void group(const float* x, int64_t idx0) {
+    float b1 = best;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      second = __builtin_amdgcn_fmed3f(b1, second, x[j]);
+      b1 = fmaxf(b1, x[j]);
+    }
+    ArgmaxPick::group<N>(x, idx0);
+  }
+  template <int U, int W>
+  __device__ __forceinline__ void block(const float* x, int64_t idx0, int64_t ustride) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) group<W>(x + u * W, idx0 + u * ustride);
+  }
+};
+
+// The second-largest score of a group's elements, given each thread's
+// (best, index, second) and the group's argmax (best, idx) in thread 0:
+// the largest of every other thread's best and the winning thread's second.
+// Valid in thread 0.
+__device__ __forceinline__ float block_second(float tbest, int tidx, float tsecond, float best, int idx, float* s_v,
+                                              int* s_i, int* s_n) {
+  if (threadIdx.x == 0) { s_v[0] = best; s_i[0] = idx; }
+  __syncthreads();
+  const bool win = tbest == s_v[0] && tidx == s_i[0];
+  __syncthreads();
+  float c = win ? tsecond : tbest;
+  int ci = 0, cn = 0;
+  block_argmax(c, ci, cn, s_v, s_i, s_n);
+  return c;
+}
+
 // Argmax of z/T + g over a logit row and its Gumbel row read together.
-template <int DT>
+template <int DT, class Pick>
 __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64_t v1, float inv_t,
-                              ArgmaxPick& pk) {
+                              Pick& pk) {
   using E = Elem<DT>;
   constexpr int W = E::kVec;
   const int t = threadIdx.x;
@@ -155,7 +259,7 @@ __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64
   if (!gal) {  // Gumbel row not aligned with the logits: scalar path
     for (int64_t j = v0 + t; j < v1; j += kBlock) {
       float x[1] = {__builtin_fmaf(E::load1(xr, j), inv_t, gr[j])};
-      pk.group<1>(x, j);
+      pk.template group<1>(x, j);
     }
     return;
   }
@@ -163,7 +267,7 @@ __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64
   const int64_t a1 = a0 + nvec * W;
   if (t < head) {
     float x[1] = {__builtin_fmaf(E::load1(xr, v0 + t), inv_t, gr[v0 + t])};
-    pk.group<1>(x, v0 + t);
+    pk.template group<1>(x, v0 + t);
   }
   const char* xb = xr + a0 * E::kBytes;
   const char* gb = reinterpret_cast<const char*>(gr + a0);
@@ -185,8 +289,8 @@ __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64
       x0[j] = __builtin_fmaf(x0[j], inv_t, __uint_as_float(g0[j / 4][j % 4]));
       x1[j] = __builtin_fmaf(x1[j], inv_t, __uint_as_float(g1[j / 4][j % 4]));
     }
-    pk.group<W>(x0, a0 + i * W);
-    pk.group<W>(x1, a0 + (i + kBlock) * W);
+    pk.template group<W>(x0, a0 + i * W);
+    pk.template group<W>(x1, a0 + (i + kBlock) * W);
   }
   for (; i < nvec; i += kBlock) {
     u32x4 xv = load16(xb + i * 16);
@@ -197,16 +301,16 @@ __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64
     E::unpack(xv, x);
 #pragma unroll
     for (int j = 0; j < W; ++j) x[j] = __builtin_fmaf(x[j], inv_t, __uint_as_float(g[j / 4][j % 4]));
-    pk.group<W>(x, a0 + i * W);
+    pk.template group<W>(x, a0 + i * W);
   }
   if (a1 + t < v1) {
     float x[1] = {__builtin_fmaf(E::load1(xr, a1 + t), inv_t, gr[a1 + t])};
-    pk.group<1>(x, a1 + t);
+    pk.template group<1>(x, a1 + t);
   }
 }
 
-// The walk of one sequence.
-__device__ void tree_walk(const TreeArgs& a, const FlatSplit& f, int b, int* s_pos, int* s_tok) {
+// The walk of one sequence, from the per-state selections of k_tree_gumbel.
+__device__ void tree_walk(const TreeArgs& a, int b, int* s_pos, int* s_tok) {
   __shared__ int s_st, s_child, s_y, s_len, s_ncommit;
   const int t = threadIdx.x;
   const int S = a.S;
@@ -236,30 +340,18 @@ __device__ void tree_walk(const TreeArgs& a, const FlatSplit& f, int b, int* s_p
   __syncthreads();
   st = 0;
   const bool valid = !(s_st & SEQ_BAD_INPUT);
-  // Status of every row that was read: all masked rows (state equality).
-  if (valid && !a.fixed) {
-    const int64_t pairs = static_cast<int64_t>(ns) * a.L;
-    for (int64_t q = t; q < pairs; q += kBlock) {
-      const int64_t sy = base + q / a.L;
-      const int s = static_cast<int>(q % a.L);
-      if (!a.masked[sy * a.L + s]) continue;
-      float M, Sum;
-      combine_conf(a, f, sy * a.L + s, M, Sum);
-      st |= stats_status(M, Sum);
-    }
-  }
-  // Phi(y) per state.
+  // Phi(y) per state: s* with the status of the state's rows, the token
+  // from the chunks' picks (largest score, lowest index).
   for (int y = t; y < S; y += kBlock) {
     int pos = -1, tok = -1;
-    float conf = __builtin_nanf("");
+    float conf = __builtin_nanf(""), pgap = 0.f, tgap = 0.f;
     if (valid && y < ns) {
       const int64_t sy = base + y;
       pos = a.sel[sy];
+      st |= a.selstat[sy];
       if (pos >= 0) {
-        float M, Sum;
-        combine_conf(a, f, sy * a.L + pos, M, Sum);
-        st |= stats_status(M, Sum);
-        conf = 1.f / Sum;
+        conf = a.selconf[sy];
+        pgap = a.selgap[sy];
         float v = -kInf;
         int idx = -1, nan = 0;
         const float2* pk = a.pick + sy * a.split2;
@@ -270,6 +362,14 @@ __device__ void tree_walk(const TreeArgs& a, const FlatSplit& f, int b, int* s_p
         }
         st |= nan ? SEQ_NONFINITE : max_status(v);
         tok = idx;
+        if (a.tok_margin) {
+          float v2 = -kInf;
+          for (int k = 0; k < a.split2; ++k) {
+            const bool win = pk[k].x == v && __float_as_int(pk[k].y) == idx;
+            v2 = fmaxf(v2, win ? a.pick2[sy * a.split2 + k] : pk[k].x);
+          }
+          tgap = v - v2;
+        }
       }
     }
     s_pos[y] = pos;
@@ -277,6 +377,8 @@ __device__ void tree_walk(const TreeArgs& a, const FlatSplit& f, int b, int* s_p
     if (a.sel_pos) a.sel_pos[base + y] = pos;
     if (a.sel_tok) a.sel_tok[base + y] = tok;
     if (a.sel_conf) a.sel_conf[base + y] = conf;
+    if (a.pos_margin) a.pos_margin[base + y] = pgap;
+    if (a.tok_margin) a.tok_margin[base + y] = tgap;
   }
   if (st) atomicOr(&s_st, st);
   __syncthreads();
@@ -334,10 +436,15 @@ __device__ void tree_walk(const TreeArgs& a, const FlatSplit& f, int b, int* s_p
   }
 }
 
-template <int DT>
+// Per (state, vocabulary chunk): s*(y) (chunk 0 stores it with the state's
+// row status, the confidence at s* and the gap of the two best), then the
+// chunk's argmax of z/T + G[s*] (z at T = 0).  TWO: also the chunk's
+// second-largest score (tok_margin).
+template <int DT, bool TWO>
 __global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
   __shared__ float s_v[kWaves];
-  __shared__ int s_i[kWaves], s_n[kWaves], s_sel;
+  __shared__ int s_i[kWaves], s_n[kWaves], s_sel[2];
+  __shared__ float s_f[2];
   const int64_t gid = blockIdx.x;
   const int64_t sy = gid / a.split2;
   const int sp = static_cast<int>(gid % a.split2);
@@ -346,27 +453,38 @@ __global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
   const int ns = state_count(a.num_states, b, a.S);
   if (ns > 0 && y < ns) {
     const FlatSplit f = make_split(*a.count, a.V, Elem<DT>::kBytes, a.grid);
-    const int s = select_position(a, f, b, y, s_v, s_i, s_n, &s_sel);
-    if (sp == 0 && threadIdx.x == 0) a.sel[sy] = s;
+    const Selection sel = select_position(a, f, b, y, a.pos_margin != nullptr && sp == 0, s_v, s_i, s_n, s_sel, s_f);
+    if (sp == 0 && threadIdx.x == 0) {
+      a.sel[sy] = sel.pos;
+      a.selstat[sy] = sel.status;
+      a.selconf[sy] = sel.conf;
+      a.selgap[sy] = sel.gap;
+    }
+    const int s = sel.pos;
     if (s >= 0) {
       const char* xr = static_cast<const char*>(a.logits) +
                        (b * a.ss + y * a.sy + s * a.sp) * Elem<DT>::kBytes;
       const int64_t v0 = static_cast<int64_t>(sp) * a.chunk2;
       const int64_t v1 = v0 + a.chunk2 < a.V ? v0 + a.chunk2 : a.V;
-      ArgmaxPick pk;
-      int64_t idx;
+      typename std::conditional<TWO, ArgmaxPick2, ArgmaxPick>::type pk;
       if (a.inv_t > 0.f) {
         const float* gr = a.gumbel + b * a.gs + s * a.gp;
         gumbel_argmax<DT>(xr, gr, v0, v1, a.inv_t, pk);
       } else {
         stream_row<DT, 4>(xr, v0, v1, pk);
       }
-      idx = pk.bidx;
       float v = pk.best;
-      int ii = static_cast<int>(idx);
+      int ii = static_cast<int>(pk.bidx);
       int nan = pk.nan ? 1 : 0;
+      const float tb = v;
+      const int ti = ii;
       block_argmax(v, ii, nan, s_v, s_i, s_n);
       if (threadIdx.x == 0) a.pick[gid] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
+      if constexpr (TWO) {
+        __syncthreads();
+        const float v2 = block_second(tb, ti, pk.second, v, ii, s_v, s_i, s_n);
+        if (threadIdx.x == 0) a.pick2[gid] = v2;
+      }
     }
   }
 }
@@ -374,8 +492,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
   __shared__ int s_pos[kMaxStates], s_tok[kMaxStates];
-  const FlatSplit f = make_split(*a.count, a.V, Elem<DT>::kBytes, a.grid);
-  tree_walk(a, f, blockIdx.x, s_pos, s_tok);
+  tree_walk(a, blockIdx.x, s_pos, s_tok);
 }
 
 template <typename K>
@@ -385,10 +502,12 @@ static const void* fn(K* k) {
 
 bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
   const bool bf = dtype == DT_BF16;
+  const bool two = a.tok_margin != nullptr;
+  const void* gum = bf ? (two ? fn(k_tree_gumbel<DT_BF16, true>) : fn(k_tree_gumbel<DT_BF16, false>))
+                       : (two ? fn(k_tree_gumbel<DT_F32, true>) : fn(k_tree_gumbel<DT_F32, false>));
   return launch_threads(fn(k_tree_plan), 1, kPlanThreads, stream, a) &&
          launch(bf ? fn(k_tree_conf<DT_BF16>) : fn(k_tree_conf<DT_F32>), a.grid, stream, a, ev) &&
-         launch(bf ? fn(k_tree_gumbel<DT_BF16>) : fn(k_tree_gumbel<DT_F32>),
-                static_cast<int64_t>(a.B) * a.S * a.split2, stream, a) &&
+         launch(gum, static_cast<int64_t>(a.B) * a.S * a.split2, stream, a) &&
          launch(bf ? fn(k_tree_walk<DT_BF16>) : fn(k_tree_walk<DT_F32>), a.B, stream, a);
 }
 

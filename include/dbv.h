@@ -142,9 +142,12 @@ typedef enum {
  *   row_tv [B, K] float32: TV(p_i, q_i) = 1/2 sum_v |p_i(v) - q_i(v)| of
  *       each draft row i < n_b (target and drafter at their temperatures;
  *       [TT] Sec. 2 Eq. 1-2: the lossless acceptance rate of row i is
- *       1 - TV), 0 past n_b.  Diagnostic mode: one more pass over the draft
- *       block's target and drafter rows.  verify_sparse: TV against the
- *       stored Q; verify_spot_chain: TV of the token rows, p against qhat.
+ *       1 - TV), 0 past n_b and for sequences whose draft length is
+ *       invalid, NaN for a row pair that holds NaN / +inf or no finite
+ *       logit.  Diagnostic mode: one more kernel, one group per draft row,
+ *       reading the draft block's target and drafter rows once more.
+ *       verify_sparse: TV against the stored Q, from the stored entries
+ *       alone; verify_spot_chain: TV of the token rows, p against qhat.
  *   verify_gumbel_tree:
  *   pos_margin [B, S] float32: relative gap (c1 - c2) / c1 of the two largest
  *       confidences over the masked positions of each state (1 with one
@@ -153,7 +156,8 @@ typedef enum {
  *   tok_margin [B, S] float32: the gap between the two largest scores
  *       z_v / T + G[s*, v] (T > 0) or logits (T = 0) at s*: the margin of the
  *       coupled transition's token (0 for terminal and unused states).
- *       Tracking the runner-up score costs one more compare per element.
+ *       Tracking the runner-up score costs one more compare per element of
+ *       the selected rows.
  */
 typedef struct dbv_options {
   uint32_t size;

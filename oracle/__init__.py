@@ -52,7 +52,7 @@ from .rows import (  # noqa: F401
     STATUS_BAD_INPUT, STATUS_NONFINITE, STATUS_EMPTY_ROW, STATUS_Q_ZERO,
     STATUS_Z_ZERO, STATUS_ERROR_MASK, NEAR_MARGIN,
     row_status, tempered_softmax, argmax_lowest, acceptance_test,
-    inverse_cdf, residual_weights, stopping_index,
+    inverse_cdf, residual_weights, stopping_index, total_variation,
 )
 from .chain import verify_greedy, verify_rejection, verify_lenient, verify_cactus  # noqa: F401
 from .cactus import (  # noqa: F401

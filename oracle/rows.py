@@ -119,6 +119,14 @@ def inverse_cdf(w, u):
     return c, margin, Z
 
 
+def total_variation(p, q):
+    """TV(p, q) = 1/2 sum_v |p(v) - q(v)| of two distributions on one
+    vocabulary.  Two Tradeoffs, Sec. 2 (Eq. 1-2): the lossless verifier
+    accepts a draft from q with probability 1 - TV(p, q), its diagnostic
+    quantity per row."""
+    return 0.5 * float(np.sum(np.abs(np.asarray(p, np.float64) - np.asarray(q, np.float64))))
+
+
 def residual_weights(p, q, lam=0.0):
     """Unnormalised correction law [p~ - q]_+ at a rejected position.
 

@@ -364,6 +364,7 @@ def test_options_are_validated(lib):
     # Diagnostic outputs an entry point does not produce.
     assert _greedy(lib, opts=_opts(accept_margin=FAKE)) == INVALID
     assert _tree(lib, opts=_opts(draw_margin=FAKE)) == INVALID
+    assert _tree(lib, opts=_opts(row_tv=FAKE)) == INVALID
     assert _any_order(lib, opts=_opts(row_tv=FAKE)) == INVALID
     assert _trunc(lib, opts=_opts(pos_margin=FAKE)) == INVALID
     assert _ddhyp(lib, opts=_opts(tok_margin=FAKE)) == INVALID
@@ -383,7 +384,9 @@ def test_options_accepted_without_gpu(lib):
     assert _reject(lib, lenient=True, opts=_opts(accept_margin=FAKE)) == nodev
     assert _spot(lib, opts=_opts(draw_margin=FAKE)) == nodev
     assert _sparse(lib, opts=_opts(accept_margin=FAKE)) == nodev
-    assert _tree(lib, opts=_opts(**ev)) == nodev
+    assert _tree(lib, opts=_opts(pos_margin=FAKE, tok_margin=FAKE, **ev)) == nodev
+    assert _reject(lib, cactus=True, opts=_opts(row_tv=FAKE)) == nodev
+    assert _sparse(lib, opts=_opts(row_tv=FAKE)) == nodev
     assert _ddtree(lib, opts=_opts(**ev)) == nodev
 
 

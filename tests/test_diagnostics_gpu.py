@@ -1,6 +1,10 @@
 """The per-call options of the C ABI on the GPU: per-decision margins
-against the oracle's margins, the timing events, and launch geometry
-(max_groups) that leaves every integer output unchanged."""
+against the oracle's margins, the timing events, launch geometry
+(max_groups) that leaves every integer output unchanged, the per-row total
+variation TV(p_i, q_i) (dense, stored sparse Q and the joint-space chain,
+including rows where one token holds nearly all of both rows' mass) against
+the oracle's float64 TV, and the tree verifier's position and token margins
+against the oracle's."""
 
 import sys
 
@@ -183,3 +187,104 @@ def test_timing_events_are_per_call(dev):
         call()
     torch.cuda.synchronize()
     assert b.elapsed_time(e) == t1
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("sigma,Tt,Td", [(0.7, 1.0, 1.0), (0.01, 1.0, 1.0), (1.5, 0.8, 1.3)])
+def test_row_tv(dev, dtype, sigma, Tt, Td):
+    """row_tv = TV(p_i, q_i) of every draft row against the oracle's float64
+    TV (rows in the cancelling regime included), 0 past n_b; the outputs of
+    the call are unchanged by the diagnostic."""
+    say("row tv", dtype, sigma, Tt, Td)
+    x = _chain(31 + int(sigma * 10), 10, 7, 4099, dtype, sigma)
+    xd = {k: v.to(dev) for k, v in x.items()}
+    args = (xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"], 0.5)
+    kw = dict(draft_len=xd["draft_len"], temperature_target=Tt, temperature_draft=Td)
+    r = dbv.verify_lenient(*args, row_tv=True, **kw)
+    r0 = dbv.verify_lenient(*args, **kw)
+    for k in r0:
+        assert torch.equal(r[k], r0[k]), k
+    xn = _np(x)
+    tv = np64(r["row_tv"])
+    rtol = PROB_RTOL[str(dtype).split(".")[-1]]
+    B, K = x["draft_tokens"].shape
+    for b in range(B):
+        n = int(x["draft_len"][b])
+        for i in range(K):
+            if i >= n:
+                assert tv[b, i] == 0.0
+                continue
+            p = oracle.tempered_softmax(xn["tgt"][b, i], Tt)
+            q = oracle.tempered_softmax(xn["drf"][b, i], Td)
+            t = oracle.total_variation(p, q)
+            assert abs(tv[b, i] - t) <= rtol * t + 2.0 ** -24, (b, i, tv[b, i], t)
+
+
+def test_row_tv_sparse_and_joint_space(dev):
+    """Stored sparse Q: TV(p, Q) from the stored entries; joint-space chain:
+    TV of the token rows p and qhat."""
+    say("row tv sparse / joint space")
+    x = workloads.sparse_inputs(91, 6, 5, 3001, torch.float32)
+    xd = {k: v.to(dev) if torch.is_tensor(v) else v for k, v in x.items()}
+    r = dbv.verify_sparse(xd["tgt"], xd["q_idx"], xd["q_prob"], xd["q_nnz"], xd["draft_tokens"], xd["u_accept"],
+                          xd["u_resample"], draft_len=xd["draft_len"], row_tv=True)
+    tv = np64(r["row_tv"])
+    qi, qp, qn = npi(x["q_idx"]), np64(x["q_prob"]), npi(x["q_nnz"])
+    for b in range(6):
+        for i in range(5):
+            if i >= int(x["draft_len"][b]):
+                assert tv[b, i] == 0.0
+                continue
+            p = oracle.tempered_softmax(np64(x["tgt"][b, i]), 1.0)
+            t = oracle.total_variation(p, oracle.dense_q(qi[b, i], qp[b, i], qn[b, i], 3001))
+            assert abs(tv[b, i] - t) <= 1e-5 * t + 2.0 ** -24, (b, i, tv[b, i], t)
+    s = workloads.spot_chain_inputs(92, 5, 4, 2003, torch.float32, random_lengths=True)
+    sd = {k: v.to(dev) if torch.is_tensor(v) else v for k, v in s.items()}
+    g = dbv.verify_spot_chain(sd["tgt"], sd["drf"], sd["pos_star"], sd["prop_pos"], sd["prop_tok"],
+                              sd["q_pos_star"], sd["u_accept"], sd["u_resample"], gumbel=sd["gumbel"], tau=0.6,
+                              draft_len=sd["draft_len"], row_tv=True)
+    tv = np64(g["row_tv"])
+    for b in range(5):
+        for i in range(4):
+            if i >= int(s["draft_len"][b]):
+                assert tv[b, i] == 0.0
+                continue
+            p = oracle.tempered_softmax(np64(s["tgt"][b, i]), 1.0)
+            q = oracle.tempered_softmax(np64(s["drf"][b, i]), 1.0)
+            t = oracle.total_variation(p, q)
+            assert abs(tv[b, i] - t) <= 1e-5 * t + 2.0 ** -24, (b, i, tv[b, i], t)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_tree_margins(dev, T):
+    """pos_margin (relative gap of the two best confidences) and tok_margin
+    (gap of the two best scores at s*) against the oracle's margins; the
+    outputs of the call are unchanged by them."""
+    say("tree margins", T)
+    t = workloads.tree_inputs(71, 4, 24, 12, 30011, torch.float32, sigma_node=0.05, temperature=max(T, 1.0))
+    td = {k: v.to(dev) if torch.is_tensor(v) else v for k, v in t.items()}
+    kw = dict(masked=td["masked"], gumbel=td["gumbel"] if T > 0 else None, temperature=T,
+              num_states=td["num_states"])
+    r = dbv.verify_gumbel_tree(td["logits"], td["parent"], td["edge_pos"], td["edge_tok"], margins=True, **kw)
+    r0 = dbv.verify_gumbel_tree(td["logits"], td["parent"], td["edge_pos"], td["edge_tok"], **kw)
+    for k in r0:
+        assert torch.equal(r[k], r0[k]), k
+    tn = {k: (np64(v) if v.dtype.is_floating_point else npi(v)) if torch.is_tensor(v) else v for k, v in t.items()}
+    o = oracle.verify_gumbel_tree(tn["logits"], t["masked"].numpy(), tn["parent"], tn["edge_pos"], tn["edge_tok"],
+                                  tn["num_states"], tn["gumbel"] if T > 0 else None, T)
+    pm, tm = np64(r["pos_margin"]), np64(r["tok_margin"])
+    B, S = pm.shape
+    for b in range(B):
+        ns = int(t["num_states"][b])
+        for y in range(S):
+            if y >= ns or o["sel_pos"][b, y] < 0:
+                assert pm[b, y] == 0.0 and tm[b, y] == 0.0
+                continue
+            om = o["pos_margin"][b, y]
+            assert (pm[b, y] == 1.0) if not np.isfinite(om) else abs(pm[b, y] - om) <= 1e-5, (b, y, pm[b, y], om)
+            if T > 0:
+                assert abs(tm[b, y] - o["tok_margin"][b, y]) <= 1e-4 * max(1.0, o["tok_margin"][b, y]), (b, y)
+            else:
+                xs = tn["logits"][b, y, int(o["sel_pos"][b, y])]
+                top = np.sort(xs)
+                assert tm[b, y] == pytest.approx(top[-1] - top[-2], abs=1e-6)

@@ -91,6 +91,28 @@ def test_exact_acceptance_rate_is_one_minus_tv(lam):
         assert beta == pytest.approx(1.0 - (1.0 - lam) * _tv(p, q), abs=1e-12)
 
 
+def test_total_variation_is_the_largest_event_gap():
+    # TV(p, q) = max over events A of |p(A) - q(A)|: brute force over every
+    # subset of a 9-token vocabulary, plus the rejection probability of the
+    # lossless test, sum_d q(d) (1 - alpha(d)) (Two Tradeoffs Sec. 2).
+    import itertools
+    rng = np.random.default_rng(12)
+    for trial in range(6):
+        V = 9
+        p = oracle.tempered_softmax(rng.normal(0, 2, V), 1.0)
+        q = oracle.tempered_softmax(rng.normal(0, 2, V), 1.0)
+        if trial == 0:
+            q = p.copy()
+        best = max(abs(sum(p[list(A)]) - sum(q[list(A)]))
+                   for r in range(V + 1) for A in itertools.combinations(range(V), r))
+        tv = oracle.total_variation(p, q)
+        assert abs(tv - best) < 1e-14
+        rej = sum(q[d] * (1.0 - oracle.acceptance_test(0.5, p[d], q[d])[1]) for d in range(V))
+        assert abs(tv - rej) < 1e-14
+    # disjoint supports
+    assert oracle.total_variation([0.5, 0.5, 0, 0], [0, 0, 0.25, 0.75]) == 1.0
+
+
 def test_printed_lossless_acceptance_from_dK():
     # Two Tradeoffs App. F.4: lossless acceptance 1 - d_K.  A pair (p, q) with
     # TV = d_K gives exactly the printed acceptance through the oracle's test.

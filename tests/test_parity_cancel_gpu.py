@@ -30,25 +30,29 @@ def say(*a):
     sys.stdout.flush()
 
 
-def _inputs(seed, B, K, V, dtype, T):
+def _inputs(seed, B, K, V, dtype, T, peak=6.0):
     g = torch.Generator().manual_seed(seed)
     z = torch.randn(B, K + 1, V, generator=g) * 3
-    z[torch.arange(B)[:, None], torch.arange(K + 1)[None, :], torch.randint(0, V, (B, K + 1), generator=g)] += 6
+    z[torch.arange(B)[:, None], torch.arange(K + 1)[None, :], torch.randint(0, V, (B, K + 1), generator=g)] += peak
     tgt = z.to(dtype)
     drf = (tgt[:, :K].float() + SIGMA * torch.randn(B, K, V, generator=g)).to(dtype)
-    q = torch.softmax(drf.float() / T, -1)
+    # float64, so that argmax(q - p) below is not decided by rounding where
+    # one token holds nearly all of both rows' mass
+    q = torch.softmax(drf.double() / T, -1)
     d = torch.multinomial(q.reshape(-1, V), 1, generator=g).reshape(B, K).to(torch.int32)
     n = torch.full((B,), K, dtype=torch.int32)
-    n[: B // 4] = torch.randint(0, K + 1, (B // 4,), generator=g).to(torch.int32)
+    n[B // 2: B // 2 + B // 4] = torch.randint(0, K + 1, (B // 4,), generator=g).to(torch.int32)
     ua = torch.rand(B, K, generator=g)
     # The first half of the sequences draft, at a random position, the token
-    # where q most exceeds p, with an accept uniform just below 1: that draft
-    # is rejected (also under a tiny Cactus budget) and the sequence draws
-    # from the cancelling residual.
+    # with the largest q - p among those where q exceeds p by at least 0.1%,
+    # with an accept uniform just below 1: that draft is rejected (also under
+    # a tiny Cactus budget) and the sequence draws from the cancelling
+    # residual.
     p = torch.softmax(tgt[:, :K].double() / T, -1)
     for b in range(B // 2):
         i = int(torch.randint(0, K, (1,), generator=g))
-        d[b, i] = int(torch.argmax(q[b, i].double() - p[b, i]))
+        ex = q[b, i] - p[b, i]
+        d[b, i] = int(torch.argmax(torch.where(q[b, i] >= 1.001 * p[b, i], ex, torch.full_like(ex, -1.0))))
         ua[b, :i + 1] = 0.0
         ua[b, i] = 1.0 - 1e-6
     ur = torch.rand(B, K + 1, generator=g)
@@ -59,16 +63,18 @@ def _np(x):
     return {k: np64(v) if v.dtype.is_floating_point else npi(v) for k, v in x.items()}
 
 
-CASES = [(torch.float32, 513), (torch.float32, 32000), (torch.bfloat16, 513), (torch.bfloat16, 32000),
-         (torch.float32, 151936)]
+CASES = [(torch.float32, 513, 6.0), (torch.float32, 32000, 6.0), (torch.bfloat16, 513, 6.0),
+         (torch.bfloat16, 32000, 6.0), (torch.float32, 151936, 6.0),
+         # a planted token that carries nearly all of both rows' mass
+         (torch.float32, 4099, 20.0), (torch.bfloat16, 4099, 20.0)]
 
 
-@pytest.mark.parametrize("dtype,V", CASES)
+@pytest.mark.parametrize("dtype,V,peak", CASES)
 @pytest.mark.parametrize("rule", ["rejection", "lenient", "cactus"])
-def test_cancelling_residual(dev, dtype, V, rule):
+def test_cancelling_residual(dev, dtype, V, peak, rule):
     T = 1.0
-    say("cancelling residual", rule, dtype, V)
-    x = _inputs(1000 + V % 997 + (dtype == torch.bfloat16), 24, 6, V, dtype, T)
+    say("cancelling residual", rule, dtype, V, peak)
+    x = _inputs(1000 + V % 997 + (dtype == torch.bfloat16), 24, 6, V, dtype, T, peak)
     xd = {k: v.to(dev) for k, v in x.items()}
     args = (xd["tgt"], xd["drf"], xd["draft_tokens"], xd["u_accept"], xd["u_resample"])
     xn = _np(x)
@@ -85,14 +91,14 @@ def test_cancelling_residual(dev, dtype, V, rule):
     else:
         # a budget small enough that gamma - p(d) stays below the
         # forced drafts' q(d) - p(d), so they are still rejected
-        r = dbv.verify_cactus(*args, 1e-8, draft_len=xd["draft_len"])
-        o = oracle.verify_cactus(*oargs, 1e-8, xn["u_accept"], xn["u_resample"])
-        near = check_sampling(r, xn, o, 0.0, T, T, dn, delta=1e-8)
+        r = dbv.verify_cactus(*args, 1e-12, draft_len=xd["draft_len"])
+        o = oracle.verify_cactus(*oargs, 1e-12, xn["u_accept"], xn["u_resample"])
+        near = check_sampling(r, xn, o, 0.0, T, T, dn, delta=1e-12)
     h = npi(r["accept_len"])
     resid = int((h < npi(x["draft_len"])).sum())
     assert resid >= 8, "the case must exercise the residual draw"
     z = np64(r["residual_mass"])[h < npi(x["draft_len"])]
-    record(f"cancelling q = p + N(0, 0.01^2) {rule} B=24 K=6 V={V} {dn}", near)
+    record(f"cancelling q = p + N(0, 0.01^2) {rule} B=24 K=6 V={V} {dn} peak={peak}", near)
     say("residual draws", resid, "Z range", float(z.min()), float(z.max()), dict(near))
 
 
