@@ -9,6 +9,8 @@ and the correction or bonus draw.  Workloads (sizes of the pages' setups):
 
   c1  tiny rejection verify       B=1  K=4  V=1024   fp32
   c2  batch lossless verify       B=8  K=8  V=32000  bf16
+  c1r, c2r                        c1 replicated 32768 times and c2 128 times
+                                  along B: one call of at least 1 GB
   c3  lenient verify              B=32 K=16 V=128256 bf16, sigma=1, T=1, lambda=0.5
   c4  coupled-Gumbel tree verify  B=16 S=64 L=32 V=151936 bf16   (default: the
                                   largest workload that fits one GPU)
@@ -60,6 +62,8 @@ ROTATE_BYTES = 1 << 30         # replicate inputs up to this many bytes
 
 DESCR = {
     "c1": "tiny rejection verify B=1 K=4 V=1024 fp32",
+    "c1r": "tiny rejection verify replicated R=32768: B=32768 K=4 V=1024 fp32 (1.2 GB per call)",
+    "c2r": "batch lossless verify replicated R=128: B=1024 K=8 V=32000 bf16 (1.1 GB per call)",
     "c2": "batch lossless verify B=8 K=8 V=32000 bf16",
     "c3": "lenient verify B=32 K=16 V=128256 bf16 sigma=1 T=1 lambda=0.5",
     "c4": "coupled-Gumbel tree verify B=16 S=64 L=32 V=151936 bf16",
@@ -72,6 +76,8 @@ DESCR = {
     "c4d": "DDTree construction B=16 L=32 V=151936 bf16 T=1 D=20",
     "c5loop": "Packed-SS greedy loop B=64 W=32 V=131072 bf16 L=256, drafter right at 90% of positions",
 }
+CHAIN = ("c1", "c2", "c3", "c3c", "c1r", "c2r")
+REPLICATE = {"c1r": 32768, "c2r": 128}
 DD_BUDGET = 20
 SPOT_TAU = 0.6
 CACTUS_DELTA = 1.0
@@ -162,14 +168,19 @@ class Case:
         self.name = name
         self.dev = dev
         eb = 2
-        if name in ("c1", "c2", "c3", "c3c"):
-            if name == "c1":
+        if name in CHAIN:
+            if name in ("c1", "c1r"):
                 x = workloads.config1()
                 eb = 4
-            elif name == "c2":
+            elif name in ("c2", "c2r"):
                 x = workloads.config2()
             else:
                 x = workloads.config3(1.0, 1.0)
+            if name in REPLICATE:
+                # the batch replicated R times along B: one call of >= 1 GB
+                R = REPLICATE[name]
+                x = {k: (v.repeat((R,) + (1,) * (v.dim() - 1)) if torch.is_tensor(v) else v)
+                     for k, v in x.items()}
             self.lam = 0.5 if name == "c3" else 0.0
             B, K1, V = x["tgt"].shape
             K = K1 - 1
@@ -349,8 +360,8 @@ class Case:
         from tests.parity import np64, npi
         x = self.cpu_inputs
         name = self.name
-        if name in ("c1", "c2", "c3", "c3c"):
-            B = x["tgt"].shape[0]
+        if name in CHAIN:
+            B = min(x["tgt"].shape[0], 64)
             T = x["temperature"]
             tgt, drf = np64(x["tgt"]), np64(x["drf"])
             d, n = npi(x["draft_tokens"]), npi(x["draft_len"])
@@ -693,7 +704,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": dict(workload=DESCR[args.workload], **case.shape,
-                       logits="f32" if args.workload == "c1" else "bf16",
+                       logits="f32" if args.workload in ("c1", "c1r") else "bf16",
                        positions_per_step=case.positions, rows_per_step=case.rows, rotation_sets=R,
                        wall_s=round(wall, 4)),
         "rows_per_s": case.rows / (ms * 1e-3),

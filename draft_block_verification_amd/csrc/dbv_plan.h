@@ -202,9 +202,8 @@ struct DrawRecord {
                      // integer reference of the row maximum and isp = 1/S
                      // (times the Cactus rescaling of the other tokens; 0
                      // where the residual is known to vanish)
-  float mp, mq;      // the largest logits of target and drafter row h
-  float C;           // residual: log2(q(v) / p~(v)) =
-                     //   ((y_v - mq) kq - (x_v - mp) kp) + C
+  float chi, clo;    // residual: log2(q(v) / p~(v)) = (y_v kq - x_v kp) +
+                     // chi + clo (the row constant in two parts)
   float u;           // resample uniform of row h
   int excl;          // Cactus: the drafted token of row h, whose weight is
   float wexcl;       // wexcl = [gamma - q(d)]_+; -1 for the linear rule

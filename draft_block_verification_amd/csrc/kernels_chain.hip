@@ -375,31 +375,64 @@ __device__ __forceinline__ float one_minus_exp2(float d) {
 // (1 - lambda) factor, which the normalisation removes; for the Cactus rule
 // isp also carries the rescaling (1 - gamma) / (1 - p(d)) of every token but
 // the drafted one, element `excl`, whose weight is wexcl = [gamma - q(d)]_+.
+// The row constant of the log-ratio, C - (mq kq - mp kp) for the rows'
+// largest logits mp, mq, in float64 (the products of float32 values are
+// exact there), split into float32 hi + lo.
+__device__ __forceinline__ void split_row_constant(float C, float mp, float mq, float kp, float kq, float& hi,
+                                                   float& lo) {
+  const double A = kp == kq ? (static_cast<double>(mq) - static_cast<double>(mp)) * static_cast<double>(kp)
+                            : static_cast<double>(mq) * kq - static_cast<double>(mp) * kp;
+  const double c = static_cast<double>(C) - A;
+  hi = static_cast<float>(c);
+  const double r = c - static_cast<double>(hi);
+  lo = r == r ? static_cast<float>(r) : 0.f;   // an infinite C leaves no low part
+}
+
 struct DrawWeight {
-  float kp, ep, isp, kq, C;
-  float mp, mq;  // the rows' largest logits
+  float kp, ep, isp, kq;
+  float chi, clo;  // the row constant of the log-ratio, hi + lo
   int resid;
-  int same_t;    // kp == kq
+  int same_t;      // kp == kq
   int excl;
   float wexcl;
   double isp64;
-  // d = log2(q(v) / p~(v)) from the logits' distances to their rows' maxima
-  // (exact in float32 near the maxima, 0 at a token that is both rows'
-  // maximum, whose d is then C itself).
+  // d = log2(q(v) / p~(v)) = (y kq - x kp) + chi + clo.  The logit term is
+  // formed without rounding where it is small: y - x is exact for bf16
+  // logits and, for float32 ones, carries its rounding error (TwoSum), and
+  // with two temperatures x kp is split into an exact sum.  The row constant
+  // holds the two rows' log-partition difference in float64 precision, so d
+  // keeps float32 relative precision wherever p and q nearly cancel.
+  template <int DT>
   __device__ __forceinline__ float log_ratio(float x, float y) const {
-    const float dx = x - mp, dy = y - mq;
-    return same_t ? __builtin_fmaf(dy - dx, kp, C) : __builtin_fmaf(dy, kq, -(dx * kp)) + C;
+    if (same_t) {
+      const float s = y - x;
+      float d = __builtin_fmaf(s, kp, chi);
+      if constexpr (DT == DT_F32) {
+        const float bp = s - y;
+        const float err = (y - (s - bp)) + (-x - bp);
+        // NaN only where s is infinite, where d already is too
+        d += fminf(fmaxf(__builtin_fmaf(err, kp, clo), -1e30f), 1e30f);
+      } else {
+        d += clo;
+      }
+      return d;
+    }
+    const float hx = x * kp;
+    const float lx = __builtin_fmaf(x, kp, -hx);
+    return ((__builtin_fmaf(y, kq, -hx) - lx) + chi) + clo;
   }
-  __device__ __forceinline__ float operator()(float x, float y) const {
+  template <int DT>
+  __device__ __forceinline__ float weight(float x, float y) const {
     const float e = fast_exp2(__builtin_fmaf(x, kp, -ep));
     if (!resid) return e;
-    const float d = log_ratio(x, y);
+    const float d = log_ratio<DT>(x, y);
     // d >= 0: q >= p; d NaN only where p = 0 (x = -inf)
     return d < 0.f ? e * isp * one_minus_exp2(d) : 0.f;
   }
   // The weight of element e.
+  template <int DT>
   __device__ __forceinline__ float at(uint32_t e, float x, float y) const {
-    const float v = (*this)(x, y);
+    const float v = weight<DT>(x, y);
     return static_cast<int>(e) == excl ? wexcl : v;
   }
   // [p - Q]_+ against a stored sparse Q: p itself off the list (Q = 0); on
@@ -528,10 +561,10 @@ __device__ __forceinline__ void tile_masses(const char* xr, const char* yr, int6
           E::unpack(rx[k], x);
           E::unpack(ry[k], y);
 #pragma unroll
-          for (int j = 0; j < W; ++j) m += w.at(e + j, x[j], y[j]);
+          for (int j = 0; j < W; ++j) m += w.template at<DT>(e + j, x[j], y[j]);
         } else {
           for (int j = 0; j < W; ++j)
-            if (e + j < Vn) m += w.at(e + j, E::load1(xr, e + j), w.resid ? E::load1(yr, e + j) : 0.f);
+            if (e + j < Vn) m += w.template at<DT>(e + j, E::load1(xr, e + j), w.resid ? E::load1(yr, e + j) : 0.f);
         }
 #pragma unroll
         for (int sh = 32; sh >= 1; sh >>= 1) m += wave_shfl_xor(m, sh);
@@ -833,17 +866,15 @@ __device__ __forceinline__ DrawRecord draw_decide(const SampleArgs& a, int b, bo
   rec.ep = ref_exp(s.Mp[h], a.kp);
   rec.isp64 = 1.0 / stats64_total(s.Mp[h], s.Rp[h], a.kp);
   rec.isp = static_cast<float>(rec.isp64);
-  rec.mp = s.Mp[h];
-  rec.mq = 0.f;
   // log2(q(v) / p(v)) = ((y_v - mq) kq - (x_v - mp) kp) + C with
   // C = log2(Sp' / Sq'), Sp' = 1 + Rp' the target row's sum relative to its
   // maximum's term (Rp' its rest relative to it, likewise for q).  In that
   // form C is exact to the rests' relative precision: where one token holds
   // nearly all of both rows' mass, C is the small difference of the two
-  // rests, which the residual weight at that token needs.
+  // rests, which the residual weight at that token needs.  The weights take
+  // (y_v kq - x_v kp) + (C - (mq kq - mp kp)), the row constant in float64.
   float Cf = 0.f;
   if (resid && !sparse) {
-    rec.mq = s.Mq[h];
     Cf = log2_sum_ratio(stats64_rest_rel(s.Mp[h], s.Rp[h], a.kp), stats64_rest_rel(s.Mq[h], s.Rq[h], a.kq));
   }
   rec.u = a.u_resample[static_cast<int64_t>(b) * (a.K + 1) + h];
@@ -882,15 +913,15 @@ __device__ __forceinline__ DrawRecord draw_decide(const SampleArgs& a, int b, bo
     rec.excl = s.dh;
     rec.wexcl = fmaxf(s.pth - s.qh, 0.f);
   }
-  rec.C = Cf;
+  if (resid && !sparse) split_row_constant(Cf, s.Mp[h], s.Mq[h], a.kp, a.kq, rec.chi, rec.clo);
   return rec;
 }
 
 __device__ __forceinline__ DrawWeight draw_weight(const SampleArgs& a, const DrawRecord& r) {
   DrawWeight w;
   w.kp = a.kp; w.ep = r.ep; w.isp = r.isp;
-  w.kq = a.kq; w.C = r.C;
-  w.mp = r.mp; w.mq = r.mq;
+  w.kq = a.kq;
+  w.chi = r.chi; w.clo = r.clo;
   w.isp64 = r.isp64;
   w.resid = r.resid;
   w.same_t = a.kp == a.kq;
@@ -1083,11 +1114,11 @@ __global__ __launch_bounds__(kBlock) void k_row_tv(SampleArgs a) {
     const float eq = s_row[2], isq = s_row[3];
     const char* yr = static_cast<const char*>(a.drf) + (b * a.ds + static_cast<int64_t>(i) * a.dr) * E::kBytes;
     DrawWeight w{};
-    w.kp = a.kp; w.kq = a.kq; w.C = s_row[4];
-    w.mp = s_row[6]; w.mq = s_row[7];
+    w.kp = a.kp; w.kq = a.kq;
+    split_row_constant(s_row[4], s_row[6], s_row[7], a.kp, a.kq, w.chi, w.clo);
     w.same_t = a.kp == a.kq;
     auto absdiff = [&](float x, float y) {
-      const float d = w.log_ratio(x, y);
+      const float d = w.template log_ratio<DT>(x, y);
       if (!(d == d)) return 0.f;   // both logits -inf: p = q = 0
       return d < 0.f ? fast_exp2(__builtin_fmaf(x, a.kp, -ep)) * isp * one_minus_exp2(d)
                      : fast_exp2(__builtin_fmaf(y, a.kq, -eq)) * isq * one_minus_exp2(-d);
@@ -1282,12 +1313,13 @@ __device__ __forceinline__ void draw_select(const SampleArgs& a, int b, const Dr
       if (w.resid) E::unpack(load16(yr + e0 * E::kBytes), y);
 #pragma unroll
       for (int j = 0; j < E::kVec; ++j)
-        wt[j] = w.at(static_cast<uint32_t>(e0 + j), x[j], w.resid ? y[j] : 0.f);
+        wt[j] = w.template at<DT>(static_cast<uint32_t>(e0 + j), x[j], w.resid ? y[j] : 0.f);
     } else {
 #pragma unroll
       for (int j = 0; j < E::kVec; ++j) {
         const int64_t e = e0 + j;
-        wt[j] = e < a.V ? w.at(static_cast<uint32_t>(e), E::load1(xr, e), w.resid ? E::load1(yr, e) : 0.f) : 0.f;
+        wt[j] = e < a.V ? w.template at<DT>(static_cast<uint32_t>(e), E::load1(xr, e), w.resid ? E::load1(yr, e) : 0.f)
+                        : 0.f;
       }
     }
 #pragma unroll
