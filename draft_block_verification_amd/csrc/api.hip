@@ -558,6 +558,8 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const
 
   dbv::TreeArgs a{};
   a.B = B; a.S = S; a.L = L; a.V = V;
+  a.divL = dbv::FastDiv32(static_cast<uint32_t>(L));
+  a.divS = dbv::FastDiv32(static_cast<uint32_t>(S));
   a.logits = logits; a.ss = seq_stride; a.sy = state_stride; a.sp = pos_stride;
   a.masked = masked; a.parent = parent; a.edge_pos = edge_pos; a.edge_tok = edge_tok;
   a.num_states = num_states; a.next_pos = mode == DBV_TREE_FIXED_POSITION ? next_pos : nullptr;

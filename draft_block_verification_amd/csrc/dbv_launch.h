@@ -119,6 +119,7 @@ struct TreeArgs {
   float* selgap;                             // per state: relative gap of the two best confidences
   int64_t grid;                              // groups of the row-streaming launch
   int split2; int64_t chunk2;
+  FastDiv32 divL, divS;                      // division by L and by S
 };
 
 // Top-k / top-p truncation of rows [B, K, V] (row i of sequence b read

@@ -45,6 +45,23 @@ DBV_HD inline int64_t udiv(int64_t a, int64_t b) {
 }
 
 DBV_HD inline int64_t cdiv(int64_t a, int64_t b) { return udiv(a + b - 1, b); }
+
+// Division of 32-bit unsigned values by a fixed divisor d >= 1 through one
+// multiply-high and a shift (the round-up method): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(m, n) + n) >> l for
+// every n < 2^32 (the sum formed in 64 bits).
+struct FastDiv32 {
+  uint32_t m = 1, l = 0;
+  FastDiv32() = default;
+  explicit FastDiv32(uint32_t d) {
+    while ((uint64_t(1) << l) < d) ++l;
+    m = static_cast<uint32_t>(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+  }
+  DBV_HD uint32_t div(uint32_t n) const {
+    const uint64_t t = (static_cast<uint64_t>(m) * n) >> 32;
+    return static_cast<uint32_t>((t + n) >> l);
+  }
+};
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // ---------------------------------------------------------------------------

@@ -32,12 +32,10 @@ __device__ __forceinline__ int state_count(const int32_t* num_states, int b, int
 // Flat row id (b*S + y)*L + s -> (sequence, state, position); ids are below
 // 2^31 (checked by the host), so 32-bit arithmetic suffices.
 __device__ __forceinline__ void split_flat(const TreeArgs& a, uint32_t flat, int& b, int& y, int& s) {
-  const uint32_t L = static_cast<uint32_t>(a.L);
-  const uint32_t sy = flat / L;
-  s = static_cast<int>(flat - sy * L);
-  const uint32_t S = static_cast<uint32_t>(a.S);
-  const uint32_t bb = sy / S;
-  y = static_cast<int>(sy - bb * S);
+  const uint32_t sy = a.divL.div(flat);
+  s = static_cast<int>(flat - sy * static_cast<uint32_t>(a.L));
+  const uint32_t bb = a.divS.div(sy);
+  y = static_cast<int>(sy - bb * static_cast<uint32_t>(a.S));
   b = static_cast<int>(bb);
 }
 
@@ -53,53 +51,92 @@ __device__ __forceinline__ bool tree_row_needed(const TreeArgs& a, uint32_t flat
 }
 
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanPer = 16;   // row ids per thread per pass
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kPlanPer = 8;    // row ids per thread per pass
+constexpr int kScanPer = kPlanPer * kPlanWaves / 64;   // wave counts per lane of the scan
+static_assert(kPlanPer * kPlanWaves % 64 == 0, "the scan takes whole lanes");
 
+// Row id t0 + k * kPlanThreads + threadIdx.x is element k of a thread, so
+// that every wave reads and writes 64 consecutive ids (coalesced).  List
+// order is id order: the listing position of an id is the count of needed
+// ids before it, from per-wave ballots and one scan of the kPlanPer x
+// kPlanWaves wave counts in id order.
 __global__ __launch_bounds__(kPlanThreads) void k_tree_plan(TreeArgs a) {
-  __shared__ int s_w[kPlanThreads / 64];
+  __shared__ int s_cnt[kPlanPer * kPlanWaves];
   const uint32_t F = static_cast<uint32_t>(a.B) * a.S * a.L;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const uint64_t below = (uint64_t(1) << lane) - 1;
   int base = 0;  // stream rows listed by earlier passes
   for (uint32_t t0 = 0; t0 < F; t0 += kPlanThreads * kPlanPer) {
-    const uint32_t f0 = t0 + threadIdx.x * kPlanPer;
     // Every request of this thread's ids is issued before any is used (ids
-    // past F are clamped to F - 1 and ignored).
-    int ns[kPlanPer], pos[kPlanPer], ys[kPlanPer], ss[kPlanPer];
-    uint8_t mk[kPlanPer];
+    // past F are clamped to F - 1 and ignored): the state count of the
+    // sequence and the mask byte (the given position in the fixed mode).
+    int ns[kPlanPer], aux[kPlanPer];
 #pragma unroll
     for (int k = 0; k < kPlanPer; ++k) {
-      const uint32_t flat = f0 + k < F ? f0 + k : F - 1;
-      int b;
-      split_flat(a, flat, b, ys[k], ss[k]);
+      const uint32_t id = t0 + k * kPlanThreads + threadIdx.x;
+      const uint32_t flat = id < F ? id : F - 1;
+      int b, y, sp;
+      split_flat(a, flat, b, y, sp);
       ns[k] = state_count(a.num_states, b, a.S);
-      const int64_t sy = static_cast<int64_t>(b) * a.S + ys[k];
-      pos[k] = a.fixed ? a.next_pos[sy] : 0;
-      mk[k] = a.fixed ? 0 : a.masked[flat];
+      aux[k] = a.fixed ? a.next_pos[static_cast<int64_t>(b) * a.S + y] : a.masked[flat];
     }
     uint32_t bits = 0;
-    int c = 0;
 #pragma unroll
     for (int k = 0; k < kPlanPer; ++k) {
-      const bool need = f0 + k < F && ns[k] >= 0 && ys[k] < ns[k] && (a.fixed ? pos[k] == ss[k] : mk[k] != 0);
-      if (need) {
-        bits |= 1u << k;
-        ++c;
+      const uint32_t id = t0 + k * kPlanThreads + threadIdx.x;
+      int b, y, sp;
+      split_flat(a, id < F ? id : F - 1, b, y, sp);
+      const bool need = id < F && ns[k] >= 0 && y < ns[k] && (a.fixed ? aux[k] == sp : aux[k] != 0);
+      bits |= static_cast<uint32_t>(need) << k;
+      const uint64_t m = __ballot(need);
+      if (lane == 0) s_cnt[k * kPlanWaves + wv] = __popcll(m);
+    }
+    __syncthreads();
+    // Exclusive scan of the kPlanPer * kPlanWaves counts in id order by
+    // wave 0, kScanPer consecutive counts per lane.
+    if (wv == 0) {
+      int c[kScanPer], sum = 0;
+#pragma unroll
+      for (int j = 0; j < kScanPer; ++j) {
+        c[j] = s_cnt[lane * kScanPer + j];
+        sum += c[j];
+      }
+      int inc = sum;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += o;
+      }
+      int run = inc - sum;
+#pragma unroll
+      for (int j = 0; j < kScanPer; ++j) {
+        s_cnt[lane * kScanPer + j] = run;
+        run += c[j];
       }
     }
-    int total;
-    int off = base + group_exclusive_scan<kPlanThreads / 64>(c, total, s_w);
+    __syncthreads();
+    uint64_t mlast = 0;
 #pragma unroll
     for (int k = 0; k < kPlanPer; ++k) {
-      if (f0 + k < F) {
-        if ((bits >> k) & 1u) {
-          a.list[off] = static_cast<int32_t>(f0 + k);
-          a.map[f0 + k] = off;
-          ++off;
-        } else {
-          a.map[f0 + k] = -1;
-        }
+      const uint32_t id = t0 + k * kPlanThreads + threadIdx.x;
+      const bool need = (bits >> k) & 1u;
+      const uint64_t m = __ballot(need);
+      if (id < F) {
+        const int off = base + s_cnt[k * kPlanWaves + wv] + __popcll(m & below);
+        if (need) a.list[off] = static_cast<int32_t>(id);
+        a.map[id] = need ? off : -1;
       }
+      mlast = m;
     }
-    base += total;
+    // the pass total: the offset of the last wave count plus that count
+    __syncthreads();
+    if (threadIdx.x == kPlanThreads - 1)
+      s_cnt[0] = s_cnt[(kPlanPer - 1) * kPlanWaves + wv] + static_cast<int>(__popcll(mlast));
+    __syncthreads();
+    base += s_cnt[0];
+    __syncthreads();
   }
   if (threadIdx.x == 0) *a.count = base;
 }

@@ -117,7 +117,40 @@ static void check_merged(const std::vector<int>& parts, int64_t V, int64_t eb, i
   }
 }
 
+// FastDiv32 against plain division: every divisor up to 4096 and around
+// powers of two, over small values, values near multiples and the top of
+// the range.
+static void check_fastdiv() {
+  std::vector<uint32_t> ds;
+  for (uint32_t d = 1; d <= 4096; ++d) ds.push_back(d);
+  for (int k = 12; k < 32; ++k)
+    for (int64_t o = -3; o <= 3; ++o) ds.push_back(static_cast<uint32_t>((int64_t(1) << k) + o));
+  ds.push_back(2147483647u);
+  ds.push_back(2147483648u);
+  for (uint32_t d : ds) {
+    const dbv::FastDiv32 f(d);
+    auto chk = [&](uint64_t n) {
+      if (n > 0xffffffffull) return;
+      const uint32_t v = static_cast<uint32_t>(n);
+      if (f.div(v) != v / d) {
+        std::printf("FastDiv32 %u / %u: %u != %u\n", v, d, f.div(v), v / d);
+        std::exit(1);
+      }
+    };
+    for (uint64_t n = 0; n < 3000; ++n) chk(n);
+    for (uint64_t q : {1ull, 2ull, 3ull, 1000ull, 65535ull, 1000003ull})
+      for (int64_t o = -2; o <= 2; ++o) chk(q * d + o);
+    for (uint64_t n = 0xffffffffull - 3000; n <= 0xffffffffull; ++n) chk(n);
+    uint64_t x = 88172645463325252ull ^ d;
+    for (int i = 0; i < 2000; ++i) {
+      x ^= x << 13; x ^= x >> 7; x ^= x << 17;
+      chk(x & 0xffffffffull);
+    }
+  }
+}
+
 int main() {
+  check_fastdiv();
   // Sequences of P-part target rows followed by one-part drafter rows.
   for (int P : {2, 3})
     for (int64_t V : {1, 7, 1000, 2048, 32000, 151936})
