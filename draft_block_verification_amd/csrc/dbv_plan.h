@@ -28,6 +28,7 @@ constexpr int kWavesPlan = 4;             // waves per 256-thread group
 constexpr int64_t kMaxGrid = 1024;
 constexpr int64_t kUnitBytes = 4096;      // granularity of a group's range
 constexpr int kMaxSplit = 64;
+constexpr int kXcds = 8;              // XCDs of an MI355X; workgroups go to them in turn
 constexpr int kMaxDraft = 1024;       // K and W limit of the chain modes
 constexpr int kMaxStates = 1024;      // S limit of the tree mode
 constexpr int kMaxBlockLen = 1024;    // L limit of the tree mode

@@ -9,9 +9,12 @@
 //                  listed row (the position's confidence is 1/S = max_v p);
 //                  the listed rows form one stream split evenly over the
 //                  groups (FlatSplit)
-//   k_tree_gumbel  per (state, vocabulary chunk): s*(y) from the confidences
-//                  (lowest position on ties), then the argmax over v of
-//                  z_v / T + G[s*, v] (z_v at T = 0) -- the token of Phi(y).
+//   k_tree_select  per state: s*(y) from the confidences (lowest position on
+//                  ties), the status of the state's rows and its margins
+//   k_tree_gumbel  per (state, vocabulary chunk): the argmax over v of
+//                  z_v / T + G[s*, v] (z_v at T = 0) -- the token of Phi(y);
+//                  states sharing s* run side by side on one XCD, so each
+//                  Gumbel chunk is mostly read from HBM once
 //   k_tree_walk    per sequence: validates the tree, gathers Phi(y) for every
 //                  state, walks from the root along the child equal to Phi(y)
 //                  and commits Phi of the last accepted state.
@@ -309,25 +312,25 @@ __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64
   const char* xb = xr + a0 * E::kBytes;
   const char* gb = reinterpret_cast<const char*>(gr + a0);
   constexpr int GV = W / 4;  // 16-byte Gumbel loads per logit vector
+  constexpr int U = 4;       // logit vectors in flight per lane
   int64_t i = t;
-  for (; i + kBlock < nvec; i += 2 * kBlock) {
-    u32x4 xr0 = load16(xb + i * 16), xr1 = load16(xb + (i + kBlock) * 16);
-    u32x4 g0[GV], g1[GV];
+  for (; i + (U - 1) * kBlock < nvec; i += U * kBlock) {
+    u32x4 xv[U], g[U][GV];
 #pragma unroll
-    for (int q = 0; q < GV; ++q) {
-      g0[q] = load16(gb + (i * W + q * 4) * 4);
-      g1[q] = load16(gb + ((i + kBlock) * W + q * 4) * 4);
-    }
-    float x0[W], x1[W];
-    E::unpack(xr0, x0);
-    E::unpack(xr1, x1);
+    for (int u = 0; u < U; ++u) {
+      xv[u] = load16(xb + (i + u * kBlock) * 16);
 #pragma unroll
-    for (int j = 0; j < W; ++j) {
-      x0[j] = __builtin_fmaf(x0[j], inv_t, __uint_as_float(g0[j / 4][j % 4]));
-      x1[j] = __builtin_fmaf(x1[j], inv_t, __uint_as_float(g1[j / 4][j % 4]));
+      for (int q = 0; q < GV; ++q) g[u][q] = load16(gb + ((i + u * kBlock) * W + q * 4) * 4);
     }
-    pk.template group<W>(x0, a0 + i * W);
-    pk.template group<W>(x1, a0 + (i + kBlock) * W);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[W];
+      E::unpack(xv[u], x);
+#pragma unroll
+      for (int j = 0; j < W; ++j) x[j] = __builtin_fmaf(x[j], inv_t, __uint_as_float(g[u][j / 4][j % 4]));
+      pk.template group<W>(x, a0 + (i + u * kBlock) * W);
+    }
   }
   for (; i < nvec; i += kBlock) {
     u32x4 xv = load16(xb + i * 16);
@@ -343,6 +346,74 @@ __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64
   if (a1 + t < v1) {
     float x[1] = {__builtin_fmaf(E::load1(xr, a1 + t), inv_t, gr[a1 + t])};
     pk.template group<1>(x, a1 + t);
+  }
+}
+
+// Argmax of z/T + g for up to NB logit rows that share one Gumbel row (the
+// states of one batch have the same s*): each Gumbel vector is loaded once
+// and used for every row.  Rows and the Gumbel row must be 16-byte aligned
+// at v0 (the caller checks); n rows are live (uniform across the group).
+template <int DT, int NB, class Pick>
+__device__ void gumbel_argmax_batch(const char* const (&xr)[NB], int n, const float* gr, int64_t v0, int64_t v1,
+                                    float inv_t, Pick (&pk)[NB]) {
+  using E = Elem<DT>;
+  constexpr int W = E::kVec;
+  constexpr int GV = W / 4;
+  constexpr int U = 2;   // vectors in flight per row and lane
+  const int t = threadIdx.x;
+  const int64_t nvec = (v1 - v0) / W;
+  const char* gb = reinterpret_cast<const char*>(gr + v0);
+  int64_t i = t;
+  for (; i + (U - 1) * kBlock < nvec; i += U * kBlock) {
+    u32x4 g[U][GV], xv[NB][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < GV; ++q) g[u][q] = load16(gb + ((i + u * kBlock) * W + q * 4) * 4);
+#pragma unroll
+    for (int r = 0; r < NB; ++r)
+      if (r < n)
+#pragma unroll
+        for (int u = 0; u < U; ++u) xv[r][u] = load16(xr[r] + (v0 + (i + u * kBlock) * W) * E::kBytes);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      if (r < n) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float x[W];
+          E::unpack(xv[r][u], x);
+#pragma unroll
+          for (int j = 0; j < W; ++j) x[j] = __builtin_fmaf(x[j], inv_t, __uint_as_float(g[u][j / 4][j % 4]));
+          pk[r].template group<W>(x, v0 + (i + u * kBlock) * W);
+        }
+      }
+    }
+  }
+  for (; i < nvec; i += kBlock) {
+    u32x4 g[GV];
+#pragma unroll
+    for (int q = 0; q < GV; ++q) g[q] = load16(gb + (i * W + q * 4) * 4);
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      if (r < n) {
+        float x[W];
+        E::unpack(load16(xr[r] + (v0 + i * W) * E::kBytes), x);
+#pragma unroll
+        for (int j = 0; j < W; ++j) x[j] = __builtin_fmaf(x[j], inv_t, __uint_as_float(g[j / 4][j % 4]));
+        pk[r].template group<W>(x, v0 + i * W);
+      }
+    }
+  }
+  for (int64_t e = v0 + nvec * W + t; e < v1; e += kBlock) {
+    const float ge = gr[e];
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      if (r < n) {
+        float x[1] = {__builtin_fmaf(E::load1(xr[r], e), inv_t, ge)};
+        pk[r].template group<1>(x, e);
+      }
+    }
   }
 }
 
@@ -473,55 +544,148 @@ __device__ void tree_walk(const TreeArgs& a, int b, int* s_pos, int* s_tok) {
   }
 }
 
-// Per (state, vocabulary chunk): s*(y) (chunk 0 stores it with the state's
-// row status, the confidence at s* and the gap of the two best), then the
-// chunk's argmax of z/T + G[s*] (z at T = 0).  TWO: also the chunk's
-// second-largest score (tok_margin).
-template <int DT, bool TWO>
-__global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
+// Per state: s*(y) with the status of the state's rows, the confidence at
+// s* and (pos_margin) the gap of the two best confidences.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_tree_select(TreeArgs a) {
   __shared__ float s_v[kWaves];
   __shared__ int s_i[kWaves], s_n[kWaves], s_sel[2];
   __shared__ float s_f[2];
-  const int64_t gid = blockIdx.x;
-  const int64_t sy = gid / a.split2;
-  const int sp = static_cast<int>(gid % a.split2);
+  const int64_t sy = blockIdx.x;
   const int b = static_cast<int>(sy / a.S);
-  const int y = static_cast<int>(sy % a.S);
+  const int y = static_cast<int>(sy - static_cast<int64_t>(b) * a.S);
   const int ns = state_count(a.num_states, b, a.S);
   if (ns > 0 && y < ns) {
     const FlatSplit f = make_split(*a.count, a.V, Elem<DT>::kBytes, a.grid);
-    const Selection sel = select_position(a, f, b, y, a.pos_margin != nullptr && sp == 0, s_v, s_i, s_n, s_sel, s_f);
-    if (sp == 0 && threadIdx.x == 0) {
+    const Selection sel = select_position(a, f, b, y, a.pos_margin != nullptr, s_v, s_i, s_n, s_sel, s_f);
+    if (threadIdx.x == 0) {
       a.sel[sy] = sel.pos;
       a.selstat[sy] = sel.status;
       a.selconf[sy] = sel.conf;
       a.selgap[sy] = sel.gap;
     }
-    const int s = sel.pos;
-    if (s >= 0) {
-      const char* xr = static_cast<const char*>(a.logits) +
-                       (b * a.ss + y * a.sy + s * a.sp) * Elem<DT>::kBytes;
-      const int64_t v0 = static_cast<int64_t>(sp) * a.chunk2;
-      const int64_t v1 = v0 + a.chunk2 < a.V ? v0 + a.chunk2 : a.V;
-      typename std::conditional<TWO, ArgmaxPick2, ArgmaxPick>::type pk;
-      if (a.inv_t > 0.f) {
-        const float* gr = a.gumbel + b * a.gs + s * a.gp;
-        gumbel_argmax<DT>(xr, gr, v0, v1, a.inv_t, pk);
-      } else {
-        stream_row<DT, 4>(xr, v0, v1, pk);
+  }
+}
+
+// States of at most this many per sequence are taken in batches of states
+// sharing s* (below); larger trees state by state in index order.
+constexpr int kGroupStates = 128;
+constexpr int kBatch = 4;   // states per batch
+
+// Per (batch of states, vocabulary chunk): each state's argmax over the chunk
+// of z/T + G[s*] (z at T = 0).  TWO: also the chunk's second-largest score
+// (tok_margin).  A sequence's states are ordered by (s*, index) and cut into
+// batches of at most kBatch consecutive states with the same s*, so one load
+// of a Gumbel chunk serves the whole batch.  Work items are (sequence,
+// chunk, batch); each block's item is chosen so that every XCD (workgroups go
+// to the eight in turn) takes a contiguous run of items.
+template <int DT, bool TWO>
+__global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
+  using E = Elem<DT>;
+  using Pick = typename std::conditional<TWO, ArgmaxPick2, ArgmaxPick>::type;
+  __shared__ float s_v[kWaves];
+  __shared__ int s_i[kWaves], s_n[kWaves];
+  __shared__ int s_key[kGroupStates], s_q[kGroupStates], s_rank[kGroupStates], s_flag[kGroupStates];
+  __shared__ int s_y[kBatch], s_cnt;
+  const int64_t items = static_cast<int64_t>(a.B) * a.split2 * a.S;
+  const int64_t per = (items + kXcds - 1) / kXcds;
+  const int64_t w = static_cast<int64_t>(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (w >= items) return;
+  const int64_t bc = w / a.S;
+  const int j = static_cast<int>(w - bc * a.S);
+  const int b = static_cast<int>(bc / a.split2);
+  const int sp = static_cast<int>(bc - static_cast<int64_t>(b) * a.split2);
+  const int ns = state_count(a.num_states, b, a.S);
+  if (ns <= 0 || j >= ns) return;
+  const int64_t base = static_cast<int64_t>(b) * a.S;
+  int n, s;
+  if (a.S <= kGroupStates) {
+    // The rank r of each state by (s*, index), states without a selection
+    // last; its place q within its s* group; a batch starts where
+    // q % kBatch == 0; a state's batch id is the number of batch starts up to
+    // its rank, minus one, and its slot in the batch q % kBatch.
+    for (int t = threadIdx.x; t < a.S; t += kBlock) {
+      const int p = t < ns ? a.sel[base + t] : -1;
+      s_key[t] = p >= 0 ? p : a.L;
+    }
+    if (threadIdx.x == 0) s_cnt = 0;
+    __syncthreads();
+    for (int t = threadIdx.x; t < a.S; t += kBlock) {
+      const int kt = s_key[t];
+      int r = 0, less = 0;
+      for (int u = 0; u < a.S; ++u) {
+        const int ku = s_key[u];
+        less += ku < kt ? 1 : 0;
+        r += (ku < kt || (ku == kt && u < t)) ? 1 : 0;
       }
-      float v = pk.best;
-      int ii = static_cast<int>(pk.bidx);
-      int nan = pk.nan ? 1 : 0;
+      s_rank[t] = r;
+      s_q[t] = r - less;
+      s_flag[r] = (r - less) % kBatch == 0 ? 1 : 0;
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < a.S; t += kBlock) {
+      const int r = s_rank[t];
+      int bid = -1;
+      for (int u = 0; u <= r; ++u) bid += s_flag[u];
+      if (bid == j && s_key[t] < a.L) {
+        const int slot = s_q[t] % kBatch;
+        s_y[slot] = t;
+        atomicMax(&s_cnt, slot + 1);
+      }
+    }
+    __syncthreads();
+    n = s_cnt;
+    if (n == 0) return;
+    s = s_key[s_y[0]];
+  } else {
+    n = 1;
+    if (threadIdx.x == 0) s_y[0] = j;
+    __syncthreads();
+    s = a.sel[base + j];
+    if (s < 0) return;
+  }
+  const int64_t v0 = static_cast<int64_t>(sp) * a.chunk2;
+  const int64_t v1 = v0 + a.chunk2 < a.V ? v0 + a.chunk2 : a.V;
+  const char* xr[kBatch];
+  uintptr_t al = 0;
+#pragma unroll
+  for (int r = 0; r < kBatch; ++r) {
+    const int y = s_y[r < n ? r : 0];
+    xr[r] = static_cast<const char*>(a.logits) + (b * a.ss + y * a.sy + s * a.sp) * E::kBytes;
+    al |= reinterpret_cast<uintptr_t>(xr[r] + v0 * E::kBytes);
+  }
+  Pick pk[kBatch];
+  if (a.inv_t > 0.f) {
+    const float* gr = a.gumbel + b * a.gs + s * a.gp;
+    if (((al | reinterpret_cast<uintptr_t>(gr + v0)) & 15u) == 0) {
+      gumbel_argmax_batch<DT, kBatch>(xr, n, gr, v0, v1, a.inv_t, pk);
+    } else {
+#pragma unroll
+      for (int r = 0; r < kBatch; ++r)
+        if (r < n) gumbel_argmax<DT>(xr[r], gr, v0, v1, a.inv_t, pk[r]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r)
+      if (r < n) stream_row<DT, 4>(xr[r], v0, v1, pk[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < kBatch; ++r) {
+    if (r < n) {
+      const int64_t gid = (base + s_y[r]) * a.split2 + sp;
+      float v = pk[r].best;
+      int ii = static_cast<int>(pk[r].bidx);
+      int nan = pk[r].nan ? 1 : 0;
       const float tb = v;
       const int ti = ii;
       block_argmax(v, ii, nan, s_v, s_i, s_n);
       if (threadIdx.x == 0) a.pick[gid] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
       if constexpr (TWO) {
         __syncthreads();
-        const float v2 = block_second(tb, ti, pk.second, v, ii, s_v, s_i, s_n);
+        const float v2 = block_second(tb, ti, pk[r].second, v, ii, s_v, s_i, s_n);
         if (threadIdx.x == 0) a.pick2[gid] = v2;
       }
+      __syncthreads();
     }
   }
 }
@@ -542,9 +706,12 @@ bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingE
   const bool two = a.tok_margin != nullptr;
   const void* gum = bf ? (two ? fn(k_tree_gumbel<DT_BF16, true>) : fn(k_tree_gumbel<DT_BF16, false>))
                        : (two ? fn(k_tree_gumbel<DT_F32, true>) : fn(k_tree_gumbel<DT_F32, false>));
+  const int64_t items = static_cast<int64_t>(a.B) * a.S * a.split2;
   return launch_threads(fn(k_tree_plan), 1, kPlanThreads, stream, a) &&
          launch(bf ? fn(k_tree_conf<DT_BF16>) : fn(k_tree_conf<DT_F32>), a.grid, stream, a, ev) &&
-         launch(gum, static_cast<int64_t>(a.B) * a.S * a.split2, stream, a) &&
+         launch(bf ? fn(k_tree_select<DT_BF16>) : fn(k_tree_select<DT_F32>), static_cast<int64_t>(a.B) * a.S, stream,
+                a) &&
+         launch(gum, (items + kXcds - 1) / kXcds * kXcds, stream, a) &&
          launch(bf ? fn(k_tree_walk<DT_BF16>) : fn(k_tree_walk<DT_F32>), a.B, stream, a);
 }
 
