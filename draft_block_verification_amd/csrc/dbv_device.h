@@ -77,7 +77,8 @@ __device__ __forceinline__ u32x4 load16(const char* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Row streaming by NT threads (default: one 256-thread group).  Visits
+// Row streaming by NT threads (default: one 256-thread group; NT = 64: the
+// calling wave alone).  Visits
 // elements [v0, v1) of `row`; every thread sees its own elements in
 // increasing index order.  The op receives groups:
 //   op.template group<N>(x, idx0)  -- N contiguous values starting at idx0
@@ -96,7 +97,7 @@ __device__ __forceinline__ void stream_row(const void* row, int64_t v0, int64_t 
   const int64_t a0 = v0 + head;
   const int64_t nvec = (v1 - a0) / W;
   const int64_t a1 = a0 + nvec * W;
-  const int t = threadIdx.x;
+  const int t = static_cast<int>(threadIdx.x) % NT;
 
   if (t < head) {
     float x[1] = {E::load1(row, v0 + t)};
@@ -532,8 +533,8 @@ __device__ __forceinline__ int group_exclusive_scan(int v, int& total, int* s_w)
 // ---------------------------------------------------------------------------
 // Sequence directory of a chain call's stream, rebuilt in LDS by every group:
 // sequence b contributes count(b) consecutive stream rows.  Sequences are
-// taken in blocks of q (at most kSeqBlocks blocks); pre[j] is the first
-// stream row of block j and pre[nblk] the number of rows R.
+// taken in blocks of q, a power of two (at most kSeqBlocks blocks); pre[j]
+// is the first stream row of block j and pre[nblk] the number of rows R.
 // ---------------------------------------------------------------------------
 struct SeqDir {
   int q;
@@ -543,21 +544,56 @@ struct SeqDir {
 template <class CountFn>
 __device__ __forceinline__ SeqDir build_seq_dir(int B, CountFn count, int* pre, int* s_w) {
   SeqDir d;
-  d.q = static_cast<int>(cdiv(B, kSeqBlocks));
+  // q: a power of two, so that a wave's 64 consecutive sequences cover whole
+  // blocks (q <= 64) or lie in one block (q >= 64)
+  d.q = 1;
+  while (static_cast<int64_t>(d.q) * kSeqBlocks < B) d.q <<= 1;
   d.nblk = static_cast<int>(cdiv(B, d.q));
   constexpr int kPer = kSeqBlocks / kBlock;     // blocks per thread
   int sums[kPer];
   int mine = 0;
+  if (d.q > 1) {
+    // Block sums: each wave reads the counts of 64 consecutive sequences at
+    // a time (four such loads in flight), sums them over segments of
+    // min(q, 64) lanes, and the first lane of each segment adds the sum to
+    // its block.
+    for (int j = threadIdx.x; j < d.nblk; j += kBlock) pre[j] = 0;
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int seg = d.q < 64 ? d.q : 64;
+    constexpr int kChunks = 4;
+    for (int c0 = wv * 64; c0 < B; c0 += kChunks * kBlock) {
+      int c[kChunks];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int j = threadIdx.x * kPer + k;
-    int s = 0;
-    if (j < d.nblk) {
-      const int b1 = (j + 1) * d.q < B ? (j + 1) * d.q : B;
-      for (int b = j * d.q; b < b1; ++b) s += count(b);
+      for (int k = 0; k < kChunks; ++k) {
+        const int b = c0 + k * kBlock + lane;
+        c[k] = b < B ? count(b) : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < kChunks; ++k) {
+        int v = c[k];
+        for (int m = 1; m < seg; m <<= 1) v += __shfl_xor(v, m, 64);
+        const int b = c0 + k * kBlock + lane;
+        if ((lane & (seg - 1)) == 0 && b < B && v != 0) atomicAdd(&pre[b / d.q], v);
+      }
     }
-    sums[k] = s;
-    mine += s;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = threadIdx.x * kPer + k;
+      sums[k] = j < d.nblk ? pre[j] : 0;
+      mine += sums[k];
+    }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = threadIdx.x * kPer + k;
+      const int s = j < d.nblk ? count(j) : 0;
+      sums[k] = s;
+      mine += s;
+    }
   }
   int total;
   int off = group_exclusive_scan<kWaves>(mine, total, s_w);
@@ -604,20 +640,105 @@ __device__ __forceinline__ int find_seq(const SeqDir& d, const int* pre, int r, 
   return b;
 }
 
-// Group 0 writes the first stream row of every sequence, pre_out[b], and
-// pre_out[B] = R, for the kernels that follow.
+// A group's position in the sequence directory: the sequence of the last
+// row looked up, its first stream row and its row count.
+struct SeqCursor {
+  int b = -1;
+  int first = 0;
+  int cnt = 0;
+};
+
+// find_seq continued from the cursor when row r lies at or past the
+// cursor's sequence: a group visits its rows in increasing order, so each
+// sequence it crosses is counted once instead of walking its directory block
+// again for every row.
 template <class CountFn>
-__device__ __forceinline__ void write_seq_starts(const SeqDir& d, const int* pre, int B, CountFn count,
-                                                 int32_t* pre_out) {
-  for (int j = threadIdx.x; j < d.nblk; j += kBlock) {
-    int acc = pre[j];
-    const int b1 = (j + 1) * d.q < B ? (j + 1) * d.q : B;
-    for (int b = j * d.q; b < b1; ++b) {
-      pre_out[b] = acc;
-      acc += count(b);
+__device__ __forceinline__ int find_seq(const SeqDir& d, const int* pre, int r, CountFn count, SeqCursor& c) {
+  if (c.b < 0 || r < c.first) {
+    c.b = find_seq(d, pre, r, count, c.first, c.cnt);
+  } else {
+    while (r >= c.first + c.cnt) {
+      c.first += c.cnt;
+      ++c.b;
+      c.cnt = count(c.b);
     }
   }
-  if (threadIdx.x == 0) pre_out[B] = pre[d.nblk];
+  return c.b;
+}
+
+// find_seq for one wave (every lane with the same r), continuing from the
+// wave's cursor: the counts of the next 64 sequences are read at once and
+// the sequence holding r found by a prefix sum over the lanes, so a lookup
+// costs one round of loads per 64 sequences passed instead of one per
+// sequence.  B bounds the sequences counted.
+template <class CountFn>
+__device__ __forceinline__ int find_seq_wave(const SeqDir& d, const int* pre, int r, int B, CountFn count,
+                                             SeqCursor& c) {
+  if (c.b >= 0 && r >= c.first && r < c.first + c.cnt) return c.b;
+  int b0, acc;
+  if (c.b >= 0 && r >= c.first) {
+    b0 = c.b + 1;
+    acc = c.first + c.cnt;
+  } else {
+    int lo = 0, hi = d.nblk - 1;
+    while (lo < hi) {  // largest block j with pre[j] <= r
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= r) lo = mid;
+      else hi = mid - 1;
+    }
+    b0 = lo * d.q;
+    acc = pre[lo];
+  }
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  for (;;) {
+    const int bl = b0 + lane;
+    const int cl = bl < B ? count(bl) : 0;
+    int ps = cl;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const int o = __shfl_up(ps, m, 64);
+      if (lane >= m) ps += o;
+    }
+    const uint64_t hit = __ballot(acc + ps > r);
+    if (hit) {
+      const int L = __builtin_ctzll(hit);
+      c.b = b0 + L;
+      c.cnt = __shfl(cl, L, 64);
+      c.first = acc + __shfl(ps, L, 64) - c.cnt;
+      return c.b;
+    }
+    acc += __shfl(ps, 63, 64);
+    b0 += 64;
+  }
+}
+
+// The first stream row of every sequence, pre_out[b], and pre_out[B] = R,
+// for the kernels that follow, written by all G groups of the launch: group
+// g takes directory blocks g, g + G, ...; wave 0 of the group reads the
+// counts of 64 of a block's sequences at a time and turns them into starts
+// by a prefix sum over its lanes.
+template <class CountFn>
+__device__ __forceinline__ void write_seq_starts(const SeqDir& d, const int* pre, int B, CountFn count,
+                                                 int32_t* pre_out, int g, int G) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  for (int j = g; j < d.nblk; j += G) {
+    int acc = pre[j];
+    const int b1 = (j + 1) * d.q < B ? (j + 1) * d.q : B;
+    for (int b0 = j * d.q; b0 < b1; b0 += 64) {
+      const int b = b0 + lane;
+      const int c = b < b1 ? count(b) : 0;
+      int ps = c;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const int o = __shfl_up(ps, m, 64);
+        if (lane >= m) ps += o;
+      }
+      if (b < b1) pre_out[b] = acc + ps - c;
+      acc += __shfl(ps, 63, 64);
+    }
+  }
+  if (g == 0 && lane == 0) pre_out[B] = pre[d.nblk];
 }
 
 // ---------------------------------------------------------------------------

@@ -81,13 +81,14 @@ __global__ __launch_bounds__(kBlock) void k_ao_rows(AnyOrderArgs a) {
   __shared__ int s_w[kWaves];
   auto count = [&](int b) { return a.rows[b]; };
   const SeqDir dir = build_seq_dir(a.B, count, s_pre, s_w);
-  if (blockIdx.x == 0) write_seq_starts(dir, s_pre, a.B, count, a.pre);
+  write_seq_starts(dir, s_pre, a.B, count, a.pre, blockIdx.x, gridDim.x);
   const FlatSplit f = make_split(s_pre[dir.nblk], a.V, Elem<DT>::kBytes, a.grid);
   const int64_t g = blockIdx.x;
   if (g >= f.G) return;
+  SeqCursor cur;
   for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1) {
-    int first, cnt;
-    const int b = find_seq(dir, s_pre, static_cast<int>(r), count, first, cnt);
+    const int b = find_seq(dir, s_pre, static_cast<int>(r), count, cur);
+    const int first = cur.first;
     const int j = static_cast<int>(r) - first;
     const int nv = a.nver[b];
     const char* rowp =

@@ -17,6 +17,8 @@
 //   k_draw_select      per sequence (256 or 1024 threads): the tile, then the token,
 //                      where the running mass first exceeds u*Z (vocabulary
 //                      order), and output assembly.
+//   k_draw_fused       per sequence (256 threads), rows of a few tiles: the
+//                      decision, the tile masses and the select in one group
 // The kernel boundaries are the only cross-group synchronisation.
 #include "dbv_device.h"
 #include "dbv_launch.h"
@@ -52,13 +54,14 @@ __global__ __launch_bounds__(kBlock) void k_greedy_rows(GreedyArgs a) {
   __shared__ int s_w[kWaves];
   auto count = [&](int b) { return greedy_targets(a, b) + a.W; };
   const SeqDir dir = build_seq_dir(a.B, count, s_pre, s_w);
-  if (blockIdx.x == 0) write_seq_starts(dir, s_pre, a.B, count, a.pre);
+  write_seq_starts(dir, s_pre, a.B, count, a.pre, blockIdx.x, gridDim.x);
   const FlatSplit f = make_split(s_pre[dir.nblk], a.V, Elem<DT>::kBytes, a.grid);
   const int64_t g = blockIdx.x;
   if (g >= f.G) return;
+  SeqCursor cur;
   for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1) {
-    int first, cnt;
-    const int b = find_seq(dir, s_pre, static_cast<int>(r), count, first, cnt);
+    const int b = find_seq(dir, s_pre, static_cast<int>(r), count, cur);
+    const int first = cur.first, cnt = cur.cnt;
     const int j = static_cast<int>(r) - first;
     const int nt = cnt - a.W;
     const char* rowp =
@@ -271,16 +274,20 @@ __device__ void stats_and_gumbel(const char* xr, const float* gr, int64_t v0, in
   if (a1 + t < v1) one(a1 + t);
 }
 
+// Rows of at most this many bytes are streamed a piece per wave.
+constexpr int64_t kSmallRowBytes = 16384;
+
 // GUM: target rows are read with their Gumbel rows (joint-space chain with
 // coupled-noise links).
-template <int DT, bool GUM>
+// SMALL: rows of at most kSmallRowBytes, streamed a piece per wave.
+template <int DT, bool GUM, bool SMALL = false>
 __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
   __shared__ int s_pre[kSeqBlocks + 1];
   __shared__ int s_w[kWaves];
   constexpr int P = GUM ? (Elem<DT>::kBytes + 4) / Elem<DT>::kBytes : 1;
   auto count = [&](int b) { return sample_count(a, b, P); };
   const SeqDir dir = build_seq_dir(a.B, count, s_pre, s_w);
-  if (blockIdx.x == 0) write_seq_starts(dir, s_pre, a.B, count, a.pre);
+  write_seq_starts(dir, s_pre, a.B, count, a.pre, blockIdx.x, gridDim.x);
   const FlatSplit f = make_split(s_pre[dir.nblk], a.V, Elem<DT>::kBytes, a.grid);
   const int64_t g = blockIdx.x;
   if (g >= f.G) return;
@@ -313,9 +320,16 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
     accp = ArgmaxPick();
     pend = -1;
   };
+  // Short rows (a few loads per lane) are taken a whole piece per wave, so
+  // that each piece costs one wave reduction instead of four.
+  static_assert(!(GUM && SMALL), "Gumbel rows take the group path");
+  int piece = 0;
+  SeqCursor cur;
   for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1) {
-    int first, cnt;
-    const int b = find_seq(dir, s_pre, static_cast<int>(r), count, first, cnt);
+    if (SMALL && (piece++ % kWaves) != wave_id()) return;
+    const int b = SMALL ? find_seq_wave(dir, s_pre, static_cast<int>(r), a.B, count, cur)
+                        : find_seq(dir, s_pre, static_cast<int>(r), count, cur);
+    const int first = cur.first, cnt = cur.cnt;
     const int j = static_cast<int>(r) - first;
     const int n = a.drows ? (cnt - P) / (P + 1) : cnt / P - 1;
     const bool target = j < P * (n + 1);
@@ -340,6 +354,17 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
     }
     if (GUM && pend >= 0) flush();
     SoftmaxStats64 st(k);
+    if constexpr (SMALL) {
+      // One wave per piece: its statistics, and the identity in the other
+      // waves' slots of the piece.
+      stream_row<DT, kUnroll, SoftmaxStats64, 64>(rowp, v0, v1, st);
+      float M = st.M;
+      double R = static_cast<double>(st.R);
+      wave_stats64(M, R, k);
+      const int lane = lane_id();
+      if (lane < kWaves) put((r + g) * kWaves + lane, lane == wave_id() ? M : -kInf, lane == wave_id() ? R : 0.0);
+      return;
+    }
     stream_row<DT, kUnroll>(rowp, v0, v1, st);
     float M = st.M;
     double R = static_cast<double>(st.R);
@@ -1139,7 +1164,6 @@ __global__ __launch_bounds__(kBlock) void k_row_tv(SampleArgs a) {
   }
 }
 
-constexpr int kDrawWaves = kDrawThreads / 64;
 
 // LDS of the select step for NT threads holding TPT tile masses each (the
 // tile array serves the zero-mass fallback, which recomputes every tile).
@@ -1436,31 +1460,36 @@ __global__ __launch_bounds__(LDS::kThreads) void k_draw_select(SampleArgs a) {
   }
 }
 
-// The whole draw of one sequence in one group of kDrawThreads threads (for
+// The whole draw of one sequence in one group of kSmallSelect threads (for
 // rows of at most kFusedDrawTiles tiles): the decision, every tile mass of
-// row h into LDS, then the draw.
+// row h into LDS, then the draw.  Four waves keep a row of a few tiles as
+// close to its loads as sixteen would, and let four times as many
+// sequences share a CU.
 template <int DT, int FAM>
-__global__ __launch_bounds__(kDrawThreads) void k_draw_fused(SampleArgs a) {
+__global__ __launch_bounds__(kSmallSelect) void k_draw_fused(SampleArgs a) {
   static_assert(FAM != FAM_SPARSE, "stored sparse Q takes the split draw");
+  static_assert(kFusedDrawTiles <= SmallSelectLds::kThreads * SmallSelectLds::kTiles, "fused rows fit the LDS");
+  constexpr int NT = SmallSelectLds::kThreads;
+  constexpr int TPT = SmallSelectLds::kTiles;
   __shared__ DecideLds sd;
-  __shared__ SelectLds s;
+  __shared__ SmallSelectLds s;
   const int b = blockIdx.x;
   const int t = threadIdx.x;
-  const DrawRecord rec = draw_decide<DT, kDrawThreads, FAM>(a, b, true, sd);
+  const DrawRecord rec = draw_decide<DT, NT, FAM>(a, b, true, sd);
   if (rec.status & SEQ_ERROR_MASK) return;
   const int budget = a.budget ? a.budget[b] : INT_MAX;
-  int dt[(kMaxDraft + kDrawThreads - 1) / kDrawThreads];
-  load_draft_tokens<kDrawThreads>(a, b, dt);
+  int dt[(kMaxDraft + NT - 1) / NT];
+  load_draft_tokens<NT>(a, b, dt);
   const char *xr, *yr;
   draw_rows<DT>(a, b, rec.h, rec.resid != 0, xr, yr);
   const bool vec = ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0;
   const int ntiles = a.tiles;
-  if (rec.fixed < 0) tile_masses<DT, kDrawWaves, 4>(xr, yr, a.V, 0, ntiles, vec, draw_weight(a, rec), s.tile);
+  if (rec.fixed < 0) tile_masses<DT, NT / 64, 4>(xr, yr, a.V, 0, ntiles, vec, draw_weight(a, rec), s.tile);
   __syncthreads();
-  const int q = static_cast<int>(cdiv(ntiles, kDrawThreads));
-  float m0[kDrawTilesPerThread];
+  const int q = static_cast<int>(cdiv(ntiles, NT));
+  float m0[TPT];
 #pragma unroll
-  for (int k = 0; k < kDrawTilesPerThread; ++k) {
+  for (int k = 0; k < TPT; ++k) {
     const int tile = t * q + k;
     m0[k] = (k < q && tile < ntiles) ? s.tile[tile] : 0.f;
   }
@@ -1483,7 +1512,9 @@ bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const Tim
 
 bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
   const bool bf = dtype == DT_BF16;
+  const bool short_rows = a.V * (bf ? 2 : 4) <= kSmallRowBytes;
   const void* rows = a.gumbel ? (bf ? fn(k_sample_rows<DT_BF16, true>) : fn(k_sample_rows<DT_F32, true>))
+                     : short_rows ? (bf ? fn(k_sample_rows<DT_BF16, false, true>) : fn(k_sample_rows<DT_F32, false, true>))
                               : (bf ? fn(k_sample_rows<DT_BF16, false>) : fn(k_sample_rows<DT_F32, false>));
   if (!launch(rows, a.grid, stream, a, ev)) return false;
   const int fam = a.rule == RULE_SPOT ? FAM_SPOT : (a.rule == RULE_SPARSE ? FAM_SPARSE : FAM_TOKEN);
@@ -1508,7 +1539,7 @@ bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const Tim
                                        {fn(k_row_tv<DT_F32, FAM_SPARSE>), fn(k_row_tv<DT_BF16, FAM_SPARSE>)}};
   if (a.row_tv && !launch(tv[fam][bf], static_cast<int64_t>(a.B) * a.K, stream, a)) return false;
   if (a.tiles <= kFusedDrawTiles && fam != FAM_SPARSE)
-    return launch_threads(fused[fam][bf], a.B, kDrawThreads, stream, a);
+    return launch_threads(fused[fam][bf], a.B, kSmallSelect, stream, a);
   const bool small = a.tiles <= kSmallSelect * kSmallSelectTiles;
   return launch(mass[fam][bf], static_cast<int64_t>(a.B) * a.chunks, stream, a) &&
          launch_threads(select[small][fam][bf], a.B, small ? kSmallSelect : kDrawThreads, stream, a);
