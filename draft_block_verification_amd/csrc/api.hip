@@ -581,6 +581,8 @@ dbv_status verify_gumbel_tree(int B, int S, int L, int V, dbv_dtype dtype, const
   a.selconf = reinterpret_cast<float*>(w + plan.off_selconf);
   a.selstat = reinterpret_cast<int32_t*>(w + plan.off_selstat);
   a.selgap = reinterpret_cast<float*>(w + plan.off_selgap);
+  a.batch = reinterpret_cast<int4*>(w + plan.off_batch);
+  a.nbat = reinterpret_cast<int32_t*>(w + plan.off_nbat);
   a.pos_margin = co.pos_margin;
   a.tok_margin = co.tok_margin;
   a.grid = dbv::stream_grid(plan.max_rows, V, static_cast<int64_t>(elem_bytes(dtype)), group_cap(co));

@@ -117,6 +117,8 @@ struct TreeArgs {
   float* selconf;                            // per state: confidence at s*
   int32_t* selstat;                          // per state: status of its rows
   float* selgap;                             // per state: relative gap of the two best confidences
+  int4* batch;                               // per (sequence, batch slot): {s*, n}, then the n states
+  int32_t* nbat;                             // per sequence: batches of the Gumbel argmax
   int64_t grid;                              // groups of the row-streaming launch
   int split2; int64_t chunk2;
   FastDiv32 divL, divS;                      // division by L and by S

@@ -301,7 +301,13 @@ inline SamplePlan plan_sample(int B, int K, int V, int64_t elem_bytes) {
 
 // ------------------------------------------------------------------ tree ---
 // Stream order: the needed (state, position) rows in (b, y, s) order, listed
-// by the planning kernel.
+// by the planning kernel: one group of kTreePlanThreads threads, kTreePlanPer
+// row ids per thread and pass.  Its list has room for one slot per planning
+// thread past B*S*L, its map for the ids of a partial last pass, so that
+// every store of a pass is made without a branch.
+constexpr int kTreePlanThreads = 1024;
+constexpr int kTreePlanPer = 16;
+constexpr int64_t kTreePlanPass = static_cast<int64_t>(kTreePlanThreads) * kTreePlanPer;
 struct TreePlan {
   int64_t max_rows;    // B*S*L
   int64_t states;      // B*S
@@ -317,6 +323,8 @@ struct TreePlan {
   size_t off_selconf;  // float per state: confidence at the selected position
   size_t off_selstat;  // int per state: status bits of the state's rows
   size_t off_selgap;   // float per state: relative gap of the two best confidences
+  size_t off_batch;    // two int4 per (sequence, batch slot): {s*, n, 0, 0}, the batch's states
+  size_t off_nbat;     // int per sequence: batches of the Gumbel argmax
   size_t bytes;
 };
 
@@ -343,15 +351,17 @@ inline TreePlan plan_tree(int B, int S, int L, int V) {
   p.split2 = static_cast<int>(cdiv(V, p.chunk2));
   p.off_count = 0;
   p.off_list = 256;
-  p.off_map = p.off_list + align256(static_cast<size_t>(p.max_rows) * 4);
-  p.off_conf = p.off_map + align256(static_cast<size_t>(p.max_rows) * 4);
+  p.off_map = p.off_list + align256(static_cast<size_t>(p.max_rows + kTreePlanThreads) * 4);
+  p.off_conf = p.off_map + align256(static_cast<size_t>(p.max_rows + kTreePlanPass) * 4);
   p.off_pick = p.off_conf + partial_bytes(p.max_rows);
   p.off_pick2 = p.off_pick + align256(static_cast<size_t>(p.states) * p.split2 * 8);
   p.off_sel = p.off_pick2 + align256(static_cast<size_t>(p.states) * p.split2 * 4);
   p.off_selconf = p.off_sel + align256(static_cast<size_t>(p.states) * 4);
   p.off_selstat = p.off_selconf + align256(static_cast<size_t>(p.states) * 4);
   p.off_selgap = p.off_selstat + align256(static_cast<size_t>(p.states) * 4);
-  p.bytes = p.off_selgap + align256(static_cast<size_t>(p.states) * 4);
+  p.off_batch = p.off_selgap + align256(static_cast<size_t>(p.states) * 4);
+  p.off_nbat = p.off_batch + align256(static_cast<size_t>(p.states) * 32);
+  p.bytes = p.off_nbat + align256(static_cast<size_t>(B) * 4);
   return p;
 }
 

@@ -11,10 +11,12 @@
 //                  groups (FlatSplit)
 //   k_tree_select  per state: s*(y) from the confidences (lowest position on
 //                  ties), the status of the state's rows and its margins
-//   k_tree_gumbel  per (state, vocabulary chunk): the argmax over v of
-//                  z_v / T + G[s*, v] (z_v at T = 0) -- the token of Phi(y);
-//                  states sharing s* run side by side on one XCD, so each
-//                  Gumbel chunk is mostly read from HBM once
+//   k_tree_batch   per sequence: its states with a selection, ordered by
+//                  (s*, index) and cut into batches of states sharing s*
+//   k_tree_gumbel  per (batch, vocabulary chunk): the argmax over v of
+//                  z_v / T + G[s*, v] (z_v at T = 0) for each state of the
+//                  batch -- the token of Phi(y); one load of a Gumbel chunk
+//                  serves the batch, and batches of one s* run on one XCD
 //   k_tree_walk    per sequence: validates the tree, gathers Phi(y) for every
 //                  state, walks from the root along the child equal to Phi(y)
 //                  and commits Phi of the last accepted state.
@@ -53,9 +55,9 @@ __device__ __forceinline__ bool tree_row_needed(const TreeArgs& a, uint32_t flat
   return a.fixed ? a.next_pos[sy] == s : a.masked[flat] != 0;
 }
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = kTreePlanThreads;
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kPlanPer = 8;    // row ids per thread per pass
+constexpr int kPlanPer = kTreePlanPer;    // row ids per thread per pass
 constexpr int kScanPer = kPlanPer * kPlanWaves / 64;   // wave counts per lane of the scan
 static_assert(kPlanPer * kPlanWaves % 64 == 0, "the scan takes whole lanes");
 
@@ -63,83 +65,111 @@ static_assert(kPlanPer * kPlanWaves % 64 == 0, "the scan takes whole lanes");
 // that every wave reads and writes 64 consecutive ids (coalesced).  List
 // order is id order: the listing position of an id is the count of needed
 // ids before it, from per-wave ballots and one scan of the kPlanPer x
-// kPlanWaves wave counts in id order.
-__global__ __launch_bounds__(kPlanThreads) void k_tree_plan(TreeArgs a) {
-  __shared__ int s_cnt[kPlanPer * kPlanWaves];
-  const uint32_t F = static_cast<uint32_t>(a.B) * a.S * a.L;
+// kPlanWaves wave counts in id order.  The next pass's loads are issued
+// before this pass's stores, and every store is unconditional (ids past F
+// and rows not needed write to the padding past the list and the map), so
+// the compiler can count the stores and a wait for the loads is not a wait
+// for the stores as well (the counter retires them in issue order).
+struct PlanLoads {
+  int ns[kPlanPer], aux[kPlanPer];
+};
+
+// The state count of each id's sequence (NS: from num_states, else S) and
+// its mask byte (FIXED: the given position); ids past F are clamped to F - 1
+// and ignored.  The modes are template arguments so that the loads form one
+// straight run.
+template <bool FIXED, bool NS>
+__device__ __forceinline__ void plan_load(const TreeArgs& a, uint32_t t0, uint32_t F, PlanLoads& l) {
+#pragma unroll
+  for (int k = 0; k < kPlanPer; ++k) {
+    const uint32_t id = t0 + k * kPlanThreads + threadIdx.x;
+    const uint32_t flat = id < F ? id : F - 1;
+    int b, y, sp;
+    split_flat(a, flat, b, y, sp);
+    l.ns[k] = NS ? a.num_states[b] : a.S;
+    l.aux[k] = FIXED ? a.next_pos[static_cast<int64_t>(b) * a.S + y] : a.masked[flat];
+  }
+}
+
+// One pass over ids t0 .. t0 + kPass - 1, whose loads are in l: lists the
+// needed ids after the `base` rows of earlier passes, issues the next pass's
+// loads into l, and returns base plus the rows listed.
+template <bool FIXED, bool NS>
+__device__ __forceinline__ int plan_pass(const TreeArgs& a, uint32_t t0, uint32_t F, int base, PlanLoads& l,
+                                         int* s_cnt, int* s_total) {
+  constexpr uint32_t kPass = kPlanThreads * kPlanPer;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const uint64_t below = (uint64_t(1) << lane) - 1;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int k = 0; k < kPlanPer; ++k) {
+    const uint32_t id = t0 + k * kPlanThreads + threadIdx.x;
+    int b, y, sp;
+    split_flat(a, id < F ? id : F - 1, b, y, sp);
+    // a state count outside [1, S] lists nothing (state_count); & rather
+    // than && keeps the test free of branches
+    const bool need = (id < F) & (l.ns[k] >= 1) & (l.ns[k] <= a.S) & (y < l.ns[k]) &
+                      (FIXED ? l.aux[k] == sp : l.aux[k] != 0);
+    bits |= static_cast<uint32_t>(need) << k;
+    const uint64_t m = __ballot(need);
+    if (lane == 0) s_cnt[k * kPlanWaves + wv] = __popcll(m);
+  }
+  if (t0 + kPass < F) plan_load<FIXED, NS>(a, t0 + kPass, F, l);
+  __syncthreads();
+  // Exclusive scan of the kPlanPer * kPlanWaves counts in id order by wave 0,
+  // kScanPer consecutive counts per lane; the pass total to s_total.
+  if (wv == 0) {
+    int c[kScanPer], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      c[j] = s_cnt[lane * kScanPer + j];
+      sum += c[j];
+    }
+    int inc = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += o;
+    }
+    int run = inc - sum;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      s_cnt[lane * kScanPer + j] = run;
+      run += c[j];
+    }
+    if (lane == 63) *s_total = inc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kPlanPer; ++k) {
+    const uint32_t id = t0 + k * kPlanThreads + threadIdx.x;
+    const bool need = (bits >> k) & 1u;
+    const uint64_t m = __ballot(need);
+    const int off = base + s_cnt[k * kPlanWaves + wv] + __popcll(m & below);
+    a.list[need ? static_cast<int64_t>(off) : static_cast<int64_t>(F) + threadIdx.x] = static_cast<int32_t>(id);
+    a.map[id] = need ? off : -1;   // id < F + kPass: within the padded map
+  }
+  const int n = *s_total;
+  __syncthreads();
+  return base + n;
+}
+
+// The first pass is peeled from the loop, so that the loop is entered only
+// where a pass's stores follow the next pass's loads, and its waits for
+// those loads count the stores.
+template <bool FIXED, bool NS>
+__global__ __launch_bounds__(kPlanThreads) void k_tree_plan(TreeArgs a) {
+  __shared__ int s_cnt[kPlanPer * kPlanWaves];
+  __shared__ int s_total;
+  const uint32_t F = static_cast<uint32_t>(a.B) * a.S * a.L;
+  constexpr uint32_t kPass = kPlanThreads * kPlanPer;
   int base = 0;  // stream rows listed by earlier passes
-  for (uint32_t t0 = 0; t0 < F; t0 += kPlanThreads * kPlanPer) {
-    // Every request of this thread's ids is issued before any is used (ids
-    // past F are clamped to F - 1 and ignored): the state count of the
-    // sequence and the mask byte (the given position in the fixed mode).
-    int ns[kPlanPer], aux[kPlanPer];
-#pragma unroll
-    for (int k = 0; k < kPlanPer; ++k) {
-      const uint32_t id = t0 + k * kPlanThreads + threadIdx.x;
-      const uint32_t flat = id < F ? id : F - 1;
-      int b, y, sp;
-      split_flat(a, flat, b, y, sp);
-      ns[k] = state_count(a.num_states, b, a.S);
-      aux[k] = a.fixed ? a.next_pos[static_cast<int64_t>(b) * a.S + y] : a.masked[flat];
-    }
-    uint32_t bits = 0;
-#pragma unroll
-    for (int k = 0; k < kPlanPer; ++k) {
-      const uint32_t id = t0 + k * kPlanThreads + threadIdx.x;
-      int b, y, sp;
-      split_flat(a, id < F ? id : F - 1, b, y, sp);
-      const bool need = id < F && ns[k] >= 0 && y < ns[k] && (a.fixed ? aux[k] == sp : aux[k] != 0);
-      bits |= static_cast<uint32_t>(need) << k;
-      const uint64_t m = __ballot(need);
-      if (lane == 0) s_cnt[k * kPlanWaves + wv] = __popcll(m);
-    }
-    __syncthreads();
-    // Exclusive scan of the kPlanPer * kPlanWaves counts in id order by
-    // wave 0, kScanPer consecutive counts per lane.
-    if (wv == 0) {
-      int c[kScanPer], sum = 0;
-#pragma unroll
-      for (int j = 0; j < kScanPer; ++j) {
-        c[j] = s_cnt[lane * kScanPer + j];
-        sum += c[j];
-      }
-      int inc = sum;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += o;
-      }
-      int run = inc - sum;
-#pragma unroll
-      for (int j = 0; j < kScanPer; ++j) {
-        s_cnt[lane * kScanPer + j] = run;
-        run += c[j];
-      }
-    }
-    __syncthreads();
-    uint64_t mlast = 0;
-#pragma unroll
-    for (int k = 0; k < kPlanPer; ++k) {
-      const uint32_t id = t0 + k * kPlanThreads + threadIdx.x;
-      const bool need = (bits >> k) & 1u;
-      const uint64_t m = __ballot(need);
-      if (id < F) {
-        const int off = base + s_cnt[k * kPlanWaves + wv] + __popcll(m & below);
-        if (need) a.list[off] = static_cast<int32_t>(id);
-        a.map[id] = need ? off : -1;
-      }
-      mlast = m;
-    }
-    // the pass total: the offset of the last wave count plus that count
-    __syncthreads();
-    if (threadIdx.x == kPlanThreads - 1)
-      s_cnt[0] = s_cnt[(kPlanPer - 1) * kPlanWaves + wv] + static_cast<int>(__popcll(mlast));
-    __syncthreads();
-    base += s_cnt[0];
-    __syncthreads();
+  if (F > 0) {
+    PlanLoads l;
+    plan_load<FIXED, NS>(a, 0, F, l);
+    base = plan_pass<FIXED, NS>(a, 0, F, base, l, s_cnt, &s_total);
+    for (uint32_t t0 = kPass; t0 < F; t0 += kPass) base = plan_pass<FIXED, NS>(a, t0, F, base, l, s_cnt, &s_total);
   }
   if (threadIdx.x == 0) *a.count = base;
 }
@@ -568,89 +598,152 @@ __global__ __launch_bounds__(kBlock) void k_tree_select(TreeArgs a) {
 }
 
 // States of at most this many per sequence are taken in batches of states
-// sharing s* (below); larger trees state by state in index order.
+// sharing s* (below); larger trees one state per batch in index order.
 constexpr int kGroupStates = 128;
-constexpr int kBatch = 4;   // states per batch
+constexpr int kBatch = 4;   // states per batch (at most 4: one int4 holds them)
+static_assert(kBatch >= 1 && kBatch <= 4, "batch size");
 
-// Per (batch of states, vocabulary chunk): each state's argmax over the chunk
-// of z/T + G[s*] (z at T = 0).  TWO: also the chunk's second-largest score
-// (tok_margin).  A sequence's states are ordered by (s*, index) and cut into
-// batches of at most kBatch consecutive states with the same s*, so one load
-// of a Gumbel chunk serves the whole batch.  Work items are (sequence,
-// chunk, batch); each block's item is chosen so that every XCD (workgroups go
-// to the eight in turn) takes a contiguous run of items.
+// Per sequence: the states y < num_states with a selection, ordered by
+// (s*, index) and cut into batches of at most kBatch consecutive states with
+// the same s*.  Batch j of sequence b is batch[2 (b S + j)] = {s*, n, 0, 0}
+// and batch[2 (b S + j) + 1] = its n states (-1 past n); nbat[b] = the
+// number of batches (0 for an invalid state count).  In a tree of more than
+// kGroupStates states batch j is state j alone (n = 0 without a selection).
+__global__ __launch_bounds__(kBlock) void k_tree_batch(TreeArgs a) {
+  static_assert(kGroupStates % 4 == 0 && kGroupStates <= kBlock, "keys are read four at a time, one rank per thread");
+  __shared__ __align__(16) int s_key[kGroupStates];
+  __shared__ int s_rank[kGroupStates], s_q[kGroupStates], s_flag[kGroupStates], s_bid[kGroupStates];
+  __shared__ int s_bs[kGroupStates], s_bn[kGroupStates], s_by[kGroupStates][kBatch];
+  __shared__ int s_wave[kWaves], s_nb;
+  const int b = blockIdx.x;
+  const int ns = state_count(a.num_states, b, a.S);
+  const int64_t base = static_cast<int64_t>(b) * a.S;
+  int4* out = a.batch + 2 * base;
+  if (ns <= 0) {
+    if (threadIdx.x == 0) a.nbat[b] = 0;
+    return;
+  }
+  if (a.S > kGroupStates) {
+    for (int t = threadIdx.x; t < ns; t += kBlock) {
+      const int p = a.sel[base + t];
+      out[2 * t] = make_int4(p, p >= 0 ? 1 : 0, 0, 0);
+      out[2 * t + 1] = make_int4(t, -1, -1, -1);
+    }
+    if (threadIdx.x == 0) a.nbat[b] = ns;
+    return;
+  }
+  const int t = threadIdx.x;
+  // Key of state t: s*, or L (after every position) for a state past ns or
+  // without a selection; such states join no batch.  Slots past S hold
+  // INT_MAX, above every key.
+  if (t < kGroupStates) {
+    const int p = t < ns ? a.sel[base + t] : -1;
+    s_key[t] = t >= a.S ? INT_MAX : p >= 0 ? p : a.L;
+    s_bn[t] = 0;
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) s_by[t][r] = -1;
+  }
+  __syncthreads();
+  // rank r of state t by (key, index) and its place q among the states with
+  // its key; a batch starts at every q divisible by kBatch
+  int kt = INT_MAX, r = 0;
+  if (t < a.S) {
+    kt = s_key[t];
+    int less = 0;
+#pragma unroll
+    for (int u = 0; u < kGroupStates; u += 4) {
+      const int4 k4 = *reinterpret_cast<const int4*>(&s_key[u]);
+      const int ku[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        less += ku[e] < kt ? 1 : 0;
+        r += (ku[e] < kt || (ku[e] == kt && u + e < t)) ? 1 : 0;
+      }
+    }
+    s_rank[t] = r;
+    s_q[t] = r - less;
+    s_flag[r] = ((r - less) % kBatch == 0 && kt < a.L) ? 1 : 0;
+  }
+  __syncthreads();
+  // batch id of rank r: the batch starts at ranks up to r, minus one (an
+  // inclusive count by wave ballots, then the counts of earlier waves)
+  const int lane = t & 63, wv = t >> 6;
+  const int f = t < a.S ? s_flag[t] : 0;
+  const uint64_t m = __ballot(f != 0);
+  if (lane == 0) s_wave[wv] = __popcll(m);
+  __syncthreads();
+  if (t < a.S) {
+    int c = __popcll(m & ((uint64_t(2) << lane) - 1));   // lanes 0..lane
+    for (int w = 0; w < wv; ++w) c += s_wave[w];
+    s_bid[t] = c - 1;
+  }
+  if (t == 0) {
+    int nb = 0;
+    for (int w = 0; w < kWaves; ++w) nb += s_wave[w];
+    s_nb = nb;
+  }
+  __syncthreads();
+  if (t < a.S && kt < a.L) {
+    const int bid = s_bid[r];
+    const int slot = s_q[t] % kBatch;
+    s_by[bid][slot] = t;
+    atomicMax(&s_bn[bid], slot + 1);
+    if (slot == 0) s_bs[bid] = kt;
+  }
+  __syncthreads();
+  const int nb = s_nb;
+  for (int j = t; j < nb; j += kBlock) {
+    out[2 * j] = make_int4(s_bs[j], s_bn[j], 0, 0);
+    int ys[4] = {-1, -1, -1, -1};
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) ys[r] = s_by[j][r];
+    out[2 * j + 1] = make_int4(ys[0], ys[1], ys[2], ys[3]);
+  }
+  if (t == 0) a.nbat[b] = nb;
+}
+
+// Items of the Gumbel argmax, one group each: (batch slot j, sequence,
+// chunk) in that order, j-major, the (sequence, chunk) count padded to a
+// multiple of the XCD count, so that the items of one (sequence, chunk) for
+// consecutive j -- batches that mostly share s*, so read the same Gumbel
+// chunk -- land on one XCD (workgroups go to the XCDs in turn), and the live
+// batches of every sequence are dispatched first.
+__host__ __device__ inline int64_t gumbel_stride(int B, int split2) {
+  return (static_cast<int64_t>(B) * split2 + kXcds - 1) / kXcds * kXcds;
+}
+
+// Item w: each state's argmax over the chunk of z/T + G[s*] (z at T = 0).
+// TWO: also the chunk's second-largest score (tok_margin).  One load of a
+// Gumbel chunk serves every state of the batch.  Every thread of the group
+// calls it with the same w.
 template <int DT, bool TWO>
-__global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
+__device__ __forceinline__ void gumbel_item(const TreeArgs& a, int64_t w, float* s_v, int* s_i, int* s_n) {
   using E = Elem<DT>;
   using Pick = typename std::conditional<TWO, ArgmaxPick2, ArgmaxPick>::type;
-  __shared__ float s_v[kWaves];
-  __shared__ int s_i[kWaves], s_n[kWaves];
-  __shared__ int s_key[kGroupStates], s_q[kGroupStates], s_rank[kGroupStates], s_flag[kGroupStates];
-  __shared__ int s_y[kBatch], s_cnt;
-  const int64_t items = static_cast<int64_t>(a.B) * a.split2 * a.S;
-  const int64_t per = (items + kXcds - 1) / kXcds;
-  const int64_t w = static_cast<int64_t>(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-  if (w >= items) return;
-  const int64_t bc = w / a.S;
-  const int j = static_cast<int>(w - bc * a.S);
-  const int b = static_cast<int>(bc / a.split2);
-  const int sp = static_cast<int>(bc - static_cast<int64_t>(b) * a.split2);
-  const int ns = state_count(a.num_states, b, a.S);
-  if (ns <= 0 || j >= ns) return;
+  const int64_t P = gumbel_stride(a.B, a.split2);
+  const int j = static_cast<int>(w / P);
+  const int64_t rem = w - j * P;
+  if (rem >= static_cast<int64_t>(a.B) * a.split2) return;
+  const int b = static_cast<int>(rem / a.split2);
+  const int sp = static_cast<int>(rem - static_cast<int64_t>(b) * a.split2);
+  if (j >= a.nbat[b]) return;
   const int64_t base = static_cast<int64_t>(b) * a.S;
-  int n, s;
-  if (a.S <= kGroupStates) {
-    // The rank r of each state by (s*, index), states without a selection
-    // last; its place q within its s* group; a batch starts where
-    // q % kBatch == 0; a state's batch id is the number of batch starts up to
-    // its rank, minus one, and its slot in the batch q % kBatch.
-    for (int t = threadIdx.x; t < a.S; t += kBlock) {
-      const int p = t < ns ? a.sel[base + t] : -1;
-      s_key[t] = p >= 0 ? p : a.L;
-    }
-    if (threadIdx.x == 0) s_cnt = 0;
-    __syncthreads();
-    for (int t = threadIdx.x; t < a.S; t += kBlock) {
-      const int kt = s_key[t];
-      int r = 0, less = 0;
-      for (int u = 0; u < a.S; ++u) {
-        const int ku = s_key[u];
-        less += ku < kt ? 1 : 0;
-        r += (ku < kt || (ku == kt && u < t)) ? 1 : 0;
-      }
-      s_rank[t] = r;
-      s_q[t] = r - less;
-      s_flag[r] = (r - less) % kBatch == 0 ? 1 : 0;
-    }
-    __syncthreads();
-    for (int t = threadIdx.x; t < a.S; t += kBlock) {
-      const int r = s_rank[t];
-      int bid = -1;
-      for (int u = 0; u <= r; ++u) bid += s_flag[u];
-      if (bid == j && s_key[t] < a.L) {
-        const int slot = s_q[t] % kBatch;
-        s_y[slot] = t;
-        atomicMax(&s_cnt, slot + 1);
-      }
-    }
-    __syncthreads();
-    n = s_cnt;
-    if (n == 0) return;
-    s = s_key[s_y[0]];
-  } else {
-    n = 1;
-    if (threadIdx.x == 0) s_y[0] = j;
-    __syncthreads();
-    s = a.sel[base + j];
-    if (s < 0) return;
-  }
+  const int4 hd = a.batch[2 * (base + j)];
+  const int4 yv = a.batch[2 * (base + j) + 1];
+  const int n = hd.y < kBatch ? hd.y : kBatch;
+  const int s = hd.x;
+  if (n <= 0 || s < 0 || s >= a.L) return;
+  const int ya[4] = {yv.x, yv.y, yv.z, yv.w};
+  int sy[kBatch];
+#pragma unroll
+  for (int r = 0; r < kBatch; ++r) sy[r] = ya[r];
   const int64_t v0 = static_cast<int64_t>(sp) * a.chunk2;
   const int64_t v1 = v0 + a.chunk2 < a.V ? v0 + a.chunk2 : a.V;
   const char* xr[kBatch];
   uintptr_t al = 0;
 #pragma unroll
   for (int r = 0; r < kBatch; ++r) {
-    const int y = s_y[r < n ? r : 0];
+    const int y = sy[r < n ? r : 0];
     xr[r] = static_cast<const char*>(a.logits) + (b * a.ss + y * a.sy + s * a.sp) * E::kBytes;
     al |= reinterpret_cast<uintptr_t>(xr[r] + v0 * E::kBytes);
   }
@@ -672,7 +765,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
 #pragma unroll
   for (int r = 0; r < kBatch; ++r) {
     if (r < n) {
-      const int64_t gid = (base + s_y[r]) * a.split2 + sp;
+      const int64_t gid = (base + sy[r]) * a.split2 + sp;
       float v = pk[r].best;
       int ii = static_cast<int>(pk[r].bidx);
       int nan = pk[r].nan ? 1 : 0;
@@ -688,6 +781,13 @@ __global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
       __syncthreads();
     }
   }
+}
+
+template <int DT, bool TWO>
+__global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
+  __shared__ float s_v[kWaves];
+  __shared__ int s_i[kWaves], s_n[kWaves];
+  gumbel_item<DT, TWO>(a, blockIdx.x, s_v, s_i, s_n);
 }
 
 template <int DT>
@@ -706,12 +806,16 @@ bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingE
   const bool two = a.tok_margin != nullptr;
   const void* gum = bf ? (two ? fn(k_tree_gumbel<DT_BF16, true>) : fn(k_tree_gumbel<DT_BF16, false>))
                        : (two ? fn(k_tree_gumbel<DT_F32, true>) : fn(k_tree_gumbel<DT_F32, false>));
-  const int64_t items = static_cast<int64_t>(a.B) * a.S * a.split2;
-  return launch_threads(fn(k_tree_plan), 1, kPlanThreads, stream, a) &&
+  const int64_t items = static_cast<int64_t>(a.S) * gumbel_stride(a.B, a.split2);
+  const bool ns = a.num_states != nullptr;
+  const void* plan = a.fixed ? (ns ? fn(k_tree_plan<true, true>) : fn(k_tree_plan<true, false>))
+                             : (ns ? fn(k_tree_plan<false, true>) : fn(k_tree_plan<false, false>));
+  return launch_threads(plan, 1, kPlanThreads, stream, a) &&
          launch(bf ? fn(k_tree_conf<DT_BF16>) : fn(k_tree_conf<DT_F32>), a.grid, stream, a, ev) &&
          launch(bf ? fn(k_tree_select<DT_BF16>) : fn(k_tree_select<DT_F32>), static_cast<int64_t>(a.B) * a.S, stream,
                 a) &&
-         launch(gum, (items + kXcds - 1) / kXcds * kXcds, stream, a) &&
+         launch(fn(k_tree_batch), a.B, stream, a) &&
+         launch(gum, items, stream, a) &&
          launch(bf ? fn(k_tree_walk<DT_BF16>) : fn(k_tree_walk<DT_F32>), a.B, stream, a);
 }
 

@@ -259,11 +259,17 @@ int main() {
           CHECK(t.off_list % 256 == 0 && t.off_map % 256 == 0 && t.off_conf % 256 == 0 &&
                     t.off_pick % 256 == 0 && t.off_sel % 256 == 0, "tree offsets");
           CHECK(t.off_list >= t.off_count + 4, "list overlaps count");
-          CHECK(t.off_map >= t.off_list + rows * 4, "map overlaps list");
-          CHECK(t.off_conf >= t.off_map + rows * 4, "conf overlaps map");
+          CHECK(t.off_map >= t.off_list + (rows + kTreePlanThreads) * 4, "map overlaps list padding");
+          CHECK(t.off_conf >= t.off_map + (rows + kTreePlanPass) * 4, "conf overlaps map padding");
           CHECK(t.off_pick >= t.off_conf + (rows + kMaxGrid) * kWavesPlan * 8, "pick overlaps conf");
           CHECK(t.off_sel >= t.off_pick + static_cast<size_t>(t.states) * t.split2 * 8, "sel overlaps pick");
-          CHECK(t.bytes >= t.off_sel + static_cast<size_t>(t.states) * 4, "tree bytes");
+          CHECK(t.off_selconf >= t.off_sel + static_cast<size_t>(t.states) * 4, "selconf overlaps sel");
+          CHECK(t.off_selstat >= t.off_selconf + static_cast<size_t>(t.states) * 4, "selstat overlaps selconf");
+          CHECK(t.off_selgap >= t.off_selstat + static_cast<size_t>(t.states) * 4, "selgap overlaps selstat");
+          CHECK(t.off_batch % 256 == 0 && t.off_nbat % 256 == 0, "batch offsets");
+          CHECK(t.off_batch >= t.off_selgap + static_cast<size_t>(t.states) * 4, "batch overlaps selgap");
+          CHECK(t.off_nbat >= t.off_batch + static_cast<size_t>(t.states) * 32, "nbat overlaps batch");
+          CHECK(t.bytes >= t.off_nbat + static_cast<size_t>(B) * 4, "tree bytes");
         }
       }
     }
