@@ -155,6 +155,57 @@ __device__ __forceinline__ int plan_pass(const TreeArgs& a, uint32_t t0, uint32_
   return base + n;
 }
 
+// Is flat row id u (< F) needed: a valid state's masked position, or its
+// given position in the fixed mode?  Reads the state count and the mask
+// byte (the given position) of u.
+template <bool FIXED, bool NS>
+__device__ __forceinline__ bool plan_need(const TreeArgs& a, uint32_t u) {
+  int b, y, sp;
+  split_flat(a, u, b, y, sp);
+  const int ns = NS ? a.num_states[b] : a.S;
+  const int aux = FIXED ? a.next_pos[static_cast<int64_t>(b) * a.S + y] : a.masked[u];
+  return (ns >= 1) & (ns <= a.S) & (y < ns) & (FIXED ? aux == sp : aux != 0);
+}
+
+// Trees of at most kPlanWideMax row ids: one group of kPlanThreads threads
+// per kPlanThreads consecutive ids, one id per thread.  Group g counts the
+// needed ids before its range itself (about g ids per thread, spread over
+// the group), so the groups need nothing from each other; the list position
+// of an id is that count plus the needed ids before it in the group (wave
+// ballots and the wave counts).  The last group writes the stream length.
+constexpr uint32_t kPlanWideMax = 1u << 18;
+
+template <bool FIXED, bool NS>
+__global__ __launch_bounds__(kPlanThreads) void k_tree_plan_wide(TreeArgs a) {
+  __shared__ int s_w[kPlanWaves], s_c[kPlanWaves];
+  const uint32_t F = static_cast<uint32_t>(a.B) * a.S * a.L;
+  const uint32_t g0 = blockIdx.x * kPlanThreads;
+  const uint32_t id = g0 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const bool need = id < F && plan_need<FIXED, NS>(a, id);
+  int before = 0;
+#pragma unroll 8
+  for (uint32_t u = threadIdx.x; u < g0; u += kPlanThreads) before += plan_need<FIXED, NS>(a, u) ? 1 : 0;
+  for (int m = 32; m >= 1; m >>= 1) before += __shfl_xor(before, m, 64);
+  const uint64_t bal = __ballot(need);
+  if (lane == 0) {
+    s_c[wv] = before;
+    s_w[wv] = __popcll(bal);
+  }
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanWaves; ++w) {
+    base += s_c[w];
+    if (w < wv) total += s_w[w];
+  }
+  const int off = base + total + __popcll(bal & ((uint64_t(1) << lane) - 1));
+  a.list[need ? static_cast<int64_t>(off) : static_cast<int64_t>(F) + threadIdx.x] = static_cast<int32_t>(id);
+  a.map[id] = need ? off : -1;   // id < F + kPlanThreads: within the padded map
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == kPlanThreads - 1) *a.count = off + (need ? 1 : 0);
+}
+
 // The first pass is peeled from the loop, so that the loop is entered only
 // where a pass's stores follow the next pass's loads, and its waits for
 // those loads count the stores.
@@ -808,9 +859,15 @@ bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingE
                        : (two ? fn(k_tree_gumbel<DT_F32, true>) : fn(k_tree_gumbel<DT_F32, false>));
   const int64_t items = static_cast<int64_t>(a.S) * gumbel_stride(a.B, a.split2);
   const bool ns = a.num_states != nullptr;
-  const void* plan = a.fixed ? (ns ? fn(k_tree_plan<true, true>) : fn(k_tree_plan<true, false>))
-                             : (ns ? fn(k_tree_plan<false, true>) : fn(k_tree_plan<false, false>));
-  return launch_threads(plan, 1, kPlanThreads, stream, a) &&
+  const uint32_t F = static_cast<uint32_t>(a.B) * a.S * a.L;
+  const bool wide = F <= kPlanWideMax;
+  const void* plan =
+      wide ? (a.fixed ? (ns ? fn(k_tree_plan_wide<true, true>) : fn(k_tree_plan_wide<true, false>))
+                      : (ns ? fn(k_tree_plan_wide<false, true>) : fn(k_tree_plan_wide<false, false>)))
+           : (a.fixed ? (ns ? fn(k_tree_plan<true, true>) : fn(k_tree_plan<true, false>))
+                      : (ns ? fn(k_tree_plan<false, true>) : fn(k_tree_plan<false, false>)));
+  const int64_t plan_groups = wide ? (static_cast<int64_t>(F) + kPlanThreads - 1) / kPlanThreads : 1;
+  return launch_threads(plan, plan_groups, kPlanThreads, stream, a) &&
          launch(bf ? fn(k_tree_conf<DT_BF16>) : fn(k_tree_conf<DT_F32>), a.grid, stream, a, ev) &&
          launch(bf ? fn(k_tree_select<DT_BF16>) : fn(k_tree_select<DT_F32>), static_cast<int64_t>(a.B) * a.S, stream,
                 a) &&

@@ -708,6 +708,23 @@ def test_tree_parity(dev, dtype, T):
     say("near", dict(near), "path_len", list(o["path_len"]))
 
 
+@pytest.mark.parametrize("B", [33, 70])
+def test_tree_many_rows(dev, B):
+    """B*S*L = 135168 rows (the multi-group listing, 132 groups) and 286720
+    rows (more than 2^18: the one-group listing, 18 passes)."""
+    say("tree many rows B", B, "S 64 L 64 V 7")
+    x = workloads.tree_inputs(77 + B, B, 64, 64, 7, torch.bfloat16, sigma_node=0.5, temperature=1.0)
+    g = dbv.verify_gumbel_tree(x["logits"].to(dev), x["parent"].to(dev), x["edge_pos"].to(dev),
+                               x["edge_tok"].to(dev), masked=x["masked"].to(dev), gumbel=x["gumbel"].to(dev),
+                               temperature=1.0, num_states=x["num_states"].to(dev))
+    xn = _np_inputs(x)
+    xn["masked"] = x["masked"].numpy()
+    o = oracle.verify_gumbel_tree(xn["logits"], xn["masked"], xn["parent"], xn["edge_pos"], xn["edge_tok"],
+                                  xn["num_states"], xn["gumbel"], 1.0)
+    near = check_tree(g, xn, o, "bfloat16", 1.0)
+    say("near", dict(near))
+
+
 def test_tree_fixed_position(dev):
     say("tree fixed position")
     x = workloads.tree_inputs(61, 2, 10, 5, 4001, torch.bfloat16, sigma_node=0.05)
