@@ -859,13 +859,22 @@ __device__ __forceinline__ void combine_rows_pick(int nrows, const float2* part,
   }
 }
 
-// Serial merge of one row's partials (one thread).
+// Serial merge of one row's n >= 1 partials in order (one thread).  The
+// first eight are requested together (a row's partials are mostly the four
+// wave partials of one or two groups), the rest one by one.
 __device__ __forceinline__ void merge_span_stats(const float2* part, int64_t first, int64_t n, float k,
                                                  float& M, float& S) {
+  constexpr int U = 8;
   M = -kInf;
   S = 0.f;
   const float2* p = part + first;
-  for (int64_t j = 0; j < n; ++j) stats_merge(M, S, p[j].x, p[j].y, k);
+  float2 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) v[u] = p[u < n ? u : n - 1];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (u < n) stats_merge(M, S, v[u].x, v[u].y, k);
+  for (int64_t j = U; j < n; ++j) stats_merge(M, S, p[j].x, p[j].y, k);
 }
 
 // Row status from a reduced maximum: NaN / +inf -> nonfinite, -inf -> empty.

@@ -1,10 +1,13 @@
 // Draft-tree verification by shared-Gumbel state equality (SPOT, Sec. 4.1,
 // Sec. 4.3 and App. A.1).
 //
-//   k_tree_plan    one group: lists the needed rows -- every masked row of
-//                  every valid state, or in the fixed-position mode only the
-//                  given position's row -- in (sequence, state, position)
-//                  order, and maps each (state, position) to its list index
+//   k_tree_plan    lists the needed rows -- every masked row of every valid
+//                  state, or in the fixed-position mode only the given
+//                  position's row -- in (sequence, state, position) order,
+//                  and maps each (state, position) to its list index: one
+//                  group per 1024 row ids, each counting the needed ids
+//                  before its range itself (trees of at most 2^18 row ids),
+//                  else one group in passes
 //   k_tree_conf    persistent: softmax statistics (M, S) partials of every
 //                  listed row (the position's confidence is 1/S = max_v p);
 //                  the listed rows form one stream split evenly over the
@@ -654,27 +657,106 @@ constexpr int kGroupStates = 128;
 constexpr int kBatch = 4;   // states per batch (at most 4: one int4 holds them)
 static_assert(kBatch >= 1 && kBatch <= 4, "batch size");
 
-// Per sequence: the states y < num_states with a selection, ordered by
+// Batching of one sequence's states in LDS.
+struct BatchLds {
+  __align__(16) int key[kGroupStates];
+  int rank[kGroupStates], q[kGroupStates], flag[kGroupStates], bid[kGroupStates];
+  int bs[kGroupStates], bn[kGroupStates], by[kGroupStates][kBatch];
+  int wave[kPlanWaves], nb;
+};
+
+// The states y < num_states of sequence b with a selection, ordered by
 // (s*, index) and cut into batches of at most kBatch consecutive states with
 // the same s*.  Batch j of sequence b is batch[2 (b S + j)] = {s*, n, 0, 0}
 // and batch[2 (b S + j) + 1] = its n states (-1 past n); nbat[b] = the
-// number of batches (0 for an invalid state count).  In a tree of more than
-// kGroupStates states batch j is state j alone (n = 0 without a selection).
+// number of batches.  On entry (before a barrier) s.key[t], t <
+// kGroupStates, holds state t's s*, L (after every position) for a state
+// past ns or without a selection -- such states join no batch -- and
+// INT_MAX past S.  S <= kGroupStates; NT threads, NT >= kGroupStates.
+template <int NT>
+__device__ __forceinline__ void batch_states(const TreeArgs& a, int b, BatchLds& s) {
+  static_assert(kGroupStates % 4 == 0 && kGroupStates <= NT && NT / 64 <= kPlanWaves, "batching layout");
+  const int t = threadIdx.x;
+  int4* out = a.batch + 2 * static_cast<int64_t>(b) * a.S;
+  if (t < kGroupStates) {
+    s.bn[t] = 0;
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) s.by[t][r] = -1;
+  }
+  __syncthreads();
+  // rank r of state t by (key, index) and its place q among the states with
+  // its key; a batch starts at every q divisible by kBatch
+  int kt = INT_MAX, r = 0;
+  if (t < a.S) {
+    kt = s.key[t];
+    int less = 0;
+#pragma unroll
+    for (int u = 0; u < kGroupStates; u += 4) {
+      const int4 k4 = *reinterpret_cast<const int4*>(&s.key[u]);
+      const int ku[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        less += ku[e] < kt ? 1 : 0;
+        r += (ku[e] < kt || (ku[e] == kt && u + e < t)) ? 1 : 0;
+      }
+    }
+    s.rank[t] = r;
+    s.q[t] = r - less;
+    s.flag[r] = ((r - less) % kBatch == 0 && kt < a.L) ? 1 : 0;
+  }
+  __syncthreads();
+  // batch id of rank r: the batch starts at ranks up to r, minus one (an
+  // inclusive count by wave ballots, then the counts of earlier waves)
+  const int lane = t & 63, wv = t >> 6;
+  const int f = t < a.S ? s.flag[t] : 0;
+  const uint64_t m = __ballot(f != 0);
+  if (lane == 0) s.wave[wv] = __popcll(m);
+  __syncthreads();
+  if (t < a.S) {
+    int c = __popcll(m & ((uint64_t(2) << lane) - 1));   // lanes 0..lane
+    for (int w = 0; w < wv; ++w) c += s.wave[w];
+    s.bid[t] = c - 1;
+  }
+  if (t == 0) {
+    int nb = 0;
+    for (int w = 0; w < NT / 64; ++w) nb += s.wave[w];
+    s.nb = nb;
+  }
+  __syncthreads();
+  if (t < a.S && kt < a.L) {
+    const int bid = s.bid[r];
+    const int slot = s.q[t] % kBatch;
+    s.by[bid][slot] = t;
+    atomicMax(&s.bn[bid], slot + 1);
+    if (slot == 0) s.bs[bid] = kt;
+  }
+  __syncthreads();
+  const int nb = s.nb;
+  for (int j = t; j < nb; j += NT) {
+    out[2 * j] = make_int4(s.bs[j], s.bn[j], 0, 0);
+    int ys[4] = {-1, -1, -1, -1};
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) ys[q] = s.by[j][q];
+    out[2 * j + 1] = make_int4(ys[0], ys[1], ys[2], ys[3]);
+  }
+  if (t == 0) a.nbat[b] = nb;
+}
+
+// The batches of sequence b from the selections k_tree_select wrote (see
+// batch_states); nbat[b] = 0 for an invalid state count.  In a tree of more
+// than kGroupStates states batch j is state j alone (n = 0 without a
+// selection).
 __global__ __launch_bounds__(kBlock) void k_tree_batch(TreeArgs a) {
-  static_assert(kGroupStates % 4 == 0 && kGroupStates <= kBlock, "keys are read four at a time, one rank per thread");
-  __shared__ __align__(16) int s_key[kGroupStates];
-  __shared__ int s_rank[kGroupStates], s_q[kGroupStates], s_flag[kGroupStates], s_bid[kGroupStates];
-  __shared__ int s_bs[kGroupStates], s_bn[kGroupStates], s_by[kGroupStates][kBatch];
-  __shared__ int s_wave[kWaves], s_nb;
+  __shared__ BatchLds s;
   const int b = blockIdx.x;
   const int ns = state_count(a.num_states, b, a.S);
   const int64_t base = static_cast<int64_t>(b) * a.S;
-  int4* out = a.batch + 2 * base;
   if (ns <= 0) {
     if (threadIdx.x == 0) a.nbat[b] = 0;
     return;
   }
   if (a.S > kGroupStates) {
+    int4* out = a.batch + 2 * base;
     for (int t = threadIdx.x; t < ns; t += kBlock) {
       const int p = a.sel[base + t];
       out[2 * t] = make_int4(p, p >= 0 ? 1 : 0, 0, 0);
@@ -684,73 +766,11 @@ __global__ __launch_bounds__(kBlock) void k_tree_batch(TreeArgs a) {
     return;
   }
   const int t = threadIdx.x;
-  // Key of state t: s*, or L (after every position) for a state past ns or
-  // without a selection; such states join no batch.  Slots past S hold
-  // INT_MAX, above every key.
   if (t < kGroupStates) {
     const int p = t < ns ? a.sel[base + t] : -1;
-    s_key[t] = t >= a.S ? INT_MAX : p >= 0 ? p : a.L;
-    s_bn[t] = 0;
-#pragma unroll
-    for (int r = 0; r < kBatch; ++r) s_by[t][r] = -1;
+    s.key[t] = t >= a.S ? INT_MAX : p >= 0 ? p : a.L;
   }
-  __syncthreads();
-  // rank r of state t by (key, index) and its place q among the states with
-  // its key; a batch starts at every q divisible by kBatch
-  int kt = INT_MAX, r = 0;
-  if (t < a.S) {
-    kt = s_key[t];
-    int less = 0;
-#pragma unroll
-    for (int u = 0; u < kGroupStates; u += 4) {
-      const int4 k4 = *reinterpret_cast<const int4*>(&s_key[u]);
-      const int ku[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        less += ku[e] < kt ? 1 : 0;
-        r += (ku[e] < kt || (ku[e] == kt && u + e < t)) ? 1 : 0;
-      }
-    }
-    s_rank[t] = r;
-    s_q[t] = r - less;
-    s_flag[r] = ((r - less) % kBatch == 0 && kt < a.L) ? 1 : 0;
-  }
-  __syncthreads();
-  // batch id of rank r: the batch starts at ranks up to r, minus one (an
-  // inclusive count by wave ballots, then the counts of earlier waves)
-  const int lane = t & 63, wv = t >> 6;
-  const int f = t < a.S ? s_flag[t] : 0;
-  const uint64_t m = __ballot(f != 0);
-  if (lane == 0) s_wave[wv] = __popcll(m);
-  __syncthreads();
-  if (t < a.S) {
-    int c = __popcll(m & ((uint64_t(2) << lane) - 1));   // lanes 0..lane
-    for (int w = 0; w < wv; ++w) c += s_wave[w];
-    s_bid[t] = c - 1;
-  }
-  if (t == 0) {
-    int nb = 0;
-    for (int w = 0; w < kWaves; ++w) nb += s_wave[w];
-    s_nb = nb;
-  }
-  __syncthreads();
-  if (t < a.S && kt < a.L) {
-    const int bid = s_bid[r];
-    const int slot = s_q[t] % kBatch;
-    s_by[bid][slot] = t;
-    atomicMax(&s_bn[bid], slot + 1);
-    if (slot == 0) s_bs[bid] = kt;
-  }
-  __syncthreads();
-  const int nb = s_nb;
-  for (int j = t; j < nb; j += kBlock) {
-    out[2 * j] = make_int4(s_bs[j], s_bn[j], 0, 0);
-    int ys[4] = {-1, -1, -1, -1};
-#pragma unroll
-    for (int r = 0; r < kBatch; ++r) ys[r] = s_by[j][r];
-    out[2 * j + 1] = make_int4(ys[0], ys[1], ys[2], ys[3]);
-  }
-  if (t == 0) a.nbat[b] = nb;
+  batch_states<kBlock>(a, b, s);
 }
 
 // Items of the Gumbel argmax, one group each: (batch slot j, sequence,

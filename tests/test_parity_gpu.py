@@ -708,12 +708,14 @@ def test_tree_parity(dev, dtype, T):
     say("near", dict(near), "path_len", list(o["path_len"]))
 
 
-@pytest.mark.parametrize("B", [33, 70])
-def test_tree_many_rows(dev, B):
-    """B*S*L = 135168 rows (the multi-group listing, 132 groups) and 286720
-    rows (more than 2^18: the one-group listing, 18 passes)."""
-    say("tree many rows B", B, "S 64 L 64 V 7")
-    x = workloads.tree_inputs(77 + B, B, 64, 64, 7, torch.bfloat16, sigma_node=0.5, temperature=1.0)
+@pytest.mark.parametrize("B,S,L", [(33, 64, 64), (70, 64, 64), (4, 128, 80), (3, 200, 48)])
+def test_tree_many_rows(dev, B, S, L):
+    """The listing and batching paths by tree size: B*S*L = 135168 row ids
+    (listing by 132 groups) and 286720 (more than 2^18: one group in
+    passes); S = 128 (the most states batched by s*, positions up to 80) and
+    S = 200 (one state per batch)."""
+    say("tree many rows B", B, "S", S, "L", L, "V 7")
+    x = workloads.tree_inputs(77 + B, B, S, L, 7, torch.bfloat16, sigma_node=0.5, temperature=1.0)
     g = dbv.verify_gumbel_tree(x["logits"].to(dev), x["parent"].to(dev), x["edge_pos"].to(dev),
                                x["edge_tok"].to(dev), masked=x["masked"].to(dev), gumbel=x["gumbel"].to(dev),
                                temperature=1.0, num_states=x["num_states"].to(dev))
