@@ -10,18 +10,22 @@
 //        row's NaN / +inf check comes from the thread maxima;
 //     2. tau = the smallest, over the waves, of each wave's ceil(k/16)-th
 //        largest thread maximum: at least k logits are >= tau;
-//     3. the kept entries >= tau are the candidates; each finds its token
-//        id inside its group; a radix select in LDS gives the k-th largest
-//        key and, where more logits equal it than the top-k needs, the
-//        token-id cut-off (ties go to the lower ids);
+//     3. the kept entries >= tau are the candidates, each with its place
+//        (group start, occurrence), which orders equal logits as their
+//        token ids do; with at most kRankCand candidates each counts its rank by
+//        (logit descending, place ascending) against the others, else a
+//        radix select in LDS gives the k-th largest key and the place
+//        cut-off (ties go to the lower ids); the k kept find their token
+//        ids inside their groups;
 //     4. if some thread dropped a logit >= that k-th key, the candidates may
 //        miss a kept token: the row is read again and every logit >= tau
 //        collected (and if those overflow LDS, a radix select over the
 //        whole row, one pass per 8-bit digit, takes their place);
-//     5. the k kept sorted by (logit descending, id ascending) by counting
-//        ranks; weights exp((x - x_max) / T); the shortest prefix whose
-//        mass reaches p of the total (all k for p = 1), renormalised and
-//        written in order.
+//     5. the k kept sorted by (logit descending, id ascending) (already in
+//        rank order on the counting path); weights exp((x - x_max) / T);
+//        the shortest prefix whose mass reaches p of the total (all k for
+//        p = 1), renormalised and written in order (by one wave for k <=
+//        64).
 #include "dbv_device.h"
 #include "dbv_launch.h"
 
@@ -46,6 +50,7 @@ constexpr int key_bits() {
 constexpr int kTB = 1024;          // threads per row
 constexpr int kTW = kTB / 64;      // waves per row
 constexpr int kTruncCand = 4096;   // LDS candidates (>= 3 per thread)
+constexpr int kRankCand = 256;     // candidates ranked by counting (else radix select)
 static_assert(kTruncCand >= 3 * kTB, "every thread's three kept logits fit");
 
 struct TruncLds {
@@ -53,6 +58,7 @@ struct TruncLds {
   int bad, digit, above, n, keep, nc;
   uint32_t tau_key, drop_key;
   uint32_t wtau[kTW];
+  __align__(16) uint2 rk[kRankCand + 2];   // ranked candidates: key, place
   float cx[kTruncCand];            // candidates: logit and token id
   int cid[kTruncCand];
   uint32_t ckey[kMaxNnz];          // the kept k
@@ -365,6 +371,7 @@ __global__ __launch_bounds__(kTB, 8) void k_truncate(TruncArgs a) {
   const int64_t V = a.V;
   const int k = a.top_k < V ? a.top_k : static_cast<int>(V);
   constexpr int KB = key_bits<DT>();
+  static_assert(Elem<DT>::kVec <= 8, "a place packs the occurrence in three bits");
 
   // 1. one pass: each thread's top three, the largest dropped logit
   if (t == 0) {
@@ -402,13 +409,14 @@ __global__ __launch_bounds__(kTB, 8) void k_truncate(TruncArgs a) {
   }
   const uint32_t tkey = s.tau_key;
 
-  // 3. candidates: the kept logits >= tau, with their token ids
+  // 3. candidates: the kept logits >= tau, with their places g * 8 + c
+  //    (group start g, occurrence c < W <= 8 among its equal logits)
   {
     auto cand = [&](float v, int g, int c) {
       if (g >= 0 && order_key<DT>(v) >= tkey) {
         const int slot = atomicAdd(&s.nc, 1);   // at most 3 per thread: always fits
         s.cx[slot] = v;
-        s.cid[slot] = find_in_group<DT>(row, V, g, c, v);
+        s.cid[slot] = g * 8 + c;
       }
     };
     cand(op.v0, op.g0, op.c0);
@@ -430,15 +438,55 @@ __global__ __launch_bounds__(kTB, 8) void k_truncate(TruncArgs a) {
   };
   uint32_t kth = 0, id_cut = 0;
   bool exact = nc >= k;
-  if (exact) {
-    radix_select<KB>(s, k, lds_hist, kth, id_cut);
+  // kept entries in s.ckey / s.cidx / s.kx hold places, not token ids, on
+  // the candidate paths; `ranked`: already in rank order
+  bool ranked = false;
+  if (exact && nc <= kRankCand) {
+    // (key, place) pairs, two per 16-byte read; the pad pair (key 0, place
+    // INT_MAX) ranks below every candidate
+    if (t <= nc) s.rk[t] = t < nc ? make_uint2(order_key<DT>(s.cx[t]), static_cast<uint32_t>(s.cid[t]))
+                                  : make_uint2(0u, 0x7FFFFFFFu);
+    __syncthreads();
+    if (t < nc) {
+      const uint32_t kc = s.rk[t].x;
+      const int pc = s.cid[t];
+      int rank = 0;
+#pragma unroll 8
+      for (int d = 0; d < nc; d += 2) {
+        const uint4 q = *reinterpret_cast<const uint4*>(&s.rk[d]);
+        // | and & rather than || and &&: no branch, the loads stay in one run
+        rank += static_cast<int>((q.x > kc) | ((q.x == kc) & (static_cast<int>(q.y) < pc)));
+        rank += static_cast<int>((q.z > kc) | ((q.z == kc) & (static_cast<int>(q.w) < pc)));
+      }
+      if (rank < k) {
+        s.ckey[rank] = kc;
+        s.cidx[rank] = pc;
+        s.kx[rank] = s.cx[t];
+      }
+    }
+    __syncthreads();
+    kth = s.ckey[k - 1];
+    ranked = true;
     // a dropped logit at or above the k-th key may belong to the top k
+    exact = s.drop_key < kth;
+    if (exact && t == 0) s.n = k;
+  } else if (exact) {
+    radix_select<KB>(s, k, lds_hist, kth, id_cut);
     exact = s.drop_key < kth;
   }
   __syncthreads();
   if (exact) {
-    for (int c = t; c < nc; c += kTB) keep_token(s, order_key<DT>(s.cx[c]), s.cx[c], s.cid[c], kth, id_cut);
+    if (!ranked)
+      for (int c = t; c < nc; c += kTB) keep_token(s, order_key<DT>(s.cx[c]), s.cx[c], s.cid[c], kth, id_cut);
+    __syncthreads();
+    // the kept places to token ids
+    const int mk = s.n < kMaxNnz ? s.n : kMaxNnz;
+    if (t < mk) {
+      const int pc = s.cidx[t];
+      s.cidx[t] = find_in_group<DT>(row, V, pc >> 3, pc & 7, s.kx[t]);
+    }
   } else {
+    ranked = false;
     // 4. read the row again: every logit >= tau
     if (t == 0) s.nc = 0;
     __syncthreads();
@@ -465,16 +513,23 @@ __global__ __launch_bounds__(kTB, 8) void k_truncate(TruncArgs a) {
 
   // 5. sort, weights, top-p prefix
   const int m = s.n < kMaxNnz ? s.n : kMaxNnz;   // == k
-  for (int c = t; c < m; c += kTB) {
-    const uint32_t kc = s.ckey[c];
-    const int ic = s.cidx[c];
-    int rank = 0;
-    for (int d = 0; d < m; ++d) {
-      const uint32_t kd = s.ckey[d];
-      rank += (kd > kc || (kd == kc && s.cidx[d] < ic)) ? 1 : 0;
+  if (ranked) {
+    if (t < m) {
+      s.sidx[t] = s.cidx[t];
+      s.sx[t] = s.kx[t];
     }
-    s.sidx[rank] = ic;
-    s.sx[rank] = s.kx[c];
+  } else {
+    for (int c = t; c < m; c += kTB) {
+      const uint32_t kc = s.ckey[c];
+      const int ic = s.cidx[c];
+      int rank = 0;
+      for (int d = 0; d < m; ++d) {
+        const uint32_t kd = s.ckey[d];
+        rank += (kd > kc || (kd == kc && s.cidx[d] < ic)) ? 1 : 0;
+      }
+      s.sidx[rank] = ic;
+      s.sx[rank] = s.kx[c];
+    }
   }
   __syncthreads();
   const float xmax = s.sx[0];
@@ -483,6 +538,27 @@ __global__ __launch_bounds__(kTB, 8) void k_truncate(TruncArgs a) {
   const float wt = (t < m && !bad) ? fast_exp2((s.sx[t] - xmax) * a.kq) : 0.f;
   const int lane = t & 63;
   const int w = t >> 6;
+  if (m <= 64) {
+    // one wave: the same sums as below, where waves past the first add 0
+    if (w == 0) {
+      float inc = wt;
+#pragma unroll
+      for (int q = 1; q < 64; q <<= 1) {
+        const float o = __shfl_up(inc, q, 64);
+        if (lane >= q) inc += o;
+      }
+      const float total = __shfl(inc, 63, 64);
+      const uint64_t hit = __ballot(a.top_p < 1.f && t < m && inc >= a.top_p * total);
+      const int keep = hit ? __ffsll(static_cast<unsigned long long>(hit)) : m;
+      const float sum = __shfl(inc, keep - 1, 64);
+      if (!bad && t < keep) {
+        a.q_idx[out + t] = s.sidx[t];
+        a.q_prob[out + t] = wt / sum;
+      }
+      if (t == 0) a.q_nnz[r] = bad ? -1 : keep;
+    }
+    return;
+  }
   float inc = wt;
 #pragma unroll
   for (int q = 1; q < 64; q <<= 1) {
