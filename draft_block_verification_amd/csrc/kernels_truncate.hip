@@ -55,7 +55,7 @@ static_assert(kTruncCand >= 3 * kTB, "every thread's three kept logits fit");
 
 struct TruncLds {
   int hist[256];
-  int bad, digit, above, n, keep, nc;
+  int bad, digit, above, n, keep, nc, chunk;
   uint32_t tau_key, drop_key;
   uint32_t wtau[kTW];
   __align__(16) uint2 rk[kRankCand + 2];   // ranked candidates: key, place
@@ -352,6 +352,71 @@ __device__ __forceinline__ uint32_t wave_kth_key(uint32_t key, int kw) {
   return res;
 }
 
+// stream_row over [0, V) for a whole group whose waves share the SIMDs
+// (several waves each): the waves claim chunks of U vectors per lane from
+// s.chunk in turn, instead of fixed strides, so that a wave the SIMD
+// arbiter favours takes more chunks and the waves finish together.  Each
+// lane's vectors still come in increasing order.  s.chunk must be 0.
+template <int DT, int U, class Op>
+__device__ __forceinline__ void stream_row_claimed(const char* row, int64_t V, Op& op, int* chunk) {
+  using E = Elem<DT>;
+  constexpr int W = E::kVec;
+  constexpr int CV = 64 * U;   // vectors of one chunk
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(row);
+  int64_t head = static_cast<int64_t>(((16u - (a & 15u)) & 15u) / E::kBytes);
+  if (head > V) head = V;
+  const int64_t nvec = (V - head) / W;
+  const int64_t a1 = head + nvec * W;
+  if (t < head) {
+    float x[1] = {E::load1(row, t)};
+    op.template group<1>(x, t);
+  }
+  const char* vb = row + head * E::kBytes;
+  const int64_t nchunk = (nvec + CV - 1) / CV;
+  for (;;) {
+    int c = 0;
+    if (lane == 0) c = atomicAdd(chunk, 1);
+    c = __builtin_amdgcn_readfirstlane(c);
+    if (c >= nchunk) break;
+    const int64_t i0 = static_cast<int64_t>(c) * CV + lane;
+    if (static_cast<int64_t>(c + 1) * CV <= nvec) {
+      u32x4 r[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) r[u] = load16(vb + (i0 + u * 64) * 16);
+      __builtin_amdgcn_sched_barrier(0);
+      float x[U * W];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float y[W];
+        E::unpack(r[u], y);
+#pragma unroll
+        for (int j = 0; j < W; ++j) x[u * W + j] = y[j];
+      }
+      op.template block<U, W>(x, head + i0 * W, static_cast<int64_t>(64) * W);
+    } else {   // the last chunk, partly past the row
+      u32x4 r[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i0 + u * 64 < nvec) r[u] = load16(vb + (i0 + u * 64) * 16);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (i0 + u * 64 < nvec) {
+          float y[W];
+          E::unpack(r[u], y);
+          op.template group<W>(y, head + (i0 + u * 64) * W);
+        }
+      }
+    }
+  }
+  if (a1 + t < V) {
+    float x[1] = {E::load1(row, a1 + t)};
+    op.template group<1>(x, a1 + t);
+  }
+}
+
 // Two groups per CU: at most 64 VGPRs (8 waves per SIMD).
 template <int DT>
 __global__ __launch_bounds__(kTB, 8) void k_truncate(TruncArgs a) {
@@ -378,12 +443,13 @@ __global__ __launch_bounds__(kTB, 8) void k_truncate(TruncArgs a) {
     s.bad = 0;
     s.nc = 0;
     s.n = 0;
+    s.chunk = 0;
     s.tau_key = 0xFFFFFFFFu;
     s.drop_key = 0;
   }
   __syncthreads();
   Top3Op op;
-  stream_row<DT, 2, Top3Op, kTB>(row, 0, V, op);
+  stream_row_claimed<DT, 2>(row, V, op, &s.chunk);
   // one LDS atomic per wave for the row check and the largest dropped key
   // (a thread that dropped nothing reports -inf: a k-th key of -inf, from a
   // row with fewer than k finite logits, always takes the exact path)
