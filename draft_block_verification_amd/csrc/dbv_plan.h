@@ -329,8 +329,9 @@ struct TreePlan {
 };
 
 // Vocabulary chunks per state for the Gumbel argmax (one row per state):
-// about kGumbelGroups groups in all, chunks of at least 4096 elements.
-constexpr int64_t kGumbelGroups = 4096;
+// about kGumbelGroups one-wave items in all, chunks of at least 4096
+// elements.
+constexpr int64_t kGumbelGroups = 16384;
 inline int choose_split(int64_t rows, int64_t V) {
   if (rows <= 0) return 1;
   int64_t s = cdiv(kGumbelGroups, rows);

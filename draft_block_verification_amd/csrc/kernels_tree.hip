@@ -352,24 +352,8 @@ struct ArgmaxPick2 : ArgmaxPick {
   }
 };
 
-// The second-largest score of a group's elements, given each thread's
-// (best, index, second) and the group's argmax (best, idx) in thread 0:
-// the largest of every other thread's best and the winning thread's second.
-// Valid in thread 0.
-__device__ __forceinline__ float block_second(float tbest, int tidx, float tsecond, float best, int idx, float* s_v,
-                                              int* s_i, int* s_n) {
-  if (threadIdx.x == 0) { s_v[0] = best; s_i[0] = idx; }
-  __syncthreads();
-  const bool win = tbest == s_v[0] && tidx == s_i[0];
-  __syncthreads();
-  float c = win ? tsecond : tbest;
-  int ci = 0, cn = 0;
-  block_argmax(c, ci, cn, s_v, s_i, s_n);
-  return c;
-}
-
 // Argmax of z/T + g over a logit row and its Gumbel row read together.
-template <int DT, class Pick>
+template <int DT, int NT, class Pick>
 __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64_t v1, float inv_t,
                               Pick& pk) {
   using E = Elem<DT>;
@@ -381,7 +365,7 @@ __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64
   const int64_t a0 = v0 + head;
   const bool gal = ((reinterpret_cast<uintptr_t>(gr + a0)) & 15u) == 0;
   if (!gal) {  // Gumbel row not aligned with the logits: scalar path
-    for (int64_t j = v0 + t; j < v1; j += kBlock) {
+    for (int64_t j = v0 + t; j < v1; j += NT) {
       float x[1] = {__builtin_fmaf(E::load1(xr, j), inv_t, gr[j])};
       pk.template group<1>(x, j);
     }
@@ -398,13 +382,13 @@ __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64
   constexpr int GV = W / 4;  // 16-byte Gumbel loads per logit vector
   constexpr int U = 4;       // logit vectors in flight per lane
   int64_t i = t;
-  for (; i + (U - 1) * kBlock < nvec; i += U * kBlock) {
+  for (; i + (U - 1) * NT < nvec; i += U * NT) {
     u32x4 xv[U], g[U][GV];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      xv[u] = load16(xb + (i + u * kBlock) * 16);
+      xv[u] = load16(xb + (i + u * NT) * 16);
 #pragma unroll
-      for (int q = 0; q < GV; ++q) g[u][q] = load16(gb + ((i + u * kBlock) * W + q * 4) * 4);
+      for (int q = 0; q < GV; ++q) g[u][q] = load16(gb + ((i + u * NT) * W + q * 4) * 4);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -413,10 +397,10 @@ __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64
       E::unpack(xv[u], x);
 #pragma unroll
       for (int j = 0; j < W; ++j) x[j] = __builtin_fmaf(x[j], inv_t, __uint_as_float(g[u][j / 4][j % 4]));
-      pk.template group<W>(x, a0 + (i + u * kBlock) * W);
+      pk.template group<W>(x, a0 + (i + u * NT) * W);
     }
   }
-  for (; i < nvec; i += kBlock) {
+  for (; i < nvec; i += NT) {
     u32x4 xv = load16(xb + i * 16);
     u32x4 g[GV];
 #pragma unroll
@@ -437,7 +421,7 @@ __device__ void gumbel_argmax(const char* xr, const float* gr, int64_t v0, int64
 // states of one batch have the same s*): each Gumbel vector is loaded once
 // and used for every row.  Rows and the Gumbel row must be 16-byte aligned
 // at v0 (the caller checks); n rows are live (uniform across the group).
-template <int DT, int NB, class Pick>
+template <int DT, int NB, int NT, class Pick>
 __device__ void gumbel_argmax_batch(const char* const (&xr)[NB], int n, const float* gr, int64_t v0, int64_t v1,
                                     float inv_t, Pick (&pk)[NB]) {
   using E = Elem<DT>;
@@ -448,17 +432,17 @@ __device__ void gumbel_argmax_batch(const char* const (&xr)[NB], int n, const fl
   const int64_t nvec = (v1 - v0) / W;
   const char* gb = reinterpret_cast<const char*>(gr + v0);
   int64_t i = t;
-  for (; i + (U - 1) * kBlock < nvec; i += U * kBlock) {
+  for (; i + (U - 1) * NT < nvec; i += U * NT) {
     u32x4 g[U][GV], xv[NB][U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int q = 0; q < GV; ++q) g[u][q] = load16(gb + ((i + u * kBlock) * W + q * 4) * 4);
+      for (int q = 0; q < GV; ++q) g[u][q] = load16(gb + ((i + u * NT) * W + q * 4) * 4);
 #pragma unroll
     for (int r = 0; r < NB; ++r)
       if (r < n)
 #pragma unroll
-        for (int u = 0; u < U; ++u) xv[r][u] = load16(xr[r] + (v0 + (i + u * kBlock) * W) * E::kBytes);
+        for (int u = 0; u < U; ++u) xv[r][u] = load16(xr[r] + (v0 + (i + u * NT) * W) * E::kBytes);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
@@ -469,12 +453,12 @@ __device__ void gumbel_argmax_batch(const char* const (&xr)[NB], int n, const fl
           E::unpack(xv[r][u], x);
 #pragma unroll
           for (int j = 0; j < W; ++j) x[j] = __builtin_fmaf(x[j], inv_t, __uint_as_float(g[u][j / 4][j % 4]));
-          pk[r].template group<W>(x, v0 + (i + u * kBlock) * W);
+          pk[r].template group<W>(x, v0 + (i + u * NT) * W);
         }
       }
     }
   }
-  for (; i < nvec; i += kBlock) {
+  for (; i < nvec; i += NT) {
     u32x4 g[GV];
 #pragma unroll
     for (int q = 0; q < GV; ++q) g[q] = load16(gb + (i * W + q * 4) * 4);
@@ -489,7 +473,7 @@ __device__ void gumbel_argmax_batch(const char* const (&xr)[NB], int n, const fl
       }
     }
   }
-  for (int64_t e = v0 + nvec * W + t; e < v1; e += kBlock) {
+  for (int64_t e = v0 + nvec * W + t; e < v1; e += NT) {
     const float ge = gr[e];
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
@@ -547,10 +531,19 @@ __device__ void tree_walk(const TreeArgs& a, int b, int* s_pos, int* s_tok) {
         float v = -kInf;
         int idx = -1, nan = 0;
         const float2* pk = a.pick + sy * a.split2;
-        for (int k = 0; k < a.split2; ++k) {
-          const int i2 = __float_as_int(pk[k].y);
-          if (pk[k].x != pk[k].x) { nan = 1; continue; }
-          if (pick_better(pk[k].x, i2, v, idx)) { v = pk[k].x; idx = i2; }
+        // the chunks in order, eight requested at a time
+        for (int k0 = 0; k0 < a.split2; k0 += 8) {
+          float2 q[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) q[u] = pk[k0 + u < a.split2 ? k0 + u : a.split2 - 1];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            if (k0 + u < a.split2) {
+              const int i2 = __float_as_int(q[u].y);
+              if (q[u].x != q[u].x) nan = 1;
+              else if (pick_better(q[u].x, i2, v, idx)) { v = q[u].x; idx = i2; }
+            }
+          }
         }
         st |= nan ? SEQ_NONFINITE : max_status(v);
         tok = idx;
@@ -783,12 +776,17 @@ __host__ __device__ inline int64_t gumbel_stride(int B, int split2) {
   return (static_cast<int64_t>(B) * split2 + kXcds - 1) / kXcds * kXcds;
 }
 
-// Item w: each state's argmax over the chunk of z/T + G[s*] (z at T = 0).
-// TWO: also the chunk's second-largest score (tok_margin).  One load of a
-// Gumbel chunk serves every state of the batch.  Every thread of the group
-// calls it with the same w.
+// One wave per Gumbel item: with many small groups instead of fewer large
+// ones the hardware places about the same work on every CU (with 256-thread
+// items the CUs held 13 to 20 states and the kernel waited for the fullest).
+constexpr int kGumbelThreads = 64;
+
+// Item w, one wave: each state's argmax over the chunk of z/T + G[s*] (z at
+// T = 0).  TWO: also the chunk's second-largest score (tok_margin).  One
+// load of a Gumbel chunk serves every state of the batch.
 template <int DT, bool TWO>
-__device__ __forceinline__ void gumbel_item(const TreeArgs& a, int64_t w, float* s_v, int* s_i, int* s_n) {
+__device__ __forceinline__ void gumbel_item(const TreeArgs& a, int64_t w) {
+  constexpr int NT = kGumbelThreads;
   using E = Elem<DT>;
   using Pick = typename std::conditional<TWO, ArgmaxPick2, ArgmaxPick>::type;
   const int64_t P = gumbel_stride(a.B, a.split2);
@@ -822,16 +820,16 @@ __device__ __forceinline__ void gumbel_item(const TreeArgs& a, int64_t w, float*
   if (a.inv_t > 0.f) {
     const float* gr = a.gumbel + b * a.gs + s * a.gp;
     if (((al | reinterpret_cast<uintptr_t>(gr + v0)) & 15u) == 0) {
-      gumbel_argmax_batch<DT, kBatch>(xr, n, gr, v0, v1, a.inv_t, pk);
+      gumbel_argmax_batch<DT, kBatch, NT>(xr, n, gr, v0, v1, a.inv_t, pk);
     } else {
 #pragma unroll
       for (int r = 0; r < kBatch; ++r)
-        if (r < n) gumbel_argmax<DT>(xr[r], gr, v0, v1, a.inv_t, pk[r]);
+        if (r < n) gumbel_argmax<DT, NT>(xr[r], gr, v0, v1, a.inv_t, pk[r]);
     }
   } else {
 #pragma unroll
     for (int r = 0; r < kBatch; ++r)
-      if (r < n) stream_row<DT, 4>(xr[r], v0, v1, pk[r]);
+      if (r < n) stream_row<DT, 4, Pick, NT>(xr[r], v0, v1, pk[r]);
   }
 #pragma unroll
   for (int r = 0; r < kBatch; ++r) {
@@ -842,23 +840,23 @@ __device__ __forceinline__ void gumbel_item(const TreeArgs& a, int64_t w, float*
       int nan = pk[r].nan ? 1 : 0;
       const float tb = v;
       const int ti = ii;
-      block_argmax(v, ii, nan, s_v, s_i, s_n);
+      wave_argmax(v, ii, nan);
       if (threadIdx.x == 0) a.pick[gid] = make_float2(nan ? __builtin_nanf("") : v, __int_as_float(ii));
       if constexpr (TWO) {
-        __syncthreads();
-        const float v2 = block_second(tb, ti, pk[r].second, v, ii, s_v, s_i, s_n);
-        if (threadIdx.x == 0) a.pick2[gid] = v2;
+        // the largest of every other lane's best and the winning lane's
+        // second
+        float c = (tb == v && ti == ii) ? pk[r].second : tb;
+        int ci = 0, cn = 0;
+        wave_argmax(c, ci, cn);
+        if (threadIdx.x == 0) a.pick2[gid] = c;
       }
-      __syncthreads();
     }
   }
 }
 
 template <int DT, bool TWO>
-__global__ __launch_bounds__(kBlock) void k_tree_gumbel(TreeArgs a) {
-  __shared__ float s_v[kWaves];
-  __shared__ int s_i[kWaves], s_n[kWaves];
-  gumbel_item<DT, TWO>(a, blockIdx.x, s_v, s_i, s_n);
+__global__ __launch_bounds__(kGumbelThreads) void k_tree_gumbel(TreeArgs a) {
+  gumbel_item<DT, TWO>(a, blockIdx.x);
 }
 
 template <int DT>
@@ -892,7 +890,7 @@ bool launch_tree(const TreeArgs& a, int dtype, hipStream_t stream, const TimingE
          launch(bf ? fn(k_tree_select<DT_BF16>) : fn(k_tree_select<DT_F32>), static_cast<int64_t>(a.B) * a.S, stream,
                 a) &&
          launch(fn(k_tree_batch), a.B, stream, a) &&
-         launch(gum, items, stream, a) &&
+         launch_threads(gum, items, kGumbelThreads, stream, a) &&
          launch(bf ? fn(k_tree_walk<DT_BF16>) : fn(k_tree_walk<DT_F32>), a.B, stream, a);
 }
 
