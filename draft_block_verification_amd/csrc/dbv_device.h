@@ -786,12 +786,15 @@ __device__ __forceinline__ void combine_rows_stats(int nrows, const float2* part
 
 // kf(r) is the log2(e)/T of row r; done(r, M, R) receives the row's
 // maximum and float64 rest.
-template <int NT = kBlock, class KFn, class SpanFn, class DoneFn>
+// LANES lanes per row (a power of two up to kRowLanes): fewer lanes take
+// more rows per pass, so that a sequence's rows are all requested at once.
+template <int NT = kBlock, int LANES = kRowLanes, class KFn, class SpanFn, class DoneFn>
 __device__ __forceinline__ void combine_rows_stats64(int nrows, const Stat64* part, KFn kf, SpanFn span,
                                                      DoneFn done) {
-  const int sub = threadIdx.x % kRowLanes;
-  for (int r0 = 0; r0 < nrows; r0 += NT / kRowLanes) {
-    const int r = r0 + static_cast<int>(threadIdx.x) / kRowLanes;
+  static_assert(LANES >= 1 && LANES <= kRowLanes && (LANES & (LANES - 1)) == 0, "lanes per row");
+  const int sub = threadIdx.x % LANES;
+  for (int r0 = 0; r0 < nrows; r0 += NT / LANES) {
+    const int r = r0 + static_cast<int>(threadIdx.x) / LANES;
     const float k = kf(r < nrows ? r : nrows - 1);
     float M = -kInf;
     double S = 0.0;
@@ -799,11 +802,11 @@ __device__ __forceinline__ void combine_rows_stats64(int nrows, const Stat64* pa
       int64_t first, n;
       span(r, first, n);
       const Stat64* p = part + first;
-      for (int64_t j0 = 0; j0 < n; j0 += kRowLanes * kRowLoads) {
+      for (int64_t j0 = 0; j0 < n; j0 += LANES * kRowLoads) {
         Stat64 buf[kRowLoads];
 #pragma unroll
         for (int q = 0; q < kRowLoads; ++q) {
-          const int64_t j = j0 + sub + static_cast<int64_t>(q) * kRowLanes;
+          const int64_t j = j0 + sub + static_cast<int64_t>(q) * LANES;
           if (j < n) buf[q] = p[j];
           else { buf[q].M = -kInf; buf[q].R = 0.0; }
         }
@@ -812,7 +815,7 @@ __device__ __forceinline__ void combine_rows_stats64(int nrows, const Stat64* pa
       }
     }
 #pragma unroll
-    for (int m = kRowLanes / 2; m >= 1; m >>= 1) {
+    for (int m = LANES / 2; m >= 1; m >>= 1) {
       const float M2 = __shfl_xor(M, m, 64);
       const double S2 = __shfl_xor(S, m, 64);
       stats64_merge(M, S, M2, S2, k);

@@ -736,25 +736,30 @@ __device__ __forceinline__ DrawRecord draw_decide(const SampleArgs& a, int b, bo
     // The target rows 0..n and the drafter rows 0..n-1 in one pass, so all
     // their partials are requested together.
     const int nd = a.drows ? n : 0;
-    combine_rows_stats64<NT>(
-        n + 1 + nd, a.stats, [&](int r) { return r <= n ? a.kp : a.kq; },
-        [&](int r, int64_t& first_slot, int64_t& cnt) {
-          if (r <= n) {
-            tspan(r, first_slot, cnt);
-          } else {
-            split_row_slots(f, p0 + static_cast<int64_t>(P) * (n + 1) + (r - n - 1), first_slot, cnt);
-            first_slot *= kWaves;
-            cnt *= kWaves;
-          }
-        },
-        [&](int r, float M, double R) {
-          if (r <= n) {
-            s.Mp[r] = M; s.Rp[r] = R;
-          } else {
-            s.Mq[r - n - 1] = M; s.Rq[r - n - 1] = R;
-          }
-          st |= stats64_status(M, R);
-        });
+    const int nr = n + 1 + nd;
+    auto kfn = [&](int r) { return r <= n ? a.kp : a.kq; };
+    auto span = [&](int r, int64_t& first_slot, int64_t& cnt) {
+      if (r <= n) {
+        tspan(r, first_slot, cnt);
+      } else {
+        split_row_slots(f, p0 + static_cast<int64_t>(P) * (n + 1) + (r - n - 1), first_slot, cnt);
+        first_slot *= kWaves;
+        cnt *= kWaves;
+      }
+    };
+    auto done = [&](int r, float M, double R) {
+      if (r <= n) {
+        s.Mp[r] = M; s.Rp[r] = R;
+      } else {
+        s.Mq[r - n - 1] = M; s.Rq[r - n - 1] = R;
+      }
+      st |= stats64_status(M, R);
+    };
+    // Half the lanes per row where that takes every row in one pass.
+    if (nr > NT / kRowLanes && nr <= 2 * NT / kRowLanes)
+      combine_rows_stats64<NT, kRowLanes / 2>(nr, a.stats, kfn, span, done);
+    else
+      combine_rows_stats64<NT>(nr, a.stats, kfn, span, done);
     if (P > 1)
       combine_rows_pick<NT>(n + 1, a.gpart, tspan, [&](int r, float v, int idx, int nan) {
         s.g[r] = idx;
