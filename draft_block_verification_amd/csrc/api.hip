@@ -236,6 +236,7 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.rec = reinterpret_cast<dbv::DrawRecord*>(w + plan.off_rec);
   a.tmass = reinterpret_cast<float*>(w + plan.off_tmass);
   a.sq = reinterpret_cast<dbv::SparseRow*>(w + plan.off_sq);
+  a.blk = B > dbv::kSeqBlocks ? reinterpret_cast<int32_t*>(w + plan.off_blk) : nullptr;
   const int64_t P = rl.gumbel ? dbv::gumbel_parts(static_cast<int64_t>(eb)) : 1;
   a.grid = dbv::stream_grid(static_cast<int64_t>(B) * (P * (K + 1) + K), V, static_cast<int64_t>(eb),
                             group_cap(co));

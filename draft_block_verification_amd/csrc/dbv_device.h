@@ -541,14 +541,36 @@ struct SeqDir {
   int nblk;
 };
 
-template <class CountFn>
-__device__ __forceinline__ SeqDir build_seq_dir(int B, CountFn count, int* pre, int* s_w) {
+// q: a power of two, so that a wave's 64 consecutive sequences cover whole
+// blocks (q <= 64) or lie in one block (q >= 64); at most kSeqBlocks blocks.
+__host__ __device__ inline SeqDir seq_dir_shape(int B) {
   SeqDir d;
-  // q: a power of two, so that a wave's 64 consecutive sequences cover whole
-  // blocks (q <= 64) or lie in one block (q >= 64)
   d.q = 1;
   while (static_cast<int64_t>(d.q) * kSeqBlocks < B) d.q <<= 1;
-  d.nblk = static_cast<int>(cdiv(B, d.q));
+  d.nblk = static_cast<int>((B + d.q - 1) / d.q);
+  return d;
+}
+
+// The LDS prefix pre[] from each thread's kSeqBlocks / kBlock block sums
+// (blocks threadIdx.x * kPer + k) and their total `mine`.
+template <int kPer>
+__device__ __forceinline__ void finish_seq_dir(const SeqDir& d, const int (&sums)[kPer], int mine, int* pre,
+                                               int* s_w) {
+  int total;
+  int off = group_exclusive_scan<kWaves>(mine, total, s_w);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int j = threadIdx.x * kPer + k;
+    if (j < d.nblk) pre[j] = off;
+    off += sums[k];
+  }
+  if (threadIdx.x == 0) pre[d.nblk] = total;
+  __syncthreads();
+}
+
+template <class CountFn>
+__device__ __forceinline__ SeqDir build_seq_dir(int B, CountFn count, int* pre, int* s_w) {
+  const SeqDir d = seq_dir_shape(B);
   constexpr int kPer = kSeqBlocks / kBlock;     // blocks per thread
   int sums[kPer];
   int mine = 0;
@@ -595,16 +617,26 @@ __device__ __forceinline__ SeqDir build_seq_dir(int B, CountFn count, int* pre, 
       mine += s;
     }
   }
-  int total;
-  int off = group_exclusive_scan<kWaves>(mine, total, s_w);
+  finish_seq_dir(d, sums, mine, pre, s_w);
+  return d;
+}
+
+// The directory from block sums that a preceding kernel wrote (blk[j] = the
+// rows of block j, k_seq_blocks), for calls of more than kSeqBlocks
+// sequences: one load per block instead of every sequence's count in every
+// group.
+__device__ __forceinline__ SeqDir load_seq_dir(int B, const int32_t* blk, int* pre, int* s_w) {
+  SeqDir d = seq_dir_shape(B);
+  constexpr int kPer = kSeqBlocks / kBlock;
+  int sums[kPer];
+  int mine = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int j = threadIdx.x * kPer + k;
-    if (j < d.nblk) pre[j] = off;
-    off += sums[k];
+    sums[k] = j < d.nblk ? blk[j] : 0;
+    mine += sums[k];
   }
-  if (threadIdx.x == 0) pre[d.nblk] = total;
-  __syncthreads();
+  finish_seq_dir(d, sums, mine, pre, s_w);
   return d;
 }
 

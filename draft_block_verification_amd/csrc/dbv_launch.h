@@ -63,6 +63,7 @@ struct SampleArgs {
   Stat64* stats;                       // per (slot, wave): M and the float64 sum
   float2* gpart;                       // per (slot, wave), with Gumbel rows
   int32_t* pre;                        // [B + 1] first stream row per sequence
+  int32_t* blk;                        // [kSeqBlocks] rows per directory block, or NULL (B <= kSeqBlocks)
   DrawRecord* rec;                     // per sequence
   float* tmass;                        // per (sequence, draw tile)
   SparseRow* sq;                       // per sequence: stored sparse Q of row h

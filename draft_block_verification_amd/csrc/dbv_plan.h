@@ -279,6 +279,8 @@ struct SamplePlan {
   size_t off_rec;      // DrawRecord per sequence
   size_t off_tmass;    // float per (sequence, draw tile)
   size_t off_sq;       // SparseRow per sequence (stored sparse Q of row h)
+  size_t off_blk;      // int32 [kSeqBlocks]: stream rows per directory block
+                       // (B > kSeqBlocks: summed once by k_seq_blocks)
   size_t bytes;
 };
 
@@ -295,7 +297,8 @@ inline SamplePlan plan_sample(int B, int K, int V, int64_t elem_bytes) {
   p.off_rec = p.off_pre + align256(static_cast<size_t>(B + 1) * 4);
   p.off_tmass = p.off_rec + align256(static_cast<size_t>(B) * sizeof(DrawRecord));
   p.off_sq = p.off_tmass + align256(static_cast<size_t>(B) * p.tiles * 4);
-  p.bytes = p.off_sq + align256(static_cast<size_t>(B) * sizeof(SparseRow));
+  p.off_blk = p.off_sq + align256(static_cast<size_t>(B) * sizeof(SparseRow));
+  p.bytes = p.off_blk + align256(static_cast<size_t>(kSeqBlocks) * 4);
   return p;
 }
 

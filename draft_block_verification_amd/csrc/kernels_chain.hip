@@ -277,6 +277,25 @@ __device__ void stats_and_gumbel(const char* xr, const float* gr, int64_t v0, in
 // Rows of at most this many bytes are streamed a piece per wave.
 constexpr int64_t kSmallRowBytes = 16384;
 
+// Rows per directory block for calls of more than kSeqBlocks sequences
+// (SeqDir): one wave per block sums its sequences' row counts, 64 at a
+// time, so that the row kernel's groups load the block sums instead of
+// counting every sequence each.
+template <int DT, bool GUM>
+__global__ __launch_bounds__(kBlock) void k_seq_blocks(SampleArgs a) {
+  constexpr int P = GUM ? (Elem<DT>::kBytes + 4) / Elem<DT>::kBytes : 1;
+  const SeqDir d = seq_dir_shape(a.B);
+  const int j = static_cast<int>(blockIdx.x) * kWaves + wave_id();
+  if (j >= d.nblk) return;
+  const int lane = lane_id();
+  const int b1 = (j + 1) * d.q < a.B ? (j + 1) * d.q : a.B;
+  int sum = 0;
+  for (int b = j * d.q + lane; b < b1; b += 64) sum += sample_count(a, b, P);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+  if (lane == 0) a.blk[j] = sum;
+}
+
 // GUM: target rows are read with their Gumbel rows (joint-space chain with
 // coupled-noise links).
 // SMALL: rows of at most kSmallRowBytes, streamed a piece per wave.
@@ -286,7 +305,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
   __shared__ int s_w[kWaves];
   constexpr int P = GUM ? (Elem<DT>::kBytes + 4) / Elem<DT>::kBytes : 1;
   auto count = [&](int b) { return sample_count(a, b, P); };
-  const SeqDir dir = build_seq_dir(a.B, count, s_pre, s_w);
+  const SeqDir dir = a.blk ? load_seq_dir(a.B, a.blk, s_pre, s_w) : build_seq_dir(a.B, count, s_pre, s_w);
   write_seq_starts(dir, s_pre, a.B, count, a.pre, blockIdx.x, gridDim.x);
   const FlatSplit f = make_split(s_pre[dir.nblk], a.V, Elem<DT>::kBytes, a.grid);
   const int64_t g = blockIdx.x;
@@ -1521,6 +1540,11 @@ bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const Tim
   const void* rows = a.gumbel ? (bf ? fn(k_sample_rows<DT_BF16, true>) : fn(k_sample_rows<DT_F32, true>))
                      : short_rows ? (bf ? fn(k_sample_rows<DT_BF16, false, true>) : fn(k_sample_rows<DT_F32, false, true>))
                               : (bf ? fn(k_sample_rows<DT_BF16, false>) : fn(k_sample_rows<DT_F32, false>));
+  if (a.blk) {
+    const void* blocks = a.gumbel ? (bf ? fn(k_seq_blocks<DT_BF16, true>) : fn(k_seq_blocks<DT_F32, true>))
+                                  : (bf ? fn(k_seq_blocks<DT_BF16, false>) : fn(k_seq_blocks<DT_F32, false>));
+    if (!launch(blocks, (seq_dir_shape(a.B).nblk + kWaves - 1) / kWaves, stream, a)) return false;
+  }
   if (!launch(rows, a.grid, stream, a, ev)) return false;
   const int fam = a.rule == RULE_SPOT ? FAM_SPOT : (a.rule == RULE_SPARSE ? FAM_SPARSE : FAM_TOKEN);
   // [family][dtype == bf16]

@@ -235,7 +235,10 @@ int main() {
                 "pre overlaps gpart");
           CHECK(s.off_rec >= s.off_pre + static_cast<size_t>(B + 1) * 4, "rec overlaps pre");
           CHECK(s.off_tmass >= s.off_rec + static_cast<size_t>(B) * sizeof(DrawRecord), "tmass overlaps rec");
-          CHECK(s.bytes >= s.off_tmass + static_cast<size_t>(B) * s.tiles * 4, "sample bytes");
+          CHECK(s.off_sq >= s.off_tmass + static_cast<size_t>(B) * s.tiles * 4, "sq overlaps tmass");
+          CHECK(s.off_blk % 256 == 0 && s.off_blk >= s.off_sq + static_cast<size_t>(B) * sizeof(SparseRow),
+                "blk overlaps sq");
+          CHECK(s.bytes >= s.off_blk + static_cast<size_t>(kSeqBlocks) * 4, "sample bytes");
         }
 
         const GreedyPlan g = plan_greedy(B, K, K + 1, static_cast<int>(V));
