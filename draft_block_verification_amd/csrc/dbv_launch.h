@@ -198,14 +198,14 @@ struct TimingEvents {
 // grid still records both events so that the caller can read them.
 template <typename Arg>
 bool launch_threads(const void* kern, int64_t grid, int threads, hipStream_t stream, const Arg& arg,
-                    const TimingEvents& ev = TimingEvents()) {
+                    const TimingEvents& ev = TimingEvents(), size_t lds_bytes = 0) {
   if (grid <= 0) {
     if (ev.begin) (void)hipEventRecord(ev.begin, stream);
     if (ev.end) (void)hipEventRecord(ev.end, stream);
     return true;
   }
   void* args[] = {const_cast<Arg*>(&arg)};
-  return hipExtLaunchKernel(kern, dim3(static_cast<unsigned>(grid)), dim3(threads), args, 0, stream,
+  return hipExtLaunchKernel(kern, dim3(static_cast<unsigned>(grid)), dim3(threads), args, lds_bytes, stream,
                             ev.begin, ev.end, 0) == hipSuccess;
 }
 

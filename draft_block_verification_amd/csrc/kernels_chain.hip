@@ -656,21 +656,47 @@ __device__ __forceinline__ float prob64(float x, float k, float M, double R) {
   return fast_exp2(__builtin_fmaf(x, k, -ref_exp(M, k))) * static_cast<float>(1.0 / stats64_total(M, R, k));
 }
 
-// LDS of the decision step (per sequence): row statistics of the target rows
-// 0..n and drafter rows 0..n-1, and d, p(d), p~(d), q(d) of the rejected
-// draft.
-struct DecideLds {
-  float Mp[kMaxDraft + 1];
-  double Rp[kMaxDraft + 1];
-  // Drafter rows' statistics, or (stored sparse Q) each draft's token and
-  // Q(d) summed from its row's entries.
-  union { float Mq[kMaxDraft]; float qd[kMaxDraft]; };
-  union { double Rq[kMaxDraft]; int dtok[kMaxDraft]; };
-  int g[kMaxDraft + 1];      // joint-space chain: Gumbel argmax of target rows
+// LDS of the decision step (per sequence): the status, h, and d, p(d),
+// p~(d), q(d) of the rejected draft ...
+struct DecideScalars {
   int st, h;
   int dh, modeh;
   float ph, pth, qh, ch;
 };
+
+// ... and, in the launch's dynamic LDS sized for the call's K
+// (decide_lds_bytes), the row statistics of the target rows 0..n and the
+// drafter rows 0..n-1 -- or (stored sparse Q) each draft's token and Q(d)
+// summed from its row's entries -- and (joint-space chain) the Gumbel argmax
+// of the target rows.  Every thread holds the same view.
+struct DecideLds {
+  double* Rp;
+  double* Rq;
+  float* Mp;
+  float* Mq;
+  int* g;
+  float* qd;     // aliases Mq
+  int* dtok;     // aliases Rq
+  DecideScalars* sc;
+};
+
+__host__ __device__ constexpr size_t decide_lds_bytes(int K) {
+  return static_cast<size_t>(K + 1) * 8 + static_cast<size_t>(K) * 8 + static_cast<size_t>(K + 1) * 4 +
+         static_cast<size_t>(K) * 4 + static_cast<size_t>(K + 1) * 4;
+}
+
+__device__ __forceinline__ DecideLds decide_view(char* dyn, int K, DecideScalars* sc) {
+  DecideLds v;
+  v.Rp = reinterpret_cast<double*>(dyn);
+  v.Rq = v.Rp + (K + 1);
+  v.Mp = reinterpret_cast<float*>(v.Rq + K);
+  v.Mq = v.Mp + (K + 1);
+  v.g = reinterpret_cast<int*>(v.Mq + K);
+  v.qd = v.Mq;
+  v.dtok = reinterpret_cast<int*>(v.Rq);
+  v.sc = sc;
+  return v;
+}
 
 // The decision of sequence b by a group of NT threads:
 //  1. Every input is requested at once: the length, budget, draft tokens,
@@ -731,8 +757,8 @@ __device__ __forceinline__ DrawRecord draw_decide(const SampleArgs& a, int b, bo
   if (t == 0) {
     // pos_star of the bonus row n (rows 0..n-1 are checked with their links)
     const bool bad_star = spot && !nbad && a.pos_star[static_cast<int64_t>(b) * (a.K + 1) + n] < 0;
-    s.st = (nbad || budget < 0 || bad_star) ? SEQ_BAD_INPUT : 0;
-    s.h = n;
+    s.sc->st = (nbad || budget < 0 || bad_star) ? SEQ_BAD_INPUT : 0;
+    s.sc->h = n;
   }
   __syncthreads();
   if (!nbad) {
@@ -815,11 +841,11 @@ __device__ __forceinline__ DrawRecord draw_decide(const SampleArgs& a, int b, bo
       if (v == s.dtok[i]) atomicAdd(&s.qd[i], pr);
     }
   }
-  if (st) atomicOr(&s.st, st);
+  if (st) atomicOr(&s.sc->st, st);
   __syncthreads();
   DrawRecord rec{};
-  if (s.st & SEQ_ERROR_MASK) {
-    rec.status = s.st;
+  if (s.sc->st & SEQ_ERROR_MASK) {
+    rec.status = s.sc->st;
     if (first) {
       int32_t* out = a.out_tokens + static_cast<int64_t>(b) * (a.K + 1);
       for (int i = t; i <= a.K; i += NT) out[i] = -1;
@@ -835,7 +861,7 @@ __device__ __forceinline__ DrawRecord draw_decide(const SampleArgs& a, int b, bo
         a.num_out[b] = 0;
         if (a.residual_mass) a.residual_mass[b] = 0.f;
         if (a.draw_margin) a.draw_margin[b] = 1.f;
-        if (a.status) a.status[b] = s.st;
+        if (a.status) a.status[b] = s.sc->st;
       }
     }
     return rec;
@@ -868,17 +894,17 @@ __device__ __forceinline__ DrawRecord draw_decide(const SampleArgs& a, int b, bo
           acc = on && di[k] == s.g[i];
           al = acc ? 1.f : 0.f;
         } else {
-          if (on && q == 0.f && p > 0.f) atomicOr(&s.st, SEQ_Q_ZERO);
+          if (on && q == 0.f && p > 0.f) atomicOr(&s.sc->st, SEQ_Q_ZERO);
           al = on ? (q > 0.f ? fminf(1.f, p / q) : (p > 0.f ? 1.f : 0.f)) : 0.f;
           acc = on && ui[k] * q < p;
         }
       } else {
         pt = a.rule == RULE_CACTUS ? cactus_gamma(p, a.delta) : (1.f - a.lam) * p + a.lam * q;
-        if (q == 0.f && pt > 0.f) atomicOr(&s.st, SEQ_Q_ZERO);
+        if (q == 0.f && pt > 0.f) atomicOr(&s.sc->st, SEQ_Q_ZERO);
         al = q > 0.f ? fminf(1.f, pt / q) : (pt > 0.f ? 1.f : 0.f);
         acc = ui[k] * q < pt;
       }
-      if (!acc) atomicMin(&s.h, i);
+      if (!acc) atomicMin(&s.sc->h, i);
     }
     pk[k] = p;
     ptk[k] = pt;
@@ -893,23 +919,23 @@ __device__ __forceinline__ DrawRecord draw_decide(const SampleArgs& a, int b, bo
   }
   __syncthreads();
   // Uniform across the group: keeps the row addresses in scalar registers.
-  const int h = __builtin_amdgcn_readfirstlane(s.h);
+  const int h = __builtin_amdgcn_readfirstlane(s.sc->h);
   const bool resid = h < n;
   if (resid && a.rule != RULE_LINEAR) {
     // The owner of draft h shares its token, probabilities and verifier.
 #pragma unroll
     for (int k = 0; k < DPT; ++k)
       if (t + k * NT == h) {
-        s.dh = di[k];
-        s.ph = pk[k];
-        s.pth = ptk[k];
-        s.qh = qk[k];
-        s.modeh = mk[k];
-        s.ch = ck[k];
+        s.sc->dh = di[k];
+        s.sc->ph = pk[k];
+        s.sc->pth = ptk[k];
+        s.sc->qh = qk[k];
+        s.sc->modeh = mk[k];
+        s.sc->ch = ck[k];
       }
     __syncthreads();
   }
-  rec.status = s.st;
+  rec.status = s.sc->st;
   rec.h = h;
   rec.resid = resid ? (sparse ? 2 : 1) : 0;
   rec.ep = ref_exp(s.Mp[h], a.kp);
@@ -938,13 +964,13 @@ __device__ __forceinline__ DrawRecord draw_decide(const SampleArgs& a, int b, bo
   rec.wexcl = 0.f;
   rec.fixed = -1;
   if (spot) {
-    if (resid ? s.modeh != 0 : a.gumbel != nullptr) {
+    if (resid ? s.sc->modeh != 0 : a.gumbel != nullptr) {
       // A match link's rejection, or the bonus with Gumbel rows: the commit
       // is the target's coupled-noise token; nothing is drawn.
       rec.fixed = s.g[h];
       rec.resid = 0;
     } else if (resid) {
-      Cf += log2f(s.ch);   // residual [p - c qhat]_+
+      Cf += log2f(s.sc->ch);   // residual [p - c qhat]_+
     }
   }
   if (resid && a.rule == RULE_CACTUS) {
@@ -952,15 +978,15 @@ __device__ __forceinline__ DrawRecord draw_decide(const SampleArgs& a, int b, bo
     // c_rest = 1 - (gamma - p(d)) / (1 - p(d)) is often within an ulp of 1:
     // its logarithm comes from the excess gamma - p(d) (exact in float64)
     // through log1p.
-    const double ph = s.ph;
-    const double c_rest = ph < 1.0 ? (1.0 - static_cast<double>(s.pth)) / (1.0 - ph) : 0.0;
+    const double ph = s.sc->ph;
+    const double c_rest = ph < 1.0 ? (1.0 - static_cast<double>(s.sc->pth)) / (1.0 - ph) : 0.0;
     rec.isp = static_cast<float>(rec.isp * c_rest);
     rec.isp64 *= c_rest;
     // residual [c_rest p - q]_+
-    Cf -= ph < 1.0 ? static_cast<float>(log1p(-(static_cast<double>(s.pth) - ph) / (1.0 - ph)) * 1.4426950408889634)
+    Cf -= ph < 1.0 ? static_cast<float>(log1p(-(static_cast<double>(s.sc->pth) - ph) / (1.0 - ph)) * 1.4426950408889634)
                    : -kInf;
-    rec.excl = s.dh;
-    rec.wexcl = fmaxf(s.pth - s.qh, 0.f);
+    rec.excl = s.sc->dh;
+    rec.wexcl = fmaxf(s.sc->pth - s.sc->qh, 0.f);
   }
   if (resid && !sparse) split_row_constant(Cf, s.Mp[h], s.Mq[h], a.kp, a.kq, rec.chi, rec.clo);
   return rec;
@@ -996,7 +1022,9 @@ __device__ __forceinline__ void draw_rows(const SampleArgs& a, int b, int h, boo
 // p; the select step redoes the tiles that hold stored entries.
 template <int DT, int FAM>
 __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleArgs a) {
-  __shared__ DecideLds s;
+  extern __shared__ __align__(16) char s_dyn[];
+  __shared__ DecideScalars s_sc;
+  DecideLds s = decide_view(s_dyn, a.K, &s_sc);
   const int b = blockIdx.x / a.chunks;
   const int c = blockIdx.x - b * a.chunks;
   const DrawRecord rec = draw_decide<DT, kBlock, FAM>(a, b, c == 0, s);
@@ -1495,7 +1523,9 @@ __global__ __launch_bounds__(kSmallSelect) void k_draw_fused(SampleArgs a) {
   static_assert(kFusedDrawTiles <= SmallSelectLds::kThreads * SmallSelectLds::kTiles, "fused rows fit the LDS");
   constexpr int NT = SmallSelectLds::kThreads;
   constexpr int TPT = SmallSelectLds::kTiles;
-  __shared__ DecideLds sd;
+  extern __shared__ __align__(16) char s_dyn[];
+  __shared__ DecideScalars s_sc;
+  DecideLds sd = decide_view(s_dyn, a.K, &s_sc);
   __shared__ SmallSelectLds s;
   const int b = blockIdx.x;
   const int t = threadIdx.x;
@@ -1567,10 +1597,12 @@ bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const Tim
                                        {fn(k_row_tv<DT_F32, FAM_SPOT>), fn(k_row_tv<DT_BF16, FAM_SPOT>)},
                                        {fn(k_row_tv<DT_F32, FAM_SPARSE>), fn(k_row_tv<DT_BF16, FAM_SPARSE>)}};
   if (a.row_tv && !launch(tv[fam][bf], static_cast<int64_t>(a.B) * a.K, stream, a)) return false;
+  // the decision's row statistics in dynamic LDS, sized for this K
+  const size_t dl = decide_lds_bytes(a.K);
   if (a.tiles <= kFusedDrawTiles && fam != FAM_SPARSE)
-    return launch_threads(fused[fam][bf], a.B, kSmallSelect, stream, a);
+    return launch_threads(fused[fam][bf], a.B, kSmallSelect, stream, a, TimingEvents(), dl);
   const bool small = a.tiles <= kSmallSelect * kSmallSelectTiles;
-  return launch(mass[fam][bf], static_cast<int64_t>(a.B) * a.chunks, stream, a) &&
+  return launch_threads(mass[fam][bf], static_cast<int64_t>(a.B) * a.chunks, kBlock, stream, a, TimingEvents(), dl) &&
          launch_threads(select[small][fam][bf], a.B, small ? kSmallSelect : kDrawThreads, stream, a);
 }
 
