@@ -239,7 +239,7 @@ dbv_status sample_common(int B, int K, int V, dbv_dtype dtype, const void* tgt, 
   a.blk = B > dbv::kSeqBlocks ? reinterpret_cast<int32_t*>(w + plan.off_blk) : nullptr;
   const int64_t P = rl.gumbel ? dbv::gumbel_parts(static_cast<int64_t>(eb)) : 1;
   a.grid = dbv::stream_grid(static_cast<int64_t>(B) * (P * (K + 1) + K), V, static_cast<int64_t>(eb),
-                            group_cap(co));
+                            group_cap(co), dbv::sample_max_grid(V, static_cast<int64_t>(eb), rl.gumbel));
   a.tiles = static_cast<int>(plan.tiles);
   a.tpc = static_cast<int>(plan.tpc);
   a.chunks = static_cast<int>(plan.chunks);

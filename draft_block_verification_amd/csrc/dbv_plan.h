@@ -120,18 +120,32 @@ DBV_HD inline void split_row_slots(const FlatSplit& f, int64_t r, int64_t& first
 }
 
 // Launch grid of a streaming kernel: enough groups for the largest stream
-// the call can need, at most kMaxGrid and the resident groups of the device.
+// the call can need, at most max_grid and the resident groups of the device.
 // (Giving small streams fewer, fuller groups measured no faster.)
-inline int64_t stream_grid(int64_t max_rows, int64_t V, int64_t elem_bytes, int64_t resident) {
+inline int64_t stream_grid(int64_t max_rows, int64_t V, int64_t elem_bytes, int64_t resident,
+                           int64_t max_grid = kMaxGrid) {
   const int64_t units = cdiv(max_rows * V, kUnitBytes / elem_bytes);
-  int64_t g = resident < kMaxGrid ? resident : kMaxGrid;
+  int64_t g = resident < max_grid ? resident : max_grid;
   return units < g ? units : g;
 }
 
 // Bytes of the per-(slot, wave) partials (float2: 8 bytes; the sampling
-// statistics with a float64 sum: 16) for up to max_rows rows.
-inline size_t partial_bytes(int64_t max_rows, size_t bytes_per = 8) {
-  return align256(static_cast<size_t>(max_rows + kMaxGrid) * kWavesPlan * bytes_per);
+// statistics with a float64 sum: 16) for up to max_rows rows and max_grid
+// groups.
+inline size_t partial_bytes(int64_t max_rows, size_t bytes_per = 8, int64_t max_grid = kMaxGrid) {
+  return align256(static_cast<size_t>(max_rows + max_grid) * kWavesPlan * bytes_per);
+}
+
+// Sampling rows of at most kSmallRowBytes are streamed a piece per wave.
+// The fp32 instance of that kernel holds few enough registers for seven
+// groups per CU, so its grid may take up to kMaxGridShort groups (more
+// pieces in flight per CU); partial buffers of sampling calls are sized for
+// it.
+constexpr int64_t kSmallRowBytes = 16384;
+constexpr int64_t kMaxGridShort = 7 * 256;
+DBV_HD inline bool short_rows(int64_t V, int64_t elem_bytes) { return V * elem_bytes <= kSmallRowBytes; }
+inline int64_t sample_max_grid(int64_t V, int64_t elem_bytes, bool gumbel) {
+  return !gumbel && elem_bytes == 4 && short_rows(V, elem_bytes) ? kMaxGridShort : kMaxGrid;
 }
 
 // The correction / bonus draw.  Its row is cut into tiles of 64 16-byte
@@ -292,8 +306,9 @@ inline SamplePlan plan_sample(int B, int K, int V, int64_t elem_bytes) {
   p.tpc = draw_tiles_per_chunk(B, V, elem_bytes);
   p.chunks = cdiv(p.tiles, p.tpc);
   p.off_stats = 0;
-  p.off_gpart = partial_bytes(p.max_vrows, 16);
-  p.off_pre = p.off_gpart + partial_bytes(p.max_vrows);
+  // partials for the short-row grid, whichever path a call takes
+  p.off_gpart = partial_bytes(p.max_vrows, 16, kMaxGridShort);
+  p.off_pre = p.off_gpart + partial_bytes(p.max_vrows, 8, kMaxGridShort);
   p.off_rec = p.off_pre + align256(static_cast<size_t>(B + 1) * 4);
   p.off_tmass = p.off_rec + align256(static_cast<size_t>(B) * sizeof(DrawRecord));
   p.off_sq = p.off_tmass + align256(static_cast<size_t>(B) * p.tiles * 4);

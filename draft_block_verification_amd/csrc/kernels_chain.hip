@@ -274,8 +274,6 @@ __device__ void stats_and_gumbel(const char* xr, const float* gr, int64_t v0, in
   if (a1 + t < v1) one(a1 + t);
 }
 
-// Rows of at most this many bytes are streamed a piece per wave.
-constexpr int64_t kSmallRowBytes = 16384;
 
 // Rows per directory block for calls of more than kSeqBlocks sequences
 // (SeqDir): one wave per block sums its sequences' row counts, 64 at a
@@ -1566,9 +1564,9 @@ bool launch_greedy(const GreedyArgs& a, int dtype, hipStream_t stream, const Tim
 
 bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const TimingEvents& ev) {
   const bool bf = dtype == DT_BF16;
-  const bool short_rows = a.V * (bf ? 2 : 4) <= kSmallRowBytes;
+  const bool short_v = short_rows(a.V, bf ? 2 : 4);
   const void* rows = a.gumbel ? (bf ? fn(k_sample_rows<DT_BF16, true>) : fn(k_sample_rows<DT_F32, true>))
-                     : short_rows ? (bf ? fn(k_sample_rows<DT_BF16, false, true>) : fn(k_sample_rows<DT_F32, false, true>))
+                     : short_v ? (bf ? fn(k_sample_rows<DT_BF16, false, true>) : fn(k_sample_rows<DT_F32, false, true>))
                               : (bf ? fn(k_sample_rows<DT_BF16, false>) : fn(k_sample_rows<DT_F32, false>));
   if (a.blk) {
     const void* blocks = a.gumbel ? (bf ? fn(k_seq_blocks<DT_BF16, true>) : fn(k_seq_blocks<DT_F32, true>))

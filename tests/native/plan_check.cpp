@@ -8,8 +8,9 @@
 //   * the partial slot r + g of every (row, group) piece is unique and below
 //     R + G, and split_row_slots(r) lists exactly the pieces of row r, in
 //     order, as consecutive slots;
-//   * a launch never has more active groups than kMaxGrid, so every slot fits
-//     the workspace sized by partial_bytes(max_rows).
+//   * a launch never has more active groups than kMaxGrid (kMaxGridShort
+//     for short fp32 sampling rows), so every slot fits the workspace sized
+//     by partial_bytes(max_rows, ..., that cap).
 // Plans: the draw tiles of the largest vocabulary fit the LDS tile array and
 // 32-bit offsets; workspace sections are 256-byte aligned and do not overlap.
 #include <cstdio>
@@ -202,6 +203,11 @@ int main() {
   // Launch grids stay within kMaxGrid for any device.
   CHECK(stream_grid(1000000, 151936, 2, 1 << 20) == kMaxGrid, "stream_grid cap");
   CHECK(stream_grid(9, 1024, 4, 2048) == 9, "stream_grid small");
+  CHECK(stream_grid(1000000, 1024, 4, 1 << 20, sample_max_grid(1024, 4, false)) == kMaxGridShort,
+        "short-row grid cap");
+  CHECK(sample_max_grid(1024, 2, false) == kMaxGrid && sample_max_grid(1024, 4, true) == kMaxGrid &&
+            sample_max_grid(8192, 4, false) == kMaxGrid && kMaxGridShort >= kMaxGrid,
+        "short-row grid only for fp32 rows of at most kSmallRowBytes without Gumbel rows");
 
   const int64_t PVs[] = {1, 2, 7, 255, 256, 257, 1000, 1024, 2047, 2048, 2049, 8191, 8192, 8193,
                          32000, 32768, 50257, 65536, 128256, 131072, 151936, 152064, 262144,
@@ -230,8 +236,9 @@ int main() {
           // Gumbel-row streams: P parts per target row, at most 3.
           const int64_t P = gumbel_parts(eb);
           CHECK(P >= 2 && P <= 3 && s.max_vrows >= static_cast<int64_t>(B) * (P * (K + 1) + K), "vrows");
-          CHECK(s.off_gpart >= static_cast<size_t>(s.max_vrows + kMaxGrid) * kWavesPlan * 8, "gpart overlaps stats");
-          CHECK(s.off_pre >= s.off_gpart + static_cast<size_t>(s.max_vrows + kMaxGrid) * kWavesPlan * 8,
+          CHECK(s.off_gpart >= static_cast<size_t>(s.max_vrows + kMaxGridShort) * kWavesPlan * 16,
+                "gpart overlaps stats");
+          CHECK(s.off_pre >= s.off_gpart + static_cast<size_t>(s.max_vrows + kMaxGridShort) * kWavesPlan * 8,
                 "pre overlaps gpart");
           CHECK(s.off_rec >= s.off_pre + static_cast<size_t>(B + 1) * 4, "rec overlaps pre");
           CHECK(s.off_tmass >= s.off_rec + static_cast<size_t>(B) * sizeof(DrawRecord), "tmass overlaps rec");
