@@ -559,9 +559,10 @@ struct QList {
 
 // SP: the residual against a stored sparse Q, weight [p - Q]_+ with p =
 // exp2(x kp + cp) isp and Q from `ql`; no drafter row is read.
+// ws (not with SP): also every element's weight, at ws[element].
 template <int DT, int NW, int TB = kTileBatch, bool SP = false>
 __device__ __forceinline__ void tile_masses(const char* xr, const char* yr, int64_t V, int t_lo, int t_hi, bool vec,
-                            const DrawWeight& w, float* out, const QList* ql = nullptr) {
+                            const DrawWeight& w, float* out, const QList* ql = nullptr, float* ws = nullptr) {
   using E = Elem<DT>;
   constexpr int W = E::kVec;
   const int lane = threadIdx.x & 63;
@@ -603,10 +604,19 @@ __device__ __forceinline__ void tile_masses(const char* xr, const char* yr, int6
           E::unpack(rx[k], x);
           E::unpack(ry[k], y);
 #pragma unroll
-          for (int j = 0; j < W; ++j) m += w.template at<DT>(e + j, x[j], y[j]);
+          for (int j = 0; j < W; ++j) {
+            const float wt = w.template at<DT>(e + j, x[j], y[j]);
+            m += wt;
+            if (ws) ws[e + j] = wt;
+          }
         } else {
-          for (int j = 0; j < W; ++j)
-            if (e + j < Vn) m += w.template at<DT>(e + j, E::load1(xr, e + j), w.resid ? E::load1(yr, e + j) : 0.f);
+          for (int j = 0; j < W; ++j) {
+            if (e + j < Vn) {
+              const float wt = w.template at<DT>(e + j, E::load1(xr, e + j), w.resid ? E::load1(yr, e + j) : 0.f);
+              m += wt;
+              if (ws) ws[e + j] = wt;
+            }
+          }
         }
 #pragma unroll
         for (int sh = 32; sh >= 1; sh >>= 1) m += wave_shfl_xor(m, sh);
@@ -681,6 +691,14 @@ struct DecideLds {
 __host__ __device__ constexpr size_t decide_lds_bytes(int K) {
   return static_cast<size_t>(K + 1) * 8 + static_cast<size_t>(K) * 8 + static_cast<size_t>(K + 1) * 4 +
          static_cast<size_t>(K) * 4 + static_cast<size_t>(K + 1) * 4;
+}
+
+// The fused draw also keeps every weight of row h in dynamic LDS, after the
+// decision's arrays, where both fit in 32 KB: the select step's rescan then
+// reads the chosen tile's weights instead of loading and weighing it again.
+__host__ __device__ constexpr size_t fused_weights_offset(int K) { return (decide_lds_bytes(K) + 15) / 16 * 16; }
+__host__ __device__ constexpr bool fused_weights_fit(int K, int64_t V) {
+  return fused_weights_offset(K) + static_cast<size_t>(V) * 4 <= 32768;
 }
 
 __device__ __forceinline__ DecideLds decide_view(char* dyn, int K, DecideScalars* sc) {
@@ -1266,7 +1284,7 @@ struct SparseLds {
 template <int DT, bool SPARSE, class LDS>
 __device__ __forceinline__ void draw_select(const SampleArgs& a, int b, const DrawRecord& rec, int budget,
                             const int (&dt)[(kMaxDraft + LDS::kThreads - 1) / LDS::kThreads],
-                            const float (&m0)[LDS::kTiles], LDS& s, SparseLds* sp) {
+                            const float (&m0)[LDS::kTiles], LDS& s, SparseLds* sp, const float* wl = nullptr) {
   constexpr int NT = LDS::kThreads;
   constexpr int TPT = LDS::kTiles;
   constexpr int DPT = (kMaxDraft + NT - 1) / NT;
@@ -1348,6 +1366,7 @@ __device__ __forceinline__ void draw_select(const SampleArgs& a, int b, const Dr
     w.resid = 0;
     w.excl = -1;
     yr = xr;
+    wl = nullptr;   // the stored weights were the residual's
     const bool vec = (reinterpret_cast<uintptr_t>(xr) & 15u) == 0;
     tile_masses<DT, NT / 64, 2>(xr, yr, a.V, 0, ntiles, vec, w, s.tile);
     __syncthreads();
@@ -1379,6 +1398,10 @@ __device__ __forceinline__ void draw_select(const SampleArgs& a, int b, const Dr
 #pragma unroll
       for (int j = 0; j < E::kVec; ++j)
         wt[j] = e0 + j < a.V ? w.sparse(E::load1(xr, e0 + j), q[j]) : 0.f;
+    } else if (wl) {
+      // the weights the mass step stored in LDS (the same values)
+#pragma unroll
+      for (int j = 0; j < E::kVec; ++j) wt[j] = e0 + j < a.V ? wl[e0 + j] : 0.f;
     } else if (e0 + E::kVec <= a.V &&
                ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0) {
       // the lane's vector of the row (and of the drafter row) in one load each
@@ -1536,7 +1559,9 @@ __global__ __launch_bounds__(kSmallSelect) void k_draw_fused(SampleArgs a) {
   draw_rows<DT>(a, b, rec.h, rec.resid != 0, xr, yr);
   const bool vec = ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(yr)) & 15u) == 0;
   const int ntiles = a.tiles;
-  if (rec.fixed < 0) tile_masses<DT, NT / 64, 4>(xr, yr, a.V, 0, ntiles, vec, draw_weight(a, rec), s.tile);
+  float* wl = fused_weights_fit(a.K, a.V) ? reinterpret_cast<float*>(s_dyn + fused_weights_offset(a.K)) : nullptr;
+  if (rec.fixed < 0)
+    tile_masses<DT, NT / 64, 4>(xr, yr, a.V, 0, ntiles, vec, draw_weight(a, rec), s.tile, nullptr, wl);
   __syncthreads();
   const int q = static_cast<int>(cdiv(ntiles, NT));
   float m0[TPT];
@@ -1546,7 +1571,7 @@ __global__ __launch_bounds__(kSmallSelect) void k_draw_fused(SampleArgs a) {
     m0[k] = (k < q && tile < ntiles) ? s.tile[tile] : 0.f;
   }
   __syncthreads();   // the fallback in draw_select may overwrite s.tile
-  draw_select<DT, false>(a, b, rec, budget, dt, m0, s, nullptr);
+  draw_select<DT, false>(a, b, rec, budget, dt, m0, s, nullptr, wl);
 }
 
 // ============================================================== launches ===
@@ -1598,7 +1623,8 @@ bool launch_sample(const SampleArgs& a, int dtype, hipStream_t stream, const Tim
   // the decision's row statistics in dynamic LDS, sized for this K
   const size_t dl = decide_lds_bytes(a.K);
   if (a.tiles <= kFusedDrawTiles && fam != FAM_SPARSE)
-    return launch_threads(fused[fam][bf], a.B, kSmallSelect, stream, a, TimingEvents(), dl);
+    return launch_threads(fused[fam][bf], a.B, kSmallSelect, stream, a, TimingEvents(),
+                          fused_weights_fit(a.K, a.V) ? fused_weights_offset(a.K) + static_cast<size_t>(a.V) * 4 : dl);
   const bool small = a.tiles <= kSmallSelect * kSmallSelectTiles;
   return launch_threads(mass[fam][bf], static_cast<int64_t>(a.B) * a.chunks, kBlock, stream, a, TimingEvents(), dl) &&
          launch_threads(select[small][fam][bf], a.B, small ? kSmallSelect : kDrawThreads, stream, a);
