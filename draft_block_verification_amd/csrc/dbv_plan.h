@@ -121,10 +121,15 @@ DBV_HD inline void split_row_slots(const FlatSplit& f, int64_t r, int64_t& first
 
 // Launch grid of a streaming kernel: enough groups for the largest stream
 // the call can need, at most max_grid and the resident groups of the device.
-// (Giving small streams fewer, fuller groups measured no faster.)
+// Streams of at most 1 MiB take four units per group: each CU a group runs
+// on fetches the kernel's code (about 25 KB), which on the tiny rejection
+// call (36 KB of rows) was over six times the rows' bytes with a group per
+// unit, and three groups take the same time as nine.  (Giving larger
+// streams fewer, fuller groups measured no faster.)
 inline int64_t stream_grid(int64_t max_rows, int64_t V, int64_t elem_bytes, int64_t resident,
                            int64_t max_grid = kMaxGrid) {
-  const int64_t units = cdiv(max_rows * V, kUnitBytes / elem_bytes);
+  const int64_t bytes = max_rows * V * elem_bytes;
+  const int64_t units = cdiv(max_rows * V, (bytes <= (int64_t(1) << 20) ? 4 * kUnitBytes : kUnitBytes) / elem_bytes);
   int64_t g = resident < max_grid ? resident : max_grid;
   return units < g ? units : g;
 }

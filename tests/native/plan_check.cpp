@@ -202,7 +202,8 @@ int main() {
 
   // Launch grids stay within kMaxGrid for any device.
   CHECK(stream_grid(1000000, 151936, 2, 1 << 20) == kMaxGrid, "stream_grid cap");
-  CHECK(stream_grid(9, 1024, 4, 2048) == 9, "stream_grid small");
+  CHECK(stream_grid(9, 1024, 4, 2048) == 3, "stream_grid small: four units a group up to 1 MiB");
+  CHECK(stream_grid(300, 1024, 4, 2048) == 300, "stream_grid: one unit a group past 1 MiB");
   CHECK(stream_grid(1000000, 1024, 4, 1 << 20, sample_max_grid(1024, 4, false)) == kMaxGridShort,
         "short-row grid cap");
   CHECK(sample_max_grid(1024, 2, false) == kMaxGrid && sample_max_grid(1024, 4, true) == kMaxGrid &&
