@@ -5,9 +5,10 @@
 //
 //   k_truncate  one group of kTB threads per row (b, i), i < n_b:
 //     1. one streaming pass: each thread keeps its three largest logits (a
-//        median-of-three cascade per element), the contiguous group and the
-//        occurrence in it of each, and the largest logit it dropped; the
-//        row's NaN / +inf check comes from the thread maxima;
+//        median-of-three cascade per element), the start of the contiguous
+//        group of each (its occurrence among the equal logits of that group
+//        follows from the entries above it), and the largest logit it
+//        dropped; the row's NaN / +inf check comes from the thread maxima;
 //     2. tau = the smallest, over the waves, of each wave's ceil(k/16)-th
 //        largest thread maximum: at least k logits are >= tau;
 //     3. the kept entries >= tau are the candidates, each with its place
@@ -58,7 +59,7 @@ struct TruncLds {
   int bad, digit, above, n, keep, nc, chunk;
   uint32_t tau_key, drop_key;
   uint32_t wtau[kTW];
-  __align__(16) uint2 rk[kRankCand + 2];   // ranked candidates: key, place
+  __align__(16) uint64_t rk[kRankCand + 2];   // ranked candidates: key, ~place
   float cx[kTruncCand];            // candidates: logit and token id
   int cid[kTruncCand];
   uint32_t ckey[kMaxNnz];          // the kept k
@@ -71,13 +72,15 @@ struct TruncLds {
 };
 
 // The three largest logits of a thread in order (equal logits: the earlier
-// first), each with the start index of its contiguous group and its
-// occurrence among the equal logits of that group, and the largest logit
-// that fell out.  The maximum propagates NaN (the row check).
+// first), each with the start index of its contiguous group, and the
+// largest logit that fell out.  The maximum propagates NaN (the row check);
+// a row with NaN never reads the others.  The occurrence of an entry among
+// the equal logits of its group is not tracked while streaming: the earlier
+// equal logits of that group rank above it, so they are the entries before
+// it with the same logit and group (occurrence1, occurrence2).
 struct Top3Op {
   float v0 = -kInf, v1 = -kInf, v2 = -kInf;
   int g0 = -1, g1 = -1, g2 = -1;
-  int c0 = 0, c1 = 0, c2 = 0;
   float drop = -kInf;
 
   template <int N>
@@ -86,47 +89,43 @@ struct Top3Op {
     // fields (a select between fields would become a select of addresses
     // and keep the tracker out of registers).
     const float o0 = v0, o1 = v1, o2 = v2;
-    const int h0 = g0, h1 = g1, h2 = g2, e0 = c0, e1 = c1, e2 = c2;
-    float n0 = o0, n1 = o1, n2 = o2, dr = drop;
+    const int h0 = g0, h1 = g1, h2 = g2;
+    // A fourth slot under the three: the largest logit that fell out is
+    // the thread's fourth largest.
+    float n0 = o0, n1 = o1, n2 = o2, n3 = drop;
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      dr = fmaxf(dr, fminf(x[j], n2));
+      n3 = __builtin_amdgcn_fmed3f(x[j], n2, n3);
       n2 = __builtin_amdgcn_fmed3f(x[j], n1, n2);
       n1 = __builtin_amdgcn_fmed3f(x[j], n0, n1);
       n0 = fmaxp(n0, x[j]);
     }
-    drop = dr;
+    drop = n3;
     // The new list is the stable merge of the old list with the group's
     // logits (old entries first on equal logits): walk it, matching old
-    // entries in order; the rest come from this group, with their
-    // occurrence among equal logits of the group.
+    // entries in order; the rest come from this group.
     const int gi = static_cast<int>(idx0);
-    // slot 0: old entry 0 or new
-    const bool m0 = n0 == o0;
-    const int q0g = m0 ? h0 : gi, q0c = m0 ? e0 : 0;
-    // slot 1: the next old entry is 1 if slot 0 took old 0, else 0
-    const float p1 = m0 ? o1 : o0;
+    const bool m0 = n0 == o0;                    // slot 0: old entry 0?
+    const float p1 = m0 ? o1 : o0;               // next old entry
     const bool m1 = n1 == p1;
-    const int q1g = m1 ? (m0 ? h1 : h0) : gi;
-    const int q1c = m1 ? (m0 ? e1 : e0) : ((!m0 && n1 == n0) ? 1 : 0);
-    // slot 2: next old entry index = m0 + m1
-    const int io = (m0 ? 1 : 0) + (m1 ? 1 : 0);
+    const int io = (m0 ? 1 : 0) + (m1 ? 1 : 0);  // old entries used so far
     const float p2 = io == 2 ? o2 : io == 1 ? o1 : o0;
     const bool m2 = n2 == p2;
-    const int q2g = m2 ? (io == 2 ? h2 : io == 1 ? h1 : h0) : gi;
-    // a new logit's occurrence: one more than the last new logit's if equal
-    const int lastc = !m1 ? q1c : (!m0 ? q0c : -1);
-    const float lastv = !m1 ? n1 : n0;
-    const bool lastnew = !m1 || !m0;
-    const int q2c = m2 ? (io == 2 ? e2 : io == 1 ? e1 : e0) : ((lastnew && lastv == n2) ? lastc + 1 : 0);
     v0 = n0; v1 = n1; v2 = n2;
-    g0 = q0g; g1 = q1g; g2 = q2g;
-    c0 = q0c; c1 = q1c; c2 = q2c;
+    g0 = m0 ? h0 : gi;
+    g1 = m1 ? (m0 ? h1 : h0) : gi;
+    g2 = m2 ? (io == 2 ? h2 : io == 1 ? h1 : h0) : gi;
   }
   template <int U, int W>
   __device__ __forceinline__ void block(const float* x, int64_t idx0, int64_t ustride) {
 #pragma unroll
     for (int u = 0; u < U; ++u) group<W>(x + u * W, idx0 + u * ustride);
+  }
+  // Occurrences of entries 1 and 2 among the equal logits of their groups
+  // (entry 0's is 0).
+  __device__ __forceinline__ int occurrence1() const { return (v1 == v0 && g1 == g0) ? 1 : 0; }
+  __device__ __forceinline__ int occurrence2() const {
+    return (v2 == v1 && g2 == g1) ? occurrence1() + 1 : 0;
   }
 };
 
@@ -303,24 +302,33 @@ static_assert(kMaxNnz <= kTB, "one kept entry per thread");
 
 // The token id of a kept logit x at occurrence c of group g: the c-th
 // element equal to x in [g, g + W) (a group holds at most W elements; a
-// one-element group's logit is its first element).
+// one-element group's logit is its first element).  load_group issues the
+// loads of the group's elements, scan_group finds the id in them, so other
+// work can run while the loads are in flight.
 template <int DT>
-__device__ __forceinline__ int find_in_group(const char* row, int64_t V, int g, int c, float x) {
-  constexpr int W = Elem<DT>::kVec;
-  float y[W];
+__device__ __forceinline__ void load_group(const char* row, int64_t V, int g, float (&y)[Elem<DT>::kVec]) {
 #pragma unroll
-  for (int j = 0; j < W; ++j) {       // every load issued before the scan
+  for (int j = 0; j < Elem<DT>::kVec; ++j) {
     const int64_t id = static_cast<int64_t>(g) + j;
     y[j] = Elem<DT>::load1(row, id < V ? id : V - 1);
   }
+}
+template <int DT>
+__device__ __forceinline__ int scan_group(int64_t V, int g, int c, float x, const float (&y)[Elem<DT>::kVec]) {
   int seen = 0, hit = -1;
 #pragma unroll
-  for (int j = 0; j < W; ++j) {
+  for (int j = 0; j < Elem<DT>::kVec; ++j) {
     const bool eq = static_cast<int64_t>(g) + j < V && y[j] == x;
     if (eq && seen == c && hit < 0) hit = g + j;
     seen += eq ? 1 : 0;
   }
   return hit;
+}
+template <int DT>
+__device__ __forceinline__ int find_in_group(const char* row, int64_t V, int g, int c, float x) {
+  float y[Elem<DT>::kVec];
+  load_group<DT>(row, V, g, y);
+  return scan_group<DT>(V, g, c, x, y);
 }
 
 // Wave-wide unsigned maximum by DPP lane moves (identity 0); every lane of
@@ -485,9 +493,9 @@ __global__ __launch_bounds__(kTB, 8) void k_truncate(TruncArgs a) {
         s.cid[slot] = g * 8 + c;
       }
     };
-    cand(op.v0, op.g0, op.c0);
-    cand(op.v1, op.g1, op.c1);
-    cand(op.v2, op.g2, op.c2);
+    cand(op.v0, op.g0, 0);
+    cand(op.v1, op.g1, op.occurrence1());
+    cand(op.v2, op.g2, op.occurrence2());
   }
   __syncthreads();
   int nc = s.nc;
@@ -504,30 +512,38 @@ __global__ __launch_bounds__(kTB, 8) void k_truncate(TruncArgs a) {
   };
   uint32_t kth = 0, id_cut = 0;
   bool exact = nc >= k;
-  // kept entries in s.ckey / s.cidx / s.kx hold places, not token ids, on
-  // the candidate paths; `ranked`: already in rank order
+  // kept entries in s.ckey / s.cidx / s.kx hold places, not token ids,
+  // after the radix select over the candidates (the rank path stores token
+  // ids); `ranked`: already in rank order
   bool ranked = false;
   if (exact && nc <= kRankCand) {
-    // (key, place) pairs, two per 16-byte read; the pad pair (key 0, place
-    // INT_MAX) ranks below every candidate
-    if (t <= nc) s.rk[t] = t < nc ? make_uint2(order_key<DT>(s.cx[t]), static_cast<uint32_t>(s.cid[t]))
-                                  : make_uint2(0u, 0x7FFFFFFFu);
+    // One 64-bit number per candidate, key above the complemented place:
+    // a larger number ranks first (larger logit, then lower place).  Two
+    // per 16-byte read; the pad 0 after the last ranks below every one.
+    if (t <= nc) s.rk[t] = t < nc ? (static_cast<uint64_t>(order_key<DT>(s.cx[t])) << 32) |
+                                        static_cast<uint32_t>(~s.cid[t])
+                                  : uint64_t(0);
     __syncthreads();
     if (t < nc) {
-      const uint32_t kc = s.rk[t].x;
+      const uint64_t mine = s.rk[t];
+      const uint32_t kc = static_cast<uint32_t>(mine >> 32);
       const int pc = s.cid[t];
+      // every candidate's group is loaded while the ranks are counted; the
+      // kept ones then store token ids, not places
+      float y[Elem<DT>::kVec];
+      load_group<DT>(row, V, pc >> 3, y);
       int rank = 0;
 #pragma unroll 8
       for (int d = 0; d < nc; d += 2) {
-        const uint4 q = *reinterpret_cast<const uint4*>(&s.rk[d]);
-        // | and & rather than || and &&: no branch, the loads stay in one run
-        rank += static_cast<int>((q.x > kc) | ((q.x == kc) & (static_cast<int>(q.y) < pc)));
-        rank += static_cast<int>((q.z > kc) | ((q.z == kc) & (static_cast<int>(q.w) < pc)));
+        const ulonglong2 q = *reinterpret_cast<const ulonglong2*>(&s.rk[d]);
+        rank += q.x > mine ? 1 : 0;
+        rank += q.y > mine ? 1 : 0;
       }
       if (rank < k) {
+        const float x = s.cx[t];
         s.ckey[rank] = kc;
-        s.cidx[rank] = pc;
-        s.kx[rank] = s.cx[t];
+        s.cidx[rank] = scan_group<DT>(V, pc >> 3, pc & 7, x, y);
+        s.kx[rank] = x;
       }
     }
     __syncthreads();
@@ -542,14 +558,15 @@ __global__ __launch_bounds__(kTB, 8) void k_truncate(TruncArgs a) {
   }
   __syncthreads();
   if (exact) {
-    if (!ranked)
+    if (!ranked) {
       for (int c = t; c < nc; c += kTB) keep_token(s, order_key<DT>(s.cx[c]), s.cx[c], s.cid[c], kth, id_cut);
-    __syncthreads();
-    // the kept places to token ids
-    const int mk = s.n < kMaxNnz ? s.n : kMaxNnz;
-    if (t < mk) {
-      const int pc = s.cidx[t];
-      s.cidx[t] = find_in_group<DT>(row, V, pc >> 3, pc & 7, s.kx[t]);
+      __syncthreads();
+      // the kept places to token ids
+      const int mk = s.n < kMaxNnz ? s.n : kMaxNnz;
+      if (t < mk) {
+        const int pc = s.cidx[t];
+        s.cidx[t] = find_in_group<DT>(row, V, pc >> 3, pc & 7, s.kx[t]);
+      }
     }
   } else {
     ranked = false;
