@@ -77,6 +77,33 @@ __device__ __forceinline__ u32x4 load16(const char* p) {
 }
 
 // ---------------------------------------------------------------------------
+// Wave priority steered by progress through a group's share of a flat
+// stream.  The SIMD arbiter issues the oldest ready wave first, so among the
+// groups that share a CU the first dispatched streams fastest and the last
+// runs alone at the end, with too few loads in flight to keep the CU's share
+// of HBM busy.  A wave raises its issue priority (s_setprio) while it is
+// behind: level 3 before half of its share, 2 before 80%, 1 before 95%, 0
+// for the rest, so the groups of a CU finish close together.  (Measured with
+// kernel-internal timestamps: the groups of a CU are dispatched in blockIdx
+// quarters, and without steering the last of them ended up to 40% later
+// than the first on large sampling calls.)
+// ---------------------------------------------------------------------------
+struct Progress {
+  int64_t off = 0;   // flat position of the current row's element 0, minus the group's start
+  int64_t th1 = 0, th2 = 0, th3 = 0;   // 50%, 80% and 95% of the group's share
+  bool on = false;
+};
+
+// done: elements of the group's share before the current step (wave-uniform).
+__device__ __forceinline__ void steer_priority(const Progress& pg, int64_t done) {
+  if (!pg.on) return;
+  if (done < pg.th1) __builtin_amdgcn_s_setprio(3);
+  else if (done < pg.th2) __builtin_amdgcn_s_setprio(2);
+  else if (done < pg.th3) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+// ---------------------------------------------------------------------------
 // Row streaming by NT threads (default: one 256-thread group; NT = 64: the
 // calling wave alone).  Visits
 // elements [v0, v1) of `row`; every thread sees its own elements in
@@ -86,7 +113,8 @@ __device__ __forceinline__ u32x4 load16(const char* p) {
 // the body, and the scalar tail.
 // ---------------------------------------------------------------------------
 template <int DT, int U, class Op, int NT = kBlock>
-__device__ __forceinline__ void stream_row(const void* row, int64_t v0, int64_t v1, Op& op) {
+__device__ __forceinline__ void stream_row(const void* row, int64_t v0, int64_t v1, Op& op,
+                                           const Progress& pg = Progress{}) {
   using E = Elem<DT>;
   constexpr int W = E::kVec;
   if (v1 <= v0) return;
@@ -105,7 +133,9 @@ __device__ __forceinline__ void stream_row(const void* row, int64_t v0, int64_t 
   }
   const char* vb = base + a0 * E::kBytes;
   int64_t i = t;
-  for (; i + (U - 1) * NT < nvec; i += U * NT) {
+  // ib: i - t, the same in every lane
+  for (int64_t ib = 0; i + (U - 1) * NT < nvec; i += U * NT, ib += U * NT) {
+    steer_priority(pg, pg.off + a0 + ib * W);
     u32x4 r[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) r[u] = load16(vb + (i + u * NT) * 16);
@@ -489,19 +519,30 @@ __device__ __forceinline__ void wave_argmax(float& v, int& idx, int& nan) {
 // Flat split helpers (the split itself is defined in dbv_plan.h).
 // ---------------------------------------------------------------------------
 
-// Visits the pieces of active group g in stream order: fn(r, v0, v1) for each
-// stream row r that meets the group's range, [v0, v1) being the part of the
-// row inside it.
+// Visits the pieces of active group g in stream order: fn(r, v0, v1, pg) for
+// each stream row r that meets the group's range, [v0, v1) being the part of
+// the row inside it, and pg the progress of element 0 of row r through the
+// group's range (for stream_row's priority steering; the priority is back
+// at 0 on return).
 template <class Fn>
 __device__ __forceinline__ void for_pieces(const FlatSplit& f, int64_t g, Fn fn) {
   int64_t e0, e1;
   split_range(f, g, e0, e1);
+  Progress pg;
+  const int64_t len = e1 - e0;
+  // shares of a few units end before the waves drift apart
+  pg.on = len >= 16 * f.Q;
+  pg.th1 = len / 2;
+  pg.th2 = len - len / 5;
+  pg.th3 = len - len / 20;
   int64_t r = udiv(e0, f.V);
   for (int64_t base = r * f.V; base < e1; ++r, base += f.V) {
     const int64_t v0 = e0 > base ? e0 - base : 0;
     const int64_t v1 = e1 < base + f.V ? e1 - base : f.V;
-    fn(r, v0, v1);
+    pg.off = base - e0;
+    fn(r, v0, v1, pg);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Exclusive scan of one int per thread over a group of NW waves, in thread

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kBlock) void k_ao_rows(AnyOrderArgs a) {
   const int64_t g = blockIdx.x;
   if (g >= f.G) return;
   SeqCursor cur;
-  for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1) {
+  for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1, const Progress& pg) {
     const int b = find_seq(dir, s_pre, static_cast<int>(r), count, cur);
     const int first = cur.first;
     const int j = static_cast<int>(r) - first;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kBlock) void k_ao_rows(AnyOrderArgs a) {
                : static_cast<const char*>(a.dr) +
                      (static_cast<int64_t>(b) * a.ds + static_cast<int64_t>(j - nv) * a.drr) * Elem<DT>::kBytes;
     ArgmaxPick pk;
-    stream_row<DT, 4>(rowp, v0, v1, pk);
+    stream_row<DT, 4>(rowp, v0, v1, pk, pg);
     float v = pk.best;
     int ii = static_cast<int>(pk.bidx);
     int nan = pk.nan ? 1 : 0;

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kBlock) void k_greedy_rows(GreedyArgs a) {
   const int64_t g = blockIdx.x;
   if (g >= f.G) return;
   SeqCursor cur;
-  for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1) {
+  for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1, const Progress& pg) {
     const int b = find_seq(dir, s_pre, static_cast<int>(r), count, cur);
     const int first = cur.first, cnt = cur.cnt;
     const int j = static_cast<int>(r) - first;
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kBlock) void k_greedy_rows(GreedyArgs a) {
                : static_cast<const char*>(a.dr) +
                      (static_cast<int64_t>(b) * a.ds + static_cast<int64_t>(j - nt) * a.drr) * Elem<DT>::kBytes;
     ArgmaxPick pk;
-    stream_row<DT, kUnroll>(rowp, v0, v1, pk);
+    stream_row<DT, kUnroll>(rowp, v0, v1, pk, pg);
     float v = pk.best;
     int ii = static_cast<int>(pk.bidx);
     int nan = pk.nan ? 1 : 0;
@@ -207,7 +207,7 @@ struct Quad<DT_F32> {
 // cannot both be aligned are read element by element.
 template <int DT, int U, class Stats>
 __device__ void stats_and_gumbel(const char* xr, const float* gr, int64_t v0, int64_t v1, float inv_t,
-                                 Stats& st, ArgmaxPick& pk) {
+                                 Stats& st, ArgmaxPick& pk, const Progress& pg, int64_t done0, int quad_units) {
   using E = Elem<DT>;
   using Q = Quad<DT>;
   constexpr int XB = 4 * E::kBytes;
@@ -249,7 +249,10 @@ __device__ void stats_and_gumbel(const char* xr, const float* gr, int64_t v0, in
   const char* xb = xr + a0 * E::kBytes;
   const char* gb = reinterpret_cast<const char*>(gr + a0);
   int64_t i = t;
-  for (; i + (U - 1) * kBlock < nq; i += U * kBlock) {
+  // ib: i - t, the same in every lane; a step of quads moves the stream
+  // position by quad_units each
+  for (int64_t ib = 0; i + (U - 1) * kBlock < nq; i += U * kBlock, ib += U * kBlock) {
+    steer_priority(pg, done0 + ib * quad_units);
     typename Q::raw xv[U];
     u32x4 g[U];
 #pragma unroll
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
   static_assert(!(GUM && SMALL), "Gumbel rows take the group path");
   int piece = 0;
   SeqCursor cur;
-  for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1) {
+  for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1, const Progress& pg) {
     if (SMALL && (piece++ % kWaves) != wave_id()) return;
     const int b = SMALL ? find_seq_wave(dir, s_pre, static_cast<int>(r), a.B, count, cur)
                         : find_seq(dir, s_pre, static_cast<int>(r), count, cur);
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
       }
       stats_and_gumbel<DT, 2 * kUnroll>(rowp, a.gumbel + b * a.gs + static_cast<int64_t>(jt) * a.grs,
                                     part_offset(a.V, P, part, v0), part_offset(a.V, P, part, v1), a.inv_t, acc,
-                                    accp);
+                                    accp, pg, pg.off + v0, 4 * P);
       return;
     }
     if (GUM && pend >= 0) flush();
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_rows(SampleArgs a) {
       if (lane < kWaves) put((r + g) * kWaves + lane, lane == wave_id() ? M : -kInf, lane == wave_id() ? R : 0.0);
       return;
     }
-    stream_row<DT, kUnroll>(rowp, v0, v1, st);
+    stream_row<DT, kUnroll>(rowp, v0, v1, st, pg);
     float M = st.M;
     double R = static_cast<double>(st.R);
     wave_stats64(M, R, k);

@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kBlock) void k_dd_rows(DDHypArgs a) {
   const int R = a.fused_plan ? row_dir(a, d, g == 0) : *a.count;
   const FlatSplit f = make_split(R, a.V, a.split_bytes, a.grid);
   if (g >= f.G) return;
-  for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1) {
+  for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1, const Progress& pg) {
     const int flat = a.fused_plan ? row_flat(a, d, static_cast<int>(r)) : a.list[r];
     const int b = flat / a.L;
     const int s = flat - b * a.L;
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(kBlock) void k_dd_rows(DDHypArgs a) {
       out = DDPart{q.M, q.S, q.v, q.g, -kInf, -1, 0.f, q.nan};
     } else {
       Top2Stats op;
-      stream_row<DT, 4>(rowp, v0, v1, op);
+      stream_row<DT, 4>(rowp, v0, v1, op, pg);
       const Top2Part q = wave_merge_dpp(Top2Part{op.st.M, op.st.S, op.v1, op.v2, op.g1, op.g2});
       out = DDPart{q.M, q.S, q.v1, q.g1, q.v2, q.g2, 0.f, 0};
     }

@@ -233,13 +233,13 @@ __global__ __launch_bounds__(kBlock) void k_tree_conf(TreeArgs a) {
   const FlatSplit f = make_split(*a.count, a.V, Elem<DT>::kBytes, a.grid);
   const int64_t g = blockIdx.x;
   if (g >= f.G) return;
-  for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1) {
+  for_pieces(f, g, [&](int64_t r, int64_t v0, int64_t v1, const Progress& pg) {
     int b, y, s;
     split_flat(a, static_cast<uint32_t>(a.list[r]), b, y, s);
     const char* rowp = static_cast<const char*>(a.logits) +
                        (b * a.ss + y * a.sy + s * a.sp) * Elem<DT>::kBytes;
     SoftmaxStats st(kLog2e);
-    stream_row<DT, 4>(rowp, v0, v1, st);
+    stream_row<DT, 4>(rowp, v0, v1, st, pg);
     float M = st.M, S = st.S;
     wave_stats(M, S, kLog2e);
     if ((threadIdx.x & 63) == 0) a.conf[(r + g) * kWaves + (threadIdx.x >> 6)] = make_float2(M, S);
