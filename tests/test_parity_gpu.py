@@ -386,6 +386,33 @@ def test_truncate_ties_and_bad_rows(dev):
             assert npi(g["q_nnz"])[0, 1] == -1 and npi(g["q_nnz"])[1, 0] == -1 and npi(g["q_nnz"])[2, 2] == -1
 
 
+def test_truncate_equal_logits_in_groups(dev):
+    # The kernel keeps, per thread, its top logits with the start of the
+    # 16-byte group each came from, and counts an entry's occurrence among
+    # equal logits of its group after the stream (the entries above it with
+    # the same logit and group).  Rows built from a few values repeated inside
+    # every group, with the row start both aligned and off by one to six
+    # elements (one-element head and tail groups), and k up to 256: token ids
+    # must be the oracle's (lowest id first among equal logits).
+    say("truncate equal logits inside groups")
+    g0 = torch.Generator().manual_seed(95)
+    pattern = torch.tensor([5.0, 5.0, 5.0, 3.0, 5.0, 5.0, 1.0, 5.0])
+    for dtype in (torch.float32, torch.bfloat16):
+        for V in (4099, 20000):
+            base = pattern.repeat(V // 8 + 1)[:V]
+            rows = torch.stack([base, base.roll(3), torch.where(torch.rand(V, generator=g0) < 0.05, 7.0, 2.0),
+                                torch.randint(0, 2, (V,), generator=g0).float() * 4.0])
+            for off in (0, 1, 6):
+                # a column offset moves the row start off the 16-byte boundary
+                big = torch.full((2, 2, V + off), -1.0e4, dtype=dtype)
+                big[:, :, off:] = rows.reshape(2, 2, V).to(dtype)
+                x = big[:, :, off:]
+                xd = big.to(dev)[:, :, off:]      # sliced on the device: rows start off alignment
+                for k, p in ((3, 1.0), (20, 0.9), (256, 0.99)):
+                    g = dbv.truncate_top_k_top_p(xd, k, p, kmax=256, temperature=1.0)
+                    _trunc_check(g, np64(x), 1.0, k, p, 256, None, str(dtype).split(".")[-1])
+
+
 def test_truncate_flat_rows(dev):
     # More logits at or above the threshold than the LDS candidates hold:
     # a flat row, a row with a few distinct values, and a row with fewer
