@@ -719,6 +719,14 @@ struct SeqCursor {
   int b = -1;
   int first = 0;
   int cnt = 0;
+  // find_seq_wave's window of 64 sequences from wb0 (wb0 < 0: none): the
+  // rows before it, its total rows, and per lane the count and inclusive
+  // prefix of sequence wb0 + lane
+  int wb0 = -1;
+  int wacc = 0;
+  int wtot = 0;
+  int wcl = 0;
+  int wps = 0;
 };
 
 // find_seq continued from the cursor when row r lies at or past the
@@ -740,30 +748,39 @@ __device__ __forceinline__ int find_seq(const SeqDir& d, const int* pre, int r, 
 }
 
 // find_seq for one wave (every lane with the same r), continuing from the
-// wave's cursor: the counts of the next 64 sequences are read at once and
-// the sequence holding r found by a prefix sum over the lanes, so a lookup
-// costs one round of loads per 64 sequences passed instead of one per
-// sequence.  B bounds the sequences counted.
+// wave's cursor: the counts of 64 sequences are read at once and kept, one
+// per lane, with their prefix sum, and the sequence holding r is found by a
+// ballot over that window, so a wave visiting increasing rows reads one
+// round of counts per 64 sequences it passes.  B bounds the sequences
+// counted.
 template <class CountFn>
 __device__ __forceinline__ int find_seq_wave(const SeqDir& d, const int* pre, int r, int B, CountFn count,
                                              SeqCursor& c) {
   if (c.b >= 0 && r >= c.first && r < c.first + c.cnt) return c.b;
-  int b0, acc;
-  if (c.b >= 0 && r >= c.first) {
-    b0 = c.b + 1;
-    acc = c.first + c.cnt;
-  } else {
-    int lo = 0, hi = d.nblk - 1;
-    while (lo < hi) {  // largest block j with pre[j] <= r
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= r) lo = mid;
-      else hi = mid - 1;
-    }
-    b0 = lo * d.q;
-    acc = pre[lo];
-  }
-  const int lane = static_cast<int>(threadIdx.x) & 63;
   for (;;) {
+    if (c.wb0 >= 0 && r >= c.wacc && r < c.wacc + c.wtot) {
+      const uint64_t hit = __ballot(c.wacc + c.wps > r);
+      const int L = __builtin_ctzll(hit);
+      c.b = c.wb0 + L;
+      c.cnt = __shfl(c.wcl, L, 64);
+      c.first = c.wacc + __shfl(c.wps, L, 64) - c.cnt;
+      return c.b;
+    }
+    int b0, acc;
+    if (c.wb0 >= 0 && r >= c.wacc) {   // past the window: the next 64
+      b0 = c.wb0 + 64;
+      acc = c.wacc + c.wtot;
+    } else {
+      int lo = 0, hi = d.nblk - 1;
+      while (lo < hi) {  // largest block j with pre[j] <= r
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= r) lo = mid;
+        else hi = mid - 1;
+      }
+      b0 = lo * d.q;
+      acc = pre[lo];
+    }
+    const int lane = static_cast<int>(threadIdx.x) & 63;
     const int bl = b0 + lane;
     const int cl = bl < B ? count(bl) : 0;
     int ps = cl;
@@ -772,16 +789,11 @@ __device__ __forceinline__ int find_seq_wave(const SeqDir& d, const int* pre, in
       const int o = __shfl_up(ps, m, 64);
       if (lane >= m) ps += o;
     }
-    const uint64_t hit = __ballot(acc + ps > r);
-    if (hit) {
-      const int L = __builtin_ctzll(hit);
-      c.b = b0 + L;
-      c.cnt = __shfl(cl, L, 64);
-      c.first = acc + __shfl(ps, L, 64) - c.cnt;
-      return c.b;
-    }
-    acc += __shfl(ps, 63, 64);
-    b0 += 64;
+    c.wb0 = b0;
+    c.wacc = acc;
+    c.wtot = __shfl(ps, 63, 64);
+    c.wcl = cl;
+    c.wps = ps;
   }
 }
 
